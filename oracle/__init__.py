@@ -1,0 +1,7 @@
+"""CPU fp64 oracle (test infrastructure only; never used by the product path)."""
+
+from .masked_attention import (  # noqa: F401
+    CANDIDATE, EMPTY, FULL, HISTORY, PARTIAL, PROFILE, REALTIME, TILE_K, TILE_Q,
+    attention_forward, attention_rows, count_visible, masked_softmax_attention,
+    rope_frequencies, tile_plan, tile_plan_request, time_rope, visibility, visible_rows,
+)

@@ -1,0 +1,327 @@
+"""CPU fp64 oracle for request-centric masked attention with time RoPE.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module; only the test suite, the smoke check and the CPU-baseline
+leg of the benchmark use it.  It shares no code with the HIP library: it
+builds the explicit visibility matrix of every request pair by pair and runs
+plain softmax attention in float64.
+
+Sources (pages as they appear in the reference text):
+
+* CADET (paper-daily.com "CADET: Context-Conditioned Ads CTR Prediction With
+  a Decoder-Only Transformer"):
+  - section "why mask the most recent hour in training", equation
+    M_ij = -inf if t_j > t_i - Delta_delay            -> delay rule
+  - section "time encoding and self-gating", equation
+    alpha_i(t) = t * phi_min / Delta_t_max * base^(2i/d) -> time RoPE
+  - section "how to score hundreds of candidates in 50 ms": candidates are
+    appended after the user sequence and see the history but not each other.
+* SORT (10100.com article 149105610), section 3.1: U2U sees only its past,
+  C2U sees all user features, C2C isolated; section 3.2.1: sliding window in
+  U2U only.
+* LazFormer (liuzhao09.github.io lazformer page), section 2.3 equations 19-21:
+  allowed relation A(p, q) with window W, targets-to-history and target
+  self-links; masked entries are -inf and SparseAttn = softmax(QK^T/sqrt(d_k)
+  + M) V.
+* MTGR (joezjh.github.io blog index, "MTGR", model-structure part): static
+  profile + history mutually visible, real-time sequence causal, each target
+  sees the static tokens plus the real-time events before its own time, and
+  no other target.
+* TM20K (liuzhao09.github.io tm20k page, section 2.1 equations): scaled
+  dot-product attention with an additive mask.
+
+Readings taken where the pages are silent or ambiguous (each one is listed in
+the design notes of the repository as well):
+
+* pair index i of the rotation runs 0 .. d/2-1 and pairs adjacent components
+  (2i, 2i+1); the rotation is counter-clockwise;
+* the softmax scale is 1/sqrt(d_head);
+* the delay rule is literal (hidden iff t_j > t_i - Delta), so with Delta > 0
+  a token does not see itself; Delta = 0 switches the time condition off;
+* the delay and the window apply to static-to-static (U2U) pairs only; the
+  window keeps keys with p_i - p_j < W;
+* real-time to real-time is p_j <= p_i and t_j <= t_i; target to real-time is
+  t_j < t_i ("before");
+* a row with no visible key outputs 0 and has log-sum-exp -inf.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+PROFILE, HISTORY, REALTIME, CANDIDATE = 0, 1, 2, 3
+EMPTY, PARTIAL, FULL = 0, 1, 2
+TILE_Q, TILE_K = 128, 64
+
+
+# ---------------------------------------------------------------------------
+# Visibility rule (explicit, per pair)
+# ---------------------------------------------------------------------------
+
+def visible_rows(seg_kind: np.ndarray, timestamps: np.ndarray, rows: np.ndarray, *,
+                 delay: int, window: int, static_bidirectional: bool) -> np.ndarray:
+    """Visibility of every key for the query rows `rows` of ONE request.
+
+    Returns a bool array [len(rows), L]: True where query i may attend key j.
+    Each entry is the rule applied to the pair (i, j) on its own; evaluating
+    a subset of rows gives the same entries as the full matrix.
+    """
+    seg_kind = np.asarray(seg_kind)
+    t = np.asarray(timestamps, dtype=np.int64)
+    L = seg_kind.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    pi = rows[:, None]
+    pj = np.arange(L, dtype=np.int64)[None, :]
+    si = seg_kind[rows][:, None]
+    sj = seg_kind[None, :]
+    ti = t[rows][:, None]
+    tj = t[None, :]
+
+    static_i = (si == PROFILE) | (si == HISTORY)
+    static_j = (sj == PROFILE) | (sj == HISTORY)
+
+    # key is a candidate: only the diagonal (C2C isolation, and U2C never)
+    vis = (sj == CANDIDATE) & (pi == pj)
+
+    # static query -> static key (U2U)
+    if static_bidirectional:
+        u2u = np.ones_like(vis)
+    else:
+        u2u = pj <= pi
+        if window > 0:
+            u2u = u2u & (pi - pj < window)
+        if delay > 0:
+            u2u = u2u & ~(tj > ti - delay)
+    vis |= static_i & static_j & u2u
+
+    # real-time query: sees every static key, and real-time keys up to itself
+    rt_i = si == REALTIME
+    vis |= rt_i & static_j
+    vis |= rt_i & (sj == REALTIME) & (pj <= pi) & (tj <= ti)
+
+    # candidate query: every static key (C2U) and real-time keys strictly before it
+    c_i = si == CANDIDATE
+    vis |= c_i & static_j
+    vis |= c_i & (sj == REALTIME) & (tj < ti)
+    return vis
+
+
+def visibility(seg_kind: np.ndarray, timestamps: np.ndarray, *, delay: int, window: int,
+               static_bidirectional: bool) -> np.ndarray:
+    """Full L x L visibility matrix of one request."""
+    L = np.asarray(seg_kind).shape[0]
+    return visible_rows(seg_kind, timestamps, np.arange(L), delay=delay, window=window,
+                        static_bidirectional=static_bidirectional)
+
+
+def count_visible(seg_kind, timestamps, *, delay, window, static_bidirectional,
+                  row_block: int = 1024) -> int:
+    """Number of visible (query, key) pairs of one request."""
+    L = np.asarray(seg_kind).shape[0]
+    total = 0
+    for r0 in range(0, L, row_block):
+        rows = np.arange(r0, min(L, r0 + row_block))
+        total += int(np.count_nonzero(visible_rows(seg_kind, timestamps, rows, delay=delay,
+                                                   window=window,
+                                                   static_bidirectional=static_bidirectional)))
+    return total
+
+
+# ---------------------------------------------------------------------------
+# Time RoPE (CADET, time-encoding section)
+# ---------------------------------------------------------------------------
+
+def rope_frequencies(d: int, phi_min: float, dt_max: float, base: float) -> np.ndarray:
+    """omega_i = phi_min / dt_max * base^(2i/d), i = 0 .. d/2-1 (radians per time unit)."""
+    i = np.arange(d // 2, dtype=np.float64)
+    return phi_min / dt_max * np.power(float(base), 2.0 * i / d)
+
+
+def time_rope(x: np.ndarray, t: np.ndarray, *, phi_min: float, dt_max: float,
+              base: float) -> np.ndarray:
+    """Rotate pairs (2i, 2i+1) of x[..., d] by alpha_i(t) = t * omega_i.
+
+    x has shape [N, ..., d]; t has shape [N] (one time per token, shared by
+    every head).  Computed in float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    omega = rope_frequencies(d, phi_min, dt_max, base)
+    t = np.asarray(t, dtype=np.float64).reshape((-1,) + (1,) * (x.ndim - 1))
+    alpha = t * omega                      # [N, 1.., d/2]
+    c, s = np.cos(alpha), np.sin(alpha)
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * c - xo * s
+    out[..., 1::2] = xe * s + xo * c
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Masked softmax attention (plain definition)
+# ---------------------------------------------------------------------------
+
+def masked_softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarray,
+                             scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """softmax(q k^T * scale + M) v for one head, M = 0 where vis else -inf.
+
+    q [Lq, d], k [Lk, d], v [Lk, d], vis bool [Lq, Lk].  Returns (o [Lq, d],
+    lse [Lq]) where lse is the natural log of the softmax denominator of the
+    scaled scores.  A row with no visible key gives o = 0 and lse = -inf.
+    """
+    s = (q @ k.T) * scale
+    s = np.where(vis, s, -np.inf)
+    has = vis.any(axis=1)
+    m = np.where(has, s.max(axis=1, initial=-np.inf), 0.0)
+    e = np.exp(s - m[:, None])             # exp(-inf) = 0 on hidden keys
+    denom = e.sum(axis=1)
+    o = np.zeros((q.shape[0], v.shape[1]), dtype=np.float64)
+    o[has] = (e[has] @ v) / denom[has, None]
+    lse = np.full(q.shape[0], -np.inf)
+    lse[has] = m[has] + np.log(denom[has])
+    return o, lse
+
+
+def attention_forward(req_offsets: np.ndarray, seg_kind: np.ndarray, timestamps: np.ndarray,
+                      q: np.ndarray, k: np.ndarray, v: np.ndarray, *, delay: int, window: int,
+                      static_bidirectional: bool, rope: Optional[Dict[str, float]] = None,
+                      rope_times: Optional[np.ndarray] = None, scale: Optional[float] = None,
+                      heads: Optional[np.ndarray] = None, requests: Optional[np.ndarray] = None,
+                      row_block: int = 1024) -> Tuple[np.ndarray, np.ndarray]:
+    """Masked attention forward over a packed batch, in float64.
+
+    q, k, v: [T, H, d] (any float dtype; upcast to float64).  With `rope`
+    (keys phi_min, dt_max, base) Q and K are rotated by time RoPE using
+    `rope_times` (default: the absolute timestamps).  Returns o [T, H, d] and
+    lse [H, T].  `heads` / `requests` restrict the work to a subset (other
+    entries stay 0 / -inf).  Rows are processed in blocks of `row_block`;
+    every row's softmax is independent, so blocking does not change results.
+    """
+    T, H, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    o = np.zeros((T, H, d), np.float64)
+    lse = np.full((H, T), -np.inf)
+    heads = np.arange(H) if heads is None else np.asarray(heads)
+    R = req_offsets.shape[0] - 1
+    requests = np.arange(R) if requests is None else np.asarray(requests)
+    if rope is not None:
+        tr = timestamps if rope_times is None else rope_times
+    for r in requests:
+        a, b = int(req_offsets[r]), int(req_offsets[r + 1])
+        L = b - a
+        if L == 0:
+            continue
+        sk, ts = seg_kind[a:b], timestamps[a:b]
+        qr, kr, vr = q[a:b], k[a:b], v[a:b]
+        if rope is not None:
+            qr = time_rope(qr, tr[a:b], **rope)
+            kr = time_rope(kr, tr[a:b], **rope)
+        for r0 in range(0, L, row_block):
+            rows = np.arange(r0, min(L, r0 + row_block))
+            vis = visible_rows(sk, ts, rows, delay=delay, window=window,
+                               static_bidirectional=static_bidirectional)
+            for h in heads:
+                oh, lh = masked_softmax_attention(qr[rows, h], kr[:, h], vr[:, h], vis, scale)
+                o[a + rows, h] = oh
+                lse[h, a + rows] = lh
+    return o, lse
+
+
+def attention_rows(req_offsets, seg_kind, timestamps, q, k, v, tokens: np.ndarray,
+                   head: int, *, delay, window, static_bidirectional, rope=None,
+                   rope_times=None, scale=None):
+    """Output rows for selected global tokens of one head (for sampled checks).
+
+    Each token is computed against its own request's keys, exactly as in
+    attention_forward.  Returns (o [n, d], lse [n]).
+    """
+    T, H, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    tokens = np.asarray(tokens, np.int64)
+    req_of = np.searchsorted(req_offsets, tokens, side="right") - 1
+    o = np.zeros((tokens.shape[0], d))
+    lse = np.full(tokens.shape[0], -np.inf)
+    tr = timestamps if rope_times is None else rope_times
+    for r in np.unique(req_of):
+        sel = np.nonzero(req_of == r)[0]
+        a, b = int(req_offsets[r]), int(req_offsets[r + 1])
+        rows = tokens[sel] - a
+        sk, ts = seg_kind[a:b], timestamps[a:b]
+        qr = np.asarray(q[a + rows, head], np.float64)
+        kr = np.asarray(k[a:b, head], np.float64)
+        vr = np.asarray(v[a:b, head], np.float64)
+        if rope is not None:
+            qr = time_rope(qr, tr[a + rows], **rope)
+            kr = time_rope(kr, tr[a:b], **rope)
+        vis = visible_rows(sk, ts, rows, delay=delay, window=window,
+                           static_bidirectional=static_bidirectional)
+        oh, lh = masked_softmax_attention(qr, kr, vr, vis, scale)
+        o[sel] = oh
+        lse[sel] = lh
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Tile plan reference (128 query rows x 64 key columns)
+# ---------------------------------------------------------------------------
+
+def tile_plan_request(seg_kind, timestamps, *, delay, window, static_bidirectional,
+                      tq: int = TILE_Q, tk: int = TILE_K):
+    """Per-tile visible counts and classes of one request.
+
+    Tile (qt, kt) covers request-local rows [tq*qt, tq*qt+tq) and columns
+    [tk*kt, tk*kt+tk).  count = number of visible in-range cells.  FULL iff all
+    tq*tk cells are in range and visible; EMPTY iff count == 0; PARTIAL
+    otherwise.  Returns (count [nqt, nkt] int64, cls [nqt, nkt] uint8).
+    """
+    L = np.asarray(seg_kind).shape[0]
+    nqt, nkt = -(-L // tq), -(-L // tk)
+    count = np.zeros((nqt, nkt), np.int64)
+    for qt in range(nqt):
+        rows = np.arange(qt * tq, min(L, qt * tq + tq))
+        vis = visible_rows(seg_kind, timestamps, rows, delay=delay, window=window,
+                           static_bidirectional=static_bidirectional)
+        padded = np.zeros((vis.shape[0], nkt * tk), dtype=bool)
+        padded[:, :L] = vis
+        count[qt] = padded.reshape(vis.shape[0], nkt, tk).sum(axis=(0, 2))
+    cls = np.full((nqt, nkt), PARTIAL, np.uint8)
+    cls[count == 0] = EMPTY
+    cls[count == tq * tk] = FULL
+    return count, cls
+
+
+def tile_plan(req_offsets, seg_kind, timestamps, *, delay, window, static_bidirectional,
+              tq: int = TILE_Q, tk: int = TILE_K) -> Dict[str, np.ndarray]:
+    """Tile plan of a packed batch: flattened per-request tile arrays plus CSR.
+
+    tile_count / tile_class: concatenation over requests of the row-major
+    [nqt_r, nkt_r] arrays.  qtile_ptr / ktile_idx: CSR over all q-tiles in
+    request order; each row lists its non-empty request-local k-tile indices in
+    ascending order.  visible_pairs: total visible pairs (per head).
+    """
+    counts, classes, ptr, idx = [], [], [0], []
+    for r in range(req_offsets.shape[0] - 1):
+        a, b = int(req_offsets[r]), int(req_offsets[r + 1])
+        c, k = tile_plan_request(seg_kind[a:b], timestamps[a:b], delay=delay, window=window,
+                                 static_bidirectional=static_bidirectional, tq=tq, tk=tk)
+        counts.append(c.ravel())
+        classes.append(k.ravel())
+        for qt in range(c.shape[0]):
+            nz = np.nonzero(c[qt])[0]
+            idx.append(nz)
+            ptr.append(ptr[-1] + nz.shape[0])
+    cat = lambda xs, dt: np.concatenate(xs).astype(dt) if xs else np.zeros(0, dt)
+    tile_count = cat(counts, np.int64)
+    return {
+        "tile_count": tile_count,
+        "tile_class": cat(classes, np.uint8),
+        "qtile_ptr": np.asarray(ptr, np.int64),
+        "ktile_idx": cat(idx, np.int64),
+        "visible_pairs": int(tile_count.sum()),
+    }
