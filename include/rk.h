@@ -1,0 +1,306 @@
+/*
+ * rk.h -- C ABI of librk: request-centric masked multi-head attention
+ * (forward) with time RoPE, for AMD Instinct MI355X (gfx950).
+ *
+ * One packed buffer holds R requests.  Each request is one user sequence:
+ * optional PROFILE tokens, HISTORY tokens, optional same-day REALTIME
+ * tokens and N CANDIDATE (target) tokens, in that order.  Every token
+ * carries an int64 timestamp in seconds.  Three operations are exported:
+ *
+ *   rk_mask_plan        classify every 128 x 64 (query x key) tile of every
+ *                       request as EMPTY / PARTIAL / FULL with its exact
+ *                       visible-pair count, list the non-empty key tiles of
+ *                       each query tile (CSR) and build the launch schedule;
+ *   rk_time_rope        rotate Q or K by time RoPE;
+ *   rk_masked_attn_fwd  softmax(Q K^T * scale + M) V over the plan, with
+ *                       optional fused time RoPE.
+ *
+ * Sources (titles and sections of the pages this library follows):
+ *  - CADET: Context-Conditioned Ads CTR Prediction With a Decoder-Only
+ *    Transformer -- "why mask the most recent hour in training" (delay
+ *    mask equation), "time encoding and self-gating" (time RoPE equation),
+ *    "how to score hundreds of candidates in 50 ms" (candidates appended to
+ *    the user sequence, seeing the history but not each other; a
+ *    FlashAttention kernel that skips fully masked blocks; packed
+ *    variable-length sequences with start/end offsets).
+ *  - SORT: A Systematically Optimized Ranking Transformer for
+ *    Industrial-scale Recommenders -- section 3.1 (U2U, C2U, C2C regions),
+ *    section 3.2.1 (sliding-window local attention in U2U), section 4
+ *    (sparse attention operator that skips fully masked blocks).
+ *  - LazFormer -- section 2.3, equations 19-21 (allowed relation with
+ *    window W; -inf mask; SparseAttn = softmax(QK^T/sqrt(d_k) + M) V).
+ *  - MTGR (Meituan generative recommendation, blog post) -- model
+ *    structure, "mixed dynamic mask".
+ *  - HSTU, appendix H (M-FALCON): one pass with the modified causal mask
+ *    equals separate causal passes per candidate.
+ *
+ * Visibility of key j for query i of the same request (p = request-local
+ * position, t = timestamp, S = {PROFILE, HISTORY}):
+ *   key j is a CANDIDATE          : visible iff i == j;
+ *   i in S, j in S                : with RK_STATIC_BIDIRECTIONAL always;
+ *                                   otherwise p_j <= p_i, and
+ *                                   (window == 0 or p_i - p_j < window), and
+ *                                   (delay == 0 or t_j <= t_i - delay);
+ *   i in S, j REALTIME            : never;
+ *   i REALTIME, j in S            : always;
+ *   i REALTIME, j REALTIME        : p_j <= p_i and t_j <= t_i;
+ *   i CANDIDATE, j in S           : always;
+ *   i CANDIDATE, j REALTIME       : t_j < t_i.
+ * A query with no visible key outputs 0 (log-sum-exp -inf).
+ *
+ * Conventions
+ *  - Every device buffer is owned by the caller.  The library never
+ *    allocates device memory: the plan lives in a caller-provided
+ *    workspace whose size is computed on the host.
+ *  - All work is asynchronous on the caller's stream (`stream` is a
+ *    hipStream_t; NULL means the default stream).  Argument validation is
+ *    synchronous and happens before anything is enqueued; a call that
+ *    returns an error has enqueued nothing.
+ *  - Checks that need device data (segment order, timestamp order) are
+ *    recorded by rk_mask_plan on the device and reported by rk_plan_stats.
+ *  - No global mutable state: concurrent calls on distinct plans and
+ *    buffers are safe.
+ *  - Every struct starts with `struct_size` (= sizeof of the struct the
+ *    caller was compiled against).
+ */
+#ifndef RK_H
+#define RK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RK_ABI_VERSION 1
+
+typedef enum rk_status {
+  RK_OK = 0,
+  RK_ERR_INVALID_ARG = 1,         /* NULL pointer, bad size, bad offsets or parameters */
+  RK_ERR_SEGMENT_ORDER = 2,       /* segment kinds out of order or out of range (device check) */
+  RK_ERR_UNSORTED_TIME = 3,       /* timestamps not non-decreasing where required (device check) */
+  RK_ERR_UNSUPPORTED = 4,         /* dtype / d_head / alignment / size not supported */
+  RK_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace smaller than the size query returned */
+  RK_ERR_HIP = 6                  /* a HIP runtime call failed */
+} rk_status;
+
+typedef enum rk_dtype { RK_F32 = 0, RK_BF16 = 1 } rk_dtype;
+
+/* Segment kinds (per token, uint8).  Non-decreasing inside a request. */
+enum { RK_SEG_PROFILE = 0, RK_SEG_HISTORY = 1, RK_SEG_REALTIME = 2, RK_SEG_CANDIDATE = 3 };
+
+/* Tile classes of the plan. */
+enum { RK_TILE_EMPTY = 0, RK_TILE_PARTIAL = 1, RK_TILE_FULL = 2 };
+
+#define RK_TILE_Q 128 /* query rows per tile */
+#define RK_TILE_K 64  /* key columns per tile */
+
+/* rk_mask_params.flags */
+#define RK_STATIC_BIDIRECTIONAL 0x1u /* PROFILE+HISTORY mutually visible (MTGR static part) */
+
+/* rk_attn_args.flags */
+#define RK_ATTN_REFERENCE_KERNEL 0x1u /* force the plain (non-MFMA) kernel */
+
+/*
+ * A packed batch (CADET, "how to score hundreds of candidates": all tokens
+ * of a batch in one buffer plus per-sequence start/end offsets).
+ *   req_offsets_host/_dev : int32 [num_requests + 1]; [0] == 0,
+ *                           non-decreasing, [num_requests] == total_tokens.
+ *                           Host and device copies must hold equal values.
+ *   seg_kind_dev          : uint8 [total_tokens], RK_SEG_*; non-decreasing
+ *                           inside each request.
+ *   timestamps_dev        : int64 [total_tokens], seconds.  Must be
+ *                           non-decreasing inside REALTIME, and inside
+ *                           PROFILE+HISTORY when the static part is causal
+ *                           and delay > 0.
+ *   anchors_dev           : int64 [num_requests]; time origin of each
+ *                           request's RoPE angles (any value; outputs of
+ *                           the attention do not depend on it).
+ * All device arrays must stay valid and unchanged while a plan built from
+ * the batch is in use.
+ */
+typedef struct rk_batch {
+  uint32_t struct_size;
+  int32_t num_requests;
+  int32_t total_tokens;
+  const int32_t* req_offsets_host;
+  const int32_t* req_offsets_dev;
+  const uint8_t* seg_kind_dev;
+  const int64_t* timestamps_dev;
+  const int64_t* anchors_dev;
+} rk_batch;
+
+/* Mask parameters (CADET delay mask; SORT / LazFormer window; MTGR static part). */
+typedef struct rk_mask_params {
+  uint32_t struct_size;
+  uint32_t flags;  /* RK_STATIC_BIDIRECTIONAL or 0 */
+  int64_t delay;   /* Delta_delay in timestamp units, >= 0; 0 = off */
+  int32_t window;  /* keys kept including self, >= 0; 0 = off */
+  int32_t reserved;
+} rk_mask_params;
+
+/* Time RoPE (CADET, "time encoding"): pair (2i, 2i+1), i = 0 .. d/2-1, of a
+ * token with time t in request r is rotated counter-clockwise by
+ *   alpha_i = (t - anchor_r) * phi_min / dt_max * base^(2i/d).
+ * dt_max is in timestamp units (1 year = 31,536,000 s on the page). */
+typedef struct rk_rope_params {
+  uint32_t struct_size;
+  uint32_t reserved;
+  double phi_min; /* > 0 */
+  double dt_max;  /* > 0 */
+  double base;    /* > 0 */
+} rk_rope_params;
+
+typedef struct rk_plan rk_plan;
+
+/* Host-side description of a plan.  Byte offsets are relative to the start
+ * of the plan workspace; the arrays there are valid once the stream has
+ * executed rk_mask_plan's work. */
+typedef struct rk_plan_info {
+  uint32_t struct_size;
+  int32_t num_requests;
+  int32_t total_tokens;
+  int32_t num_heads;
+  int64_t num_qtiles;          /* sum over requests of ceil(L_r / 128) */
+  int64_t num_tiles;           /* sum over requests of ceil(L_r/128)*ceil(L_r/64) */
+  int64_t num_sched_slots;     /* grid size of rk_masked_attn_fwd */
+  const void* workspace;
+  size_t off_tile_class;       /* uint8 [num_tiles], RK_TILE_*, requests in order, row-major [qt][kt] */
+  size_t off_tile_count;       /* int32 [num_tiles], visible pairs per tile */
+  size_t off_qtile_ptr;        /* int32 [num_qtiles + 1], CSR row pointers */
+  size_t off_ktile_idx;        /* int32 [num_tiles] (first qtile_ptr[num_qtiles] used), request-local kt, ascending */
+  size_t off_row_desc;         /* int32 [total_tokens][2]: visible keys of a query = [lo, hi) plus bit 31 of hi = self */
+  size_t off_sched;            /* int32 [num_sched_slots]: work item = qtile * num_heads + head, or -1 */
+} rk_plan_info;
+
+/* Totals of a plan (per head). */
+typedef struct rk_plan_totals {
+  uint32_t struct_size;
+  uint32_t device_errors;      /* bit 0: segment order/kind, bit 1: timestamp order */
+  int64_t visible_pairs;       /* sum of all tile counts */
+  int64_t full_tiles;
+  int64_t partial_tiles;
+  int64_t empty_tiles;
+} rk_plan_totals;
+
+/*
+ * Attention arguments.  Q, K, V, O are [token, head, d] views with d
+ * contiguous and the given element strides.  dtype RK_BF16: bf16 inputs
+ * and output, fp32 accumulation and softmax, bf16 MFMA for d_head == 64
+ * (needs 16-byte aligned base pointers and strides that are multiples of
+ * 8); d_head in {32, 64, 128} otherwise.  dtype RK_F32: fp32 throughout,
+ * d_head in {32, 64, 128}.
+ *   lse       : optional float [num_heads][total_tokens], natural-log
+ *               log-sum-exp of the scaled scores; -inf for empty rows.
+ *   scale     : score scale; 0 selects 1/sqrt(d_head).
+ *   rope      : NULL = inputs are used as given; otherwise Q and K are
+ *               rotated by time RoPE with the plan's batch timestamps and
+ *               anchors (Q while it is staged, K by a pass into the
+ *               workspace).
+ *   workspace : device memory of at least rk_attn_workspace_size bytes,
+ *               256-byte aligned (may be NULL when that size is 0).
+ * O must not overlap Q, K, V or the workspace.
+ */
+typedef struct rk_attn_args {
+  uint32_t struct_size;
+  uint32_t flags;
+  rk_dtype dtype;
+  int32_t num_heads;
+  int32_t d_head;
+  int32_t reserved;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_stride_tok, q_stride_head;
+  int64_t k_stride_tok, k_stride_head;
+  int64_t v_stride_tok, v_stride_head;
+  int64_t o_stride_tok, o_stride_head;
+  float scale;
+  float reserved2;
+  const rk_rope_params* rope;
+  void* workspace;
+  size_t workspace_bytes;
+} rk_attn_args;
+
+/* Name of a status code (static string). */
+const char* rk_status_string(rk_status s);
+
+/* ABI version (RK_ABI_VERSION of the library). */
+int32_t rk_abi_version(void);
+
+/*
+ * Bytes of plan workspace needed for `b` and `num_heads` (host only; reads
+ * b->req_offsets_host).  Errors: RK_ERR_INVALID_ARG.
+ */
+rk_status rk_plan_workspace_size(const rk_batch* b, int32_t num_heads, size_t* bytes);
+
+/*
+ * Build the tile plan of a batch (CADET "50 ms" section: skip fully masked
+ * blocks; SORT section 4: block computation with a mask pre-check that
+ * skips fully masked blocks).
+ *   workspace : device memory, 256-byte aligned, >= rk_plan_workspace_size.
+ *               Owned by the caller; must outlive every use of the plan.
+ *   plan_out  : receives a small host object, freed with rk_plan_destroy
+ *               (after the last work that uses it has completed).
+ * Per tile (qt, kt) of request r, covering request-local query rows
+ * [128 qt, 128 qt + 128) and keys [64 kt, 64 kt + 64): count = visible
+ * in-range pairs; FULL iff all 8192 cells are in range and visible; EMPTY
+ * iff count == 0; PARTIAL otherwise.  The schedule orders the query tiles
+ * of each (request, head) by descending non-empty tile count and spreads
+ * (request, head) groups over the chip's eight XCDs.
+ * Errors: RK_ERR_INVALID_ARG, RK_ERR_UNSUPPORTED (more than 2^31-1 tiles
+ * or work items), RK_ERR_WORKSPACE_TOO_SMALL, RK_ERR_HIP.
+ */
+rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_heads,
+                       void* workspace, size_t workspace_bytes, rk_plan** plan_out,
+                       void* stream);
+
+/* Host-side plan description (no device access).  Errors: INVALID_ARG. */
+rk_status rk_plan_get_info(const rk_plan* p, rk_plan_info* out);
+
+/*
+ * Synchronise `stream`, then read the plan's totals and device checks.
+ * Returns RK_ERR_SEGMENT_ORDER or RK_ERR_UNSORTED_TIME when the batch
+ * broke the segment or time order (the totals are still filled in), and
+ * RK_ERR_HIP on a runtime failure.
+ */
+rk_status rk_plan_stats(const rk_plan* p, rk_plan_totals* out, void* stream);
+
+/* Free the host object of a plan (the workspace stays the caller's). */
+void rk_plan_destroy(rk_plan* p);
+
+/*
+ * Time RoPE (CADET, "time encoding and self-gating"): rotate x_in into
+ * x_out (same shape [total_tokens, num_heads, d_head], element strides as
+ * given; in place allowed when the strides are equal).  Angles use
+ * (t - anchor_r) computed exactly in int64; the phase is reduced in
+ * double precision before sin/cos.
+ * Errors: RK_ERR_INVALID_ARG, RK_ERR_UNSUPPORTED (d_head odd or > 128),
+ * RK_ERR_HIP.
+ */
+rk_status rk_time_rope(const rk_batch* b, const rk_rope_params* r, const void* x_in, void* x_out,
+                       rk_dtype dtype, int32_t num_heads, int32_t d_head,
+                       int64_t in_stride_tok, int64_t in_stride_head,
+                       int64_t out_stride_tok, int64_t out_stride_head, void* stream);
+
+/* Workspace bytes rk_masked_attn_fwd needs for `a` on plan `p` (host only). */
+rk_status rk_attn_workspace_size(const rk_plan* p, const rk_attn_args* a, size_t* bytes);
+
+/*
+ * Masked attention forward over a plan (TM20K section 2.1 / LazFormer
+ * eq. 21: softmax(Q K^T / sqrt(d) + M) V with M = 0 on visible pairs and
+ * -inf elsewhere).  EMPTY tiles are never read; the per-element mask is
+ * evaluated on PARTIAL tiles only.  One launch over the plan's schedule.
+ * Errors: RK_ERR_INVALID_ARG (including num_heads != the plan's),
+ * RK_ERR_UNSUPPORTED, RK_ERR_WORKSPACE_TOO_SMALL, RK_ERR_HIP.
+ */
+rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RK_H */

@@ -1,0 +1,223 @@
+"""Thin Python binding over librk's C ABI (include/rk.h).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the computation runs in librk's kernels.
+Names follow the C entry points.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _rk
+from ._rk import check, lib, sized
+
+
+def _stream(stream: Optional[torch.cuda.Stream]) -> C.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return _rk.RK_F32
+    if t.dtype == torch.bfloat16:
+        return _rk.RK_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def rope_params(phi_min: float, dt_max: float, base: float) -> _rk.rk_rope_params:
+    return sized(_rk.rk_rope_params, phi_min=float(phi_min), dt_max=float(dt_max),
+                 base=float(base))
+
+
+class Batch:
+    """Device copies of one packed batch plus its rk_batch descriptor."""
+
+    def __init__(self, req_offsets, seg_kind, timestamps, anchors, device="cuda"):
+        self.req_offsets_host = np.ascontiguousarray(req_offsets, dtype=np.int32)
+        self.R = int(self.req_offsets_host.shape[0] - 1)
+        self.T = int(self.req_offsets_host[-1])
+        self.req_offsets = torch.from_numpy(self.req_offsets_host.copy()).to(device)
+        self.seg_kind = torch.from_numpy(np.ascontiguousarray(seg_kind, dtype=np.uint8)).to(device)
+        self.timestamps = torch.from_numpy(np.ascontiguousarray(timestamps, dtype=np.int64)).to(device)
+        self.anchors = torch.from_numpy(np.ascontiguousarray(anchors, dtype=np.int64)).to(device)
+        self.c = sized(_rk.rk_batch, num_requests=self.R, total_tokens=self.T,
+                       req_offsets_host=self.req_offsets_host.ctypes.data,
+                       req_offsets_dev=self.req_offsets.data_ptr(),
+                       seg_kind_dev=self.seg_kind.data_ptr(),
+                       timestamps_dev=self.timestamps.data_ptr(),
+                       anchors_dev=self.anchors.data_ptr())
+
+    @classmethod
+    def from_workload(cls, wl, device="cuda") -> "Batch":
+        return cls(wl.req_offsets, wl.seg_kind, wl.timestamps, wl.anchors, device=device)
+
+
+def rk_plan_workspace_size(batch: Batch, num_heads: int) -> int:
+    n = C.c_size_t()
+    check(lib().rk_plan_workspace_size(C.byref(batch.c), int(num_heads), C.byref(n)),
+          "rk_plan_workspace_size")
+    return int(n.value)
+
+
+class Plan:
+    """A tile plan built by rk_mask_plan in a torch-owned workspace."""
+
+    def __init__(self, batch: Batch, *, delay: int = 0, window: int = 0,
+                 static_bidirectional: bool = False, num_heads: int = 1,
+                 stream: Optional[torch.cuda.Stream] = None,
+                 workspace: Optional[torch.Tensor] = None):
+        self.batch = batch
+        self.num_heads = int(num_heads)
+        size = rk_plan_workspace_size(batch, num_heads)
+        if workspace is None:
+            workspace = torch.empty(max(size, 256), dtype=torch.uint8, device=batch.seg_kind.device)
+        self.workspace = workspace
+        self.params = sized(_rk.rk_mask_params, delay=int(delay), window=int(window),
+                            flags=_rk.RK_STATIC_BIDIRECTIONAL if static_bidirectional else 0)
+        h = C.c_void_p()
+        check(lib().rk_mask_plan(C.byref(batch.c), C.byref(self.params), self.num_heads,
+                                 C.c_void_p(workspace.data_ptr()),
+                                 C.c_size_t(workspace.numel()), C.byref(h), _stream(stream)),
+              "rk_mask_plan")
+        self.handle = h
+        info = sized(_rk.rk_plan_info)
+        check(lib().rk_plan_get_info(h, C.byref(info)), "rk_plan_get_info")
+        self.info = info
+
+    # -- views into the workspace (valid after the stream ran the planner)
+    def _view(self, off: int, n: int, dtype: torch.dtype) -> torch.Tensor:
+        nbytes = n * torch.empty(0, dtype=dtype).element_size()
+        return self.workspace[off:off + nbytes].view(dtype)
+
+    @property
+    def num_tiles(self) -> int:
+        return int(self.info.num_tiles)
+
+    @property
+    def num_qtiles(self) -> int:
+        return int(self.info.num_qtiles)
+
+    def tile_class(self) -> torch.Tensor:
+        return self._view(self.info.off_tile_class, self.num_tiles, torch.uint8)
+
+    def tile_count(self) -> torch.Tensor:
+        return self._view(self.info.off_tile_count, self.num_tiles, torch.int32)
+
+    def qtile_ptr(self) -> torch.Tensor:
+        return self._view(self.info.off_qtile_ptr, self.num_qtiles + 1, torch.int32)
+
+    def ktile_idx(self) -> torch.Tensor:
+        n = int(self.qtile_ptr()[-1].item()) if self.num_qtiles else 0
+        return self._view(self.info.off_ktile_idx, n, torch.int32)
+
+    def row_desc(self) -> torch.Tensor:
+        return self._view(self.info.off_row_desc, 2 * self.batch.T, torch.int32).view(-1, 2)
+
+    def sched(self) -> torch.Tensor:
+        return self._view(self.info.off_sched, int(self.info.num_sched_slots), torch.int32)
+
+    def stats(self, stream: Optional[torch.cuda.Stream] = None, raise_on_error: bool = True) -> dict:
+        t = sized(_rk.rk_plan_totals)
+        st = lib().rk_plan_stats(self.handle, C.byref(t), _stream(stream))
+        if st not in (_rk.RK_OK, _rk.RK_ERR_SEGMENT_ORDER, _rk.RK_ERR_UNSORTED_TIME) or (
+                raise_on_error and st != _rk.RK_OK):
+            check(st, "rk_plan_stats")
+        return {"status": st, "device_errors": int(t.device_errors),
+                "visible_pairs": int(t.visible_pairs), "full_tiles": int(t.full_tiles),
+                "partial_tiles": int(t.partial_tiles), "empty_tiles": int(t.empty_tiles)}
+
+    def close(self) -> None:
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            torch.cuda.synchronize()
+            lib().rk_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def rk_mask_plan(batch: Batch, **kw) -> Plan:
+    return Plan(batch, **kw)
+
+
+def rk_time_rope(batch: Batch, x: torch.Tensor, *, phi_min: float, dt_max: float, base: float,
+                 out: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Rotate x [T, H, d] (d contiguous) by time RoPE into out (default: new tensor)."""
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("x must be [T, H, d] with d contiguous")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    rp = rope_params(phi_min, dt_max, base)
+    check(lib().rk_time_rope(C.byref(batch.c), C.byref(rp), C.c_void_p(x.data_ptr()),
+                             C.c_void_p(out.data_ptr()), _dtype_code(x), x.shape[1], x.shape[2],
+                             x.stride(0), x.stride(1), out.stride(0), out.stride(1), _stream(stream)),
+          "rk_time_rope")
+    return out
+
+
+def _attn_args(plan: Plan, q, k, v, o, lse, scale, rope, reference, workspace):
+    for t in (q, k, v, o):
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError("q, k, v, o must be [T, H, d] with d contiguous")
+    a = sized(_rk.rk_attn_args, flags=_rk.RK_ATTN_REFERENCE_KERNEL if reference else 0,
+              dtype=_dtype_code(q), num_heads=q.shape[1], d_head=q.shape[2],
+              q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), o=o.data_ptr(),
+              lse=lse.data_ptr() if lse is not None else None,
+              q_stride_tok=q.stride(0), q_stride_head=q.stride(1),
+              k_stride_tok=k.stride(0), k_stride_head=k.stride(1),
+              v_stride_tok=v.stride(0), v_stride_head=v.stride(1),
+              o_stride_tok=o.stride(0), o_stride_head=o.stride(1),
+              scale=float(scale))
+    if rope is not None:
+        a.rope = C.cast(C.pointer(rope), C.c_void_p)
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def rk_attn_workspace_size(plan: Plan, q, k, v, *, rope=None, reference=False) -> int:
+    o = q  # only shapes/strides are read
+    rp = rope_params(**rope) if rope is not None else None
+    a = _attn_args(plan, q, k, v, o, None, 0.0, rp, reference, None)
+    n = C.c_size_t()
+    check(lib().rk_attn_workspace_size(plan.handle, C.byref(a), C.byref(n)), "rk_attn_workspace_size")
+    return int(n.value)
+
+
+def rk_masked_attn_fwd(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       want_lse: bool = False, scale: float = 0.0, rope: Optional[dict] = None,
+                       reference: bool = False, workspace: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None):
+    """Masked attention forward over `plan`.  Returns (o, lse or None).
+
+    rope: None, or dict(phi_min=..., dt_max=..., base=...) to rotate Q and K
+    by time RoPE with the plan's timestamps and anchors.
+    """
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None and want_lse:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    rp = rope_params(**rope) if rope is not None else None
+    a = _attn_args(plan, q, k, v, out, lse, scale, rp, reference, workspace)
+    n = C.c_size_t()
+    check(lib().rk_attn_workspace_size(plan.handle, C.byref(a), C.byref(n)), "rk_attn_workspace_size")
+    if n.value and workspace is None:
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=q.device)
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = n.value
+    check(lib().rk_masked_attn_fwd(plan.handle, C.byref(a), _stream(stream)), "rk_masked_attn_fwd")
+    # keep the workspace alive until the caller synchronises
+    out._rk_workspace = workspace  # type: ignore[attr-defined]
+    return out, lse

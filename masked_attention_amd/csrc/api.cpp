@@ -1,0 +1,465 @@
+// C ABI of librk (declared in include/rk.h): argument validation, plan
+// workspace layout, the host side of the launch schedule, and dispatch to
+// the HIP kernels.  Validation is synchronous and precedes every enqueue.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "rk_internal.h"
+
+using rk::Group;
+using rk::kNumXcd;
+using rk::PlanTotals;
+using rk::ReqMeta;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kInt32Max = 2147483647;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Sizes and host-side tables derived from req_offsets_host.
+struct Layout {
+  int32_t R = 0, T = 0, H = 0;
+  int64_t NQ = 0, NT = 0, G = 0, max_queue = 0, slots = 0;
+  std::vector<ReqMeta> req;
+  std::vector<int32_t> qt_req;
+  std::vector<Group> groups;        // sorted by (queue, base)
+  std::vector<int32_t> queue_start; // kNumXcd + 1
+  size_t off_req = 0, off_qt_req = 0, off_groups = 0, off_queue_start = 0, off_totals = 0,
+         host_blob = 0, off_row_desc = 0, off_tile_count = 0, off_tile_class = 0, off_qt_nnz = 0,
+         off_qtile_ptr = 0, off_ktile_idx = 0, off_ktile_cls = 0, off_qorder = 0, off_sched = 0,
+         total = 0;
+};
+
+rk_status check_batch(const rk_batch* b) {
+  if (!b || b->struct_size < sizeof(rk_batch)) return RK_ERR_INVALID_ARG;
+  if (b->num_requests < 0 || b->total_tokens < 0) return RK_ERR_INVALID_ARG;
+  if (!b->req_offsets_host) return RK_ERR_INVALID_ARG;
+  const int32_t* o = b->req_offsets_host;
+  if (o[0] != 0) return RK_ERR_INVALID_ARG;
+  for (int32_t r = 0; r < b->num_requests; ++r)
+    if (o[r + 1] < o[r]) return RK_ERR_INVALID_ARG;
+  if (o[b->num_requests] != b->total_tokens) return RK_ERR_INVALID_ARG;
+  if (b->num_requests > 0 && (!b->req_offsets_dev || !b->anchors_dev)) return RK_ERR_INVALID_ARG;
+  if (b->total_tokens > 0 && (!b->seg_kind_dev || !b->timestamps_dev)) return RK_ERR_INVALID_ARG;
+  return RK_OK;
+}
+
+rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L) {
+  rk_status st = check_batch(b);
+  if (st != RK_OK) return st;
+  if (H < 1) return RK_ERR_INVALID_ARG;
+  L->R = b->num_requests;
+  L->T = b->total_tokens;
+  L->H = H;
+  const int32_t* o = b->req_offsets_host;
+  int64_t nq = 0, nt = 0;
+  if (with_tables) L->req.resize(L->R);
+  std::vector<int64_t> weight(L->R);
+  for (int32_t r = 0; r < L->R; ++r) {
+    const int32_t len = o[r + 1] - o[r];
+    const int32_t nqt = (len + rk::kTileQ - 1) / rk::kTileQ;
+    const int32_t nkt = (len + rk::kTileK - 1) / rk::kTileK;
+    if (with_tables) {
+      ReqMeta& m = L->req[r];
+      m.tok_off = o[r];
+      m.len = len;
+      m.qt_off = (int32_t)std::min<int64_t>(nq, kInt32Max);
+      m.nqt = nqt;
+      m.nkt = nkt;
+      m.pad0 = 0;
+      m.tile_off = nt;
+      for (int k = 0; k < 4; ++k) m.seg[k] = len;
+    }
+    weight[r] = (int64_t)nqt * nkt;
+    nq += nqt;
+    nt += (int64_t)nqt * nkt;
+  }
+  if (nt >= kInt32Max || nq * (int64_t)H >= kInt32Max) return RK_ERR_UNSUPPORTED;
+  L->NQ = nq;
+  L->NT = nt;
+
+  // Launch schedule: (request, head) groups, heaviest first, each placed on
+  // the least-loaded of the eight XCD queues (dense tile count as weight).
+  std::vector<Group> gs;
+  std::vector<int64_t> gw;
+  std::vector<int> gq;
+  int64_t counts[kNumXcd] = {0};
+  {
+    std::vector<int32_t> order;
+    for (int32_t r = 0; r < L->R; ++r)
+      if (o[r + 1] > o[r]) order.push_back(r);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t c) { return weight[a] > weight[c]; });
+    int64_t loads[kNumXcd] = {0};
+    for (int32_t r : order) {
+      const int32_t nqt = (o[r + 1] - o[r] + rk::kTileQ - 1) / rk::kTileQ;
+      for (int32_t h = 0; h < H; ++h) {
+        int q = 0;
+        for (int j = 1; j < kNumXcd; ++j)
+          if (loads[j] < loads[q]) q = j;
+        Group g;
+        g.req = r;
+        g.head = h;
+        g.base = (int32_t)std::min<int64_t>(counts[q], kInt32Max);
+        g.count = nqt;
+        loads[q] += weight[r];
+        counts[q] += nqt;
+        gs.push_back(g);
+        gq.push_back(q);
+      }
+    }
+  }
+  int64_t mq = 0;
+  for (int j = 0; j < kNumXcd; ++j) mq = std::max(mq, counts[j]);
+  L->max_queue = mq;
+  L->slots = mq * kNumXcd;
+  if (L->slots >= kInt32Max) return RK_ERR_UNSUPPORTED;
+  L->G = (int64_t)gs.size();
+  if (with_tables) {
+    L->queue_start.assign(kNumXcd + 1, 0);
+    for (int j = 0; j < kNumXcd; ++j) {
+      L->queue_start[j] = (int32_t)L->groups.size();
+      for (size_t i = 0; i < gs.size(); ++i)
+        if (gq[i] == j) L->groups.push_back(gs[i]);  // bases increase within a queue
+    }
+    L->queue_start[kNumXcd] = (int32_t)L->groups.size();
+    L->qt_req.resize(nq);
+    for (int32_t r = 0; r < L->R; ++r)
+      for (int32_t i = 0; i < L->req[r].nqt; ++i) L->qt_req[L->req[r].qt_off + i] = r;
+  }
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L->off_req = take(sizeof(ReqMeta) * (size_t)L->R);
+  L->off_qt_req = take(sizeof(int32_t) * (size_t)nq);
+  L->off_groups = take(sizeof(Group) * (size_t)L->G);
+  L->off_queue_start = take(sizeof(int32_t) * (kNumXcd + 1));
+  L->off_totals = take(sizeof(PlanTotals));
+  L->host_blob = off;
+  L->off_row_desc = take(sizeof(int2) * (size_t)L->T);
+  L->off_tile_count = take(sizeof(int32_t) * (size_t)nt);
+  L->off_tile_class = take((size_t)nt);
+  L->off_qt_nnz = take(sizeof(int32_t) * (size_t)nq);
+  L->off_qtile_ptr = take(sizeof(int32_t) * (size_t)(nq + 1));
+  L->off_ktile_idx = take(sizeof(int32_t) * (size_t)nt);
+  L->off_ktile_cls = take((size_t)nt);
+  L->off_qorder = take(sizeof(int32_t) * (size_t)nq);
+  L->off_sched = take(sizeof(int32_t) * (size_t)L->slots);
+  L->total = off;
+  return RK_OK;
+}
+
+rk_status check_rope(const rk_rope_params* r) {
+  if (!r || r->struct_size < sizeof(rk_rope_params)) return RK_ERR_INVALID_ARG;
+  if (!(std::isfinite(r->phi_min) && std::isfinite(r->dt_max) && std::isfinite(r->base)))
+    return RK_ERR_INVALID_ARG;
+  if (!(r->phi_min > 0 && r->dt_max > 0 && r->base > 0)) return RK_ERR_INVALID_ARG;
+  return RK_OK;
+}
+
+rk::RopeTab make_tab(const rk_rope_params* r, int d) {
+  rk::RopeTab t;
+  std::memset(&t, 0, sizeof(t));
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < d / 2 && i < rk::kMaxHalfD; ++i)
+    t.w_rev[i] = r->phi_min / r->dt_max * std::pow(r->base, 2.0 * i / d) / two_pi;
+  return t;
+}
+
+size_t elem_size(rk_dtype dt) { return dt == RK_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+const char* rk_status_string(rk_status s) {
+  switch (s) {
+    case RK_OK: return "ok";
+    case RK_ERR_INVALID_ARG: return "invalid argument";
+    case RK_ERR_SEGMENT_ORDER: return "segment kinds out of order or out of range";
+    case RK_ERR_UNSORTED_TIME: return "timestamps not in order where required";
+    case RK_ERR_UNSUPPORTED: return "unsupported configuration";
+    case RK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case RK_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t rk_abi_version(void) { return RK_ABI_VERSION; }
+
+rk_status rk_plan_workspace_size(const rk_batch* b, int32_t num_heads, size_t* bytes) {
+  if (!bytes) return RK_ERR_INVALID_ARG;
+  Layout L;
+  rk_status st = make_layout(b, num_heads, false, &L);
+  if (st != RK_OK) return st;
+  *bytes = L.total;
+  return RK_OK;
+}
+
+rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_heads,
+                       void* workspace, size_t workspace_bytes, rk_plan** plan_out, void* stream) {
+  if (!plan_out) return RK_ERR_INVALID_ARG;
+  *plan_out = nullptr;
+  if (!m || m->struct_size < sizeof(rk_mask_params)) return RK_ERR_INVALID_ARG;
+  if (m->delay < 0 || m->window < 0 || (m->flags & ~RK_STATIC_BIDIRECTIONAL)) return RK_ERR_INVALID_ARG;
+  Layout L;
+  rk_status st = make_layout(b, num_heads, true, &L);
+  if (st != RK_OK) return st;
+  if (!workspace || ((uintptr_t)workspace % kAlign) != 0) return RK_ERR_INVALID_ARG;
+  if (workspace_bytes < L.total) return RK_ERR_WORKSPACE_TOO_SMALL;
+
+  rk_plan* p = new (std::nothrow) rk_plan();
+  if (!p) return RK_ERR_INVALID_ARG;
+  p->R = L.R;
+  p->T = L.T;
+  p->H = L.H;
+  p->NQ = L.NQ;
+  p->NT = L.NT;
+  p->G = L.G;
+  p->slots = L.slots;
+  p->max_queue = L.max_queue;
+  p->delay = m->delay;
+  p->window = m->window;
+  p->flags = m->flags;
+  p->req_offsets_dev = b->req_offsets_dev;
+  p->seg_kind_dev = b->seg_kind_dev;
+  p->timestamps_dev = b->timestamps_dev;
+  p->anchors_dev = b->anchors_dev;
+  p->workspace = workspace;
+  p->workspace_bytes = workspace_bytes;
+  p->off_req = L.off_req;
+  p->off_qt_req = L.off_qt_req;
+  p->off_groups = L.off_groups;
+  p->off_queue_start = L.off_queue_start;
+  p->off_row_desc = L.off_row_desc;
+  p->off_tile_count = L.off_tile_count;
+  p->off_tile_class = L.off_tile_class;
+  p->off_qt_nnz = L.off_qt_nnz;
+  p->off_qtile_ptr = L.off_qtile_ptr;
+  p->off_ktile_idx = L.off_ktile_idx;
+  p->off_ktile_cls = L.off_ktile_cls;
+  p->off_qorder = L.off_qorder;
+  p->off_sched = L.off_sched;
+  p->off_totals = L.off_totals;
+  p->host_blob_bytes = L.host_blob;
+  p->total_bytes = L.total;
+
+  unsigned char* ws = (unsigned char*)workspace;
+  rk::PlanDev& D = p->dev;
+  D.req = (ReqMeta*)(ws + L.off_req);
+  D.qt_req = (int32_t*)(ws + L.off_qt_req);
+  D.groups = (Group*)(ws + L.off_groups);
+  D.queue_start = (int32_t*)(ws + L.off_queue_start);
+  D.totals = (PlanTotals*)(ws + L.off_totals);
+  D.row_desc = (int2*)(ws + L.off_row_desc);
+  D.tile_count = (int32_t*)(ws + L.off_tile_count);
+  D.tile_class = (uint8_t*)(ws + L.off_tile_class);
+  D.qt_nnz = (int32_t*)(ws + L.off_qt_nnz);
+  D.qtile_ptr = (int32_t*)(ws + L.off_qtile_ptr);
+  D.ktile_idx = (int32_t*)(ws + L.off_ktile_idx);
+  D.ktile_cls = (uint8_t*)(ws + L.off_ktile_cls);
+  D.qorder = (int32_t*)(ws + L.off_qorder);
+  D.sched = (int32_t*)(ws + L.off_sched);
+
+  p->host_blob = (unsigned char*)std::calloc(L.host_blob ? L.host_blob : 1, 1);
+  if (!p->host_blob) {
+    delete p;
+    return RK_ERR_INVALID_ARG;
+  }
+  if (L.R) std::memcpy(p->host_blob + L.off_req, L.req.data(), sizeof(ReqMeta) * L.R);
+  if (L.NQ) std::memcpy(p->host_blob + L.off_qt_req, L.qt_req.data(), sizeof(int32_t) * L.NQ);
+  if (L.G) std::memcpy(p->host_blob + L.off_groups, L.groups.data(), sizeof(Group) * L.G);
+  std::memcpy(p->host_blob + L.off_queue_start, L.queue_start.data(), sizeof(int32_t) * (kNumXcd + 1));
+  // totals stay zero (calloc)
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(workspace, p->host_blob, L.host_blob, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = rk::launch_plan(p, s);
+  if (e != hipSuccess) {
+    std::free(p->host_blob);
+    delete p;
+    return RK_ERR_HIP;
+  }
+  *plan_out = p;
+  return RK_OK;
+}
+
+rk_status rk_plan_get_info(const rk_plan* p, rk_plan_info* out) {
+  if (!p || !out || out->struct_size < sizeof(rk_plan_info)) return RK_ERR_INVALID_ARG;
+  out->num_requests = p->R;
+  out->total_tokens = p->T;
+  out->num_heads = p->H;
+  out->num_qtiles = p->NQ;
+  out->num_tiles = p->NT;
+  out->num_sched_slots = p->slots;
+  out->workspace = p->workspace;
+  out->off_tile_class = p->off_tile_class;
+  out->off_tile_count = p->off_tile_count;
+  out->off_qtile_ptr = p->off_qtile_ptr;
+  out->off_ktile_idx = p->off_ktile_idx;
+  out->off_row_desc = p->off_row_desc;
+  out->off_sched = p->off_sched;
+  return RK_OK;
+}
+
+rk_status rk_plan_stats(const rk_plan* p, rk_plan_totals* out, void* stream) {
+  if (!p || !out || out->struct_size < sizeof(rk_plan_totals)) return RK_ERR_INVALID_ARG;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return RK_ERR_HIP;
+  PlanTotals t;
+  if (hipMemcpy(&t, p->dev.totals, sizeof(t), hipMemcpyDeviceToHost) != hipSuccess) return RK_ERR_HIP;
+  out->device_errors = t.errors;
+  out->visible_pairs = (int64_t)t.visible_pairs;
+  out->full_tiles = (int64_t)t.full_tiles;
+  out->partial_tiles = (int64_t)t.partial_tiles;
+  out->empty_tiles = (int64_t)t.empty_tiles;
+  if (t.errors & rk::kErrSegment) return RK_ERR_SEGMENT_ORDER;
+  if (t.errors & rk::kErrTime) return RK_ERR_UNSORTED_TIME;
+  return RK_OK;
+}
+
+void rk_plan_destroy(rk_plan* p) {
+  if (!p) return;
+  std::free(p->host_blob);
+  delete p;
+}
+
+rk_status rk_time_rope(const rk_batch* b, const rk_rope_params* r, const void* x_in, void* x_out,
+                       rk_dtype dtype, int32_t num_heads, int32_t d_head, int64_t in_stride_tok,
+                       int64_t in_stride_head, int64_t out_stride_tok, int64_t out_stride_head,
+                       void* stream) {
+  rk_status st = check_batch(b);
+  if (st != RK_OK) return st;
+  if ((st = check_rope(r)) != RK_OK) return st;
+  if (dtype != RK_F32 && dtype != RK_BF16) return RK_ERR_INVALID_ARG;
+  if (num_heads < 1 || d_head < 2) return RK_ERR_INVALID_ARG;
+  if ((d_head & 1) || d_head > 2 * rk::kMaxHalfD) return RK_ERR_UNSUPPORTED;
+  if (in_stride_tok < 0 || in_stride_head < 0 || out_stride_tok < 0 || out_stride_head < 0)
+    return RK_ERR_INVALID_ARG;
+  if (b->total_tokens > 0 && (!x_in || !x_out)) return RK_ERR_INVALID_ARG;
+  if (x_in == x_out && (in_stride_tok != out_stride_tok || in_stride_head != out_stride_head))
+    return RK_ERR_INVALID_ARG;
+  const rk::RopeTab tab = make_tab(r, d_head);
+  hipError_t e = rk::launch_rope(b->num_requests, b->total_tokens, b->req_offsets_dev,
+                                 b->timestamps_dev, b->anchors_dev, tab, x_in, x_out, dtype,
+                                 num_heads, d_head, in_stride_tok, in_stride_head, out_stride_tok,
+                                 out_stride_head, (hipStream_t)stream);
+  return e == hipSuccess ? RK_OK : RK_ERR_HIP;
+}
+
+namespace {
+
+rk_status check_attn(const rk_plan* p, const rk_attn_args* a) {
+  if (!p || !a || a->struct_size < sizeof(rk_attn_args)) return RK_ERR_INVALID_ARG;
+  if (a->dtype != RK_F32 && a->dtype != RK_BF16) return RK_ERR_INVALID_ARG;
+  if (a->num_heads != p->H) return RK_ERR_INVALID_ARG;
+  if (a->d_head != 32 && a->d_head != 64 && a->d_head != 128) return RK_ERR_UNSUPPORTED;
+  if (a->flags & ~RK_ATTN_REFERENCE_KERNEL) return RK_ERR_INVALID_ARG;
+  if (p->T > 0 && (!a->q || !a->k || !a->v || !a->o)) return RK_ERR_INVALID_ARG;
+  const int64_t st[8] = {a->q_stride_tok, a->q_stride_head, a->k_stride_tok, a->k_stride_head,
+                         a->v_stride_tok, a->v_stride_head, a->o_stride_tok, a->o_stride_head};
+  for (int64_t x : st)
+    if (x < 0) return RK_ERR_INVALID_ARG;
+  if (!(std::isfinite(a->scale) && a->scale >= 0.f)) return RK_ERR_INVALID_ARG;
+  if (a->rope) {
+    rk_status s = check_rope(a->rope);
+    if (s != RK_OK) return s;
+  }
+  return RK_OK;
+}
+
+bool mfma_eligible(const rk_attn_args* a) {
+  if (a->dtype != RK_BF16 || a->d_head != 64 || (a->flags & RK_ATTN_REFERENCE_KERNEL)) return false;
+  return true;
+}
+
+bool mfma_aligned(const rk_attn_args* a, bool k_in_workspace) {
+  auto al = [](const void* ptr) { return ((uintptr_t)ptr % 16) == 0; };
+  auto st = [](int64_t x) { return (x % 8) == 0; };
+  bool ok = al(a->q) && al(a->v) && al(a->o) && st(a->q_stride_tok) && st(a->q_stride_head) &&
+            st(a->v_stride_tok) && st(a->v_stride_head) && st(a->o_stride_tok) &&
+            st(a->o_stride_head);
+  if (!k_in_workspace) ok = ok && al(a->k) && st(a->k_stride_tok) && st(a->k_stride_head);
+  return ok;
+}
+
+size_t attn_ws_bytes(const rk_plan* p, const rk_attn_args* a) {
+  if (!a->rope) return 0;
+  return align_up((size_t)p->T * (size_t)a->num_heads * (size_t)a->d_head * elem_size(a->dtype));
+}
+
+}  // namespace
+
+rk_status rk_attn_workspace_size(const rk_plan* p, const rk_attn_args* a, size_t* bytes) {
+  if (!bytes) return RK_ERR_INVALID_ARG;
+  rk_status st = check_attn(p, a);
+  if (st != RK_OK) return st;
+  *bytes = attn_ws_bytes(p, a);
+  return RK_OK;
+}
+
+rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stream) {
+  rk_status st = check_attn(p, a);
+  if (st != RK_OK) return st;
+  const size_t need = attn_ws_bytes(p, a);
+  if (need > 0) {
+    if (!a->workspace || ((uintptr_t)a->workspace % kAlign) != 0) return RK_ERR_INVALID_ARG;
+    if (a->workspace_bytes < need) return RK_ERR_WORKSPACE_TOO_SMALL;
+  }
+  const bool use_mfma = mfma_eligible(a);
+  if (use_mfma && !mfma_aligned(a, a->rope != nullptr)) return RK_ERR_UNSUPPORTED;
+
+  rk::AttnLaunch L;
+  std::memset(&L, 0, sizeof(L));
+  L.q = a->q;
+  L.k = a->k;
+  L.v = a->v;
+  L.o = a->o;
+  L.lse = a->lse;
+  L.q_st = a->q_stride_tok;
+  L.q_sh = a->q_stride_head;
+  L.k_st = a->k_stride_tok;
+  L.k_sh = a->k_stride_head;
+  L.v_st = a->v_stride_tok;
+  L.v_sh = a->v_stride_head;
+  L.o_st = a->o_stride_tok;
+  L.o_sh = a->o_stride_head;
+  L.scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->d_head);
+  L.H = a->num_heads;
+  L.d = a->d_head;
+  L.T = p->T;
+  L.ts = p->timestamps_dev;
+  L.anchors = p->anchors_dev;
+  hipStream_t s = (hipStream_t)stream;
+  if (a->rope) {
+    L.tab = make_tab(a->rope, a->d_head);
+    L.rope_q = true;
+    // K is rotated once into the workspace ([T, H, d] dense); Q is rotated
+    // by the attention kernel while it is staged.
+    const int64_t hd = (int64_t)a->num_heads * a->d_head;
+    hipError_t e = rk::launch_rope(p->R, p->T, p->req_offsets_dev, p->timestamps_dev,
+                                   p->anchors_dev, L.tab, a->k, a->workspace, a->dtype,
+                                   a->num_heads, a->d_head, a->k_stride_tok, a->k_stride_head, hd,
+                                   a->d_head, s);
+    if (e != hipSuccess) return RK_ERR_HIP;
+    L.k = a->workspace;
+    L.k_st = hd;
+    L.k_sh = a->d_head;
+  }
+  hipError_t e = use_mfma ? rk::launch_attn_mfma_bf16_d64(p, L, s)
+                          : rk::launch_attn_reference(p, L, a->dtype, s);
+  return e == hipSuccess ? RK_OK : RK_ERR_HIP;
+}
+
+}  // extern "C"

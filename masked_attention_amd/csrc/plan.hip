@@ -1,0 +1,318 @@
+// Mask planner: row descriptors, 128x64 tile classification with exact
+// visible-pair counts, per-query-tile CSR of non-empty key tiles, and the
+// XCD-aware launch schedule.
+//
+// The visibility rule (CADET delay mask; SORT U2U/C2U/C2C and local window;
+// LazFormer eq. 19-21; MTGR mixed dynamic mask) gives every query row a
+// visible key set that is one interval [lo, hi) of request-local positions
+// plus, for candidates, the row itself:
+//   static query, causal   : [max(0, p-W+1), min(p+1, cut)) where cut is the
+//                            number of static keys with t_j <= t_i - delay
+//                            (static times are sorted, so a binary search)
+//   static query, bidir.   : [0, end of static)
+//   real-time query        : [0, p+1)  (static part, then real-time events up
+//                            to itself; sorted times make t_j <= t_i implied)
+//   candidate query        : [0, end of static + #real-time events with
+//                            t_j < t_i) plus itself.
+// Tile counts are sums of interval overlaps, so they are exact integers.
+#include "rk_internal.h"
+
+namespace rk {
+namespace {
+
+__device__ __forceinline__ int find_request(const ReqMeta* __restrict__ req, int R, int tok) {
+  // last request whose first token is <= tok; it is never empty
+  int a = 0, b = R;
+  while (a < b) {
+    int m = (a + b) >> 1;
+    if (req[m].tok_off <= tok) a = m + 1; else b = m;
+  }
+  return a - 1;
+}
+
+// number of keys in ts[0, n) with value <= x (ts non-decreasing)
+__device__ __forceinline__ int count_le(const int64_t* __restrict__ ts, int n, int64_t x) {
+  int a = 0, b = n;
+  while (a < b) {
+    int m = (a + b) >> 1;
+    if (ts[m] <= x) a = m + 1; else b = m;
+  }
+  return a;
+}
+
+// number of keys in ts[0, n) with value < x (ts non-decreasing)
+__device__ __forceinline__ int count_lt(const int64_t* __restrict__ ts, int n, int64_t x) {
+  int a = 0, b = n;
+  while (a < b) {
+    int m = (a + b) >> 1;
+    if (ts[m] < x) a = m + 1; else b = m;
+  }
+  return a;
+}
+
+// Exclusive scan of one int per thread over a block of blockDim.x (<= 1024)
+// threads.  Returns the exclusive prefix; *total receives the block sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* smem, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = (blockDim.x + 63) >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) smem[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      int t = smem[w];
+      smem[w] = run;
+      run += t;
+    }
+    smem[16] = run;
+  }
+  __syncthreads();
+  int res = smem[wave] + x - v;
+  *total = smem[16];
+  __syncthreads();
+  return res;
+}
+
+__global__ void plan_seg_kernel(PlanDev P, int R, int T, const uint8_t* __restrict__ kind,
+                                const int64_t* __restrict__ ts, int check_static_time) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T) return;
+  const int r = find_request(P.req, R, i);
+  const int p = i - P.req[r].tok_off;
+  unsigned err = 0;
+  int s = kind[i];
+  if (s > RK_SEG_CANDIDATE) { err |= kErrSegment; s = RK_SEG_CANDIDATE; }
+  int prev = -1;
+  if (p > 0) {
+    prev = kind[i - 1];
+    if (prev > RK_SEG_CANDIDATE) prev = RK_SEG_CANDIDATE;
+    if (s < prev) {
+      err |= kErrSegment;
+    } else {
+      const bool rt = (s == RK_SEG_REALTIME && prev == RK_SEG_REALTIME);
+      const bool st = check_static_time && s <= RK_SEG_HISTORY && prev <= RK_SEG_HISTORY;
+      if ((rt || st) && ts[i] < ts[i - 1]) err |= kErrTime;
+    }
+  }
+  for (int k = prev + 1; k <= s; ++k) P.req[r].seg[k] = p;
+  if (err) atomicOr(&P.totals->errors, err);
+}
+
+__global__ void plan_rowdesc_kernel(PlanDev P, int R, int T, const uint8_t* __restrict__ kind,
+                                    const int64_t* __restrict__ ts, int64_t delay, int window,
+                                    int bidir) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T) return;
+  const int r = find_request(P.req, R, i);
+  const ReqMeta m = P.req[r];
+  const int p = i - m.tok_off;
+  const int L = m.len;
+  // segment boundaries, made monotone and clamped so that any device data
+  // yields in-range descriptors
+  const int a_rt = min(max(m.seg[RK_SEG_REALTIME], 0), L);
+  const int a_c = min(max(m.seg[RK_SEG_CANDIDATE], a_rt), L);
+  const int64_t* tr = ts + m.tok_off;
+  int s = kind[i];
+  if (s > RK_SEG_CANDIDATE) s = RK_SEG_CANDIDATE;
+  int lo = 0, hi = 0, diag = 0;
+  if (s <= RK_SEG_HISTORY) {
+    if (bidir) {
+      hi = a_rt;
+    } else {
+      hi = min(p + 1, a_rt);
+      lo = window > 0 ? max(0, p - window + 1) : 0;
+      if (delay > 0) hi = min(hi, count_le(tr, a_rt, ts[i] - delay));
+    }
+  } else if (s == RK_SEG_REALTIME) {
+    hi = p + 1;
+  } else {
+    hi = a_rt + count_lt(tr + a_rt, a_c - a_rt, ts[i]);
+    diag = 1;
+  }
+  if (hi <= lo) { lo = 0; hi = 0; }
+  P.row_desc[i] = make_int2(lo, (int)((unsigned)hi | ((unsigned)diag << 31)));
+}
+
+// One block per global q-tile: exact visible count and class of each of its
+// k-tiles, and the number of non-empty k-tiles.
+__global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
+  __shared__ int2 d[kTileQ];
+  __shared__ unsigned long long acc[4];
+  __shared__ int nnz_s;
+  const int g = blockIdx.x;
+  const int r = P.qt_req[g];
+  const ReqMeta m = P.req[r];
+  const int qt = g - m.qt_off;
+  const int row0 = qt * kTileQ;
+  const int nrows = min(kTileQ, m.len - row0);
+  if (threadIdx.x < kTileQ)
+    d[threadIdx.x] = threadIdx.x < nrows ? P.row_desc[m.tok_off + row0 + threadIdx.x] : make_int2(0, 0);
+  if (threadIdx.x < 4) acc[threadIdx.x] = 0;
+  if (threadIdx.x == 0) nnz_s = 0;
+  __syncthreads();
+  unsigned long long pairs = 0, nfull = 0, npart = 0, nempty = 0;
+  int nnz = 0;
+  for (int kt = threadIdx.x; kt < m.nkt; kt += blockDim.x) {
+    const int c0 = kt * kTileK;
+    const int c1 = min(m.len, c0 + kTileK);
+    int cnt = 0;
+    for (int t = 0; t < nrows; ++t) {
+      const int lo = d[t].x;
+      const int hi = d[t].y & 0x7fffffff;
+      const int a = max(lo, c0), b = min(hi, c1);
+      cnt += max(0, b - a);
+      if (d[t].y < 0) {
+        const int pr = row0 + t;
+        if (pr >= c0 && pr < c1 && !(pr >= lo && pr < hi)) cnt += 1;
+      }
+    }
+    const uint8_t cls = cnt == 0 ? RK_TILE_EMPTY : (cnt == kTileQ * kTileK ? RK_TILE_FULL : RK_TILE_PARTIAL);
+    const int64_t t_idx = m.tile_off + (int64_t)qt * m.nkt + kt;
+    P.tile_count[t_idx] = cnt;
+    P.tile_class[t_idx] = cls;
+    pairs += cnt;
+    nnz += cnt > 0;
+    nfull += cls == RK_TILE_FULL;
+    npart += cls == RK_TILE_PARTIAL;
+    nempty += cls == RK_TILE_EMPTY;
+  }
+  atomicAdd(&acc[0], pairs);
+  atomicAdd(&acc[1], nfull);
+  atomicAdd(&acc[2], npart);
+  atomicAdd(&acc[3], nempty);
+  atomicAdd(&nnz_s, nnz);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    P.qt_nnz[g] = nnz_s;
+    atomicAdd(&P.totals->visible_pairs, acc[0]);
+    atomicAdd(&P.totals->full_tiles, acc[1]);
+    atomicAdd(&P.totals->partial_tiles, acc[2]);
+    atomicAdd(&P.totals->empty_tiles, acc[3]);
+  }
+}
+
+// Single block: qtile_ptr = exclusive scan of qt_nnz.
+__global__ __launch_bounds__(1024) void plan_scan_kernel(PlanDev P, int NQ) {
+  __shared__ int smem[32];
+  int carry = 0;
+  for (int base = 0; base < NQ; base += blockDim.x) {
+    const int i = base + threadIdx.x;
+    const int v = i < NQ ? P.qt_nnz[i] : 0;
+    int total;
+    const int ex = block_exclusive_scan(v, smem, &total);
+    if (i < NQ) P.qtile_ptr[i] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) P.qtile_ptr[NQ] = carry;
+}
+
+// One block per q-tile: ascending list of its non-empty k-tiles.
+__global__ __launch_bounds__(256) void plan_csr_kernel(PlanDev P) {
+  __shared__ int smem[32];
+  const int g = blockIdx.x;
+  const ReqMeta m = P.req[P.qt_req[g]];
+  const int qt = g - m.qt_off;
+  const int64_t row = m.tile_off + (int64_t)qt * m.nkt;
+  const int base = P.qtile_ptr[g];
+  int run = 0;
+  for (int k0 = 0; k0 < m.nkt; k0 += blockDim.x) {
+    const int kt = k0 + threadIdx.x;
+    const int flag = kt < m.nkt && P.tile_count[row + kt] > 0;
+    int total;
+    const int ex = block_exclusive_scan(flag, smem, &total);
+    if (flag) {
+      P.ktile_idx[base + run + ex] = kt;
+      P.ktile_cls[base + run + ex] = P.tile_class[row + kt];
+    }
+    run += total;
+  }
+}
+
+// One block per request: q-tiles ordered by non-empty k-tile count,
+// descending, ties by q-tile index (a rank sort).
+__global__ __launch_bounds__(256) void plan_qsort_kernel(PlanDev P) {
+  __shared__ int chunk[1024];
+  const ReqMeta m = P.req[blockIdx.x];
+  const int n = m.nqt;
+  const int* nnz = P.qt_nnz + m.qt_off;
+  for (int a0 = 0; a0 < n; a0 += blockDim.x) {
+    const int a = a0 + threadIdx.x;
+    const int na = a < n ? nnz[a] : 0;
+    int rank = 0;
+    for (int b0 = 0; b0 < n; b0 += 1024) {
+      const int nb = min(1024, n - b0);
+      __syncthreads();
+      for (int t = threadIdx.x; t < nb; t += blockDim.x) chunk[t] = nnz[b0 + t];
+      __syncthreads();
+      if (a < n) {
+        for (int t = 0; t < nb; ++t) {
+          const int v = chunk[t];
+          rank += (v > na) || (v == na && b0 + t < a);
+        }
+      }
+    }
+    if (a < n) P.qorder[m.qt_off + rank] = m.qt_off + a;
+  }
+}
+
+// One thread per launch slot: slot s runs on XCD s % 8 as item s / 8 of
+// that XCD's queue.
+__global__ void plan_sched_kernel(PlanDev P, int64_t slots, int H) {
+  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= slots) return;
+  const int q = (int)(s % kNumXcd);
+  const int idx = (int)(s / kNumXcd);
+  int a = P.queue_start[q], b = P.queue_start[q + 1];
+  int item = -1;
+  if (a < b) {
+    // last group with base <= idx
+    while (b - a > 1) {
+      const int mid = (a + b) >> 1;
+      if (P.groups[mid].base <= idx) a = mid; else b = mid;
+    }
+    const Group grp = P.groups[a];
+    const int k = idx - grp.base;
+    if (k >= 0 && k < grp.count) {
+      const int qg = P.qorder[P.req[grp.req].qt_off + k];
+      item = qg * H + grp.head;
+    }
+  }
+  P.sched[s] = item;
+}
+
+}  // namespace
+
+hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
+  const PlanDev& P = p->dev;
+  if (p->T > 0) {
+    const int blocks = (p->T + 255) / 256;
+    const int check_static = (!(p->flags & RK_STATIC_BIDIRECTIONAL)) && p->delay > 0;
+    hipLaunchKernelGGL(plan_seg_kernel, dim3(blocks), dim3(256), 0, s, P, p->R, p->T,
+                       p->seg_kind_dev, p->timestamps_dev, check_static);
+    hipLaunchKernelGGL(plan_rowdesc_kernel, dim3(blocks), dim3(256), 0, s, P, p->R, p->T,
+                       p->seg_kind_dev, p->timestamps_dev, p->delay, p->window,
+                       (int)((p->flags & RK_STATIC_BIDIRECTIONAL) != 0));
+  }
+  if (p->NQ > 0) {
+    hipLaunchKernelGGL(plan_tile_kernel, dim3((unsigned)p->NQ), dim3(256), 0, s, P);
+  }
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s, P, (int)p->NQ);
+  if (p->NQ > 0) {
+    hipLaunchKernelGGL(plan_csr_kernel, dim3((unsigned)p->NQ), dim3(256), 0, s, P);
+    hipLaunchKernelGGL(plan_qsort_kernel, dim3(p->R), dim3(256), 0, s, P);
+  }
+  if (p->slots > 0) {
+    hipLaunchKernelGGL(plan_sched_kernel, dim3((unsigned)((p->slots + 255) / 256)), dim3(256), 0, s,
+                       P, p->slots, p->H);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rk

@@ -1,0 +1,130 @@
+// Internal declarations shared by the host ABI (api.cpp) and the HIP
+// kernels (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rk.h"
+
+namespace rk {
+
+constexpr int kTileQ = RK_TILE_Q;
+constexpr int kTileK = RK_TILE_K;
+constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr int kMaxHalfD = 64;     // d_head <= 128
+
+// Per-request metadata in the plan workspace.  tok_off .. tile_off are
+// filled on the host; seg[] starts as len on the host and the device
+// records the first position of each segment kind.
+struct ReqMeta {
+  int32_t tok_off;   // first global token
+  int32_t len;       // L_r
+  int32_t qt_off;    // first global q-tile
+  int32_t nqt;       // ceil(L / 128)
+  int32_t nkt;       // ceil(L / 64)
+  int32_t pad0;
+  int64_t tile_off;  // first tile in tile_class / tile_count
+  int32_t seg[4];    // request-local start of PROFILE, HISTORY, REALTIME, CANDIDATE
+};
+static_assert(sizeof(ReqMeta) == 48, "ReqMeta layout");
+
+// (request, head) group of the launch schedule, placed in one XCD queue.
+struct Group {
+  int32_t req;
+  int32_t head;
+  int32_t base;   // first slot index inside its queue
+  int32_t count;  // number of q-tiles (= work items)
+};
+
+// Device words of plan totals; zeroed by the first planner kernel.
+struct PlanTotals {
+  unsigned long long visible_pairs;
+  unsigned long long full_tiles;
+  unsigned long long partial_tiles;
+  unsigned long long empty_tiles;
+  unsigned int errors;  // bit 0: segment order/kind, bit 1: time order
+  unsigned int pad[7];
+};
+
+constexpr unsigned kErrSegment = 1u;
+constexpr unsigned kErrTime = 2u;
+
+// Device pointers of a plan (all inside the caller's workspace).
+struct PlanDev {
+  ReqMeta* req;            // [R]
+  int32_t* qt_req;         // [NQ] request of each global q-tile
+  Group* groups;           // [G] sorted by (queue, base)
+  int32_t* queue_start;    // [kNumXcd + 1] first group of each queue
+  int2* row_desc;          // [T]
+  int32_t* tile_count;     // [NT]
+  uint8_t* tile_class;     // [NT]
+  int32_t* qt_nnz;         // [NQ]
+  int32_t* qtile_ptr;      // [NQ + 1]
+  int32_t* ktile_idx;      // [NT]
+  uint8_t* ktile_cls;      // [NT]
+  int32_t* qorder;         // [NQ]
+  int32_t* sched;          // [slots]
+  PlanTotals* totals;
+};
+
+}  // namespace rk
+
+struct rk_plan {
+  int32_t R, T, H;
+  int64_t NQ, NT, G, slots, max_queue;
+  int64_t delay;
+  int32_t window;
+  uint32_t flags;
+  // batch device arrays (caller-owned)
+  const int32_t* req_offsets_dev;
+  const uint8_t* seg_kind_dev;
+  const int64_t* timestamps_dev;
+  const int64_t* anchors_dev;
+  void* workspace;
+  size_t workspace_bytes;
+  size_t off_req, off_qt_req, off_groups, off_queue_start, off_row_desc, off_tile_count,
+      off_tile_class, off_qt_nnz, off_qtile_ptr, off_ktile_idx, off_ktile_cls, off_qorder,
+      off_sched, off_totals, host_blob_bytes, total_bytes;
+  rk::PlanDev dev;
+  // host copy of the first host_blob_bytes of the workspace (kept alive
+  // for the asynchronous upload)
+  unsigned char* host_blob;
+};
+
+namespace rk {
+
+// RoPE frequency table in revolutions per timestamp unit:
+// w_rev[i] = phi_min / dt_max * base^(2i/d) / (2 pi).
+struct RopeTab {
+  double w_rev[kMaxHalfD];
+};
+
+// ---- launchers (defined in the .hip files); return hipSuccess or an error
+hipError_t launch_plan(const rk_plan* p, hipStream_t s);
+hipError_t launch_rope(int32_t R, int32_t T, const int32_t* req_offsets, const int64_t* ts,
+                       const int64_t* anchors, const RopeTab& tab, const void* x_in, void* x_out,
+                       rk_dtype dt, int H, int d, int64_t in_st, int64_t in_sh, int64_t out_st,
+                       int64_t out_sh, hipStream_t s);
+
+struct AttnLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
+  float scale;
+  int H, d, T;
+  bool rope_q;              // rotate Q while staging (K is already rotated)
+  const int64_t* ts;
+  const int64_t* anchors;
+  RopeTab tab;
+};
+
+hipError_t launch_attn_reference(const rk_plan* p, const AttnLaunch& a, rk_dtype dt,
+                                 hipStream_t s);
+hipError_t launch_attn_mfma_bf16_d64(const rk_plan* p, const AttnLaunch& a, hipStream_t s);
+
+}  // namespace rk

@@ -1,0 +1,89 @@
+// Time RoPE (CADET, "time encoding and self-gating"): pair (2i, 2i+1) of a
+// token at time t in request r turns by alpha_i = (t - anchor_r) * omega_i,
+// omega_i = phi_min / dt_max * base^(2i/d).  The time difference is exact in
+// int64; the phase is formed in revolutions in double precision and reduced
+// to [-1/2, 1/2] before an fp32 sin/cos, so large Unix times lose nothing.
+//
+// HBM-bound elementwise pass: one thread per (token, pair); the angle is
+// computed once and applied to every head.
+#include <hip/hip_bf16.h>
+
+#include "rk_internal.h"
+
+namespace rk {
+namespace {
+
+__device__ __forceinline__ float load_elem(const float* p) { return *p; }
+__device__ __forceinline__ float load_elem(const __hip_bfloat16* p) {
+  return __uint_as_float(((unsigned)(*(const unsigned short*)p)) << 16);
+}
+__device__ __forceinline__ void store_pair(float* p, float a, float b) {
+  *(float2*)p = make_float2(a, b);
+}
+__device__ __forceinline__ unsigned short f2bf(float f) {
+  // round to nearest even (inputs are finite)
+  unsigned u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+__device__ __forceinline__ void store_pair(__hip_bfloat16* p, float a, float b) {
+  *(unsigned*)p = (unsigned)f2bf(a) | ((unsigned)f2bf(b) << 16);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(int R, int Tn, const int32_t* __restrict__ offs,
+                                                   const int64_t* __restrict__ ts,
+                                                   const int64_t* __restrict__ anchors,
+                                                   RopeTab tab, const T* x, T* y, int H, int d,
+                                                   int64_t ist, int64_t ish, int64_t ost,
+                                                   int64_t osh) {
+  __shared__ double w[kMaxHalfD];
+  const int half = d >> 1;
+  if (threadIdx.x < half) w[threadIdx.x] = tab.w_rev[threadIdx.x];
+  __syncthreads();
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)Tn * half) return;
+  const int tok = (int)(gid / half);
+  const int i = (int)(gid - (int64_t)tok * half);
+  // request of the token: last r with offs[r] <= tok
+  int a = 0, b = R;
+  while (a < b) {
+    const int m = (a + b) >> 1;
+    if (offs[m] <= tok) a = m + 1; else b = m;
+  }
+  const int r = a > 0 ? a - 1 : 0;
+  const double rev = (double)(ts[tok] - anchors[r]) * w[i];
+  const float f = (float)(rev - rint(rev));
+  float sn, cs;
+  sincosf(6.283185307179586f * f, &sn, &cs);
+  const T* xp = x + (int64_t)tok * ist + 2 * i;
+  T* yp = y + (int64_t)tok * ost + 2 * i;
+  for (int h = 0; h < H; ++h) {
+    const float x0 = load_elem(xp + (int64_t)h * ish);
+    const float x1 = load_elem(xp + (int64_t)h * ish + 1);
+    store_pair(yp + (int64_t)h * osh, x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope(int32_t R, int32_t T, const int32_t* req_offsets, const int64_t* ts,
+                       const int64_t* anchors, const RopeTab& tab, const void* x_in, void* x_out,
+                       rk_dtype dt, int H, int d, int64_t in_st, int64_t in_sh, int64_t out_st,
+                       int64_t out_sh, hipStream_t s) {
+  const int64_t n = (int64_t)T * (d / 2);
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (dt == RK_F32) {
+    hipLaunchKernelGGL(rope_kernel<float>, dim3(blocks), dim3(256), 0, s, R, T, req_offsets, ts,
+                       anchors, tab, (const float*)x_in, (float*)x_out, H, d, in_st, in_sh, out_st,
+                       out_sh);
+  } else {
+    hipLaunchKernelGGL(rope_kernel<__hip_bfloat16>, dim3(blocks), dim3(256), 0, s, R, T,
+                       req_offsets, ts, anchors, tab, (const __hip_bfloat16*)x_in,
+                       (__hip_bfloat16*)x_out, H, d, in_st, in_sh, out_st, out_sh);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rk

@@ -54,10 +54,14 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     Returns float32 values that are exactly representable in bfloat16.
     Inputs must be finite.
     """
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(x.shape)
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = x.view(np.uint32)
+    # finite values never overflow 32 bits here (largest is 0xFF7FFFFF + 0x8000)
+    lsb = (u >> 16) & 1
+    lsb += 0x7FFF
+    u += lsb
+    u &= 0xFFFF0000
+    return x
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:

@@ -1,0 +1,386 @@
+"""GPU parity: the HIP path through the C ABI against the CPU fp64 oracle.
+
+* Plan: tile classes, exact per-tile visible counts, CSR and totals are
+  bit-exact; row descriptors reproduce each oracle mask row exactly; the
+  launch schedule covers every (query tile, head) once.
+* Time RoPE: rotated Q/K against the oracle rotation by (t - anchor).
+* Attention: fp32 within 1e-4 max-abs; bf16 within 2e-2 max-abs and 1e-2
+  relative L2 against the oracle on the bf16-rounded inputs.  Small batches
+  (several tiles, ragged tails, every mask mode) are compared in full; the
+  five named workloads at full size, in the launch configuration the
+  benchmark times, are compared on sampled rows.
+"""
+
+import math
+import os
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from rk_workloads import (CANDIDATE, HISTORY, NOW, PROFILE, REALTIME, make_config,  # noqa: E402
+                          make_custom, random_layout)
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+BF16_MAX_ABS = 2e-2
+BF16_REL_L2 = 1e-2
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def rk():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import masked_attention_amd as m
+    from masked_attention_amd import _rk
+    _rk.lib()  # fails loudly if librk.so is missing
+    return m
+
+
+def _rope(wl):
+    return dict(phi_min=wl.phi_min, dt_max=wl.dt_max, base=wl.base)
+
+
+def _tensors(wl):
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(wl.q).to("cuda").to(dt)
+    k = torch.from_numpy(wl.k).to("cuda").to(dt)
+    v = torch.from_numpy(wl.v).to("cuda").to(dt)
+    return q, k, v
+
+
+def _plan(rk, wl, batch=None):
+    batch = batch or rk.Batch.from_workload(wl)
+    plan = rk.Plan(batch, delay=wl.delay, window=wl.window,
+                   static_bidirectional=wl.static_bidirectional, num_heads=wl.heads)
+    return batch, plan
+
+
+def _run(rk, wl, rope=True, reference=False, want_lse=True):
+    _say(f"[gpu] {wl.name}: T={wl.total_tokens} H={wl.heads} d={wl.d_head} {wl.dtype} "
+         f"rope={rope} reference={reference}")
+    batch, plan = _plan(rk, wl)
+    q, k, v = _tensors(wl)
+    o, lse = rk.rk_masked_attn_fwd(plan, q, k, v, rope=_rope(wl) if rope else None,
+                                   reference=reference, want_lse=want_lse)
+    torch.cuda.synchronize()
+    o_np = o.float().cpu().numpy().astype(np.float64)
+    lse_np = lse.cpu().numpy().astype(np.float64) if lse is not None else None
+    return plan, o_np, lse_np
+
+
+def _oracle_full(wl, rope=True):
+    return oracle.attention_forward(wl.req_offsets, wl.seg_kind, wl.timestamps,
+                                    wl.q.astype(np.float64), wl.k.astype(np.float64),
+                                    wl.v.astype(np.float64), delay=wl.delay, window=wl.window,
+                                    static_bidirectional=wl.static_bidirectional,
+                                    rope=_rope(wl) if rope else None)
+
+
+def _check(wl, o, ref, lse=None, ref_lse=None):
+    err = np.abs(o - ref)
+    if wl.dtype == "f32":
+        assert err.max() <= F32_TOL, f"max abs {err.max()}"
+    else:
+        rel = np.linalg.norm(o - ref) / max(np.linalg.norm(ref), 1e-30)
+        assert err.max() <= BF16_MAX_ABS, f"max abs {err.max()}"
+        assert rel <= BF16_REL_L2, f"rel L2 {rel}"
+    if lse is not None:
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isfinite(lse), fin)
+        assert np.all(np.isneginf(lse[~fin]))
+        tol = 1e-4 if wl.dtype == "f32" else 2e-2
+        if fin.any():
+            assert np.abs(lse[fin] - ref_lse[fin]).max() <= tol
+
+
+# ---------------------------------------------------------------------------
+# plan
+# ---------------------------------------------------------------------------
+
+def _check_plan(wl, plan, ref, check_rows=True):
+    torch.cuda.synchronize()
+    st = plan.stats()
+    assert st["device_errors"] == 0
+    tc = plan.tile_class().cpu().numpy()
+    cnt = plan.tile_count().cpu().numpy()
+    assert np.array_equal(tc, ref["tile_class"])
+    assert np.array_equal(cnt.astype(np.int64), ref["tile_count"])
+    assert np.array_equal(plan.qtile_ptr().cpu().numpy().astype(np.int64), ref["qtile_ptr"])
+    assert np.array_equal(plan.ktile_idx().cpu().numpy().astype(np.int64), ref["ktile_idx"])
+    assert st["visible_pairs"] == ref["visible_pairs"]
+    assert st["full_tiles"] == int((ref["tile_class"] == oracle.FULL).sum())
+    assert st["partial_tiles"] == int((ref["tile_class"] == oracle.PARTIAL).sum())
+    assert st["empty_tiles"] == int((ref["tile_class"] == oracle.EMPTY).sum())
+    # schedule: every (q-tile, head) exactly once, the rest -1
+    sched = plan.sched().cpu().numpy()
+    items = sched[sched >= 0]
+    NQ = plan.num_qtiles
+    assert np.array_equal(np.sort(items), np.arange(NQ * wl.heads))
+    if check_rows:
+        rd = plan.row_desc().cpu().numpy()
+        for r in range(wl.num_requests):
+            a, b = wl.request(r)
+            if b == a:
+                continue
+            vis = oracle.visibility(wl.seg_kind[a:b], wl.timestamps[a:b], delay=wl.delay,
+                                    window=wl.window, static_bidirectional=wl.static_bidirectional)
+            lo = rd[a:b, 0]
+            hi = rd[a:b, 1] & 0x7FFFFFFF
+            self_ = rd[a:b, 1] < 0
+            cols = np.arange(b - a)[None, :]
+            rows = np.arange(b - a)[:, None]
+            mine = ((cols >= lo[:, None]) & (cols < hi[:, None])) | (self_[:, None] & (cols == rows))
+            assert np.array_equal(mine, vis), f"request {r}"
+
+
+LAYOUT_CASES = [
+    # (name, requests builder, delay, window, bidir)
+    ("causal-ragged", lambda rng: [[(HISTORY, np.sort(rng.integers(NOW - 10**7, NOW, 300)))],
+                                   [(HISTORY, np.sort(rng.integers(NOW - 10**7, NOW, 129)))],
+                                   [(HISTORY, np.sort(rng.integers(NOW - 10**7, NOW, 1)))]], 0, 0, False),
+    ("delay-ties", lambda rng: [[(HISTORY, np.sort(rng.integers(NOW - 20000, NOW, 400)))]], 3600, 0, False),
+    ("window-cands", lambda rng: [[(HISTORY, np.sort(rng.integers(NOW - 10**7, NOW - 60, 333))),
+                                   (CANDIDATE, np.full(70, NOW))]], 0, 37, False),
+    ("window-delay", lambda rng: [[(HISTORY, np.sort(rng.integers(NOW - 10**6, NOW - 60, 260))),
+                                   (CANDIDATE, np.full(5, NOW))]], 1800, 100, False),
+    ("mtgr-small", lambda rng: [[(PROFILE, np.full(5, NOW)),
+                                 (HISTORY, np.sort(rng.integers(NOW - 10**7, NOW - 86400, 140))),
+                                 (REALTIME, np.sort(rng.integers(NOW - 86400, NOW, 30))),
+                                 (CANDIDATE, rng.integers(NOW - 86400, NOW, 21))]], 0, 0, True),
+    ("empty-and-tiny", lambda rng: [[], [(CANDIDATE, np.full(3, NOW))], [],
+                                    [(HISTORY, np.array([NOW - 5])), (CANDIDATE, np.array([NOW]))],
+                                    [(HISTORY, np.sort(rng.integers(NOW - 10**5, NOW, 128)))]], 0, 0, False),
+]
+
+
+@pytest.mark.parametrize("case", LAYOUT_CASES, ids=[c[0] for c in LAYOUT_CASES])
+def test_plan_bit_exact_small(rk, case):
+    name, build, delay, window, bidir = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    wl = make_custom(build(rng), heads=3, d_head=64, dtype="bf16", delay=delay, window=window,
+                     static_bidirectional=bidir, with_qkv=False, name=name)
+    _say(f"[gpu] plan {name}")
+    batch, plan = _plan(rk, wl)
+    ref = oracle.tile_plan(wl.req_offsets, wl.seg_kind, wl.timestamps, delay=delay,
+                           window=window, static_bidirectional=bidir)
+    _check_plan(wl, plan, ref)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_plan_bit_exact_random(rk, seed):
+    rng = np.random.default_rng(100 + seed)
+    reqs = random_layout(rng, 7, 700)
+    for bidir, delay, window in ((True, 0, 0), (False, 3600, 0), (False, 0, 50), (False, 7200, 200)):
+        wl = make_custom(reqs, heads=2, d_head=64, dtype="bf16", delay=delay, window=window,
+                         static_bidirectional=bidir, with_qkv=False)
+        _say(f"[gpu] plan random seed={seed} bidir={bidir} delay={delay} window={window}")
+        batch, plan = _plan(rk, wl)
+        ref = oracle.tile_plan(wl.req_offsets, wl.seg_kind, wl.timestamps, delay=delay,
+                               window=window, static_bidirectional=bidir)
+        _check_plan(wl, plan, ref)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_plan_bit_exact_workloads(rk, cfg):
+    wl = make_config(cfg, with_qkv=False)
+    _say(f"[gpu] plan workload {cfg}")
+    batch, plan = _plan(rk, wl)
+    ref = oracle.tile_plan(wl.req_offsets, wl.seg_kind, wl.timestamps, delay=wl.delay,
+                           window=wl.window, static_bidirectional=wl.static_bidirectional)
+    _check_plan(wl, plan, ref, check_rows=cfg in (1, 2))
+
+
+def test_plan_bit_exact_tm20k(rk):
+    """Delta = 0: the mask depends on positions only, so every request of the
+    long-sequence workload has request 0's tiles."""
+    wl = make_config(5, with_qkv=False)
+    _say("[gpu] plan workload 5")
+    batch, plan = _plan(rk, wl)
+    a, b = wl.request(0)
+    cnt, cls = oracle.tile_plan_request(wl.seg_kind[a:b], wl.timestamps[a:b], delay=0, window=0,
+                                        static_bidirectional=False)
+    torch.cuda.synchronize()
+    st = plan.stats()
+    assert st["visible_pairs"] == 8 * 200_030_001
+    n = cnt.size
+    gc = plan.tile_count().cpu().numpy().reshape(8, n)
+    gk = plan.tile_class().cpu().numpy().reshape(8, n)
+    for r in range(8):
+        assert np.array_equal(gc[r].astype(np.int64), cnt.ravel())
+        assert np.array_equal(gk[r], cls.ravel())
+    ptr = plan.qtile_ptr().cpu().numpy()
+    idx = plan.ktile_idx().cpu().numpy()
+    for g in range(0, plan.num_qtiles, 13):
+        qt = g % cnt.shape[0]
+        assert np.array_equal(idx[ptr[g]:ptr[g + 1]], np.nonzero(cnt[qt])[0])
+
+
+def test_plan_device_checks(rk):
+    """Out-of-order segments and unsorted real-time times are reported."""
+    ts = np.array([NOW - 10, NOW - 5, NOW - 7, NOW], np.int64)
+    bad_kind = make_custom([[(HISTORY, ts[:2]), (REALTIME, ts[2:3]), (HISTORY, ts[3:])]], heads=1,
+                           d_head=64, with_qkv=False)
+    batch, plan = _plan(rk, bad_kind)
+    assert plan.stats(raise_on_error=False)["status"] == 2
+    bad_time = make_custom([[(REALTIME, np.array([NOW - 1, NOW - 3])),
+                             (CANDIDATE, np.array([NOW]))]], heads=1, d_head=64, with_qkv=False)
+    batch, plan = _plan(rk, bad_time)
+    assert plan.stats(raise_on_error=False)["status"] == 3
+    ok = make_custom([[(HISTORY, np.array([NOW - 1, NOW - 3]))]], heads=1, d_head=64,
+                     with_qkv=False)  # unsorted history with delay 0 is allowed
+    batch, plan = _plan(rk, ok)
+    assert plan.stats()["status"] == 0
+
+
+# ---------------------------------------------------------------------------
+# time RoPE
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 64), ("f32", 128)])
+def test_time_rope_matches_oracle(rk, dtype, d):
+    wl = make_config(1) if dtype == "f32" and d == 32 else make_custom(
+        random_layout(np.random.default_rng(5), 4, 300), heads=3, d_head=d, dtype=dtype, seed=4)
+    _say(f"[gpu] rope {dtype} d={d}")
+    batch = rk.Batch.from_workload(wl)
+    q, k, v = _tensors(wl)
+    out = rk.rk_time_rope(batch, k, **_rope(wl))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    rel_t = (wl.timestamps - np.repeat(wl.anchors, np.diff(wl.req_offsets))).astype(np.float64)
+    ref = oracle.time_rope(wl.k.astype(np.float64), rel_t, **_rope(wl))
+    if dtype == "f32":
+        assert np.abs(got - ref).max() <= 2e-6
+    else:
+        # one bf16 rounding of the rotated value
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0**-8 + 1e-6)
+    # in place gives the same result
+    k2 = k.clone()
+    rk.rk_time_rope(batch, k2, out=k2, **_rope(wl))
+    torch.cuda.synchronize()
+    assert torch.equal(k2, out)
+
+
+# ---------------------------------------------------------------------------
+# attention: small batches compared in full
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", LAYOUT_CASES, ids=[c[0] for c in LAYOUT_CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attention_small_full(rk, case, dtype):
+    name, build, delay, window, bidir = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    wl = make_custom(build(rng), heads=2, d_head=64, dtype=dtype, delay=delay, window=window,
+                     static_bidirectional=bidir, seed=17, name=name)
+    plan, o, lse = _run(rk, wl)
+    ref, ref_lse = _oracle_full(wl)
+    _check(wl, o, ref, lse, ref_lse)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_attention_random_layouts(rk, seed, d):
+    rng = np.random.default_rng(200 + seed)
+    reqs = random_layout(rng, 5, 520)
+    for dtype in ("bf16", "f32"):
+        for bidir, delay, window in ((True, 0, 0), (False, 3600, 0), (False, 0, 90)):
+            wl = make_custom(reqs, heads=2, d_head=d, dtype=dtype, delay=delay, window=window,
+                             static_bidirectional=bidir, seed=seed)
+            plan, o, lse = _run(rk, wl)
+            ref, ref_lse = _oracle_full(wl)
+            _check(wl, o, ref, lse, ref_lse)
+
+
+def test_attention_without_rope(rk):
+    wl = make_custom(random_layout(np.random.default_rng(9), 3, 400), heads=2, d_head=64,
+                     dtype="bf16", seed=9, delay=600)
+    plan, o, lse = _run(rk, wl, rope=False)
+    ref, ref_lse = _oracle_full(wl, rope=False)
+    _check(wl, o, ref, lse, ref_lse)
+
+
+def test_mfma_and_reference_kernels_agree(rk):
+    wl = make_custom(random_layout(np.random.default_rng(10), 4, 600), heads=2, d_head=64,
+                     dtype="bf16", seed=10, window=77)
+    _, o1, l1 = _run(rk, wl)
+    _, o2, l2 = _run(rk, wl, reference=True)
+    ref, ref_lse = _oracle_full(wl)
+    _check(wl, o1, ref, l1, ref_lse)
+    _check(wl, o2, ref, l2, ref_lse)
+
+
+def test_deterministic(rk):
+    wl = make_config(2)
+    _, o1, _ = _run(rk, wl, want_lse=False)
+    _, o2, _ = _run(rk, wl, want_lse=False)
+    assert np.array_equal(o1, o2)
+
+
+def test_strided_inputs(rk):
+    """Q, K, V as views of one packed [T, 3, H, d] buffer."""
+    wl = make_custom(random_layout(np.random.default_rng(11), 3, 300), heads=2, d_head=64,
+                     dtype="bf16", seed=11, delay=3600)
+    batch, plan = _plan(rk, wl)
+    qkv = torch.from_numpy(np.stack([wl.q, wl.k, wl.v], axis=1)).to("cuda").to(torch.bfloat16)
+    q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    o, lse = rk.rk_masked_attn_fwd(plan, q, k, v, rope=_rope(wl), want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = _oracle_full(wl)
+    _check(wl, o.float().cpu().numpy().astype(np.float64), ref,
+           lse.cpu().numpy().astype(np.float64), ref_lse)
+
+
+# ---------------------------------------------------------------------------
+# attention: the five workloads at full size, sampled rows
+# ---------------------------------------------------------------------------
+
+def _sample_tokens(wl, rng, n_random=48):
+    toks = set()
+    for r in range(wl.num_requests):
+        a, b = wl.request(r)
+        if b == a:
+            continue
+        for p in (0, 1, 63, 64, 127, 128, 129, b - a - 2, b - a - 1):
+            if 0 <= p < b - a:
+                toks.add(a + p)
+        cand = np.nonzero(wl.seg_kind[a:b] == CANDIDATE)[0]
+        if cand.size:
+            toks.update((a + cand[[0, -1]]).tolist())
+        if len(toks) > 400:
+            break
+    toks.update(rng.integers(0, wl.total_tokens, size=n_random).tolist())
+    return np.array(sorted(toks), np.int64)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_attention_workloads_sampled(rk, cfg):
+    wl = make_config(cfg)
+    plan, o, lse = _run(rk, wl)
+    if cfg == 1:
+        ref, ref_lse = _oracle_full(wl)
+        _check(wl, o, ref, lse, ref_lse)
+        return
+    rng = np.random.default_rng(cfg)
+    toks = _sample_tokens(wl, rng)
+    for h in range(wl.heads):
+        ref, ref_lse = oracle.attention_rows(wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q,
+                                             wl.k, wl.v, toks, h, delay=wl.delay,
+                                             window=wl.window,
+                                             static_bidirectional=wl.static_bidirectional,
+                                             rope=_rope(wl))
+        _check(wl, o[toks, h], ref, lse[h, toks], ref_lse)
+    # fully masked rows (delay rule) are exactly zero
+    if wl.delay > 0:
+        for r in range(wl.num_requests):
+            a = wl.request(r)[0]
+            assert np.all(o[a] == 0.0) and np.all(np.isneginf(lse[:, a]))
