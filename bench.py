@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the masked-attention forward hot path on one MI355X.
+
+One step = the whole path over one batch already resident in HBM:
+  rk_mask_plan        (tile plan + launch schedule)
+  rk_time_rope        (K rotated by time RoPE)
+  rk_masked_attn_fwd  (Q rotated while staged; masked flash attention)
+The default workload is the TM20K-shaped batch (8 users x (20000 history +
+1 target), causal, H = 8, d_head = 64, bf16, time RoPE).
+
+Prints ONE JSON line.  `value` is the effective attention throughput of the
+whole step: 4 * d_head * heads * (visible pairs) / step time.  The roofline
+object is for the dominant kernel (the attention kernel), timed with HIP
+events on the stream it runs on.  The CPU baseline times the fp64 oracle on a
+bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "masked-attn fwd effective TFLOP/s (visible pairs) + % bf16 MFMA peak; candidates/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "masked_attention_amd", "csrc", "attn_mfma.hip")
+ATTN_KERNEL = "attn_mfma_bf16_d64_kernel"
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5, help="named workload 1..5 (default 5)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4,
+                    help="oracle sample: request 0 with this many heads")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def _traffic_from_profile(workload: str):
+    """HBM bytes per attention launch from the committed PMC summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if kv.get("attn_source_sha256") != sha:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _cpu_baseline(wl, n_heads: int):
+    """Time the fp64 oracle, as it stands, on request 0 and heads 0..n_heads-1."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        cores = max(int(i.get("num_threads", 1)) for i in info) if info else 1
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    a, b = wl.request(0)
+    pairs = oracle.count_visible(wl.seg_kind[a:b], wl.timestamps[a:b], delay=wl.delay,
+                                 window=wl.window, static_bidirectional=wl.static_bidirectional)
+    heads = list(range(min(n_heads, wl.heads)))
+    rope = dict(phi_min=wl.phi_min, dt_max=wl.dt_max, base=wl.base)
+    t0 = time.perf_counter()
+    oracle.attention_forward(wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q, wl.k, wl.v,
+                             delay=wl.delay, window=wl.window,
+                             static_bidirectional=wl.static_bidirectional, rope=rope,
+                             heads=heads, requests=[0])
+    dt = time.perf_counter() - t0
+    flops = 4.0 * wl.d_head * pairs * len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"request 0 ({b - a} tokens, {pairs} visible pairs per head), heads "
+                      f"0-{len(heads) - 1}, fp64 NumPy with explicit mask, {dt:.2f} s wall"}
+
+
+def main() -> int:
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the masked-attention path is built and "
+              "measured on a single MI355X (requests and heads shard across GPUs without "
+              "communication; see the design notes). Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import masked_attention_amd as rk
+    from masked_attention_amd import _rk
+    from rk_workloads import make_config
+
+    lib = _rk.lib()
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    wl = make_config(args.config)
+    H, d = wl.heads, wl.d_head
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    batch = rk.Batch.from_workload(wl, device=dev)
+    q, k, v = (torch.from_numpy(x).to(dev).to(tdt) for x in (wl.q, wl.k, wl.v))
+    krot = torch.empty_like(k)
+    o = torch.empty_like(q)
+    rope = dict(phi_min=wl.phi_min, dt_max=wl.dt_max, base=wl.base)
+    ws = torch.empty(rk.rk_plan_workspace_size(batch, H), dtype=torch.uint8, device=dev)
+    ref_plan = rk.Plan(batch, delay=wl.delay, window=wl.window,
+                       static_bidirectional=wl.static_bidirectional, num_heads=H, workspace=ws)
+    stats = ref_plan.stats()
+    pairs = stats["visible_pairs"]
+    flops = 4.0 * d * H * pairs
+
+    # raw C arguments, built once
+    mp = _rk.sized(_rk.rk_mask_params, delay=wl.delay, window=wl.window,
+                   flags=_rk.RK_STATIC_BIDIRECTIONAL if wl.static_bidirectional else 0)
+    rp = rk.binding.rope_params(**rope)
+    stream = torch.cuda.current_stream()
+    sp = C.c_void_p(stream.cuda_stream)
+    dcode = _rk.RK_BF16 if wl.dtype == "bf16" else _rk.RK_F32
+    attn = _rk.sized(_rk.rk_attn_args, flags=_rk.RK_ATTN_K_PREROTATED, dtype=dcode, num_heads=H,
+                     d_head=d, q=q.data_ptr(), k=krot.data_ptr(), v=v.data_ptr(), o=o.data_ptr(),
+                     q_stride_tok=H * d, q_stride_head=d, k_stride_tok=H * d, k_stride_head=d,
+                     v_stride_tok=H * d, v_stride_head=d, o_stride_tok=H * d, o_stride_head=d,
+                     scale=0.0)
+    attn.rope = C.cast(C.pointer(rp), C.c_void_p)
+    handles = []
+
+    def step(ev=None):
+        h = C.c_void_p()
+        if ev: ev[0].record(stream)
+        _rk.check(lib.rk_mask_plan(C.byref(batch.c), C.byref(mp), H, C.c_void_p(ws.data_ptr()),
+                                   C.c_size_t(ws.numel()), C.byref(h), sp), "rk_mask_plan")
+        if ev: ev[1].record(stream)
+        _rk.check(lib.rk_time_rope(C.byref(batch.c), C.byref(rp), C.c_void_p(k.data_ptr()),
+                                   C.c_void_p(krot.data_ptr()), dcode, H, d, H * d, d, H * d, d,
+                                   sp), "rk_time_rope")
+        if ev: ev[2].record(stream)
+        _rk.check(lib.rk_masked_attn_fwd(h, C.byref(attn), sp), "rk_masked_attn_fwd")
+        if ev: ev[3].record(stream)
+        handles.append(h)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for h in handles:
+        lib.rk_plan_destroy(h)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    plan_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    rope_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    T = wl.total_tokens
+    esz = 2 if wl.dtype == "bf16" else 4
+    attn_alg_bytes = T * H * 4 * d * esz + T * 8            # Q, K, V read + O written, times
+    rope_alg_bytes = T * H * 2 * d * esz + T * 8 + wl.num_requests * 8
+    nt = int(ref_plan.info.num_tiles)
+    nnz_tiles = int(ref_plan.qtile_ptr()[-1].item()) if ref_plan.num_qtiles else 0
+    # kind + time read, row descriptor written, class + count per tile, CSR index + class
+    plan_alg_bytes = T * 9 + T * 8 + nt * 5 + nnz_tiles * 5
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    traffic = _traffic_from_profile(wl.name)
+    n_cand = wl.n_candidates
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded generator with the workload's shapes and time law)",
+        "config": {"workload": wl.name, "requests": wl.num_requests, "tokens": T, "heads": H,
+                   "d_head": d, "visible_pairs_per_head": pairs, "candidates": n_cand,
+                   "delay_s": wl.delay, "window": wl.window,
+                   "static_bidirectional": wl.static_bidirectional},
+        "pct_bf16_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "candidates_per_s": round(n_cand / (ms_step * 1e-3), 1) if n_cand else None,
+        "stage_ms": {"plan": round(plan_ms, 4), "rope_k": round(rope_ms, 4),
+                     "attention": round(attn_ms, 4)},
+        "stage_hbm_gbs": {"plan": round(plan_alg_bytes / (plan_ms * 1e-3) / 1e9, 1),
+                          "rope_k": round(rope_alg_bytes / (rope_ms * 1e-3) / 1e9, 1)},
+        "tiles": {"full": stats["full_tiles"], "partial": stats["partial_tiles"],
+                  "empty": stats["empty_tiles"]},
+        "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "alg_bytes": attn_alg_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(wl, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

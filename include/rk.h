@@ -101,6 +101,8 @@ enum { RK_TILE_EMPTY = 0, RK_TILE_PARTIAL = 1, RK_TILE_FULL = 2 };
 
 /* rk_attn_args.flags */
 #define RK_ATTN_REFERENCE_KERNEL 0x1u /* force the plain (non-MFMA) kernel */
+#define RK_ATTN_K_PREROTATED 0x2u     /* with rope: K was already rotated by rk_time_rope
+                                         (same parameters and anchors); only Q is rotated */
 
 /*
  * A packed batch (CADET, "how to score hundreds of candidates": all tokens
@@ -197,7 +199,8 @@ typedef struct rk_plan_totals {
  *   rope      : NULL = inputs are used as given; otherwise Q and K are
  *               rotated by time RoPE with the plan's batch timestamps and
  *               anchors (Q while it is staged, K by a pass into the
- *               workspace).
+ *               workspace, or not at all with RK_ATTN_K_PREROTATED, e.g.
+ *               for a cache of rotated history keys).
  *   workspace : device memory of at least rk_attn_workspace_size bytes,
  *               256-byte aligned (may be NULL when that size is 0).
  * O must not overlap Q, K, V or the workspace.

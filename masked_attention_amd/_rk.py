@@ -28,6 +28,7 @@ RK_TILE_EMPTY, RK_TILE_PARTIAL, RK_TILE_FULL = 0, 1, 2
 RK_TILE_Q, RK_TILE_K = 128, 64
 RK_STATIC_BIDIRECTIONAL = 0x1
 RK_ATTN_REFERENCE_KERNEL = 0x1
+RK_ATTN_K_PREROTATED = 0x2
 RK_ABI_VERSION = 1
 
 

@@ -165,11 +165,14 @@ def rk_time_rope(batch: Batch, x: torch.Tensor, *, phi_min: float, dt_max: float
     return out
 
 
-def _attn_args(plan: Plan, q, k, v, o, lse, scale, rope, reference, workspace):
+def _attn_args(plan: Plan, q, k, v, o, lse, scale, rope, reference, workspace,
+               k_prerotated=False):
     for t in (q, k, v, o):
         if t.dim() != 3 or t.stride(2) != 1:
             raise ValueError("q, k, v, o must be [T, H, d] with d contiguous")
-    a = sized(_rk.rk_attn_args, flags=_rk.RK_ATTN_REFERENCE_KERNEL if reference else 0,
+    flags = (_rk.RK_ATTN_REFERENCE_KERNEL if reference else 0) | (
+        _rk.RK_ATTN_K_PREROTATED if k_prerotated else 0)
+    a = sized(_rk.rk_attn_args, flags=flags,
               dtype=_dtype_code(q), num_heads=q.shape[1], d_head=q.shape[2],
               q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), o=o.data_ptr(),
               lse=lse.data_ptr() if lse is not None else None,
@@ -186,10 +189,11 @@ def _attn_args(plan: Plan, q, k, v, o, lse, scale, rope, reference, workspace):
     return a
 
 
-def rk_attn_workspace_size(plan: Plan, q, k, v, *, rope=None, reference=False) -> int:
+def rk_attn_workspace_size(plan: Plan, q, k, v, *, rope=None, reference=False,
+                           k_prerotated=False) -> int:
     o = q  # only shapes/strides are read
     rp = rope_params(**rope) if rope is not None else None
-    a = _attn_args(plan, q, k, v, o, None, 0.0, rp, reference, None)
+    a = _attn_args(plan, q, k, v, o, None, 0.0, rp, reference, None, k_prerotated)
     n = C.c_size_t()
     check(lib().rk_attn_workspace_size(plan.handle, C.byref(a), C.byref(n)), "rk_attn_workspace_size")
     return int(n.value)
@@ -199,18 +203,20 @@ def rk_masked_attn_fwd(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Te
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                        want_lse: bool = False, scale: float = 0.0, rope: Optional[dict] = None,
                        reference: bool = False, workspace: Optional[torch.Tensor] = None,
+                       k_prerotated: bool = False,
                        stream: Optional[torch.cuda.Stream] = None):
     """Masked attention forward over `plan`.  Returns (o, lse or None).
 
     rope: None, or dict(phi_min=..., dt_max=..., base=...) to rotate Q and K
-    by time RoPE with the plan's timestamps and anchors.
+    by time RoPE with the plan's timestamps and anchors.  k_prerotated:
+    K already holds rk_time_rope's output; only Q is rotated.
     """
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None and want_lse:
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
     rp = rope_params(**rope) if rope is not None else None
-    a = _attn_args(plan, q, k, v, out, lse, scale, rp, reference, workspace)
+    a = _attn_args(plan, q, k, v, out, lse, scale, rp, reference, workspace, k_prerotated)
     n = C.c_size_t()
     check(lib().rk_attn_workspace_size(plan.handle, C.byref(a), C.byref(n)), "rk_attn_workspace_size")
     if n.value and workspace is None:

@@ -365,7 +365,8 @@ rk_status check_attn(const rk_plan* p, const rk_attn_args* a) {
   if (a->dtype != RK_F32 && a->dtype != RK_BF16) return RK_ERR_INVALID_ARG;
   if (a->num_heads != p->H) return RK_ERR_INVALID_ARG;
   if (a->d_head != 32 && a->d_head != 64 && a->d_head != 128) return RK_ERR_UNSUPPORTED;
-  if (a->flags & ~RK_ATTN_REFERENCE_KERNEL) return RK_ERR_INVALID_ARG;
+  if (a->flags & ~(RK_ATTN_REFERENCE_KERNEL | RK_ATTN_K_PREROTATED)) return RK_ERR_INVALID_ARG;
+  if ((a->flags & RK_ATTN_K_PREROTATED) && !a->rope) return RK_ERR_INVALID_ARG;
   if (p->T > 0 && (!a->q || !a->k || !a->v || !a->o)) return RK_ERR_INVALID_ARG;
   const int64_t st[8] = {a->q_stride_tok, a->q_stride_head, a->k_stride_tok, a->k_stride_head,
                          a->v_stride_tok, a->v_stride_head, a->o_stride_tok, a->o_stride_head};
@@ -395,7 +396,7 @@ bool mfma_aligned(const rk_attn_args* a, bool k_in_workspace) {
 }
 
 size_t attn_ws_bytes(const rk_plan* p, const rk_attn_args* a) {
-  if (!a->rope) return 0;
+  if (!a->rope || (a->flags & RK_ATTN_K_PREROTATED)) return 0;
   return align_up((size_t)p->T * (size_t)a->num_heads * (size_t)a->d_head * elem_size(a->dtype));
 }
 
@@ -418,7 +419,8 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
     if (a->workspace_bytes < need) return RK_ERR_WORKSPACE_TOO_SMALL;
   }
   const bool use_mfma = mfma_eligible(a);
-  if (use_mfma && !mfma_aligned(a, a->rope != nullptr)) return RK_ERR_UNSUPPORTED;
+  const bool k_rotate = a->rope && !(a->flags & RK_ATTN_K_PREROTATED);
+  if (use_mfma && !mfma_aligned(a, k_rotate)) return RK_ERR_UNSUPPORTED;
 
   rk::AttnLaunch L;
   std::memset(&L, 0, sizeof(L));
@@ -445,6 +447,8 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
   if (a->rope) {
     L.tab = make_tab(a->rope, a->d_head);
     L.rope_q = true;
+  }
+  if (k_rotate) {
     // K is rotated once into the workspace ([T, H, d] dense); Q is rotated
     // by the attention kernel while it is staged.
     const int64_t hd = (int64_t)a->num_heads * a->d_head;

@@ -384,3 +384,17 @@ def test_attention_workloads_sampled(rk, cfg):
         for r in range(wl.num_requests):
             a = wl.request(r)[0]
             assert np.all(o[a] == 0.0) and np.all(np.isneginf(lse[:, a]))
+
+
+def test_prerotated_k_matches_fused_path(rk):
+    """rk_time_rope on K followed by the attention with RK_ATTN_K_PREROTATED
+    gives the same bits as the attention rotating K itself."""
+    wl = make_custom(random_layout(np.random.default_rng(12), 3, 500), heads=2, d_head=64,
+                     dtype="bf16", seed=12, delay=3600)
+    batch, plan = _plan(rk, wl)
+    q, k, v = _tensors(wl)
+    o1, _ = rk.rk_masked_attn_fwd(plan, q, k, v, rope=_rope(wl))
+    krot = rk.rk_time_rope(batch, k, **_rope(wl))
+    o2, _ = rk.rk_masked_attn_fwd(plan, q, krot, v, rope=_rope(wl), k_prerotated=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
