@@ -34,7 +34,8 @@ struct Layout {
   std::vector<int32_t> queue_start; // kNumXcd + 1
   size_t off_req = 0, off_qt_req = 0, off_groups = 0, off_queue_start = 0, off_totals = 0,
          host_blob = 0, off_row_desc = 0, off_tile_count = 0, off_tile_class = 0, off_qt_nnz = 0,
-         off_qtile_ptr = 0, off_ktile_idx = 0, off_ktile_cls = 0, off_qorder = 0, off_sched = 0,
+         off_qt_pairs = 0, off_qt_full = 0,
+         off_qtile_ptr = 0, off_ktile_idx = 0, off_ktile_word = 0, off_qorder = 0, off_sched = 0,
          total = 0;
 };
 
@@ -152,9 +153,11 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->off_tile_count = take(sizeof(int32_t) * (size_t)nt);
   L->off_tile_class = take((size_t)nt);
   L->off_qt_nnz = take(sizeof(int32_t) * (size_t)nq);
+  L->off_qt_pairs = take(sizeof(int64_t) * (size_t)nq);
+  L->off_qt_full = take(sizeof(int32_t) * (size_t)nq);
   L->off_qtile_ptr = take(sizeof(int32_t) * (size_t)(nq + 1));
   L->off_ktile_idx = take(sizeof(int32_t) * (size_t)nt);
-  L->off_ktile_cls = take((size_t)nt);
+  L->off_ktile_word = take(sizeof(int32_t) * (size_t)nt);
   L->off_qorder = take(sizeof(int32_t) * (size_t)nq);
   L->off_sched = take(sizeof(int32_t) * (size_t)L->slots);
   L->total = off;
@@ -247,9 +250,11 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   p->off_tile_count = L.off_tile_count;
   p->off_tile_class = L.off_tile_class;
   p->off_qt_nnz = L.off_qt_nnz;
+  p->off_qt_pairs = L.off_qt_pairs;
+  p->off_qt_full = L.off_qt_full;
   p->off_qtile_ptr = L.off_qtile_ptr;
   p->off_ktile_idx = L.off_ktile_idx;
-  p->off_ktile_cls = L.off_ktile_cls;
+  p->off_ktile_word = L.off_ktile_word;
   p->off_qorder = L.off_qorder;
   p->off_sched = L.off_sched;
   p->off_totals = L.off_totals;
@@ -267,9 +272,11 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   D.tile_count = (int32_t*)(ws + L.off_tile_count);
   D.tile_class = (uint8_t*)(ws + L.off_tile_class);
   D.qt_nnz = (int32_t*)(ws + L.off_qt_nnz);
+  D.qt_pairs = (int64_t*)(ws + L.off_qt_pairs);
+  D.qt_full = (int32_t*)(ws + L.off_qt_full);
   D.qtile_ptr = (int32_t*)(ws + L.off_qtile_ptr);
   D.ktile_idx = (int32_t*)(ws + L.off_ktile_idx);
-  D.ktile_cls = (uint8_t*)(ws + L.off_ktile_cls);
+  D.ktile_word = (int32_t*)(ws + L.off_ktile_word);
   D.qorder = (int32_t*)(ws + L.off_qorder);
   D.sched = (int32_t*)(ws + L.off_sched);
 

@@ -7,7 +7,8 @@
 //
 // Per 64-key tile and wave:
 //   S^T (64 keys x 32 queries) = K_tile (64 x 64) * Q_w^T   8 x mfma 32x32x16 bf16
-//   online softmax in fp32 (exp2 with log2(e) folded into the scale)
+//   online softmax in fp32 (exp2 with log2(e) folded into the scale; the
+//   running max is only moved, and O rescaled, when it grows by > 2^8)
 //   O^T (64 d x 32 queries) += V_tile^T * P^T               8 x mfma 32x32x16 bf16
 // Computing the transposed products puts one query per lane (lane % 32) in
 // both accumulators, so the row max needs one exchange with lane ^ 32 and
@@ -43,23 +44,27 @@ constexpr int KS = 72;  // K row stride (elements)
 constexpr int VS = 68;  // V^T row stride (elements)
 constexpr int KBUF = kTileK * KS;
 constexpr int VBUF = D * VS;
+constexpr float kRescaleLog2 = 8.f;
 
 struct PlanView {
   const ReqMeta* req;
   const int32_t* qt_req;
   const int2* row_desc;
   const int32_t* qtile_ptr;
-  const int32_t* ktile_idx;
-  const uint8_t* ktile_cls;
+  const int32_t* ktile_word;
   const int32_t* sched;
 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even)
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-  // round to nearest even
-  unsigned ua = __float_as_uint(a), ub = __float_as_uint(b);
-  ua += 0x7fffu + ((ua >> 16) & 1u);
-  ub += 0x7fffu + ((ub >> 16) & 1u);
-  return (ua >> 16) | (ub & 0xffff0000u);
+  bf16x2_t r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  unsigned u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
 }
 
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
@@ -104,10 +109,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_bf16_d64_kernel(PlanView P, 
   bf16x8 qb[4];
   {
     const unsigned short* Qp = (const unsigned short*)A.q + (int64_t)tokq * A.q_st + (int64_t)head * A.q_sh;
-    float phase_dt = 0.f;
     double dtd = 0.0;
     if (A.rope_q && rvalid) dtd = (double)(A.ts[tokq] - A.anchors[req]);
-    (void)phase_dt;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint4 raw = make_uint4(0, 0, 0, 0);
@@ -146,14 +149,31 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_bf16_d64_kernel(PlanView P, 
   const unsigned short* Kb = (const unsigned short*)A.k + (int64_t)m.tok_off * A.k_st + (int64_t)head * A.k_sh;
   const unsigned short* Vb = (const unsigned short*)A.v + (int64_t)m.tok_off * A.v_st + (int64_t)head * A.v_sh;
 
+  // per-thread element offsets inside a key tile (loop invariant)
+  const int64_t ko0 = (int64_t)kk * A.k_st + 8 * kpart;
+  const int64_t ko1 = (int64_t)(kk + 32) * A.k_st + 8 * kpart;
+  const int64_t vo0 = (int64_t)(2 * vp) * A.v_st + 8 * vpart;
+  const int64_t vo1 = (int64_t)(2 * vp + 1) * A.v_st + 8 * vpart;
   uint4 rk0, rk1, rv0, rv1;
+  // Loads are unconditional so the compiler can count them: rows past the
+  // end of the request (ragged last tile only) re-read the last row, whose
+  // finite values meet a -inf score (that tile is always PARTIAL) and P = 0.
   auto gload = [&](int kt) {
-    const int c = kt * kTileK + kk;
-    rk0 = c < L ? *(const uint4*)(Kb + (int64_t)c * A.k_st + 8 * kpart) : make_uint4(0, 0, 0, 0);
-    rk1 = c + 32 < L ? *(const uint4*)(Kb + (int64_t)(c + 32) * A.k_st + 8 * kpart) : make_uint4(0, 0, 0, 0);
-    const int cv = kt * kTileK + 2 * vp;
-    rv0 = cv < L ? *(const uint4*)(Vb + (int64_t)cv * A.v_st + 8 * vpart) : make_uint4(0, 0, 0, 0);
-    rv1 = cv + 1 < L ? *(const uint4*)(Vb + (int64_t)(cv + 1) * A.v_st + 8 * vpart) : make_uint4(0, 0, 0, 0);
+    const int c0 = kt * kTileK;
+    const unsigned short* kb = Kb + (int64_t)c0 * A.k_st;
+    const unsigned short* vb = Vb + (int64_t)c0 * A.v_st;
+    if (c0 + kTileK <= L) {
+      rk0 = *(const uint4*)(kb + ko0);
+      rk1 = *(const uint4*)(kb + ko1);
+      rv0 = *(const uint4*)(vb + vo0);
+      rv1 = *(const uint4*)(vb + vo1);
+    } else {
+      const int last = L - 1 - c0;
+      rk0 = *(const uint4*)(kb + (int64_t)min(kk, last) * A.k_st + 8 * kpart);
+      rk1 = *(const uint4*)(kb + (int64_t)min(kk + 32, last) * A.k_st + 8 * kpart);
+      rv0 = *(const uint4*)(vb + (int64_t)min(2 * vp, last) * A.v_st + 8 * vpart);
+      rv1 = *(const uint4*)(vb + (int64_t)min(2 * vp + 1, last) * A.v_st + 8 * vpart);
+    }
   };
   auto lstore = [&](int buf) {
     *(uint4*)&Ks[buf * KBUF + kk * KS + 8 * kpart] = rk0;
@@ -173,22 +193,34 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_bf16_d64_kernel(PlanView P, 
   f32x16 o0, o1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) { o0[r] = 0.f; o1[r] = 0.f; }
-  float mrow = -INFINITY, lsum = 0.f;
+  float mref = -INFINITY, lsum = 0.f;
   const float sl2 = A.scale * 1.4426950408889634f;
+  const float thr = kRescaleLog2 / sl2;  // in raw score units
 
   const int e0 = P.qtile_ptr[qg];
   const int n = P.qtile_ptr[qg + 1] - e0;
+  // CSR words are software-pipelined two tiles ahead and the prefetch is
+  // unconditional (the last iteration re-reads its own tile into the idle
+  // buffer), so the loop body has no data-dependent branches around loads.
+  int kw_cur = 0, kw_nxt = 0;
   if (n > 0) {
-    gload(P.ktile_idx[e0]);
+    kw_cur = P.ktile_word[e0];
+    kw_nxt = P.ktile_word[e0 + min(1, n - 1)];
+    gload(kw_cur & 0x7fffffff);
     lstore(0);
   }
+  // Everything loaded before the loop (Q fragment, row descriptor) is
+  // complete here, so inside the loop only the next tile's prefetch is
+  // outstanding when the MFMAs start.
+  asm volatile("s_waitcnt vmcnt(0)");
   __syncthreads();
 
   for (int it = 0; it < n; ++it) {
     const int buf = it & 1;
-    const int kt = P.ktile_idx[e0 + it];
-    const bool partial = P.ktile_cls[e0 + it] == RK_TILE_PARTIAL;
-    if (it + 1 < n) gload(P.ktile_idx[e0 + it + 1]);
+    const int kt = kw_cur & 0x7fffffff;
+    const bool partial = kw_cur < 0;
+    gload(kw_nxt & 0x7fffffff);
+    const int kw_nn = P.ktile_word[e0 + min(it + 2, n - 1)];
 
     // S^T = K Q^T
     f32x16 s0, s1;
@@ -220,10 +252,19 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_bf16_d64_kernel(PlanView P, 
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(mrow, mx);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f((mrow - muse) * sl2);
-    const float nb = -muse * sl2;
+    // Lazy rescale: the reference max m_ref only moves when a row's max
+    // exceeds it by more than kRescaleLog2 (in log2 units), so P <= 2^8.
+    // The decision is made for the whole wave at once.
+    const float mnew = fmaxf(mref, mx);
+    const bool grow = mnew > mref + thr;
+    if (__any(grow)) {
+      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((mref - mnew) * sl2);
+      lsum *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { o0[r] *= alpha; o1[r] *= alpha; }
+      mref = mnew;
+    }
+    const float nb = mref == -INFINITY ? 0.f : -mref * sl2;
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -231,10 +272,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_bf16_d64_kernel(PlanView P, 
       s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], sl2, nb));
       psum += s0[r] + s1[r];
     }
-    lsum = lsum * alpha + psum;
-    mrow = mnew;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { o0[r] *= alpha; o1[r] *= alpha; }
+    lsum += psum;
 
     // P^T as B operands: step s takes accumulator block s/2, registers
     // 8 (s%2) .. 8 (s%2) + 7
@@ -271,8 +309,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_bf16_d64_kernel(PlanView P, 
       }
     }
 
-    if (it + 1 < n) lstore(buf ^ 1);
+    lstore(buf ^ 1);
     __syncthreads();
+    kw_cur = kw_nxt;
+    kw_nxt = kw_nn;
   }
 
   // ---- epilogue: O = O^T / l, lanes of both halves hold distinct d values
@@ -289,15 +329,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_bf16_d64_kernel(PlanView P, 
                                         pack_bf16x2(o1[4 * g + 2] * inv, o1[4 * g + 3] * inv));
   }
   if (A.lse && hh == 0)
-    A.lse[(int64_t)head * A.T + tokq] = ltot > 0.f ? mrow * A.scale + logf(ltot) : -INFINITY;
+    A.lse[(int64_t)head * A.T + tokq] = ltot > 0.f ? mref * A.scale + logf(ltot) : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_attn_mfma_bf16_d64(const rk_plan* p, const AttnLaunch& a, hipStream_t s) {
   if (p->slots == 0) return hipSuccess;
-  PlanView P{p->dev.req, p->dev.qt_req, p->dev.row_desc, p->dev.qtile_ptr, p->dev.ktile_idx,
-             p->dev.ktile_cls, p->dev.sched};
+  PlanView P{p->dev.req, p->dev.qt_req, p->dev.row_desc, p->dev.qtile_ptr, p->dev.ktile_word,
+             p->dev.sched};
   hipLaunchKernelGGL(attn_mfma_bf16_d64_kernel, dim3((unsigned)p->slots), dim3(256), 0, s, P, a);
   return hipGetLastError();
 }

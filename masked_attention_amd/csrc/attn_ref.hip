@@ -33,8 +33,7 @@ struct PlanView {
   const int32_t* qt_req;
   const int2* row_desc;
   const int32_t* qtile_ptr;
-  const int32_t* ktile_idx;
-  const uint8_t* ktile_cls;
+  const int32_t* ktile_word;
   const int32_t* sched;
 };
 
@@ -91,8 +90,9 @@ __global__ __launch_bounds__(128) void attn_ref_kernel(PlanView P, AttnLaunch A)
 
   const int e0 = P.qtile_ptr[qg], e1 = P.qtile_ptr[qg + 1];
   for (int e = e0; e < e1; ++e) {
-    const int kt = P.ktile_idx[e];
-    const bool partial = P.ktile_cls[e] == RK_TILE_PARTIAL;
+    const int kw = P.ktile_word[e];
+    const int kt = kw & 0x7fffffff;
+    const bool partial = kw < 0;
     __syncthreads();
     for (int x = t; x < kTileK * D; x += blockDim.x) {
       const int j = x / D, c = x - j * D;
@@ -143,8 +143,8 @@ __global__ __launch_bounds__(128) void attn_ref_kernel(PlanView P, AttnLaunch A)
 
 template <typename T, int D>
 hipError_t launch_ref(const rk_plan* p, const AttnLaunch& a, hipStream_t s) {
-  PlanView P{p->dev.req, p->dev.qt_req, p->dev.row_desc, p->dev.qtile_ptr, p->dev.ktile_idx,
-             p->dev.ktile_cls, p->dev.sched};
+  PlanView P{p->dev.req, p->dev.qt_req, p->dev.row_desc, p->dev.qtile_ptr, p->dev.ktile_word,
+             p->dev.sched};
   hipLaunchKernelGGL((attn_ref_kernel<T, D>), dim3((unsigned)p->slots), dim3(128), 0, s, P, a);
   return hipGetLastError();
 }

@@ -141,11 +141,11 @@ __global__ void plan_rowdesc_kernel(PlanDev P, int R, int T, const uint8_t* __re
 }
 
 // One block per global q-tile: exact visible count and class of each of its
-// k-tiles, and the number of non-empty k-tiles.
+// k-tiles, and the q-tile's partial totals (non-empty, FULL, pairs).
 __global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
   __shared__ int2 d[kTileQ];
-  __shared__ unsigned long long acc[4];
-  __shared__ int nnz_s;
+  __shared__ unsigned long long pairs_s;
+  __shared__ int nnz_s, full_s;
   const int g = blockIdx.x;
   const int r = P.qt_req[g];
   const ReqMeta m = P.req[r];
@@ -154,11 +154,10 @@ __global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
   const int nrows = min(kTileQ, m.len - row0);
   if (threadIdx.x < kTileQ)
     d[threadIdx.x] = threadIdx.x < nrows ? P.row_desc[m.tok_off + row0 + threadIdx.x] : make_int2(0, 0);
-  if (threadIdx.x < 4) acc[threadIdx.x] = 0;
-  if (threadIdx.x == 0) nnz_s = 0;
+  if (threadIdx.x == 0) { pairs_s = 0; nnz_s = 0; full_s = 0; }
   __syncthreads();
-  unsigned long long pairs = 0, nfull = 0, npart = 0, nempty = 0;
-  int nnz = 0;
+  unsigned long long pairs = 0;
+  int nnz = 0, nfull = 0;
   for (int kt = threadIdx.x; kt < m.nkt; kt += blockDim.x) {
     const int c0 = kt * kTileK;
     const int c1 = min(m.len, c0 + kTileK);
@@ -180,37 +179,50 @@ __global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
     pairs += cnt;
     nnz += cnt > 0;
     nfull += cls == RK_TILE_FULL;
-    npart += cls == RK_TILE_PARTIAL;
-    nempty += cls == RK_TILE_EMPTY;
   }
-  atomicAdd(&acc[0], pairs);
-  atomicAdd(&acc[1], nfull);
-  atomicAdd(&acc[2], npart);
-  atomicAdd(&acc[3], nempty);
+  // block sums through LDS atomics (integers: order does not matter)
+  atomicAdd(&pairs_s, pairs);
   atomicAdd(&nnz_s, nnz);
+  atomicAdd(&full_s, nfull);
   __syncthreads();
   if (threadIdx.x == 0) {
     P.qt_nnz[g] = nnz_s;
-    atomicAdd(&P.totals->visible_pairs, acc[0]);
-    atomicAdd(&P.totals->full_tiles, acc[1]);
-    atomicAdd(&P.totals->partial_tiles, acc[2]);
-    atomicAdd(&P.totals->empty_tiles, acc[3]);
+    P.qt_full[g] = full_s;
+    P.qt_pairs[g] = (int64_t)pairs_s;
   }
 }
 
-// Single block: qtile_ptr = exclusive scan of qt_nnz.
-__global__ __launch_bounds__(1024) void plan_scan_kernel(PlanDev P, int NQ) {
+// Single block: qtile_ptr = exclusive scan of qt_nnz; plan totals from the
+// per-q-tile partial sums.
+__global__ __launch_bounds__(1024) void plan_scan_kernel(PlanDev P, int NQ, int64_t NT) {
   __shared__ int smem[32];
+  __shared__ unsigned long long tot[2];
+  if (threadIdx.x < 2) tot[threadIdx.x] = 0;
+  __syncthreads();
   int carry = 0;
+  unsigned long long pairs = 0, nfull = 0;
   for (int base = 0; base < NQ; base += blockDim.x) {
     const int i = base + threadIdx.x;
     const int v = i < NQ ? P.qt_nnz[i] : 0;
+    if (i < NQ) {
+      pairs += (unsigned long long)P.qt_pairs[i];
+      nfull += (unsigned long long)P.qt_full[i];
+    }
     int total;
     const int ex = block_exclusive_scan(v, smem, &total);
     if (i < NQ) P.qtile_ptr[i] = carry + ex;
     carry += total;
   }
-  if (threadIdx.x == 0) P.qtile_ptr[NQ] = carry;
+  atomicAdd(&tot[0], pairs);
+  atomicAdd(&tot[1], nfull);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    P.qtile_ptr[NQ] = carry;
+    P.totals->visible_pairs = tot[0];
+    P.totals->full_tiles = tot[1];
+    P.totals->partial_tiles = (unsigned long long)carry - tot[1];
+    P.totals->empty_tiles = (unsigned long long)NT - (unsigned long long)carry;
+  }
 }
 
 // One block per q-tile: ascending list of its non-empty k-tiles.
@@ -229,7 +241,8 @@ __global__ __launch_bounds__(256) void plan_csr_kernel(PlanDev P) {
     const int ex = block_exclusive_scan(flag, smem, &total);
     if (flag) {
       P.ktile_idx[base + run + ex] = kt;
-      P.ktile_cls[base + run + ex] = P.tile_class[row + kt];
+      P.ktile_word[base + run + ex] =
+          (int)((unsigned)kt | ((unsigned)(P.tile_class[row + kt] == RK_TILE_PARTIAL) << 31));
     }
     run += total;
   }
@@ -303,7 +316,7 @@ hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
   if (p->NQ > 0) {
     hipLaunchKernelGGL(plan_tile_kernel, dim3((unsigned)p->NQ), dim3(256), 0, s, P);
   }
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s, P, (int)p->NQ);
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s, P, (int)p->NQ, p->NT);
   if (p->NQ > 0) {
     hipLaunchKernelGGL(plan_csr_kernel, dim3((unsigned)p->NQ), dim3(256), 0, s, P);
     hipLaunchKernelGGL(plan_qsort_kernel, dim3(p->R), dim3(256), 0, s, P);

@@ -38,7 +38,9 @@ struct Group {
   int32_t count;  // number of q-tiles (= work items)
 };
 
-// Device words of plan totals; zeroed by the first planner kernel.
+// Device words of plan totals: errors are OR-ed in by the segment kernel
+// (starts at zero from the host upload); the counts are written by the
+// scan kernel from per-q-tile partial sums.
 struct PlanTotals {
   unsigned long long visible_pairs;
   unsigned long long full_tiles;
@@ -60,10 +62,12 @@ struct PlanDev {
   int2* row_desc;          // [T]
   int32_t* tile_count;     // [NT]
   uint8_t* tile_class;     // [NT]
-  int32_t* qt_nnz;         // [NQ]
+  int32_t* qt_nnz;         // [NQ] non-empty k-tiles of each q-tile
+  int64_t* qt_pairs;       // [NQ] visible pairs of each q-tile
+  int32_t* qt_full;        // [NQ] FULL k-tiles of each q-tile
   int32_t* qtile_ptr;      // [NQ + 1]
   int32_t* ktile_idx;      // [NT]
-  uint8_t* ktile_cls;      // [NT]
+  int32_t* ktile_word;     // [NT] CSR entry for the kernels: kt | (PARTIAL << 31)
   int32_t* qorder;         // [NQ]
   int32_t* sched;          // [slots]
   PlanTotals* totals;
@@ -85,7 +89,7 @@ struct rk_plan {
   void* workspace;
   size_t workspace_bytes;
   size_t off_req, off_qt_req, off_groups, off_queue_start, off_row_desc, off_tile_count,
-      off_tile_class, off_qt_nnz, off_qtile_ptr, off_ktile_idx, off_ktile_cls, off_qorder,
+      off_tile_class, off_qt_nnz, off_qt_pairs, off_qt_full, off_qtile_ptr, off_ktile_idx, off_ktile_word, off_qorder,
       off_sched, off_totals, host_blob_bytes, total_bytes;
   rk::PlanDev dev;
   // host copy of the first host_blob_bytes of the workspace (kept alive

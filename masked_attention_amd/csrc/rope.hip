@@ -4,8 +4,9 @@
 // int64; the phase is formed in revolutions in double precision and reduced
 // to [-1/2, 1/2] before an fp32 sin/cos, so large Unix times lose nothing.
 //
-// HBM-bound elementwise pass: one thread per (token, pair); the angle is
-// computed once and applied to every head.
+// HBM-bound elementwise pass: the angle of a (token, pair) is computed once
+// and applied to every head.  Aligned rows with d % 8 == 0 take the 16-byte
+// vector form; anything else the one-pair-per-thread form.
 #include <hip/hip_bf16.h>
 
 #include "rk_internal.h"
@@ -65,14 +66,100 @@ __global__ __launch_bounds__(256) void rope_kernel(int R, int Tn, const int32_t*
   }
 }
 
+// Vector form for d % 8 == 0 with 16-byte aligned rows: one thread per
+// (token, group of four pairs); 16-byte (bf16) or 2 x 16-byte (fp32)
+// accesses per head.
+template <typename T>
+__global__ __launch_bounds__(256) void rope8_kernel(int R, int Tn, const int32_t* __restrict__ offs,
+                                                    const int64_t* __restrict__ ts,
+                                                    const int64_t* __restrict__ anchors,
+                                                    RopeTab tab, const T* x, T* y, int H, int d,
+                                                    int64_t ist, int64_t ish, int64_t ost,
+                                                    int64_t osh) {
+  __shared__ double w[kMaxHalfD];
+  const int half = d >> 1;
+  if (threadIdx.x < half) w[threadIdx.x] = tab.w_rev[threadIdx.x];
+  __syncthreads();
+  const int groups = d >> 3;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)Tn * groups) return;
+  const int tok = (int)(gid / groups);
+  const int g = (int)(gid - (int64_t)tok * groups);
+  int a = 0, b = R;
+  while (a < b) {
+    const int m = (a + b) >> 1;
+    if (offs[m] <= tok) a = m + 1; else b = m;
+  }
+  const int r = a > 0 ? a - 1 : 0;
+  const double dt = (double)(ts[tok] - anchors[r]);
+  float sn[4], cs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double rev = dt * w[4 * g + j];
+    const float f = (float)(rev - rint(rev));
+    sincosf(6.283185307179586f * f, &sn[j], &cs[j]);
+  }
+  const T* xp = x + (int64_t)tok * ist + 8 * g;
+  T* yp = y + (int64_t)tok * ost + 8 * g;
+  for (int h = 0; h < H; ++h) {
+    float v[8];
+    if constexpr (sizeof(T) == 2) {
+      const uint4 raw = *(const uint4*)(xp + (int64_t)h * ish);
+      const unsigned u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(u[j] << 16);
+        v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+      }
+    } else {
+      const float4 p0 = *(const float4*)(xp + (int64_t)h * ish);
+      const float4 p1 = *(const float4*)(xp + (int64_t)h * ish + 4);
+      v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+      v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+    }
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[2 * j] = v[2 * j] * cs[j] - v[2 * j + 1] * sn[j];
+      o[2 * j + 1] = v[2 * j] * sn[j] + v[2 * j + 1] * cs[j];
+    }
+    if constexpr (sizeof(T) == 2) {
+      unsigned u[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        u[j] = (unsigned)f2bf(o[2 * j]) | ((unsigned)f2bf(o[2 * j + 1]) << 16);
+      *(uint4*)(yp + (int64_t)h * osh) = make_uint4(u[0], u[1], u[2], u[3]);
+    } else {
+      *(float4*)(yp + (int64_t)h * osh) = make_float4(o[0], o[1], o[2], o[3]);
+      *(float4*)(yp + (int64_t)h * osh + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rope(int32_t R, int32_t T, const int32_t* req_offsets, const int64_t* ts,
                        const int64_t* anchors, const RopeTab& tab, const void* x_in, void* x_out,
                        rk_dtype dt, int H, int d, int64_t in_st, int64_t in_sh, int64_t out_st,
                        int64_t out_sh, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int64_t v = 16 / (dt == RK_F32 ? 4 : 2);  // elements per 16 bytes
+  const bool vec = (d % 8 == 0) && ((uintptr_t)x_in % 16 == 0) && ((uintptr_t)x_out % 16 == 0) &&
+                   in_st % v == 0 && in_sh % v == 0 && out_st % v == 0 && out_sh % v == 0;
+  if (vec) {
+    const int64_t n = (int64_t)T * (d / 8);
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (dt == RK_F32)
+      hipLaunchKernelGGL(rope8_kernel<float>, dim3(blocks), dim3(256), 0, s, R, T, req_offsets, ts,
+                         anchors, tab, (const float*)x_in, (float*)x_out, H, d, in_st, in_sh,
+                         out_st, out_sh);
+    else
+      hipLaunchKernelGGL(rope8_kernel<__hip_bfloat16>, dim3(blocks), dim3(256), 0, s, R, T,
+                         req_offsets, ts, anchors, tab, (const __hip_bfloat16*)x_in,
+                         (__hip_bfloat16*)x_out, H, d, in_st, in_sh, out_st, out_sh);
+    return hipGetLastError();
+  }
   const int64_t n = (int64_t)T * (d / 2);
-  if (n == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (dt == RK_F32) {
     hipLaunchKernelGGL(rope_kernel<float>, dim3(blocks), dim3(256), 0, s, R, T, req_offsets, ts,
