@@ -394,7 +394,9 @@ bool mfma_eligible(const rk_attn_args* a) {
 
 bool mfma_aligned(const rk_attn_args* a, bool k_in_workspace) {
   auto al = [](const void* ptr) { return ((uintptr_t)ptr % 16) == 0; };
-  auto st = [](int64_t x) { return (x % 8) == 0; };
+  // strides multiples of 8 elements (16-byte rows) and small enough that a
+  // key tile's per-thread byte offsets fit in 32 bits
+  auto st = [](int64_t x) { return (x % 8) == 0 && x <= (int64_t(1) << 24); };
   bool ok = al(a->q) && al(a->v) && al(a->o) && st(a->q_stride_tok) && st(a->q_stride_head) &&
             st(a->v_stride_tok) && st(a->v_stride_head) && st(a->o_stride_tok) &&
             st(a->o_stride_head);

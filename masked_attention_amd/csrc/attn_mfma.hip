@@ -40,10 +40,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int D = 64;
-constexpr int KS = 72;  // K row stride (elements)
-constexpr int VS = 68;  // V^T row stride (elements)
-constexpr int KBUF = kTileK * KS;
-constexpr int VBUF = D * VS;
+constexpr int TILE_ELEMS = kTileK * D;  // 64 rows x 64 bf16 = 8 KB per K or V tile
 constexpr float kRescaleLog2 = 8.f;
 
 struct PlanView {
@@ -76,20 +73,219 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
-// V^T physical word of (row d, logical word w): XOR 8 on rows with bit 4 set.
-__device__ __forceinline__ int vt_word(int d, int w) { return w ^ (((d >> 4) & 1) << 3); }
 
-__global__ __launch_bounds__(256, 2) void attn_mfma_bf16_d64_kernel(PlanView P, AttnLaunch A) {
-  __shared__ __attribute__((aligned(16))) unsigned short Ks[2 * KBUF];
-  __shared__ __attribute__((aligned(16))) unsigned short Vt[2 * VBUF];
+template <typename T>
+__device__ __forceinline__ T ldc(const T* p, int64_t i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+#else
+  return p[i];  // host pass of the single-source compile; never executed
+#endif
+}
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// LDS tiles hold 64 rows of 128 bytes (eight 16-byte slots), unpadded.
+// Logical 16-byte chunk c of row r sits in slot c ^ kswz(r) for K and
+// c ^ vswz(r) for V, so that
+//  - the ds_read_b128 of 8 consecutive K rows at one chunk hits 8 distinct
+//    slots, and
+//  - a ds_read_b64_tr_b16 group (4 consecutive V rows starting at a
+//    multiple of 4, 32 contiguous bytes each) covers all 32 banks once.
+__device__ __forceinline__ int kswz(int r) { return r & 7; }
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
+
+// Q fragment: lane holds Q[row][16 s + 8 hh .. +7], s = 0..3, rotated by
+// time RoPE when asked (fp32 math, hardware sin/cos on a phase reduced to
+// [-1/2, 1/2] revolution), packed to bf16.
+__device__ __forceinline__ void load_q(bf16x8 (&qb)[4], const AttnLaunch& A, const double* wtab,
+                                       int tokq, bool valid, int head, int req, int hh) {
+  const unsigned short* Qp = (const unsigned short*)A.q + (int64_t)tokq * A.q_st + (int64_t)head * A.q_sh;
+  double dtd = 0.0;
+  if (A.rope_q && valid) dtd = (double)(A.ts[tokq] - A.anchors[req]);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (valid) raw = *(const uint4*)(Qp + 16 * s + 8 * hh);
+    if (A.rope_q) {
+      unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 8 * s + 4 * hh + j;  // pair index
+        const double rev = dtd * wtab[i];
+        const float f = (float)(rev - rint(rev));
+        const float sn = __builtin_amdgcn_sinf(f);
+        const float cs = __builtin_amdgcn_cosf(f);
+        const float x0 = bf_lo(w[j]), x1 = bf_hi(w[j]);
+        w[j] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+      }
+      raw = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    qb[s] = as_bf16x8(raw);
+  }
+}
+
+// Per-lane source offsets of the direct global -> LDS copies.  A wave's
+// global_load_lds of 16 bytes per lane fills 1 KB of LDS contiguously
+// (lane l at byte 16 l): 8 rows.  Wave w issues copies j = 0, 1 for rows
+// 8 (2 w + j) .. +7 of both the K and the V tile.
+struct CopyMap {
+  int row[2];        // tile row written by this lane in copy j
+  unsigned kcol[2];  // byte offset of its source chunk inside a K row
+  unsigned vcol[2];  // same for V
+};
+
+__device__ __forceinline__ CopyMap copy_map(int wv, int lane) {
+  CopyMap c;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = (2 * wv + j) * 64 + lane;
+    const int r = q >> 3, slot = q & 7;
+    c.row[j] = r;
+    c.kcol[j] = 16u * (unsigned)(slot ^ kswz(r));
+    c.vcol[j] = 16u * (unsigned)(slot ^ vswz(r));
+  }
+  return c;
+}
+
+// Issue the copies of key tile kt into LDS buffers kd / vd.  Rows past the
+// end of the request (ragged last tile only) re-read the last row: finite
+// values that meet a -inf score (that tile is always PARTIAL), so P = 0.
+__device__ __forceinline__ void tile_copy(unsigned short* kd, unsigned short* vd, const CopyMap& c,
+                                          const char* Kb, const char* Vb, int64_t k_st_b,
+                                          int64_t v_st_b, unsigned kst_b, unsigned vst_b, int kt,
+                                          int L, int wv) {
+  const int c0 = kt * kTileK;
+  const int last = (c0 + kTileK > L) ? L - 1 - c0 : kTileK - 1;
+  const char* kb = Kb + (int64_t)c0 * k_st_b;
+  const char* vb = Vb + (int64_t)c0 * v_st_b;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const unsigned r = (unsigned)min(c.row[j], last);
+    __builtin_amdgcn_global_load_lds((const void*)(kb + r * kst_b + c.kcol[j]),
+                                     LDS_PTR(void, kd + (2 * wv + j) * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(vb + r * vst_b + c.vcol[j]),
+                                     LDS_PTR(void, vd + (2 * wv + j) * 512), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void mask_tile(f32x16& s0, f32x16& s1, int kt, int hh, int lo, int hi,
+                                          int self, int row) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = kt * kTileK + 8 * (r >> 2) + 4 * hh + (r & 3);
+    const bool v0 = (key >= lo && key < hi) || (self && key == row);
+    const bool v1 = (key + 32 >= lo && key + 32 < hi) || (self && key + 32 == row);
+    if (!v0) s0[r] = -INFINITY;
+    if (!v1) s1[r] = -INFINITY;
+  }
+}
+
+// One 64-key tile for one wave (32 queries): S^T = K Q^T, mask, online
+// softmax, O^T += V^T P^T.  kb / vb are the tile's LDS buffers.
+__device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, float& mref, float& lsum,
+                                          const unsigned short* kb, const unsigned short* vb,
+                                          const bf16x8 (&q)[4], int kt, bool partial, int li,
+                                          int hh, int lo, int hi, int self, int row, float sl2,
+                                          float thr) {
+  f32x16 s0, s1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int cc = 2 * s + hh;  // logical chunk: d = 16 s + 8 hh .. +7
+    const bf16x8 k0 = as_bf16x8(*(const uint4*)&kb[li * 64 + 8 * (cc ^ kswz(li))]);
+    const bf16x8 k1 = as_bf16x8(*(const uint4*)&kb[(32 + li) * 64 + 8 * (cc ^ kswz(32 + li))]);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[s], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s1, 0, 0, 0);
+  }
+  if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
+
+  float mx = s0[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  // Lazy rescale: the reference max only moves when a row's max exceeds it
+  // by more than kRescaleLog2 (log2 units), so P <= 2^8; the decision is
+  // taken for the whole wave.
+  const float mnew = fmaxf(mref, mx);
+  if (__any(mnew > mref + thr)) {
+    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((mref - mnew) * sl2);
+    lsum *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { o0[r] *= alpha; o1[r] *= alpha; }
+    mref = mnew;
+  }
+  const float nb = mref == -INFINITY ? 0.f : -mref * sl2;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, nb));
+    s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], sl2, nb));
+  }
+  // P^T as B operands (step s: accumulator block s/2, registers 8 (s%2)..+7);
+  // the row sum takes the same rounded bf16 values (v_dot2 with (1, 1)).
+  bf16x8 pb[4];
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const f32x16& src = (s < 2) ? s0 : s1;
+    const int r0 = 8 * (s & 1);
+    bf16x2_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j][0] = (__bf16)src[r0 + 2 * j];
+      w[j][1] = (__bf16)src[r0 + 2 * j + 1];
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(w[j], ones, lsum, false);
+    }
+    __builtin_memcpy(&pb[s], w, 16);
+  }
+
+  // V^T fragments by transposing reads: in each 16-lane group g, lane i
+  // points at V[k + (i >> 2)][d0 + 4 (i & 3)] and receives V[k..k+3][d0 + i].
+  const int g = (li >> 4) + 2 * hh;  // 16-lane group of this lane
+  const int i = li & 15;
+  const int rr = i >> 2;             // row offset inside the 4-row group
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int d0 = 32 * mb + 16 * (g & 1);
+      const int col = d0 + 4 * (i & 3);
+      const int ka = 16 * s + 4 * hh + rr;      // keys for e = 0..3
+      const int kb2 = ka + 8;                   // keys for e = 4..7
+      const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          LDS_PTR(v4i16, &vb[ka * 64 + 8 * ((col >> 3) ^ vswz(ka)) + (col & 7)]));
+      const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          LDS_PTR(v4i16, &vb[kb2 * 64 + 8 * ((col >> 3) ^ vswz(kb2)) + (col & 7)]));
+      bf16x8 va;
+      __builtin_memcpy(&va, &lo4, 8);
+      __builtin_memcpy((char*)&va + 8, &hi4, 8);
+      if (mb == 0)
+        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], o0, 0, 0, 0);
+      else
+        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], o1, 0, 0, 0);
+    }
+  }
+}
+
+constexpr int kThreads = 256;  // 4 waves, 32 query rows each
+
+__global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanView P, AttnLaunch A) {
+  // Two stages of K and V tiles as separate objects, so the compiler can
+  // tell the buffer being filled from the one being read.
+  __shared__ __attribute__((aligned(1024))) unsigned short K0[TILE_ELEMS], K1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) unsigned short V0[TILE_ELEMS], V1[TILE_ELEMS];
   __shared__ double wtab[D / 2];
 
-  const int item = P.sched[blockIdx.x];
+  const int item = ldc(P.sched, blockIdx.x);
   if (item < 0) return;
   const int qg = item / A.H;
   const int head = item - qg * A.H;
-  const int req = P.qt_req[qg];
-  const ReqMeta m = P.req[req];
+  const int req = ldc(P.qt_req, qg);
+  const ReqMeta m = ldc(P.req, req);
   const int qt = qg - m.qt_off;
   const int L = m.len;
 
@@ -105,34 +301,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_bf16_d64_kernel(PlanView P, 
   if (A.rope_q && tid < D / 2) wtab[tid] = A.tab.w_rev[tid];
   __syncthreads();
 
-  // ---- Q fragment: lane holds Q[row][16 s + 8 hh .. +7] for s = 0..3
-  bf16x8 qb[4];
-  {
-    const unsigned short* Qp = (const unsigned short*)A.q + (int64_t)tokq * A.q_st + (int64_t)head * A.q_sh;
-    double dtd = 0.0;
-    if (A.rope_q && rvalid) dtd = (double)(A.ts[tokq] - A.anchors[req]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (rvalid) raw = *(const uint4*)(Qp + 16 * s + 8 * hh);
-      if (A.rope_q) {
-        unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 8 * s + 4 * hh + j;  // pair index
-          const double rev = dtd * wtab[i];
-          const float f = (float)(rev - rint(rev));
-          const float sn = __builtin_amdgcn_sinf(f);
-          const float cs = __builtin_amdgcn_cosf(f);
-          const float x0 = bf_lo(w[j]), x1 = bf_hi(w[j]);
-          w[j] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
-        }
-        raw = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-      qb[s] = as_bf16x8(raw);
-    }
-  }
-
+  bf16x8 q[4];
+  load_q(q, A, wtab, tokq, rvalid, head, req, hh);
   int lo = 0, hi = 0, self = 0;
   if (rvalid) {
     const int2 dsc = P.row_desc[tokq];
@@ -141,54 +311,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_bf16_d64_kernel(PlanView P, 
     self = dsc.y < 0;
   }
 
-  // ---- staging roles
-  const int kk = tid >> 3;       // K: keys kk and kk + 32
-  const int kpart = tid & 7;     // 8-element slice of d
-  const int vp = tid >> 3;       // V: key pair (2 vp, 2 vp + 1)
-  const int vpart = tid & 7;
-  const unsigned short* Kb = (const unsigned short*)A.k + (int64_t)m.tok_off * A.k_st + (int64_t)head * A.k_sh;
-  const unsigned short* Vb = (const unsigned short*)A.v + (int64_t)m.tok_off * A.v_st + (int64_t)head * A.v_sh;
-
-  // per-thread element offsets inside a key tile (loop invariant)
-  const int64_t ko0 = (int64_t)kk * A.k_st + 8 * kpart;
-  const int64_t ko1 = (int64_t)(kk + 32) * A.k_st + 8 * kpart;
-  const int64_t vo0 = (int64_t)(2 * vp) * A.v_st + 8 * vpart;
-  const int64_t vo1 = (int64_t)(2 * vp + 1) * A.v_st + 8 * vpart;
-  uint4 rk0, rk1, rv0, rv1;
-  // Loads are unconditional so the compiler can count them: rows past the
-  // end of the request (ragged last tile only) re-read the last row, whose
-  // finite values meet a -inf score (that tile is always PARTIAL) and P = 0.
-  auto gload = [&](int kt) {
-    const int c0 = kt * kTileK;
-    const unsigned short* kb = Kb + (int64_t)c0 * A.k_st;
-    const unsigned short* vb = Vb + (int64_t)c0 * A.v_st;
-    if (c0 + kTileK <= L) {
-      rk0 = *(const uint4*)(kb + ko0);
-      rk1 = *(const uint4*)(kb + ko1);
-      rv0 = *(const uint4*)(vb + vo0);
-      rv1 = *(const uint4*)(vb + vo1);
-    } else {
-      const int last = L - 1 - c0;
-      rk0 = *(const uint4*)(kb + (int64_t)min(kk, last) * A.k_st + 8 * kpart);
-      rk1 = *(const uint4*)(kb + (int64_t)min(kk + 32, last) * A.k_st + 8 * kpart);
-      rv0 = *(const uint4*)(vb + (int64_t)min(2 * vp, last) * A.v_st + 8 * vpart);
-      rv1 = *(const uint4*)(vb + (int64_t)min(2 * vp + 1, last) * A.v_st + 8 * vpart);
-    }
-  };
-  auto lstore = [&](int buf) {
-    *(uint4*)&Ks[buf * KBUF + kk * KS + 8 * kpart] = rk0;
-    *(uint4*)&Ks[buf * KBUF + (kk + 32) * KS + 8 * kpart] = rk1;
-    unsigned* vt = (unsigned*)&Vt[buf * VBUF];
-    const unsigned a[4] = {rv0.x, rv0.y, rv0.z, rv0.w};
-    const unsigned b[4] = {rv1.x, rv1.y, rv1.z, rv1.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d0 = 8 * vpart + 2 * j;
-      // element (key 2vp, d0) pairs with (key 2vp+1, d0) into one word
-      vt[d0 * (VS / 2) + vt_word(d0, vp)] = (a[j] & 0xffffu) | (b[j] << 16);
-      vt[(d0 + 1) * (VS / 2) + vt_word(d0 + 1, vp)] = (a[j] >> 16) | (b[j] & 0xffff0000u);
-    }
-  };
+  const char* Kb = (const char*)((const unsigned short*)A.k + (int64_t)m.tok_off * A.k_st + (int64_t)head * A.k_sh);
+  const char* Vb = (const char*)((const unsigned short*)A.v + (int64_t)m.tok_off * A.v_st + (int64_t)head * A.v_sh);
+  // row strides in bytes (32-bit per-lane offsets: the host limits strides)
+  const unsigned kst_b = (unsigned)A.k_st * 2u, vst_b = (unsigned)A.v_st * 2u;
+  const CopyMap cm = copy_map(wv, lane);
 
   f32x16 o0, o1;
 #pragma unroll
@@ -197,125 +324,44 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_bf16_d64_kernel(PlanView P, 
   const float sl2 = A.scale * 1.4426950408889634f;
   const float thr = kRescaleLog2 / sl2;  // in raw score units
 
-  const int e0 = P.qtile_ptr[qg];
-  const int n = P.qtile_ptr[qg + 1] - e0;
-  // CSR words are software-pipelined two tiles ahead and the prefetch is
-  // unconditional (the last iteration re-reads its own tile into the idle
-  // buffer), so the loop body has no data-dependent branches around loads.
-  int kw_cur = 0, kw_nxt = 0;
+  const int e0 = ldc(P.qtile_ptr, qg);
+  const int n = ldc(P.qtile_ptr, qg + 1) - e0;
+  // Iteration i computes tile i from one stage while the copies of tile
+  // i+1 fill the other; they land in LDS asynchronously and are waited for
+  // just before the barrier that ends the iteration.  The loop is unrolled
+  // by two so each stage is a distinct LDS object.  The copy issued in the
+  // last iteration re-reads the last tile into the idle stage (no branch
+  // around loads).
+  int w_cur = 0;
   if (n > 0) {
-    kw_cur = P.ktile_word[e0];
-    kw_nxt = P.ktile_word[e0 + min(1, n - 1)];
-    gload(kw_cur & 0x7fffffff);
-    lstore(0);
+    w_cur = ldc(P.ktile_word, e0);
+    tile_copy(K0, V0, cm, Kb, Vb, 2 * A.k_st, 2 * A.v_st, kst_b, vst_b, w_cur & 0x7fffffff, L, wv);
   }
-  // Everything loaded before the loop (Q fragment, row descriptor) is
-  // complete here, so inside the loop only the next tile's prefetch is
-  // outstanding when the MFMAs start.
-  asm volatile("s_waitcnt vmcnt(0)");
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int it = 0; it < n; ++it) {
-    const int buf = it & 1;
-    const int kt = kw_cur & 0x7fffffff;
-    const bool partial = kw_cur < 0;
-    gload(kw_nxt & 0x7fffffff);
-    const int kw_nn = P.ktile_word[e0 + min(it + 2, n - 1)];
-
-    // S^T = K Q^T
-    f32x16 s0, s1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
-    const unsigned short* kb = &Ks[buf * KBUF];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 a0 = as_bf16x8(*(const uint4*)&kb[li * KS + 16 * s + 8 * hh]);
-      const bf16x8 a1 = as_bf16x8(*(const uint4*)&kb[(32 + li) * KS + 16 * s + 8 * hh]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[s], s1, 0, 0, 0);
+  for (int it = 0; it < n; it += 2) {
+    {
+      const int w_nxt = ldc(P.ktile_word, e0 + min(it + 1, n - 1));
+      tile_copy(K1, V1, cm, Kb, Vb, 2 * A.k_st, 2 * A.v_st, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
+      tile_step(o0, o1, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0, li, hh, lo, hi,
+                self, row, sl2, thr);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      w_cur = w_nxt;
     }
-
-    if (partial) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt * kTileK + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const bool v0 = (key >= lo && key < hi) || (self && key == row);
-        const bool v1 = (key + 32 >= lo && key + 32 < hi) || (self && key + 32 == row);
-        if (!v0) s0[r] = -INFINITY;
-        if (!v1) s1[r] = -INFINITY;
-      }
+    if (it + 1 < n) {
+      const int w_nxt = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
+      tile_copy(K0, V0, cm, Kb, Vb, 2 * A.k_st, 2 * A.v_st, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
+      tile_step(o0, o1, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0, li, hh, lo, hi,
+                self, row, sl2, thr);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      w_cur = w_nxt;
     }
-
-    float mx = s0[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Lazy rescale: the reference max m_ref only moves when a row's max
-    // exceeds it by more than kRescaleLog2 (in log2 units), so P <= 2^8.
-    // The decision is made for the whole wave at once.
-    const float mnew = fmaxf(mref, mx);
-    const bool grow = mnew > mref + thr;
-    if (__any(grow)) {
-      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((mref - mnew) * sl2);
-      lsum *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { o0[r] *= alpha; o1[r] *= alpha; }
-      mref = mnew;
-    }
-    const float nb = mref == -INFINITY ? 0.f : -mref * sl2;
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, nb));
-      s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], sl2, nb));
-      psum += s0[r] + s1[r];
-    }
-    lsum += psum;
-
-    // P^T as B operands: step s takes accumulator block s/2, registers
-    // 8 (s%2) .. 8 (s%2) + 7
-    bf16x8 pb[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f32x16& src = (s < 2) ? s0 : s1;
-      const int r0 = 8 * (s & 1);
-      const uint4 w = make_uint4(pack_bf16x2(src[r0 + 0], src[r0 + 1]),
-                                 pack_bf16x2(src[r0 + 2], src[r0 + 3]),
-                                 pack_bf16x2(src[r0 + 4], src[r0 + 5]),
-                                 pack_bf16x2(src[r0 + 6], src[r0 + 7]));
-      pb[s] = as_bf16x8(w);
-    }
-
-    // O^T += V^T P^T
-    const unsigned* vt = (const unsigned*)&Vt[buf * VBUF];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int w0 = 8 * s + 2 * hh;  // keys 16 s + 4 hh .. +3  (logical words w0, w0+1)
-      {
-        const int d = li;
-        const unsigned* rowp = vt + d * (VS / 2);
-        const uint2 x = *(const uint2*)(rowp + vt_word(d, w0));
-        const uint2 y = *(const uint2*)(rowp + vt_word(d, w0 + 4));
-        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(make_uint4(x.x, x.y, y.x, y.y)), pb[s], o0, 0, 0, 0);
-      }
-      {
-        const int d = 32 + li;
-        const unsigned* rowp = vt + d * (VS / 2);
-        const uint2 x = *(const uint2*)(rowp + vt_word(d, w0));
-        const uint2 y = *(const uint2*)(rowp + vt_word(d, w0 + 4));
-        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(make_uint4(x.x, x.y, y.x, y.y)), pb[s], o1, 0, 0, 0);
-      }
-    }
-
-    lstore(buf ^ 1);
-    __syncthreads();
-    kw_cur = kw_nxt;
-    kw_nxt = kw_nn;
   }
 
-  // ---- epilogue: O = O^T / l, lanes of both halves hold distinct d values
+  // ---- epilogue: O = O^T / l; lanes of both halves hold distinct d values
   const float ltot = lsum + __shfl_xor(lsum, 32, 64);
   if (!rvalid) return;
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
