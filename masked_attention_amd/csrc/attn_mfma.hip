@@ -6,29 +6,36 @@
 // and the per-element mask runs on PARTIAL tiles only.
 //
 // Per 64-key tile and wave:
-//   S^T (64 keys x 32 queries) = K_tile (64 x 64) * Q_w^T   8 x mfma 32x32x16 bf16
-//   online softmax in fp32 (exp2 with log2(e) folded into the scale; the
-//   running max is only moved, and O rescaled, when it grows by > 2^8)
-//   O^T (64 d x 32 queries) += V_tile^T * P^T               8 x mfma 32x32x16 bf16
-// Computing the transposed products puts one query per lane (lane % 32) in
-// both accumulators, so the row max needs one exchange with lane ^ 32 and
-// the rescale of O by exp2(m_old - m_new) is lane-local.
+//   S^T (64 keys x 32 queries) = K_tile (64 x 64) * Q_w^T - m   8 x mfma 32x32x16
+//   P = exp2(S), packed to bf16; row sum in fp32
+//   O^T (64 d x 32 queries) += V_tile^T * P^T                   8 x mfma 32x32x16
+// Q is loaded pre-multiplied by scale * log2(e), so the scores come out of
+// the matrix core in log2 units, and the product starts from an
+// accumulator that holds -m for the lane's query (m: the row's reference
+// max), so the exponent needs no further arithmetic.  The reference max is
+// not tracked per tile: it is only re-derived (scores recomputed, running
+// max taken, O and l rescaled) when a lane's tile sum leaves [0, 2^32] or
+// is not a number, which happens on a row's first visible tile and when a
+// score exceeds the reference by more than 32 log2 units.  Any P kept is
+// therefore <= 2^32, far from fp32 overflow, and bf16 P keeps its relative
+// precision at any magnitude.
 //
 // Operand layouts (v_mfma_f32_32x32x16_bf16, lane l, half h = l / 32):
 //   A[m][k]: lane holds m = l % 32, k = 8h .. 8h+7
 //   B[k][n]: lane holds n = l % 32, k = 8h .. 8h+7
 //   D[m][n]: lane holds n = l % 32, m = 8 (r/4) + 4h + (r%4), r = 0..15
-// For P^T V^T the 16-key slice of step s is consumed in the key order that
-// the S^T accumulator already holds (k = 8h + e  ->  key 16 s + 8 (e/4) +
-// 4h + e%4); V^T is read from LDS in the same order, so P never moves
-// between lanes.
+// Computing the transposed products puts one query per lane (lane % 32) in
+// both accumulators; the two lane halves hold different keys of the same
+// query.  For P^T V^T the 16-key slice of step s is consumed in the key
+// order the S^T accumulator already holds (k = 8h + e  ->  key 16 s +
+// 8 (e/4) + 4h + e%4); V^T is read in that order with transposing LDS
+// reads, so P never moves between lanes.
 //
-// LDS (double-buffered, one barrier per tile):
-//   K  [64 keys][72]  row-major, 16-byte rows padded to avoid conflicts
-//   V^T[64 d][68]     transposed while staging; word index XOR 8 on rows
-//                     16..31 / 48..63 spreads the transposing stores
-// Q is rotated by time RoPE while it is loaded (fp32, hardware sin/cos on a
-// phase reduced to [-1/2, 1/2] revolution); K arrives pre-rotated.
+// LDS: two stages of K and V tiles (64 rows x 128 bytes each, unpadded,
+// XOR-swizzled 16-byte chunks), filled by buffer loads that write LDS
+// directly; one barrier per tile.  Q is rotated by time RoPE while it is
+// loaded (fp32, hardware sin/cos on a phase reduced to [-1/2, 1/2]
+// revolution); K arrives pre-rotated.
 #include <hip/hip_bf16.h>
 
 #include "rk_internal.h"
@@ -41,7 +48,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int D = 64;
 constexpr int TILE_ELEMS = kTileK * D;  // 64 rows x 64 bf16 = 8 KB per K or V tile
-constexpr float kRescaleLog2 = 8.f;
+// A lane's tile sum above this (or not a number) sends the wave to the
+// slow path that re-derives the reference max.
+constexpr float kMaxTileSum = 4294967296.f;  // 2^32
+constexpr unsigned kBufferFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
 struct PlanView {
   const ReqMeta* req;
@@ -96,11 +106,12 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int kswz(int r) { return r & 7; }
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
 
-// Q fragment: lane holds Q[row][16 s + 8 hh .. +7], s = 0..3, rotated by
-// time RoPE when asked (fp32 math, hardware sin/cos on a phase reduced to
-// [-1/2, 1/2] revolution), packed to bf16.
+// Q fragment: lane holds Q[row][16 s + 8 hh .. +7] * qmul, s = 0..3,
+// rotated by time RoPE when asked (fp32 math, hardware sin/cos on a phase
+// reduced to [-1/2, 1/2] revolution), rounded once to bf16.
 __device__ __forceinline__ void load_q(bf16x8 (&qb)[4], const AttnLaunch& A, const double* wtab,
-                                       int tokq, bool valid, int head, int req, int hh) {
+                                       int tokq, bool valid, int head, int req, int hh,
+                                       float qmul) {
   const unsigned short* Qp = (const unsigned short*)A.q + (int64_t)tokq * A.q_st + (int64_t)head * A.q_sh;
   double dtd = 0.0;
   if (A.rope_q && valid) dtd = (double)(A.ts[tokq] - A.anchors[req]);
@@ -108,65 +119,68 @@ __device__ __forceinline__ void load_q(bf16x8 (&qb)[4], const AttnLaunch& A, con
   for (int s = 0; s < 4; ++s) {
     uint4 raw = make_uint4(0, 0, 0, 0);
     if (valid) raw = *(const uint4*)(Qp + 16 * s + 8 * hh);
-    if (A.rope_q) {
-      unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
+    unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j) {
+      float x0 = bf_lo(w[j]), x1 = bf_hi(w[j]);
+      if (A.rope_q) {
         const int i = 8 * s + 4 * hh + j;  // pair index
         const double rev = dtd * wtab[i];
         const float f = (float)(rev - rint(rev));
         const float sn = __builtin_amdgcn_sinf(f);
         const float cs = __builtin_amdgcn_cosf(f);
-        const float x0 = bf_lo(w[j]), x1 = bf_hi(w[j]);
-        w[j] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+        const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+        x0 = y0;
+        x1 = y1;
       }
-      raw = make_uint4(w[0], w[1], w[2], w[3]);
+      w[j] = pack_bf16x2(x0 * qmul, x1 * qmul);
     }
-    qb[s] = as_bf16x8(raw);
+    qb[s] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
   }
 }
 
-// Per-lane source offsets of the direct global -> LDS copies.  A wave's
-// global_load_lds of 16 bytes per lane fills 1 KB of LDS contiguously
-// (lane l at byte 16 l): 8 rows.  Wave w issues copies j = 0, 1 for rows
-// 8 (2 w + j) .. +7 of both the K and the V tile.
+// Per-lane byte offsets of the direct buffer -> LDS copies.  A wave's
+// 16-byte-per-lane buffer load with the LDS bit fills 1 KB of LDS
+// contiguously (lane l at byte 16 l): 8 rows.  Wave w issues copies
+// j = 0, 1 for rows 8 (2 w + j) .. +7 of both the K and the V tile; the
+// offsets are relative to the tile's first row and do not change.
 struct CopyMap {
-  int row[2];        // tile row written by this lane in copy j
-  unsigned kcol[2];  // byte offset of its source chunk inside a K row
-  unsigned vcol[2];  // same for V
+  unsigned koff[2];
+  unsigned voff[2];
 };
 
-__device__ __forceinline__ CopyMap copy_map(int wv, int lane) {
+__device__ __forceinline__ CopyMap copy_map(int wv, int lane, unsigned kst_b, unsigned vst_b) {
   CopyMap c;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int q = (2 * wv + j) * 64 + lane;
     const int r = q >> 3, slot = q & 7;
-    c.row[j] = r;
-    c.kcol[j] = 16u * (unsigned)(slot ^ kswz(r));
-    c.vcol[j] = 16u * (unsigned)(slot ^ vswz(r));
+    c.koff[j] = (unsigned)r * kst_b + 16u * (unsigned)(slot ^ kswz(r));
+    c.voff[j] = (unsigned)r * vst_b + 16u * (unsigned)(slot ^ vswz(r));
   }
   return c;
 }
 
-// Issue the copies of key tile kt into LDS buffers kd / vd.  Rows past the
-// end of the request (ragged last tile only) re-read the last row: finite
-// values that meet a -inf score (that tile is always PARTIAL), so P = 0.
+// Issue the copies of key tile kt into LDS buffers kd / vd.  The buffer
+// descriptor of each tile ends at the last byte of its last token, so the
+// rows past the end of the request (ragged last tile only) are out of
+// range and load zeros; that tile is always PARTIAL, so their scores are
+// masked.
 __device__ __forceinline__ void tile_copy(unsigned short* kd, unsigned short* vd, const CopyMap& c,
-                                          const char* Kb, const char* Vb, int64_t k_st_b,
-                                          int64_t v_st_b, unsigned kst_b, unsigned vst_b, int kt,
-                                          int L, int wv) {
+                                          const char* Kb, const char* Vb, unsigned kst_b,
+                                          unsigned vst_b, int kt, int L, int wv) {
   const int c0 = kt * kTileK;
-  const int last = (c0 + kTileK > L) ? L - 1 - c0 : kTileK - 1;
-  const char* kb = Kb + (int64_t)c0 * k_st_b;
-  const char* vb = Vb + (int64_t)c0 * v_st_b;
+  const unsigned last = (unsigned)min(L - c0, kTileK) - 1u;  // last row inside the request
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Kb + (int64_t)c0 * kst_b), 0, (int)(last * kst_b + 2u * D), (int)kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Vb + (int64_t)c0 * vst_b), 0, (int)(last * vst_b + 2u * D), (int)kBufferFlags);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const unsigned r = (unsigned)min(c.row[j], last);
-    __builtin_amdgcn_global_load_lds((const void*)(kb + r * kst_b + c.kcol[j]),
-                                     LDS_PTR(void, kd + (2 * wv + j) * 512), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(vb + r * vst_b + c.vcol[j]),
-                                     LDS_PTR(void, vd + (2 * wv + j) * 512), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LDS_PTR(void, kd + (2 * wv + j) * 512), 16,
+                                             c.koff[j], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LDS_PTR(void, vd + (2 * wv + j) * 512), 16,
+                                             c.voff[j], 0, 0, 0);
   }
 }
 
@@ -182,53 +196,36 @@ __device__ __forceinline__ void mask_tile(f32x16& s0, f32x16& s1, int kt, int hh
   }
 }
 
-// One 64-key tile for one wave (32 queries): S^T = K Q^T, mask, online
-// softmax, O^T += V^T P^T.  kb / vb are the tile's LDS buffers.
-__device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, float& mref, float& lsum,
-                                          const unsigned short* kb, const unsigned short* vb,
-                                          const bf16x8 (&q)[4], int kt, bool partial, int li,
-                                          int hh, int lo, int hi, int self, int row, float sl2,
-                                          float thr) {
-  f32x16 s0, s1;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+// S^T = K Q^T + c for the wave's 32 queries (c: initial accumulator).
+__device__ __forceinline__ void scores(f32x16& s0, f32x16& s1, const unsigned short* kb,
+                                       const bf16x8 (&q)[4], const f32x16& c, int li, int hh) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int cc = 2 * s + hh;  // logical chunk: d = 16 s + 8 hh .. +7
     const bf16x8 k0 = as_bf16x8(*(const uint4*)&kb[li * 64 + 8 * (cc ^ kswz(li))]);
     const bf16x8 k1 = as_bf16x8(*(const uint4*)&kb[(32 + li) * 64 + 8 * (cc ^ kswz(32 + li))]);
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[s], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[s], s == 0 ? c : s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s == 0 ? c : s1, 0, 0, 0);
   }
-  if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
+}
 
-  float mx = s0[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  // Lazy rescale: the reference max only moves when a row's max exceeds it
-  // by more than kRescaleLog2 (log2 units), so P <= 2^8; the decision is
-  // taken for the whole wave.
-  const float mnew = fmaxf(mref, mx);
-  if (__any(mnew > mref + thr)) {
-    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((mref - mnew) * sl2);
-    lsum *= alpha;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { o0[r] *= alpha; o1[r] *= alpha; }
-    mref = mnew;
-  }
-  const float nb = mref == -INFINITY ? 0.f : -mref * sl2;
+// P = exp2((S + nb) * mul) (nb only when kShift, mul only when kScale),
+// packed to bf16 as the B operands of the PV product (step s: accumulator
+// block s/2, registers 8 (s%2)..+7).  Returns the lane's sum of the
+// rounded values (v_dot2 with (1, 1)).
+template <bool kShift, bool kScale>
+__device__ __forceinline__ float probs(bf16x8 (&pb)[4], f32x16& s0, f32x16& s1, float nb,
+                                       float mul) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, nb));
-    s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], sl2, nb));
+    float x0 = kShift ? s0[r] + nb : s0[r];
+    float x1 = kShift ? s1[r] + nb : s1[r];
+    if (kScale) { x0 *= mul; x1 *= mul; }
+    s0[r] = __builtin_amdgcn_exp2f(x0);
+    s1[r] = __builtin_amdgcn_exp2f(x1);
   }
-  // P^T as B operands (step s: accumulator block s/2, registers 8 (s%2)..+7);
-  // the row sum takes the same rounded bf16 values (v_dot2 with (1, 1)).
-  bf16x8 pb[4];
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float sum = 0.f;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const f32x16& src = (s < 2) ? s0 : s1;
@@ -238,10 +235,56 @@ __device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, float& mref, f
     for (int j = 0; j < 4; ++j) {
       w[j][0] = (__bf16)src[r0 + 2 * j];
       w[j][1] = (__bf16)src[r0 + 2 * j + 1];
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(w[j], ones, lsum, false);
+      sum = __builtin_amdgcn_fdot2_f32_bf16(w[j], ones, sum, false);
     }
     __builtin_memcpy(&pb[s], w, 16);
   }
+  return sum;
+}
+
+// One 64-key tile for one wave (32 queries): scores, mask, P, O^T += V^T
+// P^T.  kb / vb are the tile's LDS buffers; negm holds -mref (or +inf while
+// the row has seen no visible key) in all 16 registers.  Scores are in
+// log2 units when kPreScaled (Q carries scale * log2(e)); otherwise they
+// are raw dot products and mul = scale * log2(e) is applied before exp2.
+template <bool kPreScaled>
+__device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, float& mref,
+                                          float& lsum, const unsigned short* kb,
+                                          const unsigned short* vb, const bf16x8 (&q)[4], int kt,
+                                          bool partial, int li, int hh, int lo, int hi, int self,
+                                          int row, float mul) {
+  f32x16 s0, s1;
+  scores(s0, s1, kb, q, negm, li, hh);
+  if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
+  bf16x8 pb[4];
+  float ts = probs<false, !kPreScaled>(pb, s0, s1, 0.f, mul);
+  if (__any(!(ts <= kMaxTileSum))) {
+    // Re-derive the reference max from this tile's raw scores (log2 units).
+    f32x16 zero;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zero[r] = 0.f;
+    scores(s0, s1, kb, q, zero, li, hh);
+    if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
+    float mx = s0[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(mref, mx);
+    if (mnew > mref) {  // false when both are -inf
+      const float alpha = __builtin_amdgcn_exp2f(kPreScaled ? mref - mnew : (mref - mnew) * mul);  // 0 when mref = -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { o0[r] *= alpha; o1[r] *= alpha; }
+      mref = mnew;
+    }
+    const float nb = mref == -INFINITY ? INFINITY : -mref;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = nb;
+    ts = probs<true, !kPreScaled>(pb, s0, s1, mref == -INFINITY ? 0.f : nb, mul);
+  }
+  lsum += ts;
 
   // V^T fragments by transposing reads: in each 16-lane group g, lane i
   // points at V[k + (i >> 2)][d0 + 4 (i & 3)] and receives V[k..k+3][d0 + i].
@@ -273,6 +316,11 @@ __device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, float& mref, f
 
 constexpr int kThreads = 256;  // 4 waves, 32 query rows each
 
+// kPreScaled: Q is rotated by time RoPE in the kernel and rounded to bf16
+// anyway, so scale * log2(e) is folded in before that single rounding.
+// Without RoPE, Q is used exactly as given and the scale is applied to the
+// fp32 scores instead.
+template <bool kPreScaled>
 __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanView P, AttnLaunch A) {
   // Two stages of K and V tiles as separate objects, so the compiler can
   // tell the buffer being filled from the one being read.
@@ -291,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int hh = lane >> 5;   // lane half
   const int li = lane & 31;   // query column of this lane
   const int row = qt * kTileQ + wv * 32 + li;
@@ -299,10 +347,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   const int tokq = m.tok_off + row;
 
   if (A.rope_q && tid < D / 2) wtab[tid] = A.tab.w_rev[tid];
+  // Start the V stages from zeros: whatever a copy leaves unwritten stays
+  // finite, so a masked key (P = 0) adds exactly 0 to O.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    *(uint4*)&V0[8 * (tid + kThreads * j)] = make_uint4(0, 0, 0, 0);
+    *(uint4*)&V1[8 * (tid + kThreads * j)] = make_uint4(0, 0, 0, 0);
+  }
   __syncthreads();
 
+  const float sl2 = A.scale * 1.4426950408889634f;  // scale * log2(e)
   bf16x8 q[4];
-  load_q(q, A, wtab, tokq, rvalid, head, req, hh);
+  load_q(q, A, wtab, tokq, rvalid, head, req, hh, kPreScaled ? sl2 : 1.f);
   int lo = 0, hi = 0, self = 0;
   if (rvalid) {
     const int2 dsc = P.row_desc[tokq];
@@ -315,14 +371,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   const char* Vb = (const char*)((const unsigned short*)A.v + (int64_t)m.tok_off * A.v_st + (int64_t)head * A.v_sh);
   // row strides in bytes (32-bit per-lane offsets: the host limits strides)
   const unsigned kst_b = (unsigned)A.k_st * 2u, vst_b = (unsigned)A.v_st * 2u;
-  const CopyMap cm = copy_map(wv, lane);
+  const CopyMap cm = copy_map(wv, lane, kst_b, vst_b);
 
-  f32x16 o0, o1;
+  f32x16 o0, o1, negm;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) { o0[r] = 0.f; o1[r] = 0.f; }
+  for (int r = 0; r < 16; ++r) { o0[r] = 0.f; o1[r] = 0.f; negm[r] = INFINITY; }
   float mref = -INFINITY, lsum = 0.f;
-  const float sl2 = A.scale * 1.4426950408889634f;
-  const float thr = kRescaleLog2 / sl2;  // in raw score units
 
   const int e0 = ldc(P.qtile_ptr, qg);
   const int n = ldc(P.qtile_ptr, qg + 1) - e0;
@@ -335,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   int w_cur = 0;
   if (n > 0) {
     w_cur = ldc(P.ktile_word, e0);
-    tile_copy(K0, V0, cm, Kb, Vb, 2 * A.k_st, 2 * A.v_st, kst_b, vst_b, w_cur & 0x7fffffff, L, wv);
+    tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_cur & 0x7fffffff, L, wv);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -343,18 +397,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   for (int it = 0; it < n; it += 2) {
     {
       const int w_nxt = ldc(P.ktile_word, e0 + min(it + 1, n - 1));
-      tile_copy(K1, V1, cm, Kb, Vb, 2 * A.k_st, 2 * A.v_st, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
-      tile_step(o0, o1, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0, li, hh, lo, hi,
-                self, row, sl2, thr);
+      tile_copy(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
+      tile_step<kPreScaled>(o0, o1, negm, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0,
+                            li, hh, lo, hi, self, row, sl2);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       w_cur = w_nxt;
     }
     if (it + 1 < n) {
       const int w_nxt = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
-      tile_copy(K0, V0, cm, Kb, Vb, 2 * A.k_st, 2 * A.v_st, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
-      tile_step(o0, o1, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0, li, hh, lo, hi,
-                self, row, sl2, thr);
+      tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
+      tile_step<kPreScaled>(o0, o1, negm, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0,
+                            li, hh, lo, hi, self, row, sl2);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       w_cur = w_nxt;
@@ -375,7 +429,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
                                         pack_bf16x2(o1[4 * g + 2] * inv, o1[4 * g + 3] * inv));
   }
   if (A.lse && hh == 0)
-    A.lse[(int64_t)head * A.T + tokq] = ltot > 0.f ? mref * A.scale + logf(ltot) : -INFINITY;
+    A.lse[(int64_t)head * A.T + tokq] =
+        ltot > 0.f ? mref * (kPreScaled ? 0.6931471805599453f : A.scale) + logf(ltot) : -INFINITY;
 }
 
 }  // namespace
@@ -384,7 +439,12 @@ hipError_t launch_attn_mfma_bf16_d64(const rk_plan* p, const AttnLaunch& a, hipS
   if (p->slots == 0) return hipSuccess;
   PlanView P{p->dev.req, p->dev.qt_req, p->dev.row_desc, p->dev.qtile_ptr, p->dev.ktile_word,
              p->dev.sched};
-  hipLaunchKernelGGL(attn_mfma_bf16_d64_kernel, dim3((unsigned)p->slots), dim3(256), 0, s, P, a);
+  if (a.rope_q)
+    hipLaunchKernelGGL(attn_mfma_bf16_d64_kernel<true>, dim3((unsigned)p->slots), dim3(kThreads), 0,
+                       s, P, a);
+  else
+    hipLaunchKernelGGL(attn_mfma_bf16_d64_kernel<false>, dim3((unsigned)p->slots),
+                       dim3(kThreads), 0, s, P, a);
   return hipGetLastError();
 }
 

@@ -398,3 +398,55 @@ def test_prerotated_k_matches_fused_path(rk):
     o2, _ = rk.rk_masked_attn_fwd(plan, q, krot, v, rope=_rope(wl), k_prerotated=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("rope", [True, False], ids=["rope", "norope"])
+def test_attention_dominant_key(rk, rope):
+    """One key per request whose score exceeds every earlier score of the
+    rows that see it by far more than 32 log2 units, placed several tiles
+    into the request: the running max then jumps mid-row, and every row
+    that sees the key must come out as that key's value row.  The query
+    offset and the key sit in dimensions 0..7, the four lowest-frequency
+    time RoPE pairs, which turn by < 1e-3 rad over the request's time span."""
+    rng = np.random.default_rng(31)
+    reqs = [
+        [(HISTORY, np.sort(rng.integers(NOW - 300 * 86400, NOW - 86400, 700))),
+         (REALTIME, np.sort(rng.integers(NOW - 86400, NOW, 40))),
+         (CANDIDATE, rng.integers(NOW - 86400, NOW, 30))],
+        [(PROFILE, np.full(5, NOW - 200 * 86400)),
+         (HISTORY, np.sort(rng.integers(NOW - 200 * 86400, NOW - 86400, 300)))],
+        [(HISTORY, np.sort(rng.integers(NOW - 100 * 86400, NOW, 200)))],
+    ]
+    wl = make_custom(reqs, heads=2, d_head=64, dtype="bf16", seed=31, delay=0)
+    wl.q[:, :, :8] += 2.0
+    offs = wl.req_offsets
+    hot = []
+    for r in range(offs.shape[0] - 1):
+        hist = np.nonzero(wl.seg_kind[offs[r]:offs[r + 1]] == HISTORY)[0]
+        j = int(offs[r] + hist[int(0.6 * hist.shape[0])])
+        wl.k[j, :, :8] = 40.0
+        hot.append(j)
+    from rk_workloads import bf16_round
+    wl.q = bf16_round(wl.q.astype(np.float32))
+    wl.k = bf16_round(wl.k.astype(np.float32))
+    plan, o, lse = _run(rk, wl, rope=rope)
+    ref, ref_lse = _oracle_full(wl, rope=rope)
+    _check(wl, o, ref)
+    # The rows that see a hot key are that key's value row to bf16 precision.
+    sees = np.zeros(wl.total_tokens, bool)
+    for r, j in enumerate(hot):
+        L = int(offs[r + 1] - offs[r])
+        rows = oracle.visible_rows(wl.seg_kind[offs[r]:offs[r + 1]],
+                                   wl.timestamps[offs[r]:offs[r + 1]], np.arange(L),
+                                   delay=wl.delay, window=wl.window,
+                                   static_bidirectional=wl.static_bidirectional)
+        for p, vis in enumerate(rows):
+            if vis[j - offs[r]]:
+                sees[offs[r] + p] = True
+                assert np.abs(o[offs[r] + p] - wl.v[j]).max() <= BF16_MAX_ABS
+    assert sees.sum() > 300
+    # lse: the bf16 query carries up to 2^-9 relative rounding into a score
+    # of ~80, so the bound here grows with |lse|.
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.all(np.abs(lse[fin] - ref_lse[fin]) <= 2e-2 + 2.0 ** -7 * np.abs(ref_lse[fin]))
