@@ -6,19 +6,16 @@
 // and the per-element mask runs on PARTIAL tiles only.
 //
 // Per 64-key tile and wave:
-//   S^T (64 keys x 32 queries) = K_tile (64 x 64) * Q_w^T - m   8 x mfma 32x32x16
-//   P = exp2(S), packed to bf16; row sum in fp32
-//   O^T (64 d x 32 queries) += V_tile^T * P^T                   8 x mfma 32x32x16
-// Q is loaded pre-multiplied by scale * log2(e), so the scores come out of
-// the matrix core in log2 units, and the product starts from an
-// accumulator that holds -m for the lane's query (m: the row's reference
-// max), so the exponent needs no further arithmetic.  The reference max is
-// not tracked per tile: it is only re-derived (scores recomputed, running
-// max taken, O and l rescaled) when a lane's tile sum leaves [0, 2^32] or
-// is not a number, which happens on a row's first visible tile and when a
-// score exceeds the reference by more than 32 log2 units.  Any P kept is
-// therefore <= 2^32, far from fp32 overflow, and bf16 P keeps its relative
-// precision at any magnitude.
+//   S^T (64 keys x 32 queries) = K_tile (64 x 64) * Q_w^T      8 x mfma 32x32x16
+//   P = exp2(S - m), packed to bf16; row sum in fp32
+//   O^T (64 d x 32 queries) += V_tile^T * P^T                  8 x mfma 32x32x16
+// With time RoPE, Q is loaded pre-multiplied by scale * log2(e) (folded in
+// before its single bf16 rounding), so the scores come out of the matrix
+// core in log2 units.  m is the row's reference max; it is not tracked per
+// tile but re-derived from the tile's scores only when a lane's tile sum of
+// P leaves [0, 2^32] or is not a number, or when a row sees its first key.
+// Any P kept is therefore <= 2^32, far from fp32 overflow, and bf16 P keeps
+// its relative precision at any magnitude.
 //
 // Operand layouts (v_mfma_f32_32x32x16_bf16, lane l, half h = l / 32):
 //   A[m][k]: lane holds m = l % 32, k = 8h .. 8h+7
@@ -48,8 +45,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int D = 64;
 constexpr int TILE_ELEMS = kTileK * D;  // 64 rows x 64 bf16 = 8 KB per K or V tile
-// A lane's tile sum above this (or not a number) sends the wave to the
-// slow path that re-derives the reference max.
+// A lane's tile sum above this (or not a number) makes the wave re-derive
+// the reference max.
 constexpr float kMaxTileSum = 4294967296.f;  // 2^32
 constexpr unsigned kBufferFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
@@ -184,48 +181,60 @@ __device__ __forceinline__ void tile_copy(unsigned short* kd, unsigned short* vd
   }
 }
 
+// Mask of one tile on the S^T accumulators: the lane's query sees key
+// c0 + 8 g + 4 hh + e (g, e = 0..3) in register 4 g + e of s0, and that key
+// + 32 in s1.  The visible keys of the row inside the tile, as a 64-bit
+// set, are its interval [lo, hi) clipped to the tile plus, for a candidate,
+// its own position; after a shift by 4 hh, register r of s0 tests bit
+// 8 (r / 4) + r % 4 of the low word and s1 the same bit of the high word.
+// A hidden score becomes -inf by a bit select against the sign-extended
+// test bit (no lane masks involved).
 __device__ __forceinline__ void mask_tile(f32x16& s0, f32x16& s1, int kt, int hh, int lo, int hi,
                                           int self, int row) {
+  const int c0 = kt * kTileK;
+  const int a = min(max(lo - c0, 0), kTileK), b = min(max(hi - c0, 0), kTileK);
+  const uint64_t below_b = b >= 64 ? ~0ull : (1ull << b) - 1ull;
+  const uint64_t below_a = a >= 64 ? ~0ull : (1ull << a) - 1ull;
+  uint64_t vis = below_b & ~below_a;
+  const int sr = row - c0;
+  if (self && sr >= 0 && sr < kTileK) vis |= 1ull << sr;
+  vis >>= 4 * hh;
+  const int w0 = (int)(unsigned)vis, w1 = (int)(unsigned)(vis >> 32);
+  const int ninf = (int)0xff800000u;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int key = kt * kTileK + 8 * (r >> 2) + 4 * hh + (r & 3);
-    const bool v0 = (key >= lo && key < hi) || (self && key == row);
-    const bool v1 = (key + 32 >= lo && key + 32 < hi) || (self && key + 32 == row);
-    if (!v0) s0[r] = -INFINITY;
-    if (!v1) s1[r] = -INFINITY;
+    const unsigned bit = 8u * (unsigned)(r >> 2) + (unsigned)(r & 3);
+    const int m0 = __builtin_amdgcn_sbfe(w0, bit, 1u);  // 0 or -1
+    const int m1 = __builtin_amdgcn_sbfe(w1, bit, 1u);
+    s0[r] = __int_as_float((__float_as_int(s0[r]) & m0) | (ninf & ~m0));
+    s1[r] = __int_as_float((__float_as_int(s1[r]) & m1) | (ninf & ~m1));
   }
 }
 
-// S^T = K Q^T + c for the wave's 32 queries (c: initial accumulator).
+// S^T = K Q^T for the wave's 32 queries.
 __device__ __forceinline__ void scores(f32x16& s0, f32x16& s1, const unsigned short* kb,
-                                       const bf16x8 (&q)[4], const f32x16& c, int li, int hh) {
+                                       const bf16x8 (&q)[4], int li, int hh) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int cc = 2 * s + hh;  // logical chunk: d = 16 s + 8 hh .. +7
     const bf16x8 k0 = as_bf16x8(*(const uint4*)&kb[li * 64 + 8 * (cc ^ kswz(li))]);
     const bf16x8 k1 = as_bf16x8(*(const uint4*)&kb[(32 + li) * 64 + 8 * (cc ^ kswz(32 + li))]);
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[s], s == 0 ? c : s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s == 0 ? c : s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[s], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s1, 0, 0, 0);
   }
 }
 
-// P = exp2((S + nb) * mul) (nb only when kShift, mul only when kScale),
-// packed to bf16 as the B operands of the PV product (step s: accumulator
-// block s/2, registers 8 (s%2)..+7).  Returns the lane's sum of the
-// rounded values (v_dot2 with (1, 1)).
-template <bool kShift, bool kScale>
-__device__ __forceinline__ float probs(bf16x8 (&pb)[4], f32x16& s0, f32x16& s1, float nb,
-                                       float mul) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float x0 = kShift ? s0[r] + nb : s0[r];
-    float x1 = kShift ? s1[r] + nb : s1[r];
-    if (kScale) { x0 *= mul; x1 *= mul; }
-    s0[r] = __builtin_amdgcn_exp2f(x0);
-    s1[r] = __builtin_amdgcn_exp2f(x1);
-  }
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float sum = 0.f;
+// P = exp2((S - m) * mul) (mul only when kScale), packed to bf16 as the B
+// operands of the PV product (step s: accumulator block s/2, registers
+// 8 (s%2)..+7).  S is left as it is.  Returns the lane's sum of the fp32
+// values (plain adds: they issue alongside the matrix cores, unlike the
+// packed-bf16 dot products).
+template <bool kScale>
+__device__ __forceinline__ float probs(bf16x8 (&pb)[4], const f32x16& s0, const f32x16& s1,
+                                       float m, float mul) {
+  float sum0 = 0.f, sum1 = 0.f;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const f32x16& src = (s < 2) ? s0 : s1;
@@ -233,56 +242,66 @@ __device__ __forceinline__ float probs(bf16x8 (&pb)[4], f32x16& s0, f32x16& s1, 
     bf16x2_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      w[j][0] = (__bf16)src[r0 + 2 * j];
-      w[j][1] = (__bf16)src[r0 + 2 * j + 1];
-      sum = __builtin_amdgcn_fdot2_f32_bf16(w[j], ones, sum, false);
+      float x0 = src[r0 + 2 * j] - m, x1 = src[r0 + 2 * j + 1] - m;
+      if (kScale) { x0 *= mul; x1 *= mul; }
+      const float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
+      w[j][0] = (__bf16)p0;
+      w[j][1] = (__bf16)p1;
+      sum0 += p0;
+      sum1 += p1;
     }
     __builtin_memcpy(&pb[s], w, 16);
   }
-  return sum;
+  return sum0 + sum1;
+}
+
+// Does query `row` see any key of tile kt?  Every row of a FULL tile does;
+// on a PARTIAL tile, its interval [lo, hi) or its own position must fall in
+// the tile.
+__device__ __forceinline__ bool row_sees(int kt, bool partial, int lo, int hi, int self, int row) {
+  const int c0 = kt * kTileK;
+  return !partial || (lo < c0 + kTileK && hi > c0) || (self && row >= c0 && row < c0 + kTileK);
 }
 
 // One 64-key tile for one wave (32 queries): scores, mask, P, O^T += V^T
-// P^T.  kb / vb are the tile's LDS buffers; negm holds -mref (or +inf while
-// the row has seen no visible key) in all 16 registers.  Scores are in
-// log2 units when kPreScaled (Q carries scale * log2(e)); otherwise they
-// are raw dot products and mul = scale * log2(e) is applied before exp2.
+// P^T.  kb / vb are the tile's LDS buffers.  Scores are in log2 units when
+// kPreScaled (Q carries scale * log2(e)); otherwise they are raw dot
+// products and mul = scale * log2(e) is applied before exp2.
+//
+// P is taken against the row's reference m = mref (0 while the row is
+// fresh: mref = -inf, no visible key seen yet) without a per-tile max.  The
+// wave re-derives the reference from this tile's scores instead when a
+// lane's tile sum leaves [0, 2^32] (or is not a number), or when a fresh
+// row sees a key of this tile: m moves up by the tile's excess over it (O
+// and l rescaled), or to the tile's max for a fresh row.
 template <bool kPreScaled>
-__device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, float& mref,
-                                          float& lsum, const unsigned short* kb,
-                                          const unsigned short* vb, const bf16x8 (&q)[4], int kt,
-                                          bool partial, int li, int hh, int lo, int hi, int self,
-                                          int row, float mul) {
+__device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, float& mref, float& lsum,
+                                          const unsigned short* kb, const unsigned short* vb,
+                                          const bf16x8 (&q)[4], int kt, bool partial, int li,
+                                          int hh, int lo, int hi, int self, int row, float mul) {
   f32x16 s0, s1;
-  scores(s0, s1, kb, q, negm, li, hh);
+  scores(s0, s1, kb, q, li, hh);
   if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
   bf16x8 pb[4];
-  float ts = probs<false, !kPreScaled>(pb, s0, s1, 0.f, mul);
-  if (__any(!(ts <= kMaxTileSum))) {
-    // Re-derive the reference max from this tile's raw scores (log2 units).
-    f32x16 zero;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) zero[r] = 0.f;
-    scores(s0, s1, kb, q, zero, li, hh);
-    if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
+  const bool fresh = mref == -INFINITY;
+  float ts = probs<!kPreScaled>(pb, s0, s1, fresh ? 0.f : mref, mul);
+  if (__any(!(ts <= kMaxTileSum) || (fresh && row_sees(kt, partial, lo, hi, self, row)))) {
     float mx = s0[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(mref, mx);
-    if (mnew > mref) {  // false when both are -inf
-      const float alpha = __builtin_amdgcn_exp2f(kPreScaled ? mref - mnew : (mref - mnew) * mul);  // 0 when mref = -inf
+    if (fresh) {
+      mref = mx;  // stays -inf when nothing of this tile is visible
+    } else if (mx > mref) {
+      const float alpha = __builtin_amdgcn_exp2f(kPreScaled ? mref - mx : (mref - mx) * mul);
       lsum *= alpha;
 #pragma unroll
       for (int r = 0; r < 16; ++r) { o0[r] *= alpha; o1[r] *= alpha; }
-      mref = mnew;
+      mref = mx;
     }
-    const float nb = mref == -INFINITY ? INFINITY : -mref;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) negm[r] = nb;
-    ts = probs<true, !kPreScaled>(pb, s0, s1, mref == -INFINITY ? 0.f : nb, mul);
+    ts = probs<!kPreScaled>(pb, s0, s1, mref == -INFINITY ? 0.f : mref, mul);
   }
   lsum += ts;
 
@@ -373,9 +392,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   const unsigned kst_b = (unsigned)A.k_st * 2u, vst_b = (unsigned)A.v_st * 2u;
   const CopyMap cm = copy_map(wv, lane, kst_b, vst_b);
 
-  f32x16 o0, o1, negm;
+  f32x16 o0, o1;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) { o0[r] = 0.f; o1[r] = 0.f; negm[r] = INFINITY; }
+  for (int r = 0; r < 16; ++r) { o0[r] = 0.f; o1[r] = 0.f; }
   float mref = -INFINITY, lsum = 0.f;
 
   const int e0 = ldc(P.qtile_ptr, qg);
@@ -398,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
     {
       const int w_nxt = ldc(P.ktile_word, e0 + min(it + 1, n - 1));
       tile_copy(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
-      tile_step<kPreScaled>(o0, o1, negm, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0,
+      tile_step<kPreScaled>(o0, o1, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0,
                             li, hh, lo, hi, self, row, sl2);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -407,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
     if (it + 1 < n) {
       const int w_nxt = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
       tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
-      tile_step<kPreScaled>(o0, o1, negm, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0,
+      tile_step<kPreScaled>(o0, o1, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0,
                             li, hh, lo, hi, self, row, sl2);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
