@@ -50,10 +50,10 @@ def _parse():
     return ap.parse_args()
 
 
-def _traffic_from_profile(workload: str):
-    """HBM bytes per attention launch from the committed PMC summary, if it
-    was taken on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_hbm_traffic_{workload}.txt")
+def _profile_kv(kind: str, workload: str):
+    """Key/value lines of profiles/attn_fwd_<kind>_<workload>.txt if that
+    summary was taken on the current attention kernel source, else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{kind}_{workload}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -62,10 +62,33 @@ def _traffic_from_profile(workload: str):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-    if kv.get("attn_source_sha256") != sha:
+    return kv if kv.get("attn_source_sha256") == sha else None
+
+
+def _traffic_from_profile(workload: str):
+    """HBM bytes per attention launch from the committed PMC summary, if it
+    was taken on the current kernel source; otherwise None."""
+    kv = _profile_kv("hbm_traffic", workload)
+    try:
+        return float(kv["hbm_bytes_per_launch"]) if kv else None
+    except (KeyError, ValueError):
+        return None
+
+
+def _mfma_util_from_profile(workload: str, attn_ms: float, achieved: float, flops: float):
+    """MFMA busy share and the clock-adjusted peak fraction from the committed
+    counter summary (current kernel source only): the kernel's active GPU
+    cycles divided by this run's launch time give the clock it ran at."""
+    kv = _profile_kv("mfma_util", workload)
+    if not kv:
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        cycles = float(kv["active_cycles_per_xcd"])
+        clock_ghz = cycles / (attn_ms * 1e-3) / 1e9
+        return {"mfma_busy_frac": float(kv["mfma_busy_frac"]),
+                "useful_of_issued_flops": round(flops / float(kv["issued_flops"]), 4),
+                "clock_ghz": round(clock_ghz, 3),
+                "frac_clock_adjusted": round(achieved / (PEAK_BF16_TFLOPS * clock_ghz / 2.4), 4)}
     except (KeyError, ValueError):
         return None
 
@@ -179,9 +202,10 @@ def main() -> int:
     for h in handles:
         lib.rk_plan_destroy(h)
     ms_step = (t1 - t0) * 1e3 / args.steps
-    plan_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    rope_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    # per-stage times: medians over the timed steps
+    plan_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    rope_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    attn_ms = float(np.median([e[2].elapsed_time(e[3]) for e in evs]))
 
     T = wl.total_tokens
     esz = 2 if wl.dtype == "bf16" else 4
@@ -193,6 +217,7 @@ def main() -> int:
     plan_alg_bytes = T * 9 + T * 8 + nt * 5 + nnz_tiles * 5
     achieved = flops / (attn_ms * 1e-3) / 1e12
     traffic = _traffic_from_profile(wl.name)
+    mfma_util = _mfma_util_from_profile(wl.name, attn_ms, achieved, flops)
     n_cand = wl.n_candidates
     out = {
         "metric": METRIC,
@@ -222,7 +247,7 @@ def main() -> int:
         "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "alg_bytes": attn_alg_bytes},
+                     "alg_bytes": attn_alg_bytes, "mfma_util": mfma_util},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
