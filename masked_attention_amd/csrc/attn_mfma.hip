@@ -211,29 +211,27 @@ __device__ __forceinline__ void mask_tile(f32x16& s0, f32x16& s1, int kt, int hh
   }
 }
 
-// S^T = K Q^T for the wave's 32 queries.
+// S^T = K Q^T + c for the wave's 32 queries (c: initial accumulator).
 __device__ __forceinline__ void scores(f32x16& s0, f32x16& s1, const unsigned short* kb,
-                                       const bf16x8 (&q)[4], int li, int hh) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+                                       const bf16x8 (&q)[4], const f32x16& c, int li, int hh) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int cc = 2 * s + hh;  // logical chunk: d = 16 s + 8 hh .. +7
     const bf16x8 k0 = as_bf16x8(*(const uint4*)&kb[li * 64 + 8 * (cc ^ kswz(li))]);
     const bf16x8 k1 = as_bf16x8(*(const uint4*)&kb[(32 + li) * 64 + 8 * (cc ^ kswz(32 + li))]);
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[s], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[s], s == 0 ? c : s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s == 0 ? c : s1, 0, 0, 0);
   }
 }
 
-// P = exp2((S - m) * mul) (mul only when kScale), packed to bf16 as the B
-// operands of the PV product (step s: accumulator block s/2, registers
-// 8 (s%2)..+7).  S is left as it is.  Returns the lane's sum of the fp32
-// values (plain adds: they issue alongside the matrix cores, unlike the
-// packed-bf16 dot products).
-template <bool kScale>
+// P = exp2((S - sh) * mul) (sh only when kShift, mul only when kScale),
+// packed to bf16 as the B operands of the PV product (step s: accumulator
+// block s/2, registers 8 (s%2)..+7).  S is left as it is.  Returns the
+// lane's sum of the fp32 values (plain adds: they issue alongside the
+// matrix cores, unlike the packed-bf16 dot products).
+template <bool kShift, bool kScale>
 __device__ __forceinline__ float probs(bf16x8 (&pb)[4], const f32x16& s0, const f32x16& s1,
-                                       float m, float mul) {
+                                       float sh, float mul) {
   float sum0 = 0.f, sum1 = 0.f;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -242,7 +240,8 @@ __device__ __forceinline__ float probs(bf16x8 (&pb)[4], const f32x16& s0, const 
     bf16x2_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float x0 = src[r0 + 2 * j] - m, x1 = src[r0 + 2 * j + 1] - m;
+      float x0 = src[r0 + 2 * j], x1 = src[r0 + 2 * j + 1];
+      if (kShift) { x0 -= sh; x1 -= sh; }
       if (kScale) { x0 *= mul; x1 *= mul; }
       const float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
       w[j][0] = (__bf16)p0;
@@ -268,23 +267,26 @@ __device__ __forceinline__ bool row_sees(int kt, bool partial, int lo, int hi, i
 // kPreScaled (Q carries scale * log2(e)); otherwise they are raw dot
 // products and mul = scale * log2(e) is applied before exp2.
 //
-// P is taken against the row's reference m = mref (0 while the row is
-// fresh: mref = -inf, no visible key seen yet) without a per-tile max.  The
-// wave re-derives the reference from this tile's scores instead when a
-// lane's tile sum leaves [0, 2^32] (or is not a number), or when a fresh
-// row sees a key of this tile: m moves up by the tile's excess over it (O
-// and l rescaled), or to the tile's max for a fresh row.
+// The QK product starts from negm, which holds -m for the lane's row in
+// all 16 registers: m = mref, or 0 while the row is fresh (mref = -inf: no
+// visible key seen yet), so the fast path takes P = exp2(S) as it comes
+// out of the matrix core.  The wave re-derives the reference from this
+// tile's shifted scores instead when a lane's tile sum leaves [0, 2^32]
+// (or is not a number), or when a fresh row sees a key of this tile: m
+// moves up by the tile's excess over it (O and l rescaled), or to the
+// tile's max for a fresh row.
 template <bool kPreScaled>
-__device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, float& mref, float& lsum,
-                                          const unsigned short* kb, const unsigned short* vb,
-                                          const bf16x8 (&q)[4], int kt, bool partial, int li,
-                                          int hh, int lo, int hi, int self, int row, float mul) {
+__device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, float& mref,
+                                          float& lsum, const unsigned short* kb,
+                                          const unsigned short* vb, const bf16x8 (&q)[4], int kt,
+                                          bool partial, int li, int hh, int lo, int hi, int self,
+                                          int row, float mul) {
   f32x16 s0, s1;
-  scores(s0, s1, kb, q, li, hh);
+  scores(s0, s1, kb, q, negm, li, hh);
   if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
   bf16x8 pb[4];
+  float ts = probs<false, !kPreScaled>(pb, s0, s1, 0.f, mul);
   const bool fresh = mref == -INFINITY;
-  float ts = probs<!kPreScaled>(pb, s0, s1, fresh ? 0.f : mref, mul);
   if (__any(!(ts <= kMaxTileSum) || (fresh && row_sees(kt, partial, lo, hi, self, row)))) {
     float mx = s0[0];
 #pragma unroll
@@ -292,16 +294,24 @@ __device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, float& mref, f
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float sh;
     if (fresh) {
+      sh = mx == -INFINITY ? 0.f : mx;
       mref = mx;  // stays -inf when nothing of this tile is visible
-    } else if (mx > mref) {
-      const float alpha = __builtin_amdgcn_exp2f(kPreScaled ? mref - mx : (mref - mx) * mul);
-      lsum *= alpha;
+    } else {
+      sh = fmaxf(mx, 0.f);
+      if (sh > 0.f) {
+        const float alpha = __builtin_amdgcn_exp2f(kPreScaled ? -sh : -sh * mul);
+        lsum *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { o0[r] *= alpha; o1[r] *= alpha; }
-      mref = mx;
+        for (int r = 0; r < 16; ++r) { o0[r] *= alpha; o1[r] *= alpha; }
+      }
+      mref += sh;
     }
-    ts = probs<!kPreScaled>(pb, s0, s1, mref == -INFINITY ? 0.f : mref, mul);
+    const float nm = mref == -INFINITY ? 0.f : -mref;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = nm;
+    ts = probs<true, !kPreScaled>(pb, s0, s1, sh, mul);
   }
   lsum += ts;
 
@@ -392,9 +402,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   const unsigned kst_b = (unsigned)A.k_st * 2u, vst_b = (unsigned)A.v_st * 2u;
   const CopyMap cm = copy_map(wv, lane, kst_b, vst_b);
 
-  f32x16 o0, o1;
+  f32x16 o0, o1, negm;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) { o0[r] = 0.f; o1[r] = 0.f; }
+  for (int r = 0; r < 16; ++r) { o0[r] = 0.f; o1[r] = 0.f; negm[r] = 0.f; }
   float mref = -INFINITY, lsum = 0.f;
 
   const int e0 = ldc(P.qtile_ptr, qg);
@@ -417,7 +427,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
     {
       const int w_nxt = ldc(P.ktile_word, e0 + min(it + 1, n - 1));
       tile_copy(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
-      tile_step<kPreScaled>(o0, o1, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0,
+      tile_step<kPreScaled>(o0, o1, negm, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0,
                             li, hh, lo, hi, self, row, sl2);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -426,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
     if (it + 1 < n) {
       const int w_nxt = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
       tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
-      tile_step<kPreScaled>(o0, o1, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0,
+      tile_step<kPreScaled>(o0, o1, negm, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0,
                             li, hh, lo, hi, self, row, sl2);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
