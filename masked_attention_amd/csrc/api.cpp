@@ -183,12 +183,31 @@ rk::RopeTab make_tab(const rk_rope_params* r, int d) {
 
 size_t elem_size(rk_dtype dt) { return dt == RK_F32 ? 4 : 2; }
 
+// An enum argument as the int the (C or ctypes) caller stored.  Values
+// outside the enumerators are not valid C++ enum values, so validation reads
+// the representation instead of the enum.
+template <typename E>
+int enum_int(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+bool valid_dtype(const rk_dtype& dt) {
+  const int v = enum_int(dt);
+  return v == RK_F32 || v == RK_BF16;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* rk_status_string(rk_status s) {
-  switch (s) {
+  // C and ctypes callers may pass any int; read its representation rather
+  // than the enum value (values outside the enumerators are not valid C++
+  // enum values).
+  switch (enum_int(s)) {
     case RK_OK: return "ok";
     case RK_ERR_INVALID_ARG: return "invalid argument";
     case RK_ERR_SEGMENT_ORDER: return "segment kinds out of order or out of range";
@@ -349,7 +368,7 @@ rk_status rk_time_rope(const rk_batch* b, const rk_rope_params* r, const void* x
   rk_status st = check_batch(b);
   if (st != RK_OK) return st;
   if ((st = check_rope(r)) != RK_OK) return st;
-  if (dtype != RK_F32 && dtype != RK_BF16) return RK_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return RK_ERR_INVALID_ARG;
   if (num_heads < 1 || d_head < 2) return RK_ERR_INVALID_ARG;
   if ((d_head & 1) || d_head > 2 * rk::kMaxHalfD) return RK_ERR_UNSUPPORTED;
   if (in_stride_tok < 0 || in_stride_head < 0 || out_stride_tok < 0 || out_stride_head < 0)
@@ -369,7 +388,7 @@ namespace {
 
 rk_status check_attn(const rk_plan* p, const rk_attn_args* a) {
   if (!p || !a || a->struct_size < sizeof(rk_attn_args)) return RK_ERR_INVALID_ARG;
-  if (a->dtype != RK_F32 && a->dtype != RK_BF16) return RK_ERR_INVALID_ARG;
+  if (!valid_dtype(a->dtype)) return RK_ERR_INVALID_ARG;
   if (a->num_heads != p->H) return RK_ERR_INVALID_ARG;
   if (a->d_head != 32 && a->d_head != 64 && a->d_head != 128) return RK_ERR_UNSUPPORTED;
   if (a->flags & ~(RK_ATTN_REFERENCE_KERNEL | RK_ATTN_K_PREROTATED)) return RK_ERR_INVALID_ARG;

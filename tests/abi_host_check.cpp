@@ -1,0 +1,191 @@
+// Host-side checks of the C ABI, built with AddressSanitizer and
+// UndefinedBehaviorSanitizer against a library whose host code carries the
+// same instrumentation (tests/test_abi_sanitizers.py builds and runs it).
+// Every call here returns from argument validation before any HIP call, so
+// no GPU is needed; a sanitizer report or a wrong status fails the run.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "rk.h"
+
+static int failures = 0;
+
+#define EXPECT(cond)                                                       \
+  do {                                                                     \
+    if (!(cond)) {                                                         \
+      std::fprintf(stderr, "FAIL %s:%d: %s\n", __FILE__, __LINE__, #cond); \
+      ++failures;                                                          \
+    }                                                                      \
+  } while (0)
+
+// Device pointers are never dereferenced by the validation paths: any
+// non-null value stands in for them.
+static void* fake(uintptr_t a) { return reinterpret_cast<void*>(a); }
+
+static rk_batch make_batch(const std::vector<int32_t>& offs, int32_t total) {
+  rk_batch b;
+  std::memset(&b, 0, sizeof(b));
+  b.struct_size = sizeof(rk_batch);
+  b.num_requests = (int32_t)offs.size() - 1;
+  b.total_tokens = total;
+  b.req_offsets_host = offs.data();
+  b.req_offsets_dev = static_cast<const int32_t*>(fake(0x1000));
+  b.seg_kind_dev = static_cast<const uint8_t*>(fake(0x2000));
+  b.timestamps_dev = static_cast<const int64_t*>(fake(0x3000));
+  b.anchors_dev = static_cast<const int64_t*>(fake(0x4000));
+  return b;
+}
+
+static void check_status_strings() {
+  EXPECT(rk_abi_version() == RK_ABI_VERSION);
+  for (int s = 0; s <= 6; ++s) EXPECT(std::strlen(rk_status_string((rk_status)s)) > 0);
+  EXPECT(rk_status_string((rk_status)99) != nullptr);
+}
+
+static void check_workspace_size() {
+  size_t n = 0;
+  std::vector<int32_t> offs = {0, 10, 10, 300};
+  rk_batch b = make_batch(offs, 300);
+  EXPECT(rk_plan_workspace_size(&b, 4, &n) == RK_OK);
+  EXPECT(n > 0 && n % 256 == 0);
+  // a large batch: 64 requests of 20001 tokens
+  std::vector<int32_t> big(65);
+  for (int i = 0; i <= 64; ++i) big[i] = 20001 * i;
+  rk_batch bb = make_batch(big, big.back());
+  EXPECT(rk_plan_workspace_size(&bb, 8, &n) == RK_OK);
+  EXPECT(n >= (size_t)64 * 157 * 313 * 10);
+  // bad offsets
+  std::vector<int32_t> o1 = {1, 10}, o2 = {0, 10, 5}, o3 = {0, 10, 20};
+  rk_batch b1 = make_batch(o1, 10), b2 = make_batch(o2, 5), b3 = make_batch(o3, 19);
+  EXPECT(rk_plan_workspace_size(&b1, 4, &n) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_plan_workspace_size(&b2, 4, &n) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_plan_workspace_size(&b3, 4, &n) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_plan_workspace_size(&b, 0, &n) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_plan_workspace_size(nullptr, 1, &n) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_plan_workspace_size(&b, 1, nullptr) == RK_ERR_INVALID_ARG);
+  rk_batch b4 = b;
+  b4.struct_size = 8;
+  EXPECT(rk_plan_workspace_size(&b4, 1, &n) == RK_ERR_INVALID_ARG);
+  rk_batch b5 = b;
+  b5.seg_kind_dev = nullptr;
+  EXPECT(rk_plan_workspace_size(&b5, 1, &n) == RK_ERR_INVALID_ARG);
+  rk_batch b6 = b;
+  b6.req_offsets_host = nullptr;
+  EXPECT(rk_plan_workspace_size(&b6, 1, &n) == RK_ERR_INVALID_ARG);
+  rk_batch b7 = make_batch(offs, 300);
+  b7.num_requests = -1;
+  EXPECT(rk_plan_workspace_size(&b7, 1, &n) == RK_ERR_INVALID_ARG);
+}
+
+static void check_mask_plan() {
+  std::vector<int32_t> offs = {0, 100, 300};
+  rk_batch b = make_batch(offs, 300);
+  size_t n = 0;
+  EXPECT(rk_plan_workspace_size(&b, 2, &n) == RK_OK);
+  rk_mask_params m;
+  std::memset(&m, 0, sizeof(m));
+  m.struct_size = sizeof(m);
+  m.delay = 3600;
+  rk_plan* h = nullptr;
+  EXPECT(rk_mask_plan(&b, &m, 2, fake(1 << 20), n - 256, &h, nullptr) ==
+         RK_ERR_WORKSPACE_TOO_SMALL);
+  EXPECT(h == nullptr);
+  EXPECT(rk_mask_plan(&b, &m, 2, fake((1 << 20) + 8), n, &h, nullptr) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_mask_plan(&b, &m, 2, nullptr, n, &h, nullptr) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_mask_plan(&b, nullptr, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_mask_plan(&b, &m, 2, fake(1 << 20), n, nullptr, nullptr) == RK_ERR_INVALID_ARG);
+  rk_mask_params bad = m;
+  bad.delay = -1;
+  EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
+  bad = m;
+  bad.window = -3;
+  EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
+  bad = m;
+  bad.flags = 4;
+  EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
+  bad = m;
+  bad.struct_size = 4;
+  EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
+}
+
+static void check_time_rope() {
+  std::vector<int32_t> offs = {0, 100};
+  rk_batch b = make_batch(offs, 100);
+  rk_rope_params r;
+  std::memset(&r, 0, sizeof(r));
+  r.struct_size = sizeof(r);
+  r.phi_min = 1e-4;
+  r.dt_max = 31536000.0;
+  r.base = 6e5;
+  void* x = fake(1 << 20);
+  void* y = fake(1 << 21);
+  EXPECT(rk_time_rope(&b, &r, x, y, RK_BF16, 2, 63, 128, 64, 128, 64, nullptr) ==
+         RK_ERR_UNSUPPORTED);
+  EXPECT(rk_time_rope(&b, &r, x, y, RK_BF16, 2, 256, 512, 256, 512, 256, nullptr) ==
+         RK_ERR_UNSUPPORTED);
+  EXPECT(rk_time_rope(&b, &r, x, y, RK_BF16, 0, 64, 128, 64, 128, 64, nullptr) ==
+         RK_ERR_INVALID_ARG);
+  EXPECT(rk_time_rope(&b, &r, x, y, (rk_dtype)7, 2, 64, 128, 64, 128, 64, nullptr) ==
+         RK_ERR_INVALID_ARG);
+  EXPECT(rk_time_rope(&b, &r, nullptr, y, RK_BF16, 2, 64, 128, 64, 128, 64, nullptr) ==
+         RK_ERR_INVALID_ARG);
+  EXPECT(rk_time_rope(&b, &r, x, y, RK_BF16, 2, 64, -1, 64, 128, 64, nullptr) ==
+         RK_ERR_INVALID_ARG);
+  EXPECT(rk_time_rope(&b, &r, x, x, RK_BF16, 2, 64, 128, 64, 256, 64, nullptr) ==
+         RK_ERR_INVALID_ARG);
+  rk_rope_params bad = r;
+  bad.phi_min = 0.0;
+  EXPECT(rk_time_rope(&b, &bad, x, y, RK_BF16, 2, 64, 128, 64, 128, 64, nullptr) ==
+         RK_ERR_INVALID_ARG);
+  bad = r;
+  bad.base = std::nan("");
+  EXPECT(rk_time_rope(&b, &bad, x, y, RK_BF16, 2, 64, 128, 64, 128, 64, nullptr) ==
+         RK_ERR_INVALID_ARG);
+  EXPECT(rk_time_rope(nullptr, &r, x, y, RK_BF16, 2, 64, 128, 64, 128, 64, nullptr) ==
+         RK_ERR_INVALID_ARG);
+}
+
+static void check_attention_without_plan() {
+  rk_attn_args a;
+  std::memset(&a, 0, sizeof(a));
+  a.struct_size = sizeof(a);
+  a.dtype = RK_BF16;
+  a.num_heads = 1;
+  a.d_head = 64;
+  size_t n = 0;
+  EXPECT(rk_masked_attn_fwd(nullptr, &a, nullptr) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_attn_workspace_size(nullptr, &a, &n) == RK_ERR_INVALID_ARG);
+  rk_plan_totals t;
+  std::memset(&t, 0, sizeof(t));
+  t.struct_size = sizeof(t);
+  EXPECT(rk_plan_stats(nullptr, &t, nullptr) == RK_ERR_INVALID_ARG);
+  rk_plan_info info;
+  std::memset(&info, 0, sizeof(info));
+  info.struct_size = sizeof(info);
+  EXPECT(rk_plan_get_info(nullptr, &info) == RK_ERR_INVALID_ARG);
+  rk_plan_destroy(nullptr);
+}
+
+int main(int argc, char** argv) {
+  if (argc > 1 && std::strcmp(argv[1], "--self-test") == 0) {
+    // proves the instrumentation is live: AddressSanitizer must stop here
+    volatile int* p = new int[4];
+    p[4] = 1;
+    delete[] p;
+    return 0;
+  }
+  check_status_strings();
+  check_workspace_size();
+  check_mask_plan();
+  check_time_rope();
+  check_attention_without_plan();
+  if (failures) {
+    std::fprintf(stderr, "%d check(s) failed\n", failures);
+    return 1;
+  }
+  std::printf("abi host checks passed\n");
+  return 0;
+}
