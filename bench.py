@@ -45,6 +45,10 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4,
                     help="oracle sample: request 0 with this many heads")
+    ap.add_argument("--candidates-only", action="store_true",
+                    help="serving step: the history keys are rotated once before timing; each "
+                         "step plans the candidates' query tiles only, rotates the candidate "
+                         "keys into the key cache and runs the attention for those tiles")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter scaling)")
     return ap.parse_args()
@@ -151,12 +155,26 @@ def main() -> int:
                        static_bidirectional=wl.static_bidirectional, num_heads=H, workspace=ws)
     stats = ref_plan.stats()
     pairs = stats["visible_pairs"]
+    if args.candidates_only:
+        # useful work of a serving step: the candidate rows' visible pairs
+        rd = ref_plan.row_desc().to(torch.int64)
+        lo, hi_raw = rd[:, 0], rd[:, 1]
+        self_bit = hi_raw < 0
+        hi = hi_raw & 0x7FFFFFFF
+        cand = batch.seg_kind == _rk.RK_SEG_CANDIDATE
+        pairs = int(((hi - lo).clamp(min=0) + self_bit.to(torch.int64))[cand].sum().item())
+        # history (and profile / real-time) keys rotated once, outside the timed steps
+        rk.rk_time_rope(batch, k, out=krot, **rope)
     flops = 4.0 * d * H * pairs
 
     # raw C arguments, built once
     mp = _rk.sized(_rk.rk_mask_params, delay=wl.delay, window=wl.window,
-                   flags=_rk.RK_STATIC_BIDIRECTIONAL if wl.static_bidirectional else 0)
+                   flags=(_rk.RK_STATIC_BIDIRECTIONAL if wl.static_bidirectional else 0) | (
+                       _rk.RK_QUERY_CANDIDATES_ONLY if args.candidates_only else 0))
     rp = rk.binding.rope_params(**rope)
+    # the step's rotation: every key, or only the candidate keys into the cache
+    rp_step = rk.binding.rope_params(
+        **rope, kinds=(1 << _rk.RK_SEG_CANDIDATE) if args.candidates_only else 0)
     stream = torch.cuda.current_stream()
     sp = C.c_void_p(stream.cuda_stream)
     dcode = _rk.RK_BF16 if wl.dtype == "bf16" else _rk.RK_F32
@@ -174,7 +192,7 @@ def main() -> int:
         _rk.check(lib.rk_mask_plan(C.byref(batch.c), C.byref(mp), H, C.c_void_p(ws.data_ptr()),
                                    C.c_size_t(ws.numel()), C.byref(h), sp), "rk_mask_plan")
         if ev: ev[1].record(stream)
-        _rk.check(lib.rk_time_rope(C.byref(batch.c), C.byref(rp), C.c_void_p(k.data_ptr()),
+        _rk.check(lib.rk_time_rope(C.byref(batch.c), C.byref(rp_step), C.c_void_p(k.data_ptr()),
                                    C.c_void_p(krot.data_ptr()), dcode, H, d, H * d, d, H * d, d,
                                    sp), "rk_time_rope")
         if ev: ev[2].record(stream)
@@ -210,14 +228,16 @@ def main() -> int:
     T = wl.total_tokens
     esz = 2 if wl.dtype == "bf16" else 4
     attn_alg_bytes = T * H * 4 * d * esz + T * 8            # Q, K, V read + O written, times
-    rope_alg_bytes = T * H * 2 * d * esz + T * 8 + wl.num_requests * 8
+    n_rot = int((batch.seg_kind == _rk.RK_SEG_CANDIDATE).sum().item()) if args.candidates_only else T
+    rope_alg_bytes = n_rot * H * 2 * d * esz + n_rot * 8 + wl.num_requests * 8
     nt = int(ref_plan.info.num_tiles)
     nnz_tiles = int(ref_plan.qtile_ptr()[-1].item()) if ref_plan.num_qtiles else 0
     # kind + time read, row descriptor written, class + count per tile, CSR index + class
     plan_alg_bytes = T * 9 + T * 8 + nt * 5 + nnz_tiles * 5
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    traffic = _traffic_from_profile(wl.name)
-    mfma_util = _mfma_util_from_profile(wl.name, attn_ms, achieved, flops)
+    wname = wl.name + (" candidates-only" if args.candidates_only else "")
+    traffic = _traffic_from_profile(wname)
+    mfma_util = _mfma_util_from_profile(wname, attn_ms, achieved, flops)
     n_cand = wl.n_candidates
     out = {
         "metric": METRIC,
@@ -232,7 +252,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded generator with the workload's shapes and time law)",
-        "config": {"workload": wl.name, "requests": wl.num_requests, "tokens": T, "heads": H,
+        "config": {"workload": wname,
+                   "requests": wl.num_requests, "tokens": T, "heads": H,
                    "d_head": d, "visible_pairs_per_head": pairs, "candidates": n_cand,
                    "delay_s": wl.delay, "window": wl.window,
                    "static_bidirectional": wl.static_bidirectional},

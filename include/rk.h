@@ -98,6 +98,16 @@ enum { RK_TILE_EMPTY = 0, RK_TILE_PARTIAL = 1, RK_TILE_FULL = 2 };
 
 /* rk_mask_params.flags */
 #define RK_STATIC_BIDIRECTIONAL 0x1u /* PROFILE+HISTORY mutually visible (MTGR static part) */
+#define RK_QUERY_CANDIDATES_ONLY 0x2u /* serving call (HSTU, App. H, M-FALCON): the launch
+                                         schedule covers only the query tiles that hold at
+                                         least one CANDIDATE row, so rk_masked_attn_fwd
+                                         writes O / LSE rows of those tiles only (rows
+                                         elsewhere are left as they were).  Masks, tile
+                                         classes, counts, CSR and totals are those of the
+                                         whole batch. */
+
+/* Segment-kind bits of rk_rope_params.kinds: bit k selects kind k. */
+#define RK_KIND_BIT(k) (1u << (k))
 
 /* rk_attn_args.flags */
 #define RK_ATTN_REFERENCE_KERNEL 0x1u /* force the plain (non-MFMA) kernel */
@@ -148,7 +158,12 @@ typedef struct rk_mask_params {
  * dt_max is in timestamp units (1 year = 31,536,000 s on the page). */
 typedef struct rk_rope_params {
   uint32_t struct_size;
-  uint32_t reserved;
+  uint32_t kinds; /* rk_time_rope only: rotate tokens whose segment kind k has
+                     RK_KIND_BIT(k) set, leave the other rows of x_out as they
+                     were; 0 = every token.  Must be 0 in rk_attn_args.rope.
+                     A serving call rotates the CANDIDATE keys into a buffer
+                     whose history keys were rotated once before (HSTU,
+                     App. H: history K/V cached across candidate batches). */
   double phi_min; /* > 0 */
   double dt_max;  /* > 0 */
   double base;    /* > 0 */

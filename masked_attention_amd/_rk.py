@@ -27,6 +27,7 @@ RK_SEG_PROFILE, RK_SEG_HISTORY, RK_SEG_REALTIME, RK_SEG_CANDIDATE = 0, 1, 2, 3
 RK_TILE_EMPTY, RK_TILE_PARTIAL, RK_TILE_FULL = 0, 1, 2
 RK_TILE_Q, RK_TILE_K = 128, 64
 RK_STATIC_BIDIRECTIONAL = 0x1
+RK_QUERY_CANDIDATES_ONLY = 0x2
 RK_ATTN_REFERENCE_KERNEL = 0x1
 RK_ATTN_K_PREROTATED = 0x2
 RK_ABI_VERSION = 1
@@ -58,7 +59,7 @@ class rk_mask_params(C.Structure):
 class rk_rope_params(C.Structure):
     _fields_ = [
         ("struct_size", C.c_uint32),
-        ("reserved", C.c_uint32),
+        ("kinds", C.c_uint32),
         ("phi_min", C.c_double),
         ("dt_max", C.c_double),
         ("base", C.c_double),

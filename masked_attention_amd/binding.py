@@ -30,9 +30,9 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def rope_params(phi_min: float, dt_max: float, base: float) -> _rk.rk_rope_params:
+def rope_params(phi_min: float, dt_max: float, base: float, kinds: int = 0) -> _rk.rk_rope_params:
     return sized(_rk.rk_rope_params, phi_min=float(phi_min), dt_max=float(dt_max),
-                 base=float(base))
+                 base=float(base), kinds=int(kinds))
 
 
 class Batch:
@@ -70,6 +70,7 @@ class Plan:
 
     def __init__(self, batch: Batch, *, delay: int = 0, window: int = 0,
                  static_bidirectional: bool = False, num_heads: int = 1,
+                 candidates_only: bool = False,
                  stream: Optional[torch.cuda.Stream] = None,
                  workspace: Optional[torch.Tensor] = None):
         self.batch = batch
@@ -78,8 +79,9 @@ class Plan:
         if workspace is None:
             workspace = torch.empty(max(size, 256), dtype=torch.uint8, device=batch.seg_kind.device)
         self.workspace = workspace
-        self.params = sized(_rk.rk_mask_params, delay=int(delay), window=int(window),
-                            flags=_rk.RK_STATIC_BIDIRECTIONAL if static_bidirectional else 0)
+        flags = (_rk.RK_STATIC_BIDIRECTIONAL if static_bidirectional else 0) | (
+            _rk.RK_QUERY_CANDIDATES_ONLY if candidates_only else 0)
+        self.params = sized(_rk.rk_mask_params, delay=int(delay), window=int(window), flags=flags)
         h = C.c_void_p()
         check(lib().rk_mask_plan(C.byref(batch.c), C.byref(self.params), self.num_heads,
                                  C.c_void_p(workspace.data_ptr()),
@@ -150,14 +152,19 @@ def rk_mask_plan(batch: Batch, **kw) -> Plan:
 
 
 def rk_time_rope(batch: Batch, x: torch.Tensor, *, phi_min: float, dt_max: float, base: float,
-                 out: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, kinds=None,
                  stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """Rotate x [T, H, d] (d contiguous) by time RoPE into out (default: new tensor)."""
+    """Rotate x [T, H, d] (d contiguous) by time RoPE into out (default: new tensor).
+
+    kinds: None (every token) or an iterable of segment kinds (RK_SEG_*): only
+    tokens of those kinds are rotated, the other rows of out are left as they
+    were (so out should be given)."""
     if x.dim() != 3 or x.stride(2) != 1:
         raise ValueError("x must be [T, H, d] with d contiguous")
     if out is None:
         out = torch.empty_like(x, memory_format=torch.contiguous_format)
-    rp = rope_params(phi_min, dt_max, base)
+    mask = 0 if kinds is None else sum(1 << int(k) for k in set(kinds))
+    rp = rope_params(phi_min, dt_max, base, kinds=mask)
     check(lib().rk_time_rope(C.byref(batch.c), C.byref(rp), C.c_void_p(x.data_ptr()),
                              C.c_void_p(out.data_ptr()), _dtype_code(x), x.shape[1], x.shape[2],
                              x.stride(0), x.stride(1), out.stride(0), out.stride(1), _stream(stream)),

@@ -166,6 +166,7 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
 
 rk_status check_rope(const rk_rope_params* r) {
   if (!r || r->struct_size < sizeof(rk_rope_params)) return RK_ERR_INVALID_ARG;
+  if (r->kinds & ~0xfu) return RK_ERR_INVALID_ARG;  // four segment kinds
   if (!(std::isfinite(r->phi_min) && std::isfinite(r->dt_max) && std::isfinite(r->base)))
     return RK_ERR_INVALID_ARG;
   if (!(r->phi_min > 0 && r->dt_max > 0 && r->base > 0)) return RK_ERR_INVALID_ARG;
@@ -235,7 +236,9 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   if (!plan_out) return RK_ERR_INVALID_ARG;
   *plan_out = nullptr;
   if (!m || m->struct_size < sizeof(rk_mask_params)) return RK_ERR_INVALID_ARG;
-  if (m->delay < 0 || m->window < 0 || (m->flags & ~RK_STATIC_BIDIRECTIONAL)) return RK_ERR_INVALID_ARG;
+  if (m->delay < 0 || m->window < 0 ||
+      (m->flags & ~(RK_STATIC_BIDIRECTIONAL | RK_QUERY_CANDIDATES_ONLY)))
+    return RK_ERR_INVALID_ARG;
   Layout L;
   rk_status st = make_layout(b, num_heads, true, &L);
   if (st != RK_OK) return st;
@@ -378,9 +381,10 @@ rk_status rk_time_rope(const rk_batch* b, const rk_rope_params* r, const void* x
     return RK_ERR_INVALID_ARG;
   const rk::RopeTab tab = make_tab(r, d_head);
   hipError_t e = rk::launch_rope(b->num_requests, b->total_tokens, b->req_offsets_dev,
-                                 b->timestamps_dev, b->anchors_dev, tab, x_in, x_out, dtype,
-                                 num_heads, d_head, in_stride_tok, in_stride_head, out_stride_tok,
-                                 out_stride_head, (hipStream_t)stream);
+                                 b->timestamps_dev, b->anchors_dev, b->seg_kind_dev, r->kinds, tab,
+                                 x_in, x_out, dtype, num_heads, d_head, in_stride_tok,
+                                 in_stride_head, out_stride_tok, out_stride_head,
+                                 (hipStream_t)stream);
   return e == hipSuccess ? RK_OK : RK_ERR_HIP;
 }
 
@@ -402,6 +406,7 @@ rk_status check_attn(const rk_plan* p, const rk_attn_args* a) {
   if (a->rope) {
     rk_status s = check_rope(a->rope);
     if (s != RK_OK) return s;
+    if (a->rope->kinds != 0) return RK_ERR_INVALID_ARG;  // the attention rotates every row
   }
   return RK_OK;
 }
@@ -481,7 +486,8 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
     // by the attention kernel while it is staged.
     const int64_t hd = (int64_t)a->num_heads * a->d_head;
     hipError_t e = rk::launch_rope(p->R, p->T, p->req_offsets_dev, p->timestamps_dev,
-                                   p->anchors_dev, L.tab, a->k, a->workspace, a->dtype,
+                                   p->anchors_dev, p->seg_kind_dev, 0u, L.tab, a->k, a->workspace,
+                                   a->dtype,
                                    a->num_heads, a->d_head, a->k_stride_tok, a->k_stride_head, hd,
                                    a->d_head, s);
     if (e != hipSuccess) return RK_ERR_HIP;

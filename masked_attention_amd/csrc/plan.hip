@@ -276,8 +276,11 @@ __global__ __launch_bounds__(256) void plan_qsort_kernel(PlanDev P) {
 }
 
 // One thread per launch slot: slot s runs on XCD s % 8 as item s / 8 of
-// that XCD's queue.
-__global__ void plan_sched_kernel(PlanDev P, int64_t slots, int H) {
+// that XCD's queue.  With cand_only, a query tile without a CANDIDATE row
+// gets no work (-1): candidates are the last segment of a request, so the
+// tiles kept are the ones from the tile of the first candidate on, which
+// within a group come first in the descending-work order.
+__global__ void plan_sched_kernel(PlanDev P, int64_t slots, int H, int cand_only) {
   const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= slots) return;
   const int q = (int)(s % kNumXcd);
@@ -293,8 +296,12 @@ __global__ void plan_sched_kernel(PlanDev P, int64_t slots, int H) {
     const Group grp = P.groups[a];
     const int k = idx - grp.base;
     if (k >= 0 && k < grp.count) {
-      const int qg = P.qorder[P.req[grp.req].qt_off + k];
-      item = qg * H + grp.head;
+      const ReqMeta m = P.req[grp.req];
+      const int qg = P.qorder[m.qt_off + k];
+      const int first_cand = m.seg[RK_SEG_CANDIDATE];  // == len without candidates
+      const bool keep = !cand_only || (first_cand < m.len &&
+                                       (qg - m.qt_off + 1) * kTileQ > first_cand);
+      if (keep) item = qg * H + grp.head;
     }
   }
   P.sched[s] = item;
@@ -323,7 +330,7 @@ hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
   }
   if (p->slots > 0) {
     hipLaunchKernelGGL(plan_sched_kernel, dim3((unsigned)((p->slots + 255) / 256)), dim3(256), 0, s,
-                       P, p->slots, p->H);
+                       P, p->slots, p->H, (int)((p->flags & RK_QUERY_CANDIDATES_ONLY) != 0));
   }
   return hipGetLastError();
 }

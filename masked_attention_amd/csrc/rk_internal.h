@@ -107,10 +107,12 @@ struct RopeTab {
 
 // ---- launchers (defined in the .hip files); return hipSuccess or an error
 hipError_t launch_plan(const rk_plan* p, hipStream_t s);
+// kinds: rotate only tokens whose segment kind k has bit k set (0 = all).
 hipError_t launch_rope(int32_t R, int32_t T, const int32_t* req_offsets, const int64_t* ts,
-                       const int64_t* anchors, const RopeTab& tab, const void* x_in, void* x_out,
-                       rk_dtype dt, int H, int d, int64_t in_st, int64_t in_sh, int64_t out_st,
-                       int64_t out_sh, hipStream_t s);
+                       const int64_t* anchors, const uint8_t* kind, unsigned kinds,
+                       const RopeTab& tab, const void* x_in, void* x_out, rk_dtype dt, int H, int d,
+                       int64_t in_st, int64_t in_sh, int64_t out_st, int64_t out_sh,
+                       hipStream_t s);
 
 struct AttnLaunch {
   const void* q;

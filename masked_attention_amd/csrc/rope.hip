@@ -31,11 +31,18 @@ __device__ __forceinline__ void store_pair(__hip_bfloat16* p, float a, float b) 
   *(unsigned*)p = (unsigned)f2bf(a) | ((unsigned)f2bf(b) << 16);
 }
 
+// Is a token of segment kind k among the kinds to rotate (bit k of kinds)?
+__device__ __forceinline__ bool selected(uint8_t k, unsigned kinds) {
+  return k < 4 && ((kinds >> k) & 1u);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kernel(int R, int Tn, const int32_t* __restrict__ offs,
                                                    const int64_t* __restrict__ ts,
                                                    const int64_t* __restrict__ anchors,
-                                                   RopeTab tab, const T* x, T* y, int H, int d,
+                                                   const uint8_t* __restrict__ kind,
+                                                   unsigned kinds, RopeTab tab, const T* x, T* y,
+                                                   int H, int d,
                                                    int64_t ist, int64_t ish, int64_t ost,
                                                    int64_t osh) {
   __shared__ double w[kMaxHalfD];
@@ -46,6 +53,7 @@ __global__ __launch_bounds__(256) void rope_kernel(int R, int Tn, const int32_t*
   if (gid >= (int64_t)Tn * half) return;
   const int tok = (int)(gid / half);
   const int i = (int)(gid - (int64_t)tok * half);
+  if (kinds && !selected(kind[tok], kinds)) return;
   // request of the token: last r with offs[r] <= tok
   int a = 0, b = R;
   while (a < b) {
@@ -73,7 +81,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void rope8_kernel(int R, int Tn, const int32_t* __restrict__ offs,
                                                     const int64_t* __restrict__ ts,
                                                     const int64_t* __restrict__ anchors,
-                                                    RopeTab tab, const T* x, T* y, int H, int d,
+                                                    const uint8_t* __restrict__ kind,
+                                                    unsigned kinds, RopeTab tab, const T* x, T* y,
+                                                    int H, int d,
                                                     int64_t ist, int64_t ish, int64_t ost,
                                                     int64_t osh) {
   __shared__ double w[kMaxHalfD];
@@ -85,6 +95,7 @@ __global__ __launch_bounds__(256) void rope8_kernel(int R, int Tn, const int32_t
   if (gid >= (int64_t)Tn * groups) return;
   const int tok = (int)(gid / groups);
   const int g = (int)(gid - (int64_t)tok * groups);
+  if (kinds && !selected(kind[tok], kinds)) return;
   int a = 0, b = R;
   while (a < b) {
     const int m = (a + b) >> 1;
@@ -139,9 +150,10 @@ __global__ __launch_bounds__(256) void rope8_kernel(int R, int Tn, const int32_t
 }  // namespace
 
 hipError_t launch_rope(int32_t R, int32_t T, const int32_t* req_offsets, const int64_t* ts,
-                       const int64_t* anchors, const RopeTab& tab, const void* x_in, void* x_out,
-                       rk_dtype dt, int H, int d, int64_t in_st, int64_t in_sh, int64_t out_st,
-                       int64_t out_sh, hipStream_t s) {
+                       const int64_t* anchors, const uint8_t* kind, unsigned kinds,
+                       const RopeTab& tab, const void* x_in, void* x_out, rk_dtype dt, int H, int d,
+                       int64_t in_st, int64_t in_sh, int64_t out_st, int64_t out_sh,
+                       hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int64_t v = 16 / (dt == RK_F32 ? 4 : 2);  // elements per 16 bytes
   const bool vec = (d % 8 == 0) && ((uintptr_t)x_in % 16 == 0) && ((uintptr_t)x_out % 16 == 0) &&
@@ -151,11 +163,11 @@ hipError_t launch_rope(int32_t R, int32_t T, const int32_t* req_offsets, const i
     const unsigned blocks = (unsigned)((n + 255) / 256);
     if (dt == RK_F32)
       hipLaunchKernelGGL(rope8_kernel<float>, dim3(blocks), dim3(256), 0, s, R, T, req_offsets, ts,
-                         anchors, tab, (const float*)x_in, (float*)x_out, H, d, in_st, in_sh,
+                         anchors, kind, kinds, tab, (const float*)x_in, (float*)x_out, H, d, in_st, in_sh,
                          out_st, out_sh);
     else
       hipLaunchKernelGGL(rope8_kernel<__hip_bfloat16>, dim3(blocks), dim3(256), 0, s, R, T,
-                         req_offsets, ts, anchors, tab, (const __hip_bfloat16*)x_in,
+                         req_offsets, ts, anchors, kind, kinds, tab, (const __hip_bfloat16*)x_in,
                          (__hip_bfloat16*)x_out, H, d, in_st, in_sh, out_st, out_sh);
     return hipGetLastError();
   }
@@ -163,11 +175,11 @@ hipError_t launch_rope(int32_t R, int32_t T, const int32_t* req_offsets, const i
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (dt == RK_F32) {
     hipLaunchKernelGGL(rope_kernel<float>, dim3(blocks), dim3(256), 0, s, R, T, req_offsets, ts,
-                       anchors, tab, (const float*)x_in, (float*)x_out, H, d, in_st, in_sh, out_st,
+                       anchors, kind, kinds, tab, (const float*)x_in, (float*)x_out, H, d, in_st, in_sh, out_st,
                        out_sh);
   } else {
     hipLaunchKernelGGL(rope_kernel<__hip_bfloat16>, dim3(blocks), dim3(256), 0, s, R, T,
-                       req_offsets, ts, anchors, tab, (const __hip_bfloat16*)x_in,
+                       req_offsets, ts, anchors, kind, kinds, tab, (const __hip_bfloat16*)x_in,
                        (__hip_bfloat16*)x_out, H, d, in_st, in_sh, out_st, out_sh);
   }
   return hipGetLastError();

@@ -106,6 +106,8 @@ static void check_mask_plan() {
   bad = m;
   bad.flags = 4;
   EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
+  bad.flags = RK_QUERY_CANDIDATES_ONLY | 8u;
+  EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
   bad = m;
   bad.struct_size = 4;
   EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
@@ -138,6 +140,10 @@ static void check_time_rope() {
          RK_ERR_INVALID_ARG);
   rk_rope_params bad = r;
   bad.phi_min = 0.0;
+  EXPECT(rk_time_rope(&b, &bad, x, y, RK_BF16, 2, 64, 128, 64, 128, 64, nullptr) ==
+         RK_ERR_INVALID_ARG);
+  bad = r;
+  bad.kinds = RK_KIND_BIT(4);  // only four segment kinds exist
   EXPECT(rk_time_rope(&b, &bad, x, y, RK_BF16, 2, 64, 128, 64, 128, 64, nullptr) ==
          RK_ERR_INVALID_ARG);
   bad = r;

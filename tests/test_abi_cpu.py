@@ -130,7 +130,8 @@ def test_mask_plan_host_errors(lib):
                             C.byref(h), None) == _rk.RK_ERR_INVALID_ARG
     assert lib.rk_mask_plan(C.byref(b), C.byref(m), 2, None, n.value, C.byref(h),
                             None) == _rk.RK_ERR_INVALID_ARG
-    for bad in (dict(delay=-1), dict(window=-3), dict(flags=4)):
+    for bad in (dict(delay=-1), dict(window=-3), dict(flags=4),
+                dict(flags=_rk.RK_QUERY_CANDIDATES_ONLY | 8)):
         mb = _rk.sized(_rk.rk_mask_params, **bad)
         assert lib.rk_mask_plan(C.byref(b), C.byref(mb), 2, C.c_void_p(1 << 20), n.value,
                                 C.byref(h), None) == _rk.RK_ERR_INVALID_ARG
@@ -158,7 +159,7 @@ def test_time_rope_host_errors(lib):
     assert call(args(x=None)) == _rk.RK_ERR_INVALID_ARG
     assert call(args(ist=-1)) == _rk.RK_ERR_INVALID_ARG
     assert call(args(y=C.c_void_p(1 << 20), ost=256)) == _rk.RK_ERR_INVALID_ARG  # in place, strides differ
-    for bad in (dict(phi_min=0.0), dict(dt_max=-1.0), dict(base=float("nan"))):
+    for bad in (dict(phi_min=0.0), dict(dt_max=-1.0), dict(base=float("nan")), dict(kinds=16)):
         rb = _rk.sized(_rk.rk_rope_params, **dict(dict(phi_min=1e-4, dt_max=1.0, base=2.0), **bad))
         assert call(args(r=C.byref(rb))) == _rk.RK_ERR_INVALID_ARG
 
