@@ -39,7 +39,8 @@
  *   key j is a CANDIDATE          : visible iff i == j;
  *   i in S, j in S                : with RK_STATIC_BIDIRECTIONAL always;
  *                                   otherwise p_j <= p_i, and
- *                                   (window == 0 or p_i - p_j < window), and
+ *                                   (window == 0 or p_i - p_j < window or
+ *                                    p_i >= |S| - global_tail), and
  *                                   (delay == 0 or t_j <= t_i - delay);
  *   i in S, j REALTIME            : never;
  *   i REALTIME, j in S            : always;
@@ -146,10 +147,12 @@ typedef struct rk_batch {
 /* Mask parameters (CADET delay mask; SORT / LazFormer window; MTGR static part). */
 typedef struct rk_mask_params {
   uint32_t struct_size;
-  uint32_t flags;  /* RK_STATIC_BIDIRECTIONAL or 0 */
-  int64_t delay;   /* Delta_delay in timestamp units, >= 0; 0 = off */
-  int32_t window;  /* keys kept including self, >= 0; 0 = off */
-  int32_t reserved;
+  uint32_t flags;       /* RK_STATIC_BIDIRECTIONAL, RK_QUERY_CANDIDATES_ONLY or 0 */
+  int64_t delay;        /* Delta_delay in timestamp units, >= 0; 0 = off */
+  int32_t window;       /* keys kept including self, >= 0; 0 = off */
+  int32_t global_tail;  /* LazFormer (section 2.3, eq. 19-21) G >= 0: the last G static
+                           (profile + history) positions of a request are global queries,
+                           exempt from the window (still causal, still delayed) */
 } rk_mask_params;
 
 /* Time RoPE (CADET, "time encoding"): pair (2i, 2i+1), i = 0 .. d/2-1, of a

@@ -52,7 +52,7 @@ class rk_mask_params(C.Structure):
         ("flags", C.c_uint32),
         ("delay", C.c_int64),
         ("window", C.c_int32),
-        ("reserved", C.c_int32),
+        ("global_tail", C.c_int32),
     ]
 
 

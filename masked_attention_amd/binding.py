@@ -70,7 +70,7 @@ class Plan:
 
     def __init__(self, batch: Batch, *, delay: int = 0, window: int = 0,
                  static_bidirectional: bool = False, num_heads: int = 1,
-                 candidates_only: bool = False,
+                 candidates_only: bool = False, global_tail: int = 0,
                  stream: Optional[torch.cuda.Stream] = None,
                  workspace: Optional[torch.Tensor] = None):
         self.batch = batch
@@ -81,7 +81,8 @@ class Plan:
         self.workspace = workspace
         flags = (_rk.RK_STATIC_BIDIRECTIONAL if static_bidirectional else 0) | (
             _rk.RK_QUERY_CANDIDATES_ONLY if candidates_only else 0)
-        self.params = sized(_rk.rk_mask_params, delay=int(delay), window=int(window), flags=flags)
+        self.params = sized(_rk.rk_mask_params, delay=int(delay), window=int(window),
+                            global_tail=int(global_tail), flags=flags)
         h = C.c_void_p()
         check(lib().rk_mask_plan(C.byref(batch.c), C.byref(self.params), self.num_heads,
                                  C.c_void_p(workspace.data_ptr()),

@@ -236,7 +236,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   if (!plan_out) return RK_ERR_INVALID_ARG;
   *plan_out = nullptr;
   if (!m || m->struct_size < sizeof(rk_mask_params)) return RK_ERR_INVALID_ARG;
-  if (m->delay < 0 || m->window < 0 ||
+  if (m->delay < 0 || m->window < 0 || m->global_tail < 0 ||
       (m->flags & ~(RK_STATIC_BIDIRECTIONAL | RK_QUERY_CANDIDATES_ONLY)))
     return RK_ERR_INVALID_ARG;
   Layout L;
@@ -257,6 +257,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   p->max_queue = L.max_queue;
   p->delay = m->delay;
   p->window = m->window;
+  p->global_tail = m->global_tail;
   p->flags = m->flags;
   p->req_offsets_dev = b->req_offsets_dev;
   p->seg_kind_dev = b->seg_kind_dev;

@@ -8,7 +8,8 @@
 // plus, for candidates, the row itself:
 //   static query, causal   : [max(0, p-W+1), min(p+1, cut)) where cut is the
 //                            number of static keys with t_j <= t_i - delay
-//                            (static times are sorted, so a binary search)
+//                            (static times are sorted, so a binary search);
+//                            lo = 0 for the last G static rows (global tail)
 //   static query, bidir.   : [0, end of static)
 //   real-time query        : [0, p+1)  (static part, then real-time events up
 //                            to itself; sorted times make t_j <= t_i implied)
@@ -107,7 +108,7 @@ __global__ void plan_seg_kernel(PlanDev P, int R, int T, const uint8_t* __restri
 
 __global__ void plan_rowdesc_kernel(PlanDev P, int R, int T, const uint8_t* __restrict__ kind,
                                     const int64_t* __restrict__ ts, int64_t delay, int window,
-                                    int bidir) {
+                                    int global_tail, int bidir) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T) return;
   const int r = find_request(P.req, R, i);
@@ -127,7 +128,8 @@ __global__ void plan_rowdesc_kernel(PlanDev P, int R, int T, const uint8_t* __re
       hi = a_rt;
     } else {
       hi = min(p + 1, a_rt);
-      lo = window > 0 ? max(0, p - window + 1) : 0;
+      // the last global_tail static positions are global queries (no window)
+      lo = (window > 0 && p < a_rt - global_tail) ? max(0, p - window + 1) : 0;
       if (delay > 0) hi = min(hi, count_le(tr, a_rt, ts[i] - delay));
     }
   } else if (s == RK_SEG_REALTIME) {
@@ -318,7 +320,7 @@ hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
                        p->seg_kind_dev, p->timestamps_dev, check_static);
     hipLaunchKernelGGL(plan_rowdesc_kernel, dim3(blocks), dim3(256), 0, s, P, p->R, p->T,
                        p->seg_kind_dev, p->timestamps_dev, p->delay, p->window,
-                       (int)((p->flags & RK_STATIC_BIDIRECTIONAL) != 0));
+                       p->global_tail, (int)((p->flags & RK_STATIC_BIDIRECTIONAL) != 0));
   }
   if (p->NQ > 0) {
     hipLaunchKernelGGL(plan_tile_kernel, dim3((unsigned)p->NQ), dim3(256), 0, s, P);

@@ -80,6 +80,7 @@ struct rk_plan {
   int64_t NQ, NT, G, slots, max_queue;
   int64_t delay;
   int32_t window;
+  int32_t global_tail;
   uint32_t flags;
   // batch device arrays (caller-owned)
   const int32_t* req_offsets_dev;

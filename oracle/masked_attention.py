@@ -62,12 +62,17 @@ TILE_Q, TILE_K = 128, 64
 # ---------------------------------------------------------------------------
 
 def visible_rows(seg_kind: np.ndarray, timestamps: np.ndarray, rows: np.ndarray, *,
-                 delay: int, window: int, static_bidirectional: bool) -> np.ndarray:
+                 delay: int, window: int, static_bidirectional: bool,
+                 global_tail: int = 0) -> np.ndarray:
     """Visibility of every key for the query rows `rows` of ONE request.
 
     Returns a bool array [len(rows), L]: True where query i may attend key j.
     Each entry is the rule applied to the pair (i, j) on its own; evaluating
     a subset of rows gives the same entries as the full matrix.
+
+    global_tail (LazFormer section 2.3, eq. 19-21, G): the last G static
+    (profile + history) positions are global queries, exempt from the
+    window; they still see only earlier keys, and the delay still applies.
     """
     seg_kind = np.asarray(seg_kind)
     t = np.asarray(timestamps, dtype=np.int64)
@@ -82,6 +87,7 @@ def visible_rows(seg_kind: np.ndarray, timestamps: np.ndarray, rows: np.ndarray,
 
     static_i = (si == PROFILE) | (si == HISTORY)
     static_j = (sj == PROFILE) | (sj == HISTORY)
+    n_static = int(np.count_nonzero((seg_kind == PROFILE) | (seg_kind == HISTORY)))
 
     # key is a candidate: only the diagonal (C2C isolation, and U2C never)
     vis = (sj == CANDIDATE) & (pi == pj)
@@ -92,7 +98,7 @@ def visible_rows(seg_kind: np.ndarray, timestamps: np.ndarray, rows: np.ndarray,
     else:
         u2u = pj <= pi
         if window > 0:
-            u2u = u2u & (pi - pj < window)
+            u2u = u2u & ((pi - pj < window) | (pi >= n_static - global_tail))
         if delay > 0:
             u2u = u2u & ~(tj > ti - delay)
     vis |= static_i & static_j & u2u
@@ -110,15 +116,15 @@ def visible_rows(seg_kind: np.ndarray, timestamps: np.ndarray, rows: np.ndarray,
 
 
 def visibility(seg_kind: np.ndarray, timestamps: np.ndarray, *, delay: int, window: int,
-               static_bidirectional: bool) -> np.ndarray:
+               static_bidirectional: bool, global_tail: int = 0) -> np.ndarray:
     """Full L x L visibility matrix of one request."""
     L = np.asarray(seg_kind).shape[0]
     return visible_rows(seg_kind, timestamps, np.arange(L), delay=delay, window=window,
-                        static_bidirectional=static_bidirectional)
+                        static_bidirectional=static_bidirectional, global_tail=global_tail)
 
 
 def count_visible(seg_kind, timestamps, *, delay, window, static_bidirectional,
-                  row_block: int = 1024) -> int:
+                  global_tail: int = 0, row_block: int = 1024) -> int:
     """Number of visible (query, key) pairs of one request."""
     L = np.asarray(seg_kind).shape[0]
     total = 0
@@ -126,7 +132,8 @@ def count_visible(seg_kind, timestamps, *, delay, window, static_bidirectional,
         rows = np.arange(r0, min(L, r0 + row_block))
         total += int(np.count_nonzero(visible_rows(seg_kind, timestamps, rows, delay=delay,
                                                    window=window,
-                                                   static_bidirectional=static_bidirectional)))
+                                                   static_bidirectional=static_bidirectional,
+                                                   global_tail=global_tail)))
     return total
 
 
@@ -190,7 +197,7 @@ def attention_forward(req_offsets: np.ndarray, seg_kind: np.ndarray, timestamps:
                       static_bidirectional: bool, rope: Optional[Dict[str, float]] = None,
                       rope_times: Optional[np.ndarray] = None, scale: Optional[float] = None,
                       heads: Optional[np.ndarray] = None, requests: Optional[np.ndarray] = None,
-                      row_block: int = 1024) -> Tuple[np.ndarray, np.ndarray]:
+                      row_block: int = 1024, global_tail: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Masked attention forward over a packed batch, in float64.
 
     q, k, v: [T, H, d] (any float dtype; upcast to float64).  With `rope`
@@ -225,7 +232,8 @@ def attention_forward(req_offsets: np.ndarray, seg_kind: np.ndarray, timestamps:
         for r0 in range(0, L, row_block):
             rows = np.arange(r0, min(L, r0 + row_block))
             vis = visible_rows(sk, ts, rows, delay=delay, window=window,
-                               static_bidirectional=static_bidirectional)
+                               static_bidirectional=static_bidirectional,
+                               global_tail=global_tail)
             for h in heads:
                 oh, lh = masked_softmax_attention(qr[rows, h], kr[:, h], vr[:, h], vis, scale)
                 o[a + rows, h] = oh
@@ -235,7 +243,7 @@ def attention_forward(req_offsets: np.ndarray, seg_kind: np.ndarray, timestamps:
 
 def attention_rows(req_offsets, seg_kind, timestamps, q, k, v, tokens: np.ndarray,
                    head: int, *, delay, window, static_bidirectional, rope=None,
-                   rope_times=None, scale=None):
+                   rope_times=None, scale=None, global_tail: int = 0):
     """Output rows for selected global tokens of one head (for sampled checks).
 
     Each token is computed against its own request's keys, exactly as in
@@ -260,7 +268,7 @@ def attention_rows(req_offsets, seg_kind, timestamps, q, k, v, tokens: np.ndarra
             qr = time_rope(qr, tr[a + rows], **rope)
             kr = time_rope(kr, tr[a:b], **rope)
         vis = visible_rows(sk, ts, rows, delay=delay, window=window,
-                           static_bidirectional=static_bidirectional)
+                           static_bidirectional=static_bidirectional, global_tail=global_tail)
         oh, lh = masked_softmax_attention(qr, kr, vr, vis, scale)
         o[sel] = oh
         lse[sel] = lh
@@ -272,7 +280,7 @@ def attention_rows(req_offsets, seg_kind, timestamps, q, k, v, tokens: np.ndarra
 # ---------------------------------------------------------------------------
 
 def tile_plan_request(seg_kind, timestamps, *, delay, window, static_bidirectional,
-                      tq: int = TILE_Q, tk: int = TILE_K):
+                      tq: int = TILE_Q, tk: int = TILE_K, global_tail: int = 0):
     """Per-tile visible counts and classes of one request.
 
     Tile (qt, kt) covers request-local rows [tq*qt, tq*qt+tq) and columns
@@ -286,7 +294,7 @@ def tile_plan_request(seg_kind, timestamps, *, delay, window, static_bidirection
     for qt in range(nqt):
         rows = np.arange(qt * tq, min(L, qt * tq + tq))
         vis = visible_rows(seg_kind, timestamps, rows, delay=delay, window=window,
-                           static_bidirectional=static_bidirectional)
+                           static_bidirectional=static_bidirectional, global_tail=global_tail)
         padded = np.zeros((vis.shape[0], nkt * tk), dtype=bool)
         padded[:, :L] = vis
         count[qt] = padded.reshape(vis.shape[0], nkt, tk).sum(axis=(0, 2))
@@ -297,7 +305,7 @@ def tile_plan_request(seg_kind, timestamps, *, delay, window, static_bidirection
 
 
 def tile_plan(req_offsets, seg_kind, timestamps, *, delay, window, static_bidirectional,
-              tq: int = TILE_Q, tk: int = TILE_K) -> Dict[str, np.ndarray]:
+              tq: int = TILE_Q, tk: int = TILE_K, global_tail: int = 0) -> Dict[str, np.ndarray]:
     """Tile plan of a packed batch: flattened per-request tile arrays plus CSR.
 
     tile_count / tile_class: concatenation over requests of the row-major
@@ -309,7 +317,8 @@ def tile_plan(req_offsets, seg_kind, timestamps, *, delay, window, static_bidire
     for r in range(req_offsets.shape[0] - 1):
         a, b = int(req_offsets[r]), int(req_offsets[r + 1])
         c, k = tile_plan_request(seg_kind[a:b], timestamps[a:b], delay=delay, window=window,
-                                 static_bidirectional=static_bidirectional, tq=tq, tk=tk)
+                                 static_bidirectional=static_bidirectional, tq=tq, tk=tk,
+                                 global_tail=global_tail)
         counts.append(c.ravel())
         classes.append(k.ravel())
         for qt in range(c.shape[0]):

@@ -92,6 +92,7 @@ class Workload:
     dt_max: float = DT_MAX
     base: float = BASE
     meta: dict = field(default_factory=dict)
+    global_tail: int = 0             # LazFormer G: last G static positions exempt from the window
 
     @property
     def num_requests(self) -> int:
@@ -226,7 +227,7 @@ def make_custom(requests: Sequence[Sequence[Tuple[int, np.ndarray]]], *, heads: 
                 dtype: str = "f32", delay: int = 0, window: int = 0,
                 static_bidirectional: bool = False, seed: int = 0,
                 anchors: Optional[np.ndarray] = None, with_qkv: bool = True,
-                name: str = "custom") -> Workload:
+                name: str = "custom", global_tail: int = 0) -> Workload:
     """Build a workload from an explicit request layout (tests, edge cases)."""
     offs, seg, ts = pack(requests)
     R = offs.shape[0] - 1
@@ -235,7 +236,7 @@ def make_custom(requests: Sequence[Sequence[Tuple[int, np.ndarray]]], *, heads: 
     wl = Workload(name=name, req_offsets=offs, seg_kind=seg, timestamps=ts,
                   anchors=np.asarray(anchors, np.int64), delay=delay, window=window,
                   static_bidirectional=static_bidirectional, heads=heads, d_head=d_head,
-                  dtype=dtype, meta={"seed": seed})
+                  dtype=dtype, meta={"seed": seed}, global_tail=global_tail)
     if with_qkv:
         rng = np.random.default_rng(seed)
         wl.q, wl.k, wl.v = draw_qkv(rng, seg.shape[0], heads, d_head, dtype)

@@ -109,6 +109,9 @@ static void check_mask_plan() {
   bad.flags = RK_QUERY_CANDIDATES_ONLY | 8u;
   EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
   bad = m;
+  bad.global_tail = -1;
+  EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
+  bad = m;
   bad.struct_size = 4;
   EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
 }

@@ -130,7 +130,7 @@ def test_mask_plan_host_errors(lib):
                             C.byref(h), None) == _rk.RK_ERR_INVALID_ARG
     assert lib.rk_mask_plan(C.byref(b), C.byref(m), 2, None, n.value, C.byref(h),
                             None) == _rk.RK_ERR_INVALID_ARG
-    for bad in (dict(delay=-1), dict(window=-3), dict(flags=4),
+    for bad in (dict(delay=-1), dict(window=-3), dict(flags=4), dict(global_tail=-1),
                 dict(flags=_rk.RK_QUERY_CANDIDATES_ONLY | 8)):
         mb = _rk.sized(_rk.rk_mask_params, **bad)
         assert lib.rk_mask_plan(C.byref(b), C.byref(mb), 2, C.c_void_p(1 << 20), n.value,

@@ -74,6 +74,42 @@ def test_lazformer_eq19_21(Lt, N, W):
     assert np.array_equal(vis, ref)
 
 
+@pytest.mark.parametrize("Lt,N,W,G", [(12, 3, 4, 3), (30, 5, 7, 10), (20, 0, 1, 20),
+                                      (25, 4, 6, 0), (9, 2, 3, 1)])
+def test_lazformer_eq19_21_global_tail(Lt, N, W, G):
+    """LazFormer section 2.3, eq. 19-21 with G global-tail queries, built
+    literally (1-based p, q): history query p sees history key q iff q <= p
+    and (p - q < W or p > Lt - G); candidates see all history and
+    themselves."""
+    n = Lt + N
+    ref = np.zeros((n, n), dtype=bool)
+    for p in range(1, n + 1):
+        for q in range(1, n + 1):
+            if p <= Lt and q <= Lt and q <= p and (p - q < W or p > Lt - G):
+                ref[p - 1, q - 1] = True
+            elif p > Lt and q <= Lt:
+                ref[p - 1, q - 1] = True
+            elif p > Lt and q > Lt and p == q:
+                ref[p - 1, q - 1] = True
+    seg = np.array([HISTORY] * Lt + [CANDIDATE] * N, np.uint8)
+    ts = np.arange(n, dtype=np.int64) + NOW
+    vis = oracle.visibility(seg, ts, delay=0, window=W, static_bidirectional=False,
+                            global_tail=G)
+    assert np.array_equal(vis, ref)
+
+
+def test_global_tail_pair_count_closed_form():
+    """History of L with window W and G global-tail queries: the first L - G
+    rows see min(p + 1, W) keys, the last G rows see p + 1 keys."""
+    L, W, G = 700, 64, 100
+    seg = np.full(L, HISTORY, np.uint8)
+    ts = np.arange(L, dtype=np.int64) + NOW
+    want = sum(min(p + 1, W) for p in range(L - G)) + sum(p + 1 for p in range(L - G, L))
+    got = oracle.count_visible(seg, ts, delay=0, window=W, static_bidirectional=False,
+                               global_tail=G)
+    assert got == want == 36384 + 65050
+
+
 def test_delay_zero_no_window_is_lower_triangle_even_with_ties():
     rng = np.random.default_rng(7)
     L = 40

@@ -62,7 +62,8 @@ def _tensors(wl):
 def _plan(rk, wl, batch=None):
     batch = batch or rk.Batch.from_workload(wl)
     plan = rk.Plan(batch, delay=wl.delay, window=wl.window,
-                   static_bidirectional=wl.static_bidirectional, num_heads=wl.heads)
+                   static_bidirectional=wl.static_bidirectional, num_heads=wl.heads,
+                   global_tail=wl.global_tail)
     return batch, plan
 
 
@@ -84,7 +85,8 @@ def _oracle_full(wl, rope=True):
                                     wl.q.astype(np.float64), wl.k.astype(np.float64),
                                     wl.v.astype(np.float64), delay=wl.delay, window=wl.window,
                                     static_bidirectional=wl.static_bidirectional,
-                                    rope=_rope(wl) if rope else None)
+                                    rope=_rope(wl) if rope else None,
+                                    global_tail=wl.global_tail)
 
 
 def _check(wl, o, ref, lse=None, ref_lse=None):
@@ -134,7 +136,8 @@ def _check_plan(wl, plan, ref, check_rows=True):
             if b == a:
                 continue
             vis = oracle.visibility(wl.seg_kind[a:b], wl.timestamps[a:b], delay=wl.delay,
-                                    window=wl.window, static_bidirectional=wl.static_bidirectional)
+                                    window=wl.window, static_bidirectional=wl.static_bidirectional,
+                                    global_tail=wl.global_tail)
             lo = rd[a:b, 0]
             hi = rd[a:b, 1] & 0x7FFFFFFF
             self_ = rd[a:b, 1] < 0
@@ -189,6 +192,26 @@ def test_plan_bit_exact_random(rk, seed):
         ref = oracle.tile_plan(wl.req_offsets, wl.seg_kind, wl.timestamps, delay=delay,
                                window=window, static_bidirectional=bidir)
         _check_plan(wl, plan, ref)
+
+
+@pytest.mark.parametrize("G", [1, 37, 300])
+def test_plan_and_attention_global_tail(rk, G):
+    """LazFormer global-tail queries (eq. 19-21, G > 0) with a window and a
+    delay: plan bit-exact (row descriptors included), attention within the
+    bf16 bar."""
+    rng = np.random.default_rng(500 + G)
+    reqs = random_layout(rng, 6, 900)
+    for window, delay in ((40, 0), (100, 3600)):
+        wl = make_custom(reqs, heads=2, d_head=64, dtype="bf16", delay=delay, window=window,
+                         global_tail=G, seed=G, name=f"global-tail-{G}-{window}")
+        _say(f"[gpu] global tail G={G} window={window} delay={delay}")
+        batch, plan = _plan(rk, wl)
+        ref = oracle.tile_plan(wl.req_offsets, wl.seg_kind, wl.timestamps, delay=delay,
+                               window=window, static_bidirectional=False, global_tail=G)
+        _check_plan(wl, plan, ref)
+        plan2, o, lse = _run(rk, wl)
+        ref_o, ref_lse = _oracle_full(wl)
+        _check(wl, o, ref_o, lse, ref_lse)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
