@@ -184,6 +184,21 @@ def main() -> int:
                      v_stride_tok=H * d, v_stride_head=d, o_stride_tok=H * d, o_stride_head=d,
                      scale=0.0)
     attn.rope = C.cast(C.pointer(rp), C.c_void_p)
+    attn_ws = None
+    if args.candidates_only:
+        # partial results of split items live in the attention workspace
+        size_plan = rk.Plan(batch, delay=wl.delay, window=wl.window,
+                            static_bidirectional=wl.static_bidirectional, num_heads=H,
+                            candidates_only=True)
+        n_ws = C.c_size_t()
+        _rk.check(lib.rk_attn_workspace_size(size_plan.handle, C.byref(attn), C.byref(n_ws)),
+                  "rk_attn_workspace_size")
+        split_stats = size_plan.stats()
+        size_plan.close()
+        if n_ws.value:
+            attn_ws = torch.empty(n_ws.value, dtype=torch.uint8, device=dev)
+            attn.workspace = attn_ws.data_ptr()
+            attn.workspace_bytes = n_ws.value
     handles = []
 
     def step(ev=None):
@@ -271,6 +286,10 @@ def main() -> int:
                      "alg_bytes": attn_alg_bytes, "mfma_util": mfma_util},
         "cpu_baseline": None,
     }
+    if args.candidates_only:
+        # the attention stage holds the attention and, for split items, the merge
+        out["split"] = {"work_entries": split_stats["work_entries"],
+                        "split_items": split_stats["split_items"]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(wl, args.cpu_heads)
     print(json.dumps(out), flush=True)

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define RK_ABI_VERSION 1
+#define RK_ABI_VERSION 2
 
 typedef enum rk_status {
   RK_OK = 0,
@@ -105,7 +105,10 @@ enum { RK_TILE_EMPTY = 0, RK_TILE_PARTIAL = 1, RK_TILE_FULL = 2 };
                                          writes O / LSE rows of those tiles only (rows
                                          elsewhere are left as they were).  Masks, tile
                                          classes, counts, CSR and totals are those of the
-                                         whole batch. */
+                                         whole batch.  When few such tiles exist, the key
+                                         range of each is cut into chunks run by separate
+                                         workgroups whose partial softmax results a merge
+                                         pass combines (more attention workspace). */
 
 /* Segment-kind bits of rk_rope_params.kinds: bit k selects kind k. */
 #define RK_KIND_BIT(k) (1u << (k))
@@ -184,7 +187,7 @@ typedef struct rk_plan_info {
   int32_t num_heads;
   int64_t num_qtiles;          /* sum over requests of ceil(L_r / 128) */
   int64_t num_tiles;           /* sum over requests of ceil(L_r/128)*ceil(L_r/64) */
-  int64_t num_sched_slots;     /* grid size of rk_masked_attn_fwd */
+  int64_t num_sched_slots;     /* one slot per (q-tile, head) work item, LPT / XCD order */
   const void* workspace;
   size_t off_tile_class;       /* uint8 [num_tiles], RK_TILE_*, requests in order, row-major [qt][kt] */
   size_t off_tile_count;       /* int32 [num_tiles], visible pairs per tile */
@@ -192,6 +195,13 @@ typedef struct rk_plan_info {
   size_t off_ktile_idx;        /* int32 [num_tiles] (first qtile_ptr[num_qtiles] used), request-local kt, ascending */
   size_t off_row_desc;         /* int32 [total_tokens][2]: visible keys of a query = [lo, hi) plus bit 31 of hi = self */
   size_t off_sched;            /* int32 [num_sched_slots]: work item = qtile * num_heads + head, or -1 */
+  int64_t num_work_slots;      /* RK_QUERY_CANDIDATES_ONLY plans: grid size of the attention
+                                  (num_sched_slots + 1024), else 0 (the grid is the schedule) */
+  size_t off_work;             /* int32 [num_work_slots][4]: (item, first, end, part) = CSR
+                                  entries [first, end) of the item's q-tile; part >= 0 names
+                                  the partial result of a split item; item -1 = idle slot */
+  size_t off_splits;           /* int32 [1024][4]: (item, first part, parts, 0) of each split
+                                  item, item -1 past the last */
 } rk_plan_info;
 
 /* Totals of a plan (per head). */
@@ -202,6 +212,8 @@ typedef struct rk_plan_totals {
   int64_t full_tiles;
   int64_t partial_tiles;
   int64_t empty_tiles;
+  int32_t work_entries;        /* used slots of the work list (RK_QUERY_CANDIDATES_ONLY) */
+  int32_t split_items;         /* items whose key range is split */
 } rk_plan_totals;
 
 /*
@@ -307,7 +319,10 @@ rk_status rk_time_rope(const rk_batch* b, const rk_rope_params* r, const void* x
                        int64_t in_stride_tok, int64_t in_stride_head,
                        int64_t out_stride_tok, int64_t out_stride_head, void* stream);
 
-/* Workspace bytes rk_masked_attn_fwd needs for `a` on plan `p` (host only). */
+/* Workspace bytes rk_masked_attn_fwd needs for `a` on plan `p` (host only):
+ * the rotated K when the call rotates K ([total_tokens][num_heads][d_head] of
+ * dtype), plus, for RK_QUERY_CANDIDATES_ONLY plans, 2048 partial results of
+ * 128 rows x (d_head + 2) floats (about 69 MB at d_head = 64). */
 rk_status rk_attn_workspace_size(const rk_plan* p, const rk_attn_args* a, size_t* bytes);
 
 /*

@@ -30,7 +30,7 @@ RK_STATIC_BIDIRECTIONAL = 0x1
 RK_QUERY_CANDIDATES_ONLY = 0x2
 RK_ATTN_REFERENCE_KERNEL = 0x1
 RK_ATTN_K_PREROTATED = 0x2
-RK_ABI_VERSION = 1
+RK_ABI_VERSION = 2
 
 
 class rk_batch(C.Structure):
@@ -82,6 +82,9 @@ class rk_plan_info(C.Structure):
         ("off_ktile_idx", C.c_size_t),
         ("off_row_desc", C.c_size_t),
         ("off_sched", C.c_size_t),
+        ("num_work_slots", C.c_int64),
+        ("off_work", C.c_size_t),
+        ("off_splits", C.c_size_t),
     ]
 
 
@@ -93,6 +96,8 @@ class rk_plan_totals(C.Structure):
         ("full_tiles", C.c_int64),
         ("partial_tiles", C.c_int64),
         ("empty_tiles", C.c_int64),
+        ("work_entries", C.c_int32),
+        ("split_items", C.c_int32),
     ]
 
 

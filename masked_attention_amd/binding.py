@@ -125,6 +125,19 @@ class Plan:
     def sched(self) -> torch.Tensor:
         return self._view(self.info.off_sched, int(self.info.num_sched_slots), torch.int32)
 
+    def work(self) -> Optional[torch.Tensor]:
+        """Work list [slots, 4] = (item, first, end, part), or None."""
+        n = int(self.info.num_work_slots)
+        if n == 0:
+            return None
+        return self._view(self.info.off_work, 4 * n, torch.int32).view(n, 4)
+
+    def splits(self) -> Optional[torch.Tensor]:
+        """Split items [1024, 4] = (item, first part, parts, 0), or None."""
+        if int(self.info.num_work_slots) == 0:
+            return None
+        return self._view(self.info.off_splits, 4 * 1024, torch.int32).view(1024, 4)
+
     def stats(self, stream: Optional[torch.cuda.Stream] = None, raise_on_error: bool = True) -> dict:
         t = sized(_rk.rk_plan_totals)
         st = lib().rk_plan_stats(self.handle, C.byref(t), _stream(stream))
@@ -133,7 +146,8 @@ class Plan:
             check(st, "rk_plan_stats")
         return {"status": st, "device_errors": int(t.device_errors),
                 "visible_pairs": int(t.visible_pairs), "full_tiles": int(t.full_tiles),
-                "partial_tiles": int(t.partial_tiles), "empty_tiles": int(t.empty_tiles)}
+                "partial_tiles": int(t.partial_tiles), "empty_tiles": int(t.empty_tiles),
+                "work_entries": int(t.work_entries), "split_items": int(t.split_items)}
 
     def close(self) -> None:
         if getattr(self, "handle", None) is not None and self.handle.value:

@@ -36,7 +36,7 @@ struct Layout {
          host_blob = 0, off_row_desc = 0, off_tile_count = 0, off_tile_class = 0, off_qt_nnz = 0,
          off_qt_pairs = 0, off_qt_full = 0,
          off_qtile_ptr = 0, off_ktile_idx = 0, off_ktile_word = 0, off_qorder = 0, off_sched = 0,
-         total = 0;
+         off_work = 0, off_splits = 0, total = 0;
 };
 
 rk_status check_batch(const rk_batch* b) {
@@ -160,6 +160,8 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->off_ktile_word = take(sizeof(int32_t) * (size_t)nt);
   L->off_qorder = take(sizeof(int32_t) * (size_t)nq);
   L->off_sched = take(sizeof(int32_t) * (size_t)L->slots);
+  L->off_work = take(sizeof(rk::WorkEntry) * (size_t)(L->slots + rk::kSplitTarget));
+  L->off_splits = take(sizeof(rk::SplitEntry) * (size_t)rk::kSplitTarget);
   L->total = off;
   return RK_OK;
 }
@@ -255,6 +257,8 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   p->G = L.G;
   p->slots = L.slots;
   p->max_queue = L.max_queue;
+  p->grid = (m->flags & RK_QUERY_CANDIDATES_ONLY) && L.slots > 0 ? L.slots + rk::kSplitTarget
+                                                                 : L.slots;
   p->delay = m->delay;
   p->window = m->window;
   p->global_tail = m->global_tail;
@@ -280,6 +284,8 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   p->off_ktile_word = L.off_ktile_word;
   p->off_qorder = L.off_qorder;
   p->off_sched = L.off_sched;
+  p->off_work = L.off_work;
+  p->off_splits = L.off_splits;
   p->off_totals = L.off_totals;
   p->host_blob_bytes = L.host_blob;
   p->total_bytes = L.total;
@@ -302,6 +308,8 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   D.ktile_word = (int32_t*)(ws + L.off_ktile_word);
   D.qorder = (int32_t*)(ws + L.off_qorder);
   D.sched = (int32_t*)(ws + L.off_sched);
+  D.work = (rk::WorkEntry*)(ws + L.off_work);
+  D.splits = (rk::SplitEntry*)(ws + L.off_splits);
 
   p->host_blob = (unsigned char*)std::calloc(L.host_blob ? L.host_blob : 1, 1);
   if (!p->host_blob) {
@@ -341,6 +349,10 @@ rk_status rk_plan_get_info(const rk_plan* p, rk_plan_info* out) {
   out->off_ktile_idx = p->off_ktile_idx;
   out->off_row_desc = p->off_row_desc;
   out->off_sched = p->off_sched;
+  const bool wl = p->grid > p->slots;
+  out->num_work_slots = wl ? p->grid : 0;
+  out->off_work = wl ? p->off_work : 0;
+  out->off_splits = wl ? p->off_splits : 0;
   return RK_OK;
 }
 
@@ -354,6 +366,8 @@ rk_status rk_plan_stats(const rk_plan* p, rk_plan_totals* out, void* stream) {
   out->full_tiles = (int64_t)t.full_tiles;
   out->partial_tiles = (int64_t)t.partial_tiles;
   out->empty_tiles = (int64_t)t.empty_tiles;
+  out->work_entries = t.n_work;
+  out->split_items = t.n_splits;
   if (t.errors & rk::kErrSegment) return RK_ERR_SEGMENT_ORDER;
   if (t.errors & rk::kErrTime) return RK_ERR_UNSORTED_TIME;
   return RK_OK;
@@ -429,9 +443,20 @@ bool mfma_aligned(const rk_attn_args* a, bool k_in_workspace) {
   return ok;
 }
 
-size_t attn_ws_bytes(const rk_plan* p, const rk_attn_args* a) {
+// Attention workspace: [rotated K, when the call rotates K][partial results
+// of split items, for plans with a work list].
+size_t attn_k_bytes(const rk_plan* p, const rk_attn_args* a) {
   if (!a->rope || (a->flags & RK_ATTN_K_PREROTATED)) return 0;
   return align_up((size_t)p->T * (size_t)a->num_heads * (size_t)a->d_head * elem_size(a->dtype));
+}
+
+size_t attn_part_bytes(const rk_plan* p, const rk_attn_args* a) {
+  if (p->grid <= p->slots) return 0;
+  return align_up((size_t)rk::kMaxParts * rk::kTileQ * (size_t)(a->d_head + 2) * sizeof(float));
+}
+
+size_t attn_ws_bytes(const rk_plan* p, const rk_attn_args* a) {
+  return attn_k_bytes(p, a) + attn_part_bytes(p, a);
 }
 
 }  // namespace
@@ -482,6 +507,8 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
     L.tab = make_tab(a->rope, a->d_head);
     L.rope_q = true;
   }
+  if (attn_part_bytes(p, a))
+    L.part = (float*)((unsigned char*)a->workspace + attn_k_bytes(p, a));
   if (k_rotate) {
     // K is rotated once into the workspace ([T, H, d] dense); Q is rotated
     // by the attention kernel while it is staged.
@@ -498,6 +525,18 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
   }
   hipError_t e = use_mfma ? rk::launch_attn_mfma_bf16_d64(p, L, s)
                           : rk::launch_attn_reference(p, L, a->dtype, s);
+  if (e == hipSuccess && L.part) {
+    // units of the kernels' reference max m: the MFMA kernel keeps it in log2
+    // units of the scaled score when it folds scale * log2(e) into a rotated
+    // Q, in raw dot-product units otherwise; the plain kernel in natural units
+    // of the scaled score
+    const float log2e = 1.4426950408889634f, ln2 = 0.6931471805599453f;
+    float to_log2, to_nat;
+    if (use_mfma && L.rope_q) { to_log2 = 1.f; to_nat = ln2; }
+    else if (use_mfma) { to_log2 = L.scale * log2e; to_nat = L.scale; }
+    else { to_log2 = log2e; to_nat = 1.f; }
+    e = rk::launch_attn_combine(p, L, a->dtype, to_log2, to_nat, s);
+  }
   return e == hipSuccess ? RK_OK : RK_ERR_HIP;
 }
 

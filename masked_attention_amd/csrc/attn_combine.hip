@@ -1,0 +1,103 @@
+// Merge of split work items (candidates-only plans with a work list).
+//
+// The key range of a split (query tile, head) item was cut into chunks of
+// CSR entries; each chunk's slot left, per query row, its unnormalised output
+// O_j = sum_k exp(s_k - m_j) v_k, its reference max m_j and its sum
+// l_j = sum_k exp(s_k - m_j).  Softmax over the union of the chunks is
+//   M = max_j m_j,  w_j = exp(m_j - M),  O = sum_j w_j O_j / sum_j w_j l_j,
+//   LSE = M + log(sum_j w_j l_j),
+// the same rescaling the online softmax applies between key tiles (HSTU,
+// App. H, M-FALCON; the flash-decoding split of a long key range).  The
+// kernels keep m in their own units; to_log2 and to_nat convert it.
+//
+// One 256-thread workgroup per split item: two threads per query row, each
+// owning half of d_head.
+#include <hip/hip_bf16.h>
+
+#include "rk_internal.h"
+
+namespace rk {
+namespace {
+
+__device__ __forceinline__ void st(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st(__hip_bfloat16* p, float v) {
+  unsigned u = __float_as_uint(v);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  *(unsigned short*)p = (unsigned short)(u >> 16);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const ReqMeta* req, const int32_t* qt_req,
+                                                           const SplitEntry* splits, AttnLaunch A,
+                                                           float to_log2, float to_nat) {
+  const SplitEntry se = splits[blockIdx.x];
+  if (se.item < 0) return;
+  const int qg = se.item / A.H;
+  const int head = se.item - qg * A.H;
+  const ReqMeta m = req[qt_req[qg]];
+  const int rl = threadIdx.x >> 1;
+  const int c0 = (threadIdx.x & 1) * (D / 2);
+  const int row = (qg - m.qt_off) * kTileQ + rl;
+  if (row >= m.len) return;
+  const int tok = m.tok_off + row;
+  constexpr int kStride = kTileQ * (D + 2);
+  const float* base = A.part + (int64_t)se.part0 * kStride;
+
+  float M = -INFINITY;
+  for (int j = 0; j < se.nparts; ++j) M = fmaxf(M, base[j * kStride + kTileQ * D + rl]);
+  float acc[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) acc[c] = 0.f;
+  float l = 0.f;
+  if (M != -INFINITY) {
+    for (int j = 0; j < se.nparts; ++j) {
+      const float* pj = base + j * kStride;
+      const float mj = pj[kTileQ * D + rl];
+      if (mj == -INFINITY) continue;  // nothing of this chunk is visible to the row
+      const float w = exp2f((mj - M) * to_log2);
+      l = fmaf(w, pj[kTileQ * D + kTileQ + rl], l);
+      const float4* o4 = (const float4*)(pj + rl * D + c0);
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        const float4 v = o4[c];
+        acc[4 * c] = fmaf(w, v.x, acc[4 * c]);
+        acc[4 * c + 1] = fmaf(w, v.y, acc[4 * c + 1]);
+        acc[4 * c + 2] = fmaf(w, v.z, acc[4 * c + 2]);
+        acc[4 * c + 3] = fmaf(w, v.w, acc[4 * c + 3]);
+      }
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  T* O = (T*)A.o + (int64_t)tok * A.o_st + (int64_t)head * A.o_sh + c0;
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) st(O + c, acc[c] * inv);
+  if (A.lse && c0 == 0)
+    A.lse[(int64_t)head * A.T + tok] = l > 0.f ? M * to_nat + logf(l) : -INFINITY;
+}
+
+template <typename T, int D>
+hipError_t launch(const rk_plan* p, const AttnLaunch& a, float to_log2, float to_nat,
+                  hipStream_t s) {
+  hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3((unsigned)kSplitTarget), dim3(256), 0, s,
+                     p->dev.req, p->dev.qt_req, p->dev.splits, a, to_log2, to_nat);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_combine(const rk_plan* p, const AttnLaunch& a, rk_dtype dt, float to_log2,
+                               float to_nat, hipStream_t s) {
+  if (p->grid <= p->slots || a.part == nullptr) return hipSuccess;
+  if (dt == RK_F32) {
+    if (a.d == 32) return launch<float, 32>(p, a, to_log2, to_nat, s);
+    if (a.d == 64) return launch<float, 64>(p, a, to_log2, to_nat, s);
+    if (a.d == 128) return launch<float, 128>(p, a, to_log2, to_nat, s);
+  } else {
+    if (a.d == 32) return launch<__hip_bfloat16, 32>(p, a, to_log2, to_nat, s);
+    if (a.d == 64) return launch<__hip_bfloat16, 64>(p, a, to_log2, to_nat, s);
+    if (a.d == 128) return launch<__hip_bfloat16, 128>(p, a, to_log2, to_nat, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rk

@@ -57,6 +57,7 @@ struct PlanView {
   const int32_t* qtile_ptr;
   const int32_t* ktile_word;
   const int32_t* sched;
+  const WorkEntry* work;  // launch slot -> (item, CSR range, part), or null
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -357,7 +358,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   __shared__ __attribute__((aligned(1024))) unsigned short V0[TILE_ELEMS], V1[TILE_ELEMS];
   __shared__ double wtab[D / 2];
 
-  const int item = ldc(P.sched, blockIdx.x);
+  // a slot runs a whole item (schedule) or a CSR range of one (work list)
+  int item, kbeg = 0, kend = -1, part = -1;
+  if (P.work) {
+    const WorkEntry we = ldc(P.work, blockIdx.x);
+    item = we.item;
+    kbeg = we.kbeg;
+    kend = we.kend;
+    part = we.part;
+  } else {
+    item = ldc(P.sched, blockIdx.x);
+  }
   if (item < 0) return;
   const int qg = item / A.H;
   const int head = item - qg * A.H;
@@ -407,8 +418,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   for (int r = 0; r < 16; ++r) { o0[r] = 0.f; o1[r] = 0.f; negm[r] = 0.f; }
   float mref = -INFINITY, lsum = 0.f;
 
-  const int e0 = ldc(P.qtile_ptr, qg);
-  const int n = ldc(P.qtile_ptr, qg + 1) - e0;
+  const int e0 = ldc(P.qtile_ptr, qg) + kbeg;
+  const int n = kend >= 0 ? kend - kbeg : ldc(P.qtile_ptr, qg + 1) - e0;
   // Iteration i computes tile i from one stage while the copies of tile
   // i+1 fill the other; they land in LDS asynchronously and are waited for
   // just before the barrier that ends the iteration.  The loop is unrolled
@@ -447,6 +458,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   // ---- epilogue: O = O^T / l; lanes of both halves hold distinct d values
   const float ltot = lsum + __shfl_xor(lsum, 32, 64);
   if (!rvalid) return;
+  if (part >= 0) {
+    // partial result of a split item: O unnormalised, reference max, sum
+    float* pp = A.part + (int64_t)part * (kTileQ * (D + 2));
+    const int rl = wv * 32 + li;
+    float* orow = pp + rl * D;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 8 * g + 4 * hh;
+      *(float4*)(orow + d) = make_float4(o0[4 * g], o0[4 * g + 1], o0[4 * g + 2], o0[4 * g + 3]);
+      *(float4*)(orow + 32 + d) =
+          make_float4(o1[4 * g], o1[4 * g + 1], o1[4 * g + 2], o1[4 * g + 3]);
+    }
+    if (hh == 0) {
+      pp[kTileQ * D + rl] = mref;
+      pp[kTileQ * D + kTileQ + rl] = ltot;
+    }
+    return;
+  }
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   unsigned short* Op = (unsigned short*)A.o + (int64_t)tokq * A.o_st + (int64_t)head * A.o_sh;
 #pragma unroll
@@ -466,14 +495,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
 
 hipError_t launch_attn_mfma_bf16_d64(const rk_plan* p, const AttnLaunch& a, hipStream_t s) {
   if (p->slots == 0) return hipSuccess;
+  const bool wl = p->grid > p->slots;
   PlanView P{p->dev.req, p->dev.qt_req, p->dev.row_desc, p->dev.qtile_ptr, p->dev.ktile_word,
-             p->dev.sched};
+             p->dev.sched, wl ? p->dev.work : nullptr};
+  const dim3 grid((unsigned)p->grid);
   if (a.rope_q)
-    hipLaunchKernelGGL(attn_mfma_bf16_d64_kernel<true>, dim3((unsigned)p->slots), dim3(kThreads), 0,
-                       s, P, a);
+    hipLaunchKernelGGL(attn_mfma_bf16_d64_kernel<true>, grid, dim3(kThreads), 0, s, P, a);
   else
-    hipLaunchKernelGGL(attn_mfma_bf16_d64_kernel<false>, dim3((unsigned)p->slots),
-                       dim3(kThreads), 0, s, P, a);
+    hipLaunchKernelGGL(attn_mfma_bf16_d64_kernel<false>, grid, dim3(kThreads), 0, s, P, a);
   return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ struct PlanView {
   const int32_t* qtile_ptr;
   const int32_t* ktile_word;
   const int32_t* sched;
+  const WorkEntry* work;  // launch slot -> (item, CSR range, part), or null
 };
 
 template <typename T, int D>
@@ -42,7 +43,16 @@ __global__ __launch_bounds__(128) void attn_ref_kernel(PlanView P, AttnLaunch A)
   __shared__ float Ks[kTileK][D];
   __shared__ float Vs[kTileK][D];
   __shared__ double w[kMaxHalfD];
-  const int item = P.sched[blockIdx.x];
+  int item, kbeg = 0, kend = -1, part = -1;
+  if (P.work) {
+    const WorkEntry we = P.work[blockIdx.x];
+    item = we.item;
+    kbeg = we.kbeg;
+    kend = we.kend;
+    part = we.part;
+  } else {
+    item = P.sched[blockIdx.x];
+  }
   if (item < 0) return;
   const int qg = item / A.H;
   const int head = item - qg * A.H;
@@ -88,7 +98,8 @@ __global__ __launch_bounds__(128) void attn_ref_kernel(PlanView P, AttnLaunch A)
 #pragma unroll
   for (int c = 0; c < D; ++c) acc[c] = 0.f;
 
-  const int e0 = P.qtile_ptr[qg], e1 = P.qtile_ptr[qg + 1];
+  const int e0 = P.qtile_ptr[qg] + kbeg;
+  const int e1 = kend >= 0 ? P.qtile_ptr[qg] + kend : P.qtile_ptr[qg + 1];
   for (int e = e0; e < e1; ++e) {
     const int kw = P.ktile_word[e];
     const int kt = kw & 0x7fffffff;
@@ -134,6 +145,15 @@ __global__ __launch_bounds__(128) void attn_ref_kernel(PlanView P, AttnLaunch A)
   }
 
   if (!valid) return;
+  if (part >= 0) {
+    // partial result of a split item: O unnormalised, running max, sum
+    float* pp = A.part + (int64_t)part * (kTileQ * (D + 2));
+#pragma unroll
+    for (int c = 0; c < D; ++c) pp[t * D + c] = acc[c];
+    pp[kTileQ * D + t] = mrow;
+    pp[kTileQ * D + kTileQ + t] = lsum;
+    return;
+  }
   T* O = (T*)A.o;
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
@@ -143,9 +163,10 @@ __global__ __launch_bounds__(128) void attn_ref_kernel(PlanView P, AttnLaunch A)
 
 template <typename T, int D>
 hipError_t launch_ref(const rk_plan* p, const AttnLaunch& a, hipStream_t s) {
+  const bool wl = p->grid > p->slots;
   PlanView P{p->dev.req, p->dev.qt_req, p->dev.row_desc, p->dev.qtile_ptr, p->dev.ktile_word,
-             p->dev.sched};
-  hipLaunchKernelGGL((attn_ref_kernel<T, D>), dim3((unsigned)p->slots), dim3(128), 0, s, P, a);
+             p->dev.sched, wl ? p->dev.work : nullptr};
+  hipLaunchKernelGGL((attn_ref_kernel<T, D>), dim3((unsigned)p->grid), dim3(128), 0, s, P, a);
   return hipGetLastError();
 }
 

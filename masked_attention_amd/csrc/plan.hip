@@ -309,6 +309,81 @@ __global__ void plan_sched_kernel(PlanDev P, int64_t slots, int H, int cand_only
   P.sched[s] = item;
 }
 
+// Work list of a candidates-only plan (one block of 1024 threads).  The
+// active items of the schedule are taken in slot order (thread t owns a
+// contiguous range of slots, so the order survives the scans).  With fewer
+// active items than half the target, an item whose CSR holds n key tiles is
+// cut into c = ceil(n / C) chunks of equal length (to one tile), where C = max(
+// kSplitMinChunk, ceil(total tiles / kSplitTarget)): then sum(c) <= target +
+// items <= slots + target entries and the split items' parts number at most
+// 2 * target.  Slots past the last entry, and split slots past the last
+// split item, get item -1.
+__global__ __launch_bounds__(1024) void plan_work_kernel(PlanDev P, int slots, int grid, int H) {
+  __shared__ int smem[32];
+  __shared__ long long tiles_sh[16];
+  const int t = threadIdx.x;
+  const int per = (slots + blockDim.x - 1) / blockDim.x;
+  const int s0 = min(slots, t * per), s1 = min(slots, s0 + per);
+  auto ntiles = [&](int item) {
+    const int qg = item / H;
+    return P.qtile_ptr[qg + 1] - P.qtile_ptr[qg];
+  };
+  int act = 0;
+  long long tiles = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int item = P.sched[s];
+    if (item >= 0) {
+      ++act;
+      tiles += ntiles(item);
+    }
+  }
+  int n_act;
+  (void)block_exclusive_scan(act, smem, &n_act);
+  // block sum of the tile counts
+  long long v = tiles;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((t & 63) == 0) tiles_sh[t >> 6] = v;
+  __syncthreads();
+  long long total_tiles = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) total_tiles += tiles_sh[w];
+  const bool split = 2 * n_act < kSplitTarget;
+  const long long cl = (total_tiles + kSplitTarget - 1) / kSplitTarget;
+  const int C = (int)max((long long)kSplitMinChunk, cl);  // used only when split
+
+  int wcnt = 0, pcnt = 0, scnt = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int item = P.sched[s];
+    if (item < 0) continue;
+    const int n = ntiles(item);
+    const int c = split ? max(1, (n + C - 1) / C) : 1;
+    wcnt += c;
+    if (c > 1) { pcnt += c; ++scnt; }
+  }
+  int w_tot, p_tot, s_tot;
+  int w = block_exclusive_scan(wcnt, smem, &w_tot);
+  int part = block_exclusive_scan(pcnt, smem, &p_tot);
+  int sp = block_exclusive_scan(scnt, smem, &s_tot);
+  for (int s = s0; s < s1; ++s) {
+    const int item = P.sched[s];
+    if (item < 0) continue;
+    const int n = ntiles(item);
+    const int c = split ? max(1, (n + C - 1) / C) : 1;
+    if (c > 1) P.splits[sp++] = SplitEntry{item, part, c, 0};
+    for (int j = 0; j < c; ++j) {
+      // chunk lengths differ by at most one and none is empty (c <= n)
+      const int kb = (int)((long long)j * n / c), ke = (int)((long long)(j + 1) * n / c);
+      P.work[w++] = WorkEntry{item, kb, ke, c > 1 ? part++ : -1};
+    }
+  }
+  for (int s = w_tot + t; s < grid; s += blockDim.x) P.work[s] = WorkEntry{-1, 0, 0, -1};
+  for (int s = s_tot + t; s < kSplitTarget; s += blockDim.x) P.splits[s] = SplitEntry{-1, 0, 0, 0};
+  if (t == 0) {
+    P.totals->n_work = w_tot;
+    P.totals->n_splits = s_tot;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
@@ -333,6 +408,9 @@ hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
   if (p->slots > 0) {
     hipLaunchKernelGGL(plan_sched_kernel, dim3((unsigned)((p->slots + 255) / 256)), dim3(256), 0, s,
                        P, p->slots, p->H, (int)((p->flags & RK_QUERY_CANDIDATES_ONLY) != 0));
+    if (p->grid > p->slots)
+      hipLaunchKernelGGL(plan_work_kernel, dim3(1), dim3(1024), 0, s, P, (int)p->slots,
+                         (int)p->grid, p->H);
   }
   return hipGetLastError();
 }

@@ -47,8 +47,28 @@ struct PlanTotals {
   unsigned long long partial_tiles;
   unsigned long long empty_tiles;
   unsigned int errors;  // bit 0: segment order/kind, bit 1: time order
-  unsigned int pad[7];
+  int n_work;           // work-list entries (candidates-only plans)
+  int n_splits;         // items split into partial results
+  unsigned int pad[5];
 };
+
+// Work list of a candidates-only plan: launch slot b of the attention runs
+// CSR entries [kbeg, kend) of work item `item` (q-tile * H + head); part >= 0
+// means the item's key range is split and this slot writes partial result
+// `part`, merged by the combine kernel.
+struct WorkEntry {
+  int32_t item, kbeg, kend, part;
+};
+// An item split into parts [part0, part0 + nparts).
+struct SplitEntry {
+  int32_t item, part0, nparts, pad;
+};
+
+// Splitting: aim at about kSplitTarget launch slots of work, chunks of at
+// least kSplitMinChunk key tiles, at most kMaxParts partial results.
+constexpr int kSplitTarget = 1024;
+constexpr int kSplitMinChunk = 8;
+constexpr int kMaxParts = 2 * kSplitTarget;
 
 constexpr unsigned kErrSegment = 1u;
 constexpr unsigned kErrTime = 2u;
@@ -70,6 +90,8 @@ struct PlanDev {
   int32_t* ktile_word;     // [NT] CSR entry for the kernels: kt | (PARTIAL << 31)
   int32_t* qorder;         // [NQ]
   int32_t* sched;          // [slots]
+  WorkEntry* work;         // [slots + kSplitTarget] (candidates-only plans)
+  SplitEntry* splits;      // [kSplitTarget]
   PlanTotals* totals;
 };
 
@@ -78,6 +100,7 @@ struct PlanDev {
 struct rk_plan {
   int32_t R, T, H;
   int64_t NQ, NT, G, slots, max_queue;
+  int64_t grid;             // attention launch size: slots, or slots + kSplitTarget with a work list
   int64_t delay;
   int32_t window;
   int32_t global_tail;
@@ -91,7 +114,7 @@ struct rk_plan {
   size_t workspace_bytes;
   size_t off_req, off_qt_req, off_groups, off_queue_start, off_row_desc, off_tile_count,
       off_tile_class, off_qt_nnz, off_qt_pairs, off_qt_full, off_qtile_ptr, off_ktile_idx, off_ktile_word, off_qorder,
-      off_sched, off_totals, host_blob_bytes, total_bytes;
+      off_sched, off_work, off_splits, off_totals, host_blob_bytes, total_bytes;
   rk::PlanDev dev;
   // host copy of the first host_blob_bytes of the workspace (kept alive
   // for the asynchronous upload)
@@ -125,6 +148,7 @@ struct AttnLaunch {
   float scale;
   int H, d, T;
   bool rope_q;              // rotate Q while staging (K is already rotated)
+  float* part;              // partial results of split items, or null
   const int64_t* ts;
   const int64_t* anchors;
   RopeTab tab;
@@ -133,5 +157,9 @@ struct AttnLaunch {
 hipError_t launch_attn_reference(const rk_plan* p, const AttnLaunch& a, rk_dtype dt,
                                  hipStream_t s);
 hipError_t launch_attn_mfma_bf16_d64(const rk_plan* p, const AttnLaunch& a, hipStream_t s);
+// Merge the partial results of split items into O / LSE.  to_log2 / to_nat
+// convert the kernels' reference max into log2 / natural units.
+hipError_t launch_attn_combine(const rk_plan* p, const AttnLaunch& a, rk_dtype dt, float to_log2,
+                               float to_nat, hipStream_t s);
 
 }  // namespace rk

@@ -3,14 +3,16 @@ workspace, rotated K, O, LSE) sits between two 4 KiB canary margins filled
 with 0xA5; after the planner, the rotation and the attention have run (and
 the plan totals were read), both margins of every buffer must be unchanged.
 Covers the MFMA kernel (bf16, d = 64, fused and pre-rotated K), the plain
-kernel (fp32, d = 32 and 128) and ragged layouts with every mask mode."""
+kernel (fp32, d = 32 and 128), ragged layouts with every mask mode, and
+split serving calls, whose attention workspace also holds partial results."""
 
 import numpy as np
 import pytest
 
 torch = pytest.importorskip("torch")
 
-from rk_workloads import make_config, make_custom, random_layout  # noqa: E402
+from rk_workloads import (CANDIDATE, HISTORY, make_config, make_custom,  # noqa: E402
+                          random_layout)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +47,7 @@ class Guarded:
         return bool(torch.all(lo == CANARY).item()) and bool(torch.all(hi == CANARY).item())
 
 
-def _run_guarded(rk, wl, *, rope=True, prerotate=False, reference=False):
+def _run_guarded(rk, wl, *, rope=True, prerotate=False, reference=False, candidates_only=False):
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     esz = 2 if wl.dtype == "bf16" else 4
     T, H, d = wl.total_tokens, wl.heads, wl.d_head
@@ -56,7 +58,7 @@ def _run_guarded(rk, wl, *, rope=True, prerotate=False, reference=False):
     guards.append(("plan workspace", wsp))
     plan = rk.Plan(batch, delay=wl.delay, window=wl.window,
                    static_bidirectional=wl.static_bidirectional, num_heads=H,
-                   workspace=wsp.inner)
+                   workspace=wsp.inner, candidates_only=candidates_only)
     q, k, v = (torch.from_numpy(x).to("cuda").to(dt) for x in (wl.q, wl.k, wl.v))
     rp = dict(phi_min=wl.phi_min, dt_max=wl.dt_max, base=wl.base) if rope else None
     if prerotate:
@@ -79,7 +81,10 @@ def _run_guarded(rk, wl, *, rope=True, prerotate=False, reference=False):
     st = plan.stats()
     torch.cuda.synchronize()
     assert st["device_errors"] == 0
-    assert torch.isfinite(o.float()).all()
+    if candidates_only:
+        assert st["split_items"] > 0, "layout meant to split produced no split item"
+    else:
+        assert torch.isfinite(o.float()).all()
     for name, g in guards:
         assert g.intact(), f"{wl.name}: canary of {name} overwritten"
     plan.close()
@@ -109,3 +114,13 @@ def test_guard_bands_prerotated_and_reference(rk):
 @pytest.mark.parametrize("cfg", [3, 4])
 def test_guard_bands_workloads(rk, cfg):
     _run_guarded(rk, make_config(cfg))
+
+
+@pytest.mark.parametrize("dtype,d,reference", [("bf16", 64, False), ("bf16", 64, True),
+                                               ("f32", 128, False)])
+def test_guard_bands_split(rk, dtype, d, reference):
+    rng = np.random.default_rng(320)
+    reqs = random_layout(rng, 3, 3000, kinds=(HISTORY, CANDIDATE), allow_empty=False)
+    wl = make_custom(reqs, heads=2, d_head=d, dtype=dtype, seed=320, name="guard-split")
+    _run_guarded(rk, wl, reference=reference, candidates_only=True)
+    _run_guarded(rk, wl, rope=False, reference=reference, candidates_only=True)

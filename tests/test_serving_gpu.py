@@ -4,8 +4,9 @@ call, attention computed for the candidates' query tiles only.
 
 * The candidates-only schedule covers exactly the (query tile, head) items
   whose tile holds a CANDIDATE row.
-* Those rows are bit-identical to the full call (same tiles, same order) and
-  match the oracle; every other row of O / LSE is left untouched.
+* Those rows are bit-identical to the full call (same tiles, same order)
+  unless the item's key range was split (then within a rounding step of it)
+  and match the oracle; every other row of O / LSE is left untouched.
 * Kind-filtered rotation: rotating PROFILE+HISTORY+REALTIME, then CANDIDATE,
   in place, gives the same bits as rotating everything at once, and rows of
   other kinds are left untouched.
@@ -19,6 +20,7 @@ torch = pytest.importorskip("torch")
 import oracle  # noqa: E402
 from rk_workloads import (CANDIDATE, HISTORY, PROFILE, REALTIME, make_config,  # noqa: E402
                           make_custom, random_layout)
+from test_split_gpu import assert_close_to_unsplit, check_work_list  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -129,11 +131,18 @@ def test_candidates_only_outputs(rk, which):
     o_c, l_c = _outputs(rk, wl, cand_plan, q, cache, v, prerotated=True)
     rows = _rows_of_tiles(wl, _candidate_tiles(wl))
     other = np.setdiff1d(np.arange(wl.total_tokens), rows)
-    rows_t = torch.from_numpy(rows).cuda()
     other_t = torch.from_numpy(other).cuda()
     oc16, of16 = o_c.view(torch.int16), o_full.view(torch.int16)
-    assert torch.equal(oc16[rows_t], of16[rows_t])
-    assert torch.equal(l_c[:, rows_t], l_full[:, rows_t])
+    split = check_work_list(cand_plan, wl.heads)
+    for qt in sorted(_candidate_tiles(wl)):
+        rt = torch.from_numpy(_rows_of_tiles(wl, {qt})).cuda()
+        for h in range(wl.heads):
+            if qt * wl.heads + h in split:
+                assert_close_to_unsplit(o_c[rt, h], o_full[rt, h], "bf16")
+                assert torch.allclose(l_c[h, rt], l_full[h, rt], rtol=0, atol=1e-4)
+            else:
+                assert torch.equal(oc16[rt, h], of16[rt, h])
+                assert torch.equal(l_c[h, rt], l_full[h, rt])
     if other.size:
         assert bool((oc16[other_t] == SENTINEL_I16).all())
         assert bool((l_c[:, other_t] == 12345.0).all())
