@@ -96,6 +96,8 @@ enum { RK_TILE_EMPTY = 0, RK_TILE_PARTIAL = 1, RK_TILE_FULL = 2 };
 
 #define RK_TILE_Q 128 /* query rows per tile */
 #define RK_TILE_K 64  /* key columns per tile */
+#define RK_SPLIT_SLOTS 768 /* extra attention launch slots of a RK_QUERY_CANDIDATES_ONLY
+                              plan's work list, and the rows of its split table */
 
 /* rk_mask_params.flags */
 #define RK_STATIC_BIDIRECTIONAL 0x1u /* PROFILE+HISTORY mutually visible (MTGR static part) */
@@ -196,12 +198,16 @@ typedef struct rk_plan_info {
   size_t off_row_desc;         /* int32 [total_tokens][2]: visible keys of a query = [lo, hi) plus bit 31 of hi = self */
   size_t off_sched;            /* int32 [num_sched_slots]: work item = qtile * num_heads + head, or -1 */
   int64_t num_work_slots;      /* RK_QUERY_CANDIDATES_ONLY plans: grid size of the attention
-                                  (num_sched_slots + 1024), else 0 (the grid is the schedule) */
+                                  (num_sched_slots + RK_SPLIT_SLOTS), else 0 (the grid is the
+                                  schedule) */
   size_t off_work;             /* int32 [num_work_slots][4]: (item, first, end, part) = CSR
-                                  entries [first, end) of the item's q-tile; part >= 0 names
-                                  the partial result of a split item; item -1 = idle slot */
-  size_t off_splits;           /* int32 [1024][4]: (item, first part, parts, 0) of each split
-                                  item, item -1 past the last */
+                                  entries [first, end) of the item's q-tile (end -1: all of
+                                  them); part >= 0 names the partial result of a split item;
+                                  item -1 = idle slot.  With RK_SPLIT_SLOTS / 2 or more
+                                  scheduled items it mirrors the schedule (whole items);
+                                  with fewer it lists them in schedule order, in chunks */
+  size_t off_splits;           /* int32 [RK_SPLIT_SLOTS][4]: (item, first part, parts, 0) of
+                                  each split item, item -1 past the last */
 } rk_plan_info;
 
 /* Totals of a plan (per head). */
@@ -212,7 +218,8 @@ typedef struct rk_plan_totals {
   int64_t full_tiles;
   int64_t partial_tiles;
   int64_t empty_tiles;
-  int32_t work_entries;        /* used slots of the work list (RK_QUERY_CANDIDATES_ONLY) */
+  int32_t work_entries;        /* slots of the work list in use or mirrored from the
+                                  schedule (RK_QUERY_CANDIDATES_ONLY) */
   int32_t split_items;         /* items whose key range is split */
 } rk_plan_totals;
 
@@ -321,8 +328,8 @@ rk_status rk_time_rope(const rk_batch* b, const rk_rope_params* r, const void* x
 
 /* Workspace bytes rk_masked_attn_fwd needs for `a` on plan `p` (host only):
  * the rotated K when the call rotates K ([total_tokens][num_heads][d_head] of
- * dtype), plus, for RK_QUERY_CANDIDATES_ONLY plans, 2048 partial results of
- * 128 rows x (d_head + 2) floats (about 69 MB at d_head = 64). */
+ * dtype), plus, for RK_QUERY_CANDIDATES_ONLY plans, 2 * RK_SPLIT_SLOTS partial
+ * results of 128 rows x (d_head + 2) floats (about 52 MB at d_head = 64). */
 rk_status rk_attn_workspace_size(const rk_plan* p, const rk_attn_args* a, size_t* bytes);
 
 /*

@@ -31,6 +31,7 @@ RK_QUERY_CANDIDATES_ONLY = 0x2
 RK_ATTN_REFERENCE_KERNEL = 0x1
 RK_ATTN_K_PREROTATED = 0x2
 RK_ABI_VERSION = 2
+RK_SPLIT_SLOTS = 768  # extra work-list slots of a candidates-only plan
 
 
 class rk_batch(C.Structure):

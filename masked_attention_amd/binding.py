@@ -133,10 +133,11 @@ class Plan:
         return self._view(self.info.off_work, 4 * n, torch.int32).view(n, 4)
 
     def splits(self) -> Optional[torch.Tensor]:
-        """Split items [1024, 4] = (item, first part, parts, 0), or None."""
+        """Split items [RK_SPLIT_SLOTS, 4] = (item, first part, parts, 0), or None."""
         if int(self.info.num_work_slots) == 0:
             return None
-        return self._view(self.info.off_splits, 4 * 1024, torch.int32).view(1024, 4)
+        n = _rk.RK_SPLIT_SLOTS
+        return self._view(self.info.off_splits, 4 * n, torch.int32).view(n, 4)
 
     def stats(self, stream: Optional[torch.cuda.Stream] = None, raise_on_error: bool = True) -> dict:
         t = sized(_rk.rk_plan_totals)

@@ -36,7 +36,7 @@ struct Layout {
          host_blob = 0, off_row_desc = 0, off_tile_count = 0, off_tile_class = 0, off_qt_nnz = 0,
          off_qt_pairs = 0, off_qt_full = 0,
          off_qtile_ptr = 0, off_ktile_idx = 0, off_ktile_word = 0, off_qorder = 0, off_sched = 0,
-         off_work = 0, off_splits = 0, total = 0;
+         off_work = 0, off_splits = 0, off_act = 0, total = 0;
 };
 
 rk_status check_batch(const rk_batch* b) {
@@ -162,6 +162,7 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->off_sched = take(sizeof(int32_t) * (size_t)L->slots);
   L->off_work = take(sizeof(rk::WorkEntry) * (size_t)(L->slots + rk::kSplitTarget));
   L->off_splits = take(sizeof(rk::SplitEntry) * (size_t)rk::kSplitTarget);
+  L->off_act = take(sizeof(int32_t) * (size_t)(rk::kSplitTarget / 2));
   L->total = off;
   return RK_OK;
 }
@@ -286,6 +287,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   p->off_sched = L.off_sched;
   p->off_work = L.off_work;
   p->off_splits = L.off_splits;
+  p->off_act = L.off_act;
   p->off_totals = L.off_totals;
   p->host_blob_bytes = L.host_blob;
   p->total_bytes = L.total;
@@ -310,6 +312,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   D.sched = (int32_t*)(ws + L.off_sched);
   D.work = (rk::WorkEntry*)(ws + L.off_work);
   D.splits = (rk::SplitEntry*)(ws + L.off_splits);
+  D.act_slots = (int32_t*)(ws + L.off_act);
 
   p->host_blob = (unsigned char*)std::calloc(L.host_blob ? L.host_blob : 1, 1);
   if (!p->host_blob) {

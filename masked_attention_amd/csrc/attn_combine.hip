@@ -10,8 +10,10 @@
 // App. H, M-FALCON; the flash-decoding split of a long key range).  The
 // kernels keep m in their own units; to_log2 and to_nat convert it.
 //
-// One 256-thread workgroup per split item: two threads per query row, each
-// owning half of d_head.
+// One 512-thread workgroup per split item: four threads per query row, each
+// owning a quarter of d_head.  Parts are read four at a time (their loads in
+// flight together) and merged with the online rescaling, so the running max
+// is never re-read.
 #include <hip/hip_bf16.h>
 
 #include "rk_internal.h"
@@ -26,51 +28,72 @@ __device__ __forceinline__ void st(__hip_bfloat16* p, float v) {
   *(unsigned short*)p = (unsigned short)(u >> 16);
 }
 
+constexpr int kGroup = 4;  // parts read together
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const ReqMeta* req, const int32_t* qt_req,
+__global__ __launch_bounds__(512) void attn_combine_kernel(const ReqMeta* req, const int32_t* qt_req,
                                                            const SplitEntry* splits, AttnLaunch A,
                                                            float to_log2, float to_nat) {
+  constexpr int kQ = D / 4;       // d values of this thread
+  constexpr int kV = kQ / 4;      // float4 loads per part
+  constexpr int kStride = kTileQ * (D + 2);
   const SplitEntry se = splits[blockIdx.x];
   if (se.item < 0) return;
   const int qg = se.item / A.H;
   const int head = se.item - qg * A.H;
   const ReqMeta m = req[qt_req[qg]];
-  const int rl = threadIdx.x >> 1;
-  const int c0 = (threadIdx.x & 1) * (D / 2);
+  const int rl = threadIdx.x >> 2;
+  const int c0 = (threadIdx.x & 3) * kQ;
   const int row = (qg - m.qt_off) * kTileQ + rl;
   if (row >= m.len) return;
   const int tok = m.tok_off + row;
-  constexpr int kStride = kTileQ * (D + 2);
   const float* base = A.part + (int64_t)se.part0 * kStride;
 
-  float M = -INFINITY;
-  for (int j = 0; j < se.nparts; ++j) M = fmaxf(M, base[j * kStride + kTileQ * D + rl]);
-  float acc[D / 2];
+  float M = -INFINITY, l = 0.f;
+  float acc[kQ];
 #pragma unroll
-  for (int c = 0; c < D / 2; ++c) acc[c] = 0.f;
-  float l = 0.f;
-  if (M != -INFINITY) {
-    for (int j = 0; j < se.nparts; ++j) {
-      const float* pj = base + j * kStride;
-      const float mj = pj[kTileQ * D + rl];
-      if (mj == -INFINITY) continue;  // nothing of this chunk is visible to the row
-      const float w = exp2f((mj - M) * to_log2);
-      l = fmaf(w, pj[kTileQ * D + kTileQ + rl], l);
+  for (int c = 0; c < kQ; ++c) acc[c] = 0.f;
+  for (int j0 = 0; j0 < se.nparts; j0 += kGroup) {
+    float mj[kGroup], lj[kGroup];
+    float4 v[kGroup][kV];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      // past the last part: re-read it with weight 0
+      const float* pj = base + min(j0 + u, se.nparts - 1) * kStride;
+      mj[u] = j0 + u < se.nparts ? pj[kTileQ * D + rl] : -INFINITY;
+      lj[u] = pj[kTileQ * D + kTileQ + rl];
       const float4* o4 = (const float4*)(pj + rl * D + c0);
 #pragma unroll
-      for (int c = 0; c < D / 8; ++c) {
-        const float4 v = o4[c];
-        acc[4 * c] = fmaf(w, v.x, acc[4 * c]);
-        acc[4 * c + 1] = fmaf(w, v.y, acc[4 * c + 1]);
-        acc[4 * c + 2] = fmaf(w, v.z, acc[4 * c + 2]);
-        acc[4 * c + 3] = fmaf(w, v.w, acc[4 * c + 3]);
+      for (int c = 0; c < kV; ++c) v[u][c] = o4[c];
+    }
+    float gm = mj[0];
+#pragma unroll
+    for (int u = 1; u < kGroup; ++u) gm = fmaxf(gm, mj[u]);
+    const float Mn = fmaxf(M, gm);
+    if (Mn == -INFINITY) continue;  // nothing visible to the row so far
+    const float alpha = exp2f((M - Mn) * to_log2);  // 0 while M is -inf
+    l *= alpha;
+#pragma unroll
+    for (int c = 0; c < kQ; ++c) acc[c] *= alpha;
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      // a part that saw nothing of the row has m = -inf and weight 0
+      const float w = exp2f((mj[u] - Mn) * to_log2);
+      l = fmaf(w, lj[u], l);
+#pragma unroll
+      for (int c = 0; c < kV; ++c) {
+        acc[4 * c] = fmaf(w, v[u][c].x, acc[4 * c]);
+        acc[4 * c + 1] = fmaf(w, v[u][c].y, acc[4 * c + 1]);
+        acc[4 * c + 2] = fmaf(w, v[u][c].z, acc[4 * c + 2]);
+        acc[4 * c + 3] = fmaf(w, v[u][c].w, acc[4 * c + 3]);
       }
     }
+    M = Mn;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   T* O = (T*)A.o + (int64_t)tok * A.o_st + (int64_t)head * A.o_sh + c0;
 #pragma unroll
-  for (int c = 0; c < D / 2; ++c) st(O + c, acc[c] * inv);
+  for (int c = 0; c < kQ; ++c) st(O + c, acc[c] * inv);
   if (A.lse && c0 == 0)
     A.lse[(int64_t)head * A.T + tok] = l > 0.f ? M * to_nat + logf(l) : -INFINITY;
 }
@@ -78,8 +101,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const ReqMeta* req, c
 template <typename T, int D>
 hipError_t launch(const rk_plan* p, const AttnLaunch& a, float to_log2, float to_nat,
                   hipStream_t s) {
-  hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3((unsigned)kSplitTarget), dim3(256), 0, s,
-                     p->dev.req, p->dev.qt_req, p->dev.splits, a, to_log2, to_nat);
+  // at most kSplitTarget / 2 items are split
+  hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3((unsigned)(kSplitTarget / 2)), dim3(512), 0,
+                     s, p->dev.req, p->dev.qt_req, p->dev.splits, a, to_log2, to_nat);
   return hipGetLastError();
 }
 

@@ -307,77 +307,99 @@ __global__ void plan_sched_kernel(PlanDev P, int64_t slots, int H, int cand_only
     }
   }
   P.sched[s] = item;
-}
-
-// Work list of a candidates-only plan (one block of 1024 threads).  The
-// active items of the schedule are taken in slot order (thread t owns a
-// contiguous range of slots, so the order survives the scans).  With fewer
-// active items than half the target, an item whose CSR holds n key tiles is
-// cut into c = ceil(n / C) chunks of equal length (to one tile), where C = max(
-// kSplitMinChunk, ceil(total tiles / kSplitTarget)): then sum(c) <= target +
-// items <= slots + target entries and the split items' parts number at most
-// 2 * target.  Slots past the last entry, and split slots past the last
-// split item, get item -1.
-__global__ __launch_bounds__(1024) void plan_work_kernel(PlanDev P, int slots, int grid, int H) {
-  __shared__ int smem[32];
-  __shared__ long long tiles_sh[16];
-  const int t = threadIdx.x;
-  const int per = (slots + blockDim.x - 1) / blockDim.x;
-  const int s0 = min(slots, t * per), s1 = min(slots, s0 + per);
-  auto ntiles = [&](int item) {
-    const int qg = item / H;
-    return P.qtile_ptr[qg + 1] - P.qtile_ptr[qg];
-  };
-  int act = 0;
-  long long tiles = 0;
-  for (int s = s0; s < s1; ++s) {
-    const int item = P.sched[s];
+  if (cand_only) {
+    // count the active slots (one atomic per wave) and keep the first
+    // kSplitTarget / 2 of them, in arrival order, for the work list
+    const unsigned long long act = __ballot(item >= 0);
     if (item >= 0) {
-      ++act;
-      tiles += ntiles(item);
+      const int lane = threadIdx.x & 63;
+      const int below = __popcll(act & ((1ull << lane) - 1ull));
+      int base = 0;
+      if (below == 0) base = atomicAdd(&P.totals->n_act, __popcll(act));
+      base = __shfl(base, __builtin_ctzll(act), 64);
+      const int idx = base + below;
+      if (idx < kSplitTarget / 2) P.act_slots[idx] = (int)s;
     }
   }
-  int n_act;
-  (void)block_exclusive_scan(act, smem, &n_act);
-  // block sum of the tile counts
-  long long v = tiles;
+}
+
+// Work list of a candidates-only plan (blocks of 1024 threads over the
+// launch slots).  With at least kSplitTarget / 2 active items the list
+// mirrors the schedule (whole items, kend = -1).  With fewer, block 0 builds
+// it alone from the active slots the schedule kernel collected: they are put
+// back in slot order (rank by slot), and an item whose CSR holds n key tiles
+// is cut into c = ceil(n / C) chunks of equal length (to one tile), where
+// C = max(kSplitMinChunk, ceil(total tiles / kSplitTarget)).  Then sum(c) <=
+// target + items < 1.5 * target entries, and the parts of split items number
+// fewer than kMaxParts.  Slots past the last entry, and split slots past the
+// last split item, get item -1.
+__global__ __launch_bounds__(1024) void plan_work_kernel(PlanDev P, int slots, int grid, int H) {
+  constexpr int kMaxAct = kSplitTarget / 2;
+  constexpr int kHead = 2 * kSplitTarget;  // block 0 owns slots [0, kHead) when splitting
+  __shared__ int smem[32];
+  __shared__ long long tiles_sh[16];
+  __shared__ int s_slot[kMaxAct], s_item[kMaxAct], s_n[kMaxAct];
+  const int t = threadIdx.x;
+  const int n_act = P.totals->n_act;
+  const bool split = n_act < kMaxAct;
+  if (!split) {
+    const int s = blockIdx.x * blockDim.x + t;
+    if (s < grid) P.work[s] = s < slots ? WorkEntry{P.sched[s], 0, -1, -1} : WorkEntry{-1, 0, 0, -1};
+    if (blockIdx.x == 0) {
+      for (int k = t; k < kSplitTarget; k += blockDim.x) P.splits[k] = SplitEntry{-1, 0, 0, 0};
+      if (t == 0) {
+        P.totals->n_work = slots;
+        P.totals->n_splits = 0;
+      }
+    }
+    return;
+  }
+  if (blockIdx.x > 0) {
+    const int s = blockIdx.x * blockDim.x + t;
+    if (s >= kHead && s < grid) P.work[s] = WorkEntry{-1, 0, 0, -1};
+    return;
+  }
+  int slot = 0x7fffffff, item = -1, n = 0;
+  if (t < n_act) {
+    slot = P.act_slots[t];
+    item = P.sched[slot];
+    const int qg = item / H;
+    n = P.qtile_ptr[qg + 1] - P.qtile_ptr[qg];
+    s_slot[t] = slot;
+  }
+  long long v = n;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   if ((t & 63) == 0) tiles_sh[t >> 6] = v;
   __syncthreads();
   long long total_tiles = 0;
   for (int w = 0; w < (int)(blockDim.x >> 6); ++w) total_tiles += tiles_sh[w];
-  const bool split = 2 * n_act < kSplitTarget;
+  if (t < n_act) {
+    int r = 0;
+    for (int u = 0; u < n_act; ++u) r += s_slot[u] < slot;
+    s_item[r] = item;
+    s_n[r] = n;
+  }
+  __syncthreads();
+  if (t < n_act) {
+    item = s_item[t];
+    n = s_n[t];
+  }
   const long long cl = (total_tiles + kSplitTarget - 1) / kSplitTarget;
-  const int C = (int)max((long long)kSplitMinChunk, cl);  // used only when split
-
-  int wcnt = 0, pcnt = 0, scnt = 0;
-  for (int s = s0; s < s1; ++s) {
-    const int item = P.sched[s];
-    if (item < 0) continue;
-    const int n = ntiles(item);
-    const int c = split ? max(1, (n + C - 1) / C) : 1;
-    wcnt += c;
-    if (c > 1) { pcnt += c; ++scnt; }
-  }
+  const int C = (int)max((long long)kSplitMinChunk, cl);
+  const int c = t < n_act ? max(1, (n + C - 1) / C) : 0;
   int w_tot, p_tot, s_tot;
-  int w = block_exclusive_scan(wcnt, smem, &w_tot);
-  int part = block_exclusive_scan(pcnt, smem, &p_tot);
-  int sp = block_exclusive_scan(scnt, smem, &s_tot);
-  for (int s = s0; s < s1; ++s) {
-    const int item = P.sched[s];
-    if (item < 0) continue;
-    const int n = ntiles(item);
-    const int c = split ? max(1, (n + C - 1) / C) : 1;
-    if (c > 1) P.splits[sp++] = SplitEntry{item, part, c, 0};
-    for (int j = 0; j < c; ++j) {
-      // chunk lengths differ by at most one and none is empty (c <= n)
-      const int kb = (int)((long long)j * n / c), ke = (int)((long long)(j + 1) * n / c);
-      P.work[w++] = WorkEntry{item, kb, ke, c > 1 ? part++ : -1};
-    }
+  int w = block_exclusive_scan(c, smem, &w_tot);
+  int part = block_exclusive_scan(c > 1 ? c : 0, smem, &p_tot);
+  const int sp = block_exclusive_scan(c > 1 ? 1 : 0, smem, &s_tot);
+  if (c > 1) P.splits[sp] = SplitEntry{item, part, c, 0};
+  for (int j = 0; j < c; ++j) {
+    // chunk lengths differ by at most one and none is empty (c <= n)
+    const int kb = (int)((long long)j * n / c), ke = (int)((long long)(j + 1) * n / c);
+    P.work[w++] = WorkEntry{item, kb, ke, c > 1 ? part++ : -1};
   }
-  for (int s = w_tot + t; s < grid; s += blockDim.x) P.work[s] = WorkEntry{-1, 0, 0, -1};
-  for (int s = s_tot + t; s < kSplitTarget; s += blockDim.x) P.splits[s] = SplitEntry{-1, 0, 0, 0};
+  for (int s = w_tot + t; s < min(grid, kHead); s += blockDim.x) P.work[s] = WorkEntry{-1, 0, 0, -1};
+  for (int k = s_tot + t; k < kSplitTarget; k += blockDim.x) P.splits[k] = SplitEntry{-1, 0, 0, 0};
   if (t == 0) {
     P.totals->n_work = w_tot;
     P.totals->n_splits = s_tot;
@@ -409,8 +431,8 @@ hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
     hipLaunchKernelGGL(plan_sched_kernel, dim3((unsigned)((p->slots + 255) / 256)), dim3(256), 0, s,
                        P, p->slots, p->H, (int)((p->flags & RK_QUERY_CANDIDATES_ONLY) != 0));
     if (p->grid > p->slots)
-      hipLaunchKernelGGL(plan_work_kernel, dim3(1), dim3(1024), 0, s, P, (int)p->slots,
-                         (int)p->grid, p->H);
+      hipLaunchKernelGGL(plan_work_kernel, dim3((unsigned)((p->grid + 1023) / 1024)), dim3(1024), 0,
+                         s, P, (int)p->slots, (int)p->grid, p->H);
   }
   return hipGetLastError();
 }

@@ -49,7 +49,8 @@ struct PlanTotals {
   unsigned int errors;  // bit 0: segment order/kind, bit 1: time order
   int n_work;           // work-list entries (candidates-only plans)
   int n_splits;         // items split into partial results
-  unsigned int pad[5];
+  int n_act;            // active schedule slots (candidates-only plans)
+  unsigned int pad[4];
 };
 
 // Work list of a candidates-only plan: launch slot b of the attention runs
@@ -64,9 +65,10 @@ struct SplitEntry {
   int32_t item, part0, nparts, pad;
 };
 
-// Splitting: aim at about kSplitTarget launch slots of work, chunks of at
-// least kSplitMinChunk key tiles, at most kMaxParts partial results.
-constexpr int kSplitTarget = 1024;
+// Splitting: aim at about kSplitTarget launch slots of work (one round of
+// the attention kernel at three workgroups per CU on 256 CUs), chunks of at
+// least kSplitMinChunk key tiles, fewer than kMaxParts partial results.
+constexpr int kSplitTarget = RK_SPLIT_SLOTS;
 constexpr int kSplitMinChunk = 8;
 constexpr int kMaxParts = 2 * kSplitTarget;
 
@@ -92,6 +94,7 @@ struct PlanDev {
   int32_t* sched;          // [slots]
   WorkEntry* work;         // [slots + kSplitTarget] (candidates-only plans)
   SplitEntry* splits;      // [kSplitTarget]
+  int32_t* act_slots;      // [kSplitTarget / 2] active schedule slots, arrival order
   PlanTotals* totals;
 };
 
@@ -114,7 +117,7 @@ struct rk_plan {
   size_t workspace_bytes;
   size_t off_req, off_qt_req, off_groups, off_queue_start, off_row_desc, off_tile_count,
       off_tile_class, off_qt_nnz, off_qt_pairs, off_qt_full, off_qtile_ptr, off_ktile_idx, off_ktile_word, off_qorder,
-      off_sched, off_work, off_splits, off_totals, host_blob_bytes, total_bytes;
+      off_sched, off_work, off_splits, off_act, off_totals, host_blob_bytes, total_bytes;
   rk::PlanDev dev;
   // host copy of the first host_blob_bytes of the workspace (kept alive
   // for the asynchronous upload)

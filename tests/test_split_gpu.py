@@ -5,9 +5,11 @@ With few (query tile, head) items to run, each item's CSR key range is cut
 into chunks run by separate workgroups; a merge pass rescales their partial
 softmax results to a common max and sums them.
 
-* The work list covers every scheduled item's CSR entries exactly once, in
+* With fewer than RK_SPLIT_SLOTS / 2 scheduled items, the work list covers
+  every scheduled item's CSR entries exactly once, in schedule order, in
   contiguous chunks whose lengths differ by at most one; split items number
-  their partial results consecutively and the split table names them.
+  their partial results consecutively and the split table names them.  With
+  more, it mirrors the schedule.
 * Outputs of split items match the oracle to the parity bar and the unsplit
   call to a bf16 / fp32 rounding step; unsplit items stay bit-identical.
   Covered for the MFMA kernel with Q pre-scaled (time RoPE) and raw (no
@@ -31,6 +33,7 @@ F32_TOL = 1e-4
 BF16_MAX_ABS = 2e-2
 BF16_REL_L2 = 1e-2
 SENTINEL_I16 = 0x7FC1
+SPLIT_SLOTS = 768  # RK_SPLIT_SLOTS
 
 
 @pytest.fixture(scope="module")
@@ -74,10 +77,18 @@ def check_work_list(plan, H):
     qptr = plan.qtile_ptr().cpu().numpy()
     st = plan.stats()
     nw, ns = st["work_entries"], st["split_items"]
-    assert work.shape[0] == sched.shape[0] + 1024
+    assert work.shape[0] == sched.shape[0] + SPLIT_SLOTS
     assert 0 <= nw <= work.shape[0]
     assert (work[nw:, 0] == -1).all()
     items = sched[sched >= 0]
+    if items.size >= SPLIT_SLOTS // 2:
+        # enough items to fill the chip: whole items, the schedule's own order
+        assert nw == sched.shape[0] and ns == 0
+        assert (work[:nw, 0] == sched).all()
+        assert (work[:nw, 1] == 0).all() and (work[:nw, 2] == -1).all()
+        assert (work[:nw, 3] == -1).all()
+        assert (splits[:, 0] == -1).all()
+        return {}
     pos, split, parts_seen = 0, [], []
     for it in items:
         n = int(qptr[it // H + 1] - qptr[it // H])
@@ -253,9 +264,10 @@ def test_split_rows_seeing_nothing(rk):
 
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_split_work_list_workloads(rk, cfg):
-    """The serving workload (3) and the 8 x (20000+1) causal workload (5):
-    work-list invariants on the real shapes; on workload 5 every item
-    splits (64 items, 313 key tiles each)."""
+    """The serving workload (3: 1024 items, the schedule mirrored) and the
+    8 x (20000+1) causal workload (5): work-list invariants on the real
+    shapes; on workload 5 every item splits (64 items, 313 key tiles each,
+    chunks of at most C = max(8, ceil(total / RK_SPLIT_SLOTS)) tiles)."""
     wl = make_config(cfg, with_qkv=False)
     batch = rk.Batch.from_workload(wl)
     plan = rk.Plan(batch, delay=wl.delay, window=wl.window,
@@ -263,5 +275,10 @@ def test_split_work_list_workloads(rk, cfg):
                    candidates_only=True)
     split = check_work_list(plan, wl.heads)
     if cfg == 5:
-        assert len(split) == 64 and all(c == 16 for c in split.values())
+        C = max(8, -(-64 * 313 // SPLIT_SLOTS))
+        c = -(-313 // C)
+        assert len(split) == 64 and all(v == c for v in split.values())
+        assert plan.stats()["work_entries"] == 64 * c
+    else:
+        assert not split
     plan.close()
