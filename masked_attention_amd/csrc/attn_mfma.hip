@@ -11,11 +11,12 @@
 //   O^T (64 d x 32 queries) += V_tile^T * P^T                  8 x mfma 32x32x16
 // With time RoPE, Q is loaded pre-multiplied by scale * log2(e) (folded in
 // before its single bf16 rounding), so the scores come out of the matrix
-// core in log2 units.  m is the row's reference max; it is not tracked per
-// tile but re-derived from the tile's scores only when a lane's tile sum of
-// P leaves [0, 2^32] or is not a number, or when a row sees its first key.
-// Any P kept is therefore <= 2^32, far from fp32 overflow, and bf16 P keeps
-// its relative precision at any magnitude.
+// core in log2 units.  m is the row's reference (0 at the start); it is
+// not tracked per tile but re-derived from the tile's scores only when a
+// lane's tile sum of P exceeds 2^32 or is not a number, or falls below
+// 2^-32 while the lane has accumulated nothing.  Any P kept is therefore
+// <= 2^32, far from fp32 overflow, and bf16 P keeps its relative precision
+// at any magnitude.
 //
 // Operand layouts (v_mfma_f32_32x32x16_bf16, lane l, half h = l / 32):
 //   A[m][k]: lane holds m = l % 32, k = 8h .. 8h+7
@@ -48,6 +49,9 @@ constexpr int TILE_ELEMS = kTileK * D;  // 64 rows x 64 bf16 = 8 KB per K or V t
 // A lane's tile sum above this (or not a number) makes the wave re-derive
 // the reference max.
 constexpr float kMaxTileSum = 4294967296.f;  // 2^32
+// A lane with nothing accumulated whose tile sum is below this re-derives
+// the reference max (the row's P would otherwise lose range).
+constexpr float kMinTileSum = 2.3283064365386963e-10f;  // 2^-32
 constexpr unsigned kBufferFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
 struct PlanView {
@@ -106,22 +110,39 @@ __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
 
 // Q fragment: lane holds Q[row][16 s + 8 hh .. +7] * qmul, s = 0..3,
 // rotated by time RoPE when asked (fp32 math, hardware sin/cos on a phase
-// reduced to [-1/2, 1/2] revolution), rounded once to bf16.
-__device__ __forceinline__ void load_q(bf16x8 (&qb)[4], const AttnLaunch& A, const double* wtab,
-                                       int tokq, bool valid, int head, int req, int hh,
-                                       float qmul) {
-  const unsigned short* Qp = (const unsigned short*)A.q + (int64_t)tokq * A.q_st + (int64_t)head * A.q_sh;
-  double dtd = 0.0;
-  if (A.rope_q && valid) dtd = (double)(A.ts[tokq] - A.anchors[req]);
+// reduced to [-1/2, 1/2] revolution), rounded once to bf16.  The raw
+// loads are issued first (QRaw) and consumed later (finish_q), so that the
+// first key tile's copies are in flight while Q arrives and is rotated.
+struct QRaw {
+  uint4 v[4];
+  int64_t t;  // timestamp of the row
+  int2 dsc;   // row descriptor
+};
+
+// Loads without branches: a row past the end of the request reads the
+// request's last token and is zeroed in finish_q (it is never written).
+__device__ __forceinline__ QRaw load_q_raw(const AttnLaunch& A, const int2* row_desc, int tokq_c,
+                                           int head, int hh, bool rope) {
+  QRaw r;
+  const unsigned short* Qp = (const unsigned short*)A.q + (int64_t)tokq_c * A.q_st + (int64_t)head * A.q_sh;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) r.v[s] = *(const uint4*)(Qp + 16 * s + 8 * hh);
+  r.t = rope ? A.ts[tokq_c] : 0;
+  r.dsc = row_desc[tokq_c];
+  return r;
+}
+
+template <bool kRope>
+__device__ __forceinline__ void finish_q(bf16x8 (&qb)[4], const QRaw& raw, bool valid,
+                                         int64_t anchor, const double* wtab, int hh, float qmul) {
+  const double dtd = (double)(raw.t - anchor);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (valid) raw = *(const uint4*)(Qp + 16 * s + 8 * hh);
-    unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
+    unsigned w[4] = {raw.v[s].x, raw.v[s].y, raw.v[s].z, raw.v[s].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float x0 = bf_lo(w[j]), x1 = bf_hi(w[j]);
-      if (A.rope_q) {
+      if (kRope) {
         const int i = 8 * s + 4 * hh + j;  // pair index
         const double rev = dtd * wtab[i];
         const float f = (float)(rev - rint(rev));
@@ -131,7 +152,7 @@ __device__ __forceinline__ void load_q(bf16x8 (&qb)[4], const AttnLaunch& A, con
         x0 = y0;
         x1 = y1;
       }
-      w[j] = pack_bf16x2(x0 * qmul, x1 * qmul);
+      w[j] = valid ? pack_bf16x2(x0 * qmul, x1 * qmul) : 0u;
     }
     qb[s] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
   }
@@ -269,13 +290,14 @@ __device__ __forceinline__ bool row_sees(int kt, bool partial, int lo, int hi, i
 // products and mul = scale * log2(e) is applied before exp2.
 //
 // The QK product starts from negm, which holds -m for the lane's row in
-// all 16 registers: m = mref, or 0 while the row is fresh (mref = -inf: no
-// visible key seen yet), so the fast path takes P = exp2(S) as it comes
-// out of the matrix core.  The wave re-derives the reference from this
-// tile's shifted scores instead when a lane's tile sum leaves [0, 2^32]
-// (or is not a number), or when a fresh row sees a key of this tile: m
-// moves up by the tile's excess over it (O and l rescaled), or to the
-// tile's max for a fresh row.
+// all 16 registers (m starts at 0), so the fast path takes P = exp2(S) as
+// it comes out of the matrix core.  The wave re-derives the reference from
+// this tile's shifted scores instead when a lane's tile sum exceeds 2^32
+// (or is not a number), or when a lane that has accumulated nothing sees a
+// key of this tile and its sum is below 2^-32 (P would lose range).  A row
+// with nothing accumulated (O = 0 and l = 0) moves m to the tile's max, up
+// or down; any other row moves m up by the tile's excess over it, with O
+// and l rescaled.
 template <bool kPreScaled>
 __device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, float& mref,
                                           float& lsum, const unsigned short* kb,
@@ -287,18 +309,20 @@ __device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, 
   if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
   bf16x8 pb[4];
   float ts = probs<false, !kPreScaled>(pb, s0, s1, 0.f, mul);
-  const bool fresh = mref == -INFINITY;
-  if (__any(!(ts <= kMaxTileSum) || (fresh && row_sees(kt, partial, lo, hi, self, row)))) {
+  const bool big = !(ts <= kMaxTileSum);
+  const bool tiny =
+      lsum == 0.f && ts < kMinTileSum && row_sees(kt, partial, lo, hi, self, row);
+  if (__any(big || tiny)) {
     float mx = s0[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float lrow = lsum + __shfl_xor(lsum, 32, 64);
     float sh;
-    if (fresh) {
-      sh = mx == -INFINITY ? 0.f : mx;
-      mref = mx;  // stays -inf when nothing of this tile is visible
+    if (lrow == 0.f) {
+      sh = mx == -INFINITY ? 0.f : mx;  // nothing of this tile visible: m stays
     } else {
       sh = fmaxf(mx, 0.f);
       if (sh > 0.f) {
@@ -307,11 +331,10 @@ __device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) { o0[r] *= alpha; o1[r] *= alpha; }
       }
-      mref += sh;
     }
-    const float nm = mref == -INFINITY ? 0.f : -mref;
+    mref += sh;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) negm[r] = nm;
+    for (int r = 0; r < 16; ++r) negm[r] = -mref;
     ts = probs<true, !kPreScaled>(pb, s0, s1, sh, mul);
   }
   lsum += ts;
@@ -397,15 +420,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   __syncthreads();
 
   const float sl2 = A.scale * 1.4426950408889634f;  // scale * log2(e)
-  bf16x8 q[4];
-  load_q(q, A, wtab, tokq, rvalid, head, req, hh, kPreScaled ? sl2 : 1.f);
-  int lo = 0, hi = 0, self = 0;
-  if (rvalid) {
-    const int2 dsc = P.row_desc[tokq];
-    lo = dsc.x;
-    hi = dsc.y & 0x7fffffff;
-    self = dsc.y < 0;
-  }
+  // Q's loads go out first, then the first key tile's copies; Q is rotated
+  // while those copies land.
+  const QRaw qraw = load_q_raw(A, P.row_desc, m.tok_off + min(row, L - 1), head, hh, kPreScaled);
+  const int64_t anchor = kPreScaled ? ldc(A.anchors, req) : 0;
 
   const char* Kb = (const char*)((const unsigned short*)A.k + (int64_t)m.tok_off * A.k_st + (int64_t)head * A.k_sh);
   const char* Vb = (const char*)((const unsigned short*)A.v + (int64_t)m.tok_off * A.v_st + (int64_t)head * A.v_sh);
@@ -416,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   f32x16 o0, o1, negm;
 #pragma unroll
   for (int r = 0; r < 16; ++r) { o0[r] = 0.f; o1[r] = 0.f; negm[r] = 0.f; }
-  float mref = -INFINITY, lsum = 0.f;
+  float mref = 0.f, lsum = 0.f;
 
   const int e0 = ldc(P.qtile_ptr, qg) + kbeg;
   const int n = kend >= 0 ? kend - kbeg : ldc(P.qtile_ptr, qg + 1) - e0;
@@ -425,12 +443,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   // just before the barrier that ends the iteration.  The loop is unrolled
   // by two so each stage is a distinct LDS object.  The copy issued in the
   // last iteration re-reads the last tile into the idle stage (no branch
-  // around loads).
-  int w_cur = 0;
-  if (n > 0) {
-    w_cur = ldc(P.ktile_word, e0);
-    tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_cur & 0x7fffffff, L, wv);
-  }
+  // around loads).  An item without key tiles still copies the request's
+  // first tile (in bounds, never read), so the copies are unconditional and
+  // Q's loads can be waited for without waiting for them.
+  const int w_cur0 = n > 0 ? ldc(P.ktile_word, e0) : 0;
+  int w_cur = w_cur0;
+  tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_cur0 & 0x7fffffff, L, wv);
+  bf16x8 q[4];
+  finish_q<kPreScaled>(q, qraw, rvalid, anchor, wtab, hh, kPreScaled ? sl2 : 1.f);
+  const int lo = rvalid ? qraw.dsc.x : 0;
+  const int hi = rvalid ? qraw.dsc.y & 0x7fffffff : 0;
+  const int self = rvalid && qraw.dsc.y < 0;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -471,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
           make_float4(o1[4 * g], o1[4 * g + 1], o1[4 * g + 2], o1[4 * g + 3]);
     }
     if (hh == 0) {
-      pp[kTileQ * D + rl] = mref;
+      pp[kTileQ * D + rl] = ltot > 0.f ? mref : -INFINITY;  // -inf: nothing seen
       pp[kTileQ * D + kTileQ + rl] = ltot;
     }
     return;

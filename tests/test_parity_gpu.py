@@ -473,3 +473,35 @@ def test_attention_dominant_key(rk, rope):
     fin = np.isfinite(ref_lse)
     assert np.array_equal(np.isfinite(lse), fin)
     assert np.all(np.abs(lse[fin] - ref_lse[fin]) <= 2e-2 + 2.0 ** -7 * np.abs(ref_lse[fin]))
+
+
+@pytest.mark.parametrize("rope", [True, False], ids=["rope", "norope"])
+def test_attention_scores_far_below_zero(rk, rope):
+    """Every score of every row lies about 200 log2 units below zero
+    (dimensions 0..7: query +12, key -12, the four lowest-frequency RoPE
+    pairs, which turn by < 1e-3 rad over the span).  exp2 of such a score
+    underflows fp32, so the kernel must move each row's reference down to
+    its first visible tile's max; softmax is shift invariant, so the output
+    is an ordinary weighted mean of V and the LSE is about -144."""
+    rng = np.random.default_rng(47)
+    reqs = [
+        [(HISTORY, np.sort(rng.integers(NOW - 300 * 86400, NOW - 86400, 700))),
+         (REALTIME, np.sort(rng.integers(NOW - 86400, NOW, 40))),
+         (CANDIDATE, rng.integers(NOW - 86400, NOW, 30))],
+        [(PROFILE, np.full(5, NOW - 200 * 86400)),
+         (HISTORY, np.sort(rng.integers(NOW - 200 * 86400, NOW - 86400, 300)))],
+    ]
+    wl = make_custom(reqs, heads=2, d_head=64, dtype="bf16", seed=47, delay=3600)
+    wl.q[:, :, :8] = 12.0
+    wl.k[:, :, :8] = -12.0
+    from rk_workloads import bf16_round
+    wl.q = bf16_round(wl.q.astype(np.float32))
+    wl.k = bf16_round(wl.k.astype(np.float32))
+    plan, o, lse = _run(rk, wl, rope=rope)
+    ref, ref_lse = _oracle_full(wl, rope=rope)
+    _check(wl, o, ref)
+    fin = np.isfinite(ref_lse)
+    assert fin.sum() > 0.9 * fin.size
+    assert np.all(ref_lse[fin] < -100)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.all(np.abs(lse[fin] - ref_lse[fin]) <= 2e-2 + 2.0 ** -7 * np.abs(ref_lse[fin]))
