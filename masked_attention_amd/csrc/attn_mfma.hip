@@ -134,7 +134,7 @@ __device__ __forceinline__ QRaw load_q_raw(const AttnLaunch& A, const int2* row_
 
 template <bool kRope>
 __device__ __forceinline__ void finish_q(bf16x8 (&qb)[4], const QRaw& raw, bool valid,
-                                         int64_t anchor, const double* wtab, int hh, float qmul) {
+                                         int64_t anchor, const RopeTab& tab, int hh, float qmul) {
   const double dtd = (double)(raw.t - anchor);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -143,8 +143,9 @@ __device__ __forceinline__ void finish_q(bf16x8 (&qb)[4], const QRaw& raw, bool 
     for (int j = 0; j < 4; ++j) {
       float x0 = bf_lo(w[j]), x1 = bf_hi(w[j]);
       if (kRope) {
-        const int i = 8 * s + 4 * hh + j;  // pair index
-        const double rev = dtd * wtab[i];
+        // pair 8 s + 4 hh + j: both candidates are uniform loads, hh picks
+        const double w = hh ? tab.w_rev[8 * s + 4 + j] : tab.w_rev[8 * s + j];
+        const double rev = dtd * w;
         const float f = (float)(rev - rint(rev));
         const float sn = __builtin_amdgcn_sinf(f);
         const float cs = __builtin_amdgcn_cosf(f);
@@ -379,7 +380,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   // tell the buffer being filled from the one being read.
   __shared__ __attribute__((aligned(1024))) unsigned short K0[TILE_ELEMS], K1[TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) unsigned short V0[TILE_ELEMS], V1[TILE_ELEMS];
-  __shared__ double wtab[D / 2];
 
   // a slot runs a whole item (schedule) or a CSR range of one (work list)
   int item, kbeg = 0, kend = -1, part = -1;
@@ -409,16 +409,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   const bool rvalid = row < L;
   const int tokq = m.tok_off + row;
 
-  if (A.rope_q && tid < D / 2) wtab[tid] = A.tab.w_rev[tid];
-  // Start the V stages from zeros: whatever a copy leaves unwritten stays
-  // finite, so a masked key (P = 0) adds exactly 0 to O.
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    *(uint4*)&V0[8 * (tid + kThreads * j)] = make_uint4(0, 0, 0, 0);
-    *(uint4*)&V1[8 * (tid + kThreads * j)] = make_uint4(0, 0, 0, 0);
-  }
-  __syncthreads();
-
   const float sl2 = A.scale * 1.4426950408889634f;  // scale * log2(e)
   // Q's loads go out first, then the first key tile's copies; Q is rotated
   // while those copies land.
@@ -430,6 +420,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   // row strides in bytes (32-bit per-lane offsets: the host limits strides)
   const unsigned kst_b = (unsigned)A.k_st * 2u, vst_b = (unsigned)A.v_st * 2u;
   const CopyMap cm = copy_map(wv, lane, kst_b, vst_b);
+  // Each wave zeroes the V rows its own copies fill (rows 16 wv .. +15 of
+  // both stages) and waits for those writes before its first copy: whatever
+  // a copy leaves unwritten then stays finite, so a masked key (P = 0) adds
+  // exactly 0 to O.  No other wave touches these rows, so no barrier.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    *(uint4*)&V0[(2 * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
+    *(uint4*)&V1[(2 * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
   f32x16 o0, o1, negm;
 #pragma unroll
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   int w_cur = w_cur0;
   tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_cur0 & 0x7fffffff, L, wv);
   bf16x8 q[4];
-  finish_q<kPreScaled>(q, qraw, rvalid, anchor, wtab, hh, kPreScaled ? sl2 : 1.f);
+  finish_q<kPreScaled>(q, qraw, rvalid, anchor, A.tab, hh, kPreScaled ? sl2 : 1.f);
   const int lo = rvalid ? qraw.dsc.x : 0;
   const int hi = rvalid ? qraw.dsc.y & 0x7fffffff : 0;
   const int self = rvalid && qraw.dsc.y < 0;
