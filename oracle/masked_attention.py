@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute this module; only the test suite, the smoke check and the CPU-baseline
 leg of the benchmark use it.  It shares no code with the HIP library: it
 builds the explicit visibility matrix of every request pair by pair and runs
-plain softmax attention in float64.
+plain softmax attention in float64, and takes the gradients of that
+definition by the chain rule for the backward.
 
 Sources (pages as they appear in the reference text):
 
@@ -273,6 +274,103 @@ def attention_rows(req_offsets, seg_kind, timestamps, q, k, v, tokens: np.ndarra
         o[sel] = oh
         lse[sel] = lh
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Backward of the masked softmax attention (gradients of a scalar loss)
+# ---------------------------------------------------------------------------
+
+def masked_softmax_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                                      do: np.ndarray, vis: np.ndarray, scale: float
+                                      ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of a loss with upstream gradient do = dLoss/dO, one head.
+
+    O = P v with P the row softmax of S = q k^T * scale + M (M = 0 where vis,
+    -inf elsewhere; a row with no visible key has P = 0 and O = 0).  The
+    chain rule through these three steps gives
+      dv = P^T do,   dP = do v^T,
+      dS_ij = P_ij (dP_ij - sum_l P_il dP_il)      (softmax Jacobian per row),
+      dq = scale * dS k,   dk = scale * dS^T q.
+    Returns (dq [Lq, d], dk [Lk, d], dv [Lk, d]).
+    """
+    s = (q @ k.T) * scale
+    s = np.where(vis, s, -np.inf)
+    has = vis.any(axis=1)
+    m = np.where(has, s.max(axis=1, initial=-np.inf), 0.0)
+    e = np.exp(s - m[:, None])
+    denom = np.where(has, e.sum(axis=1), 1.0)
+    p = e / denom[:, None]                 # rows without a visible key: all 0
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = (ds @ k) * scale
+    dk = (ds.T @ q) * scale
+    return dq, dk, dv
+
+
+def time_rope_transpose(g: np.ndarray, t: np.ndarray, *, phi_min: float, dt_max: float,
+                        base: float) -> np.ndarray:
+    """Apply the transpose of the time-RoPE rotation to gradients g [N, ..., d].
+
+    Each pair rotation is orthogonal, so its transpose is the rotation by
+    -alpha_i(t): the gradient with respect to the unrotated input is
+    R(t)^T times the gradient with respect to the rotated one.
+    """
+    return time_rope(g, -np.asarray(t, dtype=np.float64), phi_min=phi_min, dt_max=dt_max,
+                     base=base)
+
+
+def attention_backward(req_offsets: np.ndarray, seg_kind: np.ndarray, timestamps: np.ndarray,
+                       q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, *,
+                       delay: int, window: int, static_bidirectional: bool,
+                       rope: Optional[Dict[str, float]] = None,
+                       rope_times: Optional[np.ndarray] = None, scale: Optional[float] = None,
+                       heads: Optional[np.ndarray] = None, requests: Optional[np.ndarray] = None,
+                       global_tail: int = 0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients (dq, dk, dv) [T, H, d] of the masked attention forward of
+    attention_forward with respect to the unrotated q, k and v, for the
+    upstream gradient do [T, H, d], in float64.
+
+    With `rope`, q and k are rotated as in the forward; the gradients with
+    respect to the rotated vectors are taken back through the rotation by
+    time_rope_transpose.  Every request uses its full explicit L x L mask.
+    `heads` / `requests` restrict the work (other entries stay 0).
+    """
+    T, H, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    dq = np.zeros((T, H, d), np.float64)
+    dk = np.zeros((T, H, d), np.float64)
+    dv = np.zeros((T, H, d), np.float64)
+    heads = np.arange(H) if heads is None else np.asarray(heads)
+    R = req_offsets.shape[0] - 1
+    requests = np.arange(R) if requests is None else np.asarray(requests)
+    if rope is not None:
+        tr = timestamps if rope_times is None else rope_times
+    for r in requests:
+        a, b = int(req_offsets[r]), int(req_offsets[r + 1])
+        if b == a:
+            continue
+        vis = visibility(seg_kind[a:b], timestamps[a:b], delay=delay, window=window,
+                         static_bidirectional=static_bidirectional, global_tail=global_tail)
+        qr, kr = q[a:b], k[a:b]
+        if rope is not None:
+            qr = time_rope(qr, tr[a:b], **rope)
+            kr = time_rope(kr, tr[a:b], **rope)
+        gq = np.zeros((b - a, H, d))
+        gk = np.zeros((b - a, H, d))
+        for h in heads:
+            gq[:, h], gk[:, h], dv[a:b, h] = masked_softmax_attention_backward(
+                qr[:, h], kr[:, h], v[a:b, h], do[a:b, h], vis, scale)
+        if rope is not None:
+            gq = time_rope_transpose(gq, tr[a:b], **rope)
+            gk = time_rope_transpose(gk, tr[a:b], **rope)
+        dq[a:b, heads] = gq[:, heads]
+        dk[a:b, heads] = gk[:, heads]
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------------------

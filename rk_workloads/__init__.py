@@ -168,6 +168,18 @@ def draw_qkv(rng: np.random.Generator, T: int, H: int, d: int, dtype: str):
     return q, k, v
 
 
+def draw_grad(wl: "Workload", seed: Optional[int] = None) -> np.ndarray:
+    """Upstream gradient dO ~ N(0, 1) of shape [T, H, d] for backward tests and
+    the backward benchmark; bf16-rounded for bf16 workloads.  Drawn from its
+    own generator (seed: the workload's seed + 7919 unless given), so the
+    forward inputs are unchanged."""
+    if seed is None:
+        seed = int(wl.meta.get("seed", 0)) + 7919
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((wl.total_tokens, wl.heads, wl.d_head), dtype=np.float32)
+    return bf16_round(g) if wl.dtype == "bf16" else g
+
+
 CONFIG_NAMES = {
     1: "tiny-f32-cadet-1x(256+16)",
     2: "cadet-64x1024-delay1h",
