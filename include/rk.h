@@ -1,11 +1,11 @@
 /*
  * rk.h -- C ABI of librk: request-centric masked multi-head attention
- * (forward) with time RoPE, for AMD Instinct MI355X (gfx950).
+ * (forward and backward) with time RoPE, for AMD Instinct MI355X (gfx950).
  *
  * One packed buffer holds R requests.  Each request is one user sequence:
  * optional PROFILE tokens, HISTORY tokens, optional same-day REALTIME
  * tokens and N CANDIDATE (target) tokens, in that order.  Every token
- * carries an int64 timestamp in seconds.  Three operations are exported:
+ * carries an int64 timestamp in seconds.  The operations exported:
  *
  *   rk_mask_plan        classify every 128 x 64 (query x key) tile of every
  *                       request as EMPTY / PARTIAL / FULL with its exact
@@ -13,7 +13,8 @@
  *                       each query tile (CSR) and build the launch schedule;
  *   rk_time_rope        rotate Q or K by time RoPE;
  *   rk_masked_attn_fwd  softmax(Q K^T * scale + M) V over the plan, with
- *                       optional fused time RoPE.
+ *                       optional fused time RoPE;
+ *   rk_masked_attn_bwd  its gradients with respect to Q, K and V.
  *
  * Sources (titles and sections of the pages this library follows):
  *  - CADET: Context-Conditioned Ads CTR Prediction With a Decoder-Only
@@ -74,7 +75,7 @@
 extern "C" {
 #endif
 
-#define RK_ABI_VERSION 2
+#define RK_ABI_VERSION 3
 
 typedef enum rk_status {
   RK_OK = 0,
@@ -111,6 +112,11 @@ enum { RK_TILE_EMPTY = 0, RK_TILE_PARTIAL = 1, RK_TILE_FULL = 2 };
                                          range of each is cut into chunks run by separate
                                          workgroups whose partial softmax results a merge
                                          pass combines (more attention workspace). */
+#define RK_PLAN_BACKWARD 0x4u /* also build the key-major tables rk_masked_attn_bwd needs:
+                                 for every 64-key tile, the ascending list of 128-row query
+                                 tiles with a visible pair (FULL / PARTIAL as in the
+                                 query-major CSR), and a schedule of (key tile, head) work
+                                 items.  Not allowed with RK_QUERY_CANDIDATES_ONLY. */
 
 /* Segment-kind bits of rk_rope_params.kinds: bit k selects kind k. */
 #define RK_KIND_BIT(k) (1u << (k))
@@ -152,7 +158,8 @@ typedef struct rk_batch {
 /* Mask parameters (CADET delay mask; SORT / LazFormer window; MTGR static part). */
 typedef struct rk_mask_params {
   uint32_t struct_size;
-  uint32_t flags;       /* RK_STATIC_BIDIRECTIONAL, RK_QUERY_CANDIDATES_ONLY or 0 */
+  uint32_t flags;       /* RK_STATIC_BIDIRECTIONAL, RK_QUERY_CANDIDATES_ONLY,
+                           RK_PLAN_BACKWARD, or 0 */
   int64_t delay;        /* Delta_delay in timestamp units, >= 0; 0 = off */
   int32_t window;       /* keys kept including self, >= 0; 0 = off */
   int32_t global_tail;  /* LazFormer (section 2.3, eq. 19-21) G >= 0: the last G static
@@ -208,6 +215,15 @@ typedef struct rk_plan_info {
                                   with fewer it lists them in schedule order, in chunks */
   size_t off_splits;           /* int32 [RK_SPLIT_SLOTS][4]: (item, first part, parts, 0) of
                                   each split item, item -1 past the last */
+  /* key-major tables, filled for RK_PLAN_BACKWARD plans (offsets 0 and
+     num_ksched_slots 0 otherwise) */
+  int64_t num_ktiles;          /* sum over requests of ceil(L_r / 64) */
+  int64_t num_ksched_slots;    /* one slot per (key tile, head) work item, LPT / XCD order */
+  size_t off_kt_ptr;           /* int32 [num_ktiles + 1], CSR row pointers per global key tile */
+  size_t off_qtile_word;       /* int32 [kt_ptr[num_ktiles]]: request-local query tile, ascending,
+                                  | (1 << 31) when the tile is PARTIAL */
+  size_t off_ksched;           /* int32 [num_ksched_slots]: work item = global key tile *
+                                  num_heads + head, or -1 */
 } rk_plan_info;
 
 /* Totals of a plan (per head). */
@@ -341,6 +357,84 @@ rk_status rk_attn_workspace_size(const rk_plan* p, const rk_attn_args* a, size_t
  * RK_ERR_UNSUPPORTED, RK_ERR_WORKSPACE_TOO_SMALL, RK_ERR_HIP.
  */
 rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stream);
+
+/*
+ * Backward arguments.  Q, K, V, O, dO, dQ, dK, dV are [token, head, d]
+ * views with d contiguous and the given element strides, all of `dtype`
+ * (RK_BF16: fp32 accumulation, bf16 MFMA for d_head == 64 with 16-byte
+ * aligned base pointers and strides that are multiples of 8; RK_F32: fp32
+ * throughout).  d_head in {32, 64, 128}.
+ *   q, k, v, rope, scale, flags : exactly as given to rk_masked_attn_fwd
+ *               (RK_ATTN_REFERENCE_KERNEL, RK_ATTN_K_PREROTATED).
+ *   o, lse    : that forward call's outputs; lse (float [num_heads]
+ *               [total_tokens], natural log, -inf for empty rows) is
+ *               required.
+ *   d_o       : upstream gradient dLoss/dO.
+ *   dq, dk, dv: outputs, every row written (0 for a query that sees no key
+ *               and for a key that no query sees).  dQ and dK are the
+ *               gradients with respect to the tensors passed in: with rope
+ *               and without RK_ATTN_K_PREROTATED they are taken back
+ *               through the rotation (with respect to the unrotated Q, K);
+ *               with RK_ATTN_K_PREROTATED dk is the gradient with respect to
+ *               the rotated K that was passed.
+ *   workspace : device memory of at least rk_attn_bwd_workspace_size bytes,
+ *               256-byte aligned.
+ * Outputs must not overlap the inputs, each other or the workspace.
+ */
+typedef struct rk_attn_bwd_args {
+  uint32_t struct_size;
+  uint32_t flags;
+  rk_dtype dtype;
+  int32_t num_heads;
+  int32_t d_head;
+  int32_t reserved;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* d_o;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_stride_tok, q_stride_head;
+  int64_t k_stride_tok, k_stride_head;
+  int64_t v_stride_tok, v_stride_head;
+  int64_t o_stride_tok, o_stride_head;
+  int64_t do_stride_tok, do_stride_head;
+  int64_t dq_stride_tok, dq_stride_head;
+  int64_t dk_stride_tok, dk_stride_head;
+  int64_t dv_stride_tok, dv_stride_head;
+  float scale;
+  float reserved2;
+  const rk_rope_params* rope;
+  void* workspace;
+  size_t workspace_bytes;
+} rk_attn_bwd_args;
+
+/* Workspace bytes rk_masked_attn_bwd needs for `a` on plan `p` (host only):
+ * rowsum(dO * O) and the log2-unit LSE ([num_heads][total_tokens] fp32
+ * each), plus, with rope, the rotated Q and (unless RK_ATTN_K_PREROTATED)
+ * the rotated K ([total_tokens][num_heads][d_head] of dtype each). */
+rk_status rk_attn_bwd_workspace_size(const rk_plan* p, const rk_attn_bwd_args* a, size_t* bytes);
+
+/*
+ * Masked attention backward over a plan built with RK_PLAN_BACKWARD: the
+ * gradients of a loss with respect to Q, K and V, given dLoss/dO, for the
+ * forward softmax(Q K^T * scale + M) V of rk_masked_attn_fwd (TM20K
+ * section 2.1, LazFormer eq. 21; trained with the delay mask as in
+ * CADET, "why mask the most recent hour in training").  With P the masked
+ * row softmax: dV = P^T dO; dS = P * (dO V^T - rowsum(dO * O)); dQ =
+ * scale * dS K; dK = scale * dS^T Q.  P is recomputed from the forward's
+ * log-sum-exp.  Two launches: one per (query tile, head) over the
+ * query-major CSR writes dQ, one per (key tile, head) over the key-major
+ * CSR writes dK and dV; EMPTY tiles are never read and the per-element mask
+ * runs on PARTIAL tiles only.  No atomics: results are deterministic.
+ * Errors: RK_ERR_INVALID_ARG (plan without RK_PLAN_BACKWARD, num_heads !=
+ * the plan's, lse NULL, ...), RK_ERR_UNSUPPORTED, RK_ERR_WORKSPACE_TOO_SMALL,
+ * RK_ERR_HIP.
+ */
+rk_status rk_masked_attn_bwd(const rk_plan* p, const rk_attn_bwd_args* a, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,4 +1,4 @@
-"""Request-centric masked attention (forward) with time RoPE on MI355X.
+"""Request-centric masked attention (forward and backward) with time RoPE on MI355X.
 
 The computation lives in librk.so (HIP, gfx950); this package holds the
 library sources (csrc/), the build step (build.py) and a thin Python binding
@@ -7,6 +7,6 @@ call does, and fails loudly if it has not been built.
 """
 
 from .binding import (  # noqa: F401
-    Batch, Plan, rk_attn_workspace_size, rk_mask_plan, rk_masked_attn_fwd,
+    Batch, Plan, rk_attn_workspace_size, rk_mask_plan, rk_masked_attn_bwd, rk_masked_attn_fwd,
     rk_plan_workspace_size, rk_time_rope,
 )

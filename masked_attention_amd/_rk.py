@@ -28,9 +28,10 @@ RK_TILE_EMPTY, RK_TILE_PARTIAL, RK_TILE_FULL = 0, 1, 2
 RK_TILE_Q, RK_TILE_K = 128, 64
 RK_STATIC_BIDIRECTIONAL = 0x1
 RK_QUERY_CANDIDATES_ONLY = 0x2
+RK_PLAN_BACKWARD = 0x4
 RK_ATTN_REFERENCE_KERNEL = 0x1
 RK_ATTN_K_PREROTATED = 0x2
-RK_ABI_VERSION = 2
+RK_ABI_VERSION = 3
 RK_SPLIT_SLOTS = 768  # extra work-list slots of a candidates-only plan
 
 
@@ -86,6 +87,11 @@ class rk_plan_info(C.Structure):
         ("num_work_slots", C.c_int64),
         ("off_work", C.c_size_t),
         ("off_splits", C.c_size_t),
+        ("num_ktiles", C.c_int64),
+        ("num_ksched_slots", C.c_int64),
+        ("off_kt_ptr", C.c_size_t),
+        ("off_qtile_word", C.c_size_t),
+        ("off_ksched", C.c_size_t),
     ]
 
 
@@ -127,6 +133,39 @@ class rk_attn_args(C.Structure):
     ]
 
 
+class rk_attn_bwd_args(C.Structure):
+    _fields_ = [
+        ("struct_size", C.c_uint32),
+        ("flags", C.c_uint32),
+        ("dtype", C.c_int),
+        ("num_heads", C.c_int32),
+        ("d_head", C.c_int32),
+        ("reserved", C.c_int32),
+        ("q", C.c_void_p),
+        ("k", C.c_void_p),
+        ("v", C.c_void_p),
+        ("o", C.c_void_p),
+        ("d_o", C.c_void_p),
+        ("lse", C.c_void_p),
+        ("dq", C.c_void_p),
+        ("dk", C.c_void_p),
+        ("dv", C.c_void_p),
+        ("q_stride_tok", C.c_int64), ("q_stride_head", C.c_int64),
+        ("k_stride_tok", C.c_int64), ("k_stride_head", C.c_int64),
+        ("v_stride_tok", C.c_int64), ("v_stride_head", C.c_int64),
+        ("o_stride_tok", C.c_int64), ("o_stride_head", C.c_int64),
+        ("do_stride_tok", C.c_int64), ("do_stride_head", C.c_int64),
+        ("dq_stride_tok", C.c_int64), ("dq_stride_head", C.c_int64),
+        ("dk_stride_tok", C.c_int64), ("dk_stride_head", C.c_int64),
+        ("dv_stride_tok", C.c_int64), ("dv_stride_head", C.c_int64),
+        ("scale", C.c_float),
+        ("reserved2", C.c_float),
+        ("rope", C.c_void_p),
+        ("workspace", C.c_void_p),
+        ("workspace_bytes", C.c_size_t),
+    ]
+
+
 STRUCTS = {
     "rk_batch": rk_batch,
     "rk_mask_params": rk_mask_params,
@@ -134,6 +173,7 @@ STRUCTS = {
     "rk_plan_info": rk_plan_info,
     "rk_plan_totals": rk_plan_totals,
     "rk_attn_args": rk_attn_args,
+    "rk_attn_bwd_args": rk_attn_bwd_args,
 }
 
 # (name, restype, argtypes) of every exported entry point
@@ -152,6 +192,9 @@ FUNCTIONS = [
     ("rk_attn_workspace_size", C.c_int, [C.c_void_p, C.POINTER(rk_attn_args),
                                          C.POINTER(C.c_size_t)]),
     ("rk_masked_attn_fwd", C.c_int, [C.c_void_p, C.POINTER(rk_attn_args), C.c_void_p]),
+    ("rk_attn_bwd_workspace_size", C.c_int, [C.c_void_p, C.POINTER(rk_attn_bwd_args),
+                                             C.POINTER(C.c_size_t)]),
+    ("rk_masked_attn_bwd", C.c_int, [C.c_void_p, C.POINTER(rk_attn_bwd_args), C.c_void_p]),
 ]
 
 _lib = None

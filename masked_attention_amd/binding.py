@@ -70,7 +70,7 @@ class Plan:
 
     def __init__(self, batch: Batch, *, delay: int = 0, window: int = 0,
                  static_bidirectional: bool = False, num_heads: int = 1,
-                 candidates_only: bool = False, global_tail: int = 0,
+                 candidates_only: bool = False, global_tail: int = 0, backward: bool = False,
                  stream: Optional[torch.cuda.Stream] = None,
                  workspace: Optional[torch.Tensor] = None):
         self.batch = batch
@@ -80,7 +80,8 @@ class Plan:
             workspace = torch.empty(max(size, 256), dtype=torch.uint8, device=batch.seg_kind.device)
         self.workspace = workspace
         flags = (_rk.RK_STATIC_BIDIRECTIONAL if static_bidirectional else 0) | (
-            _rk.RK_QUERY_CANDIDATES_ONLY if candidates_only else 0)
+            _rk.RK_QUERY_CANDIDATES_ONLY if candidates_only else 0) | (
+            _rk.RK_PLAN_BACKWARD if backward else 0)
         self.params = sized(_rk.rk_mask_params, delay=int(delay), window=int(window),
                             global_tail=int(global_tail), flags=flags)
         h = C.c_void_p()
@@ -138,6 +139,30 @@ class Plan:
             return None
         n = _rk.RK_SPLIT_SLOTS
         return self._view(self.info.off_splits, 4 * n, torch.int32).view(n, 4)
+
+    @property
+    def num_ktiles(self) -> int:
+        return int(self.info.num_ktiles)
+
+    def kt_ptr(self) -> Optional[torch.Tensor]:
+        """Key-major CSR row pointers [num_ktiles + 1] (backward plans), or None."""
+        if int(self.info.num_ksched_slots) == 0:
+            return None
+        return self._view(self.info.off_kt_ptr, self.num_ktiles + 1, torch.int32)
+
+    def qtile_word(self) -> Optional[torch.Tensor]:
+        """Key-major CSR entries: request-local q-tile | (PARTIAL << 31), or None."""
+        ptr = self.kt_ptr()
+        if ptr is None:
+            return None
+        n = int(ptr[-1].item()) if self.num_ktiles else 0
+        return self._view(self.info.off_qtile_word, n, torch.int32)
+
+    def ksched(self) -> Optional[torch.Tensor]:
+        n = int(self.info.num_ksched_slots)
+        if n == 0:
+            return None
+        return self._view(self.info.off_ksched, n, torch.int32)
 
     def stats(self, stream: Optional[torch.cuda.Stream] = None, raise_on_error: bool = True) -> dict:
         t = sized(_rk.rk_plan_totals)
@@ -250,3 +275,58 @@ def rk_masked_attn_fwd(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Te
     # keep the workspace alive until the caller synchronises
     out._rk_workspace = workspace  # type: ignore[attr-defined]
     return out, lse
+
+
+def _bwd_args(q, k, v, o, do, lse, dq, dk, dv, scale, rope, reference, k_prerotated, workspace):
+    for t in (q, k, v, o, do, dq, dk, dv):
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError("q, k, v, o, do, dq, dk, dv must be [T, H, d] with d contiguous")
+    flags = (_rk.RK_ATTN_REFERENCE_KERNEL if reference else 0) | (
+        _rk.RK_ATTN_K_PREROTATED if k_prerotated else 0)
+    a = sized(_rk.rk_attn_bwd_args, flags=flags, dtype=_dtype_code(q), num_heads=q.shape[1],
+              d_head=q.shape[2], q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(),
+              o=o.data_ptr(), d_o=do.data_ptr(), lse=lse.data_ptr() if lse is not None else None,
+              dq=dq.data_ptr(), dk=dk.data_ptr(), dv=dv.data_ptr(),
+              q_stride_tok=q.stride(0), q_stride_head=q.stride(1),
+              k_stride_tok=k.stride(0), k_stride_head=k.stride(1),
+              v_stride_tok=v.stride(0), v_stride_head=v.stride(1),
+              o_stride_tok=o.stride(0), o_stride_head=o.stride(1),
+              do_stride_tok=do.stride(0), do_stride_head=do.stride(1),
+              dq_stride_tok=dq.stride(0), dq_stride_head=dq.stride(1),
+              dk_stride_tok=dk.stride(0), dk_stride_head=dk.stride(1),
+              dv_stride_tok=dv.stride(0), dv_stride_head=dv.stride(1),
+              scale=float(scale))
+    if rope is not None:
+        a.rope = C.cast(C.pointer(rope), C.c_void_p)
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def rk_masked_attn_bwd(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       o: torch.Tensor, lse: torch.Tensor, do: torch.Tensor, *,
+                       dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                       dv: Optional[torch.Tensor] = None, scale: float = 0.0,
+                       rope: Optional[dict] = None, reference: bool = False,
+                       k_prerotated: bool = False, workspace: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None):
+    """Gradients (dq, dk, dv) of the masked attention forward over `plan`
+    (built with backward=True), given the forward's o and lse and the
+    upstream gradient do.  q, k, v, scale, rope and k_prerotated are those
+    of the forward call."""
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    rp = rope_params(**rope) if rope is not None else None
+    a = _bwd_args(q, k, v, o, do, lse, dq, dk, dv, scale, rp, reference, k_prerotated, workspace)
+    n = C.c_size_t()
+    check(lib().rk_attn_bwd_workspace_size(plan.handle, C.byref(a), C.byref(n)),
+          "rk_attn_bwd_workspace_size")
+    if n.value and workspace is None:
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=q.device)
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = n.value
+    check(lib().rk_masked_attn_bwd(plan.handle, C.byref(a), _stream(stream)), "rk_masked_attn_bwd")
+    dq._rk_workspace = workspace  # type: ignore[attr-defined]
+    return dq, dk, dv

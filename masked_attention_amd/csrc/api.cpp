@@ -28,16 +28,72 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   int32_t R = 0, T = 0, H = 0;
   int64_t NQ = 0, NT = 0, G = 0, max_queue = 0, slots = 0;
+  int64_t NK = 0, kslots = 0;
   std::vector<ReqMeta> req;
   std::vector<int32_t> qt_req;
   std::vector<Group> groups;        // sorted by (queue, base)
   std::vector<int32_t> queue_start; // kNumXcd + 1
+  std::vector<int32_t> kt_req;      // key-major counterparts
+  std::vector<Group> kgroups;
+  std::vector<int32_t> kqueue_start;
   size_t off_req = 0, off_qt_req = 0, off_groups = 0, off_queue_start = 0, off_totals = 0,
          host_blob = 0, off_row_desc = 0, off_tile_count = 0, off_tile_class = 0, off_qt_nnz = 0,
          off_qt_pairs = 0, off_qt_full = 0,
          off_qtile_ptr = 0, off_ktile_idx = 0, off_ktile_word = 0, off_qorder = 0, off_sched = 0,
-         off_work = 0, off_splits = 0, off_act = 0, total = 0;
+         off_work = 0, off_splits = 0, off_act = 0, off_kt_req = 0, off_kgroups = 0,
+         off_kqueue_start = 0, off_kt_nnz = 0, off_kt_ptr = 0, off_qtile_word = 0,
+         off_korder = 0, off_ksched = 0, total = 0;
 };
+
+// Place (request, head) groups of `count(r)` work items each on the eight
+// XCD queues: requests by descending weight, each group on the least-loaded
+// queue.  Returns the longest queue; fills `out` sorted by (queue, base) and
+// `qstart` (kNumXcd + 1 entries) when asked.
+template <typename CountFn>
+int64_t place_groups(int32_t R, int32_t H, const int32_t* o, const std::vector<int64_t>& weight,
+                     CountFn count, bool fill, std::vector<Group>* out,
+                     std::vector<int32_t>* qstart) {
+  std::vector<Group> gs;
+  std::vector<int> gq;
+  int64_t counts[kNumXcd] = {0};
+  std::vector<int32_t> order;
+  for (int32_t r = 0; r < R; ++r)
+    if (o[r + 1] > o[r]) order.push_back(r);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t c) { return weight[a] > weight[c]; });
+  int64_t loads[kNumXcd] = {0};
+  for (int32_t r : order) {
+    const int32_t n = count(r);
+    for (int32_t h = 0; h < H; ++h) {
+      int q = 0;
+      for (int j = 1; j < kNumXcd; ++j)
+        if (loads[j] < loads[q]) q = j;
+      Group g;
+      g.req = r;
+      g.head = h;
+      g.base = (int32_t)std::min<int64_t>(counts[q], kInt32Max);
+      g.count = n;
+      loads[q] += weight[r];
+      counts[q] += n;
+      if (fill) {
+        gs.push_back(g);
+        gq.push_back(q);
+      }
+    }
+  }
+  int64_t mq = 0;
+  for (int j = 0; j < kNumXcd; ++j) mq = std::max(mq, counts[j]);
+  if (fill) {
+    qstart->assign(kNumXcd + 1, 0);
+    for (int j = 0; j < kNumXcd; ++j) {
+      (*qstart)[j] = (int32_t)out->size();
+      for (size_t i = 0; i < gs.size(); ++i)
+        if (gq[i] == j) out->push_back(gs[i]);  // bases increase within a queue
+    }
+    (*qstart)[kNumXcd] = (int32_t)out->size();
+  }
+  return mq;
+}
 
 rk_status check_batch(const rk_batch* b) {
   if (!b || b->struct_size < sizeof(rk_batch)) return RK_ERR_INVALID_ARG;
@@ -61,7 +117,7 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->T = b->total_tokens;
   L->H = H;
   const int32_t* o = b->req_offsets_host;
-  int64_t nq = 0, nt = 0;
+  int64_t nq = 0, nt = 0, nk = 0;
   if (with_tables) L->req.resize(L->R);
   std::vector<int64_t> weight(L->R);
   for (int32_t r = 0; r < L->R; ++r) {
@@ -75,66 +131,43 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
       m.qt_off = (int32_t)std::min<int64_t>(nq, kInt32Max);
       m.nqt = nqt;
       m.nkt = nkt;
-      m.pad0 = 0;
+      m.kt_off = (int32_t)std::min<int64_t>(nk, kInt32Max);
       m.tile_off = nt;
       for (int k = 0; k < 4; ++k) m.seg[k] = len;
     }
     weight[r] = (int64_t)nqt * nkt;
     nq += nqt;
+    nk += nkt;
     nt += (int64_t)nqt * nkt;
   }
-  if (nt >= kInt32Max || nq * (int64_t)H >= kInt32Max) return RK_ERR_UNSUPPORTED;
+  if (nt >= kInt32Max || nq * (int64_t)H >= kInt32Max || nk * (int64_t)H >= kInt32Max)
+    return RK_ERR_UNSUPPORTED;
   L->NQ = nq;
   L->NT = nt;
+  L->NK = nk;
 
-  // Launch schedule: (request, head) groups, heaviest first, each placed on
-  // the least-loaded of the eight XCD queues (dense tile count as weight).
-  std::vector<Group> gs;
-  std::vector<int64_t> gw;
-  std::vector<int> gq;
-  int64_t counts[kNumXcd] = {0};
-  {
-    std::vector<int32_t> order;
-    for (int32_t r = 0; r < L->R; ++r)
-      if (o[r + 1] > o[r]) order.push_back(r);
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int32_t a, int32_t c) { return weight[a] > weight[c]; });
-    int64_t loads[kNumXcd] = {0};
-    for (int32_t r : order) {
-      const int32_t nqt = (o[r + 1] - o[r] + rk::kTileQ - 1) / rk::kTileQ;
-      for (int32_t h = 0; h < H; ++h) {
-        int q = 0;
-        for (int j = 1; j < kNumXcd; ++j)
-          if (loads[j] < loads[q]) q = j;
-        Group g;
-        g.req = r;
-        g.head = h;
-        g.base = (int32_t)std::min<int64_t>(counts[q], kInt32Max);
-        g.count = nqt;
-        loads[q] += weight[r];
-        counts[q] += nqt;
-        gs.push_back(g);
-        gq.push_back(q);
-      }
-    }
-  }
-  int64_t mq = 0;
-  for (int j = 0; j < kNumXcd; ++j) mq = std::max(mq, counts[j]);
-  L->max_queue = mq;
-  L->slots = mq * kNumXcd;
-  if (L->slots >= kInt32Max) return RK_ERR_UNSUPPORTED;
-  L->G = (int64_t)gs.size();
+  // Launch schedules: (request, head) groups, heaviest first, each placed on
+  // the least-loaded of the eight XCD queues (dense tile count as weight);
+  // one for query-tile items, one for key-tile items (backward).
+  auto nqt_of = [&](int32_t r) { return (o[r + 1] - o[r] + rk::kTileQ - 1) / rk::kTileQ; };
+  auto nkt_of = [&](int32_t r) { return (o[r + 1] - o[r] + rk::kTileK - 1) / rk::kTileK; };
+  L->max_queue = place_groups(L->R, H, o, weight, nqt_of, with_tables, &L->groups,
+                              &L->queue_start);
+  L->slots = L->max_queue * kNumXcd;
+  const int64_t kmax = place_groups(L->R, H, o, weight, nkt_of, with_tables, &L->kgroups,
+                                    &L->kqueue_start);
+  L->kslots = kmax * kNumXcd;
+  if (L->slots >= kInt32Max || L->kslots >= kInt32Max) return RK_ERR_UNSUPPORTED;
+  int64_t ng = 0;
+  for (int32_t r = 0; r < L->R; ++r) ng += (o[r + 1] > o[r]) ? H : 0;
+  L->G = ng;
   if (with_tables) {
-    L->queue_start.assign(kNumXcd + 1, 0);
-    for (int j = 0; j < kNumXcd; ++j) {
-      L->queue_start[j] = (int32_t)L->groups.size();
-      for (size_t i = 0; i < gs.size(); ++i)
-        if (gq[i] == j) L->groups.push_back(gs[i]);  // bases increase within a queue
-    }
-    L->queue_start[kNumXcd] = (int32_t)L->groups.size();
     L->qt_req.resize(nq);
-    for (int32_t r = 0; r < L->R; ++r)
+    L->kt_req.resize(nk);
+    for (int32_t r = 0; r < L->R; ++r) {
       for (int32_t i = 0; i < L->req[r].nqt; ++i) L->qt_req[L->req[r].qt_off + i] = r;
+      for (int32_t i = 0; i < L->req[r].nkt; ++i) L->kt_req[L->req[r].kt_off + i] = r;
+    }
   }
 
   size_t off = 0;
@@ -148,6 +181,9 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->off_groups = take(sizeof(Group) * (size_t)L->G);
   L->off_queue_start = take(sizeof(int32_t) * (kNumXcd + 1));
   L->off_totals = take(sizeof(PlanTotals));
+  L->off_kt_req = take(sizeof(int32_t) * (size_t)nk);
+  L->off_kgroups = take(sizeof(Group) * (size_t)L->G);
+  L->off_kqueue_start = take(sizeof(int32_t) * (kNumXcd + 1));
   L->host_blob = off;
   L->off_row_desc = take(sizeof(int2) * (size_t)L->T);
   L->off_tile_count = take(sizeof(int32_t) * (size_t)nt);
@@ -163,6 +199,11 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->off_work = take(sizeof(rk::WorkEntry) * (size_t)(L->slots + rk::kSplitTarget));
   L->off_splits = take(sizeof(rk::SplitEntry) * (size_t)rk::kSplitTarget);
   L->off_act = take(sizeof(int32_t) * (size_t)(rk::kSplitTarget / 2));
+  L->off_kt_nnz = take(sizeof(int32_t) * (size_t)nk);
+  L->off_kt_ptr = take(sizeof(int32_t) * (size_t)(nk + 1));
+  L->off_qtile_word = take(sizeof(int32_t) * (size_t)nt);
+  L->off_korder = take(sizeof(int32_t) * (size_t)nk);
+  L->off_ksched = take(sizeof(int32_t) * (size_t)L->kslots);
   L->total = off;
   return RK_OK;
 }
@@ -240,7 +281,9 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   *plan_out = nullptr;
   if (!m || m->struct_size < sizeof(rk_mask_params)) return RK_ERR_INVALID_ARG;
   if (m->delay < 0 || m->window < 0 || m->global_tail < 0 ||
-      (m->flags & ~(RK_STATIC_BIDIRECTIONAL | RK_QUERY_CANDIDATES_ONLY)))
+      (m->flags & ~(RK_STATIC_BIDIRECTIONAL | RK_QUERY_CANDIDATES_ONLY | RK_PLAN_BACKWARD)))
+    return RK_ERR_INVALID_ARG;
+  if ((m->flags & RK_QUERY_CANDIDATES_ONLY) && (m->flags & RK_PLAN_BACKWARD))
     return RK_ERR_INVALID_ARG;
   Layout L;
   rk_status st = make_layout(b, num_heads, true, &L);
@@ -258,6 +301,8 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   p->G = L.G;
   p->slots = L.slots;
   p->max_queue = L.max_queue;
+  p->NK = L.NK;
+  p->kslots = L.kslots;
   p->grid = (m->flags & RK_QUERY_CANDIDATES_ONLY) && L.slots > 0 ? L.slots + rk::kSplitTarget
                                                                  : L.slots;
   p->delay = m->delay;
@@ -289,6 +334,14 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   p->off_splits = L.off_splits;
   p->off_act = L.off_act;
   p->off_totals = L.off_totals;
+  p->off_kt_req = L.off_kt_req;
+  p->off_kgroups = L.off_kgroups;
+  p->off_kqueue_start = L.off_kqueue_start;
+  p->off_kt_nnz = L.off_kt_nnz;
+  p->off_kt_ptr = L.off_kt_ptr;
+  p->off_qtile_word = L.off_qtile_word;
+  p->off_korder = L.off_korder;
+  p->off_ksched = L.off_ksched;
   p->host_blob_bytes = L.host_blob;
   p->total_bytes = L.total;
 
@@ -313,6 +366,14 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   D.work = (rk::WorkEntry*)(ws + L.off_work);
   D.splits = (rk::SplitEntry*)(ws + L.off_splits);
   D.act_slots = (int32_t*)(ws + L.off_act);
+  D.kt_req = (int32_t*)(ws + L.off_kt_req);
+  D.kgroups = (Group*)(ws + L.off_kgroups);
+  D.kqueue_start = (int32_t*)(ws + L.off_kqueue_start);
+  D.kt_nnz = (int32_t*)(ws + L.off_kt_nnz);
+  D.kt_ptr = (int32_t*)(ws + L.off_kt_ptr);
+  D.qtile_word = (int32_t*)(ws + L.off_qtile_word);
+  D.korder = (int32_t*)(ws + L.off_korder);
+  D.ksched = (int32_t*)(ws + L.off_ksched);
 
   p->host_blob = (unsigned char*)std::calloc(L.host_blob ? L.host_blob : 1, 1);
   if (!p->host_blob) {
@@ -323,6 +384,10 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   if (L.NQ) std::memcpy(p->host_blob + L.off_qt_req, L.qt_req.data(), sizeof(int32_t) * L.NQ);
   if (L.G) std::memcpy(p->host_blob + L.off_groups, L.groups.data(), sizeof(Group) * L.G);
   std::memcpy(p->host_blob + L.off_queue_start, L.queue_start.data(), sizeof(int32_t) * (kNumXcd + 1));
+  if (L.NK) std::memcpy(p->host_blob + L.off_kt_req, L.kt_req.data(), sizeof(int32_t) * L.NK);
+  if (L.G) std::memcpy(p->host_blob + L.off_kgroups, L.kgroups.data(), sizeof(Group) * L.G);
+  std::memcpy(p->host_blob + L.off_kqueue_start, L.kqueue_start.data(),
+              sizeof(int32_t) * (kNumXcd + 1));
   // totals stay zero (calloc)
 
   hipStream_t s = (hipStream_t)stream;
@@ -356,6 +421,12 @@ rk_status rk_plan_get_info(const rk_plan* p, rk_plan_info* out) {
   out->num_work_slots = wl ? p->grid : 0;
   out->off_work = wl ? p->off_work : 0;
   out->off_splits = wl ? p->off_splits : 0;
+  const bool bw = (p->flags & RK_PLAN_BACKWARD) != 0;
+  out->num_ktiles = p->NK;
+  out->num_ksched_slots = bw ? p->kslots : 0;
+  out->off_kt_ptr = bw ? p->off_kt_ptr : 0;
+  out->off_qtile_word = bw ? p->off_qtile_word : 0;
+  out->off_ksched = bw ? p->off_ksched : 0;
   return RK_OK;
 }
 
@@ -540,6 +611,168 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
     else { to_log2 = log2e; to_nat = 1.f; }
     e = rk::launch_attn_combine(p, L, a->dtype, to_log2, to_nat, s);
   }
+  return e == hipSuccess ? RK_OK : RK_ERR_HIP;
+}
+
+namespace {
+
+rk_status check_bwd(const rk_plan* p, const rk_attn_bwd_args* a) {
+  if (!p || !a || a->struct_size < sizeof(rk_attn_bwd_args)) return RK_ERR_INVALID_ARG;
+  if (!(p->flags & RK_PLAN_BACKWARD)) return RK_ERR_INVALID_ARG;
+  if (!valid_dtype(a->dtype)) return RK_ERR_INVALID_ARG;
+  if (a->num_heads != p->H) return RK_ERR_INVALID_ARG;
+  if (a->d_head != 32 && a->d_head != 64 && a->d_head != 128) return RK_ERR_UNSUPPORTED;
+  if (a->flags & ~(RK_ATTN_REFERENCE_KERNEL | RK_ATTN_K_PREROTATED)) return RK_ERR_INVALID_ARG;
+  if ((a->flags & RK_ATTN_K_PREROTATED) && !a->rope) return RK_ERR_INVALID_ARG;
+  if (p->T > 0 && (!a->q || !a->k || !a->v || !a->o || !a->d_o || !a->lse || !a->dq || !a->dk ||
+                   !a->dv))
+    return RK_ERR_INVALID_ARG;
+  const int64_t st[16] = {a->q_stride_tok,  a->q_stride_head,  a->k_stride_tok,  a->k_stride_head,
+                          a->v_stride_tok,  a->v_stride_head,  a->o_stride_tok,  a->o_stride_head,
+                          a->do_stride_tok, a->do_stride_head, a->dq_stride_tok, a->dq_stride_head,
+                          a->dk_stride_tok, a->dk_stride_head, a->dv_stride_tok, a->dv_stride_head};
+  for (int64_t x : st)
+    if (x < 0) return RK_ERR_INVALID_ARG;
+  if (!(std::isfinite(a->scale) && a->scale >= 0.f)) return RK_ERR_INVALID_ARG;
+  if (a->rope) {
+    rk_status s = check_rope(a->rope);
+    if (s != RK_OK) return s;
+    if (a->rope->kinds != 0) return RK_ERR_INVALID_ARG;
+  }
+  return RK_OK;
+}
+
+bool bwd_mfma_eligible(const rk_attn_bwd_args* a) {
+  return a->dtype == RK_BF16 && a->d_head == 64 && !(a->flags & RK_ATTN_REFERENCE_KERNEL);
+}
+
+// Row-aligned views for the MFMA kernels: 16-byte base pointers, strides
+// that are multiples of 8 elements and small enough for 32-bit byte offsets.
+bool bwd_mfma_aligned(const rk_attn_bwd_args* a, bool q_in_ws, bool k_in_ws) {
+  auto al = [](const void* ptr) { return ((uintptr_t)ptr % 16) == 0; };
+  auto st = [](int64_t x) { return (x % 8) == 0 && x <= (int64_t(1) << 24); };
+  bool ok = al(a->v) && al(a->o) && al(a->d_o) && al(a->dq) && al(a->dk) && al(a->dv);
+  const int64_t s[12] = {a->v_stride_tok,  a->v_stride_head,  a->o_stride_tok,  a->o_stride_head,
+                         a->do_stride_tok, a->do_stride_head, a->dq_stride_tok, a->dq_stride_head,
+                         a->dk_stride_tok, a->dk_stride_head, a->dv_stride_tok, a->dv_stride_head};
+  for (int64_t x : s) ok = ok && st(x);
+  if (!q_in_ws) ok = ok && al(a->q) && st(a->q_stride_tok) && st(a->q_stride_head);
+  if (!k_in_ws) ok = ok && al(a->k) && st(a->k_stride_tok) && st(a->k_stride_head);
+  return ok;
+}
+
+// Backward workspace: [rowsum(dO*O) H*T fp32][lse2 H*T fp32][rotated Q][rotated K].
+struct BwdWs {
+  size_t dsum = 0, lse2 = 0, q = 0, k = 0, total = 0;
+};
+
+BwdWs bwd_ws(const rk_plan* p, const rk_attn_bwd_args* a) {
+  BwdWs w;
+  const size_t ht = (size_t)p->T * (size_t)a->num_heads;
+  const size_t rows = ht * (size_t)a->d_head * elem_size(a->dtype);
+  size_t off = 0;
+  w.dsum = off;
+  off = align_up(off + ht * sizeof(float));
+  w.lse2 = off;
+  off = align_up(off + ht * sizeof(float));
+  if (a->rope) {
+    w.q = off;
+    off = align_up(off + rows);
+    if (!(a->flags & RK_ATTN_K_PREROTATED)) {
+      w.k = off;
+      off = align_up(off + rows);
+    }
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+rk_status rk_attn_bwd_workspace_size(const rk_plan* p, const rk_attn_bwd_args* a, size_t* bytes) {
+  if (!bytes) return RK_ERR_INVALID_ARG;
+  rk_status st = check_bwd(p, a);
+  if (st != RK_OK) return st;
+  *bytes = bwd_ws(p, a).total;
+  return RK_OK;
+}
+
+rk_status rk_masked_attn_bwd(const rk_plan* p, const rk_attn_bwd_args* a, void* stream) {
+  rk_status st = check_bwd(p, a);
+  if (st != RK_OK) return st;
+  const BwdWs w = bwd_ws(p, a);
+  if (p->T == 0) return RK_OK;  // nothing to write
+  if (!a->workspace || ((uintptr_t)a->workspace % kAlign) != 0) return RK_ERR_INVALID_ARG;
+  if (a->workspace_bytes < w.total) return RK_ERR_WORKSPACE_TOO_SMALL;
+  const bool rope = a->rope != nullptr;
+  const bool k_rotate = rope && !(a->flags & RK_ATTN_K_PREROTATED);
+  const bool use_mfma = bwd_mfma_eligible(a);
+  if (use_mfma && !bwd_mfma_aligned(a, rope, k_rotate)) return RK_ERR_UNSUPPORTED;
+
+  unsigned char* ws = (unsigned char*)a->workspace;
+  rk::BwdLaunch L;
+  std::memset(&L, 0, sizeof(L));
+  L.q = a->q;
+  L.k = a->k;
+  L.v = a->v;
+  L.o = a->o;
+  L.dout = a->d_o;
+  L.lse = a->lse;
+  L.dq = a->dq;
+  L.dk = a->dk;
+  L.dv = a->dv;
+  L.q_st = a->q_stride_tok;
+  L.q_sh = a->q_stride_head;
+  L.k_st = a->k_stride_tok;
+  L.k_sh = a->k_stride_head;
+  L.v_st = a->v_stride_tok;
+  L.v_sh = a->v_stride_head;
+  L.o_st = a->o_stride_tok;
+  L.o_sh = a->o_stride_head;
+  L.do_st = a->do_stride_tok;
+  L.do_sh = a->do_stride_head;
+  L.dq_st = a->dq_stride_tok;
+  L.dq_sh = a->dq_stride_head;
+  L.dk_st = a->dk_stride_tok;
+  L.dk_sh = a->dk_stride_head;
+  L.dv_st = a->dv_stride_tok;
+  L.dv_sh = a->dv_stride_head;
+  L.scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->d_head);
+  L.H = a->num_heads;
+  L.d = a->d_head;
+  L.T = p->T;
+  L.dsum = (float*)(ws + w.dsum);
+  L.lse2 = (float*)(ws + w.lse2);
+  L.ts = p->timestamps_dev;
+  L.anchors = p->anchors_dev;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t hd = (int64_t)a->num_heads * a->d_head;
+  if (rope) {
+    // Q (and K unless given rotated) are rotated once into the workspace
+    // ([T, H, d] dense); the kernels take dQ (dK) back through the rotation.
+    L.tab = make_tab(a->rope, a->d_head);
+    hipError_t e = rk::launch_rope(p->R, p->T, p->req_offsets_dev, p->timestamps_dev,
+                                   p->anchors_dev, p->seg_kind_dev, 0u, L.tab, a->q, ws + w.q,
+                                   a->dtype, a->num_heads, a->d_head, a->q_stride_tok,
+                                   a->q_stride_head, hd, a->d_head, s);
+    if (e != hipSuccess) return RK_ERR_HIP;
+    L.q = ws + w.q;
+    L.q_st = hd;
+    L.q_sh = a->d_head;
+    L.unrot_q = true;
+    if (k_rotate) {
+      e = rk::launch_rope(p->R, p->T, p->req_offsets_dev, p->timestamps_dev, p->anchors_dev,
+                          p->seg_kind_dev, 0u, L.tab, a->k, ws + w.k, a->dtype, a->num_heads,
+                          a->d_head, a->k_stride_tok, a->k_stride_head, hd, a->d_head, s);
+      if (e != hipSuccess) return RK_ERR_HIP;
+      L.k = ws + w.k;
+      L.k_st = hd;
+      L.k_sh = a->d_head;
+      L.unrot_k = true;
+    }
+  }
+  hipError_t e = use_mfma ? rk::launch_attn_bwd_mfma_bf16_d64(p, L, s)
+                          : rk::launch_attn_bwd_reference(p, L, a->dtype, s);
   return e == hipSuccess ? RK_OK : RK_ERR_HIP;
 }
 

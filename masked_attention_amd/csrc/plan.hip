@@ -250,13 +250,10 @@ __global__ __launch_bounds__(256) void plan_csr_kernel(PlanDev P) {
   }
 }
 
-// One block per request: q-tiles ordered by non-empty k-tile count,
-// descending, ties by q-tile index (a rank sort).
-__global__ __launch_bounds__(256) void plan_qsort_kernel(PlanDev P) {
-  __shared__ int chunk[1024];
-  const ReqMeta m = P.req[blockIdx.x];
-  const int n = m.nqt;
-  const int* nnz = P.qt_nnz + m.qt_off;
+// Rank sort of n tiles of one request by non-empty count, descending, ties
+// by tile index: order[rank] = off + tile.  One block.
+__device__ __forceinline__ void rank_order(int n, int off, const int* __restrict__ nnz,
+                                           int* __restrict__ order, int* chunk) {
   for (int a0 = 0; a0 < n; a0 += blockDim.x) {
     const int a = a0 + threadIdx.x;
     const int na = a < n ? nnz[a] : 0;
@@ -273,8 +270,16 @@ __global__ __launch_bounds__(256) void plan_qsort_kernel(PlanDev P) {
         }
       }
     }
-    if (a < n) P.qorder[m.qt_off + rank] = m.qt_off + a;
+    if (a < n) order[off + rank] = off + a;
   }
+}
+
+// One block per request: q-tiles ordered by non-empty k-tile count,
+// descending, ties by q-tile index.
+__global__ __launch_bounds__(256) void plan_qsort_kernel(PlanDev P) {
+  __shared__ int chunk[1024];
+  const ReqMeta m = P.req[blockIdx.x];
+  rank_order(m.nqt, m.qt_off, P.qt_nnz + m.qt_off, P.qorder, chunk);
 }
 
 // One thread per launch slot: slot s runs on XCD s % 8 as item s / 8 of
@@ -406,6 +411,92 @@ __global__ __launch_bounds__(1024) void plan_work_kernel(PlanDev P, int slots, i
   }
 }
 
+// ---- key-major tables (backward) -------------------------------------
+
+// One block per global k-tile: number of q-tiles with a visible pair in it.
+__global__ __launch_bounds__(256) void plan_kcount_kernel(PlanDev P) {
+  __shared__ int cnt_s;
+  const int g = blockIdx.x;
+  const ReqMeta m = P.req[P.kt_req[g]];
+  const int kt = g - m.kt_off;
+  if (threadIdx.x == 0) cnt_s = 0;
+  __syncthreads();
+  int c = 0;
+  for (int qt = threadIdx.x; qt < m.nqt; qt += blockDim.x)
+    c += P.tile_count[m.tile_off + (int64_t)qt * m.nkt + kt] > 0;
+  atomicAdd(&cnt_s, c);
+  __syncthreads();
+  if (threadIdx.x == 0) P.kt_nnz[g] = cnt_s;
+}
+
+// Single block: kt_ptr = exclusive scan of kt_nnz.
+__global__ __launch_bounds__(1024) void plan_kscan_kernel(PlanDev P, int NK) {
+  __shared__ int smem[32];
+  int carry = 0;
+  for (int base = 0; base < NK; base += blockDim.x) {
+    const int i = base + threadIdx.x;
+    const int v = i < NK ? P.kt_nnz[i] : 0;
+    int total;
+    const int ex = block_exclusive_scan(v, smem, &total);
+    if (i < NK) P.kt_ptr[i] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) P.kt_ptr[NK] = carry;
+}
+
+// One block per k-tile: ascending list of its non-empty q-tiles, with the
+// PARTIAL bit.
+__global__ __launch_bounds__(256) void plan_kfill_kernel(PlanDev P) {
+  __shared__ int smem[32];
+  const int g = blockIdx.x;
+  const ReqMeta m = P.req[P.kt_req[g]];
+  const int kt = g - m.kt_off;
+  const int base = P.kt_ptr[g];
+  int run = 0;
+  for (int q0 = 0; q0 < m.nqt; q0 += blockDim.x) {
+    const int qt = q0 + threadIdx.x;
+    const int64_t t_idx = m.tile_off + (int64_t)qt * m.nkt + kt;
+    const int flag = qt < m.nqt && P.tile_count[t_idx] > 0;
+    int total;
+    const int ex = block_exclusive_scan(flag, smem, &total);
+    if (flag)
+      P.qtile_word[base + run + ex] =
+          (int)((unsigned)qt | ((unsigned)(P.tile_class[t_idx] == RK_TILE_PARTIAL) << 31));
+    run += total;
+  }
+}
+
+// One block per request: k-tiles by descending non-empty q-tile count.
+__global__ __launch_bounds__(256) void plan_ksort_kernel(PlanDev P) {
+  __shared__ int chunk[1024];
+  const ReqMeta m = P.req[blockIdx.x];
+  rank_order(m.nkt, m.kt_off, P.kt_nnz + m.kt_off, P.korder, chunk);
+}
+
+// One thread per key-major launch slot (same XCD mapping as the query-major
+// schedule): item = global k-tile * H + head, or -1.
+__global__ void plan_ksched_kernel(PlanDev P, int64_t slots, int H) {
+  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= slots) return;
+  const int q = (int)(s % kNumXcd);
+  const int idx = (int)(s / kNumXcd);
+  int a = P.kqueue_start[q], b = P.kqueue_start[q + 1];
+  int item = -1;
+  if (a < b) {
+    while (b - a > 1) {
+      const int mid = (a + b) >> 1;
+      if (P.kgroups[mid].base <= idx) a = mid; else b = mid;
+    }
+    const Group grp = P.kgroups[a];
+    const int k = idx - grp.base;
+    if (k >= 0 && k < grp.count) {
+      const ReqMeta m = P.req[grp.req];
+      item = P.korder[m.kt_off + k] * H + grp.head;
+    }
+  }
+  P.ksched[s] = item;
+}
+
 }  // namespace
 
 hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
@@ -433,6 +524,14 @@ hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
     if (p->grid > p->slots)
       hipLaunchKernelGGL(plan_work_kernel, dim3((unsigned)((p->grid + 1023) / 1024)), dim3(1024), 0,
                          s, P, (int)p->slots, (int)p->grid, p->H);
+  }
+  if ((p->flags & RK_PLAN_BACKWARD) && p->NK > 0) {
+    hipLaunchKernelGGL(plan_kcount_kernel, dim3((unsigned)p->NK), dim3(256), 0, s, P);
+    hipLaunchKernelGGL(plan_kscan_kernel, dim3(1), dim3(1024), 0, s, P, (int)p->NK);
+    hipLaunchKernelGGL(plan_kfill_kernel, dim3((unsigned)p->NK), dim3(256), 0, s, P);
+    hipLaunchKernelGGL(plan_ksort_kernel, dim3(p->R), dim3(256), 0, s, P);
+    hipLaunchKernelGGL(plan_ksched_kernel, dim3((unsigned)((p->kslots + 255) / 256)), dim3(256), 0,
+                       s, P, p->kslots, p->H);
   }
   return hipGetLastError();
 }

@@ -24,7 +24,7 @@ struct ReqMeta {
   int32_t qt_off;    // first global q-tile
   int32_t nqt;       // ceil(L / 128)
   int32_t nkt;       // ceil(L / 64)
-  int32_t pad0;
+  int32_t kt_off;    // first global k-tile
   int64_t tile_off;  // first tile in tile_class / tile_count
   int32_t seg[4];    // request-local start of PROFILE, HISTORY, REALTIME, CANDIDATE
 };
@@ -96,6 +96,15 @@ struct PlanDev {
   SplitEntry* splits;      // [kSplitTarget]
   int32_t* act_slots;      // [kSplitTarget / 2] active schedule slots, arrival order
   PlanTotals* totals;
+  // key-major tables (plans built with RK_PLAN_BACKWARD)
+  int32_t* kt_req;         // [NK] request of each global k-tile
+  Group* kgroups;          // [G] (request, head) groups of k-tile work items
+  int32_t* kqueue_start;   // [kNumXcd + 1]
+  int32_t* kt_nnz;         // [NK] non-empty q-tiles of each k-tile
+  int32_t* kt_ptr;         // [NK + 1] CSR row pointers
+  int32_t* qtile_word;     // [NT] CSR entry: request-local qt | (PARTIAL << 31)
+  int32_t* korder;         // [NK] k-tiles of each request by descending kt_nnz
+  int32_t* ksched;         // [kslots] work item = k-tile * H + head, or -1
 };
 
 }  // namespace rk
@@ -103,6 +112,7 @@ struct PlanDev {
 struct rk_plan {
   int32_t R, T, H;
   int64_t NQ, NT, G, slots, max_queue;
+  int64_t NK, kslots;       // global k-tiles; k-major launch slots
   int64_t grid;             // attention launch size: slots, or slots + kSplitTarget with a work list
   int64_t delay;
   int32_t window;
@@ -117,7 +127,9 @@ struct rk_plan {
   size_t workspace_bytes;
   size_t off_req, off_qt_req, off_groups, off_queue_start, off_row_desc, off_tile_count,
       off_tile_class, off_qt_nnz, off_qt_pairs, off_qt_full, off_qtile_ptr, off_ktile_idx, off_ktile_word, off_qorder,
-      off_sched, off_work, off_splits, off_act, off_totals, host_blob_bytes, total_bytes;
+      off_sched, off_work, off_splits, off_act, off_totals, host_blob_bytes, total_bytes,
+      off_kt_req, off_kgroups, off_kqueue_start, off_kt_nnz, off_kt_ptr, off_qtile_word,
+      off_korder, off_ksched;
   rk::PlanDev dev;
   // host copy of the first host_blob_bytes of the workspace (kept alive
   // for the asynchronous upload)
@@ -156,6 +168,39 @@ struct AttnLaunch {
   const int64_t* anchors;
   RopeTab tab;
 };
+
+// Backward launch description.  q and k are the rotated Q' and K' when
+// rope is on (rotated by a pass into the workspace, or K given rotated);
+// unrot_q / unrot_k ask the kernels to take dQ / dK back through the
+// rotation (R^T) in their epilogue.  dsum and lse2 ([H][T] fp32, in the
+// workspace) are written by the dQ kernel and read by the dK/dV kernel:
+// dsum = rowsum(dO * O), lse2 = the forward log-sum-exp in log2 units
+// (+inf for rows that see nothing).
+struct BwdLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh, do_st, do_sh, dq_st, dq_sh, dk_st,
+      dk_sh, dv_st, dv_sh;
+  float scale;
+  int H, d, T;
+  bool unrot_q, unrot_k;
+  float* dsum;
+  float* lse2;
+  const int64_t* ts;
+  const int64_t* anchors;
+  RopeTab tab;
+};
+
+hipError_t launch_attn_bwd_reference(const rk_plan* p, const BwdLaunch& a, rk_dtype dt,
+                                     hipStream_t s);
+hipError_t launch_attn_bwd_mfma_bf16_d64(const rk_plan* p, const BwdLaunch& a, hipStream_t s);
 
 hipError_t launch_attn_reference(const rk_plan* p, const AttnLaunch& a, rk_dtype dt,
                                  hipStream_t s);

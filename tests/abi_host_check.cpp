@@ -104,7 +104,9 @@ static void check_mask_plan() {
   bad.window = -3;
   EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
   bad = m;
-  bad.flags = 4;
+  bad.flags = 8;
+  EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
+  bad.flags = RK_QUERY_CANDIDATES_ONLY | RK_PLAN_BACKWARD;
   EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
   bad.flags = RK_QUERY_CANDIDATES_ONLY | 8u;
   EXPECT(rk_mask_plan(&b, &bad, 2, fake(1 << 20), n, &h, nullptr) == RK_ERR_INVALID_ARG);
@@ -176,6 +178,15 @@ static void check_attention_without_plan() {
   info.struct_size = sizeof(info);
   EXPECT(rk_plan_get_info(nullptr, &info) == RK_ERR_INVALID_ARG);
   rk_plan_destroy(nullptr);
+  rk_attn_bwd_args g;
+  std::memset(&g, 0, sizeof(g));
+  g.struct_size = sizeof(g);
+  g.dtype = RK_BF16;
+  g.num_heads = 1;
+  g.d_head = 64;
+  EXPECT(rk_masked_attn_bwd(nullptr, &g, nullptr) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_masked_attn_bwd(nullptr, nullptr, nullptr) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_attn_bwd_workspace_size(nullptr, &g, &n) == RK_ERR_INVALID_ARG);
 }
 
 int main(int argc, char** argv) {

@@ -130,8 +130,9 @@ def test_mask_plan_host_errors(lib):
                             C.byref(h), None) == _rk.RK_ERR_INVALID_ARG
     assert lib.rk_mask_plan(C.byref(b), C.byref(m), 2, None, n.value, C.byref(h),
                             None) == _rk.RK_ERR_INVALID_ARG
-    for bad in (dict(delay=-1), dict(window=-3), dict(flags=4), dict(global_tail=-1),
-                dict(flags=_rk.RK_QUERY_CANDIDATES_ONLY | 8)):
+    for bad in (dict(delay=-1), dict(window=-3), dict(flags=8), dict(global_tail=-1),
+                dict(flags=_rk.RK_QUERY_CANDIDATES_ONLY | 8),
+                dict(flags=_rk.RK_QUERY_CANDIDATES_ONLY | _rk.RK_PLAN_BACKWARD)):
         mb = _rk.sized(_rk.rk_mask_params, **bad)
         assert lib.rk_mask_plan(C.byref(b), C.byref(mb), 2, C.c_void_p(1 << 20), n.value,
                                 C.byref(h), None) == _rk.RK_ERR_INVALID_ARG
@@ -174,3 +175,7 @@ def test_attention_host_errors_without_plan(lib):
     info = _rk.sized(_rk.rk_plan_info)
     assert lib.rk_plan_get_info(None, C.byref(info)) == _rk.RK_ERR_INVALID_ARG
     lib.rk_plan_destroy(None)  # no-op
+    ab = _rk.sized(_rk.rk_attn_bwd_args, dtype=_rk.RK_BF16, num_heads=1, d_head=64)
+    assert lib.rk_masked_attn_bwd(None, C.byref(ab), None) == _rk.RK_ERR_INVALID_ARG
+    assert lib.rk_attn_bwd_workspace_size(None, C.byref(ab), C.byref(n)) == _rk.RK_ERR_INVALID_ARG
+    assert lib.rk_masked_attn_bwd(None, None, None) == _rk.RK_ERR_INVALID_ARG

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "masked_attention_amd")
 BUILD = os.path.join(PKG, "_build")
 DEVICE_OBJS = ["plan.hip.o", "rope.hip.o", "attn_ref.hip.o", "attn_mfma.hip.o",
-               "attn_combine.hip.o"]
+               "attn_combine.hip.o", "attn_bwd_ref.hip.o", "attn_bwd_mfma.hip.o"]
 HIPCC = "/opt/rocm/bin/hipcc"
 
 

@@ -1,0 +1,269 @@
+"""GPU parity of the masked-attention backward (through the C ABI) against
+the CPU fp64 oracle.
+
+* Key-major tables of a backward plan: for every key tile, the ascending
+  list of query tiles with a visible pair and their PARTIAL bits are
+  bit-exact against the oracle's tile plan read by columns; the key-major
+  schedule covers every (key tile, head) once; the query-major tables are
+  the same as those of a forward-only plan.
+* Gradients: dQ, dK, dV against the oracle's chain-rule gradients on the
+  same inputs (the GPU's own forward O and LSE feed its backward).  fp32:
+  within 1e-4 max-abs.  bf16: relative L2 within 1e-2 and max-abs within
+  2e-2 * max(1, max |reference|) (bf16 outputs round to 2^-9 relative, so a
+  fixed absolute bound cannot hold for gradients above 4 in magnitude).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from rk_workloads import (CANDIDATE, HISTORY, NOW, PROFILE, REALTIME, draw_grad,  # noqa: E402
+                          make_config, make_custom, random_layout)
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+BF16_MAX_ABS = 2e-2
+BF16_REL_L2 = 1e-2
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def rk():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import masked_attention_amd as m
+    from masked_attention_amd import _rk
+    _rk.lib()
+    return m
+
+
+def _rope(wl):
+    return dict(phi_min=wl.phi_min, dt_max=wl.dt_max, base=wl.base)
+
+
+def _dt(wl):
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+
+def _plan(rk, wl, backward=True, batch=None):
+    batch = batch or rk.Batch.from_workload(wl)
+    plan = rk.Plan(batch, delay=wl.delay, window=wl.window,
+                   static_bidirectional=wl.static_bidirectional, num_heads=wl.heads,
+                   global_tail=wl.global_tail, backward=backward)
+    return batch, plan
+
+
+def _key_major_ref(wl):
+    """Oracle tile plan read by columns: per global key tile, ascending query
+    tiles with a visible pair, bit 31 set when PARTIAL."""
+    ptr, words = [0], []
+    for r in range(wl.num_requests):
+        a, b = wl.request(r)
+        if b == a:
+            continue
+        cnt, cls = oracle.tile_plan_request(wl.seg_kind[a:b], wl.timestamps[a:b], delay=wl.delay,
+                                            window=wl.window,
+                                            static_bidirectional=wl.static_bidirectional,
+                                            global_tail=wl.global_tail)
+        for kt in range(cnt.shape[1]):
+            qts = np.nonzero(cnt[:, kt])[0]
+            for qt in qts:
+                words.append(int(qt) | ((1 << 31) if cls[qt, kt] == oracle.PARTIAL else 0))
+            ptr.append(ptr[-1] + qts.shape[0])
+    w = np.array(words, dtype=np.uint32).view(np.int32) if words else np.zeros(0, np.int32)
+    return np.array(ptr, np.int64), w
+
+
+def _check_key_major(rk, wl):
+    batch, plan = _plan(rk, wl)
+    _, fplan = _plan(rk, wl, backward=False, batch=batch)
+    torch.cuda.synchronize()
+    assert plan.stats()["device_errors"] == 0
+    ptr_ref, words_ref = _key_major_ref(wl)
+    assert np.array_equal(plan.kt_ptr().cpu().numpy().astype(np.int64), ptr_ref)
+    assert np.array_equal(plan.qtile_word().cpu().numpy(), words_ref)
+    ks = plan.ksched().cpu().numpy()
+    items = np.sort(ks[ks >= 0])
+    assert np.array_equal(items, np.arange(plan.num_ktiles * wl.heads))
+    # the query-major tables are those of a forward-only plan
+    for f in ("tile_class", "tile_count", "qtile_ptr", "ktile_idx", "sched", "row_desc"):
+        assert torch.equal(getattr(plan, f)(), getattr(fplan, f)()), f
+    assert fplan.kt_ptr() is None
+
+
+def test_key_major_tables_random_layouts(rk):
+    for seed in range(6):
+        rng = np.random.default_rng(100 + seed)
+        reqs = random_layout(rng, 5, 700)
+        for bidir, delay, window, G in ((False, 3600, 0, 0), (True, 0, 0, 0), (False, 0, 130, 70),
+                                        (False, 60, 200, 0)):
+            _say(f"[gpu] key-major seed={seed} bidir={bidir} delay={delay} window={window} G={G}")
+            wl = make_custom(reqs, heads=3, d_head=64, seed=seed, delay=delay, window=window,
+                             static_bidirectional=bidir, global_tail=G, with_qkv=False)
+            _check_key_major(rk, wl)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_key_major_tables_workloads(rk, cfg):
+    _say(f"[gpu] key-major workload {cfg}")
+    _check_key_major(rk, make_config(cfg, with_qkv=False))
+
+
+def _grads_gpu(rk, wl, rope, reference=False, k_prerotated=False, strided=False):
+    batch, plan = _plan(rk, wl)
+    dt = _dt(wl)
+    q, k, v = (torch.from_numpy(x).to("cuda").to(dt) for x in (wl.q, wl.k, wl.v))
+    do = torch.from_numpy(draw_grad(wl)).to("cuda").to(dt)
+    if strided:
+        # [T, H, d] views with padded token and head strides
+        def pad(x):
+            T, H, d = x.shape
+            big = torch.zeros((T, H + 1, d + 8), dtype=x.dtype, device=x.device)
+            big[:, :H, :d] = x
+            return big[:, :H, :d]
+        q, k, v, do = pad(q), pad(k), pad(v), pad(do)
+    rp = _rope(wl) if rope else None
+    k_in = k
+    if k_prerotated:
+        k_in = rk.rk_time_rope(batch, k, **rp)
+    o, lse = rk.rk_masked_attn_fwd(plan, q, k_in, v, rope=rp, want_lse=True,
+                                   reference=reference, k_prerotated=k_prerotated)
+    dq, dk, dv = rk.rk_masked_attn_bwd(plan, q, k_in, v, o, lse, do, rope=rp,
+                                       reference=reference, k_prerotated=k_prerotated)
+    torch.cuda.synchronize()
+    f = lambda x: x.float().cpu().numpy().astype(np.float64)
+    return f(dq), f(dk), f(dv), draw_grad(wl)
+
+
+def _check_grad(wl, got, ref, what):
+    err = np.abs(got - ref)
+    if wl.dtype == "f32":
+        assert err.max() <= F32_TOL, f"{what}: max abs {err.max()}"
+    else:
+        rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+        bound = BF16_MAX_ABS * max(1.0, float(np.abs(ref).max()))
+        assert rel <= BF16_REL_L2, f"{what}: rel L2 {rel}"
+        assert err.max() <= bound, f"{what}: max abs {err.max()} > {bound}"
+
+
+def _oracle_grads(wl, do, rope, k_prerotated=False):
+    """Oracle gradients with respect to the tensors the GPU call was given:
+    unrotated q, k, v; with k_prerotated, k is passed rotated by (t - anchor),
+    so dk is the gradient with respect to that rotated key."""
+    q, k, v = (x.astype(np.float64) for x in (wl.q, wl.k, wl.v))
+    margs = dict(delay=wl.delay, window=wl.window, static_bidirectional=wl.static_bidirectional,
+                 global_tail=wl.global_tail)
+    if not k_prerotated:
+        return oracle.attention_backward(wl.req_offsets, wl.seg_kind, wl.timestamps, q, k, v,
+                                         do.astype(np.float64),
+                                         rope=_rope(wl) if rope else None, **margs)
+    t_rel = wl.timestamps - np.repeat(wl.anchors, np.diff(wl.req_offsets))
+    qr = oracle.time_rope(q, t_rel, **_rope(wl))
+    kr = oracle.time_rope(k, t_rel, **_rope(wl))
+    dq_r, dk_r, dv = oracle.attention_backward(wl.req_offsets, wl.seg_kind, wl.timestamps, qr,
+                                               kr, v, do.astype(np.float64), **margs)
+    return oracle.time_rope_transpose(dq_r, t_rel, **_rope(wl)), dk_r, dv
+
+
+CASES = [
+    # (dtype, d, reference, bidir, delay, window, G)
+    ("f32", 32, True, False, 3600, 0, 0),
+    ("f32", 64, True, True, 0, 0, 0),
+    ("f32", 128, True, False, 0, 100, 0),
+    ("bf16", 32, True, False, 60, 0, 0),
+    ("bf16", 64, True, False, 0, 90, 40),
+    ("bf16", 128, True, True, 0, 0, 0),
+    ("bf16", 64, False, False, 3600, 0, 0),
+    ("bf16", 64, False, True, 0, 0, 0),
+    ("bf16", 64, False, False, 0, 150, 64),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-{'ref' if c[2] else 'mfma'}-b{int(c[3])}-D{c[4]}-W{c[5]}-G{c[6]}" for c in CASES])
+def test_backward_matches_oracle(rk, case):
+    dtype, d, reference, bidir, delay, window, G = case
+    rng = np.random.default_rng(d + delay + window)
+    reqs = random_layout(rng, 4, 460)
+    for rope in (True, False):
+        _say(f"[gpu] backward {case} rope={rope}")
+        wl = make_custom(reqs, heads=2, d_head=d, dtype=dtype, seed=d + window, delay=delay,
+                         window=window, static_bidirectional=bidir, global_tail=G)
+        dq, dk, dv, do = _grads_gpu(rk, wl, rope, reference=reference)
+        rq, rk_, rv = _oracle_grads(wl, do, rope)
+        _check_grad(wl, dq, rq, "dq")
+        _check_grad(wl, dk, rk_, "dk")
+        _check_grad(wl, dv, rv, "dv")
+
+
+@pytest.mark.parametrize("reference", [True, False])
+def test_backward_strided_and_prerotated(rk, reference):
+    rng = np.random.default_rng(77)
+    reqs = random_layout(rng, 3, 400, allow_empty=False)
+    wl = make_custom(reqs, heads=3, d_head=64, dtype="bf16", seed=77, delay=600, window=0)
+    for strided, pre in ((True, False), (False, True)):
+        _say(f"[gpu] backward strided={strided} k_prerotated={pre} reference={reference}")
+        dq, dk, dv, do = _grads_gpu(rk, wl, True, reference=reference, k_prerotated=pre,
+                                    strided=strided)
+        rq, rk_, rv = _oracle_grads(wl, do, True, k_prerotated=pre)
+        _check_grad(wl, dq, rq, "dq")
+        _check_grad(wl, dk, rk_, "dk")
+        _check_grad(wl, dv, rv, "dv")
+
+
+def test_backward_empty_rows_and_unseen_keys_are_zero(rk):
+    """Rows that see nothing get dQ = 0 and keys nobody sees get dK = dV = 0,
+    exactly, also where the output buffers held other values."""
+    hist = np.sort(np.random.default_rng(5).integers(NOW - 6 * 3600, NOW, size=300))
+    wl = make_custom([[(HISTORY, hist)]], heads=2, d_head=64, dtype="bf16", seed=5, delay=3600)
+    batch, plan = _plan(rk, wl)
+    q, k, v = (torch.from_numpy(x).to("cuda").to(torch.bfloat16) for x in (wl.q, wl.k, wl.v))
+    do = torch.from_numpy(draw_grad(wl)).to("cuda").to(torch.bfloat16)
+    o, lse = rk.rk_masked_attn_fwd(plan, q, k, v, rope=_rope(wl), want_lse=True)
+    for reference in (True, False):
+        dq, dk, dv = (torch.full_like(q, 7.0) for _ in range(3))
+        rk.rk_masked_attn_bwd(plan, q, k, v, o, lse, do, rope=_rope(wl), dq=dq, dk=dk, dv=dv,
+                              reference=reference)
+        torch.cuda.synchronize()
+        vis = oracle.visibility(wl.seg_kind, wl.timestamps, delay=wl.delay, window=0,
+                                static_bidirectional=False)
+        empty = torch.from_numpy(~vis.any(axis=1)).cuda()
+        unseen = torch.from_numpy(~vis.any(axis=0)).cuda()
+        assert empty.sum() > 0 and unseen.sum() > 0
+        assert torch.all(dq[empty] == 0) and torch.all(dk[unseen] == 0)
+        assert torch.all(dv[unseen] == 0)
+        assert not torch.any(dq == 7.0) and not torch.any(dk == 7.0)
+
+
+def test_backward_deterministic(rk):
+    wl = make_config(2)
+    wl = make_custom([[(HISTORY, wl.timestamps[:1024])], [(HISTORY, wl.timestamps[1024:1800])]],
+                     heads=4, d_head=64, dtype="bf16", seed=3, delay=3600)
+    a = _grads_gpu(rk, wl, True)
+    b = _grads_gpu(rk, wl, True)
+    for x, y in zip(a[:3], b[:3]):
+        assert np.array_equal(x, y)
+
+
+def test_backward_rejects_forward_only_plan(rk):
+    from masked_attention_amd import _rk
+    wl = make_custom([[(HISTORY, np.arange(NOW - 200, NOW, 2, dtype=np.int64))]], heads=1,
+                     d_head=64, dtype="bf16", seed=1)
+    batch, plan = _plan(rk, wl, backward=False)
+    q = torch.from_numpy(wl.q).cuda().to(torch.bfloat16)
+    o, lse = rk.rk_masked_attn_fwd(plan, q, q, q, want_lse=True)
+    with pytest.raises(_rk.RkError) as e:
+        rk.rk_masked_attn_bwd(plan, q, q, q, o, lse, q)
+    assert e.value.status == _rk.RK_ERR_INVALID_ARG
+    _, bplan = _plan(rk, wl, batch=batch)
+    with pytest.raises(_rk.RkError) as e:
+        rk.rk_masked_attn_bwd(bplan, q, q, q, o, None, q)
+    assert e.value.status == _rk.RK_ERR_INVALID_ARG
