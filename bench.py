@@ -49,6 +49,10 @@ def _parse():
                     help="serving step: the history keys are rotated once before timing; each "
                          "step plans the candidates' query tiles only, rotates the candidate "
                          "keys into the key cache and runs the attention for those tiles")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward step instead: the forward runs once (untimed) for "
+                         "O and LSE; each step plans with the key-major tables and runs "
+                         "rk_masked_attn_bwd (Q/K rotation, dQ kernel, dK/dV kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter scaling)")
     return ap.parse_args()
@@ -123,6 +127,127 @@ def _cpu_baseline(wl, n_heads: int):
                       f"0-{len(heads) - 1}, fp64 NumPy with explicit mask, {dt:.2f} s wall"}
 
 
+def _cpu_baseline_bwd(wl, n_heads: int):
+    """Time the fp64 oracle backward, as it stands, on request 0 and heads
+    0..n_heads-1 (its forward statistics included)."""
+    import oracle
+    from rk_workloads import draw_grad
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        cores = max(int(i.get("num_threads", 1)) for i in info) if info else 1
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    a, b = wl.request(0)
+    pairs = oracle.count_visible(wl.seg_kind[a:b], wl.timestamps[a:b], delay=wl.delay,
+                                 window=wl.window, static_bidirectional=wl.static_bidirectional)
+    heads = list(range(min(n_heads, wl.heads)))
+    rope = dict(phi_min=wl.phi_min, dt_max=wl.dt_max, base=wl.base)
+    do = draw_grad(wl)
+    t0 = time.perf_counter()
+    oracle.attention_backward(wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q, wl.k, wl.v, do,
+                              delay=wl.delay, window=wl.window,
+                              static_bidirectional=wl.static_bidirectional, rope=rope,
+                              heads=heads, requests=[0])
+    dt = time.perf_counter() - t0
+    flops = 10.0 * wl.d_head * pairs * len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"request 0 ({b - a} tokens, {pairs} visible pairs per head), heads "
+                      f"0-{len(heads) - 1}, fp64 NumPy backward with explicit mask, "
+                      f"{dt:.2f} s wall"}
+
+
+def backward_main(args) -> int:
+    """One JSON line for the backward step (effective FLOPs = 10 d per
+    visible pair and head: the five d-wide products of the backward)."""
+    import numpy as np
+    import torch
+
+    import masked_attention_amd as rk
+    from rk_workloads import draw_grad, make_config
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    wl = make_config(args.config)
+    H, d = wl.heads, wl.d_head
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    batch = rk.Batch.from_workload(wl, device=dev)
+    q, k, v = (torch.from_numpy(x).to(dev).to(tdt) for x in (wl.q, wl.k, wl.v))
+    do = torch.from_numpy(draw_grad(wl)).to(dev).to(tdt)
+    rope = dict(phi_min=wl.phi_min, dt_max=wl.dt_max, base=wl.base)
+    ws = torch.empty(rk.rk_plan_workspace_size(batch, H), dtype=torch.uint8, device=dev)
+    mk = dict(delay=wl.delay, window=wl.window, static_bidirectional=wl.static_bidirectional,
+              num_heads=H, backward=True, workspace=ws)
+    plan = rk.Plan(batch, **mk)
+    pairs = plan.stats()["visible_pairs"]
+    o, lse = rk.rk_masked_attn_fwd(plan, q, k, v, rope=rope, want_lse=True)
+    dq, dk, dv = (torch.empty_like(x) for x in (q, k, v))
+    bws = None
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        p = rk.Plan(batch, **mk)
+        if ev: ev[1].record(stream)
+        rk.rk_masked_attn_bwd(p, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, rope=rope,
+                              workspace=bws)
+        if ev: ev[2].record(stream)
+        return p
+
+    plans = [step()]
+    from masked_attention_amd import _rk
+    import ctypes as C
+    a = rk.binding._bwd_args(q, k, v, o, do, lse, dq, dk, dv, 0.0,
+                             rk.binding.rope_params(**rope), False, False, None)
+    n = C.c_size_t()
+    _rk.check(_rk.lib().rk_attn_bwd_workspace_size(plan.handle, C.byref(a), C.byref(n)), "ws")
+    bws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        plans.append(step())
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plans.append(step(evs[i]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for p in plans:
+        p.close()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    plan_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    flops = 10.0 * d * H * pairs
+    achieved = flops / (bwd_ms * 1e-3) / 1e12
+    out = {
+        "metric": "masked-attn bwd effective TFLOP/s (visible pairs, 10 d FLOPs per pair and head)",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded generator with the workload's shapes and time law)",
+        "config": {"workload": wl.name + " backward", "requests": wl.num_requests,
+                   "tokens": wl.total_tokens, "heads": H, "d_head": d,
+                   "visible_pairs_per_head": pairs},
+        "pct_bf16_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "stage_ms": {"plan": round(plan_ms, 4), "backward": round(bwd_ms, 4)},
+        "roofline": {"bound": "mfma", "kernel": "rk_masked_attn_bwd (Q/K rotation, dq and dkdv "
+                     "kernels)", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline_bwd(wl, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -131,6 +256,8 @@ def main() -> int:
               "measured on a single MI355X (requests and heads shard across GPUs without "
               "communication; see the design notes). Use --gpus 1.", file=sys.stderr)
         return 2
+    if args.backward:
+        return backward_main(args)
 
     import numpy as np
     import torch

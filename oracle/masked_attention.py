@@ -373,6 +373,72 @@ def attention_backward(req_offsets: np.ndarray, seg_kind: np.ndarray, timestamps
     return dq, dk, dv
 
 
+def attention_backward_sampled(req_offsets, seg_kind, timestamps, q, k, v, do, *, request: int,
+                               head: int, rows: np.ndarray, keys: np.ndarray, delay, window,
+                               static_bidirectional, rope=None, scale=None, global_tail: int = 0,
+                               row_block: int = 1024):
+    """dq of selected rows and dk, dv of selected keys of ONE request and
+    head (request-local positions), for checks at sizes where the full
+    matrices do not fit.
+
+    Same chain rule as masked_softmax_attention_backward.  The row softmax
+    statistics (log-sum-exp and D_i = do_i . o_i) of every row of the request
+    come first, in blocks of rows; then
+      dq_i = scale * sum_j P_ij (dP_ij - D_i) k_j            for i in rows,
+      dv_j = sum_i P_ij do_i,
+      dk_j = scale * sum_i P_ij (dP_ij - D_i) q_i            for j in keys,
+    with the sums over i taken block by block.  Returns (dq [len(rows), d],
+    dk [len(keys), d], dv [len(keys), d]) with respect to the unrotated
+    vectors.
+    """
+    a, b = int(req_offsets[request]), int(req_offsets[request + 1])
+    L = b - a
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    sk, ts = seg_kind[a:b], timestamps[a:b]
+    qr = np.asarray(q[a:b, head], np.float64)
+    kr = np.asarray(k[a:b, head], np.float64)
+    vr = np.asarray(v[a:b, head], np.float64)
+    gr = np.asarray(do[a:b, head], np.float64)
+    if rope is not None:
+        qr = time_rope(qr, ts, **rope)
+        kr = time_rope(kr, ts, **rope)
+    margs = dict(delay=delay, window=window, static_bidirectional=static_bidirectional,
+                 global_tail=global_tail)
+    lse = np.full(L, -np.inf)
+    dsum = np.zeros(L)
+    for r0 in range(0, L, row_block):
+        blk = np.arange(r0, min(L, r0 + row_block))
+        vis = visible_rows(sk, ts, blk, **margs)
+        o_blk, lse[blk] = masked_softmax_attention(qr[blk], kr, vr, vis, scale)
+        dsum[blk] = (gr[blk] * o_blk).sum(axis=1)
+
+    def probs(blk, cols, vis):
+        s = (qr[blk] @ kr[cols].T) * scale
+        return np.where(vis, np.exp(s - lse[blk][:, None]), 0.0)
+
+    rows = np.asarray(rows, np.int64)
+    keys = np.asarray(keys, np.int64)
+    allk = np.arange(L)
+    vis = visible_rows(sk, ts, rows, **margs)
+    p = probs(rows, allk, vis)
+    ds = p * (gr[rows] @ vr.T - dsum[rows][:, None])
+    dq = (ds @ kr) * scale
+    dk = np.zeros((keys.shape[0], d))
+    dv = np.zeros((keys.shape[0], d))
+    for r0 in range(0, L, row_block):
+        blk = np.arange(r0, min(L, r0 + row_block))
+        visk = visible_rows(sk, ts, blk, **margs)[:, keys]
+        pk = probs(blk, keys, visk)
+        dv += pk.T @ gr[blk]
+        dsk = pk * (gr[blk] @ vr[keys].T - dsum[blk][:, None])
+        dk += (dsk.T @ qr[blk]) * scale
+    if rope is not None:
+        dq = time_rope_transpose(dq, ts[rows], **rope)
+        dk = time_rope_transpose(dk, ts[keys], **rope)
+    return dq, dk, dv
+
+
 # ---------------------------------------------------------------------------
 # Tile plan reference (128 query rows x 64 key columns)
 # ---------------------------------------------------------------------------

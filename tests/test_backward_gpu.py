@@ -267,3 +267,56 @@ def test_backward_rejects_forward_only_plan(rk):
     with pytest.raises(_rk.RkError) as e:
         rk.rk_masked_attn_bwd(bplan, q, q, q, o, None, q)
     assert e.value.status == _rk.RK_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_backward_workloads_sampled(rk, cfg):
+    """Full-size workloads in the launch configuration the backward benchmark
+    times (backward plan; forward with fused RoPE and LSE; backward with
+    RoPE), checked on sampled rows (dQ) and keys (dK, dV) of the first and
+    last requests against the oracle's per-row / per-key gradients."""
+    wl = make_config(cfg)
+    _say(f"[gpu] backward sampled workload {cfg}: T={wl.total_tokens} H={wl.heads}")
+    batch, plan = _plan(rk, wl)
+    q, k, v = (torch.from_numpy(x).to("cuda").to(torch.bfloat16) for x in (wl.q, wl.k, wl.v))
+    do_np = draw_grad(wl)
+    do = torch.from_numpy(do_np).to("cuda").to(torch.bfloat16)
+    o, lse = rk.rk_masked_attn_fwd(plan, q, k, v, rope=_rope(wl), want_lse=True)
+    dq, dk, dv = rk.rk_masked_attn_bwd(plan, q, k, v, o, lse, do, rope=_rope(wl))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg)
+    reqs = [0] if cfg == 5 else [0, wl.num_requests - 1]
+    heads = [wl.heads - 1] if cfg == 5 else [0, wl.heads - 1]
+    got, ref = [], []
+    for r in reqs:
+        a, b = wl.request(r)
+        L = b - a
+        pick = lambda n: np.unique(np.concatenate([[0, L - 1], rng.choice(L, size=n, replace=False)]))
+        rows, keys = pick(20), pick(20)
+        cand = np.nonzero(wl.seg_kind[a:b] == CANDIDATE)[0]
+        if cand.shape[0]:
+            rows = np.unique(np.concatenate([rows, cand[:3], cand[-2:]]))
+            keys = np.unique(np.concatenate([keys, cand[:2]]))
+        for h in heads:
+            rq, rk_, rv = oracle.attention_backward_sampled(
+                wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q, wl.k, wl.v, do_np, request=r,
+                head=h, rows=rows, keys=keys, delay=wl.delay, window=wl.window,
+                static_bidirectional=wl.static_bidirectional, rope=_rope(wl),
+                global_tail=wl.global_tail)
+            f = lambda x, idx: x[a + idx, h].float().cpu().numpy().astype(np.float64)
+            got += [f(dq, rows).ravel(), f(dk, keys).ravel(), f(dv, keys).ravel()]
+            ref += [rq.ravel(), rk_.ravel(), rv.ravel()]
+    got, ref = np.concatenate(got), np.concatenate(ref)
+    _check_grad(wl, got, ref, f"workload {cfg} sampled gradients")
+
+
+def test_backward_tiny_fp32_workload_full(rk):
+    """The fp32 workload (one request of 256 history + 16 candidates, H = 2,
+    d = 32, one-hour delay, time RoPE) compared element by element."""
+    wl = make_config(1)
+    _say(f"[gpu] backward {wl.name}")
+    dq, dk, dv, do = _grads_gpu(rk, wl, True)
+    rq, rk_, rv = _oracle_grads(wl, do, True)
+    _check_grad(wl, dq, rq, "dq")
+    _check_grad(wl, dk, rk_, "dk")
+    _check_grad(wl, dv, rv, "dv")

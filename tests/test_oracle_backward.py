@@ -191,3 +191,26 @@ def test_heads_and_requests_subsets():
         assert np.array_equal(p[a0:b0, 1], f[a0:b0, 1])
         assert np.array_equal(p[a2:b2, 1], f[a2:b2, 1])
         assert np.all(p[:, [0, 2]] == 0.0) and np.all(p[a1:b1] == 0.0)
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_sampled_backward_equals_full(seed):
+    """The sampled form (row statistics first, sums over row blocks) gives
+    the full backward's entries."""
+    rng = np.random.default_rng(seed)
+    reqs = random_layout(rng, 3, 300, allow_empty=False)
+    wl = make_custom(reqs, heads=2, d_head=8, seed=seed, delay=600, window=40, global_tail=5)
+    do = draw_grad(wl)
+    dq, dk, dv = _bwd(wl, do, rope=ROPE)
+    for r in range(wl.num_requests):
+        a, b = wl.request(r)
+        rows = rng.choice(b - a, size=min(9, b - a), replace=False)
+        keys = rng.choice(b - a, size=min(7, b - a), replace=False)
+        for h in range(2):
+            sq, sk_, sv = oracle.attention_backward_sampled(
+                wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q, wl.k, wl.v, do, request=r,
+                head=h, rows=rows, keys=keys, delay=wl.delay, window=wl.window,
+                static_bidirectional=False, rope=ROPE, global_tail=wl.global_tail, row_block=37)
+            assert np.allclose(sq, dq[a + rows, h], atol=1e-12, rtol=0)
+            assert np.allclose(sk_, dk[a + keys, h], atol=1e-12, rtol=0)
+            assert np.allclose(sv, dv[a + keys, h], atol=1e-12, rtol=0)
