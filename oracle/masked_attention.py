@@ -440,6 +440,99 @@ def attention_backward_sampled(req_offsets, seg_kind, timestamps, q, k, v, do, *
 
 
 # ---------------------------------------------------------------------------
+# LazFormer history compression and per-layer pruning (section 2.3)
+# ---------------------------------------------------------------------------
+
+def compressed_history_length(L: int, keep: int, group: int) -> int:
+    """Length after compression (eq. 16-18): the ell = min(L, keep) recent
+    tokens plus N = ceil((L - ell) / group) group sums."""
+    ell = min(L, keep)
+    return ell + -(-(L - ell) // group)
+
+
+def group_sum_compress(req_offsets, seg_kind, timestamps, x, *, keep: int, group: int):
+    """Compress the HISTORY segment of every request (eq. 16-18).
+
+    Per request with L history tokens in time order: the ell = min(L, keep)
+    most recent are kept as they are; the L - ell older ones are summed in
+    groups of `group`, counted back from the kept part, so a group with fewer
+    members can only be the oldest one.  The output keeps time order:
+    profile tokens, the group sums (oldest first), the kept history, then
+    real-time and candidate tokens unchanged.  A group's timestamp is that of
+    its newest member.  x: [T, ...] features (summed in float64).
+    Returns (req_offsets, seg_kind, timestamps, y).
+    """
+    x = np.asarray(x, np.float64)
+    offs, kinds, times, rows = [0], [], [], []
+    for r in range(req_offsets.shape[0] - 1):
+        a, b = int(req_offsets[r]), int(req_offsets[r + 1])
+        hist = [j for j in range(a, b) if seg_kind[j] == HISTORY]
+        ell = min(len(hist), keep)
+        old = hist[:len(hist) - ell]
+        # group boundaries counted back from the kept part
+        groups = []
+        end = len(old)
+        while end > 0:
+            start = max(0, end - group)
+            groups.append(old[start:end])
+            end = start
+        groups.reverse()
+        out = []
+        for j in range(a, b):
+            if seg_kind[j] == HISTORY:
+                continue
+            if seg_kind[j] == PROFILE:
+                out.append((PROFILE, int(timestamps[j]), x[j]))
+        for g in groups:
+            out.append((HISTORY, int(timestamps[g[-1]]), x[g].sum(axis=0)))
+        for j in hist[len(hist) - ell:]:
+            out.append((HISTORY, int(timestamps[j]), x[j]))
+        for j in range(a, b):
+            if seg_kind[j] in (REALTIME, CANDIDATE):
+                out.append((int(seg_kind[j]), int(timestamps[j]), x[j]))
+        for kd, t, row in out:
+            kinds.append(kd)
+            times.append(t)
+            rows.append(row)
+        offs.append(offs[-1] + len(out))
+    y = np.stack(rows) if rows else np.zeros((0,) + x.shape[1:])
+    return (np.asarray(offs, np.int32), np.asarray(kinds, np.uint8),
+            np.asarray(times, np.int64), y)
+
+
+def pruned_history_length(l_tilde: int, n_min: int, layer: int, num_layers: int) -> int:
+    """History positions layer `layer` (1-based) of `num_layers` keeps (eq. 22):
+    min(L~, max(N_min, Round[L~ - (l - 1) / (L - 1) * (L~ - N_min)])), Round
+    taking halves away from zero.  A single layer keeps L~."""
+    if num_layers <= 1:
+        return l_tilde
+    val = l_tilde - (layer - 1) / (num_layers - 1) * (l_tilde - n_min)
+    rnd = math.floor(abs(val) + 0.5) * (1 if val >= 0 else -1)
+    return min(l_tilde, max(n_min, rnd))
+
+
+def prune_history(req_offsets, seg_kind, timestamps, x, *, l_tilde, n_min: int, layer: int,
+                  num_layers: int):
+    """Input of layer `layer`: per request, the last N^l HISTORY tokens
+    (N^l from eq. 22 with that request's L~ = l_tilde[r]) and every PROFILE,
+    REALTIME and CANDIDATE token, in their order.  x: [T, ...].
+    Returns (req_offsets, seg_kind, timestamps, y)."""
+    x = np.asarray(x, np.float64)
+    offs, sel = [0], []
+    for r in range(req_offsets.shape[0] - 1):
+        a, b = int(req_offsets[r]), int(req_offsets[r + 1])
+        hist = [j for j in range(a, b) if seg_kind[j] == HISTORY]
+        n = pruned_history_length(int(l_tilde[r]), n_min, layer, num_layers)
+        drop = set(hist[:max(0, len(hist) - n)])
+        keep = [j for j in range(a, b) if j not in drop]
+        sel += keep
+        offs.append(offs[-1] + len(keep))
+    sel = np.asarray(sel, np.int64)
+    return (np.asarray(offs, np.int32), seg_kind[sel].astype(np.uint8),
+            timestamps[sel].astype(np.int64), x[sel])
+
+
+# ---------------------------------------------------------------------------
 # Tile plan reference (128 query rows x 64 key columns)
 # ---------------------------------------------------------------------------
 
