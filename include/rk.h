@@ -14,7 +14,10 @@
  *   rk_time_rope        rotate Q or K by time RoPE;
  *   rk_masked_attn_fwd  softmax(Q K^T * scale + M) V over the plan, with
  *                       optional fused time RoPE;
- *   rk_masked_attn_bwd  its gradients with respect to Q, K and V.
+ *   rk_masked_attn_bwd  its gradients with respect to Q, K and V;
+ *   rk_compress_layout / rk_prune_layout / rk_gather_sum
+ *                       LazFormer's history compression and per-layer
+ *                       history pruning, before and between layers.
  *
  * Sources (titles and sections of the pages this library follows):
  *  - CADET: Context-Conditioned Ads CTR Prediction With a Decoder-Only
@@ -435,6 +438,91 @@ rk_status rk_attn_bwd_workspace_size(const rk_plan* p, const rk_attn_bwd_args* a
  * RK_ERR_HIP.
  */
 rk_status rk_masked_attn_bwd(const rk_plan* p, const rk_attn_bwd_args* a, void* stream);
+
+/* ---- LazFormer pre-passes (section 2.3): history compression and per-layer
+ * history pruning.  The layout functions run on the host (they read host
+ * copies of the segment kinds and timestamps, O(total_tokens)) and describe
+ * each output token as a contiguous range of input rows; rk_gather_sum then
+ * moves the feature rows (Q, K, V, hidden states, any width) on the device.
+ * Readings where the page leaves the order open: histories are in time
+ * order; the `keep` most recent history tokens are kept; the older ones are
+ * summed in groups counted back from the kept part (a short group can only
+ * be the oldest); a group carries its newest member's timestamp; pruning
+ * drops the oldest history tokens; PROFILE, REALTIME and CANDIDATE tokens are
+ * never compressed or pruned. */
+
+/* Host copy of a packed layout. */
+typedef struct rk_host_layout {
+  uint32_t struct_size;
+  int32_t num_requests;
+  int32_t total_tokens;
+  int32_t reserved;
+  const int32_t* req_offsets; /* [num_requests + 1], as in rk_batch */
+  const uint8_t* seg_kind;    /* [total_tokens] */
+  const int64_t* timestamps;  /* [total_tokens]; HISTORY non-decreasing per request */
+} rk_host_layout;
+
+/* Caller-allocated host arrays receiving an output layout.  `capacity` is
+ * the number of tokens the arrays hold; a call whose output is longer
+ * returns RK_ERR_WORKSPACE_TOO_SMALL with total_tokens set to the length it
+ * needs and writes nothing else (capacity 0 with NULL arrays is a size
+ * query).  req_offsets must hold num_requests + 1 entries. */
+typedef struct rk_layout_out {
+  uint32_t struct_size;
+  int32_t capacity;
+  int32_t total_tokens;  /* set by the call */
+  int32_t reserved;
+  int32_t* req_offsets;  /* [num_requests + 1] */
+  uint8_t* seg_kind;     /* [capacity] */
+  int64_t* timestamps;   /* [capacity] */
+  int32_t* ranges;       /* [capacity][2]: output token i = sum of input rows
+                            [ranges[2i], ranges[2i+1]) */
+} rk_layout_out;
+
+/*
+ * Group-sum compression (LazFormer eq. 16-18): per request with L HISTORY
+ * tokens, the ell = min(L, keep) most recent stay as they are and the L - ell
+ * older ones become ceil((L - ell) / group) group sums.  Output order per
+ * request: PROFILE, group sums (oldest first), kept HISTORY, REALTIME,
+ * CANDIDATE.  keep >= 0, group >= 1.
+ * Errors: RK_ERR_INVALID_ARG, RK_ERR_SEGMENT_ORDER, RK_ERR_UNSORTED_TIME
+ * (history out of time order), RK_ERR_WORKSPACE_TOO_SMALL (see
+ * rk_layout_out).
+ */
+rk_status rk_compress_layout(const rk_host_layout* in, int32_t keep, int32_t group,
+                             rk_layout_out* out);
+
+/* History positions kept at layer `layer` (1-based) of `num_layers`
+ * (LazFormer eq. 22): min(l_tilde, max(n_min, Round[l_tilde - (layer - 1) /
+ * (num_layers - 1) * (l_tilde - n_min)])), Round taking halves away from
+ * zero; l_tilde when num_layers == 1.  Errors: RK_ERR_INVALID_ARG. */
+rk_status rk_pruned_history_length(int32_t l_tilde, int32_t n_min, int32_t layer,
+                                   int32_t num_layers, int32_t* n_out);
+
+/*
+ * Input layout of layer `layer` (LazFormer eq. 22, "the next layer receives
+ * the most recent history and all targets"): per request r, the last
+ * N = rk_pruned_history_length(l_tilde[r], ...) HISTORY tokens of `in` and
+ * every other token, in order.  l_tilde: host [num_requests], each request's
+ * compressed history length (the first layer's).
+ * Errors: as rk_compress_layout.
+ */
+rk_status rk_prune_layout(const rk_host_layout* in, const int32_t* l_tilde, int32_t n_min,
+                          int32_t layer, int32_t num_layers, rk_layout_out* out);
+
+/*
+ * y[i] = sum over input rows j in [ranges[2i], ranges[2i+1]) of x[j], for
+ * i < n_out, each row `width` elements of `dtype` (fp32 accumulation; RK_BF16
+ * rounds once, to nearest even).  ranges: device int32 [n_out][2] (from a
+ * layout function); ranges are clamped to [0, n_in), so a bad range reads
+ * no memory outside x.  Rows are `x_stride` / `y_stride` elements apart.
+ * y must not overlap x.  HBM-bound: reads the input rows once, writes the
+ * output rows once.
+ * Errors: RK_ERR_INVALID_ARG, RK_ERR_HIP.
+ */
+rk_status rk_gather_sum(const int32_t* ranges, int32_t n_out, int32_t n_in, const void* x,
+                        int64_t x_stride, void* y, int64_t y_stride, int32_t width,
+                        rk_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

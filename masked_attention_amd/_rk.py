@@ -166,6 +166,31 @@ class rk_attn_bwd_args(C.Structure):
     ]
 
 
+class rk_host_layout(C.Structure):
+    _fields_ = [
+        ("struct_size", C.c_uint32),
+        ("num_requests", C.c_int32),
+        ("total_tokens", C.c_int32),
+        ("reserved", C.c_int32),
+        ("req_offsets", C.c_void_p),
+        ("seg_kind", C.c_void_p),
+        ("timestamps", C.c_void_p),
+    ]
+
+
+class rk_layout_out(C.Structure):
+    _fields_ = [
+        ("struct_size", C.c_uint32),
+        ("capacity", C.c_int32),
+        ("total_tokens", C.c_int32),
+        ("reserved", C.c_int32),
+        ("req_offsets", C.c_void_p),
+        ("seg_kind", C.c_void_p),
+        ("timestamps", C.c_void_p),
+        ("ranges", C.c_void_p),
+    ]
+
+
 STRUCTS = {
     "rk_batch": rk_batch,
     "rk_mask_params": rk_mask_params,
@@ -174,6 +199,8 @@ STRUCTS = {
     "rk_plan_totals": rk_plan_totals,
     "rk_attn_args": rk_attn_args,
     "rk_attn_bwd_args": rk_attn_bwd_args,
+    "rk_host_layout": rk_host_layout,
+    "rk_layout_out": rk_layout_out,
 }
 
 # (name, restype, argtypes) of every exported entry point
@@ -195,6 +222,14 @@ FUNCTIONS = [
     ("rk_attn_bwd_workspace_size", C.c_int, [C.c_void_p, C.POINTER(rk_attn_bwd_args),
                                              C.POINTER(C.c_size_t)]),
     ("rk_masked_attn_bwd", C.c_int, [C.c_void_p, C.POINTER(rk_attn_bwd_args), C.c_void_p]),
+    ("rk_compress_layout", C.c_int, [C.POINTER(rk_host_layout), C.c_int32, C.c_int32,
+                                     C.POINTER(rk_layout_out)]),
+    ("rk_pruned_history_length", C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                           C.POINTER(C.c_int32)]),
+    ("rk_prune_layout", C.c_int, [C.POINTER(rk_host_layout), C.c_void_p, C.c_int32, C.c_int32,
+                                  C.c_int32, C.POINTER(rk_layout_out)]),
+    ("rk_gather_sum", C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int64,
+                                C.c_void_p, C.c_int64, C.c_int32, C.c_int, C.c_void_p]),
 ]
 
 _lib = None

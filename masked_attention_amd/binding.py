@@ -330,3 +330,98 @@ def rk_masked_attn_bwd(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Te
     check(lib().rk_masked_attn_bwd(plan.handle, C.byref(a), _stream(stream)), "rk_masked_attn_bwd")
     dq._rk_workspace = workspace  # type: ignore[attr-defined]
     return dq, dk, dv
+
+
+# ---- LazFormer pre-passes -------------------------------------------------
+
+class Layout:
+    """Host copy of a packed layout (numpy arrays) as passed to and returned
+    by the layout functions; `ranges` [T, 2] describes each token as input
+    rows [b, e) of the layout it came from (None for an original layout)."""
+
+    def __init__(self, req_offsets, seg_kind, timestamps, ranges=None):
+        self.req_offsets = np.ascontiguousarray(req_offsets, dtype=np.int32)
+        self.seg_kind = np.ascontiguousarray(seg_kind, dtype=np.uint8)
+        self.timestamps = np.ascontiguousarray(timestamps, dtype=np.int64)
+        self.ranges = ranges
+        self.R = int(self.req_offsets.shape[0] - 1)
+        self.T = int(self.req_offsets[-1]) if self.R >= 0 else 0
+
+    @classmethod
+    def from_workload(cls, wl) -> "Layout":
+        return cls(wl.req_offsets, wl.seg_kind, wl.timestamps)
+
+    def c(self) -> _rk.rk_host_layout:
+        return sized(_rk.rk_host_layout, num_requests=self.R, total_tokens=self.T,
+                     req_offsets=self.req_offsets.ctypes.data,
+                     seg_kind=self.seg_kind.ctypes.data if self.T else None,
+                     timestamps=self.timestamps.ctypes.data if self.T else None)
+
+    def history_lengths(self) -> np.ndarray:
+        """HISTORY tokens of each request."""
+        idx = np.repeat(np.arange(self.R), np.diff(self.req_offsets))
+        return np.bincount(idx[self.seg_kind == _rk.RK_SEG_HISTORY],
+                           minlength=self.R).astype(np.int32)
+
+
+def _layout_call(fn, lay: Layout, *args) -> Layout:
+    inc = lay.c()
+    out = sized(_rk.rk_layout_out, capacity=0)
+    offs = np.zeros(lay.R + 1, np.int32)
+    out.req_offsets = offs.ctypes.data
+    st = fn(C.byref(inc), *args, C.byref(out))
+    if st == _rk.RK_ERR_WORKSPACE_TOO_SMALL:
+        n = int(out.total_tokens)
+        kinds = np.zeros(n, np.uint8)
+        times = np.zeros(n, np.int64)
+        ranges = np.zeros((n, 2), np.int32)
+        out = sized(_rk.rk_layout_out, capacity=n, req_offsets=offs.ctypes.data,
+                    seg_kind=kinds.ctypes.data, timestamps=times.ctypes.data,
+                    ranges=ranges.ctypes.data)
+        st = fn(C.byref(inc), *args, C.byref(out))
+    else:
+        kinds, times, ranges = (np.zeros(0, np.uint8), np.zeros(0, np.int64),
+                                np.zeros((0, 2), np.int32))
+    check(st, fn.__name__)
+    return Layout(offs, kinds, times, ranges)
+
+
+def rk_compress_layout(lay: Layout, *, keep: int, group: int) -> Layout:
+    """LazFormer group-sum compression layout (eq. 16-18)."""
+    return _layout_call(lib().rk_compress_layout, lay, int(keep), int(group))
+
+
+def rk_pruned_history_length(l_tilde: int, n_min: int, layer: int, num_layers: int) -> int:
+    n = C.c_int32()
+    check(lib().rk_pruned_history_length(int(l_tilde), int(n_min), int(layer), int(num_layers),
+                                         C.byref(n)), "rk_pruned_history_length")
+    return int(n.value)
+
+
+def rk_prune_layout(lay: Layout, *, l_tilde, n_min: int, layer: int, num_layers: int) -> Layout:
+    """Layer input layout after pruning to the last N^l history tokens (eq. 22)."""
+    lt = np.ascontiguousarray(l_tilde, dtype=np.int32)
+    return _layout_call(lib().rk_prune_layout, lay, C.c_void_p(lt.ctypes.data), int(n_min),
+                        int(layer), int(num_layers))
+
+
+def rk_gather_sum(ranges: torch.Tensor, x: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                  stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """y[i] = sum of rows ranges[i, 0] .. ranges[i, 1] - 1 of x (rows = first
+    dimension; the rest of each row contiguous).  ranges: int32 [n, 2] on the
+    device."""
+    if ranges.dtype != torch.int32 or ranges.dim() != 2 or not ranges.is_contiguous():
+        raise ValueError("ranges must be a contiguous int32 [n, 2] tensor")
+    n_out = ranges.shape[0]
+    width = int(np.prod(x.shape[1:])) if x.dim() > 1 else 1
+    x2 = x.reshape(x.shape[0], width) if x.dim() != 2 else x
+    if x2.dim() == 2 and x2.shape[0] and x2.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    if out is None:
+        out = torch.empty((n_out,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
+    y2 = out.reshape(n_out, width)
+    check(lib().rk_gather_sum(C.c_void_p(ranges.data_ptr()), n_out, x2.shape[0],
+                              C.c_void_p(x2.data_ptr()), x2.stride(0) if x2.shape[0] else width,
+                              C.c_void_p(y2.data_ptr()), y2.stride(0) if n_out else width, width,
+                              _dtype_code(x), _stream(stream)), "rk_gather_sum")
+    return out

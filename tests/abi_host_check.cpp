@@ -189,6 +189,68 @@ static void check_attention_without_plan() {
   EXPECT(rk_attn_bwd_workspace_size(nullptr, &g, &n) == RK_ERR_INVALID_ARG);
 }
 
+static void check_layouts() {
+  // two requests: PROFILE x1, HISTORY x5, CANDIDATE x2 | HISTORY x3
+  std::vector<int32_t> offs = {0, 8, 11};
+  std::vector<uint8_t> kind = {0, 1, 1, 1, 1, 1, 3, 3, 1, 1, 1};
+  std::vector<int64_t> ts = {5, 10, 20, 30, 40, 50, 60, 60, 1, 2, 3};
+  rk_host_layout in;
+  std::memset(&in, 0, sizeof(in));
+  in.struct_size = sizeof(in);
+  in.num_requests = 2;
+  in.total_tokens = 11;
+  in.req_offsets = offs.data();
+  in.seg_kind = kind.data();
+  in.timestamps = ts.data();
+  std::vector<int32_t> o2(3);
+  rk_layout_out out;
+  std::memset(&out, 0, sizeof(out));
+  out.struct_size = sizeof(out);
+  out.req_offsets = o2.data();
+  // size query, then the call with exactly that capacity
+  EXPECT(rk_compress_layout(&in, 2, 2, &out) == RK_ERR_WORKSPACE_TOO_SMALL);
+  const int32_t n = out.total_tokens;
+  EXPECT(n == 10);  // request 0: 1 + 2 groups + 2 kept + 2; request 1: 1 group + 2 kept
+  std::vector<uint8_t> k2(n);
+  std::vector<int64_t> t2(n);
+  std::vector<int32_t> r2(2 * n);
+  out.capacity = n;
+  out.seg_kind = k2.data();
+  out.timestamps = t2.data();
+  out.ranges = r2.data();
+  EXPECT(rk_compress_layout(&in, 2, 2, &out) == RK_OK);
+  EXPECT(o2[1] == 7 && o2[2] == 10);
+  EXPECT(r2[2] == 1 && r2[3] == 2 && r2[4] == 2 && r2[5] == 4);  // short group is the oldest
+  EXPECT(t2[2] == 30);                                           // newest member's time
+  std::vector<int32_t> lt = {5, 3};
+  EXPECT(rk_prune_layout(&in, lt.data(), 1, 2, 2, &out) == RK_OK);
+  EXPECT(out.total_tokens == 5);  // 1 + 1 + 2 | 1
+  EXPECT(rk_prune_layout(&in, nullptr, 1, 2, 2, &out) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_prune_layout(&in, lt.data(), 1, 3, 2, &out) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_compress_layout(&in, -1, 2, &out) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_compress_layout(&in, 1, 0, &out) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_compress_layout(nullptr, 1, 1, &out) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_compress_layout(&in, 1, 1, nullptr) == RK_ERR_INVALID_ARG);
+  ts[3] = 1;  // history out of time order
+  EXPECT(rk_compress_layout(&in, 1, 1, &out) == RK_ERR_UNSORTED_TIME);
+  ts[3] = 30;
+  kind[2] = 0;  // PROFILE after HISTORY
+  EXPECT(rk_compress_layout(&in, 1, 1, &out) == RK_ERR_SEGMENT_ORDER);
+  kind[2] = 9;  // not a segment kind
+  EXPECT(rk_compress_layout(&in, 1, 1, &out) == RK_ERR_SEGMENT_ORDER);
+  kind[2] = 1;
+  offs[2] = 12;  // last offset != total_tokens
+  EXPECT(rk_compress_layout(&in, 1, 1, &out) == RK_ERR_INVALID_ARG);
+  offs[2] = 11;
+  int32_t m = 0;
+  EXPECT(rk_pruned_history_length(1152, 128, 3, 5, &m) == RK_OK && m == 640);
+  EXPECT(rk_pruned_history_length(1152, 128, 0, 5, &m) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_pruned_history_length(1152, 128, 1, 5, nullptr) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_gather_sum(nullptr, 1, 1, nullptr, 1, nullptr, 1, 1, (rk_dtype)5, nullptr) ==
+         RK_ERR_INVALID_ARG);
+  EXPECT(rk_gather_sum(nullptr, 0, 0, nullptr, 0, nullptr, 0, 0, RK_F32, nullptr) == RK_OK);
+}
+
 int main(int argc, char** argv) {
   if (argc > 1 && std::strcmp(argv[1], "--self-test") == 0) {
     // proves the instrumentation is live: AddressSanitizer must stop here
@@ -202,6 +264,7 @@ int main(int argc, char** argv) {
   check_mask_plan();
   check_time_rope();
   check_attention_without_plan();
+  check_layouts();
   if (failures) {
     std::fprintf(stderr, "%d check(s) failed\n", failures);
     return 1;

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "masked_attention_amd")
 BUILD = os.path.join(PKG, "_build")
 DEVICE_OBJS = ["plan.hip.o", "rope.hip.o", "attn_ref.hip.o", "attn_mfma.hip.o",
-               "attn_combine.hip.o", "attn_bwd_ref.hip.o", "attn_bwd_mfma.hip.o"]
+               "attn_combine.hip.o", "attn_bwd_ref.hip.o", "attn_bwd_mfma.hip.o",
+               "gather_sum.hip.o"]
 HIPCC = "/opt/rocm/bin/hipcc"
 
 
@@ -33,20 +34,24 @@ def test_abi_host_paths_under_asan_ubsan(tmp_path):
     objs = [os.path.join(BUILD, o) for o in DEVICE_OBJS]
     if not all(os.path.exists(o) for o in objs):
         pytest.skip("device objects not built (run __graft_entry__.build() first)")
-    api_o = str(tmp_path / "api_asan.o")
-    # host pass instrumented, device pass unchanged
-    _run([HIPCC, "-O1", "-g", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"),
-          "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
-          "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
-          "-x", "hip", "-c", os.path.join(PKG, "csrc", "api.cpp"), "-o", api_o])
+    host_objs = []
+    for src in ("api.cpp", "layout.cpp"):
+        o = str(tmp_path / (src + ".asan.o"))
+        # host pass instrumented, device pass unchanged
+        _run([HIPCC, "-O1", "-g", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"),
+              "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+              "-packed-fp32-ops", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+              "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host",
+              "-fno-omit-frame-pointer", "-x", "hip", "-c", os.path.join(PKG, "csrc", src),
+              "-o", o])
+        host_objs.append(o)
     clang = "/opt/rocm/llvm/bin/clang++"
     # directory of the shared sanitizer runtimes that -shared-libsan links to
     rt = os.path.dirname(subprocess.run([clang, "--print-file-name=libclang_rt.asan-x86_64.so"],
                                         capture_output=True, text=True).stdout.strip())
     rpath = [f"-Wl,-rpath,{rt}", "-Wl,-rpath,/opt/rocm/lib", f"-Wl,-rpath,{tmp_path}"]
     lib = str(tmp_path / "librk_asan.so")
-    _run([clang, "-shared", "-o", lib, api_o, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+    _run([clang, "-shared", "-o", lib, *host_objs, *objs, "-L/opt/rocm/lib", "-lamdhip64",
           "-fsanitize=address,undefined", "-shared-libsan", *rpath])
     exe = str(tmp_path / "abi_host_check")
     _run([clang, "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined",
