@@ -53,6 +53,10 @@ def _parse():
                     help="time the backward step instead: the forward runs once (untimed) for "
                          "O and LSE; each step plans with the key-major tables and runs "
                          "rk_masked_attn_bwd (Q/K rotation, dQ kernel, dK/dV kernel)")
+    ap.add_argument("--lazformer", action="store_true",
+                    help="time LazFormer's attention stack instead: group-sum compression of "
+                         "Q/K/V (2048 -> 1152), then per layer the pruned input gathered, "
+                         "planned (window = global tail = 128) and attended, 5 layers")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter scaling)")
     return ap.parse_args()
@@ -248,6 +252,115 @@ def backward_main(args) -> int:
     return 0
 
 
+def lazformer_main(args) -> int:
+    """One JSON line for LazFormer's attention stack (section 2.3): per
+    step, compression of Q, K, V (rk_gather_sum over rk_compress_layout's
+    ranges) and, for each of the 5 layers, the pruned layer input gathered,
+    planned and attended.  Layouts are host work done once before timing."""
+    import numpy as np
+    import torch
+
+    import masked_attention_amd as rk
+    from rk_workloads import CANDIDATE, HISTORY, NOW, history_span, make_custom
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    R, L_hist, n_cand, H, d = 64, 2048, 32, 4, 64
+    keep, group, W, G, n_min, n_layers = 1024, 8, 128, 128, 128, 5
+    rng = np.random.default_rng(1006)
+    reqs = [[(HISTORY, history_span(rng, L_hist, NOW - 60)),
+             (CANDIDATE, np.full(n_cand, NOW, np.int64))] for _ in range(R)]
+    wl = make_custom(reqs, heads=H, d_head=d, dtype="bf16", seed=1006,
+                     name=f"lazformer-{R}x({L_hist}+{n_cand})-keep{keep}-g{group}-W{W}-G{G}-5layers")
+    rope = dict(phi_min=wl.phi_min, dt_max=wl.dt_max, base=wl.base)
+    t0 = time.perf_counter()
+    lay = rk.Layout.from_workload(wl)
+    comp = rk.rk_compress_layout(lay, keep=keep, group=group)
+    lt = comp.history_lengths()
+    layers = [rk.rk_prune_layout(comp, l_tilde=lt, n_min=n_min, layer=l, num_layers=n_layers)
+              for l in range(1, n_layers + 1)]
+    host_ms = (time.perf_counter() - t0) * 1e3
+    qkv = [torch.from_numpy(a).to(dev).to(torch.bfloat16) for a in (wl.q, wl.k, wl.v)]
+    rg_c = torch.from_numpy(comp.ranges.copy()).to(dev)
+    comp_t = [torch.empty((comp.T, H, d), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    per = []
+    for lay_l in layers:
+        anchors = np.full(lay_l.R, NOW, np.int64)
+        batch = rk.Batch(lay_l.req_offsets, lay_l.seg_kind, lay_l.timestamps, anchors, device=dev)
+        ws = torch.empty(rk.rk_plan_workspace_size(batch, H), dtype=torch.uint8, device=dev)
+        per.append(dict(batch=batch, ws=ws, rg=torch.from_numpy(lay_l.ranges.copy()).to(dev),
+                        t=[torch.empty((lay_l.T, H, d), dtype=torch.bfloat16, device=dev)
+                           for _ in range(3)],
+                        o=torch.empty((lay_l.T, H, d), dtype=torch.bfloat16, device=dev)))
+    # visible pairs of every layer (from the plans)
+    pairs = []
+    for pl in per:
+        p = rk.Plan(pl["batch"], window=W, global_tail=G, num_heads=H, workspace=pl["ws"])
+        pairs.append(p.stats()["visible_pairs"])
+        p.close()
+    stream = torch.cuda.current_stream()
+    plans = []
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        for src, dst in zip(qkv, comp_t):
+            rk.rk_gather_sum(rg_c, src, out=dst)
+        if ev: ev[1].record(stream)
+        for pl in per:
+            for src, dst in zip(comp_t, pl["t"]):
+                rk.rk_gather_sum(pl["rg"], src, out=dst)
+            p = rk.Plan(pl["batch"], window=W, global_tail=G, num_heads=H, workspace=pl["ws"])
+            rk.rk_masked_attn_fwd(p, *pl["t"], out=pl["o"], rope=rope)
+            plans.append(p)
+        if ev: ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for p in plans:
+        p.close()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    comp_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    layers_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    flops = 4.0 * d * H * float(sum(pairs))
+    comp_bytes = 3 * (wl.total_tokens + comp.T) * H * d * 2 + comp.T * 8
+    out = {
+        "metric": "LazFormer attention stack: effective TFLOP/s over the visible pairs of all "
+                  "layers",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generator; history spans 1 yr)",
+        "config": {"workload": wl.name, "requests": R, "tokens": wl.total_tokens,
+                   "compressed_tokens": comp.T, "layer_tokens": [x.T for x in layers],
+                   "heads": H, "d_head": d, "visible_pairs_per_head": pairs},
+        "stage_ms": {"compress": round(comp_ms, 4), "layers": round(layers_ms, 4),
+                     "host_layouts_once": round(host_ms, 2)},
+        "stage_hbm_gbs": {"compress": round(comp_bytes / (comp_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "kernel": "gather_sum_kernel (compression of Q, K, V)",
+                     "achieved": round(comp_bytes / (comp_ms * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(comp_bytes / (comp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": None, "alg_bytes": comp_bytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -258,6 +371,8 @@ def main() -> int:
         return 2
     if args.backward:
         return backward_main(args)
+    if args.lazformer:
+        return lazformer_main(args)
 
     import numpy as np
     import torch
