@@ -4,6 +4,7 @@ from .masked_attention import (  # noqa: F401
     CANDIDATE, EMPTY, FULL, HISTORY, PARTIAL, PROFILE, REALTIME, TILE_K, TILE_Q,
     attention_backward, attention_backward_sampled, attention_forward, attention_rows,
     compressed_history_length, count_visible, group_sum_compress, masked_softmax_attention,
-    masked_softmax_attention_backward, prune_history, pruned_history_length, rope_frequencies,
+    masked_softmax_attention_backward, prune_history, pruned_history_length, qk_rmsnorm,
+    rope_frequencies,
     tile_plan, tile_plan_request, time_rope, time_rope_transpose, visibility, visible_rows,
 )

@@ -168,6 +168,15 @@ def time_rope(x: np.ndarray, t: np.ndarray, *, phi_min: float, dt_max: float,
     return out
 
 
+def qk_rmsnorm(x: np.ndarray, gamma: Optional[np.ndarray], eps: float) -> np.ndarray:
+    """QK Norm (TM20K section 2; SORT section 3.3.2: RMSNorm on Q and K before
+    the scores): every [d] row x becomes x / sqrt(mean(x^2) + eps) * gamma
+    (gamma None = 1).  float64."""
+    x = np.asarray(x, np.float64)
+    y = x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    return y if gamma is None else y * np.asarray(gamma, np.float64)
+
+
 # ---------------------------------------------------------------------------
 # Masked softmax attention (plain definition)
 # ---------------------------------------------------------------------------
@@ -198,8 +207,12 @@ def attention_forward(req_offsets: np.ndarray, seg_kind: np.ndarray, timestamps:
                       static_bidirectional: bool, rope: Optional[Dict[str, float]] = None,
                       rope_times: Optional[np.ndarray] = None, scale: Optional[float] = None,
                       heads: Optional[np.ndarray] = None, requests: Optional[np.ndarray] = None,
-                      row_block: int = 1024, global_tail: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+                      row_block: int = 1024, global_tail: int = 0,
+                      qk_norm: Optional[Dict] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Masked attention forward over a packed batch, in float64.
+
+    qk_norm: None or dict(eps=..., gamma_q=..., gamma_k=...): QK Norm of q and
+    k (qk_rmsnorm) before the rotation.
 
     q, k, v: [T, H, d] (any float dtype; upcast to float64).  With `rope`
     (keys phi_min, dt_max, base) Q and K are rotated by time RoPE using
@@ -213,6 +226,9 @@ def attention_forward(req_offsets: np.ndarray, seg_kind: np.ndarray, timestamps:
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
+    if qk_norm is not None:
+        q = qk_rmsnorm(q, qk_norm.get("gamma_q"), qk_norm["eps"])
+        k = qk_rmsnorm(k, qk_norm.get("gamma_k"), qk_norm["eps"])
     o = np.zeros((T, H, d), np.float64)
     lse = np.full((H, T), -np.inf)
     heads = np.arange(H) if heads is None else np.asarray(heads)
