@@ -49,6 +49,9 @@ def _parse():
                     help="serving step: the history keys are rotated once before timing; each "
                          "step plans the candidates' query tiles only, rotates the candidate "
                          "keys into the key cache and runs the attention for those tiles")
+    ap.add_argument("--qk-norm", action="store_true",
+                    help="forward with QK Norm (RMSNorm of Q and K rows before the rotation, "
+                         "gains 1): K normalised in its rotation pass, Q while staged")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward step instead: the forward runs once (untimed) for "
                          "O and LSE; each step plans with the key-major tables and runs "
@@ -406,7 +409,10 @@ def main() -> int:
         cand = batch.seg_kind == _rk.RK_SEG_CANDIDATE
         pairs = int(((hi - lo).clamp(min=0) + self_bit.to(torch.int64))[cand].sum().item())
         # history (and profile / real-time) keys rotated once, outside the timed steps
-        rk.rk_time_rope(batch, k, out=krot, **rope)
+        if args.qk_norm:
+            rk.rk_qk_norm_rope(batch, k, eps=1e-6, rope=rope, out=krot)
+        else:
+            rk.rk_time_rope(batch, k, out=krot, **rope)
     flops = 4.0 * d * H * pairs
 
     # raw C arguments, built once
@@ -417,6 +423,7 @@ def main() -> int:
     # the step's rotation: every key, or only the candidate keys into the cache
     rp_step = rk.binding.rope_params(
         **rope, kinds=(1 << _rk.RK_SEG_CANDIDATE) if args.candidates_only else 0)
+    nq = rk.binding.qk_norm_params(1e-6) if args.qk_norm else None
     stream = torch.cuda.current_stream()
     sp = C.c_void_p(stream.cuda_stream)
     dcode = _rk.RK_BF16 if wl.dtype == "bf16" else _rk.RK_F32
@@ -426,6 +433,8 @@ def main() -> int:
                      v_stride_tok=H * d, v_stride_head=d, o_stride_tok=H * d, o_stride_head=d,
                      scale=0.0)
     attn.rope = C.cast(C.pointer(rp), C.c_void_p)
+    if nq is not None:
+        attn.qk_norm = C.cast(C.pointer(nq), C.c_void_p)
     attn_ws = None
     if args.candidates_only:
         # partial results of split items live in the attention workspace
@@ -449,9 +458,15 @@ def main() -> int:
         _rk.check(lib.rk_mask_plan(C.byref(batch.c), C.byref(mp), H, C.c_void_p(ws.data_ptr()),
                                    C.c_size_t(ws.numel()), C.byref(h), sp), "rk_mask_plan")
         if ev: ev[1].record(stream)
-        _rk.check(lib.rk_time_rope(C.byref(batch.c), C.byref(rp_step), C.c_void_p(k.data_ptr()),
-                                   C.c_void_p(krot.data_ptr()), dcode, H, d, H * d, d, H * d, d,
-                                   sp), "rk_time_rope")
+        if nq is not None:
+            _rk.check(lib.rk_qk_norm_rope(C.byref(batch.c), C.byref(rp_step), C.c_float(1e-6),
+                                          None, C.c_void_p(k.data_ptr()),
+                                          C.c_void_p(krot.data_ptr()), dcode, H, d, H * d, d,
+                                          H * d, d, sp), "rk_qk_norm_rope")
+        else:
+            _rk.check(lib.rk_time_rope(C.byref(batch.c), C.byref(rp_step),
+                                       C.c_void_p(k.data_ptr()), C.c_void_p(krot.data_ptr()),
+                                       dcode, H, d, H * d, d, H * d, d, sp), "rk_time_rope")
         if ev: ev[2].record(stream)
         _rk.check(lib.rk_masked_attn_fwd(h, C.byref(attn), sp), "rk_masked_attn_fwd")
         if ev: ev[3].record(stream)
@@ -492,7 +507,8 @@ def main() -> int:
     # kind + time read, row descriptor written, class + count per tile, CSR index + class
     plan_alg_bytes = T * 9 + T * 8 + nt * 5 + nnz_tiles * 5
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    wname = wl.name + (" candidates-only" if args.candidates_only else "")
+    wname = wl.name + (" candidates-only" if args.candidates_only else "") + (
+        " qk-norm" if args.qk_norm else "")
     traffic = _traffic_from_profile(wname)
     mfma_util = _mfma_util_from_profile(wname, attn_ms, achieved, flops)
     n_cand = wl.n_candidates

@@ -126,8 +126,9 @@ enum { RK_TILE_EMPTY = 0, RK_TILE_PARTIAL = 1, RK_TILE_FULL = 2 };
 
 /* rk_attn_args.flags */
 #define RK_ATTN_REFERENCE_KERNEL 0x1u /* force the plain (non-MFMA) kernel */
-#define RK_ATTN_K_PREROTATED 0x2u     /* with rope: K was already rotated by rk_time_rope
-                                         (same parameters and anchors); only Q is rotated */
+#define RK_ATTN_K_PREROTATED 0x2u     /* with rope and / or qk_norm: K was already
+                                         prepared by rk_time_rope or rk_qk_norm_rope (same
+                                         parameters and anchors); only Q is transformed */
 
 /*
  * A packed batch (CADET, "how to score hundreds of candidates": all tokens
@@ -186,6 +187,19 @@ typedef struct rk_rope_params {
   double dt_max;  /* > 0 */
   double base;    /* > 0 */
 } rk_rope_params;
+
+/* QK Norm (TM20K section 2: QK Norm after the query / key projections keeps
+ * extreme scores in check; SORT section 3.3.2: RMSNorm on Q and K before the
+ * scores): every [d_head] row of Q and K becomes
+ *   x / sqrt(mean(x^2) + eps) * gamma,
+ * applied before time RoPE.  One gain vector for Q and one for K, shared by
+ * every head (the pages give no shape); NULL gains are 1. */
+typedef struct rk_qk_norm_params {
+  uint32_t struct_size;
+  float eps;             /* > 0 */
+  const float* gamma_q;  /* device fp32 [d_head] or NULL */
+  const float* gamma_k;  /* device fp32 [d_head] or NULL */
+} rk_qk_norm_params;
 
 typedef struct rk_plan rk_plan;
 
@@ -259,6 +273,9 @@ typedef struct rk_plan_totals {
  *               for a cache of rotated history keys).
  *   workspace : device memory of at least rk_attn_workspace_size bytes,
  *               256-byte aligned (may be NULL when that size is 0).
+ *   qk_norm   : NULL, or QK Norm applied to Q and K before time RoPE (Q
+ *               while it is staged, K by the pass into the workspace unless
+ *               RK_ATTN_K_PREROTATED); d_head in {32, 64, 128}.
  * O must not overlap Q, K, V or the workspace.
  */
 typedef struct rk_attn_args {
@@ -282,6 +299,7 @@ typedef struct rk_attn_args {
   const rk_rope_params* rope;
   void* workspace;
   size_t workspace_bytes;
+  const rk_qk_norm_params* qk_norm;
 } rk_attn_args;
 
 /* Name of a status code (static string). */
@@ -344,6 +362,21 @@ rk_status rk_time_rope(const rk_batch* b, const rk_rope_params* r, const void* x
                        rk_dtype dtype, int32_t num_heads, int32_t d_head,
                        int64_t in_stride_tok, int64_t in_stride_head,
                        int64_t out_stride_tok, int64_t out_stride_head, void* stream);
+
+/*
+ * QK Norm then time RoPE in one pass (the K side of a forward with qk_norm,
+ * e.g. to fill a cache of prepared keys for RK_ATTN_K_PREROTATED): every row
+ * x of x_in [total_tokens, num_heads, d_head] becomes
+ * rotate(x / sqrt(mean(x^2) + eps) * gamma) in x_out; r may be NULL (norm
+ * only).  gamma: device fp32 [d_head] or NULL (gain 1).  Strides and kinds as
+ * in rk_time_rope.  Errors: RK_ERR_INVALID_ARG, RK_ERR_UNSUPPORTED (d_head not
+ * in {32, 64, 128}), RK_ERR_HIP.
+ */
+rk_status rk_qk_norm_rope(const rk_batch* b, const rk_rope_params* r, float eps,
+                          const float* gamma, const void* x_in, void* x_out, rk_dtype dtype,
+                          int32_t num_heads, int32_t d_head, int64_t in_stride_tok,
+                          int64_t in_stride_head, int64_t out_stride_tok,
+                          int64_t out_stride_head, void* stream);
 
 /* Workspace bytes rk_masked_attn_fwd needs for `a` on plan `p` (host only):
  * the rotated K when the call rotates K ([total_tokens][num_heads][d_head] of
@@ -413,6 +446,8 @@ typedef struct rk_attn_bwd_args {
   const rk_rope_params* rope;
   void* workspace;
   size_t workspace_bytes;
+  const rk_qk_norm_params* qk_norm; /* must be NULL: the backward through QK Norm is not built
+                                       (RK_ERR_UNSUPPORTED) */
 } rk_attn_bwd_args;
 
 /* Workspace bytes rk_masked_attn_bwd needs for `a` on plan `p` (host only):

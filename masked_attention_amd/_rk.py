@@ -68,6 +68,15 @@ class rk_rope_params(C.Structure):
     ]
 
 
+class rk_qk_norm_params(C.Structure):
+    _fields_ = [
+        ("struct_size", C.c_uint32),
+        ("eps", C.c_float),
+        ("gamma_q", C.c_void_p),
+        ("gamma_k", C.c_void_p),
+    ]
+
+
 class rk_plan_info(C.Structure):
     _fields_ = [
         ("struct_size", C.c_uint32),
@@ -130,6 +139,7 @@ class rk_attn_args(C.Structure):
         ("rope", C.c_void_p),
         ("workspace", C.c_void_p),
         ("workspace_bytes", C.c_size_t),
+        ("qk_norm", C.c_void_p),
     ]
 
 
@@ -163,6 +173,7 @@ class rk_attn_bwd_args(C.Structure):
         ("rope", C.c_void_p),
         ("workspace", C.c_void_p),
         ("workspace_bytes", C.c_size_t),
+        ("qk_norm", C.c_void_p),
     ]
 
 
@@ -195,6 +206,7 @@ STRUCTS = {
     "rk_batch": rk_batch,
     "rk_mask_params": rk_mask_params,
     "rk_rope_params": rk_rope_params,
+    "rk_qk_norm_params": rk_qk_norm_params,
     "rk_plan_info": rk_plan_info,
     "rk_plan_totals": rk_plan_totals,
     "rk_attn_args": rk_attn_args,
@@ -216,6 +228,10 @@ FUNCTIONS = [
     ("rk_time_rope", C.c_int, [C.POINTER(rk_batch), C.POINTER(rk_rope_params), C.c_void_p,
                                C.c_void_p, C.c_int, C.c_int32, C.c_int32, C.c_int64, C.c_int64,
                                C.c_int64, C.c_int64, C.c_void_p]),
+    ("rk_qk_norm_rope", C.c_int, [C.POINTER(rk_batch), C.POINTER(rk_rope_params), C.c_float,
+                                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int32,
+                                  C.c_int32, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                                  C.c_void_p]),
     ("rk_attn_workspace_size", C.c_int, [C.c_void_p, C.POINTER(rk_attn_args),
                                          C.POINTER(C.c_size_t)]),
     ("rk_masked_attn_fwd", C.c_int, [C.c_void_p, C.POINTER(rk_attn_args), C.c_void_p]),

@@ -213,8 +213,41 @@ def rk_time_rope(batch: Batch, x: torch.Tensor, *, phi_min: float, dt_max: float
     return out
 
 
+def qk_norm_params(eps: float, gamma_q: Optional[torch.Tensor] = None,
+                   gamma_k: Optional[torch.Tensor] = None) -> _rk.rk_qk_norm_params:
+    """QK Norm parameters; gains are fp32 device tensors [d_head] (kept alive by
+    the caller) or None."""
+    for g in (gamma_q, gamma_k):
+        if g is not None and (g.dtype != torch.float32 or not g.is_contiguous()):
+            raise ValueError("QK Norm gains must be contiguous float32 tensors")
+    return sized(_rk.rk_qk_norm_params, eps=float(eps),
+                 gamma_q=gamma_q.data_ptr() if gamma_q is not None else None,
+                 gamma_k=gamma_k.data_ptr() if gamma_k is not None else None)
+
+
+def rk_qk_norm_rope(batch: Batch, x: torch.Tensor, *, eps: float,
+                    gamma: Optional[torch.Tensor] = None, rope: Optional[dict] = None,
+                    out: Optional[torch.Tensor] = None, kinds=None,
+                    stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """QK Norm (then time RoPE when rope is given) of x [T, H, d] into out."""
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("x must be [T, H, d] with d contiguous")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    mask = 0 if kinds is None else sum(1 << int(k) for k in set(kinds))
+    rp = rope_params(**rope, kinds=mask) if rope is not None else None
+    if gamma is not None and (gamma.dtype != torch.float32 or not gamma.is_contiguous()):
+        raise ValueError("gamma must be a contiguous float32 tensor")
+    check(lib().rk_qk_norm_rope(C.byref(batch.c), C.byref(rp) if rp is not None else None,
+                                float(eps), C.c_void_p(gamma.data_ptr() if gamma is not None else 0),
+                                C.c_void_p(x.data_ptr()), C.c_void_p(out.data_ptr()),
+                                _dtype_code(x), x.shape[1], x.shape[2], x.stride(0), x.stride(1),
+                                out.stride(0), out.stride(1), _stream(stream)), "rk_qk_norm_rope")
+    return out
+
+
 def _attn_args(plan: Plan, q, k, v, o, lse, scale, rope, reference, workspace,
-               k_prerotated=False):
+               k_prerotated=False, qk_norm=None):
     for t in (q, k, v, o):
         if t.dim() != 3 or t.stride(2) != 1:
             raise ValueError("q, k, v, o must be [T, H, d] with d contiguous")
@@ -231,6 +264,8 @@ def _attn_args(plan: Plan, q, k, v, o, lse, scale, rope, reference, workspace,
               scale=float(scale))
     if rope is not None:
         a.rope = C.cast(C.pointer(rope), C.c_void_p)
+    if qk_norm is not None:
+        a.qk_norm = C.cast(C.pointer(qk_norm), C.c_void_p)
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -251,9 +286,12 @@ def rk_masked_attn_fwd(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Te
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                        want_lse: bool = False, scale: float = 0.0, rope: Optional[dict] = None,
                        reference: bool = False, workspace: Optional[torch.Tensor] = None,
-                       k_prerotated: bool = False,
+                       k_prerotated: bool = False, qk_norm: Optional[dict] = None,
                        stream: Optional[torch.cuda.Stream] = None):
     """Masked attention forward over `plan`.  Returns (o, lse or None).
+
+    qk_norm: None, or dict(eps=..., gamma_q=tensor or None, gamma_k=tensor or
+    None): QK Norm of Q and K before the rotation.
 
     rope: None, or dict(phi_min=..., dt_max=..., base=...) to rotate Q and K
     by time RoPE with the plan's timestamps and anchors.  k_prerotated:
@@ -264,7 +302,8 @@ def rk_masked_attn_fwd(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Te
     if lse is None and want_lse:
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
     rp = rope_params(**rope) if rope is not None else None
-    a = _attn_args(plan, q, k, v, out, lse, scale, rp, reference, workspace, k_prerotated)
+    nq = qk_norm_params(**qk_norm) if qk_norm is not None else None
+    a = _attn_args(plan, q, k, v, out, lse, scale, rp, reference, workspace, k_prerotated, nq)
     n = C.c_size_t()
     check(lib().rk_attn_workspace_size(plan.handle, C.byref(a), C.byref(n)), "rk_attn_workspace_size")
     if n.value and workspace is None:

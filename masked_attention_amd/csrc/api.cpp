@@ -217,6 +217,13 @@ rk_status check_rope(const rk_rope_params* r) {
   return RK_OK;
 }
 
+rk_status check_norm(const rk_qk_norm_params* n, int d) {
+  if (!n || n->struct_size < sizeof(rk_qk_norm_params)) return RK_ERR_INVALID_ARG;
+  if (!(std::isfinite(n->eps) && n->eps > 0.f)) return RK_ERR_INVALID_ARG;
+  if (d != 32 && d != 64 && d != 128) return RK_ERR_UNSUPPORTED;
+  return RK_OK;
+}
+
 rk::RopeTab make_tab(const rk_rope_params* r, int d) {
   rk::RopeTab t;
   std::memset(&t, 0, sizeof(t));
@@ -477,6 +484,33 @@ rk_status rk_time_rope(const rk_batch* b, const rk_rope_params* r, const void* x
   return e == hipSuccess ? RK_OK : RK_ERR_HIP;
 }
 
+rk_status rk_qk_norm_rope(const rk_batch* b, const rk_rope_params* r, float eps,
+                          const float* gamma, const void* x_in, void* x_out, rk_dtype dtype,
+                          int32_t num_heads, int32_t d_head, int64_t in_stride_tok,
+                          int64_t in_stride_head, int64_t out_stride_tok,
+                          int64_t out_stride_head, void* stream) {
+  rk_status st = check_batch(b);
+  if (st != RK_OK) return st;
+  if (r && (st = check_rope(r)) != RK_OK) return st;
+  if (!valid_dtype(dtype)) return RK_ERR_INVALID_ARG;
+  if (num_heads < 1 || !(std::isfinite(eps) && eps > 0.f)) return RK_ERR_INVALID_ARG;
+  if (d_head != 32 && d_head != 64 && d_head != 128) return RK_ERR_UNSUPPORTED;
+  if (in_stride_tok < 0 || in_stride_head < 0 || out_stride_tok < 0 || out_stride_head < 0)
+    return RK_ERR_INVALID_ARG;
+  if (b->total_tokens > 0 && (!x_in || !x_out)) return RK_ERR_INVALID_ARG;
+  if (x_in == x_out && (in_stride_tok != out_stride_tok || in_stride_head != out_stride_head))
+    return RK_ERR_INVALID_ARG;
+  rk::RopeTab tab;
+  std::memset(&tab, 0, sizeof(tab));  // no rope: rotation by zero
+  if (r) tab = make_tab(r, d_head);
+  hipError_t e = rk::launch_rope(b->num_requests, b->total_tokens, b->req_offsets_dev,
+                                 b->timestamps_dev, b->anchors_dev, b->seg_kind_dev,
+                                 r ? r->kinds : 0u, tab, x_in, x_out, dtype, num_heads, d_head,
+                                 in_stride_tok, in_stride_head, out_stride_tok, out_stride_head,
+                                 (hipStream_t)stream, true, eps, gamma);
+  return e == hipSuccess ? RK_OK : RK_ERR_HIP;
+}
+
 namespace {
 
 rk_status check_attn(const rk_plan* p, const rk_attn_args* a) {
@@ -485,7 +519,11 @@ rk_status check_attn(const rk_plan* p, const rk_attn_args* a) {
   if (a->num_heads != p->H) return RK_ERR_INVALID_ARG;
   if (a->d_head != 32 && a->d_head != 64 && a->d_head != 128) return RK_ERR_UNSUPPORTED;
   if (a->flags & ~(RK_ATTN_REFERENCE_KERNEL | RK_ATTN_K_PREROTATED)) return RK_ERR_INVALID_ARG;
-  if ((a->flags & RK_ATTN_K_PREROTATED) && !a->rope) return RK_ERR_INVALID_ARG;
+  if ((a->flags & RK_ATTN_K_PREROTATED) && !a->rope && !a->qk_norm) return RK_ERR_INVALID_ARG;
+  if (a->qk_norm) {
+    rk_status s = check_norm(a->qk_norm, a->d_head);
+    if (s != RK_OK) return s;
+  }
   if (p->T > 0 && (!a->q || !a->k || !a->v || !a->o)) return RK_ERR_INVALID_ARG;
   const int64_t st[8] = {a->q_stride_tok, a->q_stride_head, a->k_stride_tok, a->k_stride_head,
                          a->v_stride_tok, a->v_stride_head, a->o_stride_tok, a->o_stride_head};
@@ -514,13 +552,14 @@ bool mfma_aligned(const rk_attn_args* a, bool k_in_workspace) {
             st(a->v_stride_tok) && st(a->v_stride_head) && st(a->o_stride_tok) &&
             st(a->o_stride_head);
   if (!k_in_workspace) ok = ok && al(a->k) && st(a->k_stride_tok) && st(a->k_stride_head);
+  if (a->qk_norm && a->qk_norm->gamma_q) ok = ok && al(a->qk_norm->gamma_q);  // 16-byte loads
   return ok;
 }
 
 // Attention workspace: [rotated K, when the call rotates K][partial results
 // of split items, for plans with a work list].
 size_t attn_k_bytes(const rk_plan* p, const rk_attn_args* a) {
-  if (!a->rope || (a->flags & RK_ATTN_K_PREROTATED)) return 0;
+  if ((!a->rope && !a->qk_norm) || (a->flags & RK_ATTN_K_PREROTATED)) return 0;
   return align_up((size_t)p->T * (size_t)a->num_heads * (size_t)a->d_head * elem_size(a->dtype));
 }
 
@@ -552,7 +591,9 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
     if (a->workspace_bytes < need) return RK_ERR_WORKSPACE_TOO_SMALL;
   }
   const bool use_mfma = mfma_eligible(a);
-  const bool k_rotate = a->rope && !(a->flags & RK_ATTN_K_PREROTATED);
+  // K is prepared (normalised and / or rotated) by a pass into the
+  // workspace unless the caller did it
+  const bool k_rotate = (a->rope || a->qk_norm) && !(a->flags & RK_ATTN_K_PREROTATED);
   if (use_mfma && !mfma_aligned(a, k_rotate)) return RK_ERR_UNSUPPORTED;
 
   rk::AttnLaunch L;
@@ -577,9 +618,16 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
   L.ts = p->timestamps_dev;
   L.anchors = p->anchors_dev;
   hipStream_t s = (hipStream_t)stream;
-  if (a->rope) {
-    L.tab = make_tab(a->rope, a->d_head);
+  if (a->rope || a->qk_norm) {
+    // Q is transformed while staged: rotated (a zero table rotates by
+    // nothing) after the optional norm
+    if (a->rope) L.tab = make_tab(a->rope, a->d_head);
     L.rope_q = true;
+  }
+  if (a->qk_norm) {
+    L.norm_q = true;
+    L.eps = a->qk_norm->eps;
+    L.gamma_q = a->qk_norm->gamma_q;
   }
   if (attn_part_bytes(p, a))
     L.part = (float*)((unsigned char*)a->workspace + attn_k_bytes(p, a));
@@ -591,7 +639,9 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
                                    p->anchors_dev, p->seg_kind_dev, 0u, L.tab, a->k, a->workspace,
                                    a->dtype,
                                    a->num_heads, a->d_head, a->k_stride_tok, a->k_stride_head, hd,
-                                   a->d_head, s);
+                                   a->d_head, s, a->qk_norm != nullptr,
+                                   a->qk_norm ? a->qk_norm->eps : 0.f,
+                                   a->qk_norm ? a->qk_norm->gamma_k : nullptr);
     if (e != hipSuccess) return RK_ERR_HIP;
     L.k = a->workspace;
     L.k_st = hd;
@@ -624,6 +674,7 @@ rk_status check_bwd(const rk_plan* p, const rk_attn_bwd_args* a) {
   if (a->d_head != 32 && a->d_head != 64 && a->d_head != 128) return RK_ERR_UNSUPPORTED;
   if (a->flags & ~(RK_ATTN_REFERENCE_KERNEL | RK_ATTN_K_PREROTATED)) return RK_ERR_INVALID_ARG;
   if ((a->flags & RK_ATTN_K_PREROTATED) && !a->rope) return RK_ERR_INVALID_ARG;
+  if (a->qk_norm) return RK_ERR_UNSUPPORTED;  // the backward through QK Norm is not built
   if (p->T > 0 && (!a->q || !a->k || !a->v || !a->o || !a->d_o || !a->lse || !a->dq || !a->dk ||
                    !a->dv))
     return RK_ERR_INVALID_ARG;

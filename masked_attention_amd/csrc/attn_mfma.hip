@@ -132,16 +132,50 @@ __device__ __forceinline__ QRaw load_q_raw(const AttnLaunch& A, const int2* row_
   return r;
 }
 
-template <bool kRope>
+// With kNorm (QK Norm) the row is first scaled by 1 / sqrt(mean(x^2) + eps)
+// and the gain gamma[d] (NULL: 1); the two lane halves hold the two halves
+// of the row and meet through one lane ^ 32 exchange.
+template <bool kRope, bool kNorm>
 __device__ __forceinline__ void finish_q(bf16x8 (&qb)[4], const QRaw& raw, bool valid,
-                                         int64_t anchor, const RopeTab& tab, int hh, float qmul) {
+                                         int64_t anchor, const RopeTab& tab, int hh, float qmul,
+                                         float eps, const float* gamma) {
   const double dtd = (double)(raw.t - anchor);
+  float nscale[4][8];
+  if (kNorm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const unsigned w[4] = {raw.v[s].x, raw.v[s].y, raw.v[s].z, raw.v[s].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ss = fmaf(bf_lo(w[j]), bf_lo(w[j]), ss);
+        ss = fmaf(bf_hi(w[j]), bf_hi(w[j]), ss);
+      }
+    }
+    ss += __shfl_xor(ss, 32, 64);
+    const float rstd = rsqrtf(ss * (1.f / D) + eps);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float4 g0 = make_float4(1.f, 1.f, 1.f, 1.f), g1 = g0;
+      if (gamma) {
+        g0 = *(const float4*)(gamma + 16 * s + 8 * hh);
+        g1 = *(const float4*)(gamma + 16 * s + 8 * hh + 4);
+      }
+      const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) nscale[s][e] = rstd * gv[e];
+    }
+  }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     unsigned w[4] = {raw.v[s].x, raw.v[s].y, raw.v[s].z, raw.v[s].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float x0 = bf_lo(w[j]), x1 = bf_hi(w[j]);
+      if (kNorm) {
+        x0 *= nscale[s][2 * j];
+        x1 *= nscale[s][2 * j + 1];
+      }
       if (kRope) {
         // pair 8 s + 4 hh + j: both candidates are uniform loads, hh picks
         const double w = hh ? tab.w_rev[8 * s + 4 + j] : tab.w_rev[8 * s + j];
@@ -374,7 +408,7 @@ constexpr int kThreads = 256;  // 4 waves, 32 query rows each
 // anyway, so scale * log2(e) is folded in before that single rounding.
 // Without RoPE, Q is used exactly as given and the scale is applied to the
 // fp32 scores instead.
-template <bool kPreScaled>
+template <bool kPreScaled, bool kNorm>
 __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanView P, AttnLaunch A) {
   // Two stages of K and V tiles as separate objects, so the compiler can
   // tell the buffer being filled from the one being read.
@@ -450,7 +484,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   int w_cur = w_cur0;
   tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_cur0 & 0x7fffffff, L, wv);
   bf16x8 q[4];
-  finish_q<kPreScaled>(q, qraw, rvalid, anchor, A.tab, hh, kPreScaled ? sl2 : 1.f);
+  finish_q<kPreScaled, kNorm>(q, qraw, rvalid, anchor, A.tab, hh, kPreScaled ? sl2 : 1.f, A.eps,
+                              A.gamma_q);
   const int lo = rvalid ? qraw.dsc.x : 0;
   const int hi = rvalid ? qraw.dsc.y & 0x7fffffff : 0;
   const int self = rvalid && qraw.dsc.y < 0;
@@ -522,10 +557,13 @@ hipError_t launch_attn_mfma_bf16_d64(const rk_plan* p, const AttnLaunch& a, hipS
   PlanView P{p->dev.req, p->dev.qt_req, p->dev.row_desc, p->dev.qtile_ptr, p->dev.ktile_word,
              p->dev.sched, wl ? p->dev.work : nullptr};
   const dim3 grid((unsigned)p->grid);
-  if (a.rope_q)
-    hipLaunchKernelGGL(attn_mfma_bf16_d64_kernel<true>, grid, dim3(kThreads), 0, s, P, a);
+  if (a.rope_q && a.norm_q)
+    hipLaunchKernelGGL((attn_mfma_bf16_d64_kernel<true, true>), grid, dim3(kThreads), 0, s, P, a);
+  else if (a.rope_q)
+    hipLaunchKernelGGL((attn_mfma_bf16_d64_kernel<true, false>), grid, dim3(kThreads), 0, s, P, a);
   else
-    hipLaunchKernelGGL(attn_mfma_bf16_d64_kernel<false>, grid, dim3(kThreads), 0, s, P, a);
+    hipLaunchKernelGGL((attn_mfma_bf16_d64_kernel<false, false>), grid, dim3(kThreads), 0, s, P,
+                       a);
   return hipGetLastError();
 }
 

@@ -72,6 +72,15 @@ __global__ __launch_bounds__(128) void attn_ref_kernel(PlanView P, AttnLaunch A)
   float q[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) q[c] = valid ? ld(Q + (int64_t)tok * A.q_st + (int64_t)head * A.q_sh + c) : 0.f;
+  if (A.norm_q && valid) {
+    // QK Norm before the rotation
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) ss = fmaf(q[c], q[c], ss);
+    const float rstd = rsqrtf(ss / (float)D + A.eps);
+#pragma unroll
+    for (int c = 0; c < D; ++c) q[c] *= rstd * (A.gamma_q ? A.gamma_q[c] : 1.f);
+  }
   if (A.rope_q && valid) {
     const int64_t dt = A.ts[tok] - A.anchors[P.qt_req[qg]];
 #pragma unroll

@@ -147,11 +147,15 @@ struct RopeTab {
 // ---- launchers (defined in the .hip files); return hipSuccess or an error
 hipError_t launch_plan(const rk_plan* p, hipStream_t s);
 // kinds: rotate only tokens whose segment kind k has bit k set (0 = all).
+// norm: RMSNorm of every [d] row (x / sqrt(mean(x^2) + eps) * gamma, gamma
+// NULL = 1) before the rotation; needs d in {32, 64, 128}.  A zero table
+// rotates by nothing (cos 0 = 1, sin 0 = 0 exactly).
 hipError_t launch_rope(int32_t R, int32_t T, const int32_t* req_offsets, const int64_t* ts,
                        const int64_t* anchors, const uint8_t* kind, unsigned kinds,
                        const RopeTab& tab, const void* x_in, void* x_out, rk_dtype dt, int H, int d,
                        int64_t in_st, int64_t in_sh, int64_t out_st, int64_t out_sh,
-                       hipStream_t s);
+                       hipStream_t s, bool norm = false, float eps = 0.f,
+                       const float* gamma = nullptr);
 
 struct AttnLaunch {
   const void* q;
@@ -162,7 +166,11 @@ struct AttnLaunch {
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
   float scale;
   int H, d, T;
-  bool rope_q;              // rotate Q while staging (K is already rotated)
+  bool rope_q;              // transform Q while staging: rotate by `tab` (all zero
+                            // for no rotation), fold the scale in (K is ready)
+  bool norm_q;              // RMSNorm Q before the rotation (QK Norm)
+  float eps;
+  const float* gamma_q;     // [d] or null
   float* part;              // partial results of split items, or null
   const int64_t* ts;
   const int64_t* anchors;

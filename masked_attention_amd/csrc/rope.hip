@@ -36,7 +36,13 @@ __device__ __forceinline__ bool selected(uint8_t k, unsigned kinds) {
   return k < 4 && ((kinds >> k) & 1u);
 }
 
-template <typename T>
+// Sum of v over the n lanes (power of two, n <= 64, aligned) holding one row.
+__device__ __forceinline__ float row_sum(float v, int n) {
+  for (int o = 1; o < n; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <typename T, bool kNorm>
 __global__ __launch_bounds__(256) void rope_kernel(int R, int Tn, const int32_t* __restrict__ offs,
                                                    const int64_t* __restrict__ ts,
                                                    const int64_t* __restrict__ anchors,
@@ -44,7 +50,8 @@ __global__ __launch_bounds__(256) void rope_kernel(int R, int Tn, const int32_t*
                                                    unsigned kinds, RopeTab tab, const T* x, T* y,
                                                    int H, int d,
                                                    int64_t ist, int64_t ish, int64_t ost,
-                                                   int64_t osh) {
+                                                   int64_t osh, float eps,
+                                                   const float* __restrict__ gamma) {
   __shared__ double w[kMaxHalfD];
   const int half = d >> 1;
   if (threadIdx.x < half) w[threadIdx.x] = tab.w_rev[threadIdx.x];
@@ -67,9 +74,18 @@ __global__ __launch_bounds__(256) void rope_kernel(int R, int Tn, const int32_t*
   sincosf(6.283185307179586f * f, &sn, &cs);
   const T* xp = x + (int64_t)tok * ist + 2 * i;
   T* yp = y + (int64_t)tok * ost + 2 * i;
+  // with kNorm the d / 2 lanes of a token (consecutive, aligned: d / 2
+  // divides 64 and 256) hold one row per head and reduce it together
+  const float g0 = kNorm && gamma ? gamma[2 * i] : 1.f;
+  const float g1 = kNorm && gamma ? gamma[2 * i + 1] : 1.f;
   for (int h = 0; h < H; ++h) {
-    const float x0 = load_elem(xp + (int64_t)h * ish);
-    const float x1 = load_elem(xp + (int64_t)h * ish + 1);
+    float x0 = load_elem(xp + (int64_t)h * ish);
+    float x1 = load_elem(xp + (int64_t)h * ish + 1);
+    if (kNorm) {
+      const float rstd = rsqrtf(row_sum(x0 * x0 + x1 * x1, half) / (float)d + eps);
+      x0 *= rstd * g0;
+      x1 *= rstd * g1;
+    }
     store_pair(yp + (int64_t)h * osh, x0 * cs - x1 * sn, x0 * sn + x1 * cs);
   }
 }
@@ -77,7 +93,7 @@ __global__ __launch_bounds__(256) void rope_kernel(int R, int Tn, const int32_t*
 // Vector form for d % 8 == 0 with 16-byte aligned rows: one thread per
 // (token, group of four pairs); 16-byte (bf16) or 2 x 16-byte (fp32)
 // accesses per head.
-template <typename T>
+template <typename T, bool kNorm>
 __global__ __launch_bounds__(256) void rope8_kernel(int R, int Tn, const int32_t* __restrict__ offs,
                                                     const int64_t* __restrict__ ts,
                                                     const int64_t* __restrict__ anchors,
@@ -85,7 +101,8 @@ __global__ __launch_bounds__(256) void rope8_kernel(int R, int Tn, const int32_t
                                                     unsigned kinds, RopeTab tab, const T* x, T* y,
                                                     int H, int d,
                                                     int64_t ist, int64_t ish, int64_t ost,
-                                                    int64_t osh) {
+                                                    int64_t osh, float eps,
+                                                    const float* __restrict__ gamma) {
   __shared__ double w[kMaxHalfD];
   const int half = d >> 1;
   if (threadIdx.x < half) w[threadIdx.x] = tab.w_rev[threadIdx.x];
@@ -112,6 +129,9 @@ __global__ __launch_bounds__(256) void rope8_kernel(int R, int Tn, const int32_t
   }
   const T* xp = x + (int64_t)tok * ist + 8 * g;
   T* yp = y + (int64_t)tok * ost + 8 * g;
+  float gm[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) gm[j] = kNorm && gamma ? gamma[8 * g + j] : 1.f;
   for (int h = 0; h < H; ++h) {
     float v[8];
     if constexpr (sizeof(T) == 2) {
@@ -127,6 +147,15 @@ __global__ __launch_bounds__(256) void rope8_kernel(int R, int Tn, const int32_t
       const float4 p1 = *(const float4*)(xp + (int64_t)h * ish + 4);
       v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
       v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+    }
+    if (kNorm) {
+      // the d / 8 lanes of a token (consecutive, aligned) hold one row
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+      const float rstd = rsqrtf(row_sum(ss, groups) / (float)d + eps);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] *= rstd * gm[j];
     }
     float o[8];
 #pragma unroll
@@ -153,35 +182,36 @@ hipError_t launch_rope(int32_t R, int32_t T, const int32_t* req_offsets, const i
                        const int64_t* anchors, const uint8_t* kind, unsigned kinds,
                        const RopeTab& tab, const void* x_in, void* x_out, rk_dtype dt, int H, int d,
                        int64_t in_st, int64_t in_sh, int64_t out_st, int64_t out_sh,
-                       hipStream_t s) {
+                       hipStream_t s, bool norm, float eps, const float* gamma) {
   if (T == 0) return hipSuccess;
   const int64_t v = 16 / (dt == RK_F32 ? 4 : 2);  // elements per 16 bytes
   const bool vec = (d % 8 == 0) && ((uintptr_t)x_in % 16 == 0) && ((uintptr_t)x_out % 16 == 0) &&
                    in_st % v == 0 && in_sh % v == 0 && out_st % v == 0 && out_sh % v == 0;
+  const int per = vec ? 8 : 2;  // elements of a row per thread
+  const int64_t n = (int64_t)T * (d / per);
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+#define RK_ROPE_LAUNCH(KERNEL, TY, NORM)                                                         \
+  hipLaunchKernelGGL((KERNEL<TY, NORM>), grid, block, 0, s, R, T, req_offsets, ts, anchors, kind, \
+                     kinds, tab, (const TY*)x_in, (TY*)x_out, H, d, in_st, in_sh, out_st, out_sh,  \
+                     eps, gamma)
   if (vec) {
-    const int64_t n = (int64_t)T * (d / 8);
-    const unsigned blocks = (unsigned)((n + 255) / 256);
-    if (dt == RK_F32)
-      hipLaunchKernelGGL(rope8_kernel<float>, dim3(blocks), dim3(256), 0, s, R, T, req_offsets, ts,
-                         anchors, kind, kinds, tab, (const float*)x_in, (float*)x_out, H, d, in_st, in_sh,
-                         out_st, out_sh);
-    else
-      hipLaunchKernelGGL(rope8_kernel<__hip_bfloat16>, dim3(blocks), dim3(256), 0, s, R, T,
-                         req_offsets, ts, anchors, kind, kinds, tab, (const __hip_bfloat16*)x_in,
-                         (__hip_bfloat16*)x_out, H, d, in_st, in_sh, out_st, out_sh);
-    return hipGetLastError();
-  }
-  const int64_t n = (int64_t)T * (d / 2);
-  const unsigned blocks = (unsigned)((n + 255) / 256);
-  if (dt == RK_F32) {
-    hipLaunchKernelGGL(rope_kernel<float>, dim3(blocks), dim3(256), 0, s, R, T, req_offsets, ts,
-                       anchors, kind, kinds, tab, (const float*)x_in, (float*)x_out, H, d, in_st, in_sh, out_st,
-                       out_sh);
+    if (dt == RK_F32) {
+      if (norm) RK_ROPE_LAUNCH(rope8_kernel, float, true);
+      else RK_ROPE_LAUNCH(rope8_kernel, float, false);
+    } else {
+      if (norm) RK_ROPE_LAUNCH(rope8_kernel, __hip_bfloat16, true);
+      else RK_ROPE_LAUNCH(rope8_kernel, __hip_bfloat16, false);
+    }
   } else {
-    hipLaunchKernelGGL(rope_kernel<__hip_bfloat16>, dim3(blocks), dim3(256), 0, s, R, T,
-                       req_offsets, ts, anchors, kind, kinds, tab, (const __hip_bfloat16*)x_in,
-                       (__hip_bfloat16*)x_out, H, d, in_st, in_sh, out_st, out_sh);
+    if (dt == RK_F32) {
+      if (norm) RK_ROPE_LAUNCH(rope_kernel, float, true);
+      else RK_ROPE_LAUNCH(rope_kernel, float, false);
+    } else {
+      if (norm) RK_ROPE_LAUNCH(rope_kernel, __hip_bfloat16, true);
+      else RK_ROPE_LAUNCH(rope_kernel, __hip_bfloat16, false);
+    }
   }
+#undef RK_ROPE_LAUNCH
   return hipGetLastError();
 }
 
