@@ -3,8 +3,9 @@
 from .masked_attention import (  # noqa: F401
     CANDIDATE, EMPTY, FULL, HISTORY, PARTIAL, PROFILE, REALTIME, TILE_K, TILE_Q,
     attention_backward, attention_backward_sampled, attention_forward, attention_rows,
-    compressed_history_length, count_visible, group_sum_compress, masked_softmax_attention,
-    masked_softmax_attention_backward, prune_history, pruned_history_length, qk_rmsnorm,
+    compressed_history_length, count_visible, group_sum_compress, hstu_rab, masked_softmax_attention,
+    masked_softmax_attention_backward, pointwise_attention,
+    pointwise_attention_forward, prune_history, pruned_history_length, qk_rmsnorm,
     rope_frequencies,
-    tile_plan, tile_plan_request, time_rope, time_rope_transpose, visibility, visible_rows,
+    tile_plan, tile_plan_request, time_bucket, time_rope, time_rope_transpose, visibility, visible_rows,
 )

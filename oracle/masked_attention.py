@@ -293,6 +293,84 @@ def attention_rows(req_offsets, seg_kind, timestamps, q, k, v, tokens: np.ndarra
 
 
 # ---------------------------------------------------------------------------
+# HSTU pointwise aggregated attention (HSTU, eq. 2)
+# ---------------------------------------------------------------------------
+
+def time_bucket(dt: int, num_buckets: int) -> int:
+    """Bucket of a time difference: floor(log2(1 + |dt|)) capped at
+    num_buckets - 1 (exact integer arithmetic: the bit length of 1 + |dt|
+    minus one)."""
+    return min(int(1 + abs(int(dt))).bit_length() - 1, num_buckets - 1)
+
+
+def hstu_rab(positions: np.ndarray, times: np.ndarray, rows: np.ndarray,
+             pos_bias: Optional[np.ndarray], time_bias: Optional[np.ndarray]) -> np.ndarray:
+    """Relative attention bias rab^{p,t} [len(rows), L] of one request, shared
+    by every head: pos_bias[min(|p_i - p_j|, P - 1)] + time_bias[bucket of
+    t_i - t_j] (time_bucket).  A None table contributes 0."""
+    rows = np.asarray(rows, np.int64)
+    L = positions.shape[0]
+    rab = np.zeros((rows.shape[0], L))
+    if pos_bias is not None:
+        dp = np.abs(positions[rows][:, None] - positions[None, :])
+        rab += np.asarray(pos_bias, np.float64)[np.minimum(dp, len(pos_bias) - 1)]
+    if time_bias is not None:
+        B = len(time_bias)
+        dt = np.abs(np.asarray(times, np.int64)[rows][:, None] - np.asarray(times, np.int64)[None, :])
+        # bit length of 1 + |dt| minus one, capped
+        bucket = np.minimum(np.floor(np.log2(1.0 + dt.astype(np.float64))).astype(np.int64), B - 1)
+        # float log2 can round up just below a power of two: correct by integers
+        bucket = np.where((np.left_shift(np.int64(1), np.maximum(bucket, 0)) > 1 + dt), bucket - 1,
+                          bucket)
+        rab += np.asarray(time_bias, np.float64)[np.clip(bucket, 0, B - 1)]
+    return rab
+
+
+def pointwise_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarray,
+                        scale: float, rab: Optional[np.ndarray]) -> np.ndarray:
+    """HSTU eq. 2 for one head: O = (SiLU(q k^T * scale + rab) * vis) v, with
+    SiLU(x) = x / (1 + exp(-x)); masked pairs contribute nothing and there is
+    no normalisation."""
+    x = (q @ k.T) * scale
+    if rab is not None:
+        x = x + rab
+    w = np.where(vis, x / (1.0 + np.exp(-x)), 0.0)
+    return w @ v
+
+
+def pointwise_attention_forward(req_offsets, seg_kind, timestamps, q, k, v, *, delay, window,
+                                static_bidirectional, scale: float = 1.0, pos_bias=None,
+                                time_bias=None, global_tail: int = 0, heads=None,
+                                requests=None, row_block: int = 1024) -> np.ndarray:
+    """HSTU pointwise attention over a packed batch with the method's mask
+    (each request's explicit visibility), float64.  Returns o [T, H, d]."""
+    T, H, d = q.shape
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    o = np.zeros((T, H, d))
+    heads = np.arange(H) if heads is None else np.asarray(heads)
+    R = req_offsets.shape[0] - 1
+    requests = np.arange(R) if requests is None else np.asarray(requests)
+    for r in requests:
+        a, b = int(req_offsets[r]), int(req_offsets[r + 1])
+        L = b - a
+        if L == 0:
+            continue
+        pos = np.arange(L, dtype=np.int64)
+        for r0 in range(0, L, row_block):
+            rows = np.arange(r0, min(L, r0 + row_block))
+            vis = visible_rows(seg_kind[a:b], timestamps[a:b], rows, delay=delay, window=window,
+                               static_bidirectional=static_bidirectional,
+                               global_tail=global_tail)
+            rab = hstu_rab(pos, timestamps[a:b], rows, pos_bias, time_bias)
+            for h in heads:
+                o[a + rows, h] = pointwise_attention(q[a + rows, h], k[a:b, h], v[a:b, h], vis,
+                                                     scale, rab)
+    return o
+
+
+# ---------------------------------------------------------------------------
 # Backward of the masked softmax attention (gradients of a scalar loss)
 # ---------------------------------------------------------------------------
 
