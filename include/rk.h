@@ -15,6 +15,8 @@
  *   rk_masked_attn_fwd  softmax(Q K^T * scale + M) V over the plan, with
  *                       optional fused time RoPE;
  *   rk_masked_attn_bwd  its gradients with respect to Q, K and V;
+ *   rk_pointwise_attn_fwd
+ *                       HSTU's pointwise (SiLU) attention over the same plan;
  *   rk_compress_layout / rk_prune_layout / rk_gather_sum
  *                       LazFormer's history compression and per-layer
  *                       history pruning, before and between layers.
@@ -473,6 +475,44 @@ rk_status rk_attn_bwd_workspace_size(const rk_plan* p, const rk_attn_bwd_args* a
  * RK_ERR_HIP.
  */
 rk_status rk_masked_attn_bwd(const rk_plan* p, const rk_attn_bwd_args* a, void* stream);
+
+/*
+ * HSTU pointwise aggregated attention (HSTU eq. 2): over the same plan and
+ * mask as rk_masked_attn_fwd,
+ *   O_i = sum over visible j of SiLU(scale * q_i . k_j + rab_ij) v_j,
+ * SiLU(x) = x / (1 + exp(-x)), with no normalisation (the pointwise form
+ * keeps the number of related history points in the output).  rab^{p,t}
+ * is shared by every head (the page): rab_ij = pos_bias[min(|p_i - p_j|,
+ * num_pos_buckets - 1)] + time_bias[min(floor(log2(1 + |t_i - t_j|)),
+ * num_time_buckets - 1)] (p request-local positions, t timestamps; the page
+ * only says "a bucketing function of the time difference"); a NULL table
+ * adds nothing.  No time RoPE (HSTU's rab carries position and time).
+ */
+typedef struct rk_pointwise_args {
+  uint32_t struct_size;
+  uint32_t flags;            /* RK_ATTN_REFERENCE_KERNEL or 0 */
+  rk_dtype dtype;            /* RK_BF16 (bf16 MFMA for d_head == 64, 16-byte aligned rows) or
+                                RK_F32; d_head in {32, 64, 128} */
+  int32_t num_heads;
+  int32_t d_head;
+  int32_t num_pos_buckets;   /* 1 .. 4096 when pos_bias is set */
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t q_stride_tok, q_stride_head;
+  int64_t k_stride_tok, k_stride_head;
+  int64_t v_stride_tok, v_stride_head;
+  int64_t o_stride_tok, o_stride_head;
+  float scale;               /* multiplies Q K^T; 0 selects 1 (no scale is printed) */
+  int32_t num_time_buckets;  /* 1 .. 64 when time_bias is set */
+  const float* pos_bias;     /* device fp32 [num_pos_buckets] or NULL */
+  const float* time_bias;    /* device fp32 [num_time_buckets] or NULL */
+} rk_pointwise_args;
+
+/* Errors: RK_ERR_INVALID_ARG (including num_heads != the plan's, a
+ * RK_QUERY_CANDIDATES_ONLY plan), RK_ERR_UNSUPPORTED, RK_ERR_HIP. */
+rk_status rk_pointwise_attn_fwd(const rk_plan* p, const rk_pointwise_args* a, void* stream);
 
 /* ---- LazFormer pre-passes (section 2.3): history compression and per-layer
  * history pruning.  The layout functions run on the host (they read host

@@ -177,6 +177,29 @@ class rk_attn_bwd_args(C.Structure):
     ]
 
 
+class rk_pointwise_args(C.Structure):
+    _fields_ = [
+        ("struct_size", C.c_uint32),
+        ("flags", C.c_uint32),
+        ("dtype", C.c_int),
+        ("num_heads", C.c_int32),
+        ("d_head", C.c_int32),
+        ("num_pos_buckets", C.c_int32),
+        ("q", C.c_void_p),
+        ("k", C.c_void_p),
+        ("v", C.c_void_p),
+        ("o", C.c_void_p),
+        ("q_stride_tok", C.c_int64), ("q_stride_head", C.c_int64),
+        ("k_stride_tok", C.c_int64), ("k_stride_head", C.c_int64),
+        ("v_stride_tok", C.c_int64), ("v_stride_head", C.c_int64),
+        ("o_stride_tok", C.c_int64), ("o_stride_head", C.c_int64),
+        ("scale", C.c_float),
+        ("num_time_buckets", C.c_int32),
+        ("pos_bias", C.c_void_p),
+        ("time_bias", C.c_void_p),
+    ]
+
+
 class rk_host_layout(C.Structure):
     _fields_ = [
         ("struct_size", C.c_uint32),
@@ -211,6 +234,7 @@ STRUCTS = {
     "rk_plan_totals": rk_plan_totals,
     "rk_attn_args": rk_attn_args,
     "rk_attn_bwd_args": rk_attn_bwd_args,
+    "rk_pointwise_args": rk_pointwise_args,
     "rk_host_layout": rk_host_layout,
     "rk_layout_out": rk_layout_out,
 }
@@ -238,6 +262,7 @@ FUNCTIONS = [
     ("rk_attn_bwd_workspace_size", C.c_int, [C.c_void_p, C.POINTER(rk_attn_bwd_args),
                                              C.POINTER(C.c_size_t)]),
     ("rk_masked_attn_bwd", C.c_int, [C.c_void_p, C.POINTER(rk_attn_bwd_args), C.c_void_p]),
+    ("rk_pointwise_attn_fwd", C.c_int, [C.c_void_p, C.POINTER(rk_pointwise_args), C.c_void_p]),
     ("rk_compress_layout", C.c_int, [C.POINTER(rk_host_layout), C.c_int32, C.c_int32,
                                      C.POINTER(rk_layout_out)]),
     ("rk_pruned_history_length", C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32,

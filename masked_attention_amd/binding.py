@@ -371,6 +371,38 @@ def rk_masked_attn_bwd(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Te
     return dq, dk, dv
 
 
+def rk_pointwise_attn_fwd(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                          out: Optional[torch.Tensor] = None, scale: float = 0.0,
+                          pos_bias: Optional[torch.Tensor] = None,
+                          time_bias: Optional[torch.Tensor] = None, reference: bool = False,
+                          stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """HSTU pointwise attention over `plan`: O_i = sum over visible j of
+    SiLU(scale q_i . k_j + rab_ij) v_j (scale 0 = 1).  pos_bias / time_bias:
+    float32 device tensors (the rab tables, shared by every head) or None."""
+    for t in (q, k, v):
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError("q, k, v must be [T, H, d] with d contiguous")
+    for t in (pos_bias, time_bias):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("bias tables must be contiguous float32 tensors")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    a = sized(_rk.rk_pointwise_args, flags=_rk.RK_ATTN_REFERENCE_KERNEL if reference else 0,
+              dtype=_dtype_code(q), num_heads=q.shape[1], d_head=q.shape[2],
+              q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), o=out.data_ptr(),
+              q_stride_tok=q.stride(0), q_stride_head=q.stride(1),
+              k_stride_tok=k.stride(0), k_stride_head=k.stride(1),
+              v_stride_tok=v.stride(0), v_stride_head=v.stride(1),
+              o_stride_tok=out.stride(0), o_stride_head=out.stride(1), scale=float(scale),
+              num_pos_buckets=pos_bias.numel() if pos_bias is not None else 0,
+              num_time_buckets=time_bias.numel() if time_bias is not None else 0,
+              pos_bias=pos_bias.data_ptr() if pos_bias is not None else None,
+              time_bias=time_bias.data_ptr() if time_bias is not None else None)
+    check(lib().rk_pointwise_attn_fwd(plan.handle, C.byref(a), _stream(stream)),
+          "rk_pointwise_attn_fwd")
+    return out
+
+
 # ---- LazFormer pre-passes -------------------------------------------------
 
 class Layout:

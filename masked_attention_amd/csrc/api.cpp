@@ -664,6 +664,57 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
   return e == hipSuccess ? RK_OK : RK_ERR_HIP;
 }
 
+rk_status rk_pointwise_attn_fwd(const rk_plan* p, const rk_pointwise_args* a, void* stream) {
+  if (!p || !a || a->struct_size < sizeof(rk_pointwise_args)) return RK_ERR_INVALID_ARG;
+  if (p->flags & RK_QUERY_CANDIDATES_ONLY) return RK_ERR_INVALID_ARG;
+  if (!valid_dtype(a->dtype) || a->num_heads != p->H) return RK_ERR_INVALID_ARG;
+  if (a->d_head != 32 && a->d_head != 64 && a->d_head != 128) return RK_ERR_UNSUPPORTED;
+  if (a->flags & ~RK_ATTN_REFERENCE_KERNEL) return RK_ERR_INVALID_ARG;
+  if (p->T > 0 && (!a->q || !a->k || !a->v || !a->o)) return RK_ERR_INVALID_ARG;
+  const int64_t st[8] = {a->q_stride_tok, a->q_stride_head, a->k_stride_tok, a->k_stride_head,
+                         a->v_stride_tok, a->v_stride_head, a->o_stride_tok, a->o_stride_head};
+  for (int64_t x : st)
+    if (x < 0) return RK_ERR_INVALID_ARG;
+  if (!std::isfinite(a->scale)) return RK_ERR_INVALID_ARG;
+  if (a->pos_bias && (a->num_pos_buckets < 1 || a->num_pos_buckets > 4096)) return RK_ERR_INVALID_ARG;
+  if (a->time_bias && (a->num_time_buckets < 1 || a->num_time_buckets > 64))
+    return RK_ERR_INVALID_ARG;
+  const bool use_mfma =
+      enum_int(a->dtype) == RK_BF16 && a->d_head == 64 && !(a->flags & RK_ATTN_REFERENCE_KERNEL);
+  if (use_mfma) {
+    auto al = [](const void* ptr) { return ((uintptr_t)ptr % 16) == 0; };
+    for (int64_t x : st)
+      if ((x % 8) != 0 || x > (int64_t(1) << 24)) return RK_ERR_UNSUPPORTED;
+    if (!al(a->q) || !al(a->k) || !al(a->v) || !al(a->o)) return RK_ERR_UNSUPPORTED;
+  }
+  rk::PwLaunch L;
+  std::memset(&L, 0, sizeof(L));
+  L.q = a->q;
+  L.k = a->k;
+  L.v = a->v;
+  L.o = a->o;
+  L.q_st = a->q_stride_tok;
+  L.q_sh = a->q_stride_head;
+  L.k_st = a->k_stride_tok;
+  L.k_sh = a->k_stride_head;
+  L.v_st = a->v_stride_tok;
+  L.v_sh = a->v_stride_head;
+  L.o_st = a->o_stride_tok;
+  L.o_sh = a->o_stride_head;
+  L.scale = a->scale != 0.f ? a->scale : 1.f;
+  L.H = a->num_heads;
+  L.d = a->d_head;
+  L.T = p->T;
+  L.pos_bias = a->pos_bias;
+  L.time_bias = a->time_bias;
+  L.np = a->pos_bias ? a->num_pos_buckets : 1;
+  L.nt = a->time_bias ? a->num_time_buckets : 1;
+  L.ts = p->timestamps_dev;
+  hipError_t e = use_mfma ? rk::launch_pointwise_mfma_bf16_d64(p, L, (hipStream_t)stream)
+                          : rk::launch_pointwise_reference(p, L, a->dtype, (hipStream_t)stream);
+  return e == hipSuccess ? RK_OK : RK_ERR_HIP;
+}
+
 namespace {
 
 rk_status check_bwd(const rk_plan* p, const rk_attn_bwd_args* a) {

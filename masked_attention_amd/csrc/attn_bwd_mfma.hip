@@ -50,24 +50,18 @@
 // chunk c of row r sits in slot c ^ swz(r), swz(r) = 2 (r & 3) + ((r >> 2) & 1),
 // which keeps both the row reads (8 consecutive rows, one chunk) and the
 // transposing reads (4 consecutive rows, two chunks) free of bank conflicts.
-#include <hip/hip_bf16.h>
-
-#include "rk_internal.h"
+#include "cdna4_common.h"
 
 namespace rk {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short v4i16 __attribute__((ext_vector_type(4)));
+using namespace cdna4;
 
 constexpr int D = 64;
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr unsigned kBufferFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+#define LDS_PTR RK_LDS_PTR
 
 struct BwdPlanView {
   const ReqMeta* req;
@@ -81,34 +75,6 @@ struct BwdPlanView {
   const int32_t* sched;
   const int32_t* ksched;
 };
-
-template <typename T>
-__device__ __forceinline__ T ldc(const T* p, int64_t i) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  return ((const __attribute__((address_space(4))) T*)p)[i];
-#else
-  return p[i];  // host pass of the single-source compile; never executed
-#endif
-}
-
-// two floats -> packed bf16 pair (round to nearest even)
-__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-  bf16x2_t r;
-  r[0] = (__bf16)a;
-  r[1] = (__bf16)b;
-  unsigned u;
-  __builtin_memcpy(&u, &r, 4);
-  return u;
-}
-
-__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
-}
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
@@ -163,14 +129,7 @@ __device__ __forceinline__ void copy_rows(unsigned short* dst, __amdgpu_buffer_r
 // c0 + 8 g + 4 hh + e is in register 4 g + e of s0, that key + 32 in s1.
 __device__ __forceinline__ void mask_keys(f32x16& s0, f32x16& s1, int kt, int hh, int lo, int hi,
                                           int self, int row) {
-  const int c0 = kt * kTileK;
-  const int a = min(max(lo - c0, 0), kTileK), b = min(max(hi - c0, 0), kTileK);
-  const uint64_t below_b = b >= 64 ? ~0ull : (1ull << b) - 1ull;
-  const uint64_t below_a = a >= 64 ? ~0ull : (1ull << a) - 1ull;
-  uint64_t vis = below_b & ~below_a;
-  const int sr = row - c0;
-  if (self && sr >= 0 && sr < kTileK) vis |= 1ull << sr;
-  vis >>= 4 * hh;
+  const uint64_t vis = tile_vis_bits(kt * kTileK, lo, hi, self, row) >> (4 * hh);
   const int w0 = (int)(unsigned)vis, w1 = (int)(unsigned)(vis >> 32);
   const int ninf = (int)0xff800000u;
 #pragma unroll

@@ -215,6 +215,25 @@ hipError_t launch_gather_sum(const int32_t* ranges, int n_out, int n_in, const v
                              int64_t xs, void* y, int64_t ys, int width, rk_dtype dt,
                              hipStream_t s);
 
+// HSTU pointwise attention launch description.
+struct PwLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
+  float scale;
+  int H, d, T;
+  const float* pos_bias;  // [np] or null
+  const float* time_bias; // [nt] or null
+  int np, nt;
+  const int64_t* ts;
+};
+
+hipError_t launch_pointwise_reference(const rk_plan* p, const PwLaunch& a, rk_dtype dt,
+                                      hipStream_t s);
+hipError_t launch_pointwise_mfma_bf16_d64(const rk_plan* p, const PwLaunch& a, hipStream_t s);
+
 hipError_t launch_attn_reference(const rk_plan* p, const AttnLaunch& a, rk_dtype dt,
                                  hipStream_t s);
 hipError_t launch_attn_mfma_bf16_d64(const rk_plan* p, const AttnLaunch& a, hipStream_t s);

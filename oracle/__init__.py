@@ -5,7 +5,7 @@ from .masked_attention import (  # noqa: F401
     attention_backward, attention_backward_sampled, attention_forward, attention_rows,
     compressed_history_length, count_visible, group_sum_compress, hstu_rab, masked_softmax_attention,
     masked_softmax_attention_backward, pointwise_attention,
-    pointwise_attention_forward, prune_history, pruned_history_length, qk_rmsnorm,
+    pointwise_attention_forward, pointwise_attention_rows, prune_history, pruned_history_length, qk_rmsnorm,
     rope_frequencies,
     tile_plan, tile_plan_request, time_bucket, time_rope, time_rope_transpose, visibility, visible_rows,
 )

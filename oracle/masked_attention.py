@@ -370,6 +370,29 @@ def pointwise_attention_forward(req_offsets, seg_kind, timestamps, q, k, v, *, d
     return o
 
 
+def pointwise_attention_rows(req_offsets, seg_kind, timestamps, q, k, v, tokens, head, *, delay,
+                             window, static_bidirectional, scale: float = 1.0, pos_bias=None,
+                             time_bias=None, global_tail: int = 0) -> np.ndarray:
+    """Pointwise attention output rows of selected global tokens of one head
+    (for sampled checks); each token against its own request's keys."""
+    tokens = np.asarray(tokens, np.int64)
+    d = q.shape[-1]
+    req_of = np.searchsorted(req_offsets, tokens, side="right") - 1
+    o = np.zeros((tokens.shape[0], d))
+    for r in np.unique(req_of):
+        sel = np.nonzero(req_of == r)[0]
+        a, b = int(req_offsets[r]), int(req_offsets[r + 1])
+        rows = tokens[sel] - a
+        vis = visible_rows(seg_kind[a:b], timestamps[a:b], rows, delay=delay, window=window,
+                           static_bidirectional=static_bidirectional, global_tail=global_tail)
+        rab = hstu_rab(np.arange(b - a, dtype=np.int64), timestamps[a:b], rows, pos_bias,
+                       time_bias)
+        o[sel] = pointwise_attention(np.asarray(q[a + rows, head], np.float64),
+                                     np.asarray(k[a:b, head], np.float64),
+                                     np.asarray(v[a:b, head], np.float64), vis, scale, rab)
+    return o
+
+
 # ---------------------------------------------------------------------------
 # Backward of the masked softmax attention (gradients of a scalar loss)
 # ---------------------------------------------------------------------------

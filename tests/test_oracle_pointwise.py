@@ -156,3 +156,17 @@ def test_candidate_permutation_equivariance():
     op = oracle.pointwise_attention_forward(wp.req_offsets, wp.seg_kind, wp.timestamps,
                                             wl.q[idx], wl.k[idx], wl.v[idx], **kw)
     assert np.allclose(op, o[idx], atol=1e-12)
+
+
+def test_rows_form_equals_full_form():
+    rng = np.random.default_rng(7)
+    wl = make_custom(random_layout(rng, 4, 90), heads=2, d_head=8, seed=7, delay=120, window=9)
+    kw = dict(delay=wl.delay, window=wl.window, static_bidirectional=False, scale=0.3,
+              pos_bias=rng.standard_normal(11), time_bias=rng.standard_normal(20))
+    o = oracle.pointwise_attention_forward(wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q,
+                                           wl.k, wl.v, **kw)
+    toks = rng.choice(wl.total_tokens, size=25, replace=False)
+    for h in range(2):
+        rows = oracle.pointwise_attention_rows(wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q,
+                                               wl.k, wl.v, toks, h, **kw)
+        assert np.array_equal(rows, o[toks, h])
