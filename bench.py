@@ -56,6 +56,10 @@ def _parse():
                     help="time the backward step instead: the forward runs once (untimed) for "
                          "O and LSE; each step plans with the key-major tables and runs "
                          "rk_masked_attn_bwd (Q/K rotation, dQ kernel, dK/dV kernel)")
+    ap.add_argument("--pointwise", action="store_true",
+                    help="time HSTU pointwise attention (SiLU, rab tables of 128 position and 32 "
+                         "time buckets, scale 1/sqrt(d)) on the workload instead: plan + "
+                         "rk_pointwise_attn_fwd")
     ap.add_argument("--lazformer", action="store_true",
                     help="time LazFormer's attention stack instead: group-sum compression of "
                          "Q/K/V (2048 -> 1152), then per layer the pruned input gathered, "
@@ -255,6 +259,78 @@ def backward_main(args) -> int:
     return 0
 
 
+def pointwise_main(args) -> int:
+    """One JSON line for HSTU pointwise attention over a named workload (the
+    same visible pairs; FLOPs counted as 4 d per visible pair and head)."""
+    import numpy as np
+    import torch
+
+    import masked_attention_amd as rk
+    from rk_workloads import make_config
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    wl = make_config(args.config)
+    H, d = wl.heads, wl.d_head
+    batch = rk.Batch.from_workload(wl, device=dev)
+    q, k, v = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (wl.q, wl.k, wl.v))
+    rng = np.random.default_rng(77)
+    pb = torch.from_numpy((rng.standard_normal(128) * 0.3).astype(np.float32)).to(dev)
+    tb = torch.from_numpy((rng.standard_normal(32) * 0.3).astype(np.float32)).to(dev)
+    ws = torch.empty(rk.rk_plan_workspace_size(batch, H), dtype=torch.uint8, device=dev)
+    mk = dict(delay=wl.delay, window=wl.window, static_bidirectional=wl.static_bidirectional,
+              num_heads=H, workspace=ws)
+    p0 = rk.Plan(batch, **mk)
+    pairs = p0.stats()["visible_pairs"]
+    p0.close()
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    plans = []
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        p = rk.Plan(batch, **mk)
+        if ev: ev[1].record(stream)
+        rk.rk_pointwise_attn_fwd(p, q, k, v, out=o, scale=1.0 / np.sqrt(d), pos_bias=pb,
+                                 time_bias=tb)
+        if ev: ev[2].record(stream)
+        plans.append(p)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for p in plans:
+        p.close()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    plan_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    attn_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    flops = 4.0 * d * H * pairs
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    out = {
+        "metric": "HSTU pointwise attention effective TFLOP/s (visible pairs)",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generator with the workload's shapes and time law)",
+        "config": {"workload": wl.name + " pointwise", "requests": wl.num_requests,
+                   "tokens": wl.total_tokens, "heads": H, "d_head": d,
+                   "visible_pairs_per_head": pairs, "pos_buckets": 128, "time_buckets": 32},
+        "stage_ms": {"plan": round(plan_ms, 4), "attention": round(attn_ms, 4)},
+        "roofline": {"bound": "mfma", "kernel": "pw_mfma_bf16_d64_kernel",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def lazformer_main(args) -> int:
     """One JSON line for LazFormer's attention stack (section 2.3): per
     step, compression of Q, K, V (rk_gather_sum over rk_compress_layout's
@@ -376,6 +452,8 @@ def main() -> int:
         return backward_main(args)
     if args.lazformer:
         return lazformer_main(args)
+    if args.pointwise:
+        return pointwise_main(args)
 
     import numpy as np
     import torch
