@@ -5,6 +5,11 @@ One step = the whole path over one batch already resident in HBM:
   rk_mask_plan        (tile plan + launch schedule)
   rk_time_rope        (K rotated by time RoPE)
   rk_masked_attn_fwd  (Q rotated while staged; masked flash attention)
+Steps are independent batches.  With --pipeline on the next step's plan
+and K rotation run on a second stream while this step's attention runs
+(double-buffered plan workspace and rotated keys); off runs each step's
+three stages back to back on one stream; auto (default) pipelines when a
+serial warmup step takes more than 1 ms.
 The default workload is the TM20K-shaped batch (8 users x (20000 history +
 1 target), causal, H = 8, d_head = 64, bf16, time RoPE).
 
@@ -64,6 +69,13 @@ def _parse():
                     help="time LazFormer's attention stack instead: group-sum compression of "
                          "Q/K/V (2048 -> 1152), then per layer the pruned input gathered, "
                          "planned (window = global tail = 128) and attended, 5 layers")
+    ap.add_argument("--pipeline", choices=("auto", "on", "off"), default="auto",
+                    help="on: the next batch's plan and K rotation (double-buffered workspace "
+                         "and rotated keys) run on a second stream while this batch's "
+                         "attention runs; off: the three stages of a step run back to back on "
+                         "one stream; auto (default): on when a serial warmup step takes more "
+                         "than 1 ms (the cross-stream synchronisation costs more than the "
+                         "overlap gains on shorter steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter scaling)")
     return ap.parse_args()
@@ -529,25 +541,52 @@ def main() -> int:
             attn.workspace = attn_ws.data_ptr()
             attn.workspace_bytes = n_ws.value
     handles = []
+    # Consecutive batches are independent: unless --serial, batch i+1's plan
+    # and K rotation run on a second stream (default priority) into the other
+    # half of a double buffer while batch i's attention runs; events order
+    # every reuse of a buffer after the attention that read it.
+    krots, wss, attns = [krot, krot.clone()], [ws, torch.empty_like(ws)], [attn]
+    a2 = _rk.rk_attn_args.from_buffer_copy(attn)
+    a2.k = krots[1].data_ptr()  # the second buffer (cached history keys copied)
+    attns.append(a2)
+    side_stream = torch.cuda.Stream()
+    ready = [torch.cuda.Event() for _ in range(2)]  # plan + rotation of buffer b done
+    freed = [torch.cuda.Event() for _ in range(2)]  # last attention reading buffer b done
+    counter = [0]
+    mode = {"pipelined": False}
 
     def step(ev=None):
+        pipelined = mode["pipelined"]
+        b = counter[0] % 2 if pipelined else 0
+        counter[0] += 1
+        side = side_stream if pipelined else stream
+        spp = C.c_void_p(side.cuda_stream)
         h = C.c_void_p()
-        if ev: ev[0].record(stream)
-        _rk.check(lib.rk_mask_plan(C.byref(batch.c), C.byref(mp), H, C.c_void_p(ws.data_ptr()),
-                                   C.c_size_t(ws.numel()), C.byref(h), sp), "rk_mask_plan")
-        if ev: ev[1].record(stream)
+        if pipelined:
+            side.wait_event(freed[b])
+        if ev: ev[0].record(side)
+        _rk.check(lib.rk_mask_plan(C.byref(batch.c), C.byref(mp), H,
+                                   C.c_void_p(wss[b].data_ptr()), C.c_size_t(wss[b].numel()),
+                                   C.byref(h), spp), "rk_mask_plan")
+        if ev: ev[1].record(side)
         if nq is not None:
             _rk.check(lib.rk_qk_norm_rope(C.byref(batch.c), C.byref(rp_step), C.c_float(1e-6),
                                           None, C.c_void_p(k.data_ptr()),
-                                          C.c_void_p(krot.data_ptr()), dcode, H, d, H * d, d,
-                                          H * d, d, sp), "rk_qk_norm_rope")
+                                          C.c_void_p(krots[b].data_ptr()), dcode, H, d, H * d,
+                                          d, H * d, d, spp), "rk_qk_norm_rope")
         else:
             _rk.check(lib.rk_time_rope(C.byref(batch.c), C.byref(rp_step),
-                                       C.c_void_p(k.data_ptr()), C.c_void_p(krot.data_ptr()),
-                                       dcode, H, d, H * d, d, H * d, d, sp), "rk_time_rope")
-        if ev: ev[2].record(stream)
-        _rk.check(lib.rk_masked_attn_fwd(h, C.byref(attn), sp), "rk_masked_attn_fwd")
+                                       C.c_void_p(k.data_ptr()), C.c_void_p(krots[b].data_ptr()),
+                                       dcode, H, d, H * d, d, H * d, d, spp), "rk_time_rope")
+        if ev: ev[2].record(side)
+        if pipelined:
+            ready[b].record(side)
+            stream.wait_event(ready[b])
         if ev: ev[3].record(stream)
+        _rk.check(lib.rk_masked_attn_fwd(h, C.byref(attns[b]), sp), "rk_masked_attn_fwd")
+        if ev: ev[4].record(stream)
+        if pipelined:
+            freed[b].record(stream)
         handles.append(h)
 
     if args.copy_calibration:
@@ -557,10 +596,20 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    # warmup serially (timed, for the auto choice), then in the chosen mode
+    torch.cuda.synchronize()
+    tw = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    warm_ms = (time.perf_counter() - tw) * 1e3 / max(1, args.warmup)
+    mode["pipelined"] = args.pipeline == "on" or (args.pipeline == "auto" and warm_ms > 1.0)
+    pipelined = mode["pipelined"]
+    if pipelined:
+        for _ in range(2):
+            step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -570,10 +619,11 @@ def main() -> int:
     for h in handles:
         lib.rk_plan_destroy(h)
     ms_step = (t1 - t0) * 1e3 / args.steps
-    # per-stage times: medians over the timed steps
+    # per-stage times: medians over the timed steps (attention: from the
+    # point its inputs are ready to its end, on the stream it runs on)
     plan_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
     rope_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
-    attn_ms = float(np.median([e[2].elapsed_time(e[3]) for e in evs]))
+    attn_ms = float(np.median([e[3].elapsed_time(e[4]) for e in evs]))
 
     T = wl.total_tokens
     esz = 2 if wl.dtype == "bf16" else 4
@@ -612,6 +662,7 @@ def main() -> int:
         "candidates_per_s": round(n_cand / (ms_step * 1e-3), 1) if n_cand else None,
         "stage_ms": {"plan": round(plan_ms, 4), "rope_k": round(rope_ms, 4),
                      "attention": round(attn_ms, 4)},
+        "pipelined": pipelined,
         "stage_hbm_gbs": {"plan": round(plan_alg_bytes / (plan_ms * 1e-3) / 1e9, 1),
                           "rope_k": round(rope_alg_bytes / (rope_ms * 1e-3) / 1e9, 1)},
         "tiles": {"full": stats["full_tiles"], "partial": stats["partial_tiles"],

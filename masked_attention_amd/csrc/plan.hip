@@ -16,6 +16,8 @@
 //   candidate query        : [0, end of static + #real-time events with
 //                            t_j < t_i) plus itself.
 // Tile counts are sums of interval overlaps, so they are exact integers.
+#include <climits>
+
 #include "rk_internal.h"
 
 namespace rk {
@@ -49,6 +51,14 @@ __device__ __forceinline__ int count_lt(const int64_t* __restrict__ ts, int n, i
     if (ts[m] < x) a = m + 1; else b = m;
   }
   return a;
+}
+
+// Sum over the 64 lanes of a wave (integers: order does not matter).
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
 }
 
 // Exclusive scan of one int per thread over a block of blockDim.x (<= 1024)
@@ -182,10 +192,15 @@ __global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
     nnz += cnt > 0;
     nfull += cls == RK_TILE_FULL;
   }
-  // block sums through LDS atomics (integers: order does not matter)
-  atomicAdd(&pairs_s, pairs);
-  atomicAdd(&nnz_s, nnz);
-  atomicAdd(&full_s, nfull);
+  // block sums: wave sums, then one LDS atomic per wave
+  pairs = wave_sum(pairs);
+  nnz = wave_sum(nnz);
+  nfull = wave_sum(nfull);
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(&pairs_s, pairs);
+    atomicAdd(&nnz_s, nnz);
+    atomicAdd(&full_s, nfull);
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     P.qt_nnz[g] = nnz_s;
@@ -215,8 +230,12 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(PlanDev P, int NQ, int6
     if (i < NQ) P.qtile_ptr[i] = carry + ex;
     carry += total;
   }
-  atomicAdd(&tot[0], pairs);
-  atomicAdd(&tot[1], nfull);
+  pairs = wave_sum(pairs);
+  nfull = wave_sum(nfull);
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(&tot[0], pairs);
+    atomicAdd(&tot[1], nfull);
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     P.qtile_ptr[NQ] = carry;
@@ -260,13 +279,22 @@ __device__ __forceinline__ void rank_order(int n, int off, const int* __restrict
     int rank = 0;
     for (int b0 = 0; b0 < n; b0 += 1024) {
       const int nb = min(1024, n - b0);
+      const int nb4 = (nb + 3) & ~3;
       __syncthreads();
-      for (int t = threadIdx.x; t < nb; t += blockDim.x) chunk[t] = nnz[b0 + t];
+      // pad to a multiple of four with a value that never ranks above a
+      // tile (counts are >= 0) and never ties
+      for (int t = threadIdx.x; t < nb4; t += blockDim.x) chunk[t] = t < nb ? nnz[b0 + t] : INT_MIN;
       __syncthreads();
       if (a < n) {
-        for (int t = 0; t < nb; ++t) {
-          const int v = chunk[t];
-          rank += (v > na) || (v == na && b0 + t < a);
+        // four counts per LDS read, several reads in flight
+#pragma unroll 4
+        for (int t = 0; t < nb4; t += 4) {
+          const int4 v = *(const int4*)&chunk[t];
+          const int i0 = b0 + t;
+          rank += (v.x > na) || (v.x == na && i0 < a);
+          rank += (v.y > na) || (v.y == na && i0 + 1 < a);
+          rank += (v.z > na) || (v.z == na && i0 + 2 < a);
+          rank += (v.w > na) || (v.w == na && i0 + 3 < a);
         }
       }
     }
@@ -277,7 +305,7 @@ __device__ __forceinline__ void rank_order(int n, int off, const int* __restrict
 // One block per request: q-tiles ordered by non-empty k-tile count,
 // descending, ties by q-tile index.
 __global__ __launch_bounds__(256) void plan_qsort_kernel(PlanDev P) {
-  __shared__ int chunk[1024];
+  __shared__ __attribute__((aligned(16))) int chunk[1024];
   const ReqMeta m = P.req[blockIdx.x];
   rank_order(m.nqt, m.qt_off, P.qt_nnz + m.qt_off, P.qorder, chunk);
 }
@@ -468,7 +496,7 @@ __global__ __launch_bounds__(256) void plan_kfill_kernel(PlanDev P) {
 
 // One block per request: k-tiles by descending non-empty q-tile count.
 __global__ __launch_bounds__(256) void plan_ksort_kernel(PlanDev P) {
-  __shared__ int chunk[1024];
+  __shared__ __attribute__((aligned(16))) int chunk[1024];
   const ReqMeta m = P.req[blockIdx.x];
   rank_order(m.nkt, m.kt_off, P.kt_nnz + m.kt_off, P.korder, chunk);
 }
