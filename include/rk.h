@@ -118,10 +118,12 @@ enum { RK_TILE_EMPTY = 0, RK_TILE_PARTIAL = 1, RK_TILE_FULL = 2 };
                                          workgroups whose partial softmax results a merge
                                          pass combines (more attention workspace). */
 #define RK_PLAN_BACKWARD 0x4u /* also build the key-major tables rk_masked_attn_bwd needs:
-                                 for every 64-key tile, the ascending list of 128-row query
-                                 tiles with a visible pair (FULL / PARTIAL as in the
-                                 query-major CSR), and a schedule of (key tile, head) work
-                                 items.  Not allowed with RK_QUERY_CANDIDATES_ONLY. */
+                                 for every block of 128 keys (k-tiles 2 kb and 2 kb + 1 of a
+                                 request), the ascending list of 128-row query tiles with a
+                                 visible pair in either k-tile (FULL only when both k-tiles
+                                 exist and are FULL, else PARTIAL), and a schedule of (key
+                                 block, head) work items.  Not allowed with
+                                 RK_QUERY_CANDIDATES_ONLY. */
 
 /* Segment-kind bits of rk_rope_params.kinds: bit k selects kind k. */
 #define RK_KIND_BIT(k) (1u << (k))
@@ -236,12 +238,13 @@ typedef struct rk_plan_info {
                                   each split item, item -1 past the last */
   /* key-major tables, filled for RK_PLAN_BACKWARD plans (offsets 0 and
      num_ksched_slots 0 otherwise) */
-  int64_t num_ktiles;          /* sum over requests of ceil(L_r / 64) */
-  int64_t num_ksched_slots;    /* one slot per (key tile, head) work item, LPT / XCD order */
-  size_t off_kt_ptr;           /* int32 [num_ktiles + 1], CSR row pointers per global key tile */
-  size_t off_qtile_word;       /* int32 [kt_ptr[num_ktiles]]: request-local query tile, ascending,
+  int64_t num_kblocks;         /* sum over requests of ceil(L_r / 128): key blocks of 128 */
+  int64_t num_ksched_slots;    /* one slot per (key block, head) work item, LPT / XCD order */
+  size_t off_kt_ptr;           /* int32 [num_kblocks + 1], CSR row pointers per global key
+                                  block */
+  size_t off_qtile_word;       /* int32 [kt_ptr[num_kblocks]]: request-local query tile, ascending,
                                   | (1 << 31) when the tile is PARTIAL */
-  size_t off_ksched;           /* int32 [num_ksched_slots]: work item = global key tile *
+  size_t off_ksched;           /* int32 [num_ksched_slots]: work item = global key block *
                                   num_heads + head, or -1 */
 } rk_plan_info;
 
@@ -467,8 +470,8 @@ rk_status rk_attn_bwd_workspace_size(const rk_plan* p, const rk_attn_bwd_args* a
  * row softmax: dV = P^T dO; dS = P * (dO V^T - rowsum(dO * O)); dQ =
  * scale * dS K; dK = scale * dS^T Q.  P is recomputed from the forward's
  * log-sum-exp.  Two launches: one per (query tile, head) over the
- * query-major CSR writes dQ, one per (key tile, head) over the key-major
- * CSR writes dK and dV; EMPTY tiles are never read and the per-element mask
+ * query-major CSR writes dQ, one per (key block of 128, head) over the
+ * key-major CSR writes dK and dV; EMPTY tiles are never read and the per-element mask
  * runs on PARTIAL tiles only.  No atomics: results are deterministic.
  * Errors: RK_ERR_INVALID_ARG (plan without RK_PLAN_BACKWARD, num_heads !=
  * the plan's, lse NULL, ...), RK_ERR_UNSUPPORTED, RK_ERR_WORKSPACE_TOO_SMALL,

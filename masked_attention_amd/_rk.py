@@ -96,7 +96,7 @@ class rk_plan_info(C.Structure):
         ("num_work_slots", C.c_int64),
         ("off_work", C.c_size_t),
         ("off_splits", C.c_size_t),
-        ("num_ktiles", C.c_int64),
+        ("num_kblocks", C.c_int64),
         ("num_ksched_slots", C.c_int64),
         ("off_kt_ptr", C.c_size_t),
         ("off_qtile_word", C.c_size_t),

@@ -141,21 +141,22 @@ class Plan:
         return self._view(self.info.off_splits, 4 * n, torch.int32).view(n, 4)
 
     @property
-    def num_ktiles(self) -> int:
-        return int(self.info.num_ktiles)
+    def num_kblocks(self) -> int:
+        """Key blocks of 128 keys (the backward's key-major items)."""
+        return int(self.info.num_kblocks)
 
     def kt_ptr(self) -> Optional[torch.Tensor]:
-        """Key-major CSR row pointers [num_ktiles + 1] (backward plans), or None."""
+        """Key-major CSR row pointers [num_kblocks + 1] (backward plans), or None."""
         if int(self.info.num_ksched_slots) == 0:
             return None
-        return self._view(self.info.off_kt_ptr, self.num_ktiles + 1, torch.int32)
+        return self._view(self.info.off_kt_ptr, self.num_kblocks + 1, torch.int32)
 
     def qtile_word(self) -> Optional[torch.Tensor]:
         """Key-major CSR entries: request-local q-tile | (PARTIAL << 31), or None."""
         ptr = self.kt_ptr()
         if ptr is None:
             return None
-        n = int(ptr[-1].item()) if self.num_ktiles else 0
+        n = int(ptr[-1].item()) if self.num_kblocks else 0
         return self._view(self.info.off_qtile_word, n, torch.int32)
 
     def ksched(self) -> Optional[torch.Tensor]:

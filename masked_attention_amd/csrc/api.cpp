@@ -131,13 +131,13 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
       m.qt_off = (int32_t)std::min<int64_t>(nq, kInt32Max);
       m.nqt = nqt;
       m.nkt = nkt;
-      m.kt_off = (int32_t)std::min<int64_t>(nk, kInt32Max);
+      m.kt_off = (int32_t)std::min<int64_t>(nk, kInt32Max);  // key blocks of 128 keys
       m.tile_off = nt;
       for (int k = 0; k < 4; ++k) m.seg[k] = len;
     }
     weight[r] = (int64_t)nqt * nkt;
     nq += nqt;
-    nk += nkt;
+    nk += nqt;  // the backward's key blocks have the q-tile's 128 positions
     nt += (int64_t)nqt * nkt;
   }
   if (nt >= kInt32Max || nq * (int64_t)H >= kInt32Max || nk * (int64_t)H >= kInt32Max)
@@ -150,11 +150,11 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   // the least-loaded of the eight XCD queues (dense tile count as weight);
   // one for query-tile items, one for key-tile items (backward).
   auto nqt_of = [&](int32_t r) { return (o[r + 1] - o[r] + rk::kTileQ - 1) / rk::kTileQ; };
-  auto nkt_of = [&](int32_t r) { return (o[r + 1] - o[r] + rk::kTileK - 1) / rk::kTileK; };
+  auto nkb_of = nqt_of;  // 128-key blocks of the backward's key-major items
   L->max_queue = place_groups(L->R, H, o, weight, nqt_of, with_tables, &L->groups,
                               &L->queue_start);
   L->slots = L->max_queue * kNumXcd;
-  const int64_t kmax = place_groups(L->R, H, o, weight, nkt_of, with_tables, &L->kgroups,
+  const int64_t kmax = place_groups(L->R, H, o, weight, nkb_of, with_tables, &L->kgroups,
                                     &L->kqueue_start);
   L->kslots = kmax * kNumXcd;
   if (L->slots >= kInt32Max || L->kslots >= kInt32Max) return RK_ERR_UNSUPPORTED;
@@ -166,7 +166,7 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
     L->kt_req.resize(nk);
     for (int32_t r = 0; r < L->R; ++r) {
       for (int32_t i = 0; i < L->req[r].nqt; ++i) L->qt_req[L->req[r].qt_off + i] = r;
-      for (int32_t i = 0; i < L->req[r].nkt; ++i) L->kt_req[L->req[r].kt_off + i] = r;
+      for (int32_t i = 0; i < L->req[r].nqt; ++i) L->kt_req[L->req[r].kt_off + i] = r;
     }
   }
 
@@ -429,7 +429,7 @@ rk_status rk_plan_get_info(const rk_plan* p, rk_plan_info* out) {
   out->off_work = wl ? p->off_work : 0;
   out->off_splits = wl ? p->off_splits : 0;
   const bool bw = (p->flags & RK_PLAN_BACKWARD) != 0;
-  out->num_ktiles = p->NK;
+  out->num_kblocks = p->NK;
   out->num_ksched_slots = bw ? p->kslots : 0;
   out->off_kt_ptr = bw ? p->off_kt_ptr : 0;
   out->off_qtile_word = bw ? p->off_qtile_word : 0;

@@ -20,18 +20,18 @@
 //   Its prologue computes D and lse2 of its rows and stores them for the
 //   second launch.
 //
-// dkdv kernel -- work item (key tile of 64 keys, head) of the key-major
-//   schedule; 4 waves: wave w owns keys 32 (w & 1) .. +31 (their K and V
-//   fragments stay in registers) and query rows 64 (w >> 1) .. +63 of each
-//   visited query tile (Q, dO, lse2, D and row descriptors double-buffered
-//   in LDS).  Per 32-row block and wave, with one key per lane:
+// dkdv kernel -- work item (key block of 128 keys, head) of the key-major
+//   schedule; 4 waves: wave w owns keys 32 w .. +31 of the block (their K
+//   and V fragments stay in registers) and walks all 128 rows of each
+//   visited query tile in four 32-row blocks (Q, dO, lse2, D and row
+//   descriptors double-buffered in LDS).  Per 32-row block and wave, with
+//   one key per lane:
 //     S  (32 q x 32 keys) = Q K^T                4 x mfma
 //     P = exp2(S * scale log2(e) - lse2_q)       (mask on PARTIAL tiles)
 //     dP (32 x 32) = dO V^T                      4 x mfma
 //     dS = P * (dP - D_q)
 //     dV^T (64 x 32) += dO^T P                   4 x mfma (dO^T and Q^T by
 //     dK^T (64 x 32) += Q^T dS                   4 x mfma  transposing reads)
-//   The two waves of a key half add their dK / dV through LDS at the end.
 //
 // With time RoPE, Q and K arrive rotated (a pass into the workspace, or K
 // given rotated); dQ and dK are taken back through the rotation (rotation by
@@ -476,17 +476,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(BwdPlanView 
   const int head = item - kg * A.H;
   const int req = ldc(P.kt_req, kg);
   const ReqMeta m = ldc(P.req, req);
-  const int kt = kg - m.kt_off;
+  const int kb = kg - m.kt_off;  // key block of 128 keys
   const int L = m.len;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kh = wv & 1;   // key half of the tile
-  const int qh = wv >> 1;  // query half of each visited tile
   const int hh = lane >> 5;
   const int li = lane & 31;
-  const int key = kt * kTileK + 32 * kh + li;  // this lane's key (request-local)
+  const int key = kb * 128 + 32 * wv + li;  // this lane's key (request-local)
   const bool kvalid = key < L;
   const int tokk = m.tok_off + key;
   const int tokc = m.tok_off + min(key, L - 1);
@@ -575,9 +573,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(BwdPlanView 
       issue(S1, w_nxt & 0x7fffffff);
       const int qrow0 = (w_cur & 0x7fffffff) * kTileQ;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        dkdv_block(dk0, dk1, dv0, dv1, S0, 64 * qh + 32 * b, kf, vf, w_cur < 0, qrow0, key, li,
-                   hh, c2);
+      for (int b = 0; b < 4; ++b)
+        dkdv_block(dk0, dk1, dv0, dv1, S0, 32 * b, kf, vf, w_cur < 0, qrow0, key, li, hh, c2);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       w_cur = w_nxt;
@@ -587,37 +584,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(BwdPlanView 
       issue(S0, w_nxt & 0x7fffffff);
       const int qrow0 = (w_cur & 0x7fffffff) * kTileQ;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        dkdv_block(dk0, dk1, dv0, dv1, S1, 64 * qh + 32 * b, kf, vf, w_cur < 0, qrow0, key, li,
-                   hh, c2);
+      for (int b = 0; b < 4; ++b)
+        dkdv_block(dk0, dk1, dv0, dv1, S1, 32 * b, kf, vf, w_cur < 0, qrow0, key, li, hh, c2);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       w_cur = w_nxt;
     }
   }
 
-  // The two waves of each key half add their partial dK, dV through LDS
-  // (stage S0 reused: 4 accumulators x 16 floats x 64 lanes = 16 KB per
-  // key half).  The last loop iteration ended with a barrier.
-  float* red = (float*)&S0 + kh * (4 * 16 * 64);
-  if (qh == 1) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      red[(0 * 16 + r) * 64 + lane] = dk0[r];
-      red[(1 * 16 + r) * 64 + lane] = dk1[r];
-      red[(2 * 16 + r) * 64 + lane] = dv0[r];
-      red[(3 * 16 + r) * 64 + lane] = dv1[r];
-    }
-  }
-  __syncthreads();
-  if (qh == 1 || !kvalid) return;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    dk0[r] += red[(0 * 16 + r) * 64 + lane];
-    dk1[r] += red[(1 * 16 + r) * 64 + lane];
-    dv0[r] += red[(2 * 16 + r) * 64 + lane];
-    dv1[r] += red[(3 * 16 + r) * 64 + lane];
-  }
+  if (!kvalid) return;
   const int64_t dt = kUnrot ? ldc(A.ts, tokk) - ldc(A.anchors, req) : 0;
   unrotate_acc(dk0, dk1, dt, A.tab, hh, A.scale, kUnrot);
   store_row((unsigned short*)A.dk + (int64_t)tokk * A.dk_st + (int64_t)head * A.dk_sh, dk0, dk1,

@@ -11,9 +11,9 @@
 //                 row's non-empty key tiles (K, V staged in LDS as fp32);
 //                 also writes D and the log-sum-exp in log2 units for the
 //                 second launch;
-//   dkdv kernel : one 64-thread workgroup per (key tile, head) of the
-//                 key-major schedule, one thread per key; walks the key
-//                 tile's non-empty query tiles in chunks of 32 rows (Q, dO,
+//   dkdv kernel : one 128-thread workgroup per (key block of 128 keys,
+//                 head) of the key-major schedule, one thread per key; walks
+//                 the block's non-empty query tiles in chunks of 32 rows (Q, dO,
 //                 log-sum-exp, D and row descriptors staged in LDS).
 // The per-element mask (visible interval [lo, hi) plus the candidate self
 // link, from the plan's row descriptors) runs on PARTIAL tiles only.  With
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(128) void attn_bwd_ref_dq_kernel(BwdPlanView P, Bwd
 constexpr int kChunk = 32;  // query rows staged at a time by the dK/dV kernel
 
 template <typename T, int D>
-__global__ __launch_bounds__(64) void attn_bwd_ref_dkdv_kernel(BwdPlanView P, BwdLaunch A) {
+__global__ __launch_bounds__(128) void attn_bwd_ref_dkdv_kernel(BwdPlanView P, BwdLaunch A) {
   __shared__ float Qs[kChunk][D];
   __shared__ float Gs[kChunk][D];
   __shared__ float ls[kChunk], ds_[kChunk];
@@ -174,10 +174,10 @@ __global__ __launch_bounds__(64) void attn_bwd_ref_dkdv_kernel(BwdPlanView P, Bw
   const int head = item - kg * A.H;
   const int req = P.kt_req[kg];
   const ReqMeta m = P.req[req];
-  const int kt = kg - m.kt_off;
+  const int kb = kg - m.kt_off;  // key block of 128 keys
   const int L = m.len;
   const int t = threadIdx.x;
-  const int j = kt * kTileK + t;  // this thread's key (request-local)
+  const int j = kb * 128 + t;  // this thread's key (request-local)
   const bool valid = j < L;
   const int tokk = m.tok_off + j;
   if (A.unrot_k && t < D / 2) w[t] = A.tab.w_rev[t];
@@ -267,7 +267,7 @@ hipError_t launch_bwd_ref(const rk_plan* p, const BwdLaunch& a, hipStream_t s) {
                 p->dev.sched,   p->dev.ksched};
   hipLaunchKernelGGL((attn_bwd_ref_dq_kernel<T, D>), dim3((unsigned)p->slots), dim3(128), 0, s, P,
                      a);
-  hipLaunchKernelGGL((attn_bwd_ref_dkdv_kernel<T, D>), dim3((unsigned)p->kslots), dim3(64), 0, s,
+  hipLaunchKernelGGL((attn_bwd_ref_dkdv_kernel<T, D>), dim3((unsigned)p->kslots), dim3(128), 0, s,
                      P, a);
   return hipGetLastError();
 }

@@ -441,18 +441,35 @@ __global__ __launch_bounds__(1024) void plan_work_kernel(PlanDev P, int slots, i
 
 // ---- key-major tables (backward) -------------------------------------
 
-// One block per global k-tile: number of q-tiles with a visible pair in it.
+// Key block kb of a request covers k-tiles 2 kb and 2 kb + 1 (the second
+// may not exist).  A q-tile has a visible pair in the block when it has one
+// in either k-tile; the entry is FULL only when both k-tiles exist and are
+// FULL (every other block entry gets the per-element mask).
+__device__ __forceinline__ bool kblock_nonempty(const PlanDev& P, const ReqMeta& m, int qt,
+                                                int kb) {
+  const int64_t row = m.tile_off + (int64_t)qt * m.nkt;
+  const int k0 = 2 * kb, k1 = 2 * kb + 1;
+  return P.tile_count[row + k0] > 0 || (k1 < m.nkt && P.tile_count[row + k1] > 0);
+}
+__device__ __forceinline__ bool kblock_full(const PlanDev& P, const ReqMeta& m, int qt, int kb) {
+  const int64_t row = m.tile_off + (int64_t)qt * m.nkt;
+  const int k0 = 2 * kb, k1 = 2 * kb + 1;
+  return k1 < m.nkt && P.tile_class[row + k0] == RK_TILE_FULL &&
+         P.tile_class[row + k1] == RK_TILE_FULL;
+}
+
+// One block per global key block: number of q-tiles with a visible pair in it.
 __global__ __launch_bounds__(256) void plan_kcount_kernel(PlanDev P) {
   __shared__ int cnt_s;
   const int g = blockIdx.x;
   const ReqMeta m = P.req[P.kt_req[g]];
-  const int kt = g - m.kt_off;
+  const int kb = g - m.kt_off;
   if (threadIdx.x == 0) cnt_s = 0;
   __syncthreads();
   int c = 0;
-  for (int qt = threadIdx.x; qt < m.nqt; qt += blockDim.x)
-    c += P.tile_count[m.tile_off + (int64_t)qt * m.nkt + kt] > 0;
-  atomicAdd(&cnt_s, c);
+  for (int qt = threadIdx.x; qt < m.nqt; qt += blockDim.x) c += kblock_nonempty(P, m, qt, kb);
+  c = wave_sum(c);
+  if ((threadIdx.x & 63) == 0) atomicAdd(&cnt_s, c);
   __syncthreads();
   if (threadIdx.x == 0) P.kt_nnz[g] = cnt_s;
 }
@@ -472,33 +489,32 @@ __global__ __launch_bounds__(1024) void plan_kscan_kernel(PlanDev P, int NK) {
   if (threadIdx.x == 0) P.kt_ptr[NK] = carry;
 }
 
-// One block per k-tile: ascending list of its non-empty q-tiles, with the
-// PARTIAL bit.
+// One block per key block: ascending list of its non-empty q-tiles, with
+// the PARTIAL bit.
 __global__ __launch_bounds__(256) void plan_kfill_kernel(PlanDev P) {
   __shared__ int smem[32];
   const int g = blockIdx.x;
   const ReqMeta m = P.req[P.kt_req[g]];
-  const int kt = g - m.kt_off;
+  const int kb = g - m.kt_off;
   const int base = P.kt_ptr[g];
   int run = 0;
   for (int q0 = 0; q0 < m.nqt; q0 += blockDim.x) {
     const int qt = q0 + threadIdx.x;
-    const int64_t t_idx = m.tile_off + (int64_t)qt * m.nkt + kt;
-    const int flag = qt < m.nqt && P.tile_count[t_idx] > 0;
+    const int flag = qt < m.nqt && kblock_nonempty(P, m, qt, kb);
     int total;
     const int ex = block_exclusive_scan(flag, smem, &total);
     if (flag)
       P.qtile_word[base + run + ex] =
-          (int)((unsigned)qt | ((unsigned)(P.tile_class[t_idx] == RK_TILE_PARTIAL) << 31));
+          (int)((unsigned)qt | ((unsigned)(!kblock_full(P, m, qt, kb)) << 31));
     run += total;
   }
 }
 
-// One block per request: k-tiles by descending non-empty q-tile count.
+// One block per request: key blocks by descending non-empty q-tile count.
 __global__ __launch_bounds__(256) void plan_ksort_kernel(PlanDev P) {
   __shared__ __attribute__((aligned(16))) int chunk[1024];
   const ReqMeta m = P.req[blockIdx.x];
-  rank_order(m.nkt, m.kt_off, P.kt_nnz + m.kt_off, P.korder, chunk);
+  rank_order(m.nqt, m.kt_off, P.kt_nnz + m.kt_off, P.korder, chunk);
 }
 
 // One thread per key-major launch slot (same XCD mapping as the query-major

@@ -24,7 +24,7 @@ struct ReqMeta {
   int32_t qt_off;    // first global q-tile
   int32_t nqt;       // ceil(L / 128)
   int32_t nkt;       // ceil(L / 64)
-  int32_t kt_off;    // first global k-tile
+  int32_t kt_off;    // first global 128-key block (backward key-major tables)
   int64_t tile_off;  // first tile in tile_class / tile_count
   int32_t seg[4];    // request-local start of PROFILE, HISTORY, REALTIME, CANDIDATE
 };
@@ -96,15 +96,16 @@ struct PlanDev {
   SplitEntry* splits;      // [kSplitTarget]
   int32_t* act_slots;      // [kSplitTarget / 2] active schedule slots, arrival order
   PlanTotals* totals;
-  // key-major tables (plans built with RK_PLAN_BACKWARD)
-  int32_t* kt_req;         // [NK] request of each global k-tile
-  Group* kgroups;          // [G] (request, head) groups of k-tile work items
+  // key-major tables (plans built with RK_PLAN_BACKWARD) over key blocks of
+  // 128 keys (k-tiles 2 kb and 2 kb + 1 of the request)
+  int32_t* kt_req;         // [NK] request of each global key block
+  Group* kgroups;          // [G] (request, head) groups of key-block work items
   int32_t* kqueue_start;   // [kNumXcd + 1]
-  int32_t* kt_nnz;         // [NK] non-empty q-tiles of each k-tile
+  int32_t* kt_nnz;         // [NK] non-empty q-tiles of each key block
   int32_t* kt_ptr;         // [NK + 1] CSR row pointers
   int32_t* qtile_word;     // [NT] CSR entry: request-local qt | (PARTIAL << 31)
-  int32_t* korder;         // [NK] k-tiles of each request by descending kt_nnz
-  int32_t* ksched;         // [kslots] work item = k-tile * H + head, or -1
+  int32_t* korder;         // [NK] key blocks of each request by descending kt_nnz
+  int32_t* ksched;         // [kslots] work item = key block * H + head, or -1
 };
 
 }  // namespace rk
@@ -112,7 +113,7 @@ struct PlanDev {
 struct rk_plan {
   int32_t R, T, H;
   int64_t NQ, NT, G, slots, max_queue;
-  int64_t NK, kslots;       // global k-tiles; k-major launch slots
+  int64_t NK, kslots;       // global 128-key blocks; key-major launch slots
   int64_t grid;             // attention launch size: slots, or slots + kSplitTarget with a work list
   int64_t delay;
   int32_t window;

@@ -1,10 +1,10 @@
 """GPU parity of the masked-attention backward (through the C ABI) against
 the CPU fp64 oracle.
 
-* Key-major tables of a backward plan: for every key tile, the ascending
-  list of query tiles with a visible pair and their PARTIAL bits are
-  bit-exact against the oracle's tile plan read by columns; the key-major
-  schedule covers every (key tile, head) once; the query-major tables are
+* Key-major tables of a backward plan: for every block of 128 keys, the
+  ascending list of query tiles with a visible pair and their PARTIAL bits
+  are bit-exact against the oracle's tile plan read by columns; the
+  key-major schedule covers every (key block, head) once; the query-major tables are
   the same as those of a forward-only plan.
 * Gradients: dQ, dK, dV against the oracle's chain-rule gradients on the
   same inputs (the GPU's own forward O and LSE feed its backward).  fp32:
@@ -63,8 +63,10 @@ def _plan(rk, wl, backward=True, batch=None):
 
 
 def _key_major_ref(wl):
-    """Oracle tile plan read by columns: per global key tile, ascending query
-    tiles with a visible pair, bit 31 set when PARTIAL."""
+    """Oracle tile plan read by columns over key blocks of 128 keys (k-tiles
+    2 kb and 2 kb + 1): per global key block, ascending query tiles with a
+    visible pair in either k-tile, bit 31 set unless both k-tiles exist and
+    are FULL."""
     ptr, words = [0], []
     for r in range(wl.num_requests):
         a, b = wl.request(r)
@@ -74,10 +76,13 @@ def _key_major_ref(wl):
                                             window=wl.window,
                                             static_bidirectional=wl.static_bidirectional,
                                             global_tail=wl.global_tail)
-        for kt in range(cnt.shape[1]):
-            qts = np.nonzero(cnt[:, kt])[0]
+        nkt = cnt.shape[1]
+        for kb in range(-(-(b - a) // 128)):
+            cols = [c for c in (2 * kb, 2 * kb + 1) if c < nkt]
+            qts = np.nonzero(cnt[:, cols].sum(axis=1))[0]
             for qt in qts:
-                words.append(int(qt) | ((1 << 31) if cls[qt, kt] == oracle.PARTIAL else 0))
+                full = len(cols) == 2 and all(cls[qt, c] == oracle.FULL for c in cols)
+                words.append(int(qt) | (0 if full else (1 << 31)))
             ptr.append(ptr[-1] + qts.shape[0])
     w = np.array(words, dtype=np.uint32).view(np.int32) if words else np.zeros(0, np.int32)
     return np.array(ptr, np.int64), w
@@ -93,7 +98,7 @@ def _check_key_major(rk, wl):
     assert np.array_equal(plan.qtile_word().cpu().numpy(), words_ref)
     ks = plan.ksched().cpu().numpy()
     items = np.sort(ks[ks >= 0])
-    assert np.array_equal(items, np.arange(plan.num_ktiles * wl.heads))
+    assert np.array_equal(items, np.arange(plan.num_kblocks * wl.heads))
     # the query-major tables are those of a forward-only plan
     for f in ("tile_class", "tile_count", "qtile_ptr", "ktile_idx", "sched", "row_desc"):
         assert torch.equal(getattr(plan, f)(), getattr(fplan, f)()), f
