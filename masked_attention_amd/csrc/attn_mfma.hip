@@ -29,9 +29,10 @@
 // 8 (e/4) + 4h + e%4); V^T is read in that order with transposing LDS
 // reads, so P never moves between lanes.
 //
-// LDS: two stages of K and V tiles (64 rows x 128 bytes each, unpadded,
-// XOR-swizzled 16-byte chunks), filled by buffer loads that write LDS
-// directly; one barrier per tile.  Q is rotated by time RoPE while it is
+// LDS: three stages of K and V tiles (64 rows x 128 bytes each, unpadded,
+// XOR-swizzled 16-byte chunks, 48 KB per workgroup), filled by buffer loads
+// that write LDS directly two tiles ahead of their use; one barrier per
+// tile.  Q is rotated by time RoPE while it is
 // loaded (fp32, hardware sin/cos on a phase reduced to [-1/2, 1/2]
 // revolution); K arrives pre-rotated.
 #include <hip/hip_bf16.h>
@@ -319,6 +320,24 @@ __device__ __forceinline__ bool row_sees(int kt, bool partial, int lo, int hi, i
   return !partial || (lo < c0 + kTileK && hi > c0) || (self && row >= c0 && row < c0 + kTileK);
 }
 
+// Scores of tile kt from K in global memory: the same bf16 rows in the same
+// product order as from LDS, so the same values.  Rows past the request's
+// end read its last row; the tile is then PARTIAL and they are masked.
+__device__ __forceinline__ void scores_global(f32x16& s0, f32x16& s1, const unsigned short* Kh,
+                                              int64_t k_st, int kt, int L, const bf16x8 (&q)[4],
+                                              const f32x16& negm, int li, int hh) {
+  const int c0 = kt * kTileK;
+  const unsigned short* r0 = Kh + (int64_t)min(c0 + li, L - 1) * k_st + 8 * hh;
+  const unsigned short* r1 = Kh + (int64_t)min(c0 + 32 + li, L - 1) * k_st + 8 * hh;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bf16x8 k0 = as_bf16x8(*(const uint4*)(r0 + 16 * s));
+    const bf16x8 k1 = as_bf16x8(*(const uint4*)(r1 + 16 * s));
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[s], s == 0 ? negm : s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s == 0 ? negm : s1, 0, 0, 0);
+  }
+}
+
 // One 64-key tile for one wave (32 queries): scores, mask, P, O^T += V^T
 // P^T.  kb / vb are the tile's LDS buffers.  Scores are in log2 units when
 // kPreScaled (Q carries scale * log2(e)); otherwise they are raw dot
@@ -332,13 +351,15 @@ __device__ __forceinline__ bool row_sees(int kt, bool partial, int lo, int hi, i
 // key of this tile and its sum is below 2^-32 (P would lose range).  A row
 // with nothing accumulated (O = 0 and l = 0) moves m to the tile's max, up
 // or down; any other row moves m up by the tile's excess over it, with O
-// and l rescaled.
+// and l rescaled.  That path recomputes the tile's scores from K in global
+// memory, so the scores need not stay live once P is packed.
 template <bool kPreScaled>
 __device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, float& mref,
                                           float& lsum, const unsigned short* kb,
                                           const unsigned short* vb, const bf16x8 (&q)[4], int kt,
                                           bool partial, int li, int hh, int lo, int hi, int self,
-                                          int row, float mul) {
+                                          int row, float mul, const unsigned short* Kh,
+                                          int64_t k_st, int L) {
   f32x16 s0, s1;
   scores(s0, s1, kb, q, negm, li, hh);
   if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
@@ -348,6 +369,9 @@ __device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, 
   const bool tiny =
       lsum == 0.f && ts < kMinTileSum && row_sees(kt, partial, lo, hi, self, row);
   if (__any(big || tiny)) {
+    // the scores are recomputed, so they need not stay live past the packing
+    scores_global(s0, s1, Kh, k_st, kt, L, q, negm, li, hh);
+    if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
     float mx = s0[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
@@ -402,6 +426,19 @@ __device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, 
   }
 }
 
+// End of a pipeline step: this wave's copies other than its four most
+// recent (the step's own) have landed and its LDS reads are done
+// (vmcnt(4) lgkmcnt(0)), then the workgroup meets.  A bare barrier: the
+// fence of __syncthreads would also wait for the copies still in flight.
+// The empty asm statements keep the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void step_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0074u);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 constexpr int kThreads = 256;  // 4 waves, 32 query rows each
 
 // kPreScaled: Q is rotated by time RoPE in the kernel and rounded to bf16
@@ -410,10 +447,12 @@ constexpr int kThreads = 256;  // 4 waves, 32 query rows each
 // fp32 scores instead.
 template <bool kPreScaled, bool kNorm>
 __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanView P, AttnLaunch A) {
-  // Two stages of K and V tiles as separate objects, so the compiler can
-  // tell the buffer being filled from the one being read.
-  __shared__ __attribute__((aligned(1024))) unsigned short K0[TILE_ELEMS], K1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) unsigned short V0[TILE_ELEMS], V1[TILE_ELEMS];
+  // Three stages of K and V tiles as separate objects, so the compiler can
+  // tell the buffers being filled from the one being read.
+  __shared__ __attribute__((aligned(1024))) unsigned short K0[TILE_ELEMS], K1[TILE_ELEMS],
+      K2[TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) unsigned short V0[TILE_ELEMS], V1[TILE_ELEMS],
+      V2[TILE_ELEMS];
 
   // a slot runs a whole item (schedule) or a CSR range of one (work list)
   int item, kbeg = 0, kend = -1, part = -1;
@@ -455,13 +494,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   const unsigned kst_b = (unsigned)A.k_st * 2u, vst_b = (unsigned)A.v_st * 2u;
   const CopyMap cm = copy_map(wv, lane, kst_b, vst_b);
   // Each wave zeroes the V rows its own copies fill (rows 16 wv .. +15 of
-  // both stages) and waits for those writes before its first copy: whatever
+  // every stage) and waits for those writes before its first copy: whatever
   // a copy leaves unwritten then stays finite, so a masked key (P = 0) adds
   // exactly 0 to O.  No other wave touches these rows, so no barrier.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     *(uint4*)&V0[(2 * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
     *(uint4*)&V1[(2 * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
+    *(uint4*)&V2[(2 * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
@@ -472,17 +512,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
 
   const int e0 = ldc(P.qtile_ptr, qg) + kbeg;
   const int n = kend >= 0 ? kend - kbeg : ldc(P.qtile_ptr, qg + 1) - e0;
-  // Iteration i computes tile i from one stage while the copies of tile
-  // i+1 fill the other; they land in LDS asynchronously and are waited for
-  // just before the barrier that ends the iteration.  The loop is unrolled
-  // by two so each stage is a distinct LDS object.  The copy issued in the
-  // last iteration re-reads the last tile into the idle stage (no branch
-  // around loads).  An item without key tiles still copies the request's
-  // first tile (in bounds, never read), so the copies are unconditional and
-  // Q's loads can be waited for without waiting for them.
+  // Step i computes tile i from stage i % 3 while the copies of tile i + 2
+  // fill stage (i + 2) % 3 (which held tile i - 1): every copy has two
+  // steps to land.  The wait before the barrier that ends step i leaves the
+  // step's own four copies (two of K, two of V per wave) in flight and
+  // covers those of tile i + 1.  The loop is unrolled by three so each
+  // stage is a distinct LDS object.  Copies past the last tile re-read the
+  // last tile into an idle stage (no branch around loads); an item without
+  // key tiles still copies the request's first tile (in bounds, never
+  // read), so the copies are unconditional and Q's loads can be waited for
+  // without waiting for them.
   const int w_cur0 = n > 0 ? ldc(P.ktile_word, e0) : 0;
-  int w_cur = w_cur0;
+  const int w_cur1 = n > 1 ? ldc(P.ktile_word, e0 + 1) : w_cur0;
+  int w_cur = w_cur0, w_nxt = w_cur1;
   tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_cur0 & 0x7fffffff, L, wv);
+  tile_copy(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_cur1 & 0x7fffffff, L, wv);
   bf16x8 q[4];
   finish_q<kPreScaled, kNorm>(q, qraw, rvalid, anchor, A.tab, hh, kPreScaled ? sl2 : 1.f, A.eps,
                               A.gamma_q);
@@ -492,26 +536,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int it = 0; it < n; it += 2) {
+  const unsigned short* Kh = (const unsigned short*)Kb;
+  for (int it = 0; it < n; it += 3) {
     {
-      const int w_nxt = ldc(P.ktile_word, e0 + min(it + 1, n - 1));
-      tile_copy(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
+      const int w_nn = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
+      tile_copy(K2, V2, cm, Kb, Vb, kst_b, vst_b, w_nn & 0x7fffffff, L, wv);
       tile_step<kPreScaled>(o0, o1, negm, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0,
-                            li, hh, lo, hi, self, row, sl2);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+                            li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+      step_barrier();
       w_cur = w_nxt;
+      w_nxt = w_nn;
     }
     if (it + 1 < n) {
-      const int w_nxt = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
-      tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
+      const int w_nn = ldc(P.ktile_word, e0 + min(it + 3, n - 1));
+      tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_nn & 0x7fffffff, L, wv);
       tile_step<kPreScaled>(o0, o1, negm, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0,
-                            li, hh, lo, hi, self, row, sl2);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+                            li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+      step_barrier();
       w_cur = w_nxt;
+      w_nxt = w_nn;
+    }
+    if (it + 2 < n) {
+      const int w_nn = ldc(P.ktile_word, e0 + min(it + 4, n - 1));
+      tile_copy(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_nn & 0x7fffffff, L, wv);
+      tile_step<kPreScaled>(o0, o1, negm, mref, lsum, K2, V2, q, w_cur & 0x7fffffff, w_cur < 0,
+                            li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+      step_barrier();
+      w_cur = w_nxt;
+      w_nxt = w_nn;
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no copy outlives the item
 
   // ---- epilogue: O = O^T / l; lanes of both halves hold distinct d values
   const float ltot = lsum + __shfl_xor(lsum, 32, 64);
