@@ -122,8 +122,9 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   std::vector<int64_t> weight(L->R);
   for (int32_t r = 0; r < L->R; ++r) {
     const int32_t len = o[r + 1] - o[r];
-    const int32_t nqt = (len + rk::kTileQ - 1) / rk::kTileQ;
-    const int32_t nkt = (len + rk::kTileK - 1) / rk::kTileK;
+    // 64-bit sums: a request may hold up to INT32_MAX tokens
+    const int32_t nqt = (int32_t)(((int64_t)len + rk::kTileQ - 1) / rk::kTileQ);
+    const int32_t nkt = (int32_t)(((int64_t)len + rk::kTileK - 1) / rk::kTileK);
     if (with_tables) {
       ReqMeta& m = L->req[r];
       m.tok_off = o[r];
@@ -149,7 +150,9 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   // Launch schedules: (request, head) groups, heaviest first, each placed on
   // the least-loaded of the eight XCD queues (dense tile count as weight);
   // one for query-tile items, one for key-tile items (backward).
-  auto nqt_of = [&](int32_t r) { return (o[r + 1] - o[r] + rk::kTileQ - 1) / rk::kTileQ; };
+  auto nqt_of = [&](int32_t r) {
+    return (int32_t)(((int64_t)o[r + 1] - o[r] + rk::kTileQ - 1) / rk::kTileQ);
+  };
   auto nkb_of = nqt_of;  // 128-key blocks of the backward's key-major items
   L->max_queue = place_groups(L->R, H, o, weight, nqt_of, with_tables, &L->groups,
                               &L->queue_start);

@@ -92,7 +92,7 @@ rk_status rk_compress_layout(const rk_host_layout* in, int32_t keep, int32_t gro
     const int32_t ell = L < keep ? L : keep;
     const int32_t n_old = L - ell;
     // groups counted back from the kept part: the first (oldest) may be short
-    const int32_t n_groups = (n_old + group - 1) / group;
+    const int32_t n_groups = (int32_t)(((int64_t)n_old + group - 1) / group);
     for (int32_t g = 0; g < n_groups; ++g) {
       const int32_t e = h0 + n_old - (n_groups - 1 - g) * group;
       const int32_t b = e - group > h0 ? e - group : h0;
