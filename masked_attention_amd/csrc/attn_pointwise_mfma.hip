@@ -78,13 +78,60 @@ struct Tabs {
   float time[kMaxTime];
 };
 
-// One key tile for one wave.
+// W = SiLU(S * scale (+ rab)) packed to bf16 as the B operands of the PV
+// product (step s: accumulator block s / 2, registers 8 (s % 2) .. +7).
+// Register r of block mb holds key c0 + 32 mb + 8 (r / 4) + 4 hh + r % 4.
+// kBias: the bias varies over the tile and is read from the tables per
+// score (otherwise it is constant and already in the accumulator);
+// kPartial: masked keys get W = 0 (visible-key bits w0 / w1, shifted by
+// 4 hh).
+template <bool kBias, bool kPartial>
+__device__ __forceinline__ void pw_weights(bf16x8 (&pb)[4], const f32x16& s0, const f32x16& s1,
+                                           float scale, int w0, int w1, const int64_t* tk,
+                                           const Tabs& tab, int c0, int hh, int row, int64_t ti,
+                                           const PwLaunch& A, bool has_pos, bool has_time) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int mb = s >> 1;
+    const f32x16& src = mb ? s1 : s0;
+    const int r0 = 8 * (s & 1);
+    bf16x2_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = r0 + 2 * j + e;
+        float x = src[r] * scale;
+        if (kBias) {
+          const int kk = 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);  // key offset in the tile
+          if (has_pos) {
+            const int dp = row - (c0 + kk);
+            x += tab.pos[min(dp < 0 ? -dp : dp, A.np - 1)];
+          }
+          if (has_time) x += tab.time[time_bucket(ti - tk[kk], A.nt)];
+        }
+        float wv = x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e));
+        if (kPartial) {
+          const unsigned bit = 8u * (unsigned)(r >> 2) + (unsigned)(r & 3);
+          const int m = __builtin_amdgcn_sbfe(mb ? w1 : w0, bit, 1u);  // 0 or -1
+          wv = __int_as_float(__float_as_int(wv) & m);
+        }
+        w[j][e] = (__bf16)wv;
+      }
+    }
+    __builtin_memcpy(&pb[s], w, 16);
+  }
+}
+
+// One key tile for one wave.  seg_sorted: the tile's keys all lie in one
+// segment whose timestamps are non-decreasing (HISTORY or REALTIME), so
+// their time range is given by the first and the last key.
 __device__ __forceinline__ void pw_tile(f32x16& o0, f32x16& o1, const unsigned short* kb,
                                         const unsigned short* vb, const int64_t* tk,
                                         const Tabs& tab, const bf16x8 (&q)[4], int kt, bool partial,
                                         int L, int li, int hh, int lo, int hi, int self, int row,
                                         int64_t ti, const PwLaunch& A, bool has_pos,
-                                        bool has_time) {
+                                        bool has_time, const ReqMeta& m) {
   const int c0 = kt * kTileK;
   const int nr = min(L - c0, kTileK);  // keys of the tile inside the request
   // ---- is the bias constant over this tile for the lane's row?
@@ -96,10 +143,19 @@ __device__ __forceinline__ void pw_tile(f32x16& o0, f32x16& o1, const unsigned s
     else fast = false;
   }
   if (has_time) {
-    const int lane = threadIdx.x & 63;
-    const int64_t t = tk[lane];
-    const int64_t tmin = wave_min64(lane < nr ? t : INT64_MAX);
-    const int64_t tmax = wave_max64(lane < nr ? t : INT64_MIN);
+    const int c1 = c0 + nr;
+    const bool seg_sorted = (c0 >= m.seg[RK_SEG_HISTORY] && c1 <= m.seg[RK_SEG_REALTIME]) ||
+                            (c0 >= m.seg[RK_SEG_REALTIME] && c1 <= m.seg[RK_SEG_CANDIDATE]);
+    int64_t tmin, tmax;
+    if (seg_sorted) {
+      tmin = tk[0];
+      tmax = tk[nr - 1];
+    } else {
+      const int lane = threadIdx.x & 63;
+      const int64_t t = tk[lane];
+      tmin = wave_min64(lane < nr ? t : INT64_MAX);
+      tmax = wave_max64(lane < nr ? t : INT64_MIN);
+    }
     const int64_t a = ti - tmax, b = ti - tmin;  // t_i - t_j over the tile
     if (a >= 0 || b <= 0) {
       const int b1 = time_bucket(a, A.nt), b2 = time_bucket(b, A.nt);
@@ -125,41 +181,29 @@ __device__ __forceinline__ void pw_tile(f32x16& o0, f32x16& o1, const unsigned s
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s1, 0, 0, 0);
   }
 
-  // ---- W = SiLU(S * scale (+ rab)), masked keys 0; register r of block
-  // mb holds key c0 + 32 mb + 8 (r / 4) + 4 hh + r % 4
-  uint64_t vis = ~0ull;
-  if (partial) vis = tile_vis_bits(c0, lo, hi, self, row);
-  vis >>= 4 * hh;
-  const int w0 = (int)(unsigned)vis, w1 = (int)(unsigned)(vis >> 32);
+  // ---- W = SiLU(S * scale (+ rab)), masked keys 0; one code path per
+  // (bias per score, mask) case, chosen per tile and wave
   bf16x8 pb[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int mb = s >> 1;
-    const f32x16& src = mb ? s1 : s0;
-    const int r0 = 8 * (s & 1);
-    bf16x2_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int r = r0 + 2 * j + e;
-        float x = src[r] * A.scale;
-        if (!uniform) {
-          const int kk = 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);  // key offset in the tile
-          if (has_pos) {
-            const int dp = row - (c0 + kk);
-            x += tab.pos[min(dp < 0 ? -dp : dp, A.np - 1)];
-          }
-          if (has_time) x += tab.time[time_bucket(ti - tk[kk], A.nt)];
-        }
-        float wv = x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e));
-        const unsigned bit = 8u * (unsigned)(r >> 2) + (unsigned)(r & 3);
-        const int m = __builtin_amdgcn_sbfe(mb ? w1 : w0, bit, 1u);  // 0 or -1
-        wv = __int_as_float(__float_as_int(wv) & m);
-        w[j][e] = (__bf16)wv;
-      }
-    }
-    __builtin_memcpy(&pb[s], w, 16);
+  int w0 = -1, w1 = -1;
+  if (partial) {
+    const uint64_t vis = tile_vis_bits(c0, lo, hi, self, row) >> (4 * hh);
+    w0 = (int)(unsigned)vis;
+    w1 = (int)(unsigned)(vis >> 32);
+  }
+  if (uniform) {
+    if (partial)
+      pw_weights<false, true>(pb, s0, s1, A.scale, w0, w1, tk, tab, c0, hh, row, ti, A, has_pos,
+                              has_time);
+    else
+      pw_weights<false, false>(pb, s0, s1, A.scale, w0, w1, tk, tab, c0, hh, row, ti, A, has_pos,
+                               has_time);
+  } else {
+    if (partial)
+      pw_weights<true, true>(pb, s0, s1, A.scale, w0, w1, tk, tab, c0, hh, row, ti, A, has_pos,
+                             has_time);
+    else
+      pw_weights<true, false>(pb, s0, s1, A.scale, w0, w1, tk, tab, c0, hh, row, ti, A, has_pos,
+                              has_time);
   }
 
   // ---- O^T += V^T W^T (V^T by transposing reads, keys in register order)
@@ -189,7 +233,7 @@ __device__ __forceinline__ void pw_tile(f32x16& o0, f32x16& o1, const unsigned s
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void pw_mfma_bf16_d64_kernel(PwView P, PwLaunch A) {
+__global__ __launch_bounds__(kThreads, 3) void pw_mfma_bf16_d64_kernel(PwView P, PwLaunch A) {
   __shared__ __attribute__((aligned(1024))) unsigned short K0[TILE_ELEMS], K1[TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) unsigned short V0[TILE_ELEMS], V1[TILE_ELEMS];
   // key timestamps of each stage: 64 used; dword copies of 256 bytes fill
@@ -297,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 2) void pw_mfma_bf16_d64_kernel(PwView P,
       const int w_nxt = ldc(P.ktile_word, e0 + min(it + 1, n - 1));
       issue(K1, V1, T1, w_nxt & 0x7fffffff);
       pw_tile(o0, o1, K0, V0, T0, tab, q, w_cur & 0x7fffffff, w_cur < 0, L, li, hh, lo, hi,
-              self, row, ti, A, has_pos, has_time);
+              self, row, ti, A, has_pos, has_time, m);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       w_cur = w_nxt;
@@ -306,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 2) void pw_mfma_bf16_d64_kernel(PwView P,
       const int w_nxt = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
       issue(K0, V0, T0, w_nxt & 0x7fffffff);
       pw_tile(o0, o1, K1, V1, T1, tab, q, w_cur & 0x7fffffff, w_cur < 0, L, li, hh, lo, hi,
-              self, row, ti, A, has_pos, has_time);
+              self, row, ti, A, has_pos, has_time, m);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       w_cur = w_nxt;
