@@ -513,8 +513,13 @@ typedef struct rk_pointwise_args {
   const float* time_bias;    /* device fp32 [num_time_buckets] or NULL */
 } rk_pointwise_args;
 
-/* Errors: RK_ERR_INVALID_ARG (including num_heads != the plan's, a
- * RK_QUERY_CANDIDATES_ONLY plan), RK_ERR_UNSUPPORTED, RK_ERR_HIP. */
+/* With a RK_QUERY_CANDIDATES_ONLY plan (the serving call of HSTU App. H:
+ * candidates against the cached history) only the O rows of query tiles that
+ * hold a CANDIDATE row are written, each tile as in the full call; other rows
+ * are left as they were.  The key range of a tile is never split (there is no
+ * softmax state to merge).
+ * Errors: RK_ERR_INVALID_ARG (including num_heads != the plan's),
+ * RK_ERR_UNSUPPORTED, RK_ERR_HIP. */
 rk_status rk_pointwise_attn_fwd(const rk_plan* p, const rk_pointwise_args* a, void* stream);
 
 /* ---- LazFormer pre-passes (section 2.3): history compression and per-layer

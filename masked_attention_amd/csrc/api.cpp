@@ -669,7 +669,6 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
 
 rk_status rk_pointwise_attn_fwd(const rk_plan* p, const rk_pointwise_args* a, void* stream) {
   if (!p || !a || a->struct_size < sizeof(rk_pointwise_args)) return RK_ERR_INVALID_ARG;
-  if (p->flags & RK_QUERY_CANDIDATES_ONLY) return RK_ERR_INVALID_ARG;
   if (!valid_dtype(a->dtype) || a->num_heads != p->H) return RK_ERR_INVALID_ARG;
   if (a->d_head != 32 && a->d_head != 64 && a->d_head != 128) return RK_ERR_UNSUPPORTED;
   if (a->flags & ~RK_ATTN_REFERENCE_KERNEL) return RK_ERR_INVALID_ARG;

@@ -141,14 +141,56 @@ def test_pointwise_workload_sampled(rk):
         _check("bf16", o[toks, h].float().cpu().numpy().astype(np.float64), ref)
 
 
-def test_pointwise_rejects_candidates_only_plan(rk):
-    from masked_attention_amd import _rk
-    wl = make_custom([[(HISTORY, np.arange(NOW - 300, NOW, 3, dtype=np.int64)),
-                       (CANDIDATE, np.full(4, NOW, np.int64))]], heads=1, d_head=64,
-                     dtype="bf16", seed=2)
+def _candidate_tile_rows(wl):
+    """Rows of the query tiles (128 rows, request-local) holding a CANDIDATE row."""
+    rows = []
+    offs = wl.req_offsets
+    for r in range(offs.shape[0] - 1):
+        a, b = int(offs[r]), int(offs[r + 1])
+        cand = np.nonzero(wl.seg_kind[a:b] == CANDIDATE)[0]
+        for qt in sorted({int(c) // 128 for c in cand}):
+            rows.extend(range(a + 128 * qt, min(b, a + 128 * qt + 128)))
+    return np.asarray(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("reference", [False, True], ids=["mfma", "ref"])
+def test_pointwise_candidates_only(rk, reference):
+    """Serving call (HSTU App. H): a candidates-only plan writes the rows of
+    the query tiles holding candidates, bit-identical to the full call (same
+    tiles in the same order), and leaves every other row as it was; the
+    candidate rows match the oracle."""
+    rng = np.random.default_rng(31)
+    reqs = [[(HISTORY, history_span(rng, n_hist, NOW - 60)),
+             (CANDIDATE, np.full(n_cand, NOW, np.int64))]
+            for n_hist, n_cand in ((900, 150), (300, 0), (1500, 40), (64, 64))]
+    wl = make_custom(reqs, heads=2, d_head=64, dtype="bf16", seed=31, delay=3600)
+    pb = (rng.standard_normal(64) * 0.3).astype(np.float32)
+    tb = (rng.standard_normal(32) * 0.3).astype(np.float32)
+    bias = dict(pos_bias=torch.from_numpy(pb).cuda(), time_bias=torch.from_numpy(tb).cuda())
     batch = rk.Batch.from_workload(wl)
-    plan = rk.Plan(batch, num_heads=1, candidates_only=True)
-    q = torch.from_numpy(wl.q).cuda().to(torch.bfloat16)
-    with pytest.raises(_rk.RkError) as e:
-        rk.rk_pointwise_attn_fwd(plan, q, q, q)
-    assert e.value.status == _rk.RK_ERR_INVALID_ARG
+    full = rk.Plan(batch, delay=wl.delay, num_heads=2)
+    cand = rk.Plan(batch, delay=wl.delay, num_heads=2, candidates_only=True)
+    q, k, v = (torch.from_numpy(a).cuda().to(torch.bfloat16) for a in (wl.q, wl.k, wl.v))
+    sentinel = 0x7FC1  # bf16 bits of a NaN no kernel writes
+    outs = []
+    for plan in (full, cand):
+        o = torch.full(q.shape, sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        rk.rk_pointwise_attn_fwd(plan, q, k, v, out=o, scale=0.125, reference=reference, **bias)
+        outs.append(o)
+    torch.cuda.synchronize()
+    rows = _candidate_tile_rows(wl)
+    other = np.setdiff1d(np.arange(wl.total_tokens), rows)
+    o_full, o_c = (o.view(torch.int16) for o in outs)
+    rt, ot = torch.from_numpy(rows).cuda(), torch.from_numpy(other).cuda()
+    assert torch.equal(o_c[rt], o_full[rt])
+    assert bool((o_c[ot] == sentinel).all())
+    cand_rows = np.nonzero(wl.seg_kind == CANDIDATE)[0]
+    for h in range(2):
+        ref = oracle.pointwise_attention_rows(wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q,
+                                              wl.k, wl.v, cand_rows, h, delay=wl.delay, window=0,
+                                              static_bidirectional=False, scale=0.125,
+                                              pos_bias=pb.astype(np.float64),
+                                              time_bias=tb.astype(np.float64))
+        _check("bf16", outs[1][cand_rows, h].float().cpu().numpy().astype(np.float64), ref)
+    full.close()
+    cand.close()
