@@ -556,6 +556,50 @@ def attention_backward_sampled(req_offsets, seg_kind, timestamps, q, k, v, do, *
     return dq, dk, dv
 
 
+def qk_rmsnorm_backward(x: np.ndarray, gamma: Optional[np.ndarray], eps: float,
+                        g: np.ndarray) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """Gradients through QK Norm (qk_rmsnorm; TM20K section 2, SORT section
+    3.3.2), float64.  For y = x * r * gamma with r = 1 / sqrt(mean(x^2) +
+    eps) over the last axis (d) and upstream g = dLoss/dy, the chain rule
+    (dr/dx_k = -r^3 x_k / d) gives
+      dx = r * gamma * g - x * r^3 * sum_j(gamma_j g_j x_j) / d,
+      dgamma = sum over every row of g * x * r   (None when gamma is None).
+    """
+    x = np.asarray(x, np.float64)
+    g = np.asarray(g, np.float64)
+    d = x.shape[-1]
+    gam = np.ones(d) if gamma is None else np.asarray(gamma, np.float64)
+    r = 1.0 / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    t = (gam * g * x).sum(axis=-1, keepdims=True)
+    dx = r * gam * g - x * r ** 3 * t / d
+    dgamma = None if gamma is None else (g * x * r).reshape(-1, d).sum(axis=0)
+    return dx, dgamma
+
+
+def attention_backward_qk_norm(req_offsets, seg_kind, timestamps, q, k, v, do, *,
+                               qk_norm: Dict, delay: int, window: int,
+                               static_bidirectional: bool, rope=None, rope_times=None,
+                               scale=None, global_tail: int = 0):
+    """Gradients of the attention forward with QK Norm (attention_forward with
+    qk_norm = dict(eps, gamma_q, gamma_k)): the masked attention backward
+    at the normalised q, k (attention_backward, which also takes the
+    gradients back through the rotation), then qk_rmsnorm_backward.  The
+    gains are shared by every head, so their gradients sum over tokens and
+    heads.  Returns (dq, dk, dv, dgamma_q, dgamma_k), float64."""
+    eps = qk_norm["eps"]
+    gq, gk = qk_norm.get("gamma_q"), qk_norm.get("gamma_k")
+    qn = qk_rmsnorm(q, gq, eps)
+    kn = qk_rmsnorm(k, gk, eps)
+    dqn, dkn, dv = attention_backward(req_offsets, seg_kind, timestamps, qn, kn, v, do,
+                                      delay=delay, window=window,
+                                      static_bidirectional=static_bidirectional, rope=rope,
+                                      rope_times=rope_times, scale=scale,
+                                      global_tail=global_tail)
+    dq, dgq = qk_rmsnorm_backward(q, gq, eps, dqn)
+    dk, dgk = qk_rmsnorm_backward(k, gk, eps, dkn)
+    return dq, dk, dv, dgq, dgk
+
+
 # ---------------------------------------------------------------------------
 # LazFormer history compression and per-layer pruning (section 2.3)
 # ---------------------------------------------------------------------------
