@@ -55,8 +55,9 @@ def _parse():
                          "step plans the candidates' query tiles only, rotates the candidate "
                          "keys into the key cache and runs the attention for those tiles")
     ap.add_argument("--qk-norm", action="store_true",
-                    help="forward with QK Norm (RMSNorm of Q and K rows before the rotation, "
-                         "gains 1): K normalised in its rotation pass, Q while staged")
+                    help="with QK Norm (RMSNorm of Q and K rows before the rotation): forward "
+                         "with gains 1 (K normalised in its rotation pass, Q while staged); "
+                         "with --backward, random gains and their gradients")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward step instead: the forward runs once (untimed) for "
                          "O and LSE; each step plans with the key-major tables and runs "
@@ -203,7 +204,13 @@ def backward_main(args) -> int:
               num_heads=H, backward=True, workspace=ws)
     plan = rk.Plan(batch, **mk)
     pairs = plan.stats()["visible_pairs"]
-    o, lse = rk.rk_masked_attn_fwd(plan, q, k, v, rope=rope, want_lse=True)
+    norm = None
+    if args.qk_norm:
+        # QK Norm with gains (their gradients are part of the step)
+        g = torch.Generator().manual_seed(11)
+        norm = dict(eps=1e-6, gamma_q=(0.5 + torch.rand(d, generator=g)).to(dev),
+                    gamma_k=(0.5 + torch.rand(d, generator=g)).to(dev))
+    o, lse = rk.rk_masked_attn_fwd(plan, q, k, v, rope=rope, want_lse=True, qk_norm=norm)
     dq, dk, dv = (torch.empty_like(x) for x in (q, k, v))
     bws = None
     stream = torch.cuda.current_stream()
@@ -213,7 +220,7 @@ def backward_main(args) -> int:
         p = rk.Plan(batch, **mk)
         if ev: ev[1].record(stream)
         rk.rk_masked_attn_bwd(p, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, rope=rope,
-                              workspace=bws)
+                              workspace=bws, qk_norm=norm)
         if ev: ev[2].record(stream)
         return p
 
@@ -222,6 +229,11 @@ def backward_main(args) -> int:
     import ctypes as C
     a = rk.binding._bwd_args(q, k, v, o, do, lse, dq, dk, dv, 0.0,
                              rk.binding.rope_params(**rope), False, False, None)
+    if norm is not None:
+        nq = rk.binding.qk_norm_params(**norm)
+        a.qk_norm = C.cast(C.pointer(nq), C.c_void_p)
+        dgs = torch.empty(2 * d, dtype=torch.float32, device=dev)
+        a.dgamma_q, a.dgamma_k = dgs.data_ptr(), dgs[d:].data_ptr()
     n = C.c_size_t()
     _rk.check(_rk.lib().rk_attn_bwd_workspace_size(plan.handle, C.byref(a), C.byref(n)), "ws")
     bws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
@@ -254,13 +266,16 @@ def backward_main(args) -> int:
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded generator with the workload's shapes and time law)",
-        "config": {"workload": wl.name + " backward", "requests": wl.num_requests,
+        "config": {"workload": wl.name + " backward" + (" qk-norm" if args.qk_norm else ""),
+                   "requests": wl.num_requests,
                    "tokens": wl.total_tokens, "heads": H, "d_head": d,
                    "visible_pairs_per_head": pairs},
         "pct_bf16_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "stage_ms": {"plan": round(plan_ms, 4), "backward": round(bwd_ms, 4)},
-        "roofline": {"bound": "mfma", "kernel": "rk_masked_attn_bwd (Q/K rotation, dq and dkdv "
-                     "kernels)", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": "rk_masked_attn_bwd (Q/K rotation" + (
+                     " with QK Norm, dq and dkdv kernels, QK Norm backward)" if args.qk_norm
+                     else ", dq and dkdv kernels)"), "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
         "cpu_baseline": None,

@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define RK_ABI_VERSION 3
+#define RK_ABI_VERSION 4
 
 typedef enum rk_status {
   RK_OK = 0,
@@ -451,14 +451,19 @@ typedef struct rk_attn_bwd_args {
   const rk_rope_params* rope;
   void* workspace;
   size_t workspace_bytes;
-  const rk_qk_norm_params* qk_norm; /* must be NULL: the backward through QK Norm is not built
-                                       (RK_ERR_UNSUPPORTED) */
+  const rk_qk_norm_params* qk_norm; /* NULL, or the forward's QK Norm: the gradients are taken
+                                       back through it (not with RK_ATTN_K_PREROTATED) */
+  float* dgamma_q;  /* with qk_norm and its gamma_q: device fp32 [d_head], dLoss/dgamma_q
+                       summed over tokens and heads; else ignored */
+  float* dgamma_k;  /* likewise for gamma_k */
 } rk_attn_bwd_args;
 
 /* Workspace bytes rk_masked_attn_bwd needs for `a` on plan `p` (host only):
  * rowsum(dO * O) and the log2-unit LSE ([num_heads][total_tokens] fp32
- * each), plus, with rope, the rotated Q and (unless RK_ATTN_K_PREROTATED)
- * the rotated K ([total_tokens][num_heads][d_head] of dtype each). */
+ * each), plus, with rope or qk_norm, the rotated (normalised) Q and, unless
+ * RK_ATTN_K_PREROTATED, K ([total_tokens][num_heads][d_head] of dtype
+ * each), plus, with a QK Norm gain, the gain gradients' partial sums
+ * (d_head fp32 per 256 rows of total_tokens * num_heads, per gain). */
 rk_status rk_attn_bwd_workspace_size(const rk_plan* p, const rk_attn_bwd_args* a, size_t* bytes);
 
 /*
@@ -472,9 +477,17 @@ rk_status rk_attn_bwd_workspace_size(const rk_plan* p, const rk_attn_bwd_args* a
  * log-sum-exp.  Two launches: one per (query tile, head) over the
  * query-major CSR writes dQ, one per (key block of 128, head) over the
  * key-major CSR writes dK and dV; EMPTY tiles are never read and the per-element mask
- * runs on PARTIAL tiles only.  No atomics: results are deterministic.
+ * runs on PARTIAL tiles only.  With qk_norm (TM20K section 2: RMSNorm of the
+ * rows of Q and K before the rotation, y = x * r * gamma, r = 1 /
+ * sqrt(mean(x^2) + eps)) the two launches run on the normalised rows and a
+ * pass per operand takes their gradients g back through the norm in place:
+ * dx = r * gamma * g - x * r^3 * sum_j(gamma_j g_j x_j) / d_head, and
+ * dgamma = sum over tokens and heads of g * x * r (bf16 operands: g is
+ * rounded to bf16 once before that pass).  No atomics: results are
+ * deterministic.
  * Errors: RK_ERR_INVALID_ARG (plan without RK_PLAN_BACKWARD, num_heads !=
- * the plan's, lse NULL, ...), RK_ERR_UNSUPPORTED, RK_ERR_WORKSPACE_TOO_SMALL,
+ * the plan's, lse NULL, a gain without its gradient pointer, qk_norm with
+ * RK_ATTN_K_PREROTATED, ...), RK_ERR_UNSUPPORTED, RK_ERR_WORKSPACE_TOO_SMALL,
  * RK_ERR_HIP.
  */
 rk_status rk_masked_attn_bwd(const rk_plan* p, const rk_attn_bwd_args* a, void* stream);

@@ -31,7 +31,7 @@ RK_QUERY_CANDIDATES_ONLY = 0x2
 RK_PLAN_BACKWARD = 0x4
 RK_ATTN_REFERENCE_KERNEL = 0x1
 RK_ATTN_K_PREROTATED = 0x2
-RK_ABI_VERSION = 3
+RK_ABI_VERSION = 4
 RK_SPLIT_SLOTS = 768  # extra work-list slots of a candidates-only plan
 
 
@@ -174,6 +174,8 @@ class rk_attn_bwd_args(C.Structure):
         ("workspace", C.c_void_p),
         ("workspace_bytes", C.c_size_t),
         ("qk_norm", C.c_void_p),
+        ("dgamma_q", C.c_void_p),
+        ("dgamma_k", C.c_void_p),
     ]
 
 

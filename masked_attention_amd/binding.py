@@ -350,16 +350,31 @@ def rk_masked_attn_bwd(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Te
                        dv: Optional[torch.Tensor] = None, scale: float = 0.0,
                        rope: Optional[dict] = None, reference: bool = False,
                        k_prerotated: bool = False, workspace: Optional[torch.Tensor] = None,
+                       qk_norm: Optional[dict] = None,
                        stream: Optional[torch.cuda.Stream] = None):
     """Gradients (dq, dk, dv) of the masked attention forward over `plan`
     (built with backward=True), given the forward's o and lse and the
-    upstream gradient do.  q, k, v, scale, rope and k_prerotated are those
-    of the forward call."""
+    upstream gradient do.  q, k, v, scale, rope, k_prerotated and qk_norm
+    (dict(eps=..., gamma_q=tensor or None, gamma_k=tensor or None)) are
+    those of the forward call.  With qk_norm the result is (dq, dk, dv,
+    dgamma_q, dgamma_k), the gains' gradients as fp32 [d] tensors (None for
+    an absent gain)."""
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
     rp = rope_params(**rope) if rope is not None else None
     a = _bwd_args(q, k, v, o, do, lse, dq, dk, dv, scale, rp, reference, k_prerotated, workspace)
+    nq, dgq, dgk = None, None, None
+    if qk_norm is not None:
+        nq = qk_norm_params(**qk_norm)
+        a.qk_norm = C.cast(C.pointer(nq), C.c_void_p)
+        d = q.shape[2]
+        if qk_norm.get("gamma_q") is not None:
+            dgq = torch.empty(d, dtype=torch.float32, device=q.device)
+            a.dgamma_q = dgq.data_ptr()
+        if qk_norm.get("gamma_k") is not None:
+            dgk = torch.empty(d, dtype=torch.float32, device=q.device)
+            a.dgamma_k = dgk.data_ptr()
     n = C.c_size_t()
     check(lib().rk_attn_bwd_workspace_size(plan.handle, C.byref(a), C.byref(n)),
           "rk_attn_bwd_workspace_size")
@@ -369,6 +384,8 @@ def rk_masked_attn_bwd(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Te
         a.workspace_bytes = n.value
     check(lib().rk_masked_attn_bwd(plan.handle, C.byref(a), _stream(stream)), "rk_masked_attn_bwd")
     dq._rk_workspace = workspace  # type: ignore[attr-defined]
+    if qk_norm is not None:
+        return dq, dk, dv, dgq, dgk
     return dq, dk, dv
 
 

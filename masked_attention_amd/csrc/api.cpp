@@ -727,7 +727,14 @@ rk_status check_bwd(const rk_plan* p, const rk_attn_bwd_args* a) {
   if (a->d_head != 32 && a->d_head != 64 && a->d_head != 128) return RK_ERR_UNSUPPORTED;
   if (a->flags & ~(RK_ATTN_REFERENCE_KERNEL | RK_ATTN_K_PREROTATED)) return RK_ERR_INVALID_ARG;
   if ((a->flags & RK_ATTN_K_PREROTATED) && !a->rope) return RK_ERR_INVALID_ARG;
-  if (a->qk_norm) return RK_ERR_UNSUPPORTED;  // the backward through QK Norm is not built
+  if (a->qk_norm) {
+    rk_status s = check_norm(a->qk_norm, a->d_head);
+    if (s != RK_OK) return s;
+    // the gradient of K is taken back through the norm, so K comes as is
+    if (a->flags & RK_ATTN_K_PREROTATED) return RK_ERR_INVALID_ARG;
+    if ((a->qk_norm->gamma_q && !a->dgamma_q) || (a->qk_norm->gamma_k && !a->dgamma_k))
+      return RK_ERR_INVALID_ARG;
+  }
   if (p->T > 0 && (!a->q || !a->k || !a->v || !a->o || !a->d_o || !a->lse || !a->dq || !a->dk ||
                    !a->dv))
     return RK_ERR_INVALID_ARG;
@@ -765,9 +772,10 @@ bool bwd_mfma_aligned(const rk_attn_bwd_args* a, bool q_in_ws, bool k_in_ws) {
   return ok;
 }
 
-// Backward workspace: [rowsum(dO*O) H*T fp32][lse2 H*T fp32][rotated Q][rotated K].
+// Backward workspace: [rowsum(dO*O) H*T fp32][lse2 H*T fp32][rotated
+// (normalised) Q][rotated (normalised) K][gain gradient partials of Q][of K].
 struct BwdWs {
-  size_t dsum = 0, lse2 = 0, q = 0, k = 0, total = 0;
+  size_t dsum = 0, lse2 = 0, q = 0, k = 0, pq = 0, pk = 0, total = 0;
 };
 
 BwdWs bwd_ws(const rk_plan* p, const rk_attn_bwd_args* a) {
@@ -779,7 +787,7 @@ BwdWs bwd_ws(const rk_plan* p, const rk_attn_bwd_args* a) {
   off = align_up(off + ht * sizeof(float));
   w.lse2 = off;
   off = align_up(off + ht * sizeof(float));
-  if (a->rope) {
+  if (a->rope || a->qk_norm) {
     w.q = off;
     off = align_up(off + rows);
     if (!(a->flags & RK_ATTN_K_PREROTATED)) {
@@ -787,8 +795,39 @@ BwdWs bwd_ws(const rk_plan* p, const rk_attn_bwd_args* a) {
       off = align_up(off + rows);
     }
   }
+  if (a->qk_norm) {
+    const size_t part = (size_t)rk::norm_bwd_blocks((int64_t)ht) * (size_t)a->d_head * sizeof(float);
+    if (a->qk_norm->gamma_q) {
+      w.pq = off;
+      off = align_up(off + part);
+    }
+    if (a->qk_norm->gamma_k) {
+      w.pk = off;
+      off = align_up(off + part);
+    }
+  }
   w.total = off;
   return w;
+}
+
+// The pass that takes dQ or dK back through QK Norm (in place).
+hipError_t norm_bwd(const rk_plan* p, const rk_attn_bwd_args* a, const void* x, int64_t x_st,
+                    int64_t x_sh, void* g, int64_t g_st, int64_t g_sh, const float* gamma,
+                    float* partial, float* dgamma, hipStream_t s) {
+  rk::NormBwdArgs n;
+  n.x = x;
+  n.x_st = x_st;
+  n.x_sh = x_sh;
+  n.g = g;
+  n.g_st = g_st;
+  n.g_sh = g_sh;
+  n.gamma = gamma;
+  n.eps = a->qk_norm->eps;
+  n.rows = (int64_t)p->T * a->num_heads;
+  n.H = a->num_heads;
+  n.partial = gamma ? partial : nullptr;
+  n.dgamma = gamma ? dgamma : nullptr;
+  return rk::launch_norm_bwd(n, a->dtype, a->d_head, s);
 }
 
 }  // namespace
@@ -805,13 +844,29 @@ rk_status rk_masked_attn_bwd(const rk_plan* p, const rk_attn_bwd_args* a, void* 
   rk_status st = check_bwd(p, a);
   if (st != RK_OK) return st;
   const BwdWs w = bwd_ws(p, a);
-  if (p->T == 0) return RK_OK;  // nothing to write
+  hipStream_t s = (hipStream_t)stream;
+  if (p->T == 0) {
+    // nothing to write but the gain gradients, which are zero
+    if (a->qk_norm) {
+      hipError_t e = norm_bwd(p, a, nullptr, 0, 0, nullptr, 0, 0, a->qk_norm->gamma_q, nullptr,
+                              a->dgamma_q, s);
+      if (e == hipSuccess)
+        e = norm_bwd(p, a, nullptr, 0, 0, nullptr, 0, 0, a->qk_norm->gamma_k, nullptr,
+                     a->dgamma_k, s);
+      if (e != hipSuccess) return RK_ERR_HIP;
+    }
+    return RK_OK;
+  }
   if (!a->workspace || ((uintptr_t)a->workspace % kAlign) != 0) return RK_ERR_INVALID_ARG;
   if (a->workspace_bytes < w.total) return RK_ERR_WORKSPACE_TOO_SMALL;
   const bool rope = a->rope != nullptr;
-  const bool k_rotate = rope && !(a->flags & RK_ATTN_K_PREROTATED);
+  const bool norm = a->qk_norm != nullptr;
+  // Q and K are rotated (and normalised) into the workspace; K unless the
+  // caller gave it rotated
+  const bool prep = rope || norm;
+  const bool k_prep = prep && !(a->flags & RK_ATTN_K_PREROTATED);
   const bool use_mfma = bwd_mfma_eligible(a);
-  if (use_mfma && !bwd_mfma_aligned(a, rope, k_rotate)) return RK_ERR_UNSUPPORTED;
+  if (use_mfma && !bwd_mfma_aligned(a, prep, k_prep)) return RK_ERR_UNSUPPORTED;
 
   unsigned char* ws = (unsigned char*)a->workspace;
   rk::BwdLaunch L;
@@ -849,34 +904,46 @@ rk_status rk_masked_attn_bwd(const rk_plan* p, const rk_attn_bwd_args* a, void* 
   L.lse2 = (float*)(ws + w.lse2);
   L.ts = p->timestamps_dev;
   L.anchors = p->anchors_dev;
-  hipStream_t s = (hipStream_t)stream;
   const int64_t hd = (int64_t)a->num_heads * a->d_head;
-  if (rope) {
-    // Q (and K unless given rotated) are rotated once into the workspace
-    // ([T, H, d] dense); the kernels take dQ (dK) back through the rotation.
-    L.tab = make_tab(a->rope, a->d_head);
+  const float eps = norm ? a->qk_norm->eps : 0.f;
+  if (prep) {
+    // Q (and K unless given rotated) are normalised (QK Norm) and rotated
+    // once into the workspace ([T, H, d] dense; a zero table rotates by
+    // nothing); the kernels take dQ (dK) back through the rotation.
+    if (rope) L.tab = make_tab(a->rope, a->d_head);
     hipError_t e = rk::launch_rope(p->R, p->T, p->req_offsets_dev, p->timestamps_dev,
                                    p->anchors_dev, p->seg_kind_dev, 0u, L.tab, a->q, ws + w.q,
                                    a->dtype, a->num_heads, a->d_head, a->q_stride_tok,
-                                   a->q_stride_head, hd, a->d_head, s);
+                                   a->q_stride_head, hd, a->d_head, s, norm, eps,
+                                   norm ? a->qk_norm->gamma_q : nullptr);
     if (e != hipSuccess) return RK_ERR_HIP;
     L.q = ws + w.q;
     L.q_st = hd;
     L.q_sh = a->d_head;
-    L.unrot_q = true;
-    if (k_rotate) {
+    L.unrot_q = rope;
+    if (k_prep) {
       e = rk::launch_rope(p->R, p->T, p->req_offsets_dev, p->timestamps_dev, p->anchors_dev,
                           p->seg_kind_dev, 0u, L.tab, a->k, ws + w.k, a->dtype, a->num_heads,
-                          a->d_head, a->k_stride_tok, a->k_stride_head, hd, a->d_head, s);
+                          a->d_head, a->k_stride_tok, a->k_stride_head, hd, a->d_head, s, norm,
+                          eps, norm ? a->qk_norm->gamma_k : nullptr);
       if (e != hipSuccess) return RK_ERR_HIP;
       L.k = ws + w.k;
       L.k_st = hd;
       L.k_sh = a->d_head;
-      L.unrot_k = true;
+      L.unrot_k = rope;
     }
   }
   hipError_t e = use_mfma ? rk::launch_attn_bwd_mfma_bf16_d64(p, L, s)
                           : rk::launch_attn_bwd_reference(p, L, a->dtype, s);
+  if (e == hipSuccess && norm) {
+    // dQ and dK hold the gradients of the normalised rows: take them back
+    // through the norm in place, with the gains' gradients
+    e = norm_bwd(p, a, a->q, a->q_stride_tok, a->q_stride_head, a->dq, a->dq_stride_tok,
+                 a->dq_stride_head, a->qk_norm->gamma_q, (float*)(ws + w.pq), a->dgamma_q, s);
+    if (e == hipSuccess)
+      e = norm_bwd(p, a, a->k, a->k_stride_tok, a->k_stride_head, a->dk, a->dk_stride_tok,
+                   a->dk_stride_head, a->qk_norm->gamma_k, (float*)(ws + w.pk), a->dgamma_k, s);
+  }
   return e == hipSuccess ? RK_OK : RK_ERR_HIP;
 }
 

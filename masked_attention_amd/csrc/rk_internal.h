@@ -243,4 +243,26 @@ hipError_t launch_attn_mfma_bf16_d64(const rk_plan* p, const AttnLaunch& a, hipS
 hipError_t launch_attn_combine(const rk_plan* p, const AttnLaunch& a, rk_dtype dt, float to_log2,
                                float to_nat, hipStream_t s);
 
+// Backward through QK Norm, in place on the gradient rows g (see
+// norm_bwd.hip): rows = T * H rows of d elements, row (tok, head) at
+// tok * st + head * sh.  partial: norm_bwd_blocks(rows) * d floats, or null
+// when there is no gain (then dgamma is null too).
+struct NormBwdArgs {
+  const void* x;  // the rows before the norm
+  int64_t x_st, x_sh;
+  void* g;        // dLoss/dy in, dLoss/dx out
+  int64_t g_st, g_sh;
+  const float* gamma;  // [d] or null (gain 1)
+  float eps;
+  int64_t rows;
+  int H;
+  float* partial;
+  float* dgamma;  // [d] or null
+};
+constexpr int kRowsPerNormBlock = 512;
+inline int64_t norm_bwd_blocks(int64_t rows) {
+  return (rows + kRowsPerNormBlock - 1) / kRowsPerNormBlock;
+}
+hipError_t launch_norm_bwd(const NormBwdArgs& a, rk_dtype dt, int d, hipStream_t s);
+
 }  // namespace rk

@@ -18,7 +18,8 @@ PKG = os.path.join(ROOT, "masked_attention_amd")
 BUILD = os.path.join(PKG, "_build")
 DEVICE_OBJS = ["plan.hip.o", "rope.hip.o", "attn_ref.hip.o", "attn_mfma.hip.o",
                "attn_combine.hip.o", "attn_bwd_ref.hip.o", "attn_bwd_mfma.hip.o",
-               "gather_sum.hip.o", "attn_pointwise_ref.hip.o", "attn_pointwise_mfma.hip.o"]
+               "gather_sum.hip.o", "attn_pointwise_ref.hip.o", "attn_pointwise_mfma.hip.o",
+               "norm_bwd.hip.o"]
 HIPCC = "/opt/rocm/bin/hipcc"
 
 

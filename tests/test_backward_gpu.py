@@ -325,3 +325,147 @@ def test_backward_tiny_fp32_workload_full(rk):
     _check_grad(wl, dq, rq, "dq")
     _check_grad(wl, dk, rk_, "dk")
     _check_grad(wl, dv, rv, "dv")
+
+
+QKN_CASES = [
+    # (dtype, d, reference, rope, gains)
+    ("f32", 32, True, True, True),
+    ("f32", 64, True, False, True),
+    ("f32", 128, True, True, False),
+    ("bf16", 64, True, True, True),
+    ("bf16", 128, True, False, True),
+    ("bf16", 64, False, True, True),
+    ("bf16", 64, False, False, True),
+    ("bf16", 64, False, True, False),
+]
+
+
+def _check_gain(dtype, got, ref, what):
+    err = np.abs(got - ref)
+    scale = max(1.0, float(np.abs(ref).max()))
+    if dtype == "f32":
+        assert err.max() <= 1e-4 * scale, f"{what}: max abs {err.max()} (scale {scale})"
+    else:
+        rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+        assert rel <= BF16_REL_L2 and err.max() <= BF16_MAX_ABS * scale, (what, rel, err.max())
+
+
+@pytest.mark.parametrize("case", QKN_CASES, ids=[
+    f"{c[0]}-d{c[1]}-{'ref' if c[2] else 'mfma'}-{'rope' if c[3] else 'norope'}-"
+    f"{'gains' if c[4] else 'nogain'}" for c in QKN_CASES])
+def test_backward_qk_norm_matches_oracle(rk, case):
+    """Backward through QK Norm (RMSNorm of the Q and K rows before the
+    rotation): dQ, dK, dV and the gains' gradients against the oracle's
+    chain rule (attention backward at the normalised rows, then the norm's)."""
+    dtype, d, reference, rope, gains = case
+    _say(f"[gpu] backward qk-norm {case}")
+    rng = np.random.default_rng(500 + d)
+    wl = make_custom(random_layout(rng, 3, 400), heads=2, d_head=d, dtype=dtype, seed=11 + d,
+                     delay=600, window=0)
+    gq = rng.uniform(0.5, 1.5, d).astype(np.float32) if gains else None
+    gk = rng.uniform(0.5, 1.5, d).astype(np.float32) if gains else None
+    eps = 1e-6
+    batch, plan = _plan(rk, wl)
+    dt = _dt(wl)
+    q, k, v = (torch.from_numpy(x).to("cuda").to(dt) for x in (wl.q, wl.k, wl.v))
+    do_np = draw_grad(wl)
+    do = torch.from_numpy(do_np).to("cuda").to(dt)
+    tg = lambda g: torch.from_numpy(g).cuda() if g is not None else None
+    norm = dict(eps=eps, gamma_q=tg(gq), gamma_k=tg(gk))
+    rp = _rope(wl) if rope else None
+    o, lse = rk.rk_masked_attn_fwd(plan, q, k, v, rope=rp, want_lse=True, reference=reference,
+                                   qk_norm=norm)
+    dq, dk, dv, dgq, dgk = rk.rk_masked_attn_bwd(plan, q, k, v, o, lse, do, rope=rp,
+                                                 reference=reference, qk_norm=norm)
+    torch.cuda.synchronize()
+    q64, k64, v64 = (x.astype(np.float64) for x in (wl.q, wl.k, wl.v))
+    g64 = lambda g: g.astype(np.float64) if g is not None else None
+    rq, rk_, rv, rgq, rgk = oracle.attention_backward_qk_norm(
+        wl.req_offsets, wl.seg_kind, wl.timestamps, q64, k64, v64, do_np.astype(np.float64),
+        qk_norm=dict(eps=eps, gamma_q=g64(gq), gamma_k=g64(gk)), delay=wl.delay,
+        window=wl.window, static_bidirectional=False, rope=rp)
+    f = lambda x: x.float().cpu().numpy().astype(np.float64)
+    _check_grad(wl, f(dq), rq, "dq")
+    _check_grad(wl, f(dk), rk_, "dk")
+    _check_grad(wl, f(dv), rv, "dv")
+    if gains:
+        _check_gain(dtype, dgq.cpu().numpy().astype(np.float64), rgq, "dgamma_q")
+        _check_gain(dtype, dgk.cpu().numpy().astype(np.float64), rgk, "dgamma_k")
+    else:
+        assert dgq is None and dgk is None
+    # the pass is deterministic
+    again = rk.rk_masked_attn_bwd(plan, q, k, v, o, lse, do, rope=rp, reference=reference,
+                                  qk_norm=norm)
+    torch.cuda.synchronize()
+    assert torch.equal(again[0], dq) and torch.equal(again[1], dk)
+    if gains:
+        assert torch.equal(again[3], dgq) and torch.equal(again[4], dgk)
+
+
+def test_backward_qk_norm_workload_sampled(rk):
+    """MTGR-shaped workload (16 x (32 + 3000 + 200 + 100), H = 8, static part
+    bidirectional) with QK Norm and RoPE: sampled rows (dQ) and keys (dK, dV)
+    of the first and last requests against the oracle at the normalised
+    rows, taken back through the norm row by row."""
+    wl = make_config(4)
+    _say(f"[gpu] backward qk-norm sampled workload 4: T={wl.total_tokens} H={wl.heads}")
+    rng = np.random.default_rng(44)
+    d = wl.d_head
+    gq = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    gk = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    eps = 1e-6
+    batch, plan = _plan(rk, wl)
+    q, k, v = (torch.from_numpy(x).to("cuda").to(torch.bfloat16) for x in (wl.q, wl.k, wl.v))
+    do_np = draw_grad(wl)
+    do = torch.from_numpy(do_np).to("cuda").to(torch.bfloat16)
+    norm = dict(eps=eps, gamma_q=torch.from_numpy(gq).cuda(), gamma_k=torch.from_numpy(gk).cuda())
+    o, lse = rk.rk_masked_attn_fwd(plan, q, k, v, rope=_rope(wl), want_lse=True, qk_norm=norm)
+    dq, dk, dv, _, _ = rk.rk_masked_attn_bwd(plan, q, k, v, o, lse, do, rope=_rope(wl),
+                                             qk_norm=norm)
+    torch.cuda.synchronize()
+    got, ref = [], []
+    for r in (0, wl.num_requests - 1):
+        a, b = wl.request(r)
+        L = b - a
+        pick = lambda n: np.unique(np.concatenate([[0, L - 1], rng.choice(L, size=n, replace=False)]))
+        rows, keys = pick(20), pick(20)
+        qn, kn = wl.q.astype(np.float64), wl.k.astype(np.float64)
+        qn[a:b] = oracle.qk_rmsnorm(qn[a:b], gq.astype(np.float64), eps)
+        kn[a:b] = oracle.qk_rmsnorm(kn[a:b], gk.astype(np.float64), eps)
+        for h in (0, wl.heads - 1):
+            gq_rows, gk_keys, rv = oracle.attention_backward_sampled(
+                wl.req_offsets, wl.seg_kind, wl.timestamps, qn, kn, wl.v, do_np, request=r,
+                head=h, rows=rows, keys=keys, delay=wl.delay, window=wl.window,
+                static_bidirectional=wl.static_bidirectional, rope=_rope(wl))
+            rq, _ = oracle.qk_rmsnorm_backward(wl.q[a + rows, h], gq.astype(np.float64), eps,
+                                               gq_rows)
+            rk_, _ = oracle.qk_rmsnorm_backward(wl.k[a + keys, h], gk.astype(np.float64), eps,
+                                                gk_keys)
+            f = lambda x, idx: x[a + idx, h].float().cpu().numpy().astype(np.float64)
+            got += [f(dq, rows).ravel(), f(dk, keys).ravel(), f(dv, keys).ravel()]
+            ref += [rq.ravel(), rk_.ravel(), rv.ravel()]
+    _check_grad(wl, np.concatenate(got), np.concatenate(ref), "workload 4 qk-norm sampled")
+
+
+def test_backward_qk_norm_rejections(rk):
+    """QK Norm with a pre-rotated K, and a gain without its gradient
+    pointer, are invalid arguments."""
+    import ctypes as C
+
+    from masked_attention_amd import _rk
+    from masked_attention_amd.binding import _bwd_args, qk_norm_params
+    wl = make_custom([[(HISTORY, np.arange(NOW - 900, NOW, 3, dtype=np.int64))]], heads=1,
+                     d_head=64, dtype="bf16", seed=3)
+    batch, plan = _plan(rk, wl)
+    q = torch.from_numpy(wl.q).cuda().to(torch.bfloat16)
+    lse = torch.zeros((1, wl.total_tokens), dtype=torch.float32, device="cuda")
+    g = torch.ones(64, dtype=torch.float32, device="cuda")
+    with pytest.raises(_rk.RkError) as e:
+        rk.rk_masked_attn_bwd(plan, q, q, q, q, lse, q, rope=_rope(wl), k_prerotated=True,
+                              qk_norm=dict(eps=1e-6))
+    assert e.value.status == _rk.RK_ERR_INVALID_ARG
+    out = [torch.empty_like(q) for _ in range(3)]
+    a = _bwd_args(q, q, q, q, q, lse, *out, 0.0, None, False, False, None)
+    nq = qk_norm_params(1e-6, gamma_q=g)
+    a.qk_norm = C.cast(C.pointer(nq), C.c_void_p)
+    assert _rk.lib().rk_masked_attn_bwd(plan.handle, C.byref(a), None) == _rk.RK_ERR_INVALID_ARG
