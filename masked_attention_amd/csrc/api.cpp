@@ -36,6 +36,9 @@ struct Layout {
   std::vector<int32_t> kt_req;      // key-major counterparts
   std::vector<Group> kgroups;
   std::vector<int32_t> kqueue_start;
+  std::vector<int32_t> ilv;         // see PlanDev::ilv
+  size_t ilv_cap = 0;               // int32 entries reserved for ilv
+  size_t off_ilv = 0;
   size_t off_req = 0, off_qt_req = 0, off_groups = 0, off_queue_start = 0, off_totals = 0,
          host_blob = 0, off_row_desc = 0, off_tile_count = 0, off_tile_class = 0, off_qt_nnz = 0,
          off_qt_pairs = 0, off_qt_full = 0,
@@ -157,13 +160,51 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->max_queue = place_groups(L->R, H, o, weight, nqt_of, with_tables, &L->groups,
                               &L->queue_start);
   L->slots = L->max_queue * kNumXcd;
+  int64_t ng = 0;
+  for (int32_t r = 0; r < L->R; ++r) ng += (o[r + 1] > o[r]) ? H : 0;
+  L->G = ng;
+  // Blocks: consecutive groups of a queue packed while their items total at
+  // most kInterleaveItems (a larger group is a block of its own); inside a
+  // block the groups are sorted by count, largest first, all get the
+  // block's first slot as base, and the block's slots take every group's
+  // largest item, then every group's second largest, ...
+  L->ilv_cap = 2 * (size_t)L->G;
+  for (int32_t r = 0; r < L->R; ++r)
+    if (o[r + 1] > o[r]) L->ilv_cap += (size_t)H * (2 + (size_t)nqt_of(r));
+  if (with_tables && L->G > 0) {
+    L->ilv.assign(2 * (size_t)L->G, 0);
+    for (int q = 0; q < kNumXcd; ++q) {
+      int32_t b = L->queue_start[q];
+      const int32_t e = L->queue_start[q + 1];
+      while (b < e) {
+        int32_t f = b + 1;
+        int64_t items = L->groups[b].count;
+        while (f < e && items + L->groups[f].count <= rk::kInterleaveItems)
+          items += L->groups[f++].count;
+        const int32_t base = L->groups[b].base;  // the block's first slot
+        std::stable_sort(L->groups.begin() + b, L->groups.begin() + f,
+                         [](const Group& x, const Group& y) { return x.count > y.count; });
+        const int32_t K = L->groups[b].count;
+        const int32_t table = (int32_t)L->ilv.size();
+        L->ilv.push_back(K);
+        for (int32_t k = 0; k <= K; ++k) {
+          int64_t c = 0;
+          for (int32_t g = b; g < f; ++g) c += std::min(L->groups[g].count, k);
+          L->ilv.push_back((int32_t)c);
+        }
+        for (int32_t g = b; g < f; ++g) {
+          L->groups[g].base = base;
+          L->ilv[g] = b;
+          L->ilv[L->G + g] = table;
+        }
+        b = f;
+      }
+    }
+  }
   const int64_t kmax = place_groups(L->R, H, o, weight, nkb_of, with_tables, &L->kgroups,
                                     &L->kqueue_start);
   L->kslots = kmax * kNumXcd;
   if (L->slots >= kInt32Max || L->kslots >= kInt32Max) return RK_ERR_UNSUPPORTED;
-  int64_t ng = 0;
-  for (int32_t r = 0; r < L->R; ++r) ng += (o[r + 1] > o[r]) ? H : 0;
-  L->G = ng;
   if (with_tables) {
     L->qt_req.resize(nq);
     L->kt_req.resize(nk);
@@ -187,6 +228,7 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->off_kt_req = take(sizeof(int32_t) * (size_t)nk);
   L->off_kgroups = take(sizeof(Group) * (size_t)L->G);
   L->off_kqueue_start = take(sizeof(int32_t) * (kNumXcd + 1));
+  L->off_ilv = take(sizeof(int32_t) * L->ilv_cap);
   L->host_blob = off;
   L->off_row_desc = take(sizeof(int2) * (size_t)L->T);
   L->off_tile_count = take(sizeof(int32_t) * (size_t)nt);
@@ -352,6 +394,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   p->off_qtile_word = L.off_qtile_word;
   p->off_korder = L.off_korder;
   p->off_ksched = L.off_ksched;
+  p->off_ilv = L.off_ilv;
   p->host_blob_bytes = L.host_blob;
   p->total_bytes = L.total;
 
@@ -384,6 +427,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   D.qtile_word = (int32_t*)(ws + L.off_qtile_word);
   D.korder = (int32_t*)(ws + L.off_korder);
   D.ksched = (int32_t*)(ws + L.off_ksched);
+  D.ilv = (int32_t*)(ws + L.off_ilv);
 
   p->host_blob = (unsigned char*)std::calloc(L.host_blob ? L.host_blob : 1, 1);
   if (!p->host_blob) {
@@ -398,6 +442,8 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   if (L.G) std::memcpy(p->host_blob + L.off_kgroups, L.kgroups.data(), sizeof(Group) * L.G);
   std::memcpy(p->host_blob + L.off_kqueue_start, L.kqueue_start.data(),
               sizeof(int32_t) * (kNumXcd + 1));
+  if (!L.ilv.empty())
+    std::memcpy(p->host_blob + L.off_ilv, L.ilv.data(), sizeof(int32_t) * L.ilv.size());
   // totals stay zero (calloc)
 
   hipStream_t s = (hipStream_t)stream;

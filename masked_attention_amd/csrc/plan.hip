@@ -315,21 +315,39 @@ __global__ __launch_bounds__(256) void plan_qsort_kernel(PlanDev P) {
 // gets no work (-1): candidates are the last segment of a request, so the
 // tiles kept are the ones from the tile of the first candidate on, which
 // within a group come first in the descending-work order.
-__global__ void plan_sched_kernel(PlanDev P, int64_t slots, int H, int cand_only) {
+__global__ void plan_sched_kernel(PlanDev P, int64_t slots, int H, int cand_only, int G) {
   const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= slots) return;
   const int q = (int)(s % kNumXcd);
   const int idx = (int)(s / kNumXcd);
   int a = P.queue_start[q], b = P.queue_start[q + 1];
   int item = -1;
+  int ga = -1, k = -1;  // group and its rank-k item of this slot
   if (a < b) {
-    // last group with base <= idx
+    // the block holding the slot: its groups share the block's first slot
+    // as base (the last group with base <= idx is one of them)
     while (b - a > 1) {
       const int mid = (a + b) >> 1;
       if (P.groups[mid].base <= idx) a = mid; else b = mid;
     }
-    const Group grp = P.groups[a];
-    const int k = idx - grp.base;
+    const int f = P.ilv[a];                    // first group of the block
+    const int* T = P.ilv + P.ilv[G + a];       // K, then C(0..K)
+    const int K = T[0];
+    const int* C = T + 1;
+    const int local = idx - P.groups[f].base;
+    if (local >= 0 && local < C[K]) {
+      // rank k of every group of the block with more than k items, k = 0, 1, ...
+      int lo = 0, hi = K;  // C[lo] <= local < C[hi]; C increases strictly
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (C[mid] <= local) lo = mid; else hi = mid;
+      }
+      k = lo;
+      ga = f + (local - C[lo]);
+    }
+  }
+  if (ga >= 0) {
+    const Group grp = P.groups[ga];
     if (k >= 0 && k < grp.count) {
       const ReqMeta m = P.req[grp.req];
       const int qg = P.qorder[m.qt_off + k];
@@ -564,7 +582,8 @@ hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
   }
   if (p->slots > 0) {
     hipLaunchKernelGGL(plan_sched_kernel, dim3((unsigned)((p->slots + 255) / 256)), dim3(256), 0, s,
-                       P, p->slots, p->H, (int)((p->flags & RK_QUERY_CANDIDATES_ONLY) != 0));
+                       P, p->slots, p->H, (int)((p->flags & RK_QUERY_CANDIDATES_ONLY) != 0),
+                       (int)p->G);
     if (p->grid > p->slots)
       hipLaunchKernelGGL(plan_work_kernel, dim3((unsigned)((p->grid + 1023) / 1024)), dim3(1024), 0,
                          s, P, (int)p->slots, (int)p->grid, p->H);

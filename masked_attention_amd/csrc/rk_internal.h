@@ -13,6 +13,13 @@ namespace rk {
 constexpr int kTileQ = RK_TILE_Q;
 constexpr int kTileK = RK_TILE_K;
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
+// Query-tile items one XCD runs at once in the forward (32 CUs x 3
+// workgroups).  Consecutive (request, head) groups of a queue are packed
+// into blocks of at most this many items (a larger group is a block of its
+// own); blocks run one after another and the groups of a block are
+// interleaved by rank, so about as many groups are in flight as when they
+// run one after another, without a saw-tooth of item sizes.
+constexpr int kInterleaveItems = 96;
 constexpr int kMaxHalfD = 64;     // d_head <= 128
 
 // Per-request metadata in the plan workspace.  tok_off .. tile_off are
@@ -92,6 +99,9 @@ struct PlanDev {
   int32_t* ktile_word;     // [NT] CSR entry for the kernels: kt | (PARTIAL << 31)
   int32_t* qorder;         // [NQ]
   int32_t* sched;          // [slots]
+  int32_t* ilv;            // blocks of the schedule: [G] first group of each group's block,
+                           // [G] offset in ilv of the block's table: K (largest count),
+                           // then C(k) = sum over its groups of min(count, k), k = 0..K
   WorkEntry* work;         // [slots + kSplitTarget] (candidates-only plans)
   SplitEntry* splits;      // [kSplitTarget]
   int32_t* act_slots;      // [kSplitTarget / 2] active schedule slots, arrival order
@@ -130,7 +140,7 @@ struct rk_plan {
       off_tile_class, off_qt_nnz, off_qt_pairs, off_qt_full, off_qtile_ptr, off_ktile_idx, off_ktile_word, off_qorder,
       off_sched, off_work, off_splits, off_act, off_totals, host_blob_bytes, total_bytes,
       off_kt_req, off_kgroups, off_kqueue_start, off_kt_nnz, off_kt_ptr, off_qtile_word,
-      off_korder, off_ksched;
+      off_korder, off_ksched, off_ilv;
   rk::PlanDev dev;
   // host copy of the first host_blob_bytes of the workspace (kept alive
   // for the asynchronous upload)

@@ -505,3 +505,54 @@ def test_attention_scores_far_below_zero(rk, rope):
     assert np.all(ref_lse[fin] < -100)
     assert np.array_equal(np.isfinite(lse), fin)
     assert np.all(np.abs(lse[fin] - ref_lse[fin]) <= 2e-2 + 2.0 ** -7 * np.abs(ref_lse[fin]))
+
+
+@pytest.mark.parametrize("cfg", [2, 4, 5])
+def test_schedule_order(rk, cfg):
+    """Launch order inside each XCD queue (slot s runs on queue s % 8): the
+    queue is a sequence of blocks, each holding the items of whole
+    (request, head) groups, at most 96 items unless it is one group; every
+    group of a block starts in the block's first slots (its largest item),
+    and each group's items come in non-increasing size."""
+    wl = make_config(cfg, with_qkv=False)
+    _say(f"[gpu] schedule order workload {cfg}")
+    batch, plan = _plan(rk, wl)
+    torch.cuda.synchronize()
+    sched = plan.sched().cpu().numpy()
+    nnz = np.diff(plan.qtile_ptr().cpu().numpy().astype(np.int64))
+    H = wl.heads
+    nqts = [-(-(int(b) - int(a)) // 128) for a, b in zip(wl.req_offsets[:-1], wl.req_offsets[1:])]
+    qt_req = np.repeat(np.arange(wl.num_requests), nqts)
+    multi = 0
+    for q in range(8):
+        items = sched[q::8]
+        items = items[items >= 0]
+        groups = (qt_req[items // H] * H + items % H).tolist()
+        sizes = nnz[items // H].tolist()
+        total = {g: groups.count(g) for g in set(groups)}
+        left = dict(total)
+        last = {}
+        i = 0
+        while i < len(items):
+            # a block: its groups start in its first slots
+            block = []
+            while i < len(items) and groups[i] not in last:
+                block.append(groups[i])
+                last[groups[i]] = sizes[i]
+                left[groups[i]] -= 1
+                i += 1
+            n = len(block)
+            while i < len(items) and any(left[g] for g in block):
+                g = groups[i]
+                assert g in block, f"queue {q}: group {g} starts inside a block"
+                assert sizes[i] <= last[g], f"queue {q}: a group's item sizes grow"
+                last[g] = sizes[i]
+                left[g] -= 1
+                i += 1
+            size = sum(total[g] for g in block)
+            assert size <= 96 or n == 1, (q, size, n)
+            multi += n > 1
+    if cfg in (2, 4):
+        assert multi > 0, "small groups expected to share blocks"
+    else:
+        assert multi == 0, "groups of more than 96 items run alone"
