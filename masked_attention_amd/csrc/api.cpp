@@ -37,8 +37,9 @@ struct Layout {
   std::vector<Group> kgroups;
   std::vector<int32_t> kqueue_start;
   std::vector<int32_t> ilv;         // see PlanDev::ilv
-  size_t ilv_cap = 0;               // int32 entries reserved for ilv
-  size_t off_ilv = 0;
+  std::vector<int32_t> kilv;        // the same for kgroups
+  size_t ilv_cap = 0;               // int32 entries reserved for ilv (and for kilv)
+  size_t off_ilv = 0, off_kilv = 0;
   size_t off_req = 0, off_qt_req = 0, off_groups = 0, off_queue_start = 0, off_totals = 0,
          host_blob = 0, off_row_desc = 0, off_tile_count = 0, off_tile_class = 0, off_qt_nnz = 0,
          off_qt_pairs = 0, off_qt_full = 0,
@@ -96,6 +97,47 @@ int64_t place_groups(int32_t R, int32_t H, const int32_t* o, const std::vector<i
     (*qstart)[kNumXcd] = (int32_t)out->size();
   }
   return mq;
+}
+
+// Blocks of a schedule: consecutive groups of a queue packed while their
+// items total at most kInterleaveItems (a larger group is a block of its
+// own); inside a block the groups are sorted by count, largest first, all
+// get the block's first slot as base, and the block's slots take every
+// group's largest item, then every group's second largest, ...  Fills `ilv`
+// as PlanDev::ilv describes (2 G + sum over blocks of K + 2 entries, at
+// most 2 G + sum over groups of count + 2).
+void build_blocks(std::vector<Group>* groups, const std::vector<int32_t>& qstart, int64_t G,
+                  std::vector<int32_t>* ilv) {
+  ilv->clear();
+  if (G == 0) return;
+  std::vector<Group>& gs = *groups;
+  ilv->assign(2 * (size_t)G, 0);
+  for (int q = 0; q < kNumXcd; ++q) {
+    int32_t b = qstart[q];
+    const int32_t e = qstart[q + 1];
+    while (b < e) {
+      int32_t f = b + 1;
+      int64_t items = gs[b].count;
+      while (f < e && items + gs[f].count <= rk::kInterleaveItems) items += gs[f++].count;
+      const int32_t base = gs[b].base;  // the block's first slot
+      std::stable_sort(gs.begin() + b, gs.begin() + f,
+                       [](const Group& x, const Group& y) { return x.count > y.count; });
+      const int32_t K = gs[b].count;
+      const int32_t table = (int32_t)ilv->size();
+      ilv->push_back(K);
+      for (int32_t k = 0; k <= K; ++k) {
+        int64_t c = 0;
+        for (int32_t g = b; g < f; ++g) c += std::min(gs[g].count, k);
+        ilv->push_back((int32_t)c);
+      }
+      for (int32_t g = b; g < f; ++g) {
+        gs[g].base = base;
+        (*ilv)[g] = b;
+        (*ilv)[G + g] = table;
+      }
+      b = f;
+    }
+  }
 }
 
 rk_status check_batch(const rk_batch* b) {
@@ -163,47 +205,14 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   int64_t ng = 0;
   for (int32_t r = 0; r < L->R; ++r) ng += (o[r + 1] > o[r]) ? H : 0;
   L->G = ng;
-  // Blocks: consecutive groups of a queue packed while their items total at
-  // most kInterleaveItems (a larger group is a block of its own); inside a
-  // block the groups are sorted by count, largest first, all get the
-  // block's first slot as base, and the block's slots take every group's
-  // largest item, then every group's second largest, ...
   L->ilv_cap = 2 * (size_t)L->G;
   for (int32_t r = 0; r < L->R; ++r)
     if (o[r + 1] > o[r]) L->ilv_cap += (size_t)H * (2 + (size_t)nqt_of(r));
-  if (with_tables && L->G > 0) {
-    L->ilv.assign(2 * (size_t)L->G, 0);
-    for (int q = 0; q < kNumXcd; ++q) {
-      int32_t b = L->queue_start[q];
-      const int32_t e = L->queue_start[q + 1];
-      while (b < e) {
-        int32_t f = b + 1;
-        int64_t items = L->groups[b].count;
-        while (f < e && items + L->groups[f].count <= rk::kInterleaveItems)
-          items += L->groups[f++].count;
-        const int32_t base = L->groups[b].base;  // the block's first slot
-        std::stable_sort(L->groups.begin() + b, L->groups.begin() + f,
-                         [](const Group& x, const Group& y) { return x.count > y.count; });
-        const int32_t K = L->groups[b].count;
-        const int32_t table = (int32_t)L->ilv.size();
-        L->ilv.push_back(K);
-        for (int32_t k = 0; k <= K; ++k) {
-          int64_t c = 0;
-          for (int32_t g = b; g < f; ++g) c += std::min(L->groups[g].count, k);
-          L->ilv.push_back((int32_t)c);
-        }
-        for (int32_t g = b; g < f; ++g) {
-          L->groups[g].base = base;
-          L->ilv[g] = b;
-          L->ilv[L->G + g] = table;
-        }
-        b = f;
-      }
-    }
-  }
+  if (with_tables) build_blocks(&L->groups, L->queue_start, L->G, &L->ilv);
   const int64_t kmax = place_groups(L->R, H, o, weight, nkb_of, with_tables, &L->kgroups,
                                     &L->kqueue_start);
   L->kslots = kmax * kNumXcd;
+  if (with_tables) build_blocks(&L->kgroups, L->kqueue_start, L->G, &L->kilv);
   if (L->slots >= kInt32Max || L->kslots >= kInt32Max) return RK_ERR_UNSUPPORTED;
   if (with_tables) {
     L->qt_req.resize(nq);
@@ -229,6 +238,7 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->off_kgroups = take(sizeof(Group) * (size_t)L->G);
   L->off_kqueue_start = take(sizeof(int32_t) * (kNumXcd + 1));
   L->off_ilv = take(sizeof(int32_t) * L->ilv_cap);
+  L->off_kilv = take(sizeof(int32_t) * L->ilv_cap);
   L->host_blob = off;
   L->off_row_desc = take(sizeof(int2) * (size_t)L->T);
   L->off_tile_count = take(sizeof(int32_t) * (size_t)nt);
@@ -395,6 +405,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   p->off_korder = L.off_korder;
   p->off_ksched = L.off_ksched;
   p->off_ilv = L.off_ilv;
+  p->off_kilv = L.off_kilv;
   p->host_blob_bytes = L.host_blob;
   p->total_bytes = L.total;
 
@@ -428,6 +439,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   D.korder = (int32_t*)(ws + L.off_korder);
   D.ksched = (int32_t*)(ws + L.off_ksched);
   D.ilv = (int32_t*)(ws + L.off_ilv);
+  D.kilv = (int32_t*)(ws + L.off_kilv);
 
   p->host_blob = (unsigned char*)std::calloc(L.host_blob ? L.host_blob : 1, 1);
   if (!p->host_blob) {
@@ -444,6 +456,8 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
               sizeof(int32_t) * (kNumXcd + 1));
   if (!L.ilv.empty())
     std::memcpy(p->host_blob + L.off_ilv, L.ilv.data(), sizeof(int32_t) * L.ilv.size());
+  if (!L.kilv.empty())
+    std::memcpy(p->host_blob + L.off_kilv, L.kilv.data(), sizeof(int32_t) * L.kilv.size());
   // totals stay zero (calloc)
 
   hipStream_t s = (hipStream_t)stream;

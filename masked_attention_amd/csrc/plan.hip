@@ -315,37 +315,45 @@ __global__ __launch_bounds__(256) void plan_qsort_kernel(PlanDev P) {
 // gets no work (-1): candidates are the last segment of a request, so the
 // tiles kept are the ones from the tile of the first candidate on, which
 // within a group come first in the descending-work order.
+// The group `ga` and rank `k` whose item sits at position `idx` of XCD
+// queue `q` of a blocked schedule (groups sorted by (queue, base), the
+// groups of a block share the block's first slot as base; ilv as
+// PlanDev::ilv describes); ga = -1 for a slot past the block's items.
+__device__ void slot_of(const Group* groups, const int32_t* qstart, const int32_t* ilv, int G,
+                        int q, int idx, int* ga, int* k) {
+  int a = qstart[q], b = qstart[q + 1];
+  *ga = -1;
+  *k = -1;
+  if (a >= b) return;
+  // the block holding the slot (the last group with base <= idx is one of it)
+  while (b - a > 1) {
+    const int mid = (a + b) >> 1;
+    if (groups[mid].base <= idx) a = mid; else b = mid;
+  }
+  const int f = ilv[a];                    // first group of the block
+  const int* T = ilv + ilv[G + a];         // K, then C(0..K)
+  const int K = T[0];
+  const int* C = T + 1;
+  const int local = idx - groups[f].base;
+  if (local < 0 || local >= C[K]) return;
+  // rank k of every group of the block with more than k items, k = 0, 1, ...
+  int lo = 0, hi = K;  // C[lo] <= local < C[hi]; C increases strictly
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (C[mid] <= local) lo = mid; else hi = mid;
+  }
+  *k = lo;
+  *ga = f + (local - C[lo]);
+}
+
 __global__ void plan_sched_kernel(PlanDev P, int64_t slots, int H, int cand_only, int G) {
   const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= slots) return;
   const int q = (int)(s % kNumXcd);
   const int idx = (int)(s / kNumXcd);
-  int a = P.queue_start[q], b = P.queue_start[q + 1];
   int item = -1;
   int ga = -1, k = -1;  // group and its rank-k item of this slot
-  if (a < b) {
-    // the block holding the slot: its groups share the block's first slot
-    // as base (the last group with base <= idx is one of them)
-    while (b - a > 1) {
-      const int mid = (a + b) >> 1;
-      if (P.groups[mid].base <= idx) a = mid; else b = mid;
-    }
-    const int f = P.ilv[a];                    // first group of the block
-    const int* T = P.ilv + P.ilv[G + a];       // K, then C(0..K)
-    const int K = T[0];
-    const int* C = T + 1;
-    const int local = idx - P.groups[f].base;
-    if (local >= 0 && local < C[K]) {
-      // rank k of every group of the block with more than k items, k = 0, 1, ...
-      int lo = 0, hi = K;  // C[lo] <= local < C[hi]; C increases strictly
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (C[mid] <= local) lo = mid; else hi = mid;
-      }
-      k = lo;
-      ga = f + (local - C[lo]);
-    }
-  }
+  slot_of(P.groups, P.queue_start, P.ilv, G, q, idx, &ga, &k);
   if (ga >= 0) {
     const Group grp = P.groups[ga];
     if (k >= 0 && k < grp.count) {
@@ -537,20 +545,15 @@ __global__ __launch_bounds__(256) void plan_ksort_kernel(PlanDev P) {
 
 // One thread per key-major launch slot (same XCD mapping as the query-major
 // schedule): item = global k-tile * H + head, or -1.
-__global__ void plan_ksched_kernel(PlanDev P, int64_t slots, int H) {
+__global__ void plan_ksched_kernel(PlanDev P, int64_t slots, int H, int G) {
   const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= slots) return;
-  const int q = (int)(s % kNumXcd);
-  const int idx = (int)(s / kNumXcd);
-  int a = P.kqueue_start[q], b = P.kqueue_start[q + 1];
+  int ga = -1, k = -1;
+  slot_of(P.kgroups, P.kqueue_start, P.kilv, G, (int)(s % kNumXcd), (int)(s / kNumXcd), &ga,
+          &k);
   int item = -1;
-  if (a < b) {
-    while (b - a > 1) {
-      const int mid = (a + b) >> 1;
-      if (P.kgroups[mid].base <= idx) a = mid; else b = mid;
-    }
-    const Group grp = P.kgroups[a];
-    const int k = idx - grp.base;
+  if (ga >= 0) {
+    const Group grp = P.kgroups[ga];
     if (k >= 0 && k < grp.count) {
       const ReqMeta m = P.req[grp.req];
       item = P.korder[m.kt_off + k] * H + grp.head;
@@ -594,7 +597,7 @@ hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
     hipLaunchKernelGGL(plan_kfill_kernel, dim3((unsigned)p->NK), dim3(256), 0, s, P);
     hipLaunchKernelGGL(plan_ksort_kernel, dim3(p->R), dim3(256), 0, s, P);
     hipLaunchKernelGGL(plan_ksched_kernel, dim3((unsigned)((p->kslots + 255) / 256)), dim3(256), 0,
-                       s, P, p->kslots, p->H);
+                       s, P, p->kslots, p->H, (int)p->G);
   }
   return hipGetLastError();
 }

@@ -13,8 +13,8 @@ namespace rk {
 constexpr int kTileQ = RK_TILE_Q;
 constexpr int kTileK = RK_TILE_K;
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
-// Query-tile items one XCD runs at once in the forward (32 CUs x 3
-// workgroups).  Consecutive (request, head) groups of a queue are packed
+// Work items one XCD runs at once in the forward (32 CUs x 3 workgroups;
+// the backward's kernels run 2 per CU and take the same blocks).  Consecutive (request, head) groups of a queue are packed
 // into blocks of at most this many items (a larger group is a block of its
 // own); blocks run one after another and the groups of a block are
 // interleaved by rank, so about as many groups are in flight as when they
@@ -116,6 +116,7 @@ struct PlanDev {
   int32_t* qtile_word;     // [NT] CSR entry: request-local qt | (PARTIAL << 31)
   int32_t* korder;         // [NK] key blocks of each request by descending kt_nnz
   int32_t* ksched;         // [kslots] work item = key block * H + head, or -1
+  int32_t* kilv;           // blocks of the key-major schedule, laid out as ilv
 };
 
 }  // namespace rk
@@ -140,7 +141,7 @@ struct rk_plan {
       off_tile_class, off_qt_nnz, off_qt_pairs, off_qt_full, off_qtile_ptr, off_ktile_idx, off_ktile_word, off_qorder,
       off_sched, off_work, off_splits, off_act, off_totals, host_blob_bytes, total_bytes,
       off_kt_req, off_kgroups, off_kqueue_start, off_kt_nnz, off_kt_ptr, off_qtile_word,
-      off_korder, off_ksched, off_ilv;
+      off_korder, off_ksched, off_ilv, off_kilv;
   rk::PlanDev dev;
   // host copy of the first host_blob_bytes of the workspace (kept alive
   // for the asynchronous upload)

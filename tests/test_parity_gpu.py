@@ -507,28 +507,15 @@ def test_attention_scores_far_below_zero(rk, rope):
     assert np.all(np.abs(lse[fin] - ref_lse[fin]) <= 2e-2 + 2.0 ** -7 * np.abs(ref_lse[fin]))
 
 
-@pytest.mark.parametrize("cfg", [2, 4, 5])
-def test_schedule_order(rk, cfg):
-    """Launch order inside each XCD queue (slot s runs on queue s % 8): the
-    queue is a sequence of blocks, each holding the items of whole
-    (request, head) groups, at most 96 items unless it is one group; every
-    group of a block starts in the block's first slots (its largest item),
-    and each group's items come in non-increasing size."""
-    wl = make_config(cfg, with_qkv=False)
-    _say(f"[gpu] schedule order workload {cfg}")
-    batch, plan = _plan(rk, wl)
-    torch.cuda.synchronize()
-    sched = plan.sched().cpu().numpy()
-    nnz = np.diff(plan.qtile_ptr().cpu().numpy().astype(np.int64))
-    H = wl.heads
-    nqts = [-(-(int(b) - int(a)) // 128) for a, b in zip(wl.req_offsets[:-1], wl.req_offsets[1:])]
-    qt_req = np.repeat(np.arange(wl.num_requests), nqts)
+def _check_blocks(sched, sizes_of, group_of):
+    """Blocks of each XCD queue (slot s runs on queue s % 8) of a schedule;
+    returns how many blocks hold more than one group."""
     multi = 0
     for q in range(8):
         items = sched[q::8]
         items = items[items >= 0]
-        groups = (qt_req[items // H] * H + items % H).tolist()
-        sizes = nnz[items // H].tolist()
+        groups = group_of(items).tolist()
+        sizes = sizes_of(items).tolist()
         total = {g: groups.count(g) for g in set(groups)}
         left = dict(total)
         last = {}
@@ -552,7 +539,35 @@ def test_schedule_order(rk, cfg):
             size = sum(total[g] for g in block)
             assert size <= 96 or n == 1, (q, size, n)
             multi += n > 1
-    if cfg in (2, 4):
-        assert multi > 0, "small groups expected to share blocks"
-    else:
-        assert multi == 0, "groups of more than 96 items run alone"
+    return multi
+
+
+@pytest.mark.parametrize("cfg", [2, 4, 5])
+def test_schedule_order(rk, cfg):
+    """Launch order inside each XCD queue, for the forward's query-tile
+    schedule and the backward's key-block schedule: the queue is a sequence
+    of blocks, each holding the items of whole (request, head) groups, at
+    most 96 items unless it is one group; every group of a block starts in
+    the block's first slots (its largest item), and each group's items come
+    in non-increasing size (non-empty tiles of the query tile, or of the key
+    block)."""
+    wl = make_config(cfg, with_qkv=False)
+    _say(f"[gpu] schedule order workload {cfg}")
+    batch = rk.Batch.from_workload(wl)
+    plan = rk.Plan(batch, delay=wl.delay, window=wl.window,
+                   static_bidirectional=wl.static_bidirectional, num_heads=wl.heads,
+                   global_tail=wl.global_tail, backward=True)
+    torch.cuda.synchronize()
+    H = wl.heads
+    nqts = [-(-(int(b) - int(a)) // 128) for a, b in zip(wl.req_offsets[:-1], wl.req_offsets[1:])]
+    tile_req = np.repeat(np.arange(wl.num_requests), nqts)  # also each key block's request
+    group_of = lambda items: tile_req[items // H] * H + items % H
+    for name, sched, ptr in (("query tiles", plan.sched(), plan.qtile_ptr()),
+                             ("key blocks", plan.ksched(), plan.kt_ptr())):
+        nnz = np.diff(ptr.cpu().numpy().astype(np.int64))
+        multi = _check_blocks(sched.cpu().numpy(), lambda items: nnz[items // H], group_of)
+        if cfg in (2, 4):
+            assert multi > 0, f"{name}: small groups expected to share blocks"
+        else:
+            assert multi == 0, f"{name}: groups of more than 96 items run alone"
+    plan.close()
