@@ -154,10 +154,19 @@ __global__ void plan_rowdesc_kernel(PlanDev P, int R, int T, const uint8_t* __re
 
 // One block per global q-tile: exact visible count and class of each of its
 // k-tiles, and the q-tile's partial totals (non-empty, FULL, pairs).
+// From the extremes of the rows' intervals [lo, hi) (lo_max, hi_min, lo_min,
+// hi_max over the q-tile's rows) most k-tiles [c0, c1) are decided without
+// visiting the rows: a whole tile (128 rows, 64 keys) with lo_max <= c0 and
+// c1 <= hi_min is FULL (8192 pairs; a row's own key, if in the tile, is
+// inside its interval); a tile with c0 >= hi_max or c1 <= lo_min that holds
+// no row's own position is EMPTY.  The rest are counted row by row; with
+// fewer than 256 k-tiles the rows are split among S = 2^j consecutive lanes
+// per k-tile (S * nkt <= 256, S <= 64), whose counts meet by shuffles.
 __global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
   __shared__ int2 d[kTileQ];
   __shared__ unsigned long long pairs_s;
   __shared__ int nnz_s, full_s;
+  __shared__ int lim[4];  // lo_max, hi_min, lo_min, hi_max
   const int g = blockIdx.x;
   const int r = P.qt_req[g];
   const ReqMeta m = P.req[r];
@@ -166,31 +175,77 @@ __global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
   const int nrows = min(kTileQ, m.len - row0);
   if (threadIdx.x < kTileQ)
     d[threadIdx.x] = threadIdx.x < nrows ? P.row_desc[m.tok_off + row0 + threadIdx.x] : make_int2(0, 0);
-  if (threadIdx.x == 0) { pairs_s = 0; nnz_s = 0; full_s = 0; }
+  if (threadIdx.x == 0) {
+    pairs_s = 0; nnz_s = 0; full_s = 0;
+    lim[0] = INT_MIN; lim[1] = INT_MAX; lim[2] = INT_MAX; lim[3] = INT_MIN;
+  }
   __syncthreads();
+  if (threadIdx.x < kTileQ) {  // waves 0 and 1: the rows' extremes
+    const bool ok = (int)threadIdx.x < nrows;
+    const int lo = d[threadIdx.x].x, hi = d[threadIdx.x].y & 0x7fffffff;
+    int v0 = ok ? lo : INT_MIN, v1 = ok ? hi : INT_MAX, v2 = ok ? lo : INT_MAX,
+        v3 = ok ? hi : INT_MIN;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      v0 = max(v0, __shfl_xor(v0, o, 64));
+      v1 = min(v1, __shfl_xor(v1, o, 64));
+      v2 = min(v2, __shfl_xor(v2, o, 64));
+      v3 = max(v3, __shfl_xor(v3, o, 64));
+    }
+    if ((threadIdx.x & 63) == 0) {
+      atomicMax(&lim[0], v0);
+      atomicMin(&lim[1], v1);
+      atomicMin(&lim[2], v2);
+      atomicMax(&lim[3], v3);
+    }
+  }
+  __syncthreads();
+  const int lo_max = lim[0], hi_min = lim[1], lo_min = lim[2], hi_max = lim[3];
+  int S = 1;  // lanes per k-tile (uniform over the block)
+  while (S < 64 && 2 * S * m.nkt <= (int)blockDim.x) S *= 2;
+  const int slice = threadIdx.x & (S - 1);
+  const int per = kTileQ / S;  // rows of a lane: slice * per .. + per
+  const int t0 = slice * per, t1 = min(nrows, t0 + per);
+  const int step = blockDim.x / S;
   unsigned long long pairs = 0;
   int nnz = 0, nfull = 0;
-  for (int kt = threadIdx.x; kt < m.nkt; kt += blockDim.x) {
+  // every lane of a k-tile's group runs the same trip count and takes the
+  // same branch (both depend on kt only), so the shuffles below see all S
+  // lanes
+  for (int kt0 = 0; kt0 < m.nkt; kt0 += step) {
+    const int kt = kt0 + (int)threadIdx.x / S;
     const int c0 = kt * kTileK;
     const int c1 = min(m.len, c0 + kTileK);
     int cnt = 0;
-    for (int t = 0; t < nrows; ++t) {
-      const int lo = d[t].x;
-      const int hi = d[t].y & 0x7fffffff;
-      const int a = max(lo, c0), b = min(hi, c1);
-      cnt += max(0, b - a);
-      if (d[t].y < 0) {
-        const int pr = row0 + t;
-        if (pr >= c0 && pr < c1 && !(pr >= lo && pr < hi)) cnt += 1;
+    if (kt < m.nkt) {
+      const bool full = nrows == kTileQ && c1 - c0 == kTileK && lo_max <= c0 && c1 <= hi_min;
+      const bool empty = (c0 >= hi_max || c1 <= lo_min) && (c1 <= row0 || c0 >= row0 + nrows);
+      if (full) {
+        cnt = slice == 0 ? kTileQ * kTileK : 0;
+      } else if (!empty) {
+        for (int t = t0; t < t1; ++t) {
+          const int lo = d[t].x;
+          const int hi = d[t].y & 0x7fffffff;
+          const int a = max(lo, c0), b = min(hi, c1);
+          cnt += max(0, b - a);
+          if (d[t].y < 0) {
+            const int pr = row0 + t;
+            if (pr >= c0 && pr < c1 && !(pr >= lo && pr < hi)) cnt += 1;
+          }
+        }
       }
     }
-    const uint8_t cls = cnt == 0 ? RK_TILE_EMPTY : (cnt == kTileQ * kTileK ? RK_TILE_FULL : RK_TILE_PARTIAL);
-    const int64_t t_idx = m.tile_off + (int64_t)qt * m.nkt + kt;
-    P.tile_count[t_idx] = cnt;
-    P.tile_class[t_idx] = cls;
-    pairs += cnt;
-    nnz += cnt > 0;
-    nfull += cls == RK_TILE_FULL;
+    for (int o = 1; o < S; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
+    if (kt < m.nkt && slice == 0) {
+      const uint8_t cls =
+          cnt == 0 ? RK_TILE_EMPTY : (cnt == kTileQ * kTileK ? RK_TILE_FULL : RK_TILE_PARTIAL);
+      const int64_t t_idx = m.tile_off + (int64_t)qt * m.nkt + kt;
+      P.tile_count[t_idx] = cnt;
+      P.tile_class[t_idx] = cls;
+      pairs += cnt;
+      nnz += cnt > 0;
+      nfull += cls == RK_TILE_FULL;
+    }
   }
   // block sums: wave sums, then one LDS atomic per wave
   pairs = wave_sum(pairs);
@@ -246,29 +301,6 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(PlanDev P, int NQ, int6
   }
 }
 
-// One block per q-tile: ascending list of its non-empty k-tiles.
-__global__ __launch_bounds__(256) void plan_csr_kernel(PlanDev P) {
-  __shared__ int smem[32];
-  const int g = blockIdx.x;
-  const ReqMeta m = P.req[P.qt_req[g]];
-  const int qt = g - m.qt_off;
-  const int64_t row = m.tile_off + (int64_t)qt * m.nkt;
-  const int base = P.qtile_ptr[g];
-  int run = 0;
-  for (int k0 = 0; k0 < m.nkt; k0 += blockDim.x) {
-    const int kt = k0 + threadIdx.x;
-    const int flag = kt < m.nkt && P.tile_count[row + kt] > 0;
-    int total;
-    const int ex = block_exclusive_scan(flag, smem, &total);
-    if (flag) {
-      P.ktile_idx[base + run + ex] = kt;
-      P.ktile_word[base + run + ex] =
-          (int)((unsigned)kt | ((unsigned)(P.tile_class[row + kt] == RK_TILE_PARTIAL) << 31));
-    }
-    run += total;
-  }
-}
-
 // Rank sort of n tiles of one request by non-empty count, descending, ties
 // by tile index: order[rank] = off + tile.  One block.
 __device__ __forceinline__ void rank_order(int n, int off, const int* __restrict__ nnz,
@@ -302,19 +334,37 @@ __device__ __forceinline__ void rank_order(int n, int off, const int* __restrict
   }
 }
 
-// One block per request: q-tiles ordered by non-empty k-tile count,
-// descending, ties by q-tile index.
-__global__ __launch_bounds__(256) void plan_qsort_kernel(PlanDev P) {
+// Blocks 0 .. NQ - 1, one per q-tile: ascending list of its non-empty
+// k-tiles.  Blocks NQ .. NQ + R - 1, one per request: its q-tiles ordered
+// by non-empty k-tile count, descending, ties by q-tile index.
+__global__ __launch_bounds__(256) void plan_csr_sort_kernel(PlanDev P, int NQ) {
+  __shared__ int smem[32];
   __shared__ __attribute__((aligned(16))) int chunk[1024];
-  const ReqMeta m = P.req[blockIdx.x];
-  rank_order(m.nqt, m.qt_off, P.qt_nnz + m.qt_off, P.qorder, chunk);
+  if ((int)blockIdx.x >= NQ) {
+    const ReqMeta m = P.req[blockIdx.x - NQ];
+    rank_order(m.nqt, m.qt_off, P.qt_nnz + m.qt_off, P.qorder, chunk);
+    return;
+  }
+  const int g = blockIdx.x;
+  const ReqMeta m = P.req[P.qt_req[g]];
+  const int qt = g - m.qt_off;
+  const int64_t row = m.tile_off + (int64_t)qt * m.nkt;
+  const int base = P.qtile_ptr[g];
+  int run = 0;
+  for (int k0 = 0; k0 < m.nkt; k0 += blockDim.x) {
+    const int kt = k0 + threadIdx.x;
+    const int flag = kt < m.nkt && P.tile_count[row + kt] > 0;
+    int total;
+    const int ex = block_exclusive_scan(flag, smem, &total);
+    if (flag) {
+      P.ktile_idx[base + run + ex] = kt;
+      P.ktile_word[base + run + ex] =
+          (int)((unsigned)kt | ((unsigned)(P.tile_class[row + kt] == RK_TILE_PARTIAL) << 31));
+    }
+    run += total;
+  }
 }
 
-// One thread per launch slot: slot s runs on XCD s % 8 as item s / 8 of
-// that XCD's queue.  With cand_only, a query tile without a CANDIDATE row
-// gets no work (-1): candidates are the last segment of a request, so the
-// tiles kept are the ones from the tile of the first candidate on, which
-// within a group come first in the descending-work order.
 // The group `ga` and rank `k` whose item sits at position `idx` of XCD
 // queue `q` of a blocked schedule (groups sorted by (queue, base), the
 // groups of a block share the block's first slot as base; ilv as
@@ -346,6 +396,11 @@ __device__ void slot_of(const Group* groups, const int32_t* qstart, const int32_
   *ga = f + (local - C[lo]);
 }
 
+// One thread per launch slot: slot s runs on XCD s % 8 as item s / 8 of
+// that XCD's queue.  With cand_only, a query tile without a CANDIDATE row
+// gets no work (-1): candidates are the last segment of a request, so the
+// tiles kept are the ones from the tile of the first candidate on, which
+// within a group come first in the descending-work order.
 __global__ void plan_sched_kernel(PlanDev P, int64_t slots, int H, int cand_only, int G) {
   const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= slots) return;
@@ -580,8 +635,8 @@ hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
   }
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s, P, (int)p->NQ, p->NT);
   if (p->NQ > 0) {
-    hipLaunchKernelGGL(plan_csr_kernel, dim3((unsigned)p->NQ), dim3(256), 0, s, P);
-    hipLaunchKernelGGL(plan_qsort_kernel, dim3(p->R), dim3(256), 0, s, P);
+    hipLaunchKernelGGL(plan_csr_sort_kernel, dim3((unsigned)(p->NQ + p->R)), dim3(256), 0, s, P,
+                       (int)p->NQ);
   }
   if (p->slots > 0) {
     hipLaunchKernelGGL(plan_sched_kernel, dim3((unsigned)((p->slots + 255) / 256)), dim3(256), 0, s,
