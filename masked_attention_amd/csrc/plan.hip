@@ -23,16 +23,6 @@
 namespace rk {
 namespace {
 
-__device__ __forceinline__ int find_request(const ReqMeta* __restrict__ req, int R, int tok) {
-  // last request whose first token is <= tok; it is never empty
-  int a = 0, b = R;
-  while (a < b) {
-    int m = (a + b) >> 1;
-    if (req[m].tok_off <= tok) a = m + 1; else b = m;
-  }
-  return a - 1;
-}
-
 // number of keys in ts[0, n) with value <= x (ts non-decreasing)
 __device__ __forceinline__ int count_le(const int64_t* __restrict__ ts, int n, int64_t x) {
   int a = 0, b = n;
@@ -91,12 +81,26 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* smem, int* total
   return res;
 }
 
-__global__ void plan_seg_kernel(PlanDev P, int R, int T, const uint8_t* __restrict__ kind,
-                                const int64_t* __restrict__ ts, int check_static_time) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T) return;
-  const int r = find_request(P.req, R, i);
-  const int p = i - P.req[r].tok_off;
+// Token of thread t of block g (one block of kTileQ threads per global
+// q-tile): row t of the q-tile, or -1 past the request's end.  The q-tile's
+// request comes from the host-built qt_req table, not from a search.
+__device__ __forceinline__ int tile_token(const PlanDev& P, int* r_out, int* p_out) {
+  const int g = blockIdx.x;
+  const int r = P.qt_req[g];
+  const ReqMeta m = P.req[r];
+  const int p = (g - m.qt_off) * kTileQ + (int)threadIdx.x;
+  *r_out = r;
+  *p_out = p;
+  return p < m.len ? m.tok_off + p : -1;
+}
+
+__global__ __launch_bounds__(kTileQ) void plan_seg_kernel(PlanDev P,
+                                                          const uint8_t* __restrict__ kind,
+                                                          const int64_t* __restrict__ ts,
+                                                          int check_static_time) {
+  int r, p;
+  const int i = tile_token(P, &r, &p);
+  if (i < 0) return;
   unsigned err = 0;
   int s = kind[i];
   if (s > RK_SEG_CANDIDATE) { err |= kErrSegment; s = RK_SEG_CANDIDATE; }
@@ -116,14 +120,15 @@ __global__ void plan_seg_kernel(PlanDev P, int R, int T, const uint8_t* __restri
   if (err) atomicOr(&P.totals->errors, err);
 }
 
-__global__ void plan_rowdesc_kernel(PlanDev P, int R, int T, const uint8_t* __restrict__ kind,
-                                    const int64_t* __restrict__ ts, int64_t delay, int window,
-                                    int global_tail, int bidir) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T) return;
-  const int r = find_request(P.req, R, i);
+__global__ __launch_bounds__(kTileQ) void plan_rowdesc_kernel(PlanDev P,
+                                                              const uint8_t* __restrict__ kind,
+                                                              const int64_t* __restrict__ ts,
+                                                              int64_t delay, int window,
+                                                              int global_tail, int bidir) {
+  int r, p;
+  const int i = tile_token(P, &r, &p);
+  if (i < 0) return;
   const ReqMeta m = P.req[r];
-  const int p = i - m.tok_off;
   const int L = m.len;
   // segment boundaries, made monotone and clamped so that any device data
   // yields in-range descriptors
@@ -622,11 +627,11 @@ __global__ void plan_ksched_kernel(PlanDev P, int64_t slots, int H, int G) {
 hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
   const PlanDev& P = p->dev;
   if (p->T > 0) {
-    const int blocks = (p->T + 255) / 256;
+    // one block per global q-tile (NQ > 0 whenever T > 0)
     const int check_static = (!(p->flags & RK_STATIC_BIDIRECTIONAL)) && p->delay > 0;
-    hipLaunchKernelGGL(plan_seg_kernel, dim3(blocks), dim3(256), 0, s, P, p->R, p->T,
+    hipLaunchKernelGGL(plan_seg_kernel, dim3((unsigned)p->NQ), dim3(kTileQ), 0, s, P,
                        p->seg_kind_dev, p->timestamps_dev, check_static);
-    hipLaunchKernelGGL(plan_rowdesc_kernel, dim3(blocks), dim3(256), 0, s, P, p->R, p->T,
+    hipLaunchKernelGGL(plan_rowdesc_kernel, dim3((unsigned)p->NQ), dim3(kTileQ), 0, s, P,
                        p->seg_kind_dev, p->timestamps_dev, p->delay, p->window,
                        p->global_tail, (int)((p->flags & RK_STATIC_BIDIRECTIONAL) != 0));
   }
