@@ -194,6 +194,29 @@ def test_plan_bit_exact_random(rk, seed):
         _check_plan(wl, plan, ref)
 
 
+@pytest.mark.parametrize("delay,window,bidir", [(0, 0, False), (3600, 0, False), (0, 300, False),
+                                                 (1800, 1000, False), (0, 0, True)])
+def test_plan_bit_exact_lengths(rk, delay, window, bidir):
+    """Requests whose k-tile counts give every split of a tile's rows over
+    lanes in the tile-count kernel (1 to 64 lanes per k-tile: 129+, 65-128,
+    33-64, 17-32, 9-16, 5-8, 3-4 and 1-2 k-tiles), with candidates and
+    real-time tokens, counted bit-exactly against the oracle."""
+    rng = np.random.default_rng(7 + delay + window + bidir)
+    reqs = []
+    for n in (9000, 5000, 3000, 1500, 700, 400, 200, 100, 1):
+        hist = np.sort(rng.integers(NOW - 10**6, NOW - 3600, n)).astype(np.int64)
+        rt = np.sort(rng.integers(NOW - 3600, NOW, 40)).astype(np.int64)
+        reqs.append([(HISTORY, hist), (REALTIME, rt), (CANDIDATE, np.full(25, NOW, np.int64))])
+    wl = make_custom(reqs, heads=2, d_head=64, dtype="bf16", delay=delay, window=window,
+                     static_bidirectional=bidir, with_qkv=False, name="lengths")
+    _say(f"[gpu] plan lengths delay={delay} window={window} bidir={bidir}")
+    batch, plan = _plan(rk, wl)
+    ref = oracle.tile_plan(wl.req_offsets, wl.seg_kind, wl.timestamps, delay=delay,
+                           window=window, static_bidirectional=bidir)
+    _check_plan(wl, plan, ref)
+    plan.close()
+
+
 @pytest.mark.parametrize("G", [1, 37, 300])
 def test_plan_and_attention_global_tail(rk, G):
     """LazFormer global-tail queries (eq. 19-21, G > 0) with a window and a
