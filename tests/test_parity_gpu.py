@@ -432,6 +432,35 @@ def test_attention_workloads_sampled(rk, cfg):
             assert np.all(o[a] == 0.0) and np.all(np.isneginf(lse[:, a]))
 
 
+@pytest.mark.parametrize("delay,window", [(0, 0), (3600, 4096)])
+def test_attention_long_request(rk, delay, window):
+    """One request of 131,072 history tokens and 64 candidates (2048 k-tiles
+    per q-tile row, 8.6e9 visible pairs per head: past 32-bit counts).  The
+    plan's total is checked against the closed form when no delay or
+    window applies (causal history L (L + 1) / 2, each candidate L keys and
+    itself); sampled output rows against the oracle."""
+    rng = np.random.default_rng(131 + delay)
+    Lh, Nc = 131072, 64
+    hist = np.sort(rng.integers(NOW - 10**8, NOW - 60, Lh)).astype(np.int64)
+    wl = make_custom([[(HISTORY, hist), (CANDIDATE, np.full(Nc, NOW, np.int64))]], heads=2,
+                     d_head=64, dtype="bf16", seed=131, delay=delay, window=window,
+                     name="long-request")
+    plan, o, lse = _run(rk, wl)
+    st = plan.stats()
+    assert st["device_errors"] == 0
+    if delay == 0 and window == 0:
+        assert st["visible_pairs"] == Lh * (Lh + 1) // 2 + Nc * (Lh + 1)
+    toks = np.unique(np.concatenate([
+        np.array([0, 1, 63, 64, 127, 128, 4095, 4096, 65535, 65536, Lh - 1, Lh, Lh + Nc - 1]),
+        rng.integers(0, Lh + Nc, 24)])).astype(np.int64)
+    for h in range(wl.heads):
+        ref, ref_lse = oracle.attention_rows(wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q,
+                                             wl.k, wl.v, toks, h, delay=delay, window=window,
+                                             static_bidirectional=False, rope=_rope(wl))
+        _check(wl, o[toks, h], ref, lse[h, toks], ref_lse)
+    plan.close()
+
+
 def test_prerotated_k_matches_fused_path(rk):
     """rk_time_rope on K followed by the attention with RK_ATTN_K_PREROTATED
     gives the same bits as the attention rotating K itself."""
