@@ -143,9 +143,18 @@ enum { RK_TILE_EMPTY = 0, RK_TILE_PARTIAL = 1, RK_TILE_FULL = 2 };
  *   seg_kind_dev          : uint8 [total_tokens], RK_SEG_*; non-decreasing
  *                           inside each request.
  *   timestamps_dev        : int64 [total_tokens], seconds.  Must be
- *                           non-decreasing inside REALTIME, and inside
- *                           PROFILE+HISTORY when the static part is causal
- *                           and delay > 0.
+ *                           non-decreasing inside REALTIME and, when the
+ *                           static part is causal and delay > 0, inside
+ *                           PROFILE and inside HISTORY (each on its own).
+ *                           In that mode the keys a static row sees by the
+ *                           delay rule are a prefix of PROFILE and a prefix
+ *                           of HISTORY, and they must form one run of
+ *                           positions: profile tokens dated at the anchor
+ *                           ("now", the pages give them no time) or dated
+ *                           no later than the first history token always
+ *                           do; profile times interleaved with history
+ *                           times can leave a row with two runs, which is
+ *                           reported as RK_ERR_UNSORTED_TIME.
  *   anchors_dev           : int64 [num_requests]; time origin of each
  *                           request's RoPE angles (any value; outputs of
  *                           the attention do not depend on it).
@@ -251,7 +260,8 @@ typedef struct rk_plan_info {
 /* Totals of a plan (per head). */
 typedef struct rk_plan_totals {
   uint32_t struct_size;
-  uint32_t device_errors;      /* bit 0: segment order/kind, bit 1: timestamp order */
+  uint32_t device_errors;      /* bit 0: segment order/kind, bit 1: timestamp order,
+                                  bit 2: a static row's delayed keys form two runs */
   int64_t visible_pairs;       /* sum of all tile counts */
   int64_t full_tiles;
   int64_t partial_tiles;

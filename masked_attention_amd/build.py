@@ -44,8 +44,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(objdir, src + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-        cmd = [hipcc, *COMMON, *DEVICE, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        # every source, the host-only .cpp files included, is compiled as HIP
+        # (they use the HIP runtime's types and launch the kernels)
+        cmd = [hipcc, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

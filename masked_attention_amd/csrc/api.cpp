@@ -513,7 +513,7 @@ rk_status rk_plan_stats(const rk_plan* p, rk_plan_totals* out, void* stream) {
   out->work_entries = t.n_work;
   out->split_items = t.n_splits;
   if (t.errors & rk::kErrSegment) return RK_ERR_SEGMENT_ORDER;
-  if (t.errors & rk::kErrTime) return RK_ERR_UNSORTED_TIME;
+  if (t.errors & (rk::kErrTime | rk::kErrStaticSplit)) return RK_ERR_UNSORTED_TIME;
   return RK_OK;
 }
 
@@ -573,6 +573,8 @@ rk_status rk_qk_norm_rope(const rk_batch* b, const rk_rope_params* r, float eps,
                                  (hipStream_t)stream, true, eps, gamma);
   return e == hipSuccess ? RK_OK : RK_ERR_HIP;
 }
+
+}  // extern "C"
 
 namespace {
 
@@ -636,6 +638,8 @@ size_t attn_ws_bytes(const rk_plan* p, const rk_attn_args* a) {
 }
 
 }  // namespace
+
+extern "C" {
 
 rk_status rk_attn_workspace_size(const rk_plan* p, const rk_attn_args* a, size_t* bytes) {
   if (!bytes) return RK_ERR_INVALID_ARG;
@@ -777,6 +781,8 @@ rk_status rk_pointwise_attn_fwd(const rk_plan* p, const rk_pointwise_args* a, vo
   return e == hipSuccess ? RK_OK : RK_ERR_HIP;
 }
 
+}  // extern "C"
+
 namespace {
 
 rk_status check_bwd(const rk_plan* p, const rk_attn_bwd_args* a) {
@@ -891,6 +897,8 @@ hipError_t norm_bwd(const rk_plan* p, const rk_attn_bwd_args* a, const void* x, 
 }
 
 }  // namespace
+
+extern "C" {
 
 rk_status rk_attn_bwd_workspace_size(const rk_plan* p, const rk_attn_bwd_args* a, size_t* bytes) {
   if (!bytes) return RK_ERR_INVALID_ARG;

@@ -42,6 +42,7 @@ struct PwView {
   const int32_t* qtile_ptr;
   const int32_t* ktile_word;
   const int32_t* sched;
+  const unsigned* info;  // plan info word (kInfoHistoryUnsorted)
 };
 
 // LDS K / V tiles: 64 rows of 128 bytes, 16-byte chunk c of row r in slot
@@ -124,14 +125,15 @@ __device__ __forceinline__ void pw_weights(bf16x8 (&pb)[4], const f32x16& s0, co
 }
 
 // One key tile for one wave.  seg_sorted: the tile's keys all lie in one
-// segment whose timestamps are non-decreasing (HISTORY or REALTIME), so
-// their time range is given by the first and the last key.
+// segment whose timestamps are non-decreasing (REALTIME, or HISTORY when
+// the planner found every history in time order), so their time range is
+// given by the first and the last key.
 __device__ __forceinline__ void pw_tile(f32x16& o0, f32x16& o1, const unsigned short* kb,
                                         const unsigned short* vb, const int64_t* tk,
                                         const Tabs& tab, const bf16x8 (&q)[4], int kt, bool partial,
                                         int L, int li, int hh, int lo, int hi, int self, int row,
                                         int64_t ti, const PwLaunch& A, bool has_pos,
-                                        bool has_time, const ReqMeta& m) {
+                                        bool has_time, const ReqMeta& m, bool hist_sorted) {
   const int c0 = kt * kTileK;
   const int nr = min(L - c0, kTileK);  // keys of the tile inside the request
   // ---- is the bias constant over this tile for the lane's row?
@@ -144,7 +146,8 @@ __device__ __forceinline__ void pw_tile(f32x16& o0, f32x16& o1, const unsigned s
   }
   if (has_time) {
     const int c1 = c0 + nr;
-    const bool seg_sorted = (c0 >= m.seg[RK_SEG_HISTORY] && c1 <= m.seg[RK_SEG_REALTIME]) ||
+    const bool seg_sorted =
+        (hist_sorted && c0 >= m.seg[RK_SEG_HISTORY] && c1 <= m.seg[RK_SEG_REALTIME]) ||
                             (c0 >= m.seg[RK_SEG_REALTIME] && c1 <= m.seg[RK_SEG_CANDIDATE]);
     int64_t tmin, tmax;
     if (seg_sorted) {
@@ -274,6 +277,7 @@ __global__ __launch_bounds__(kThreads, 3) void pw_mfma_bf16_d64_kernel(PwView P,
   const int hi = rvalid ? dsc.y & 0x7fffffff : 0;
   const int self = rvalid && dsc.y < 0;
   const bool has_pos = A.pos_bias != nullptr, has_time = A.time_bias != nullptr;
+  const bool hist_sorted = !(ldc(P.info, 0) & kInfoHistoryUnsorted);
   for (int x = tid; x < A.np && has_pos; x += kThreads) tab.pos[x] = A.pos_bias[x];
   for (int x = tid; x < A.nt && has_time; x += kThreads) tab.time[x] = A.time_bias[x];
 
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 3) void pw_mfma_bf16_d64_kernel(PwView P,
       const int w_nxt = ldc(P.ktile_word, e0 + min(it + 1, n - 1));
       issue(K1, V1, T1, w_nxt & 0x7fffffff);
       pw_tile(o0, o1, K0, V0, T0, tab, q, w_cur & 0x7fffffff, w_cur < 0, L, li, hh, lo, hi,
-              self, row, ti, A, has_pos, has_time, m);
+              self, row, ti, A, has_pos, has_time, m, hist_sorted);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       w_cur = w_nxt;
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 3) void pw_mfma_bf16_d64_kernel(PwView P,
       const int w_nxt = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
       issue(K0, V0, T0, w_nxt & 0x7fffffff);
       pw_tile(o0, o1, K1, V1, T1, tab, q, w_cur & 0x7fffffff, w_cur < 0, L, li, hh, lo, hi,
-              self, row, ti, A, has_pos, has_time, m);
+              self, row, ti, A, has_pos, has_time, m, hist_sorted);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       w_cur = w_nxt;
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 3) void pw_mfma_bf16_d64_kernel(PwView P,
 hipError_t launch_pointwise_mfma_bf16_d64(const rk_plan* p, const PwLaunch& a, hipStream_t s) {
   if (p->slots == 0) return hipSuccess;
   PwView P{p->dev.req, p->dev.qt_req, p->dev.row_desc, p->dev.qtile_ptr, p->dev.ktile_word,
-           p->dev.sched};
+           p->dev.sched, &p->dev.totals->info};
   hipLaunchKernelGGL(pw_mfma_bf16_d64_kernel, dim3((unsigned)p->slots), dim3(kThreads), 0, s, P,
                      a);
   return hipGetLastError();

@@ -6,9 +6,17 @@
 // LazFormer eq. 19-21; MTGR mixed dynamic mask) gives every query row a
 // visible key set that is one interval [lo, hi) of request-local positions
 // plus, for candidates, the row itself:
-//   static query, causal   : [max(0, p-W+1), min(p+1, cut)) where cut is the
-//                            number of static keys with t_j <= t_i - delay
-//                            (static times are sorted, so a binary search);
+//   static query, causal   : [max(0, p-W+1), p+1) intersected, with a delay,
+//                            with the keys dated at or before t_i - delay:
+//                            a prefix of PROFILE and a prefix of HISTORY
+//                            (each segment is in time order, so one binary
+//                            search per segment).  Their union is one run
+//                            when every profile key is that old (profile
+//                            dated before the history), when no profile key
+//                            is (profile dated at the anchor, "now"), or
+//                            when one of the two parts falls outside the
+//                            causal window; a row left with two runs is
+//                            reported as a timestamp-order error.
 //                            lo = 0 for the last G static rows (global tail)
 //   static query, bidir.   : [0, end of static)
 //   real-time query        : [0, p+1)  (static part, then real-time events up
@@ -101,7 +109,7 @@ __global__ __launch_bounds__(kTileQ) void plan_seg_kernel(PlanDev P,
   int r, p;
   const int i = tile_token(P, &r, &p);
   if (i < 0) return;
-  unsigned err = 0;
+  unsigned err = 0, info = 0;
   int s = kind[i];
   if (s > RK_SEG_CANDIDATE) { err |= kErrSegment; s = RK_SEG_CANDIDATE; }
   int prev = -1;
@@ -110,14 +118,18 @@ __global__ __launch_bounds__(kTileQ) void plan_seg_kernel(PlanDev P,
     if (prev > RK_SEG_CANDIDATE) prev = RK_SEG_CANDIDATE;
     if (s < prev) {
       err |= kErrSegment;
-    } else {
-      const bool rt = (s == RK_SEG_REALTIME && prev == RK_SEG_REALTIME);
-      const bool st = check_static_time && s <= RK_SEG_HISTORY && prev <= RK_SEG_HISTORY;
-      if ((rt || st) && ts[i] < ts[i - 1]) err |= kErrTime;
+    } else if (s == prev && ts[i] < ts[i - 1]) {
+      // real-time events must be in time order; PROFILE and HISTORY each
+      // must be when the delay rule searches them.  An out-of-order history
+      // is otherwise allowed and only noted (the pointwise form then reads
+      // its key-time ranges key by key).
+      if (s == RK_SEG_REALTIME || (check_static_time && s <= RK_SEG_HISTORY)) err |= kErrTime;
+      if (s == RK_SEG_HISTORY) info = kInfoHistoryUnsorted;
     }
   }
   for (int k = prev + 1; k <= s; ++k) P.req[r].seg[k] = p;
   if (err) atomicOr(&P.totals->errors, err);
+  if (info) atomicOr(&P.totals->info, info);
 }
 
 __global__ __launch_bounds__(kTileQ) void plan_rowdesc_kernel(PlanDev P,
@@ -145,7 +157,25 @@ __global__ __launch_bounds__(kTileQ) void plan_rowdesc_kernel(PlanDev P,
       hi = min(p + 1, a_rt);
       // the last global_tail static positions are global queries (no window)
       lo = (window > 0 && p < a_rt - global_tail) ? max(0, p - window + 1) : 0;
-      if (delay > 0) hi = min(hi, count_le(tr, a_rt, ts[i] - delay));
+      if (delay > 0) {
+        // keys dated at or before the cut: [0, cp) of PROFILE and
+        // [a_h, a_h + ch) of HISTORY
+        const int a_h = min(max(m.seg[RK_SEG_HISTORY], 0), a_rt);
+        const int64_t cut = ts[i] - delay;
+        const int cp = count_le(tr, a_h, cut);
+        const int ch = count_le(tr + a_h, a_rt - a_h, cut);
+        const bool prof_run = min(cp, hi) > lo;
+        const bool hist_run = min(a_h + ch, hi) > max(a_h, lo);
+        if (cp == a_h) {
+          hi = min(hi, a_h + ch);  // the whole profile, then a history prefix
+        } else if (hist_run) {
+          if (prof_run) atomicOr(&P.totals->errors, kErrStaticSplit);  // two runs
+          lo = max(lo, a_h);
+          hi = min(hi, a_h + ch);
+        } else {
+          hi = min(hi, cp);
+        }
+      }
     }
   } else if (s == RK_SEG_REALTIME) {
     hi = p + 1;
@@ -179,7 +209,7 @@ __global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
   const int row0 = qt * kTileQ;
   const int nrows = min(kTileQ, m.len - row0);
   if (threadIdx.x < kTileQ)
-    d[threadIdx.x] = threadIdx.x < nrows ? P.row_desc[m.tok_off + row0 + threadIdx.x] : make_int2(0, 0);
+    d[threadIdx.x] = (int)threadIdx.x < nrows ? P.row_desc[m.tok_off + row0 + threadIdx.x] : make_int2(0, 0);
   if (threadIdx.x == 0) {
     pairs_s = 0; nnz_s = 0; full_s = 0;
     lim[0] = INT_MIN; lim[1] = INT_MAX; lim[2] = INT_MAX; lim[3] = INT_MIN;

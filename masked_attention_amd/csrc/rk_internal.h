@@ -53,11 +53,12 @@ struct PlanTotals {
   unsigned long long full_tiles;
   unsigned long long partial_tiles;
   unsigned long long empty_tiles;
-  unsigned int errors;  // bit 0: segment order/kind, bit 1: time order
+  unsigned int errors;  // kErrSegment | kErrTime | kErrStaticSplit
   int n_work;           // work-list entries (candidates-only plans)
   int n_splits;         // items split into partial results
   int n_act;            // active schedule slots (candidates-only plans)
-  unsigned int pad[4];
+  unsigned int info;    // kInfoHistoryUnsorted (not an error)
+  unsigned int pad[3];
 };
 
 // Work list of a candidates-only plan: launch slot b of the attention runs
@@ -79,8 +80,14 @@ constexpr int kSplitTarget = RK_SPLIT_SLOTS;
 constexpr int kSplitMinChunk = 8;
 constexpr int kMaxParts = 2 * kSplitTarget;
 
-constexpr unsigned kErrSegment = 1u;
-constexpr unsigned kErrTime = 2u;
+constexpr unsigned kErrSegment = 1u;      // segment kinds out of order or out of range
+constexpr unsigned kErrTime = 2u;         // timestamps out of order where the mask needs order
+constexpr unsigned kErrStaticSplit = 4u;  // a static row's visible keys would form two runs
+                                          // (profile times interleaved with history times)
+// Some HISTORY segment is not in time order (allowed when no delay rule
+// searches it): kernels must not take a history tile's time range from its
+// end keys.
+constexpr unsigned kInfoHistoryUnsorted = 1u;
 
 // Device pointers of a plan (all inside the caller's workspace).
 struct PlanDev {

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void rope_kernel(int R, int Tn, const int32_t*
                                                    const float* __restrict__ gamma) {
   __shared__ double w[kMaxHalfD];
   const int half = d >> 1;
-  if (threadIdx.x < half) w[threadIdx.x] = tab.w_rev[threadIdx.x];
+  if ((int)threadIdx.x < half) w[threadIdx.x] = tab.w_rev[threadIdx.x];
   __syncthreads();
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)Tn * half) return;
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void rope8_kernel(int R, int Tn, const int32_t
                                                     const float* __restrict__ gamma) {
   __shared__ double w[kMaxHalfD];
   const int half = d >> 1;
-  if (threadIdx.x < half) w[threadIdx.x] = tab.w_rev[threadIdx.x];
+  if ((int)threadIdx.x < half) w[threadIdx.x] = tab.w_rev[threadIdx.x];
   __syncthreads();
   const int groups = d >> 3;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

@@ -259,9 +259,12 @@ def random_layout(rng: np.random.Generator, n_requests: int, max_len: int, *,
                   kinds=(PROFILE, HISTORY, REALTIME, CANDIDATE), allow_empty: bool = True):
     """Random ragged requests (segment lengths may be zero) for edge-case tests.
 
-    Profile tokens get the earliest history timestamp (or one day ago), so the
-    static part is in time order; real-time events are sorted; candidate times
-    are in random order.
+    Profile tokens are dated, per request: at the anchor NOW (the pages give
+    profile tokens no time; half of the requests), at the earliest history
+    timestamp (a quarter), or at sorted times up to 30 days before the
+    earliest history timestamp (a quarter).  Every choice keeps PROFILE and
+    HISTORY each in time order.  Real-time events are sorted; candidate
+    times are in random order.
     """
     reqs = []
     for _ in range(n_requests):
@@ -269,12 +272,18 @@ def random_layout(rng: np.random.Generator, n_requests: int, max_len: int, *,
         cuts = np.sort(rng.integers(0, budget + 1, size=len(kinds) - 1))
         lens = dict(zip(kinds, (int(x) for x in np.diff(np.concatenate([[0], cuts, [budget]])))))
         hist = history_raw(rng, lens.get(HISTORY, 0), NOW - DAY)
-        t_prof = int(hist[0]) if hist.shape[0] else NOW - DAY
+        t_first = int(hist[0]) if hist.shape[0] else NOW - DAY
+        prof_mode = int(rng.integers(0, 4))
         segs = []
         for kind in kinds:
             n = lens[kind]
             if kind == PROFILE:
-                ts = np.full(n, t_prof, np.int64)
+                if prof_mode < 2:
+                    ts = np.full(n, NOW, np.int64)
+                elif prof_mode == 2:
+                    ts = np.full(n, t_first, np.int64)
+                else:
+                    ts = np.sort(rng.integers(t_first - 30 * DAY, t_first + 1, size=n)).astype(np.int64)
             elif kind == HISTORY:
                 ts = hist
             elif kind == REALTIME:

@@ -116,6 +116,34 @@ def test_pointwise_long_history_fast_and_slow_bias(rk):
             _check("bf16", o[toks, h].float().cpu().numpy().astype(np.float64), ref)
 
 
+def test_pointwise_unsorted_history(rk):
+    """Histories out of time order are allowed without a delay rule; the
+    planner notes them and the MFMA kernel then takes every history tile's
+    time range key by key instead of from its end keys.  Time buckets of
+    one second: any misjudged range changes a bucket inside a tile."""
+    rng = np.random.default_rng(19)
+    reqs = []
+    for n in (700, 260, 1):
+        h = history_span(rng, n, NOW - 60)
+        rng.shuffle(h[: n // 2])  # older half shuffled
+        reqs.append([(HISTORY, h), (CANDIDATE, np.full(5, NOW, np.int64))])
+    wl = make_custom(reqs, heads=2, d_head=64, dtype="bf16", seed=19)
+    assert np.any(np.diff(wl.timestamps[:700]) < 0)
+    tb = (rng.standard_normal(26) * 0.5).astype(np.float32)
+    batch = rk.Batch.from_workload(wl)
+    plan = rk.Plan(batch, num_heads=2)
+    assert plan.stats()["status"] == 0
+    q, k, v = (torch.from_numpy(a).cuda().to(torch.bfloat16) for a in (wl.q, wl.k, wl.v))
+    o = rk.rk_pointwise_attn_fwd(plan, q, k, v, scale=0.125, time_bias=torch.from_numpy(tb).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.pointwise_attention_forward(wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q,
+                                             wl.k, wl.v, delay=0, window=0,
+                                             static_bidirectional=False, scale=0.125,
+                                             time_bias=tb.astype(np.float64))
+    _check("bf16", o.float().cpu().numpy().astype(np.float64), ref)
+    plan.close()
+
+
 def test_pointwise_workload_sampled(rk):
     """TM20K-shaped batch (8 x (20000 + 1), H = 8), causal, rab tables of 128
     position and 32 time buckets, on sampled rows of two requests."""
