@@ -64,12 +64,14 @@ TILE_Q, TILE_K = 128, 64
 
 def visible_rows(seg_kind: np.ndarray, timestamps: np.ndarray, rows: np.ndarray, *,
                  delay: int, window: int, static_bidirectional: bool,
-                 global_tail: int = 0) -> np.ndarray:
-    """Visibility of every key for the query rows `rows` of ONE request.
+                 global_tail: int = 0, cols: Optional[np.ndarray] = None) -> np.ndarray:
+    """Visibility of every key (or of the keys `cols`) for the query rows
+    `rows` of ONE request.
 
-    Returns a bool array [len(rows), L]: True where query i may attend key j.
-    Each entry is the rule applied to the pair (i, j) on its own; evaluating
-    a subset of rows gives the same entries as the full matrix.
+    Returns a bool array [len(rows), L] (or [len(rows), len(cols)]): True
+    where query i may attend key j.  Each entry is the rule applied to the
+    pair (i, j) on its own; evaluating a subset of rows or keys gives the same
+    entries as the full matrix.
 
     global_tail (LazFormer section 2.3, eq. 19-21, G): the last G static
     (profile + history) positions are global queries, exempt from the
@@ -79,12 +81,13 @@ def visible_rows(seg_kind: np.ndarray, timestamps: np.ndarray, rows: np.ndarray,
     t = np.asarray(timestamps, dtype=np.int64)
     L = seg_kind.shape[0]
     rows = np.asarray(rows, dtype=np.int64)
+    cols = np.arange(L, dtype=np.int64) if cols is None else np.asarray(cols, dtype=np.int64)
     pi = rows[:, None]
-    pj = np.arange(L, dtype=np.int64)[None, :]
+    pj = cols[None, :]
     si = seg_kind[rows][:, None]
-    sj = seg_kind[None, :]
+    sj = seg_kind[cols][None, :]
     ti = t[rows][:, None]
-    tj = t[None, :]
+    tj = t[cols][None, :]
 
     static_i = (si == PROFILE) | (si == HISTORY)
     static_j = (sj == PROFILE) | (sj == HISTORY)
@@ -499,8 +502,10 @@ def attention_backward_sampled(req_offsets, seg_kind, timestamps, q, k, v, do, *
     matrices do not fit.
 
     Same chain rule as masked_softmax_attention_backward.  The row softmax
-    statistics (log-sum-exp and D_i = do_i . o_i) of every row of the request
-    come first, in blocks of rows; then
+    statistics (log-sum-exp and D_i = do_i . o_i) come first, in blocks of
+    rows, for the rows the sampled gradients use: the rows of `rows` and
+    every row that sees one of `keys` (any other row has P_ij = 0 for every
+    sampled key and enters no sum below); then
       dq_i = scale * sum_j P_ij (dP_ij - D_i) k_j            for i in rows,
       dv_j = sum_i P_ij do_i,
       dk_j = scale * sum_i P_ij (dP_ij - D_i) q_i            for j in keys,
@@ -522,10 +527,18 @@ def attention_backward_sampled(req_offsets, seg_kind, timestamps, q, k, v, do, *
         kr = time_rope(kr, ts, **rope)
     margs = dict(delay=delay, window=window, static_bidirectional=static_bidirectional,
                  global_tail=global_tail)
-    lse = np.full(L, -np.inf)
-    dsum = np.zeros(L)
+    rows = np.asarray(rows, np.int64)
+    keys = np.asarray(keys, np.int64)
+    need = np.zeros(L, bool)
+    need[rows] = True
     for r0 in range(0, L, row_block):
         blk = np.arange(r0, min(L, r0 + row_block))
+        need[blk] |= visible_rows(sk, ts, blk, cols=keys, **margs).any(axis=1)
+    needed = np.nonzero(need)[0]
+    lse = np.full(L, -np.inf)
+    dsum = np.zeros(L)
+    for r0 in range(0, needed.shape[0], row_block):
+        blk = needed[r0:r0 + row_block]
         vis = visible_rows(sk, ts, blk, **margs)
         o_blk, lse[blk] = masked_softmax_attention(qr[blk], kr, vr, vis, scale)
         dsum[blk] = (gr[blk] * o_blk).sum(axis=1)
@@ -534,8 +547,6 @@ def attention_backward_sampled(req_offsets, seg_kind, timestamps, q, k, v, do, *
         s = (qr[blk] @ kr[cols].T) * scale
         return np.where(vis, np.exp(s - lse[blk][:, None]), 0.0)
 
-    rows = np.asarray(rows, np.int64)
-    keys = np.asarray(keys, np.int64)
     allk = np.arange(L)
     vis = visible_rows(sk, ts, rows, **margs)
     p = probs(rows, allk, vis)
@@ -543,9 +554,9 @@ def attention_backward_sampled(req_offsets, seg_kind, timestamps, q, k, v, do, *
     dq = (ds @ kr) * scale
     dk = np.zeros((keys.shape[0], d))
     dv = np.zeros((keys.shape[0], d))
-    for r0 in range(0, L, row_block):
-        blk = np.arange(r0, min(L, r0 + row_block))
-        visk = visible_rows(sk, ts, blk, **margs)[:, keys]
+    for r0 in range(0, needed.shape[0], row_block):
+        blk = needed[r0:r0 + row_block]
+        visk = visible_rows(sk, ts, blk, cols=keys, **margs)
         pk = probs(blk, keys, visk)
         dv += pk.T @ gr[blk]
         dsk = pk * (gr[blk] @ vr[keys].T - dsum[blk][:, None])

@@ -274,14 +274,37 @@ def test_backward_rejects_forward_only_plan(rk):
     assert e.value.status == _rk.RK_ERR_INVALID_ARG
 
 
+def _sampled_positions(wl, cfg, r, rng):
+    """Rows (dQ) and keys (dK, dV) of request r compared on a full-size
+    workload: its first and last positions, random ones and candidates.
+    On the TM20K shape the keys of requests other than the first are drawn
+    from the last 1024 positions (the oracle then needs the statistics of
+    those rows only)."""
+    a, b = wl.request(r)
+    L = b - a
+    pick = lambda lo, n: rng.choice(np.arange(lo, L), size=min(n, L - lo), replace=False)
+    rows = np.concatenate([[0, L - 1], pick(0, 6)])
+    if cfg == 5 and r > 0:
+        keys = np.concatenate([[L - 1], pick(max(0, L - 1024), 4)])
+    else:
+        keys = np.concatenate([[0, L - 1], pick(0, 6)])
+    cand = np.nonzero(wl.seg_kind[a:b] == CANDIDATE)[0]
+    if cand.shape[0]:
+        rows = np.concatenate([rows, cand[:2], cand[-2:]])
+        keys = np.concatenate([keys, cand[:2]])
+    return np.unique(rows), np.unique(keys)
+
+
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_backward_workloads_sampled(rk, cfg):
+def test_backward_workloads(rk, cfg):
     """Full-size workloads in the launch configuration the backward benchmark
     times (backward plan; forward with fused RoPE and LSE; backward with
-    RoPE), checked on sampled rows (dQ) and keys (dK, dV) of the first and
-    last requests against the oracle's per-row / per-key gradients."""
+    RoPE).  The CADET-shaped workload (2) is compared in full; the others on
+    sampled rows (dQ) and keys (dK, dV) of every request, each request on
+    its own head (head r mod H), against the oracle's per-row / per-key
+    gradients."""
     wl = make_config(cfg)
-    _say(f"[gpu] backward sampled workload {cfg}: T={wl.total_tokens} H={wl.heads}")
+    _say(f"[gpu] backward workload {cfg}: T={wl.total_tokens} H={wl.heads}")
     batch, plan = _plan(rk, wl)
     q, k, v = (torch.from_numpy(x).to("cuda").to(torch.bfloat16) for x in (wl.q, wl.k, wl.v))
     do_np = draw_grad(wl)
@@ -289,28 +312,31 @@ def test_backward_workloads_sampled(rk, cfg):
     o, lse = rk.rk_masked_attn_fwd(plan, q, k, v, rope=_rope(wl), want_lse=True)
     dq, dk, dv = rk.rk_masked_attn_bwd(plan, q, k, v, o, lse, do, rope=_rope(wl))
     torch.cuda.synchronize()
+    host = lambda x: x.float().cpu().numpy().astype(np.float64)
+    if cfg == 2:
+        rq, rk_, rv = oracle.attention_backward(
+            wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q, wl.k, wl.v, do_np, delay=wl.delay,
+            window=wl.window, static_bidirectional=wl.static_bidirectional, rope=_rope(wl))
+        _check_grad(wl, host(dq), rq, "dq")
+        _check_grad(wl, host(dk), rk_, "dk")
+        _check_grad(wl, host(dv), rv, "dv")
+        return
     rng = np.random.default_rng(cfg)
-    reqs = [0] if cfg == 5 else [0, wl.num_requests - 1]
-    heads = [wl.heads - 1] if cfg == 5 else [0, wl.heads - 1]
+    dq_h, dk_h, dv_h = host(dq), host(dk), host(dv)
     got, ref = [], []
-    for r in reqs:
+    for r in range(wl.num_requests):
         a, b = wl.request(r)
-        L = b - a
-        pick = lambda n: np.unique(np.concatenate([[0, L - 1], rng.choice(L, size=n, replace=False)]))
-        rows, keys = pick(20), pick(20)
-        cand = np.nonzero(wl.seg_kind[a:b] == CANDIDATE)[0]
-        if cand.shape[0]:
-            rows = np.unique(np.concatenate([rows, cand[:3], cand[-2:]]))
-            keys = np.unique(np.concatenate([keys, cand[:2]]))
-        for h in heads:
-            rq, rk_, rv = oracle.attention_backward_sampled(
-                wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q, wl.k, wl.v, do_np, request=r,
-                head=h, rows=rows, keys=keys, delay=wl.delay, window=wl.window,
-                static_bidirectional=wl.static_bidirectional, rope=_rope(wl),
-                global_tail=wl.global_tail)
-            f = lambda x, idx: x[a + idx, h].float().cpu().numpy().astype(np.float64)
-            got += [f(dq, rows).ravel(), f(dk, keys).ravel(), f(dv, keys).ravel()]
-            ref += [rq.ravel(), rk_.ravel(), rv.ravel()]
+        h = r % wl.heads
+        rows, keys = _sampled_positions(wl, cfg, r, rng)
+        rq, rk_, rv = oracle.attention_backward_sampled(
+            wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q, wl.k, wl.v, do_np, request=r,
+            head=h, rows=rows, keys=keys, delay=wl.delay, window=wl.window,
+            static_bidirectional=wl.static_bidirectional, rope=_rope(wl),
+            global_tail=wl.global_tail)
+        got += [dq_h[a + rows, h].ravel(), dk_h[a + keys, h].ravel(), dv_h[a + keys, h].ravel()]
+        ref += [rq.ravel(), rk_.ravel(), rv.ravel()]
+        if r % 8 == 7 or r == wl.num_requests - 1:
+            _say(f"[gpu] backward workload {cfg}: requests up to {r} sampled")
     got, ref = np.concatenate(got), np.concatenate(ref)
     _check_grad(wl, got, ref, f"workload {cfg} sampled gradients")
 

@@ -190,3 +190,24 @@ def test_first_rows_fully_masked_under_delay():
     L = 256
     assert vis[L:, :L].all()
     assert np.array_equal(vis[L:, L:], np.eye(16, dtype=bool))
+
+
+def test_key_subset_equals_full_matrix():
+    """Rows and keys evaluated as a subset give the full matrix's entries
+    (every segment kind, delay with anchor-dated and earlier profiles,
+    window, global tail)."""
+    from rk_workloads import random_layout
+    rng = np.random.default_rng(41)
+    wl = make_custom(random_layout(rng, 6, 300, allow_empty=False), heads=1, d_head=2,
+                     with_qkv=False)
+    for bidir, delay, window, G in ((True, 0, 0, 0), (False, 600, 0, 0), (False, 300, 25, 4)):
+        for r in range(wl.num_requests):
+            a, b = wl.request(r)
+            seg, ts = wl.seg_kind[a:b], wl.timestamps[a:b]
+            full = oracle.visibility(seg, ts, delay=delay, window=window,
+                                     static_bidirectional=bidir, global_tail=G)
+            rows = rng.choice(b - a, size=min(11, b - a), replace=False)
+            cols = rng.choice(b - a, size=min(13, b - a), replace=False)
+            sub = oracle.visible_rows(seg, ts, rows, delay=delay, window=window,
+                                      static_bidirectional=bidir, global_tail=G, cols=cols)
+            assert np.array_equal(sub, full[np.ix_(rows, cols)])
