@@ -98,7 +98,11 @@ def test_attention_with_qk_norm(rk, case):
     batch = rk.Batch.from_workload(wl)
     plan = rk.Plan(batch, delay=wl.delay, window=wl.window, global_tail=wl.global_tail,
                    num_heads=wl.heads)
-    q, k, v = (torch.from_numpy(a * 2.0).cuda().to(tdt) for a in (wl.q, wl.k, wl.v))
+    # Q and K scaled by 2 (the norm removes it); V as drawn, so that |O|
+    # stays well below 8, where the output's bf16 half-ulp (2^-9 |O|) alone
+    # would use most of the 2e-2 bound
+    q, k = (torch.from_numpy(a * 2.0).cuda().to(tdt) for a in (wl.q, wl.k))
+    v = torch.from_numpy(wl.v).cuda().to(tdt)
     qn, kn, vn = (t.float().cpu().numpy().astype(np.float64) for t in (q, k, v))
     for rope in (_rope(wl), None):
         for pre in (False, True):
