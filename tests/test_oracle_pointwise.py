@@ -169,4 +169,6 @@ def test_rows_form_equals_full_form():
     for h in range(2):
         rows = oracle.pointwise_attention_rows(wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q,
                                                wl.k, wl.v, toks, h, **kw)
-        assert np.array_equal(rows, o[toks, h])
+        # the same sums, run as BLAS products of different shapes: equal up to
+        # the last bits of an fp64 rounding (|o| < 100 here)
+        assert np.abs(rows - o[toks, h]).max() <= 1e-13
