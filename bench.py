@@ -79,6 +79,18 @@ def _parse():
                          "overlap gains on shorter steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="no GPU work: print a summary of the rocprofv3 --kernel-trace --stats "
+                         "output in DIR (needs --bench-line: the JSON line the profiled run "
+                         "printed); the attention kernel is summarised over the timed launches")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "MFMA_DIR"),
+                    help="no GPU work: write the attention kernel's calibrated HBM traffic and "
+                         "MFMA-utilisation summaries under profiles/ from three rocprofv3 --pmc "
+                         "runs (FETCH_SIZE; WRITE_SIZE; MFMA counters), each of a bench.py run "
+                         "with --copy-calibration (needs --bench-line)")
+    ap.add_argument("--bench-line", metavar="FILE", help="file whose last line is a bench JSON line")
+    ap.add_argument("--profile-cmd", action="append", default=[],
+                    help="profiler command to record in a summary (repeatable)")
     return ap.parse_args()
 
 
@@ -123,6 +135,40 @@ def _mfma_util_from_profile(workload: str, attn_ms: float, achieved: float, flop
                 "frac_clock_adjusted": round(achieved / (PEAK_BF16_TFLOPS * clock_ghz / 2.4), 4)}
     except (KeyError, ValueError):
         return None
+
+
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector
+
+
+def _roofline(dtype: str, flops: float, alg_bytes: int, ms: float, traffic):
+    """Roofline of the attention kernel: the bound is whichever of the matrix
+    cores (visible-pair FLOPs at the dense bf16 MFMA peak) and HBM (the
+    algorithmic bytes at 8 TB/s) needs more time; the fp32 path runs on the
+    vector ALUs.  The other bound's figures ride along under `other`."""
+    sec = ms * 1e-3
+    tf = flops / sec / 1e12
+    gbs = alg_bytes / sec / 1e9
+    peak_c = PEAK_FP32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
+    if dtype == "f32":
+        main = {"bound": "alu", "kernel": "attn_ref_kernel", "achieved": round(tf, 3),
+                "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_TFLOPS, 5)}
+        other = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(gbs / PEAK_HBM_GBS, 5)}
+    else:
+        mf = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+              "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        hb = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+              "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        hbm_first = alg_bytes / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_BF16_TFLOPS * 1e12)
+        main, other = (hb, mf) if hbm_first else (mf, hb)
+        main = {"bound": main["bound"], "kernel": ATTN_KERNEL,
+                **{k: v for k, v in main.items() if k != "bound"}}
+    main.update({"traffic": traffic, "alg_bytes": alg_bytes,
+                 "bound_time_us": {"alu" if dtype == "f32" else "mfma":
+                                   round(flops / (peak_c * 1e12) * 1e6, 2),
+                                   "hbm": round(alg_bytes / (PEAK_HBM_GBS * 1e9) * 1e6, 2)},
+                 "other": other})
+    return main
 
 
 def _cpu_baseline(wl, n_heads: int):
@@ -467,8 +513,194 @@ def lazformer_main(args) -> int:
     return 0
 
 
+def _short_kernel(name: str) -> str:
+    import re
+    if "elementwise" in name:
+        return "torch elementwise (input upload)"
+    m = re.search(r"(\w+_kernel(<[^>(]*>)?)", name)
+    if m:
+        return m.group(1).replace("__hip_bfloat16", "bf16")
+    return name.split("(")[0][:44]
+
+
+def _csv_rows(path: str):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath: str, suffix: str) -> str:
+    for root, _, files in os.walk(dirpath):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+
+
+def _bench_line(path: str) -> dict:
+    lines = [ln for ln in open(path).read().splitlines() if ln.strip().startswith("{")]
+    return json.loads(lines[-1])
+
+
+def _header(title: str, args) -> list:
+    out = [f"# {title}", "# commands (on the MI355X box, from the repository root):"]
+    out += [f"#   {c}" for c in args.profile_cmd]
+    argv = " ".join(a if " " not in a and "(" not in a else repr(a) for a in sys.argv[1:])
+    out.append(f"#   python3 bench.py {argv}")
+    return out
+
+
+def summarize_trace(args) -> int:
+    """Kernel-trace summary of a profiled bench run: every kernel over all its
+    launches (from the stats CSV), then the attention kernel over the timed
+    launches only (the bench line says where they are in launch order) and
+    the planner / rotation kernels over the serial steps at the end."""
+    import statistics
+    b = _bench_line(args.bench_line)
+    wl = b["config"]["workload"]
+    out = _header(f"rocprofv3 kernel-trace summary: {wl}", args)
+    stats = _csv_rows(_find(args.summarize_trace, "kernel_stats.csv"))
+    trace = _csv_rows(_find(args.summarize_trace, "kernel_trace.csv"))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    out += ["", "All launches (kernel_stats.csv; microseconds):",
+            f"{'kernel':<44s} {'calls':>6s} {'total_us':>12s} {'avg_us':>10s} {'pct':>7s}"]
+    for r in stats:
+        out.append(f"{_short_kernel(r['Name']):<44s} {int(r['Calls']):>6d} "
+                   f"{float(r['TotalDurationNs']) / 1e3:>12.1f} {float(r['AverageNs']) / 1e3:>10.1f} "
+                   f"{float(r['Percentage']):>7.2f}")
+    by = {}
+    for r in trace:
+        by.setdefault(_short_kernel(r["Kernel_Name"]), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    la = b["launches"]
+    attn_key = [k for k in by if k.startswith("attn_mfma") or k.startswith("attn_ref")]
+    out += ["", "Attention kernel over the timed launches (kernel_trace.csv, in launch order: "
+            f"{la['attention_before_timed']} before, {la['attention_timed']} timed, "
+            f"{la['serial_after']} serial after):"]
+    flops = 4.0 * b["config"]["d_head"] * b["config"]["heads"] * b["config"]["visible_pairs_per_head"]
+    for k in attn_key:
+        d = by[k]
+        t0 = la["attention_before_timed"]
+        timed = d[t0:t0 + la["attention_timed"]]
+        if len(timed) != la["attention_timed"]:
+            out.append(f"  {k}: {len(d)} launches, fewer than the bench line implies")
+            continue
+        mean, med = statistics.mean(timed), statistics.median(timed)
+        peak = b["roofline"]["peak"] if b["roofline"]["unit"] == "TFLOP/s" else PEAK_BF16_TFLOPS
+        out += [f"  {k}: {len(timed)} launches: mean {mean:.1f} us, median {med:.1f} us, "
+                f"min {min(timed):.1f} us, max {max(timed):.1f} us",
+                f"  effective TFLOP/s from the trace mean: {flops / (mean * 1e-6) / 1e12:.1f} "
+                f"({flops / (mean * 1e-6) / 1e12 / peak:.4f} of {peak:.0f}); bench line: "
+                f"{b['ms_per_step'] * 1e3:.1f} us per step, attention events median "
+                f"{b['stage_ms']['attention'] * 1e3:.1f} us, mean "
+                f"{b.get('attention_mean_ms', float('nan')) * 1e3:.1f} us"]
+    ns = la["serial_after"]
+    out += ["", f"Planner and rotation kernels over the {ns} serial steps at the end (median us "
+            "per launch; each stage alone on the GPU):"]
+    tot = 0.0
+    for k, d in by.items():
+        if k.startswith("plan_") or k.startswith("rope"):
+            m = statistics.median(d[-ns:])
+            tot += m if k.startswith("plan_") else 0.0
+            out.append(f"  {k:<42s} {m:>9.1f}")
+    out.append(f"  planner kernels per step {tot:.1f} us; bench line serial stages: "
+               f"{json.dumps(b.get('stage_ms_serial'))} ms")
+    print("\n".join(out))
+    return 0
+
+
+def summarize_pmc(args) -> int:
+    """Calibrated HBM traffic and MFMA utilisation of the attention kernel
+    from three counter runs, written to the two profiles/ files bench.py
+    reads (with the kernel source hash they were taken on)."""
+    import statistics
+    b = _bench_line(args.bench_line)
+    wl = b["config"]["workload"]
+    alg = b["roofline"]["alg_bytes"]
+    fetch_dir, write_dir, mfma_dir = args.summarize_pmc
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+
+    def per(path, counter):
+        out = {}
+        for r in _csv_rows(path):
+            if r["Counter_Name"] == counter:
+                out.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(
+                    float(r["Counter_Value"]))
+        return out
+
+    f = per(_find(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    w = per(_find(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    cf = max(v for (k, g), vs in f.items() if "copyBuffer" in k for v in vs)
+    cw = max(v for (k, g), vs in w.items() if "copyBuffer" in k for v in vs)
+    af = [v for (k, g), vs in f.items() if ATTN_KERNEL in k for v in vs]
+    aw = [v for (k, g), vs in w.items() if ATTN_KERNEL in k for v in vs]
+    sf, sw = 1048576.0 / cf, 1048576.0 / cw  # the 1 GiB copy moves 1048576 KiB each way
+    fb = statistics.mean(af) * sf * 1024
+    wb = statistics.mean(aw) * sw * 1024
+    head = _header(f"HBM traffic of the attention kernel, {wl}", args)
+    txt = head + [
+        "# Counters are KiB per dispatch.  Calibration: the 1 GiB device copy (--copy-calibration,",
+        f"# __amd_rocclr_copyBuffer) reads {cf:.1f} KiB by FETCH_SIZE and writes {cw:.1f} KiB by",
+        f"# WRITE_SIZE for 1048576 KiB moved each way, so FETCH_SIZE is scaled by {sf:.4f} and",
+        f"# WRITE_SIZE by {sw:.4f}.",
+        f"# Attention FETCH_SIZE per launch ({len(af)} launches): "
+        + ", ".join(f"{x:.1f}" for x in af) + " KiB",
+        f"# Attention WRITE_SIZE per launch ({len(aw)} launches): "
+        + ", ".join(f"{x:.1f}" for x in aw) + " KiB",
+        f"# Algorithmic bytes per launch (Q, K, V read once, O written once, timestamps): {alg}",
+        f"attn_source_sha256: {sha}",
+        f"fetch_bytes_per_launch: {fb:.0f}",
+        f"write_bytes_per_launch: {wb:.0f}",
+        f"hbm_bytes_per_launch: {fb + wb:.0f}",
+        f"traffic_over_algorithmic: {(fb + wb) / alg:.3f}"]
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_hbm_traffic_{wl}.txt")
+    open(path, "w").write("\n".join(txt) + "\n")
+    m, dur = {}, []
+    for r in _csv_rows(_find(mfma_dir, "counter_collection.csv")):
+        if ATTN_KERNEL in r["Kernel_Name"]:
+            m.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                dur.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    mean = {k: statistics.mean(v) for k, v in m.items()}
+    act = mean["GRBM_GUI_ACTIVE"] / 8           # summed over the 8 XCDs
+    busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024  # summed over the 1024 SIMDs
+    issued = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    d = statistics.mean(dur)
+    waves = ""
+    if "SQ_WAVE_CYCLES" in mean and "SQ_BUSY_CYCLES" in mean:
+        # resident wave-cycles, counted in units of 4 cycles and summed over
+        # the chip, per SIMD and active cycle
+        waves = f"waves_per_simd: {mean['SQ_WAVE_CYCLES'] * 4 / (act * 1024):.3f}"
+    txt = _header(f"MFMA utilisation of the attention kernel, {wl}", args) + [
+        f"# Means over {len(dur)} attention dispatches.  GRBM_GUI_ACTIVE is summed over the 8 XCDs",
+        "# and SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs; one v_mfma_f32_32x32x16_bf16 counts",
+        "# 32 busy cycles and 64 bf16 MOPs (512 FLOPs each).  waves_per_simd = SQ_WAVE_CYCLES",
+        "# * 4 / (active cycles per XCD * 1024 SIMDs): resident waves per SIMD (3 at most here).",
+        *[f"#   {k:<29s} {v:.4e}" for k, v in sorted(mean.items())],
+        f"#   dispatch duration (ns)        {d:.4e}",
+        "# mfma_busy_frac = MFMA busy cycles per SIMD / active cycles per XCD: the share of the",
+        "# kernel's cycles in which a SIMD's matrix core was busy, independent of the clock.",
+        "# issued_flops counts the MFMA work issued (whole tiles, masked parts of PARTIAL tiles",
+        "# included); bench.py divides the visible-pair FLOPs by it.",
+        f"attn_source_sha256: {sha}",
+        f"active_cycles_per_xcd: {act:.0f}",
+        f"mfma_busy_cycles_per_simd: {busy:.0f}",
+        f"mfma_busy_frac: {busy / act:.4f}",
+        f"issued_flops: {issued:.6e}",
+        f"clock_ghz_under_profiler: {act / d:.3f}"] + ([waves] if waves else [])
+    path2 = os.path.join(ROOT, "profiles", f"attn_fwd_mfma_util_{wl}.txt")
+    open(path2, "w").write("\n".join(txt) + "\n")
+    print(path)
+    print(path2)
+    return 0
+
+
 def main() -> int:
     args = _parse()
+    if args.summarize_trace:
+        return summarize_trace(args)
+    if args.summarize_pmc:
+        return summarize_pmc(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: the masked-attention path is built and "
@@ -631,14 +863,27 @@ def main() -> int:
         step(evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for h in handles:
-        lib.rk_plan_destroy(h)
     ms_step = (t1 - t0) * 1e3 / args.steps
     # per-stage times: medians over the timed steps (attention: from the
     # point its inputs are ready to its end, on the stream it runs on)
     plan_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
     rope_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
     attn_ms = float(np.median([e[3].elapsed_time(e[4]) for e in evs]))
+    attn_mean_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
+    # after the timed region: serial steps (one stream, nothing overlapping)
+    # give each stage's own time, hence the planner's and the rotation's HBM
+    # rates
+    mode["pipelined"] = False
+    n_serial = max(3, min(args.steps, 10))
+    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_serial)]
+    for i in range(n_serial):
+        step(sevs[i])
+    torch.cuda.synchronize()
+    for h in handles:
+        lib.rk_plan_destroy(h)
+    plan_ms_s = float(np.median([e[0].elapsed_time(e[1]) for e in sevs]))
+    rope_ms_s = float(np.median([e[1].elapsed_time(e[2]) for e in sevs]))
+    attn_ms_s = float(np.median([e[3].elapsed_time(e[4]) for e in sevs]))
 
     T = wl.total_tokens
     esz = 2 if wl.dtype == "bf16" else 4
@@ -654,6 +899,8 @@ def main() -> int:
         " qk-norm" if args.qk_norm else "")
     traffic = _traffic_from_profile(wname)
     mfma_util = _mfma_util_from_profile(wname, attn_ms, achieved, flops)
+    roof = _roofline(wl.dtype, flops, attn_alg_bytes, attn_ms, traffic)
+    roof["mfma_util"] = mfma_util
     n_cand = wl.n_candidates
     out = {
         "metric": METRIC,
@@ -678,14 +925,21 @@ def main() -> int:
         "stage_ms": {"plan": round(plan_ms, 4), "rope_k": round(rope_ms, 4),
                      "attention": round(attn_ms, 4)},
         "pipelined": pipelined,
-        "stage_hbm_gbs": {"plan": round(plan_alg_bytes / (plan_ms * 1e-3) / 1e9, 1),
-                          "rope_k": round(rope_alg_bytes / (rope_ms * 1e-3) / 1e9, 1)},
+        "attention_mean_ms": round(attn_mean_ms, 4),
+        # stage times of serial steps run after the timed region (each stage
+        # alone on the GPU); the HBM rates are the algorithmic bytes over them
+        "stage_ms_serial": {"plan": round(plan_ms_s, 4), "rope_k": round(rope_ms_s, 4),
+                            "attention": round(attn_ms_s, 4)},
+        "stage_hbm_gbs": {"plan": round(plan_alg_bytes / (plan_ms_s * 1e-3) / 1e9, 1),
+                          "rope_k": round(rope_alg_bytes / (rope_ms_s * 1e-3) / 1e9, 1)},
+        "stage_alg_bytes": {"plan": plan_alg_bytes, "rope_k": rope_alg_bytes},
         "tiles": {"full": stats["full_tiles"], "partial": stats["partial_tiles"],
                   "empty": stats["empty_tiles"]},
-        "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL, "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "alg_bytes": attn_alg_bytes, "mfma_util": mfma_util},
+        "roofline": roof,
+        # attention launches of this run in launch order: warmup steps, steps
+        # that prime the pipelined mode, the timed steps, then the serial steps
+        "launches": {"attention_before_timed": args.warmup + (2 if pipelined else 0),
+                     "attention_timed": args.steps, "serial_after": n_serial},
         "cpu_baseline": None,
     }
     if args.candidates_only:
