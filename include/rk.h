@@ -409,6 +409,31 @@ rk_status rk_attn_workspace_size(const rk_plan* p, const rk_attn_args* a, size_t
  */
 rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stream);
 
+/* Bytes of the library's scratch array on each GPU (128 MiB), used by
+ * rk_masked_attn_fwd_noalloc. */
+#define RK_STATIC_SCRATCH_BYTES (128u << 20)
+
+/*
+ * rk_masked_attn_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same operation, kernels and results, with the workspace
+ * taken from an array the library holds on each GPU instead of from the
+ * caller.  a->workspace must be NULL and a->workspace_bytes 0.  The array
+ * (RK_STATIC_SCRATCH_BYTES) is placed on a GPU when the library's scratch
+ * module is first used there and stays until the process ends; this call
+ * allocates nothing.  The array of the current device is used.  Every call
+ * on one GPU shares that array: calls that may overlap on one GPU (different
+ * streams, or host threads without ordering) race and must be serialised by
+ * the caller; calls in order on one stream are safe.  Nothing in the array
+ * needs to start at zero (every byte a call reads it wrote earlier in the
+ * same call).
+ * Errors: as rk_masked_attn_fwd; RK_ERR_INVALID_ARG when a workspace is
+ * passed; RK_ERR_WORKSPACE_TOO_SMALL when rk_attn_workspace_size for `a`
+ * exceeds RK_STATIC_SCRATCH_BYTES (e.g. K rotated by the call for more than
+ * 128 MiB of keys: pass K pre-rotated instead).
+ */
+rk_status rk_masked_attn_fwd_noalloc(const rk_plan* p, const rk_attn_args* a, void* stream);
+
 /*
  * Backward arguments.  Q, K, V, O, dO, dQ, dK, dV are [token, head, d]
  * views with d contiguous and the given element strides, all of `dtype`

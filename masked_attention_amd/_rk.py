@@ -261,6 +261,7 @@ FUNCTIONS = [
     ("rk_attn_workspace_size", C.c_int, [C.c_void_p, C.POINTER(rk_attn_args),
                                          C.POINTER(C.c_size_t)]),
     ("rk_masked_attn_fwd", C.c_int, [C.c_void_p, C.POINTER(rk_attn_args), C.c_void_p]),
+    ("rk_masked_attn_fwd_noalloc", C.c_int, [C.c_void_p, C.POINTER(rk_attn_args), C.c_void_p]),
     ("rk_attn_bwd_workspace_size", C.c_int, [C.c_void_p, C.POINTER(rk_attn_bwd_args),
                                              C.POINTER(C.c_size_t)]),
     ("rk_masked_attn_bwd", C.c_int, [C.c_void_p, C.POINTER(rk_attn_bwd_args), C.c_void_p]),

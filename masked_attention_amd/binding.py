@@ -317,6 +317,23 @@ def rk_masked_attn_fwd(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Te
     return out, lse
 
 
+def rk_masked_attn_fwd_noalloc(plan: Plan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                               out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                               scale: float = 0.0, rope: Optional[dict] = None,
+                               reference: bool = False, k_prerotated: bool = False,
+                               qk_norm: Optional[dict] = None,
+                               stream: Optional[torch.cuda.Stream] = None):
+    """rk_masked_attn_fwd with the library's per-GPU scratch array in place of
+    a workspace: nothing is allocated, so `out` (and `lse`, if wanted) come
+    from the caller.  Returns (out, lse)."""
+    rp = rope_params(**rope) if rope is not None else None
+    nq = qk_norm_params(**qk_norm) if qk_norm is not None else None
+    a = _attn_args(plan, q, k, v, out, lse, scale, rp, reference, None, k_prerotated, nq)
+    check(lib().rk_masked_attn_fwd_noalloc(plan.handle, C.byref(a), _stream(stream)),
+          "rk_masked_attn_fwd_noalloc")
+    return out, lse
+
+
 def _bwd_args(q, k, v, o, do, lse, dq, dk, dv, scale, rope, reference, k_prerotated, workspace):
     for t in (q, k, v, o, do, dq, dk, dv):
         if t.dim() != 3 or t.stride(2) != 1:

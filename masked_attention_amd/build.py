@@ -20,7 +20,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "plan.hip", "rope.hip", "attn_ref.hip", "attn_mfma.hip", "attn_combine.hip",
            "attn_bwd_ref.hip", "attn_bwd_mfma.hip", "layout.cpp", "gather_sum.hip",
-           "attn_pointwise_ref.hip", "attn_pointwise_mfma.hip", "norm_bwd.hip"]
+           "attn_pointwise_ref.hip", "attn_pointwise_mfma.hip", "norm_bwd.hip", "scratch.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

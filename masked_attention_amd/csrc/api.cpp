@@ -731,6 +731,24 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
   return e == hipSuccess ? RK_OK : RK_ERR_HIP;
 }
 
+rk_status rk_masked_attn_fwd_noalloc(const rk_plan* p, const rk_attn_args* a, void* stream) {
+  rk_status st = check_attn(p, a);
+  if (st != RK_OK) return st;
+  // the library's scratch array takes the place of the workspace
+  if (a->workspace || a->workspace_bytes) return RK_ERR_INVALID_ARG;
+  const size_t need = attn_ws_bytes(p, a);
+  if (need > (size_t)RK_STATIC_SCRATCH_BYTES) return RK_ERR_WORKSPACE_TOO_SMALL;
+  rk_attn_args b;
+  std::memcpy(&b, a, sizeof(b));
+  if (need > 0) {
+    void* ws = nullptr;
+    if (rk::static_scratch(&ws) != hipSuccess) return RK_ERR_HIP;
+    b.workspace = ws;
+    b.workspace_bytes = (size_t)RK_STATIC_SCRATCH_BYTES;
+  }
+  return rk_masked_attn_fwd(p, &b, stream);
+}
+
 rk_status rk_pointwise_attn_fwd(const rk_plan* p, const rk_pointwise_args* a, void* stream) {
   if (!p || !a || a->struct_size < sizeof(rk_pointwise_args)) return RK_ERR_INVALID_ARG;
   if (!valid_dtype(a->dtype) || a->num_heads != p->H) return RK_ERR_INVALID_ARG;

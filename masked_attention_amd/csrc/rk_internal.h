@@ -256,6 +256,10 @@ hipError_t launch_pointwise_mfma_bf16_d64(const rk_plan* p, const PwLaunch& a, h
 hipError_t launch_attn_reference(const rk_plan* p, const AttnLaunch& a, rk_dtype dt,
                                  hipStream_t s);
 hipError_t launch_attn_mfma_bf16_d64(const rk_plan* p, const AttnLaunch& a, hipStream_t s);
+// Device address of the library's scratch array on the current GPU
+// (RK_STATIC_SCRATCH_BYTES, 256-byte aligned), looked up on the first call
+// per device (scratch.hip).
+hipError_t static_scratch(void** out);
 // Merge the partial results of split items into O / LSE.  to_log2 / to_nat
 // convert the kernels' reference max into log2 / natural units.
 hipError_t launch_attn_combine(const rk_plan* p, const AttnLaunch& a, rk_dtype dt, float to_log2,
