@@ -498,7 +498,7 @@ typedef struct rk_attn_bwd_args {
  * each), plus, with rope or qk_norm, the rotated (normalised) Q and, unless
  * RK_ATTN_K_PREROTATED, K ([total_tokens][num_heads][d_head] of dtype
  * each), plus, with a QK Norm gain, the gain gradients' partial sums
- * (d_head fp32 per 256 rows of total_tokens * num_heads, per gain). */
+ * (d_head fp32 per 512 rows of total_tokens * num_heads, per gain). */
 rk_status rk_attn_bwd_workspace_size(const rk_plan* p, const rk_attn_bwd_args* a, size_t* bytes);
 
 /*

@@ -36,10 +36,11 @@ struct Layout {
   std::vector<int32_t> kt_req;      // key-major counterparts
   std::vector<Group> kgroups;
   std::vector<int32_t> kqueue_start;
+  std::vector<int32_t> group_of;    // see PlanDev::group_of
   std::vector<int32_t> ilv;         // see PlanDev::ilv
   std::vector<int32_t> kilv;        // the same for kgroups
   size_t ilv_cap = 0;               // int32 entries reserved for ilv (and for kilv)
-  size_t off_ilv = 0, off_kilv = 0;
+  size_t off_ilv = 0, off_kilv = 0, off_group_of = 0;
   size_t off_req = 0, off_qt_req = 0, off_groups = 0, off_queue_start = 0, off_totals = 0,
          host_blob = 0, off_row_desc = 0, off_tile_count = 0, off_tile_class = 0, off_qt_nnz = 0,
          off_qt_pairs = 0, off_qt_full = 0,
@@ -208,7 +209,12 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->ilv_cap = 2 * (size_t)L->G;
   for (int32_t r = 0; r < L->R; ++r)
     if (o[r + 1] > o[r]) L->ilv_cap += (size_t)H * (2 + (size_t)nqt_of(r));
-  if (with_tables) build_blocks(&L->groups, L->queue_start, L->G, &L->ilv);
+  if (with_tables) {
+    build_blocks(&L->groups, L->queue_start, L->G, &L->ilv);
+    L->group_of.assign((size_t)L->R * H, -1);
+    for (int64_t ga = 0; ga < L->G; ++ga)
+      L->group_of[(size_t)L->groups[ga].req * H + L->groups[ga].head] = (int32_t)ga;
+  }
   const int64_t kmax = place_groups(L->R, H, o, weight, nkb_of, with_tables, &L->kgroups,
                                     &L->kqueue_start);
   L->kslots = kmax * kNumXcd;
@@ -239,6 +245,7 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->off_kqueue_start = take(sizeof(int32_t) * (kNumXcd + 1));
   L->off_ilv = take(sizeof(int32_t) * L->ilv_cap);
   L->off_kilv = take(sizeof(int32_t) * L->ilv_cap);
+  L->off_group_of = take(sizeof(int32_t) * (size_t)L->R * (size_t)H);
   L->host_blob = off;
   L->off_row_desc = take(sizeof(int2) * (size_t)L->T);
   L->off_tile_count = take(sizeof(int32_t) * (size_t)nt);
@@ -406,6 +413,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   p->off_ksched = L.off_ksched;
   p->off_ilv = L.off_ilv;
   p->off_kilv = L.off_kilv;
+  p->off_group_of = L.off_group_of;
   p->host_blob_bytes = L.host_blob;
   p->total_bytes = L.total;
 
@@ -440,6 +448,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   D.ksched = (int32_t*)(ws + L.off_ksched);
   D.ilv = (int32_t*)(ws + L.off_ilv);
   D.kilv = (int32_t*)(ws + L.off_kilv);
+  D.group_of = (int32_t*)(ws + L.off_group_of);
 
   p->host_blob = (unsigned char*)std::calloc(L.host_blob ? L.host_blob : 1, 1);
   if (!p->host_blob) {
@@ -458,6 +467,9 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
     std::memcpy(p->host_blob + L.off_ilv, L.ilv.data(), sizeof(int32_t) * L.ilv.size());
   if (!L.kilv.empty())
     std::memcpy(p->host_blob + L.off_kilv, L.kilv.data(), sizeof(int32_t) * L.kilv.size());
+  if (!L.group_of.empty())
+    std::memcpy(p->host_blob + L.off_group_of, L.group_of.data(),
+                sizeof(int32_t) * L.group_of.size());
   // totals stay zero (calloc)
 
   hipStream_t s = (hipStream_t)stream;

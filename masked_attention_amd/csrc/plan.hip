@@ -89,135 +89,174 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* smem, int* total
   return res;
 }
 
-// Token of thread t of block g (one block of kTileQ threads per global
-// q-tile): row t of the q-tile, or -1 past the request's end.  The q-tile's
-// request comes from the host-built qt_req table, not from a search.
-__device__ __forceinline__ int tile_token(const PlanDev& P, int* r_out, int* p_out) {
-  const int g = blockIdx.x;
-  const int r = P.qt_req[g];
-  const ReqMeta m = P.req[r];
-  const int p = (g - m.qt_off) * kTileQ + (int)threadIdx.x;
-  *r_out = r;
-  *p_out = p;
-  return p < m.len ? m.tok_off + p : -1;
+// Block-wide sum of one value per thread (blockDim.x a multiple of 64,
+// at most 1024): wave sums, then the waves' sums in order.  Every thread
+// gets the total.
+__device__ __forceinline__ long long block_sum(long long v, long long* red) {
+  v = wave_sum(v);
+  const int nw = (int)(blockDim.x >> 6);
+  __syncthreads();  // red may still be read from a previous call
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  long long t = 0;
+  for (int w = 0; w < nw; ++w) t += red[w];
+  return t;
 }
 
-__global__ __launch_bounds__(kTileQ) void plan_seg_kernel(PlanDev P,
-                                                          const uint8_t* __restrict__ kind,
-                                                          const int64_t* __restrict__ ts,
-                                                          int check_static_time) {
-  int r, p;
-  const int i = tile_token(P, &r, &p);
-  if (i < 0) return;
-  unsigned err = 0, info = 0;
-  int s = kind[i];
-  if (s > RK_SEG_CANDIDATE) { err |= kErrSegment; s = RK_SEG_CANDIDATE; }
-  int prev = -1;
-  if (p > 0) {
-    prev = kind[i - 1];
-    if (prev > RK_SEG_CANDIDATE) prev = RK_SEG_CANDIDATE;
-    if (s < prev) {
-      err |= kErrSegment;
-    } else if (s == prev && ts[i] < ts[i - 1]) {
-      // real-time events must be in time order; PROFILE and HISTORY each
-      // must be when the delay rule searches them.  An out-of-order history
-      // is otherwise allowed and only noted (the pointwise form then reads
-      // its key-time ranges key by key).
-      if (s == RK_SEG_REALTIME || (check_static_time && s <= RK_SEG_HISTORY)) err |= kErrTime;
-      if (s == RK_SEG_HISTORY) info = kInfoHistoryUnsorted;
-    }
+// Request-local starts of segment kinds 1..3 of one request (lo_s[k - 1] =
+// number of tokens of kind < k; kinds are non-decreasing inside a request)
+// by a sampled search over its kinds: each round takes 256 evenly spaced
+// samples of every boundary's window and keeps the one gap that holds the
+// boundary, so a window of n positions takes ceil(log_256 n) rounds (two
+// at 20,000 tokens).  Kinds out of order (reported by the row checks)
+// still give values in [0, L].  lo_s, hi_s: __shared__ int[3].
+__device__ void seg_search(const uint8_t* __restrict__ kr, int L, int* lo_s, int* hi_s) {
+  const int t = threadIdx.x;  // blockDim.x == 256
+  if (t < 3) {
+    lo_s[t] = 0;
+    hi_s[t] = L;
   }
-  for (int k = prev + 1; k <= s; ++k) P.req[r].seg[k] = p;
-  if (err) atomicOr(&P.totals->errors, err);
-  if (info) atomicOr(&P.totals->info, info);
-}
-
-__global__ __launch_bounds__(kTileQ) void plan_rowdesc_kernel(PlanDev P,
-                                                              const uint8_t* __restrict__ kind,
-                                                              const int64_t* __restrict__ ts,
-                                                              int64_t delay, int window,
-                                                              int global_tail, int bidir) {
-  int r, p;
-  const int i = tile_token(P, &r, &p);
-  if (i < 0) return;
-  const ReqMeta m = P.req[r];
-  const int L = m.len;
-  // segment boundaries, made monotone and clamped so that any device data
-  // yields in-range descriptors
-  const int a_rt = min(max(m.seg[RK_SEG_REALTIME], 0), L);
-  const int a_c = min(max(m.seg[RK_SEG_CANDIDATE], a_rt), L);
-  const int64_t* tr = ts + m.tok_off;
-  int s = kind[i];
-  if (s > RK_SEG_CANDIDATE) s = RK_SEG_CANDIDATE;
-  int lo = 0, hi = 0, diag = 0;
-  if (s <= RK_SEG_HISTORY) {
-    if (bidir) {
-      hi = a_rt;
-    } else {
-      hi = min(p + 1, a_rt);
-      // the last global_tail static positions are global queries (no window)
-      lo = (window > 0 && p < a_rt - global_tail) ? max(0, p - window + 1) : 0;
-      if (delay > 0) {
-        // keys dated at or before the cut: [0, cp) of PROFILE and
-        // [a_h, a_h + ch) of HISTORY
-        const int a_h = min(max(m.seg[RK_SEG_HISTORY], 0), a_rt);
-        const int64_t cut = ts[i] - delay;
-        const int cp = count_le(tr, a_h, cut);
-        const int ch = count_le(tr + a_h, a_rt - a_h, cut);
-        const bool prof_run = min(cp, hi) > lo;
-        const bool hist_run = min(a_h + ch, hi) > max(a_h, lo);
-        if (cp == a_h) {
-          hi = min(hi, a_h + ch);  // the whole profile, then a history prefix
-        } else if (hist_run) {
-          if (prof_run) atomicOr(&P.totals->errors, kErrStaticSplit);  // two runs
-          lo = max(lo, a_h);
-          hi = min(hi, a_h + ch);
+  __syncthreads();
+  while (lo_s[0] < hi_s[0] || lo_s[1] < hi_s[1] || lo_s[2] < hi_s[2]) {
+    int lo[3], hi[3], step[3], c[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      lo[k] = lo_s[k];
+      hi[k] = hi_s[k];
+      const int n = hi[k] - lo[k];  // the boundary lies in [lo, hi]
+      step[k] = n > 0 ? (n - 1) / 256 + 1 : 1;
+      const int64_t pos = lo[k] + (int64_t)t * step[k];
+      c[k] = __syncthreads_count(n > 0 && pos < hi[k] && kr[pos] <= k);
+    }
+    if (t < 3) {
+      const int k = t;
+      if (hi[k] > lo[k]) {
+        if (c[k] == 0) {
+          hi_s[k] = lo[k];  // the window's first token already has kind >= k + 1
         } else {
-          hi = min(hi, cp);
+          // sample c - 1 is below kind k + 1, sample c (if any) is not
+          lo_s[k] = lo[k] + (c[k] - 1) * step[k] + 1;
+          hi_s[k] = (int)min((int64_t)hi[k], (int64_t)lo[k] + (int64_t)c[k] * step[k]);
         }
       }
     }
-  } else if (s == RK_SEG_REALTIME) {
-    hi = p + 1;
-  } else {
-    hi = a_rt + count_lt(tr + a_rt, a_c - a_rt, ts[i]);
-    diag = 1;
+    __syncthreads();
   }
-  if (hi <= lo) { lo = 0; hi = 0; }
-  P.row_desc[i] = make_int2(lo, (int)((unsigned)hi | ((unsigned)diag << 31)));
 }
 
-// One block per global q-tile: exact visible count and class of each of its
-// k-tiles, and the q-tile's partial totals (non-empty, FULL, pairs).
-// From the extremes of the rows' intervals [lo, hi) (lo_max, hi_min, lo_min,
-// hi_max over the q-tile's rows) most k-tiles [c0, c1) are decided without
-// visiting the rows: a whole tile (128 rows, 64 keys) with lo_max <= c0 and
-// c1 <= hi_min is FULL (8192 pairs; a row's own key, if in the tile, is
-// inside its interval); a tile with c0 >= hi_max or c1 <= lo_min that holds
-// no row's own position is EMPTY.  The rest are counted row by row; with
-// fewer than 256 k-tiles the rows are split among S = 2^j consecutive lanes
-// per k-tile (S * nkt <= 256, S <= 64), whose counts meet by shuffles.
-__global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
+// One block (256 threads) per global q-tile: the request's segment starts
+// (sampled search; the request's first q-tile records them), the order
+// checks and visible interval (row descriptor) of each of its 128 rows, and
+// the exact visible count and class of each of its k-tiles with the
+// q-tile's partial totals (non-empty, FULL, pairs).  It also marks its
+// share of the launch schedule idle; the CSR kernel writes the items.
+//
+// Row checks: segment kinds non-decreasing and in range; real-time events
+// in time order; PROFILE and HISTORY each in time order when the delay rule
+// searches them (an out-of-order history is otherwise only noted).
+//
+// Tile counts: from the extremes of the rows' intervals [lo, hi) (lo_max,
+// hi_min, lo_min, hi_max over the q-tile's rows) most k-tiles [c0, c1) are
+// decided without visiting the rows: a whole tile (128 rows, 64 keys) with
+// lo_max <= c0 and c1 <= hi_min is FULL (8192 pairs; a row's own key, if in
+// the tile, is inside its interval); a tile with c0 >= hi_max or c1 <=
+// lo_min that holds no row's own position is EMPTY.  The rest are counted
+// row by row; with fewer than 256 k-tiles the rows are split among S = 2^j
+// consecutive lanes per k-tile (S * nkt <= 256, S <= 64), whose counts
+// meet by shuffles.
+__global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
+    PlanDev P, const uint8_t* __restrict__ kind, const int64_t* __restrict__ ts, int64_t delay,
+    int window, int global_tail, int bidir, int check_static_time, int slots) {
   __shared__ int2 d[kTileQ];
   __shared__ unsigned long long pairs_s;
   __shared__ int nnz_s, full_s;
   __shared__ int lim[4];  // lo_max, hi_min, lo_min, hi_max
+  __shared__ int lo_s[3], hi_s[3];
   const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  for (int64_t x = (int64_t)g * blockDim.x + tid; x < slots; x += (int64_t)gridDim.x * blockDim.x)
+    P.sched[x] = -1;
   const int r = P.qt_req[g];
   const ReqMeta m = P.req[r];
   const int qt = g - m.qt_off;
+  const int L = m.len;
   const int row0 = qt * kTileQ;
-  const int nrows = min(kTileQ, m.len - row0);
-  if (threadIdx.x < kTileQ)
-    d[threadIdx.x] = (int)threadIdx.x < nrows ? P.row_desc[m.tok_off + row0 + threadIdx.x] : make_int2(0, 0);
-  if (threadIdx.x == 0) {
+  const int nrows = min(kTileQ, L - row0);
+  const int64_t* tr = ts + m.tok_off;
+  seg_search(kind + m.tok_off, L, lo_s, hi_s);
+  if (qt == 0 && tid < 4) P.req[r].seg[tid] = tid == 0 ? 0 : lo_s[tid - 1];
+  // segment boundaries, made monotone and clamped so that any device data
+  // yields in-range descriptors
+  const int a_rt = min(max(lo_s[RK_SEG_REALTIME - 1], 0), L);
+  const int a_c = min(max(lo_s[RK_SEG_CANDIDATE - 1], a_rt), L);
+  const int a_h = min(max(lo_s[RK_SEG_HISTORY - 1], 0), a_rt);
+  if (tid == 0) {
     pairs_s = 0; nnz_s = 0; full_s = 0;
     lim[0] = INT_MIN; lim[1] = INT_MAX; lim[2] = INT_MAX; lim[3] = INT_MIN;
   }
+  if (tid < kTileQ) {
+    int2 desc = make_int2(0, 0);
+    if (tid < nrows) {
+      const int p = row0 + tid;
+      const int i = m.tok_off + p;
+      unsigned err = 0, info = 0;
+      int s = kind[i];
+      if (s > RK_SEG_CANDIDATE) { err |= kErrSegment; s = RK_SEG_CANDIDATE; }
+      if (p > 0) {
+        int prev = kind[i - 1];
+        if (prev > RK_SEG_CANDIDATE) prev = RK_SEG_CANDIDATE;
+        if (s < prev) {
+          err |= kErrSegment;
+        } else if (s == prev && ts[i] < ts[i - 1]) {
+          if (s == RK_SEG_REALTIME || (check_static_time && s <= RK_SEG_HISTORY)) err |= kErrTime;
+          if (s == RK_SEG_HISTORY) info = kInfoHistoryUnsorted;
+        }
+      }
+      int lo = 0, hi = 0, diag = 0;
+      if (s <= RK_SEG_HISTORY) {
+        if (bidir) {
+          hi = a_rt;
+        } else {
+          hi = min(p + 1, a_rt);
+          // the last global_tail static positions are global queries (no window)
+          lo = (window > 0 && p < a_rt - global_tail) ? max(0, p - window + 1) : 0;
+          if (delay > 0) {
+            // keys dated at or before the cut: [0, cp) of PROFILE and
+            // [a_h, a_h + ch) of HISTORY
+            const int64_t cut = ts[i] - delay;
+            const int cp = count_le(tr, a_h, cut);
+            const int ch = count_le(tr + a_h, a_rt - a_h, cut);
+            const bool prof_run = min(cp, hi) > lo;
+            const bool hist_run = min(a_h + ch, hi) > max(a_h, lo);
+            if (cp == a_h) {
+              hi = min(hi, a_h + ch);  // the whole profile, then a history prefix
+            } else if (hist_run) {
+              if (prof_run) err |= kErrStaticSplit;  // two runs
+              lo = max(lo, a_h);
+              hi = min(hi, a_h + ch);
+            } else {
+              hi = min(hi, cp);
+            }
+          }
+        }
+      } else if (s == RK_SEG_REALTIME) {
+        hi = p + 1;
+      } else {
+        hi = a_rt + count_lt(tr + a_rt, a_c - a_rt, ts[i]);
+        diag = 1;
+      }
+      if (hi <= lo) { lo = 0; hi = 0; }
+      desc = make_int2(lo, (int)((unsigned)hi | ((unsigned)diag << 31)));
+      P.row_desc[i] = desc;
+      if (err) atomicOr(&P.totals->errors, err);
+      if (info) atomicOr(&P.totals->info, info);
+    }
+    d[tid] = desc;
+  }
   __syncthreads();
-  if (threadIdx.x < kTileQ) {  // waves 0 and 1: the rows' extremes
-    const bool ok = (int)threadIdx.x < nrows;
-    const int lo = d[threadIdx.x].x, hi = d[threadIdx.x].y & 0x7fffffff;
+  if (tid < kTileQ) {  // waves 0 and 1: the rows' extremes
+    const bool ok = tid < nrows;
+    const int lo = d[tid].x, hi = d[tid].y & 0x7fffffff;
     int v0 = ok ? lo : INT_MIN, v1 = ok ? hi : INT_MAX, v2 = ok ? lo : INT_MAX,
         v3 = ok ? hi : INT_MIN;
 #pragma unroll
@@ -227,7 +266,7 @@ __global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
       v2 = min(v2, __shfl_xor(v2, o, 64));
       v3 = max(v3, __shfl_xor(v3, o, 64));
     }
-    if ((threadIdx.x & 63) == 0) {
+    if ((tid & 63) == 0) {
       atomicMax(&lim[0], v0);
       atomicMin(&lim[1], v1);
       atomicMin(&lim[2], v2);
@@ -238,7 +277,7 @@ __global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
   const int lo_max = lim[0], hi_min = lim[1], lo_min = lim[2], hi_max = lim[3];
   int S = 1;  // lanes per k-tile (uniform over the block)
   while (S < 64 && 2 * S * m.nkt <= (int)blockDim.x) S *= 2;
-  const int slice = threadIdx.x & (S - 1);
+  const int slice = tid & (S - 1);
   const int per = kTileQ / S;  // rows of a lane: slice * per .. + per
   const int t0 = slice * per, t1 = min(nrows, t0 + per);
   const int step = blockDim.x / S;
@@ -248,9 +287,9 @@ __global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
   // same branch (both depend on kt only), so the shuffles below see all S
   // lanes
   for (int kt0 = 0; kt0 < m.nkt; kt0 += step) {
-    const int kt = kt0 + (int)threadIdx.x / S;
+    const int kt = kt0 + tid / S;
     const int c0 = kt * kTileK;
-    const int c1 = min(m.len, c0 + kTileK);
+    const int c1 = min(L, c0 + kTileK);
     int cnt = 0;
     if (kt < m.nkt) {
       const bool full = nrows == kTileQ && c1 - c0 == kTileK && lo_max <= c0 && c1 <= hi_min;
@@ -286,53 +325,93 @@ __global__ __launch_bounds__(256) void plan_tile_kernel(PlanDev P) {
   pairs = wave_sum(pairs);
   nnz = wave_sum(nnz);
   nfull = wave_sum(nfull);
-  if ((threadIdx.x & 63) == 0) {
+  if ((tid & 63) == 0) {
     atomicAdd(&pairs_s, pairs);
     atomicAdd(&nnz_s, nnz);
     atomicAdd(&full_s, nfull);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     P.qt_nnz[g] = nnz_s;
     P.qt_full[g] = full_s;
     P.qt_pairs[g] = (int64_t)pairs_s;
   }
 }
 
-// Single block: qtile_ptr = exclusive scan of qt_nnz; plan totals from the
-// per-q-tile partial sums.
-__global__ __launch_bounds__(1024) void plan_scan_kernel(PlanDev P, int NQ, int64_t NT) {
+// Blocks 0 .. NQ - 1, one per global q-tile: the start of its CSR row (the
+// non-empty k-tiles of all earlier q-tiles), its rank among its request's
+// q-tiles (descending non-empty count, ties by index), the ascending list
+// of its non-empty k-tiles, and, unless the schedule is built by
+// plan_sched_kernel, its H items' slots of the blocked XCD schedule
+// (slot_of below, inverted: the item of group ga at rank k sits at queue
+// position base + C(k) + (ga - first group of its block)).  Block NQ: the
+// plan's totals.
+__global__ __launch_bounds__(256) void plan_csr_sched_kernel(PlanDev P, int NQ, int64_t NT, int H,
+                                                             int G, int write_sched) {
   __shared__ int smem[32];
-  __shared__ unsigned long long tot[2];
-  if (threadIdx.x < 2) tot[threadIdx.x] = 0;
-  __syncthreads();
-  int carry = 0;
-  unsigned long long pairs = 0, nfull = 0;
-  for (int base = 0; base < NQ; base += blockDim.x) {
-    const int i = base + threadIdx.x;
-    const int v = i < NQ ? P.qt_nnz[i] : 0;
-    if (i < NQ) {
-      pairs += (unsigned long long)P.qt_pairs[i];
-      nfull += (unsigned long long)P.qt_full[i];
+  __shared__ long long red[16];
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (g == NQ) {
+    long long nnz = 0, pairs = 0, nfull = 0;
+    for (int i = tid; i < NQ; i += blockDim.x) {
+      nnz += P.qt_nnz[i];
+      pairs += P.qt_pairs[i];
+      nfull += P.qt_full[i];
     }
+    nnz = block_sum(nnz, red);
+    pairs = block_sum(pairs, red);
+    nfull = block_sum(nfull, red);
+    if (tid == 0) {
+      P.qtile_ptr[NQ] = (int)nnz;
+      P.totals->visible_pairs = (unsigned long long)pairs;
+      P.totals->full_tiles = (unsigned long long)nfull;
+      P.totals->partial_tiles = (unsigned long long)(nnz - nfull);
+      P.totals->empty_tiles = (unsigned long long)(NT - nnz);
+    }
+    return;
+  }
+  const int r = P.qt_req[g];
+  const ReqMeta m = P.req[r];
+  const int qt = g - m.qt_off;
+  long long acc = 0;
+  for (int i = tid; i < g; i += blockDim.x) acc += P.qt_nnz[i];
+  const int base = (int)block_sum(acc, red);
+  const int na = P.qt_nnz[g];
+  long long rk = 0;
+  for (int j = tid; j < m.nqt; j += blockDim.x) {
+    const int nb = P.qt_nnz[m.qt_off + j];
+    rk += (nb > na) || (nb == na && j < qt);
+  }
+  const int rank = (int)block_sum(rk, red);
+  if (tid == 0) {
+    P.qtile_ptr[g] = base;
+    P.qorder[m.qt_off + rank] = g;
+  }
+  const int64_t row = m.tile_off + (int64_t)qt * m.nkt;
+  int run = 0;
+  for (int k0 = 0; k0 < m.nkt; k0 += blockDim.x) {
+    const int kt = k0 + tid;
+    const int flag = kt < m.nkt && P.tile_count[row + kt] > 0;
     int total;
-    const int ex = block_exclusive_scan(v, smem, &total);
-    if (i < NQ) P.qtile_ptr[i] = carry + ex;
-    carry += total;
+    const int ex = block_exclusive_scan(flag, smem, &total);
+    if (flag) {
+      P.ktile_idx[base + run + ex] = kt;
+      P.ktile_word[base + run + ex] =
+          (int)((unsigned)kt | ((unsigned)(P.tile_class[row + kt] == RK_TILE_PARTIAL) << 31));
+    }
+    run += total;
   }
-  pairs = wave_sum(pairs);
-  nfull = wave_sum(nfull);
-  if ((threadIdx.x & 63) == 0) {
-    atomicAdd(&tot[0], pairs);
-    atomicAdd(&tot[1], nfull);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    P.qtile_ptr[NQ] = carry;
-    P.totals->visible_pairs = tot[0];
-    P.totals->full_tiles = tot[1];
-    P.totals->partial_tiles = (unsigned long long)carry - tot[1];
-    P.totals->empty_tiles = (unsigned long long)NT - (unsigned long long)carry;
+  if (write_sched) {
+    for (int h = tid; h < H; h += blockDim.x) {
+      const int ga = P.group_of[(int64_t)r * H + h];
+      const int f = P.ilv[ga];                  // first group of ga's block
+      const int* C = P.ilv + P.ilv[G + ga] + 1;  // the block's C(k)
+      const int idx = P.groups[f].base + C[rank] + (ga - f);
+      int q = 0;
+      while (q < kNumXcd - 1 && ga >= P.queue_start[q + 1]) ++q;
+      P.sched[(int64_t)idx * kNumXcd + q] = g * H + h;
+    }
   }
 }
 
@@ -366,37 +445,6 @@ __device__ __forceinline__ void rank_order(int n, int off, const int* __restrict
       }
     }
     if (a < n) order[off + rank] = off + a;
-  }
-}
-
-// Blocks 0 .. NQ - 1, one per q-tile: ascending list of its non-empty
-// k-tiles.  Blocks NQ .. NQ + R - 1, one per request: its q-tiles ordered
-// by non-empty k-tile count, descending, ties by q-tile index.
-__global__ __launch_bounds__(256) void plan_csr_sort_kernel(PlanDev P, int NQ) {
-  __shared__ int smem[32];
-  __shared__ __attribute__((aligned(16))) int chunk[1024];
-  if ((int)blockIdx.x >= NQ) {
-    const ReqMeta m = P.req[blockIdx.x - NQ];
-    rank_order(m.nqt, m.qt_off, P.qt_nnz + m.qt_off, P.qorder, chunk);
-    return;
-  }
-  const int g = blockIdx.x;
-  const ReqMeta m = P.req[P.qt_req[g]];
-  const int qt = g - m.qt_off;
-  const int64_t row = m.tile_off + (int64_t)qt * m.nkt;
-  const int base = P.qtile_ptr[g];
-  int run = 0;
-  for (int k0 = 0; k0 < m.nkt; k0 += blockDim.x) {
-    const int kt = k0 + threadIdx.x;
-    const int flag = kt < m.nkt && P.tile_count[row + kt] > 0;
-    int total;
-    const int ex = block_exclusive_scan(flag, smem, &total);
-    if (flag) {
-      P.ktile_idx[base + run + ex] = kt;
-      P.ktile_word[base + run + ex] =
-          (int)((unsigned)kt | ((unsigned)(P.tile_class[row + kt] == RK_TILE_PARTIAL) << 31));
-    }
-    run += total;
   }
 }
 
@@ -656,27 +704,21 @@ __global__ void plan_ksched_kernel(PlanDev P, int64_t slots, int H, int G) {
 
 hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
   const PlanDev& P = p->dev;
-  if (p->T > 0) {
+  const bool cand_only = (p->flags & RK_QUERY_CANDIDATES_ONLY) != 0;
+  if (p->NQ > 0) {
     // one block per global q-tile (NQ > 0 whenever T > 0)
     const int check_static = (!(p->flags & RK_STATIC_BIDIRECTIONAL)) && p->delay > 0;
-    hipLaunchKernelGGL(plan_seg_kernel, dim3((unsigned)p->NQ), dim3(kTileQ), 0, s, P,
-                       p->seg_kind_dev, p->timestamps_dev, check_static);
-    hipLaunchKernelGGL(plan_rowdesc_kernel, dim3((unsigned)p->NQ), dim3(kTileQ), 0, s, P,
-                       p->seg_kind_dev, p->timestamps_dev, p->delay, p->window,
-                       p->global_tail, (int)((p->flags & RK_STATIC_BIDIRECTIONAL) != 0));
+    hipLaunchKernelGGL(plan_rows_tiles_kernel, dim3((unsigned)p->NQ), dim3(256), 0, s, P,
+                       p->seg_kind_dev, p->timestamps_dev, p->delay, p->window, p->global_tail,
+                       (int)((p->flags & RK_STATIC_BIDIRECTIONAL) != 0), check_static,
+                       (int)p->slots);
   }
-  if (p->NQ > 0) {
-    hipLaunchKernelGGL(plan_tile_kernel, dim3((unsigned)p->NQ), dim3(256), 0, s, P);
-  }
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s, P, (int)p->NQ, p->NT);
-  if (p->NQ > 0) {
-    hipLaunchKernelGGL(plan_csr_sort_kernel, dim3((unsigned)(p->NQ + p->R)), dim3(256), 0, s, P,
-                       (int)p->NQ);
-  }
-  if (p->slots > 0) {
+  // blocks 0 .. NQ - 1 per q-tile, block NQ the totals (zero tiles: totals only)
+  hipLaunchKernelGGL(plan_csr_sched_kernel, dim3((unsigned)(p->NQ + 1)), dim3(256), 0, s, P,
+                     (int)p->NQ, p->NT, p->H, (int)p->G, (int)!cand_only);
+  if (cand_only && p->slots > 0) {
     hipLaunchKernelGGL(plan_sched_kernel, dim3((unsigned)((p->slots + 255) / 256)), dim3(256), 0, s,
-                       P, p->slots, p->H, (int)((p->flags & RK_QUERY_CANDIDATES_ONLY) != 0),
-                       (int)p->G);
+                       P, p->slots, p->H, 1, (int)p->G);
     if (p->grid > p->slots)
       hipLaunchKernelGGL(plan_work_kernel, dim3((unsigned)((p->grid + 1023) / 1024)), dim3(1024), 0,
                          s, P, (int)p->slots, (int)p->grid, p->H);

@@ -95,6 +95,7 @@ struct PlanDev {
   int32_t* qt_req;         // [NQ] request of each global q-tile
   Group* groups;           // [G] sorted by (queue, base)
   int32_t* queue_start;    // [kNumXcd + 1] first group of each queue
+  int32_t* group_of;       // [R * H] index in groups of (request, head), -1 for empty requests
   int2* row_desc;          // [T]
   int32_t* tile_count;     // [NT]
   uint8_t* tile_class;     // [NT]
@@ -148,7 +149,7 @@ struct rk_plan {
       off_tile_class, off_qt_nnz, off_qt_pairs, off_qt_full, off_qtile_ptr, off_ktile_idx, off_ktile_word, off_qorder,
       off_sched, off_work, off_splits, off_act, off_totals, host_blob_bytes, total_bytes,
       off_kt_req, off_kgroups, off_kqueue_start, off_kt_nnz, off_kt_ptr, off_qtile_word,
-      off_korder, off_ksched, off_ilv, off_kilv;
+      off_korder, off_ksched, off_ilv, off_kilv, off_group_of;
   rk::PlanDev dev;
   // host copy of the first host_blob_bytes of the workspace (kept alive
   // for the asynchronous upload)
