@@ -65,6 +65,9 @@
  *    returns an error has enqueued nothing.
  *  - Checks that need device data (segment order, timestamp order) are
  *    recorded by rk_mask_plan on the device and reported by rk_plan_stats.
+ *    Every kernel that runs over a plan whose checks failed stores NaN in
+ *    each value it writes (O, LSE, dQ, dK, dV, the pointwise output), so a
+ *    misused plan is visible even to a caller that never reads the stats.
  *  - No global mutable state: concurrent calls on distinct plans and
  *    buffers are safe.
  *  - Every struct starts with `struct_size` (= sizeof of the struct the

@@ -695,6 +695,7 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
   L.d = a->d_head;
   L.T = p->T;
   L.ts = p->timestamps_dev;
+  L.plan_err = &p->dev.totals->errors;
   L.anchors = p->anchors_dev;
   hipStream_t s = (hipStream_t)stream;
   if (a->rope || a->qk_norm) {
@@ -806,6 +807,7 @@ rk_status rk_pointwise_attn_fwd(const rk_plan* p, const rk_pointwise_args* a, vo
   L.np = a->pos_bias ? a->num_pos_buckets : 1;
   L.nt = a->time_bias ? a->num_time_buckets : 1;
   L.ts = p->timestamps_dev;
+  L.plan_err = &p->dev.totals->errors;
   hipError_t e = use_mfma ? rk::launch_pointwise_mfma_bf16_d64(p, L, (hipStream_t)stream)
                           : rk::launch_pointwise_reference(p, L, a->dtype, (hipStream_t)stream);
   return e == hipSuccess ? RK_OK : RK_ERR_HIP;
@@ -1001,6 +1003,7 @@ rk_status rk_masked_attn_bwd(const rk_plan* p, const rk_attn_bwd_args* a, void* 
   L.dsum = (float*)(ws + w.dsum);
   L.lse2 = (float*)(ws + w.lse2);
   L.ts = p->timestamps_dev;
+  L.plan_err = &p->dev.totals->errors;
   L.anchors = p->anchors_dev;
   const int64_t hd = (int64_t)a->num_heads * a->d_head;
   const float eps = norm ? a->qk_norm->eps : 0.f;

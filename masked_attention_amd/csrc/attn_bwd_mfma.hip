@@ -251,6 +251,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdPlanView P,
   __shared__ __attribute__((aligned(1024))) unsigned short V0[TILE_ELEMS], V1[TILE_ELEMS];
   const int item = ldc(P.sched, blockIdx.x);
   if (item < 0) return;
+  const float pz = plan_poison(A.plan_err);
   const int qg = item / A.H;
   const int head = item - qg * A.H;
   const int req = ldc(P.qt_req, qg);
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdPlanView P,
 
   if (!rvalid) return;
   const int64_t dt = kUnrot ? ldc(A.ts, tokq) - ldc(A.anchors, req) : 0;
-  unrotate_acc(dq0, dq1, dt, A.tab, hh, A.scale, kUnrot);
+  unrotate_acc(dq0, dq1, dt, A.tab, hh, A.scale * pz, kUnrot);
   store_row((unsigned short*)A.dq + (int64_t)tokq * A.dq_st + (int64_t)head * A.dq_sh, dq0, dq1,
             hh);
 }
@@ -472,6 +473,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(BwdPlanView 
   __shared__ __attribute__((aligned(1024))) QStage S0, S1;
   const int item = ldc(P.ksched, blockIdx.x);
   if (item < 0) return;
+  const float pz = plan_poison(A.plan_err);
   const int kg = item / A.H;
   const int head = item - kg * A.H;
   const int req = ldc(P.kt_req, kg);
@@ -594,7 +596,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_kernel(BwdPlanView 
 
   if (!kvalid) return;
   const int64_t dt = kUnrot ? ldc(A.ts, tokk) - ldc(A.anchors, req) : 0;
-  unrotate_acc(dk0, dk1, dt, A.tab, hh, A.scale, kUnrot);
+  unrotate_acc(dk0, dk1, dt, A.tab, hh, A.scale * pz, kUnrot);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    dv0[r] *= pz;
+    dv1[r] *= pz;
+  }
   store_row((unsigned short*)A.dk + (int64_t)tokk * A.dk_st + (int64_t)head * A.dk_sh, dk0, dk1,
             hh);
   store_row((unsigned short*)A.dv + (int64_t)tokk * A.dv_st + (int64_t)head * A.dv_sh, dv0, dv1,

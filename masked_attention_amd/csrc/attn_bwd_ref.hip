@@ -151,8 +151,9 @@ __global__ __launch_bounds__(128) void attn_bwd_ref_dq_kernel(BwdPlanView P, Bwd
     }
   }
   if (!valid) return;
+  const float sc = A.scale * plan_poison(A.plan_err);
 #pragma unroll
-  for (int c = 0; c < D; ++c) acc[c] *= A.scale;
+  for (int c = 0; c < D; ++c) acc[c] *= sc;
   if (A.unrot_q) unrotate<D>(acc, A.ts[tok] - A.anchors[req], w);
   T* dQ = (T*)A.dq;
 #pragma unroll
@@ -248,8 +249,12 @@ __global__ __launch_bounds__(128) void attn_bwd_ref_dkdv_kernel(BwdPlanView P, B
     }
   }
   if (!valid) return;
+  const float pz = plan_poison(A.plan_err);
 #pragma unroll
-  for (int c = 0; c < D; ++c) dk[c] *= A.scale;
+  for (int c = 0; c < D; ++c) {
+    dk[c] *= A.scale * pz;
+    dv[c] *= pz;
+  }
   if (A.unrot_k) unrotate<D>(dk, A.ts[tokk] - A.anchors[req], w);
   T* dK = (T*)A.dk;
   T* dV = (T*)A.dv;

@@ -90,12 +90,13 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const ReqMeta* req, c
     }
     M = Mn;
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float pz = plan_poison(A.plan_err);
+  const float inv = (l > 0.f ? 1.f / l : 0.f) * pz;
   T* O = (T*)A.o + (int64_t)tok * A.o_st + (int64_t)head * A.o_sh + c0;
 #pragma unroll
   for (int c = 0; c < kQ; ++c) st(O + c, acc[c] * inv);
   if (A.lse && c0 == 0)
-    A.lse[(int64_t)head * A.T + tok] = l > 0.f ? M * to_nat + logf(l) : -INFINITY;
+    A.lse[(int64_t)head * A.T + tok] = (l > 0.f ? M * to_nat + logf(l) : -INFINITY) * pz;
 }
 
 template <typename T, int D>

@@ -466,6 +466,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
     item = ldc(P.sched, blockIdx.x);
   }
   if (item < 0) return;
+  const float pz = plan_poison(A.plan_err);
   const int qg = item / A.H;
   const int head = item - qg * A.H;
   const int req = ldc(P.qt_req, qg);
@@ -589,7 +590,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
     }
     return;
   }
-  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  const float inv = (ltot > 0.f ? 1.f / ltot : 0.f) * pz;
   unsigned short* Op = (unsigned short*)A.o + (int64_t)tokq * A.o_st + (int64_t)head * A.o_sh;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -601,7 +602,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   }
   if (A.lse && hh == 0)
     A.lse[(int64_t)head * A.T + tokq] =
-        ltot > 0.f ? mref * (kPreScaled ? 0.6931471805599453f : A.scale) + logf(ltot) : -INFINITY;
+        (ltot > 0.f ? mref * (kPreScaled ? 0.6931471805599453f : A.scale) + logf(ltot)
+                    : -INFINITY) * pz;
 }
 
 }  // namespace

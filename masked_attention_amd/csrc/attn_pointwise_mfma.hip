@@ -246,6 +246,7 @@ __global__ __launch_bounds__(kThreads, 3) void pw_mfma_bf16_d64_kernel(PwView P,
 
   const int item = ldc(P.sched, blockIdx.x);
   if (item < 0) return;
+  const float pz = plan_poison(A.plan_err);
   const int qg = item / A.H;
   const int head = item - qg * A.H;
   const int req = ldc(P.qt_req, qg);
@@ -362,6 +363,11 @@ __global__ __launch_bounds__(kThreads, 3) void pw_mfma_bf16_d64_kernel(PwView P,
   }
 
   if (!rvalid) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    o0[r] *= pz;
+    o1[r] *= pz;
+  }
   unsigned short* Op = (unsigned short*)A.o + (int64_t)tokq * A.o_st + (int64_t)head * A.o_sh;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {

@@ -108,9 +108,10 @@ __global__ __launch_bounds__(128) void pw_ref_kernel(const ReqMeta* __restrict__
     }
   }
   if (!valid) return;
+  const float pz = plan_poison(A.plan_err);
   T* O = (T*)A.o;
 #pragma unroll
-  for (int c = 0; c < D; ++c) st(O + (int64_t)tok * A.o_st + (int64_t)head * A.o_sh + c, acc[c]);
+  for (int c = 0; c < D; ++c) st(O + (int64_t)tok * A.o_st + (int64_t)head * A.o_sh + c, acc[c] * pz);
 }
 
 template <typename T, int D>

@@ -164,10 +164,11 @@ __global__ __launch_bounds__(128) void attn_ref_kernel(PlanView P, AttnLaunch A)
     return;
   }
   T* O = (T*)A.o;
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const float pz = plan_poison(A.plan_err);
+  const float inv = (lsum > 0.f ? 1.f / lsum : 0.f) * pz;
 #pragma unroll
   for (int c = 0; c < D; ++c) st(O + (int64_t)tok * A.o_st + (int64_t)head * A.o_sh + c, acc[c] * inv);
-  if (A.lse) A.lse[(int64_t)head * A.T + tok] = lsum > 0.f ? mrow + logf(lsum) : -INFINITY;
+  if (A.lse) A.lse[(int64_t)head * A.T + tok] = (lsum > 0.f ? mrow + logf(lsum) : -INFINITY) * pz;
 }
 
 template <typename T, int D>

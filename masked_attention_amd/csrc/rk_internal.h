@@ -158,6 +158,14 @@ struct rk_plan {
 
 namespace rk {
 
+// 1 when the plan's device checks passed, NaN otherwise.  Every kernel that
+// runs over a plan multiplies what it stores by this, so a plan built from a
+// batch that broke the segment or time order gives NaN rows, not silently
+// wrong ones.
+__device__ __forceinline__ float plan_poison(const unsigned* plan_err) {
+  return *plan_err ? __builtin_nanf("") : 1.f;
+}
+
 // RoPE frequency table in revolutions per timestamp unit:
 // w_rev[i] = phi_min / dt_max * base^(2i/d) / (2 pi).
 struct RopeTab {
@@ -192,6 +200,7 @@ struct AttnLaunch {
   float eps;
   const float* gamma_q;     // [d] or null
   float* part;              // partial results of split items, or null
+  const unsigned* plan_err; // the plan's device error word (plan_poison)
   const int64_t* ts;
   const int64_t* anchors;
   RopeTab tab;
@@ -221,6 +230,7 @@ struct BwdLaunch {
   bool unrot_q, unrot_k;
   float* dsum;
   float* lse2;
+  const unsigned* plan_err; // the plan's device error word (plan_poison)
   const int64_t* ts;
   const int64_t* anchors;
   RopeTab tab;
@@ -247,6 +257,7 @@ struct PwLaunch {
   const float* pos_bias;  // [np] or null
   const float* time_bias; // [nt] or null
   int np, nt;
+  const unsigned* plan_err; // the plan's device error word (plan_poison)
   const int64_t* ts;
 };
 

@@ -344,6 +344,47 @@ def test_plan_static_time_checks(rk):
     plan.close()
 
 
+def test_failed_plan_outputs_nan(rk):
+    """A plan whose device checks failed (real-time events out of time order)
+    makes every kernel over it store NaN: forward O and LSE (MFMA and plain
+    kernels, and the merge of split key ranges), the backward's dQ, dK, dV
+    and the pointwise form."""
+    from rk_workloads import draw_grad
+    rng = np.random.default_rng(29)
+    # 3000 history keys: the candidate tile's key range is long enough to split
+    reqs = [[(HISTORY, np.sort(rng.integers(NOW - 10**6, NOW - 3600, 3000))),
+             (REALTIME, np.array([NOW - 100, NOW - 500, NOW - 200])),
+             (CANDIDATE, np.full(5, NOW))],
+            [(HISTORY, np.sort(rng.integers(NOW - 10**6, NOW, 200)))]]
+    for dtype, reference in (("bf16", False), ("f32", True)):
+        _say(f"[gpu] failed plan {dtype} reference={reference}")
+        wl = make_custom(reqs, heads=2, d_head=64, dtype=dtype, seed=29)
+        batch = rk.Batch.from_workload(wl)
+        plan = rk.Plan(batch, num_heads=2, backward=True)
+        assert plan.stats(raise_on_error=False)["status"] == 3
+        q, k, v = _tensors(wl)
+        do = torch.from_numpy(draw_grad(wl)).to("cuda").to(q.dtype)
+        o, lse = rk.rk_masked_attn_fwd(plan, q, k, v, rope=_rope(wl), reference=reference,
+                                       want_lse=True)
+        dq, dk, dv = rk.rk_masked_attn_bwd(plan, q, k, v, o, lse, do, rope=_rope(wl),
+                                           reference=reference)
+        po = rk.rk_pointwise_attn_fwd(plan, q, k, v, scale=0.125, reference=reference)
+        torch.cuda.synchronize()
+        for name, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv),
+                        ("pointwise", po)):
+            assert bool(torch.isnan(t.float()).all()), name
+        plan.close()
+        # a serving call whose few candidate tiles are split and merged
+        cplan = rk.Plan(batch, num_heads=2, candidates_only=True)
+        assert cplan.stats(raise_on_error=False)["split_items"] > 0
+        o2 = torch.zeros_like(q)
+        rk.rk_masked_attn_fwd(cplan, q, k, v, out=o2, rope=_rope(wl), reference=reference)
+        torch.cuda.synchronize()
+        cand = torch.from_numpy(np.nonzero(wl.seg_kind == CANDIDATE)[0]).cuda()
+        assert bool(torch.isnan(o2[cand].float()).all())
+        cplan.close()
+
+
 # ---------------------------------------------------------------------------
 # time RoPE
 # ---------------------------------------------------------------------------
