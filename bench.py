@@ -88,6 +88,10 @@ def _parse():
                          "MFMA-utilisation summaries under profiles/ from three rocprofv3 --pmc "
                          "runs (FETCH_SIZE; WRITE_SIZE; MFMA counters), each of a bench.py run "
                          "with --copy-calibration (needs --bench-line)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="measure the chip's sustained bf16 MFMA rate instead (a whole-chip loop "
+                         "of v_mfma_f32_32x32x16_bf16 at 8 waves per SIMD, on constant and on "
+                         "random operands; built with hipcc at run time)")
     ap.add_argument("--bench-line", metavar="FILE", help="file whose last line is a bench JSON line")
     ap.add_argument("--profile-cmd", action="append", default=[],
                     help="profiler command to record in a summary (repeatable)")
@@ -695,8 +699,108 @@ def summarize_pmc(args) -> int:
     return 0
 
 
+# Whole-chip MFMA loop: 2048 workgroups of 4 waves (8 waves per SIMD), each
+# wave issuing 8 independent-accumulator-pair v_mfma_f32_32x32x16_bf16 per
+# iteration on operands that are either constant or random bf16 values that
+# rotate between instructions.  The rate comes from HIP events around the
+# second launch of each kind (the first warms the clock up).
+_CEILING_SRC = r"""
+#include <hip/hip_runtime.h>
+#include <cstdio>
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+template <int RANDOM>
+__global__ __launch_bounds__(256) void mfma_loop(float* out, long long* cyc, int iters,
+                                                 unsigned seed) {
+  const int t = threadIdx.x;
+  bf16x8 fa[4], fb[4];
+  unsigned x = seed ^ (t * 2654435761u) ^ (blockIdx.x * 40503u);
+  for (int j = 0; j < 4; ++j)
+    for (int i = 0; i < 8; ++i) {
+      x = x * 1664525u + 1013904223u;
+      fa[j][i] = (__bf16)(RANDOM ? (float)((x >> 9) & 0xffff) / 65536.f - 0.5f : 0.25f);
+      x = x * 1664525u + 1013904223u;
+      fb[j][i] = (__bf16)(RANDOM ? (float)((x >> 9) & 0xffff) / 65536.f - 0.5f : 0.5f);
+    }
+  f32x16 a0 = {}, a1 = {};
+  const long long c0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j], fb[j], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[(j + 1) & 3], fa[(j + 2) & 3], a1, 0, 0, 0);
+    }
+  }
+  const long long c1 = __builtin_amdgcn_s_memtime();
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += a0[i] + a1[i];
+  out[blockIdx.x * blockDim.x + t] = s;
+  if (t == 0) cyc[blockIdx.x] = c1 - c0;
+}
+template <int R>
+static void run(const char* name, float* out, long long* cyc, int iters) {
+  hipLaunchKernelGGL(mfma_loop<R>, dim3(2048), dim3(256), 0, 0, out, cyc, iters, 7u);
+  (void)hipDeviceSynchronize();
+  hipEvent_t e0, e1;
+  (void)hipEventCreate(&e0);
+  (void)hipEventCreate(&e1);
+  (void)hipEventRecord(e0);
+  hipLaunchKernelGGL(mfma_loop<R>, dim3(2048), dim3(256), 0, 0, out, cyc, iters, 9u);
+  (void)hipEventRecord(e1);
+  (void)hipEventSynchronize(e1);
+  float ms = 0.f;
+  (void)hipEventElapsedTime(&ms, e0, e1);
+  static long long h[2048];
+  (void)hipMemcpy(h, cyc, sizeof(h), hipMemcpyDeviceToHost);
+  long long mx = 0;
+  for (long long v : h) mx = v > mx ? v : mx;
+  const double flops = 2048.0 * 4 * iters * 8 * 32768.0;
+  printf("%s %.4f %.6e %.6e\n", name, ms, flops, (double)mx);
+}
+int main() {
+  float* out;
+  long long* cyc;
+  if (hipMalloc(&out, 2048 * 256 * sizeof(float)) != hipSuccess) return 1;
+  if (hipMalloc(&cyc, 2048 * sizeof(long long)) != hipSuccess) return 1;
+  for (int rep = 0; rep < 2; ++rep) {
+    run<0>("constant", out, cyc, 20000);
+    run<1>("random", out, cyc, 20000);
+  }
+  return 0;
+}
+"""
+
+
+def mfma_ceiling_main(args) -> int:
+    """One JSON line: the sustained bf16 MFMA rate of a whole-chip
+    v_mfma_f32_32x32x16_bf16 loop on constant and on random operands."""
+    import shutil
+    import subprocess
+    import tempfile
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "ceiling.hip"), os.path.join(d, "ceiling")
+        open(src, "w").write(_CEILING_SRC)
+        subprocess.run([hipcc, "-O3", "--offload-arch=gfx950", "-Xclang", "-target-feature",
+                        "-Xclang", "-packed-fp32-ops", "-o", exe, src], check=True,
+                       capture_output=True)
+        res = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    runs = []
+    for line in res.splitlines():
+        name, ms, flops, cyc = line.split()
+        ms, flops, cyc = float(ms), float(flops), float(cyc)
+        runs.append({"operands": name, "ms": round(ms, 3),
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "frac_of_2500": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+    print(json.dumps({"metric": "sustained bf16 MFMA rate, whole-chip v_mfma_f32_32x32x16_bf16 "
+                                "loop (2048 workgroups x 4 waves)", "runs": runs}), flush=True)
+    return 0
+
+
 def main() -> int:
     args = _parse()
+    if args.mfma_ceiling:
+        return mfma_ceiling_main(args)
     if args.summarize_trace:
         return summarize_trace(args)
     if args.summarize_pmc:
