@@ -38,7 +38,7 @@ METRIC = "masked-attn fwd effective TFLOP/s (visible pairs) + % bf16 MFMA peak; 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ATTN_SRC = os.path.join(ROOT, "masked_attention_amd", "csrc", "attn_mfma.hip")
-ATTN_KERNEL = "attn_mfma_bf16_d64_kernel"
+ATTN_KERNEL = "attn_mfma_bf16_kernel"
 
 
 def _parse():

@@ -616,7 +616,9 @@ rk_status check_attn(const rk_plan* p, const rk_attn_args* a) {
 }
 
 bool mfma_eligible(const rk_attn_args* a) {
-  if (a->dtype != RK_BF16 || a->d_head != 64 || (a->flags & RK_ATTN_REFERENCE_KERNEL)) return false;
+  if (a->dtype != RK_BF16 || (a->d_head != 64 && a->d_head != 128) ||
+      (a->flags & RK_ATTN_REFERENCE_KERNEL))
+    return false;
   return true;
 }
 
@@ -727,7 +729,7 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
     L.k_st = hd;
     L.k_sh = a->d_head;
   }
-  hipError_t e = use_mfma ? rk::launch_attn_mfma_bf16_d64(p, L, s)
+  hipError_t e = use_mfma ? rk::launch_attn_mfma_bf16(p, L, s)
                           : rk::launch_attn_reference(p, L, a->dtype, s);
   if (e == hipSuccess && L.part) {
     // units of the kernels' reference max m: the MFMA kernel keeps it in log2

@@ -45,15 +45,19 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int D = 64;
-constexpr int TILE_ELEMS = kTileK * D;  // 64 rows x 64 bf16 = 8 KB per K or V tile
+// Tile geometry for d_head D (64 or 128): a K or V tile is 64 rows of 2 D
+// bytes (8 KB at d = 64); each wave moves D / 32 one-kilobyte pieces of it.
+template <int D>
+constexpr int tile_elems() { return kTileK * D; }
+template <int D>
+constexpr int wave_copies() { return D / 32; }
 // A lane's tile sum above this (or not a number) makes the wave re-derive
 // the reference max.
 constexpr float kMaxTileSum = 4294967296.f;  // 2^32
 // A lane with nothing accumulated whose tile sum is below this re-derives
 // the reference max (the row's P would otherwise lose range).
 constexpr float kMinTileSum = 2.3283064365386963e-10f;  // 2^-32
-constexpr unsigned kBufferFlags = 0x00020000u;  // raw buffer, 32-bit data format
+[[maybe_unused]] constexpr unsigned kBufferFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
 struct PlanView {
   const ReqMeta* req;
@@ -114,20 +118,22 @@ __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
 // reduced to [-1/2, 1/2] revolution), rounded once to bf16.  The raw
 // loads are issued first (QRaw) and consumed later (finish_q), so that the
 // first key tile's copies are in flight while Q arrives and is rotated.
+template <int D>
 struct QRaw {
-  uint4 v[4];
+  uint4 v[D / 16];
   int64_t t;  // timestamp of the row
   int2 dsc;   // row descriptor
 };
 
 // Loads without branches: a row past the end of the request reads the
 // request's last token and is zeroed in finish_q (it is never written).
-__device__ __forceinline__ QRaw load_q_raw(const AttnLaunch& A, const int2* row_desc, int tokq_c,
-                                           int head, int hh, bool rope) {
-  QRaw r;
+template <int D>
+__device__ __forceinline__ QRaw<D> load_q_raw(const AttnLaunch& A, const int2* row_desc,
+                                              int tokq_c, int head, int hh, bool rope) {
+  QRaw<D> r;
   const unsigned short* Qp = (const unsigned short*)A.q + (int64_t)tokq_c * A.q_st + (int64_t)head * A.q_sh;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) r.v[s] = *(const uint4*)(Qp + 16 * s + 8 * hh);
+  for (int s = 0; s < D / 16; ++s) r.v[s] = *(const uint4*)(Qp + 16 * s + 8 * hh);
   r.t = rope ? A.ts[tokq_c] : 0;
   r.dsc = row_desc[tokq_c];
   return r;
@@ -136,16 +142,16 @@ __device__ __forceinline__ QRaw load_q_raw(const AttnLaunch& A, const int2* row_
 // With kNorm (QK Norm) the row is first scaled by 1 / sqrt(mean(x^2) + eps)
 // and the gain gamma[d] (NULL: 1); the two lane halves hold the two halves
 // of the row and meet through one lane ^ 32 exchange.
-template <bool kRope, bool kNorm>
-__device__ __forceinline__ void finish_q(bf16x8 (&qb)[4], const QRaw& raw, bool valid,
+template <bool kRope, bool kNorm, int D>
+__device__ __forceinline__ void finish_q(bf16x8 (&qb)[D / 16], const QRaw<D>& raw, bool valid,
                                          int64_t anchor, const RopeTab& tab, int hh, float qmul,
                                          float eps, const float* gamma) {
   const double dtd = (double)(raw.t - anchor);
-  float nscale[4][8];
+  float nscale[D / 16][8];
   if (kNorm) {
     float ss = 0.f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < D / 16; ++s) {
       const unsigned w[4] = {raw.v[s].x, raw.v[s].y, raw.v[s].z, raw.v[s].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -156,7 +162,7 @@ __device__ __forceinline__ void finish_q(bf16x8 (&qb)[4], const QRaw& raw, bool 
     ss += __shfl_xor(ss, 32, 64);
     const float rstd = rsqrtf(ss * (1.f / D) + eps);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < D / 16; ++s) {
       float4 g0 = make_float4(1.f, 1.f, 1.f, 1.f), g1 = g0;
       if (gamma) {
         g0 = *(const float4*)(gamma + 16 * s + 8 * hh);
@@ -168,7 +174,7 @@ __device__ __forceinline__ void finish_q(bf16x8 (&qb)[4], const QRaw& raw, bool 
     }
   }
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < D / 16; ++s) {
     unsigned w[4] = {raw.v[s].x, raw.v[s].y, raw.v[s].z, raw.v[s].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -196,20 +202,23 @@ __device__ __forceinline__ void finish_q(bf16x8 (&qb)[4], const QRaw& raw, bool 
 
 // Per-lane byte offsets of the direct buffer -> LDS copies.  A wave's
 // 16-byte-per-lane buffer load with the LDS bit fills 1 KB of LDS
-// contiguously (lane l at byte 16 l): 8 rows.  Wave w issues copies
-// j = 0, 1 for rows 8 (2 w + j) .. +7 of both the K and the V tile; the
-// offsets are relative to the tile's first row and do not change.
+// contiguously (lane l at byte 16 l): 512 / D rows of D / 8 chunks (8 rows
+// at d = 64).  Wave w issues copies j = 0 .. D / 32 - 1, piece
+// (D / 32) w + j of both the K and the V tile; the offsets are relative to
+// the tile's first row and do not change.
+template <int D>
 struct CopyMap {
-  unsigned koff[2];
-  unsigned voff[2];
+  unsigned koff[D / 32];
+  unsigned voff[D / 32];
 };
 
-__device__ __forceinline__ CopyMap copy_map(int wv, int lane, unsigned kst_b, unsigned vst_b) {
-  CopyMap c;
+template <int D>
+__device__ __forceinline__ CopyMap<D> copy_map(int wv, int lane, unsigned kst_b, unsigned vst_b) {
+  CopyMap<D> c;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = (2 * wv + j) * 64 + lane;
-    const int r = q >> 3, slot = q & 7;
+  for (int j = 0; j < D / 32; ++j) {
+    const int q = (D / 32 * wv + j) * 64 + lane;
+    const int r = q / (D / 8), slot = q % (D / 8);
     c.koff[j] = (unsigned)r * kst_b + 16u * (unsigned)(slot ^ kswz(r));
     c.voff[j] = (unsigned)r * vst_b + 16u * (unsigned)(slot ^ vswz(r));
   }
@@ -221,9 +230,11 @@ __device__ __forceinline__ CopyMap copy_map(int wv, int lane, unsigned kst_b, un
 // rows past the end of the request (ragged last tile only) are out of
 // range and load zeros; that tile is always PARTIAL, so their scores are
 // masked.
-__device__ __forceinline__ void tile_copy(unsigned short* kd, unsigned short* vd, const CopyMap& c,
+template <int D>
+__device__ __forceinline__ void tile_copy(unsigned short* kd, unsigned short* vd, const CopyMap<D>& c,
                                           const char* Kb, const char* Vb, unsigned kst_b,
                                           unsigned vst_b, int kt, int L, int wv) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins do not exist in the host pass
   const int c0 = kt * kTileK;
   const unsigned last = (unsigned)min(L - c0, kTileK) - 1u;  // last row inside the request
   const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
@@ -231,12 +242,13 @@ __device__ __forceinline__ void tile_copy(unsigned short* kd, unsigned short* vd
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(Vb + (int64_t)c0 * vst_b), 0, (int)(last * vst_b + 2u * D), (int)kBufferFlags);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LDS_PTR(void, kd + (2 * wv + j) * 512), 16,
+  for (int j = 0; j < D / 32; ++j) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LDS_PTR(void, kd + (D / 32 * wv + j) * 512), 16,
                                              c.koff[j], 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LDS_PTR(void, vd + (2 * wv + j) * 512), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LDS_PTR(void, vd + (D / 32 * wv + j) * 512), 16,
                                              c.voff[j], 0, 0, 0);
   }
+#endif
 }
 
 // Mask of one tile on the S^T accumulators: the lane's query sees key
@@ -270,13 +282,15 @@ __device__ __forceinline__ void mask_tile(f32x16& s0, f32x16& s1, int kt, int hh
 }
 
 // S^T = K Q^T + c for the wave's 32 queries (c: initial accumulator).
+template <int D>
 __device__ __forceinline__ void scores(f32x16& s0, f32x16& s1, const unsigned short* kb,
-                                       const bf16x8 (&q)[4], const f32x16& c, int li, int hh) {
+                                       const bf16x8 (&q)[D / 16], const f32x16& c, int li,
+                                       int hh) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < D / 16; ++s) {
     const int cc = 2 * s + hh;  // logical chunk: d = 16 s + 8 hh .. +7
-    const bf16x8 k0 = as_bf16x8(*(const uint4*)&kb[li * 64 + 8 * (cc ^ kswz(li))]);
-    const bf16x8 k1 = as_bf16x8(*(const uint4*)&kb[(32 + li) * 64 + 8 * (cc ^ kswz(32 + li))]);
+    const bf16x8 k0 = as_bf16x8(*(const uint4*)&kb[li * D + 8 * (cc ^ kswz(li))]);
+    const bf16x8 k1 = as_bf16x8(*(const uint4*)&kb[(32 + li) * D + 8 * (cc ^ kswz(32 + li))]);
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[s], s == 0 ? c : s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s == 0 ? c : s1, 0, 0, 0);
   }
@@ -323,19 +337,44 @@ __device__ __forceinline__ bool row_sees(int kt, bool partial, int lo, int hi, i
 // Scores of tile kt from K in global memory: the same bf16 rows in the same
 // product order as from LDS, so the same values.  Rows past the request's
 // end read its last row; the tile is then PARTIAL and they are masked.
+template <int D>
 __device__ __forceinline__ void scores_global(f32x16& s0, f32x16& s1, const unsigned short* Kh,
-                                              int64_t k_st, int kt, int L, const bf16x8 (&q)[4],
-                                              const f32x16& negm, int li, int hh) {
+                                              int64_t k_st, int kt, int L,
+                                              const bf16x8 (&q)[D / 16], const f32x16& negm,
+                                              int li, int hh) {
   const int c0 = kt * kTileK;
   const unsigned short* r0 = Kh + (int64_t)min(c0 + li, L - 1) * k_st + 8 * hh;
   const unsigned short* r1 = Kh + (int64_t)min(c0 + 32 + li, L - 1) * k_st + 8 * hh;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < D / 16; ++s) {
     const bf16x8 k0 = as_bf16x8(*(const uint4*)(r0 + 16 * s));
     const bf16x8 k1 = as_bf16x8(*(const uint4*)(r1 + 16 * s));
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[s], s == 0 ? negm : s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s == 0 ? negm : s1, 0, 0, 0);
   }
+}
+
+// O^T accumulators of one wave, 32 d values per block (d = 64 uses the first
+// two).  Named members rather than an array: an array indexed by a loop
+// counter stays in memory until the loops are unrolled, and the register
+// allocation that comes out of that is much larger.
+struct OAcc {
+  f32x16 b0, b1, b2, b3;
+};
+
+__device__ __forceinline__ f32x16 acc_get(const OAcc& o, int mb) {
+  return mb == 0 ? o.b0 : mb == 1 ? o.b1 : mb == 2 ? o.b2 : o.b3;
+}
+
+__device__ __forceinline__ void acc_mfma(OAcc& o, int mb, const bf16x8& a, const bf16x8& b) {
+  if (mb == 0)
+    o.b0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o.b0, 0, 0, 0);
+  else if (mb == 1)
+    o.b1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o.b1, 0, 0, 0);
+  else if (mb == 2)
+    o.b2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o.b2, 0, 0, 0);
+  else
+    o.b3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o.b3, 0, 0, 0);
 }
 
 // One 64-key tile for one wave (32 queries): scores, mask, P, O^T += V^T
@@ -353,15 +392,16 @@ __device__ __forceinline__ void scores_global(f32x16& s0, f32x16& s1, const unsi
 // or down; any other row moves m up by the tile's excess over it, with O
 // and l rescaled.  That path recomputes the tile's scores from K in global
 // memory, so the scores need not stay live once P is packed.
-template <bool kPreScaled>
-__device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, float& mref,
+template <bool kPreScaled, int D>
+__device__ __forceinline__ void tile_step(OAcc& o, f32x16& negm, float& mref,
                                           float& lsum, const unsigned short* kb,
-                                          const unsigned short* vb, const bf16x8 (&q)[4], int kt,
+                                          const unsigned short* vb, const bf16x8 (&q)[D / 16],
+                                          int kt,
                                           bool partial, int li, int hh, int lo, int hi, int self,
                                           int row, float mul, const unsigned short* Kh,
                                           int64_t k_st, int L) {
   f32x16 s0, s1;
-  scores(s0, s1, kb, q, negm, li, hh);
+  scores<D>(s0, s1, kb, q, negm, li, hh);
   if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
   bf16x8 pb[4];
   float ts = probs<false, !kPreScaled>(pb, s0, s1, 0.f, mul);
@@ -370,7 +410,7 @@ __device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, 
       lsum == 0.f && ts < kMinTileSum && row_sees(kt, partial, lo, hi, self, row);
   if (__any(big || tiny)) {
     // the scores are recomputed, so they need not stay live past the packing
-    scores_global(s0, s1, Kh, k_st, kt, L, q, negm, li, hh);
+    scores_global<D>(s0, s1, Kh, k_st, kt, L, q, negm, li, hh);
     if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
     float mx = s0[0];
 #pragma unroll
@@ -388,7 +428,14 @@ __device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, 
         const float alpha = __builtin_amdgcn_exp2f(kPreScaled ? -sh : -sh * mul);
         lsum *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { o0[r] *= alpha; o1[r] *= alpha; }
+        for (int r = 0; r < 16; ++r) {
+          o.b0[r] *= alpha;
+          o.b1[r] *= alpha;
+          if (D > 64) {
+            o.b2[r] *= alpha;
+            o.b3[r] *= alpha;
+          }
+        }
       }
     }
     mref += sh;
@@ -406,22 +453,19 @@ __device__ __forceinline__ void tile_step(f32x16& o0, f32x16& o1, f32x16& negm, 
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < D / 32; ++mb) {
       const int d0 = 32 * mb + 16 * (g & 1);
       const int col = d0 + 4 * (i & 3);
       const int ka = 16 * s + 4 * hh + rr;      // keys for e = 0..3
       const int kb2 = ka + 8;                   // keys for e = 4..7
       const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          LDS_PTR(v4i16, &vb[ka * 64 + 8 * ((col >> 3) ^ vswz(ka)) + (col & 7)]));
+          LDS_PTR(v4i16, &vb[ka * D + 8 * ((col >> 3) ^ vswz(ka)) + (col & 7)]));
       const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          LDS_PTR(v4i16, &vb[kb2 * 64 + 8 * ((col >> 3) ^ vswz(kb2)) + (col & 7)]));
+          LDS_PTR(v4i16, &vb[kb2 * D + 8 * ((col >> 3) ^ vswz(kb2)) + (col & 7)]));
       bf16x8 va;
       __builtin_memcpy(&va, &lo4, 8);
       __builtin_memcpy((char*)&va + 8, &hi4, 8);
-      if (mb == 0)
-        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], o0, 0, 0, 0);
-      else
-        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], o1, 0, 0, 0);
+      acc_mfma(o, mb, va, pb[s]);
     }
   }
 }
@@ -445,14 +489,21 @@ constexpr int kThreads = 256;  // 4 waves, 32 query rows each
 // anyway, so scale * log2(e) is folded in before that single rounding.
 // Without RoPE, Q is used exactly as given and the scale is applied to the
 // fp32 scores instead.
-template <bool kPreScaled, bool kNorm>
-__global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanView P, AttnLaunch A) {
-  // Three stages of K and V tiles as separate objects, so the compiler can
-  // tell the buffers being filled from the one being read.
-  __shared__ __attribute__((aligned(1024))) unsigned short K0[TILE_ELEMS], K1[TILE_ELEMS],
-      K2[TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) unsigned short V0[TILE_ELEMS], V1[TILE_ELEMS],
-      V2[TILE_ELEMS];
+//
+// d = 64 keeps three LDS stages (48 KB, three workgroups per CU); d = 128
+// keeps two (64 KB, two workgroups per CU, which is also what its registers
+// allow), so a copy has one step to land instead of two.
+template <bool kPreScaled, bool kNorm, int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P, AttnLaunch A) {
+  constexpr int kStages = D <= 64 ? 3 : 2;
+  constexpr int kTile = tile_elems<D>();
+  constexpr int kWc = wave_copies<D>();
+  // The stages as separate objects, so the compiler can tell the buffers
+  // being filled from the one being read.
+  __shared__ __attribute__((aligned(1024))) unsigned short K0[kTile], K1[kTile],
+      K2[kStages == 3 ? kTile : 8];
+  __shared__ __attribute__((aligned(1024))) unsigned short V0[kTile], V1[kTile],
+      V2[kStages == 3 ? kTile : 8];
 
   // a slot runs a whole item (schedule) or a CSR range of one (work list)
   int item, kbeg = 0, kend = -1, part = -1;
@@ -486,51 +537,56 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   const float sl2 = A.scale * 1.4426950408889634f;  // scale * log2(e)
   // Q's loads go out first, then the first key tile's copies; Q is rotated
   // while those copies land.
-  const QRaw qraw = load_q_raw(A, P.row_desc, m.tok_off + min(row, L - 1), head, hh, kPreScaled);
+  const QRaw<D> qraw =
+      load_q_raw<D>(A, P.row_desc, m.tok_off + min(row, L - 1), head, hh, kPreScaled);
   const int64_t anchor = kPreScaled ? ldc(A.anchors, req) : 0;
 
   const char* Kb = (const char*)((const unsigned short*)A.k + (int64_t)m.tok_off * A.k_st + (int64_t)head * A.k_sh);
   const char* Vb = (const char*)((const unsigned short*)A.v + (int64_t)m.tok_off * A.v_st + (int64_t)head * A.v_sh);
   // row strides in bytes (32-bit per-lane offsets: the host limits strides)
   const unsigned kst_b = (unsigned)A.k_st * 2u, vst_b = (unsigned)A.v_st * 2u;
-  const CopyMap cm = copy_map(wv, lane, kst_b, vst_b);
-  // Each wave zeroes the V rows its own copies fill (rows 16 wv .. +15 of
-  // every stage) and waits for those writes before its first copy: whatever
-  // a copy leaves unwritten then stays finite, so a masked key (P = 0) adds
-  // exactly 0 to O.  No other wave touches these rows, so no barrier.
+  const CopyMap<D> cm = copy_map<D>(wv, lane, kst_b, vst_b);
+  // Each wave zeroes the V rows its own copies fill (pieces kWc wv .. +kWc
+  // - 1 of every stage) and waits for those writes before its first copy:
+  // whatever a copy leaves unwritten then stays finite, so a masked key
+  // (P = 0) adds exactly 0 to O.  No other wave touches these rows, so no
+  // barrier.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    *(uint4*)&V0[(2 * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
-    *(uint4*)&V1[(2 * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
-    *(uint4*)&V2[(2 * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < kWc; ++j) {
+    *(uint4*)&V0[(kWc * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
+    *(uint4*)&V1[(kWc * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
+    if (kStages == 3) *(uint4*)&V2[(kWc * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
-  f32x16 o0, o1, negm;
+  OAcc o;
+  f32x16 negm;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) { o0[r] = 0.f; o1[r] = 0.f; negm[r] = 0.f; }
+  for (int r = 0; r < 16; ++r) negm[r] = 0.f;
+  o.b0 = o.b1 = o.b2 = o.b3 = negm;
   float mref = 0.f, lsum = 0.f;
 
   const int e0 = ldc(P.qtile_ptr, qg) + kbeg;
   const int n = kend >= 0 ? kend - kbeg : ldc(P.qtile_ptr, qg + 1) - e0;
-  // Step i computes tile i from stage i % 3 while the copies of tile i + 2
-  // fill stage (i + 2) % 3 (which held tile i - 1): every copy has two
-  // steps to land.  The wait before the barrier that ends step i leaves the
-  // step's own four copies (two of K, two of V per wave) in flight and
-  // covers those of tile i + 1.  The loop is unrolled by three so each
-  // stage is a distinct LDS object.  Copies past the last tile re-read the
-  // last tile into an idle stage (no branch around loads); an item without
-  // key tiles still copies the request's first tile (in bounds, never
-  // read), so the copies are unconditional and Q's loads can be waited for
-  // without waiting for them.
+  // Three stages: step i computes tile i from stage i % 3 while the copies
+  // of tile i + 2 fill stage (i + 2) % 3 (which held tile i - 1): every copy
+  // has two steps to land.  The wait before the barrier that ends step i
+  // leaves the step's own copies (two of K, two of V per wave) in flight and
+  // covers those of tile i + 1.  The loop is unrolled by three so each stage
+  // is a distinct LDS object.  Two stages: step i computes tile i while the
+  // copies of tile i + 1 fill the other stage, and waits for all of them.
+  // Copies past the last tile re-read the last tile into an idle stage (no
+  // branch around loads); an item without key tiles still copies the
+  // request's first tile (in bounds, never read), so the copies are
+  // unconditional and Q's loads can be waited for without waiting for them.
   const int w_cur0 = n > 0 ? ldc(P.ktile_word, e0) : 0;
   const int w_cur1 = n > 1 ? ldc(P.ktile_word, e0 + 1) : w_cur0;
   int w_cur = w_cur0, w_nxt = w_cur1;
-  tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_cur0 & 0x7fffffff, L, wv);
-  tile_copy(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_cur1 & 0x7fffffff, L, wv);
-  bf16x8 q[4];
-  finish_q<kPreScaled, kNorm>(q, qraw, rvalid, anchor, A.tab, hh, kPreScaled ? sl2 : 1.f, A.eps,
-                              A.gamma_q);
+  tile_copy<D>(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_cur0 & 0x7fffffff, L, wv);
+  if (kStages == 3) tile_copy<D>(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_cur1 & 0x7fffffff, L, wv);
+  bf16x8 q[D / 16];
+  finish_q<kPreScaled, kNorm, D>(q, qraw, rvalid, anchor, A.tab, hh, kPreScaled ? sl2 : 1.f,
+                                 A.eps, A.gamma_q);
   const int lo = rvalid ? qraw.dsc.x : 0;
   const int hi = rvalid ? qraw.dsc.y & 0x7fffffff : 0;
   const int self = rvalid && qraw.dsc.y < 0;
@@ -538,33 +594,56 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   __syncthreads();
 
   const unsigned short* Kh = (const unsigned short*)Kb;
-  for (int it = 0; it < n; it += 3) {
-    {
-      const int w_nn = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
-      tile_copy(K2, V2, cm, Kb, Vb, kst_b, vst_b, w_nn & 0x7fffffff, L, wv);
-      tile_step<kPreScaled>(o0, o1, negm, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0,
-                            li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
-      step_barrier();
-      w_cur = w_nxt;
-      w_nxt = w_nn;
+  if (kStages == 3) {
+    for (int it = 0; it < n; it += 3) {
+      {
+        const int w_nn = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
+        tile_copy<D>(K2, V2, cm, Kb, Vb, kst_b, vst_b, w_nn & 0x7fffffff, L, wv);
+        tile_step<kPreScaled, D>(o, negm, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0,
+                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+        step_barrier();
+        w_cur = w_nxt;
+        w_nxt = w_nn;
+      }
+      if (it + 1 < n) {
+        const int w_nn = ldc(P.ktile_word, e0 + min(it + 3, n - 1));
+        tile_copy<D>(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_nn & 0x7fffffff, L, wv);
+        tile_step<kPreScaled, D>(o, negm, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0,
+                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+        step_barrier();
+        w_cur = w_nxt;
+        w_nxt = w_nn;
+      }
+      if (it + 2 < n) {
+        const int w_nn = ldc(P.ktile_word, e0 + min(it + 4, n - 1));
+        tile_copy<D>(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_nn & 0x7fffffff, L, wv);
+        tile_step<kPreScaled, D>(o, negm, mref, lsum, K2, V2, q, w_cur & 0x7fffffff, w_cur < 0,
+                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+        step_barrier();
+        w_cur = w_nxt;
+        w_nxt = w_nn;
+      }
     }
-    if (it + 1 < n) {
-      const int w_nn = ldc(P.ktile_word, e0 + min(it + 3, n - 1));
-      tile_copy(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_nn & 0x7fffffff, L, wv);
-      tile_step<kPreScaled>(o0, o1, negm, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0,
-                            li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
-      step_barrier();
-      w_cur = w_nxt;
-      w_nxt = w_nn;
-    }
-    if (it + 2 < n) {
-      const int w_nn = ldc(P.ktile_word, e0 + min(it + 4, n - 1));
-      tile_copy(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_nn & 0x7fffffff, L, wv);
-      tile_step<kPreScaled>(o0, o1, negm, mref, lsum, K2, V2, q, w_cur & 0x7fffffff, w_cur < 0,
-                            li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
-      step_barrier();
-      w_cur = w_nxt;
-      w_nxt = w_nn;
+  } else {
+    for (int it = 0; it < n; it += 2) {
+      {
+        tile_copy<D>(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
+        tile_step<kPreScaled, D>(o, negm, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0,
+                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        w_cur = w_nxt;
+        w_nxt = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
+      }
+      if (it + 1 < n) {
+        tile_copy<D>(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
+        tile_step<kPreScaled, D>(o, negm, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0,
+                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        w_cur = w_nxt;
+        w_nxt = ldc(P.ktile_word, e0 + min(it + 3, n - 1));
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no copy outlives the item
@@ -578,11 +657,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
     const int rl = wv * 32 + li;
     float* orow = pp + rl * D;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = 8 * g + 4 * hh;
-      *(float4*)(orow + d) = make_float4(o0[4 * g], o0[4 * g + 1], o0[4 * g + 2], o0[4 * g + 3]);
-      *(float4*)(orow + 32 + d) =
-          make_float4(o1[4 * g], o1[4 * g + 1], o1[4 * g + 2], o1[4 * g + 3]);
+    for (int mb = 0; mb < D / 32; ++mb) {
+      const f32x16 ob = acc_get(o, mb);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * mb + 8 * g + 4 * hh;
+        *(float4*)(orow + d) = make_float4(ob[4 * g], ob[4 * g + 1], ob[4 * g + 2], ob[4 * g + 3]);
+      }
     }
     if (hh == 0) {
       pp[kTileQ * D + rl] = ltot > 0.f ? mref : -INFINITY;  // -inf: nothing seen
@@ -593,12 +674,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
   const float inv = (ltot > 0.f ? 1.f / ltot : 0.f) * pz;
   unsigned short* Op = (unsigned short*)A.o + (int64_t)tokq * A.o_st + (int64_t)head * A.o_sh;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int d = 8 * g + 4 * hh;
-    *(uint2*)(Op + d) = make_uint2(pack_bf16x2(o0[4 * g] * inv, o0[4 * g + 1] * inv),
-                                   pack_bf16x2(o0[4 * g + 2] * inv, o0[4 * g + 3] * inv));
-    *(uint2*)(Op + 32 + d) = make_uint2(pack_bf16x2(o1[4 * g] * inv, o1[4 * g + 1] * inv),
-                                        pack_bf16x2(o1[4 * g + 2] * inv, o1[4 * g + 3] * inv));
+  for (int mb = 0; mb < D / 32; ++mb) {
+    const f32x16 ob = acc_get(o, mb);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * mb + 8 * g + 4 * hh;
+      *(uint2*)(Op + d) = make_uint2(pack_bf16x2(ob[4 * g] * inv, ob[4 * g + 1] * inv),
+                                     pack_bf16x2(ob[4 * g + 2] * inv, ob[4 * g + 3] * inv));
+    }
   }
   if (A.lse && hh == 0)
     A.lse[(int64_t)head * A.T + tokq] =
@@ -606,22 +689,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_d64_kernel(PlanVie
                     : -INFINITY) * pz;
 }
 
+template <int D>
+hipError_t launch_d(const PlanView& P, const AttnLaunch& a, dim3 grid, hipStream_t s) {
+  if (a.rope_q && a.norm_q)
+    hipLaunchKernelGGL((attn_mfma_bf16_kernel<true, true, D>), grid, dim3(kThreads), 0, s, P, a);
+  else if (a.rope_q)
+    hipLaunchKernelGGL((attn_mfma_bf16_kernel<true, false, D>), grid, dim3(kThreads), 0, s, P, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_bf16_kernel<false, false, D>), grid, dim3(kThreads), 0, s, P,
+                       a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_attn_mfma_bf16_d64(const rk_plan* p, const AttnLaunch& a, hipStream_t s) {
+hipError_t launch_attn_mfma_bf16(const rk_plan* p, const AttnLaunch& a, hipStream_t s) {
   if (p->slots == 0) return hipSuccess;
   const bool wl = p->grid > p->slots;
   PlanView P{p->dev.req, p->dev.qt_req, p->dev.row_desc, p->dev.qtile_ptr, p->dev.ktile_word,
              p->dev.sched, wl ? p->dev.work : nullptr};
   const dim3 grid((unsigned)p->grid);
-  if (a.rope_q && a.norm_q)
-    hipLaunchKernelGGL((attn_mfma_bf16_d64_kernel<true, true>), grid, dim3(kThreads), 0, s, P, a);
-  else if (a.rope_q)
-    hipLaunchKernelGGL((attn_mfma_bf16_d64_kernel<true, false>), grid, dim3(kThreads), 0, s, P, a);
-  else
-    hipLaunchKernelGGL((attn_mfma_bf16_d64_kernel<false, false>), grid, dim3(kThreads), 0, s, P,
-                       a);
-  return hipGetLastError();
+  if (a.d == 128) return launch_d<128>(P, a, grid, s);
+  return launch_d<64>(P, a, grid, s);
 }
 
 }  // namespace rk

@@ -267,7 +267,8 @@ hipError_t launch_pointwise_mfma_bf16_d64(const rk_plan* p, const PwLaunch& a, h
 
 hipError_t launch_attn_reference(const rk_plan* p, const AttnLaunch& a, rk_dtype dt,
                                  hipStream_t s);
-hipError_t launch_attn_mfma_bf16_d64(const rk_plan* p, const AttnLaunch& a, hipStream_t s);
+// bf16 MFMA forward; d_head 64 or 128
+hipError_t launch_attn_mfma_bf16(const rk_plan* p, const AttnLaunch& a, hipStream_t s);
 // Device address of the library's scratch array on the current GPU
 // (RK_STATIC_SCRATCH_BYTES, 256-byte aligned), looked up on the first call
 // per device (scratch.hip).

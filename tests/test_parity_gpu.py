@@ -443,16 +443,18 @@ def test_attention_random_layouts(rk, seed, d):
             _check(wl, o, ref, lse, ref_lse)
 
 
-def test_attention_without_rope(rk):
-    wl = make_custom(random_layout(np.random.default_rng(9), 3, 400), heads=2, d_head=64,
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_without_rope(rk, d):
+    wl = make_custom(random_layout(np.random.default_rng(9), 3, 400), heads=2, d_head=d,
                      dtype="bf16", seed=9, delay=600)
     plan, o, lse = _run(rk, wl, rope=False)
     ref, ref_lse = _oracle_full(wl, rope=False)
     _check(wl, o, ref, lse, ref_lse)
 
 
-def test_mfma_and_reference_kernels_agree(rk):
-    wl = make_custom(random_layout(np.random.default_rng(10), 4, 600), heads=2, d_head=64,
+@pytest.mark.parametrize("d", [64, 128])
+def test_mfma_and_reference_kernels_agree(rk, d):
+    wl = make_custom(random_layout(np.random.default_rng(10), 4, 600), heads=2, d_head=d,
                      dtype="bf16", seed=10, window=77)
     _, o1, l1 = _run(rk, wl)
     _, o2, l2 = _run(rk, wl, reference=True)
@@ -543,6 +545,34 @@ def test_attention_tm20k_every_item(rk):
                                              rope=_rope(wl))
         _check(wl, o[toks, h], ref, lse[h, toks], ref_lse)
         _say(f"[gpu] workload 5 head {h}: {toks.shape[0]} rows match")
+
+
+def test_attention_d128_every_item(rk):
+    """bf16 with d_head = 128 (the MFMA kernel's two-stage form): four heads
+    over requests of 1,500 to 6,000 history tokens with realtime events and
+    candidates under a one-hour delay; rows 0, 63, 64 and 127 of every query
+    tile of every request and head against the oracle."""
+    rng = np.random.default_rng(128)
+    reqs = []
+    for lh, nr, nc in ((6000, 40, 64), (1500, 0, 200), (3900, 120, 1), (4500, 7, 33)):
+        hist = np.sort(rng.integers(NOW - 10**7, NOW - 60, lh)).astype(np.int64)
+        segs = [(HISTORY, hist)]
+        if nr:
+            segs.append((REALTIME, np.sort(rng.integers(NOW - 7200, NOW, nr)).astype(np.int64)))
+        segs.append((CANDIDATE, np.full(nc, NOW, np.int64)))
+        reqs.append(segs)
+    wl = make_custom(reqs, heads=4, d_head=128, dtype="bf16", seed=128, delay=3600,
+                     name="d128-every-item")
+    plan, o, lse = _run(rk, wl)
+    toks = _item_edge_tokens(wl)
+    for h in range(wl.heads):
+        ref, ref_lse = oracle.attention_rows(wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q,
+                                             wl.k, wl.v, toks, h, delay=wl.delay,
+                                             window=wl.window,
+                                             static_bidirectional=wl.static_bidirectional,
+                                             rope=_rope(wl))
+        _check(wl, o[toks, h], ref, lse[h, toks], ref_lse)
+        _say(f"[gpu] d128 head {h}: {toks.shape[0]} rows match")
 
 
 @pytest.mark.parametrize("delay,window", [(0, 0), (3600, 4096)])

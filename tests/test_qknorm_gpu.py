@@ -4,7 +4,7 @@ the C ABI against the CPU fp64 oracle.
 * rk_qk_norm_rope (norm, then rotation by t - anchor, or norm only):
   fp32 within 1e-5, bf16 within one bf16 rounding (2^-8 relative to the
   row's magnitude); vector and scalar paths; every d it supports.
-* Attention with qk_norm: MFMA (bf16, d = 64) and plain kernels (fp32 and
+* Attention with qk_norm: MFMA (bf16, d = 64 and 128) and plain kernels (fp32 and
   bf16, d = 32, 64, 128), K normalised by the attention's own pass or
   prepared by rk_qk_norm_rope (RK_ATTN_K_PREROTATED), against the oracle;
   fp32 within 1e-4 max-abs, bf16 within 2e-2 max-abs and 1e-2 relative L2.

@@ -12,9 +12,9 @@ softmax results to a common max and sums them.
   more, it mirrors the schedule.
 * Outputs of split items match the oracle to the parity bar and the unsplit
   call to a bf16 / fp32 rounding step; unsplit items stay bit-identical.
-  Covered for the MFMA kernel with Q pre-scaled (time RoPE) and raw (no
-  RoPE), and for the plain kernel (fp32 and bf16, d_head 32 and 128): the
-  three units the kernels keep their running max in.
+  Covered for the MFMA kernel (d_head 64 and 128) with Q pre-scaled (time
+  RoPE) and raw (no RoPE), and for the plain kernel (fp32 and bf16, d_head
+  32, 64 and 128): the three units the kernels keep their running max in.
 * Rows that see nothing in any chunk come out as 0 and LSE -inf.
 """
 
@@ -152,7 +152,9 @@ CASES = [
     ("bf16", 64, True, True),     # plain kernel: max in natural units
     ("f32", 32, True, False),
     ("f32", 128, False, False),
-    ("bf16", 128, True, False),
+    ("bf16", 128, True, False),   # MFMA at d_head 128 (two-stage form)
+    ("bf16", 128, False, False),
+    ("bf16", 128, True, True),    # plain kernel at d_head 128
 ]
 
 
