@@ -45,7 +45,7 @@ struct Layout {
          host_blob = 0, off_row_desc = 0, off_tile_count = 0, off_tile_class = 0, off_qt_nnz = 0,
          off_qt_pairs = 0, off_qt_full = 0,
          off_qtile_ptr = 0, off_ktile_idx = 0, off_ktile_word = 0, off_qorder = 0, off_sched = 0,
-         off_work = 0, off_splits = 0, off_act = 0, off_kt_req = 0, off_kgroups = 0,
+         off_work = 0, off_irec = 0, off_splits = 0, off_act = 0, off_kt_req = 0, off_kgroups = 0,
          off_kqueue_start = 0, off_kt_nnz = 0, off_kt_ptr = 0, off_qtile_word = 0,
          off_korder = 0, off_ksched = 0, total = 0;
 };
@@ -259,6 +259,7 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->off_qorder = take(sizeof(int32_t) * (size_t)nq);
   L->off_sched = take(sizeof(int32_t) * (size_t)L->slots);
   L->off_work = take(sizeof(rk::WorkEntry) * (size_t)(L->slots + rk::kSplitTarget));
+  L->off_irec = take(sizeof(rk::ItemRec) * (size_t)(L->slots + rk::kSplitTarget));
   L->off_splits = take(sizeof(rk::SplitEntry) * (size_t)rk::kSplitTarget);
   L->off_act = take(sizeof(int32_t) * (size_t)(rk::kSplitTarget / 2));
   L->off_kt_nnz = take(sizeof(int32_t) * (size_t)nk);
@@ -400,6 +401,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   p->off_qorder = L.off_qorder;
   p->off_sched = L.off_sched;
   p->off_work = L.off_work;
+  p->off_irec = L.off_irec;
   p->off_splits = L.off_splits;
   p->off_act = L.off_act;
   p->off_totals = L.off_totals;
@@ -436,6 +438,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   D.qorder = (int32_t*)(ws + L.off_qorder);
   D.sched = (int32_t*)(ws + L.off_sched);
   D.work = (rk::WorkEntry*)(ws + L.off_work);
+  D.irec = (rk::ItemRec*)(ws + L.off_irec);
   D.splits = (rk::SplitEntry*)(ws + L.off_splits);
   D.act_slots = (int32_t*)(ws + L.off_act);
   D.kt_req = (int32_t*)(ws + L.off_kt_req);

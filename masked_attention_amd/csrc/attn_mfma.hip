@@ -60,13 +60,9 @@ constexpr float kMinTileSum = 2.3283064365386963e-10f;  // 2^-32
 [[maybe_unused]] constexpr unsigned kBufferFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
 struct PlanView {
-  const ReqMeta* req;
-  const int32_t* qt_req;
+  const ItemRec* irec;  // launch slot -> item record
   const int2* row_desc;
-  const int32_t* qtile_ptr;
   const int32_t* ktile_word;
-  const int32_t* sched;
-  const WorkEntry* work;  // launch slot -> (item, CSR range, part), or null
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -505,52 +501,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
   __shared__ __attribute__((aligned(1024))) unsigned short V0[kTile], V1[kTile],
       V2[kStages == 3 ? kTile : 8];
 
-  // a slot runs a whole item (schedule) or a CSR range of one (work list)
-  int item, kbeg = 0, kend = -1, part = -1;
-  if (P.work) {
-    const WorkEntry we = ldc(P.work, blockIdx.x);
-    item = we.item;
-    kbeg = we.kbeg;
-    kend = we.kend;
-    part = we.part;
-  } else {
-    item = ldc(P.sched, blockIdx.x);
-  }
-  if (item < 0) return;
-  const float pz = plan_poison(A.plan_err);
-  const int qg = item / A.H;
-  const int head = item - qg * A.H;
-  const int req = ldc(P.qt_req, qg);
-  const ReqMeta m = ldc(P.req, req);
-  const int qt = qg - m.qt_off;
-  const int L = m.len;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
-  const int hh = lane >> 5;   // lane half
-  const int li = lane & 31;   // query column of this lane
-  const int row = qt * kTileQ + wv * 32 + li;
-  const bool rvalid = row < L;
-  const int tokq = m.tok_off + row;
-
-  const float sl2 = A.scale * 1.4426950408889634f;  // scale * log2(e)
-  // Q's loads go out first, then the first key tile's copies; Q is rotated
-  // while those copies land.
-  const QRaw<D> qraw =
-      load_q_raw<D>(A, P.row_desc, m.tok_off + min(row, L - 1), head, hh, kPreScaled);
-  const int64_t anchor = kPreScaled ? ldc(A.anchors, req) : 0;
-
-  const char* Kb = (const char*)((const unsigned short*)A.k + (int64_t)m.tok_off * A.k_st + (int64_t)head * A.k_sh);
-  const char* Vb = (const char*)((const unsigned short*)A.v + (int64_t)m.tok_off * A.v_st + (int64_t)head * A.v_sh);
-  // row strides in bytes (32-bit per-lane offsets: the host limits strides)
-  const unsigned kst_b = (unsigned)A.k_st * 2u, vst_b = (unsigned)A.v_st * 2u;
-  const CopyMap<D> cm = copy_map<D>(wv, lane, kst_b, vst_b);
   // Each wave zeroes the V rows its own copies fill (pieces kWc wv .. +kWc
   // - 1 of every stage) and waits for those writes before its first copy:
   // whatever a copy leaves unwritten then stays finite, so a masked key
   // (P = 0) adds exactly 0 to O.  No other wave touches these rows, so no
-  // barrier.
+  // barrier.  This comes first, while the only memory accesses in flight
+  // are the slot's own record and arguments, so the wait delays nothing.
 #pragma unroll
   for (int j = 0; j < kWc; ++j) {
     *(uint4*)&V0[(kWc * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
@@ -559,6 +518,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
+  // a slot runs a whole item or a CSR range of one (split chunk)
+  const ItemRec ir = ldc(P.irec, blockIdx.x);
+  if (ir.head < 0) return;
+  const float pz = plan_poison(A.plan_err);
+  const int head = ir.head;
+  const int L = ir.len;
+  const int part = ir.part;
+
+  const int hh = lane >> 5;   // lane half
+  const int li = lane & 31;   // query column of this lane
+  const int row = ir.row0 + wv * 32 + li;
+  const bool rvalid = row < L;
+  const int tokq = ir.tok_off + row;
+
+  const float sl2 = A.scale * 1.4426950408889634f;  // scale * log2(e)
+  // Q's loads go out first, then the first key tile's copies; Q is rotated
+  // while those copies land.
+  const QRaw<D> qraw =
+      load_q_raw<D>(A, P.row_desc, ir.tok_off + min(row, L - 1), head, hh, kPreScaled);
+  const int64_t anchor = kPreScaled ? ldc(A.anchors, ir.req) : 0;
+
+  const char* Kb = (const char*)((const unsigned short*)A.k + (int64_t)ir.tok_off * A.k_st + (int64_t)head * A.k_sh);
+  const char* Vb = (const char*)((const unsigned short*)A.v + (int64_t)ir.tok_off * A.v_st + (int64_t)head * A.v_sh);
+  // row strides in bytes (32-bit per-lane offsets: the host limits strides)
+  const unsigned kst_b = (unsigned)A.k_st * 2u, vst_b = (unsigned)A.v_st * 2u;
+  const CopyMap<D> cm = copy_map<D>(wv, lane, kst_b, vst_b);
   OAcc o;
   f32x16 negm;
 #pragma unroll
@@ -566,8 +551,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
   o.b0 = o.b1 = o.b2 = o.b3 = negm;
   float mref = 0.f, lsum = 0.f;
 
-  const int e0 = ldc(P.qtile_ptr, qg) + kbeg;
-  const int n = kend >= 0 ? kend - kbeg : ldc(P.qtile_ptr, qg + 1) - e0;
+  const int e0 = ir.e0;
+  const int n = ir.n;
   // Three stages: step i computes tile i from stage i % 3 while the copies
   // of tile i + 2 fill stage (i + 2) % 3 (which held tile i - 1): every copy
   // has two steps to land.  The wait before the barrier that ends step i
@@ -576,11 +561,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
   // is a distinct LDS object.  Two stages: step i computes tile i while the
   // copies of tile i + 1 fill the other stage, and waits for all of them.
   // Copies past the last tile re-read the last tile into an idle stage (no
-  // branch around loads); an item without key tiles still copies the
-  // request's first tile (in bounds, never read), so the copies are
-  // unconditional and Q's loads can be waited for without waiting for them.
-  const int w_cur0 = n > 0 ? ldc(P.ktile_word, e0) : 0;
-  const int w_cur1 = n > 1 ? ldc(P.ktile_word, e0 + 1) : w_cur0;
+  // branch around loads; making them conditional measured slower); an item
+  // without key tiles still copies the request's first tile (in bounds,
+  // never read), so the copies are unconditional and Q's loads can be
+  // waited for without waiting for them.
+  const int w_cur0 = ir.w0;
+  const int w_cur1 = ir.w1;
   int w_cur = w_cur0, w_nxt = w_cur1;
   tile_copy<D>(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_cur0 & 0x7fffffff, L, wv);
   if (kStages == 3) tile_copy<D>(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_cur1 & 0x7fffffff, L, wv);
@@ -705,9 +691,7 @@ hipError_t launch_d(const PlanView& P, const AttnLaunch& a, dim3 grid, hipStream
 
 hipError_t launch_attn_mfma_bf16(const rk_plan* p, const AttnLaunch& a, hipStream_t s) {
   if (p->slots == 0) return hipSuccess;
-  const bool wl = p->grid > p->slots;
-  PlanView P{p->dev.req, p->dev.qt_req, p->dev.row_desc, p->dev.qtile_ptr, p->dev.ktile_word,
-             p->dev.sched, wl ? p->dev.work : nullptr};
+  PlanView P{p->dev.irec, p->dev.row_desc, p->dev.ktile_word};
   const dim3 grid((unsigned)p->grid);
   if (a.d == 128) return launch_d<128>(P, a, grid, s);
   return launch_d<64>(P, a, grid, s);

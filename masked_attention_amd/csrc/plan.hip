@@ -144,6 +144,37 @@ __device__ void seg_search(const uint8_t* __restrict__ kr, int L, int* lo_s, int
   }
 }
 
+// Record of a launch slot without work.
+__device__ __forceinline__ ItemRec no_item_rec() {
+  ItemRec rc;
+  rc.tok_off = rc.len = rc.row0 = rc.e0 = rc.n = rc.req = rc.w0 = rc.w1 = 0;
+  rc.head = rc.part = -1;
+  rc.pad[0] = rc.pad[1] = 0;
+  return rc;
+}
+
+// Record of item (q-tile * H + head) over CSR entries [kbeg, kend) of its
+// row (kend < 0: the whole row); the CSR must be complete.
+__device__ __forceinline__ ItemRec item_rec(const PlanDev& P, int item, int kbeg, int kend,
+                                            int part, int H) {
+  if (item < 0) return no_item_rec();
+  const int qg = item / H;
+  const int r = P.qt_req[qg];
+  const ReqMeta m = P.req[r];
+  ItemRec rc = no_item_rec();
+  rc.tok_off = m.tok_off;
+  rc.len = m.len;
+  rc.row0 = (qg - m.qt_off) * kTileQ;
+  rc.head = item - qg * H;
+  rc.e0 = P.qtile_ptr[qg] + kbeg;
+  rc.n = kend >= 0 ? kend - kbeg : P.qtile_ptr[qg + 1] - rc.e0;
+  rc.req = r;
+  rc.part = part;
+  rc.w0 = rc.n > 0 ? P.ktile_word[rc.e0] : 0;
+  rc.w1 = rc.n > 1 ? P.ktile_word[rc.e0 + 1] : rc.w0;
+  return rc;
+}
+
 // One block (256 threads) per global q-tile: the request's segment starts
 // (sampled search; the request's first q-tile records them), the order
 // checks and visible interval (row descriptor) of each of its 128 rows, and
@@ -174,8 +205,10 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
   __shared__ int lo_s[3], hi_s[3];
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
-  for (int64_t x = (int64_t)g * blockDim.x + tid; x < slots; x += (int64_t)gridDim.x * blockDim.x)
+  for (int64_t x = (int64_t)g * blockDim.x + tid; x < slots; x += (int64_t)gridDim.x * blockDim.x) {
     P.sched[x] = -1;
+    P.irec[x] = no_item_rec();
+  }
   const int r = P.qt_req[g];
   const ReqMeta m = P.req[r];
   const int qt = g - m.qt_off;
@@ -350,6 +383,7 @@ __global__ __launch_bounds__(256) void plan_csr_sched_kernel(PlanDev P, int NQ, 
                                                              int G, int write_sched) {
   __shared__ int smem[32];
   __shared__ long long red[16];
+  __shared__ int w01[2];  // the row's first two CSR words
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   if (g == NQ) {
@@ -396,13 +430,25 @@ __global__ __launch_bounds__(256) void plan_csr_sched_kernel(PlanDev P, int NQ, 
     int total;
     const int ex = block_exclusive_scan(flag, smem, &total);
     if (flag) {
-      P.ktile_idx[base + run + ex] = kt;
-      P.ktile_word[base + run + ex] =
+      const int word =
           (int)((unsigned)kt | ((unsigned)(P.tile_class[row + kt] == RK_TILE_PARTIAL) << 31));
+      P.ktile_idx[base + run + ex] = kt;
+      P.ktile_word[base + run + ex] = word;
+      if (run + ex < 2) w01[run + ex] = word;
     }
     run += total;
   }
   if (write_sched) {
+    __syncthreads();
+    ItemRec rc = no_item_rec();
+    rc.tok_off = m.tok_off;
+    rc.len = m.len;
+    rc.row0 = qt * kTileQ;
+    rc.e0 = base;
+    rc.n = na;
+    rc.req = r;
+    rc.w0 = na > 0 ? w01[0] : 0;
+    rc.w1 = na > 1 ? w01[1] : rc.w0;
     for (int h = tid; h < H; h += blockDim.x) {
       const int ga = P.group_of[(int64_t)r * H + h];
       const int f = P.ilv[ga];                  // first group of ga's block
@@ -411,6 +457,8 @@ __global__ __launch_bounds__(256) void plan_csr_sched_kernel(PlanDev P, int NQ, 
       int q = 0;
       while (q < kNumXcd - 1 && ga >= P.queue_start[q + 1]) ++q;
       P.sched[(int64_t)idx * kNumXcd + q] = g * H + h;
+      rc.head = h;
+      P.irec[(int64_t)idx * kNumXcd + q] = rc;
     }
   }
 }
@@ -504,6 +552,7 @@ __global__ void plan_sched_kernel(PlanDev P, int64_t slots, int H, int cand_only
     }
   }
   P.sched[s] = item;
+  P.irec[s] = item_rec(P, item, 0, -1, -1, H);
   if (cand_only) {
     // count the active slots (one atomic per wave) and keep the first
     // kSplitTarget / 2 of them, in arrival order, for the work list
@@ -541,7 +590,12 @@ __global__ __launch_bounds__(1024) void plan_work_kernel(PlanDev P, int slots, i
   const bool split = n_act < kMaxAct;
   if (!split) {
     const int s = blockIdx.x * blockDim.x + t;
-    if (s < grid) P.work[s] = s < slots ? WorkEntry{P.sched[s], 0, -1, -1} : WorkEntry{-1, 0, 0, -1};
+    if (s < grid && s >= slots) {  // slots below: the schedule kernel wrote their records
+      P.work[s] = WorkEntry{-1, 0, 0, -1};
+      P.irec[s] = no_item_rec();
+    } else if (s < slots) {
+      P.work[s] = WorkEntry{P.sched[s], 0, -1, -1};
+    }
     if (blockIdx.x == 0) {
       for (int k = t; k < kSplitTarget; k += blockDim.x) P.splits[k] = SplitEntry{-1, 0, 0, 0};
       if (t == 0) {
@@ -553,7 +607,10 @@ __global__ __launch_bounds__(1024) void plan_work_kernel(PlanDev P, int slots, i
   }
   if (blockIdx.x > 0) {
     const int s = blockIdx.x * blockDim.x + t;
-    if (s >= kHead && s < grid) P.work[s] = WorkEntry{-1, 0, 0, -1};
+    if (s >= kHead && s < grid) {
+      P.work[s] = WorkEntry{-1, 0, 0, -1};
+      P.irec[s] = no_item_rec();
+    }
     return;
   }
   int slot = 0x7fffffff, item = -1, n = 0;
@@ -593,9 +650,14 @@ __global__ __launch_bounds__(1024) void plan_work_kernel(PlanDev P, int slots, i
   for (int j = 0; j < c; ++j) {
     // chunk lengths differ by at most one and none is empty (c <= n)
     const int kb = (int)((long long)j * n / c), ke = (int)((long long)(j + 1) * n / c);
-    P.work[w++] = WorkEntry{item, kb, ke, c > 1 ? part++ : -1};
+    const int pi = c > 1 ? part++ : -1;
+    P.irec[w] = item_rec(P, item, kb, ke, pi, H);
+    P.work[w++] = WorkEntry{item, kb, ke, pi};
   }
-  for (int s = w_tot + t; s < min(grid, kHead); s += blockDim.x) P.work[s] = WorkEntry{-1, 0, 0, -1};
+  for (int s = w_tot + t; s < min(grid, kHead); s += blockDim.x) {
+    P.work[s] = WorkEntry{-1, 0, 0, -1};
+    P.irec[s] = no_item_rec();
+  }
   for (int k = s_tot + t; k < kSplitTarget; k += blockDim.x) P.splits[k] = SplitEntry{-1, 0, 0, 0};
   if (t == 0) {
     P.totals->n_work = w_tot;

@@ -68,6 +68,26 @@ struct PlanTotals {
 struct WorkEntry {
   int32_t item, kbeg, kend, part;
 };
+// What a forward kernel needs to start one launch slot's work, written by
+// the planner next to the slot's schedule or work entry so that a
+// workgroup's first memory access (one 48-byte scalar load) hands it the
+// request geometry, the CSR range and its first two entries: the Q loads
+// and the first key tiles' copies then go out one memory latency after
+// launch instead of four (schedule -> q-tile's request -> request -> CSR).
+struct ItemRec {
+  int32_t tok_off;  // first global token of the request
+  int32_t len;      // request length
+  int32_t row0;     // first row of the q-tile, request-local
+  int32_t head;     // -1: the slot has no work
+  int32_t e0;       // first CSR entry of the slot's range
+  int32_t n;        // CSR entries in the range
+  int32_t req;      // request
+  int32_t part;     // partial-result index of a split chunk, -1 for a whole item
+  int32_t w0, w1;   // CSR words e0 and e0 + 1 (w1 = w0 when n < 2; both 0 when n == 0)
+  int32_t pad[2];
+};
+static_assert(sizeof(ItemRec) == 48, "ItemRec layout");
+
 // An item split into parts [part0, part0 + nparts).
 struct SplitEntry {
   int32_t item, part0, nparts, pad;
@@ -111,6 +131,7 @@ struct PlanDev {
                            // [G] offset in ilv of the block's table: K (largest count),
                            // then C(k) = sum over its groups of min(count, k), k = 0..K
   WorkEntry* work;         // [slots + kSplitTarget] (candidates-only plans)
+  ItemRec* irec;           // [slots + kSplitTarget] record of every forward launch slot
   SplitEntry* splits;      // [kSplitTarget]
   int32_t* act_slots;      // [kSplitTarget / 2] active schedule slots, arrival order
   PlanTotals* totals;
@@ -149,7 +170,7 @@ struct rk_plan {
       off_tile_class, off_qt_nnz, off_qt_pairs, off_qt_full, off_qtile_ptr, off_ktile_idx, off_ktile_word, off_qorder,
       off_sched, off_work, off_splits, off_act, off_totals, host_blob_bytes, total_bytes,
       off_kt_req, off_kgroups, off_kqueue_start, off_kt_nnz, off_kt_ptr, off_qtile_word,
-      off_korder, off_ksched, off_ilv, off_kilv, off_group_of;
+      off_korder, off_ksched, off_ilv, off_kilv, off_group_of, off_irec;
   rk::PlanDev dev;
   // host copy of the first host_blob_bytes of the workspace (kept alive
   // for the asynchronous upload)
