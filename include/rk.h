@@ -276,11 +276,14 @@ typedef struct rk_plan_totals {
 
 /*
  * Attention arguments.  Q, K, V, O are [token, head, d] views with d
- * contiguous and the given element strides.  dtype RK_BF16: bf16 inputs
- * and output, fp32 accumulation and softmax, bf16 MFMA for d_head == 64
- * (needs 16-byte aligned base pointers and strides that are multiples of
- * 8); d_head in {32, 64, 128} otherwise.  dtype RK_F32: fp32 throughout,
- * d_head in {32, 64, 128}.
+ * contiguous and the given element strides.  d_head is any multiple of 8
+ * from 8 to 128 (CADET's 88, for example): the kernels run at the next
+ * instance width (64 or 128 on the matrix cores, 32, 64 or 128 on the plain
+ * kernel) with zero columns that never touch the tensors.  dtype RK_BF16:
+ * bf16 inputs and output, fp32 accumulation and softmax, bf16 MFMA (needs
+ * 16-byte aligned base pointers and strides that are multiples of 8;
+ * RK_ATTN_REFERENCE_KERNEL selects the plain kernel).  dtype RK_F32: fp32
+ * throughout on the plain kernel.
  *   lse       : optional float [num_heads][total_tokens], natural-log
  *               log-sum-exp of the scaled scores; -inf for empty rows.
  *   scale     : score scale; 0 selects 1/sqrt(d_head).

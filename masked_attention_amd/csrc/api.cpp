@@ -597,7 +597,9 @@ rk_status check_attn(const rk_plan* p, const rk_attn_args* a) {
   if (!p || !a || a->struct_size < sizeof(rk_attn_args)) return RK_ERR_INVALID_ARG;
   if (!valid_dtype(a->dtype)) return RK_ERR_INVALID_ARG;
   if (a->num_heads != p->H) return RK_ERR_INVALID_ARG;
-  if (a->d_head != 32 && a->d_head != 64 && a->d_head != 128) return RK_ERR_UNSUPPORTED;
+  // any multiple of 8 up to 128 (the kernels pad to an instance width);
+  // QK Norm keeps to 32, 64 and 128 (check_norm)
+  if (a->d_head < 8 || a->d_head > 128 || (a->d_head % 8) != 0) return RK_ERR_UNSUPPORTED;
   if (a->flags & ~(RK_ATTN_REFERENCE_KERNEL | RK_ATTN_K_PREROTATED)) return RK_ERR_INVALID_ARG;
   if ((a->flags & RK_ATTN_K_PREROTATED) && !a->rope && !a->qk_norm) return RK_ERR_INVALID_ARG;
   if (a->qk_norm) {
@@ -619,10 +621,15 @@ rk_status check_attn(const rk_plan* p, const rk_attn_args* a) {
 }
 
 bool mfma_eligible(const rk_attn_args* a) {
-  if (a->dtype != RK_BF16 || (a->d_head != 64 && a->d_head != 128) ||
-      (a->flags & RK_ATTN_REFERENCE_KERNEL))
-    return false;
-  return true;
+  return a->dtype == RK_BF16 && !(a->flags & RK_ATTN_REFERENCE_KERNEL);
+}
+
+// Instance width of the forward kernel that runs: d_head rounded up to 64
+// or 128 (MFMA) or to 32, 64 or 128 (plain kernel).
+int kernel_dp(const rk_attn_args* a) {
+  const int d = a->d_head;
+  if (mfma_eligible(a)) return d <= 64 ? 64 : 128;
+  return d <= 32 ? 32 : d <= 64 ? 64 : 128;
 }
 
 bool mfma_aligned(const rk_attn_args* a, bool k_in_workspace) {
@@ -647,7 +654,7 @@ size_t attn_k_bytes(const rk_plan* p, const rk_attn_args* a) {
 
 size_t attn_part_bytes(const rk_plan* p, const rk_attn_args* a) {
   if (p->grid <= p->slots) return 0;
-  return align_up((size_t)rk::kMaxParts * rk::kTileQ * (size_t)(a->d_head + 2) * sizeof(float));
+  return align_up((size_t)rk::kMaxParts * rk::kTileQ * (size_t)(kernel_dp(a) + 2) * sizeof(float));
 }
 
 size_t attn_ws_bytes(const rk_plan* p, const rk_attn_args* a) {
@@ -698,6 +705,7 @@ rk_status rk_masked_attn_fwd(const rk_plan* p, const rk_attn_args* a, void* stre
   L.scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->d_head);
   L.H = a->num_heads;
   L.d = a->d_head;
+  L.dp = kernel_dp(a);
   L.T = p->T;
   L.ts = p->timestamps_dev;
   L.plan_err = &p->dev.totals->errors;

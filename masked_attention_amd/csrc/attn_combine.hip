@@ -94,7 +94,8 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const ReqMeta* req, c
   const float inv = (l > 0.f ? 1.f / l : 0.f) * pz;
   T* O = (T*)A.o + (int64_t)tok * A.o_st + (int64_t)head * A.o_sh + c0;
 #pragma unroll
-  for (int c = 0; c < kQ; ++c) st(O + c, acc[c] * inv);
+  for (int c = 0; c < kQ; ++c)
+    if (c0 + c < A.d) st(O + c, acc[c] * inv);  // columns past d_head are padding
   if (A.lse && c0 == 0)
     A.lse[(int64_t)head * A.T + tok] = (l > 0.f ? M * to_nat + logf(l) : -INFINITY) * pz;
 }
@@ -113,14 +114,16 @@ hipError_t launch(const rk_plan* p, const AttnLaunch& a, float to_log2, float to
 hipError_t launch_attn_combine(const rk_plan* p, const AttnLaunch& a, rk_dtype dt, float to_log2,
                                float to_nat, hipStream_t s) {
   if (p->grid <= p->slots || a.part == nullptr) return hipSuccess;
+  // the parts have the producing kernel's width dp
+  if (a.d > a.dp) return hipErrorInvalidValue;
   if (dt == RK_F32) {
-    if (a.d == 32) return launch<float, 32>(p, a, to_log2, to_nat, s);
-    if (a.d == 64) return launch<float, 64>(p, a, to_log2, to_nat, s);
-    if (a.d == 128) return launch<float, 128>(p, a, to_log2, to_nat, s);
+    if (a.dp == 32) return launch<float, 32>(p, a, to_log2, to_nat, s);
+    if (a.dp == 64) return launch<float, 64>(p, a, to_log2, to_nat, s);
+    if (a.dp == 128) return launch<float, 128>(p, a, to_log2, to_nat, s);
   } else {
-    if (a.d == 32) return launch<__hip_bfloat16, 32>(p, a, to_log2, to_nat, s);
-    if (a.d == 64) return launch<__hip_bfloat16, 64>(p, a, to_log2, to_nat, s);
-    if (a.d == 128) return launch<__hip_bfloat16, 128>(p, a, to_log2, to_nat, s);
+    if (a.dp == 32) return launch<__hip_bfloat16, 32>(p, a, to_log2, to_nat, s);
+    if (a.dp == 64) return launch<__hip_bfloat16, 64>(p, a, to_log2, to_nat, s);
+    if (a.dp == 128) return launch<__hip_bfloat16, 128>(p, a, to_log2, to_nat, s);
   }
   return hipErrorInvalidValue;
 }

@@ -121,15 +121,17 @@ struct QRaw {
   int2 dsc;   // row descriptor
 };
 
-// Loads without branches: a row past the end of the request reads the
-// request's last token and is zeroed in finish_q (it is never written).
+// A row past the end of the request reads the request's last token and is
+// zeroed in finish_q (it is never written).  Chunks past d_head (a padded
+// instance) are not read and are zero.
 template <int D>
 __device__ __forceinline__ QRaw<D> load_q_raw(const AttnLaunch& A, const int2* row_desc,
-                                              int tokq_c, int head, int hh, bool rope) {
+                                              int tokq_c, int head, int hh, bool rope, int d) {
   QRaw<D> r;
   const unsigned short* Qp = (const unsigned short*)A.q + (int64_t)tokq_c * A.q_st + (int64_t)head * A.q_sh;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) r.v[s] = *(const uint4*)(Qp + 16 * s + 8 * hh);
+  for (int s = 0; s < D / 16; ++s)
+    r.v[s] = 16 * s + 8 * hh < d ? *(const uint4*)(Qp + 16 * s + 8 * hh) : make_uint4(0, 0, 0, 0);
   r.t = rope ? A.ts[tokq_c] : 0;
   r.dsc = row_desc[tokq_c];
   return r;
@@ -156,7 +158,7 @@ __device__ __forceinline__ void finish_q(bf16x8 (&qb)[D / 16], const QRaw<D>& ra
       }
     }
     ss += __shfl_xor(ss, 32, 64);
-    const float rstd = rsqrtf(ss * (1.f / D) + eps);
+    const float rstd = rsqrtf(ss * (1.f / D) + eps);  // QK Norm runs only with d == D
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       float4 g0 = make_float4(1.f, 1.f, 1.f, 1.f), g1 = g0;
@@ -201,7 +203,10 @@ __device__ __forceinline__ void finish_q(bf16x8 (&qb)[D / 16], const QRaw<D>& ra
 // contiguously (lane l at byte 16 l): 512 / D rows of D / 8 chunks (8 rows
 // at d = 64).  Wave w issues copies j = 0 .. D / 32 - 1, piece
 // (D / 32) w + j of both the K and the V tile; the offsets are relative to
-// the tile's first row and do not change.
+// the tile's first row and do not change.  A chunk past d_head (a padded
+// instance) gets an offset past every buffer's range: its copy loads
+// nothing from memory and its LDS slot keeps the zero it was given.
+constexpr unsigned kOutOfRange = 0x80000000u;
 template <int D>
 struct CopyMap {
   unsigned koff[D / 32];
@@ -209,14 +214,17 @@ struct CopyMap {
 };
 
 template <int D>
-__device__ __forceinline__ CopyMap<D> copy_map(int wv, int lane, unsigned kst_b, unsigned vst_b) {
+__device__ __forceinline__ CopyMap<D> copy_map(int wv, int lane, unsigned kst_b, unsigned vst_b,
+                                                int d) {
   CopyMap<D> c;
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
     const int q = (D / 32 * wv + j) * 64 + lane;
     const int r = q / (D / 8), slot = q % (D / 8);
-    c.koff[j] = (unsigned)r * kst_b + 16u * (unsigned)(slot ^ kswz(r));
-    c.voff[j] = (unsigned)r * vst_b + 16u * (unsigned)(slot ^ vswz(r));
+    // lane q writes physical slot q % (D / 8) of row r: logical chunk slot ^ swizzle
+    const int ck = slot ^ kswz(r), cv = slot ^ vswz(r);
+    c.koff[j] = 8 * ck < d ? (unsigned)r * kst_b + 16u * (unsigned)ck : kOutOfRange;
+    c.voff[j] = 8 * cv < d ? (unsigned)r * vst_b + 16u * (unsigned)cv : kOutOfRange;
   }
   return c;
 }
@@ -335,7 +343,7 @@ __device__ __forceinline__ bool row_sees(int kt, bool partial, int lo, int hi, i
 // end read its last row; the tile is then PARTIAL and they are masked.
 template <int D>
 __device__ __forceinline__ void scores_global(f32x16& s0, f32x16& s1, const unsigned short* Kh,
-                                              int64_t k_st, int kt, int L,
+                                              int64_t k_st, int kt, int L, int d,
                                               const bf16x8 (&q)[D / 16], const f32x16& negm,
                                               int li, int hh) {
   const int c0 = kt * kTileK;
@@ -343,8 +351,10 @@ __device__ __forceinline__ void scores_global(f32x16& s0, f32x16& s1, const unsi
   const unsigned short* r1 = Kh + (int64_t)min(c0 + 32 + li, L - 1) * k_st + 8 * hh;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    const bf16x8 k0 = as_bf16x8(*(const uint4*)(r0 + 16 * s));
-    const bf16x8 k1 = as_bf16x8(*(const uint4*)(r1 + 16 * s));
+    // chunks past d_head are zero, as in LDS
+    const bool in = 16 * s + 8 * hh < d;
+    const bf16x8 k0 = as_bf16x8(in ? *(const uint4*)(r0 + 16 * s) : make_uint4(0, 0, 0, 0));
+    const bf16x8 k1 = as_bf16x8(in ? *(const uint4*)(r1 + 16 * s) : make_uint4(0, 0, 0, 0));
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[s], s == 0 ? negm : s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s == 0 ? negm : s1, 0, 0, 0);
   }
@@ -395,7 +405,7 @@ __device__ __forceinline__ void tile_step(OAcc& o, f32x16& negm, float& mref,
                                           int kt,
                                           bool partial, int li, int hh, int lo, int hi, int self,
                                           int row, float mul, const unsigned short* Kh,
-                                          int64_t k_st, int L) {
+                                          int64_t k_st, int L, int d) {
   f32x16 s0, s1;
   scores<D>(s0, s1, kb, q, negm, li, hh);
   if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
@@ -406,7 +416,7 @@ __device__ __forceinline__ void tile_step(OAcc& o, f32x16& negm, float& mref,
       lsum == 0.f && ts < kMinTileSum && row_sees(kt, partial, lo, hi, self, row);
   if (__any(big || tiny)) {
     // the scores are recomputed, so they need not stay live past the packing
-    scores_global<D>(s0, s1, Kh, k_st, kt, L, q, negm, li, hh);
+    scores_global<D>(s0, s1, Kh, k_st, kt, L, d, q, negm, li, hh);
     if (partial) mask_tile(s0, s1, kt, hh, lo, hi, self, row);
     float mx = s0[0];
 #pragma unroll
@@ -489,7 +499,10 @@ constexpr int kThreads = 256;  // 4 waves, 32 query rows each
 // d = 64 keeps three LDS stages (48 KB, three workgroups per CU); d = 128
 // keeps two (64 KB, two workgroups per CU, which is also what its registers
 // allow), so a copy has one step to land instead of two.
-template <bool kPreScaled, bool kNorm, int D>
+//
+// kPad: d_head is below D (a padded instance); the exact instances keep no
+// trace of the padding logic.
+template <bool kPreScaled, bool kNorm, int D, bool kPad>
 __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P, AttnLaunch A) {
   constexpr int kStages = D <= 64 ? 3 : 2;
   constexpr int kTile = tile_elems<D>();
@@ -501,6 +514,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
   __shared__ __attribute__((aligned(1024))) unsigned short V0[kTile], V1[kTile],
       V2[kStages == 3 ? kTile : 8];
 
+  const int dh = kPad ? A.d : D;  // d_head
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -510,11 +524,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
   // (P = 0) adds exactly 0 to O.  No other wave touches these rows, so no
   // barrier.  This comes first, while the only memory accesses in flight
   // are the slot's own record and arguments, so the wait delays nothing.
+  // A padded instance (d_head < D) zeroes K too: its padding columns meet
+  // Q's zeros in the scores.
 #pragma unroll
   for (int j = 0; j < kWc; ++j) {
     *(uint4*)&V0[(kWc * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
     *(uint4*)&V1[(kWc * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
     if (kStages == 3) *(uint4*)&V2[(kWc * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
+    if (kPad) {
+      *(uint4*)&K0[(kWc * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
+      *(uint4*)&K1[(kWc * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
+      if (kStages == 3) *(uint4*)&K2[(kWc * wv + j) * 512 + 8 * lane] = make_uint4(0, 0, 0, 0);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
@@ -536,14 +557,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
   // Q's loads go out first, then the first key tile's copies; Q is rotated
   // while those copies land.
   const QRaw<D> qraw =
-      load_q_raw<D>(A, P.row_desc, ir.tok_off + min(row, L - 1), head, hh, kPreScaled);
+      load_q_raw<D>(A, P.row_desc, ir.tok_off + min(row, L - 1), head, hh, kPreScaled, dh);
   const int64_t anchor = kPreScaled ? ldc(A.anchors, ir.req) : 0;
 
   const char* Kb = (const char*)((const unsigned short*)A.k + (int64_t)ir.tok_off * A.k_st + (int64_t)head * A.k_sh);
   const char* Vb = (const char*)((const unsigned short*)A.v + (int64_t)ir.tok_off * A.v_st + (int64_t)head * A.v_sh);
   // row strides in bytes (32-bit per-lane offsets: the host limits strides)
   const unsigned kst_b = (unsigned)A.k_st * 2u, vst_b = (unsigned)A.v_st * 2u;
-  const CopyMap<D> cm = copy_map<D>(wv, lane, kst_b, vst_b);
+  const CopyMap<D> cm = copy_map<D>(wv, lane, kst_b, vst_b, dh);
   OAcc o;
   f32x16 negm;
 #pragma unroll
@@ -586,7 +607,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
         const int w_nn = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
         tile_copy<D>(K2, V2, cm, Kb, Vb, kst_b, vst_b, w_nn & 0x7fffffff, L, wv);
         tile_step<kPreScaled, D>(o, negm, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0,
-                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L, dh);
         step_barrier();
         w_cur = w_nxt;
         w_nxt = w_nn;
@@ -595,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
         const int w_nn = ldc(P.ktile_word, e0 + min(it + 3, n - 1));
         tile_copy<D>(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_nn & 0x7fffffff, L, wv);
         tile_step<kPreScaled, D>(o, negm, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0,
-                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L, dh);
         step_barrier();
         w_cur = w_nxt;
         w_nxt = w_nn;
@@ -604,7 +625,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
         const int w_nn = ldc(P.ktile_word, e0 + min(it + 4, n - 1));
         tile_copy<D>(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_nn & 0x7fffffff, L, wv);
         tile_step<kPreScaled, D>(o, negm, mref, lsum, K2, V2, q, w_cur & 0x7fffffff, w_cur < 0,
-                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L, dh);
         step_barrier();
         w_cur = w_nxt;
         w_nxt = w_nn;
@@ -615,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
       {
         tile_copy<D>(K1, V1, cm, Kb, Vb, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
         tile_step<kPreScaled, D>(o, negm, mref, lsum, K0, V0, q, w_cur & 0x7fffffff, w_cur < 0,
-                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L, dh);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         w_cur = w_nxt;
@@ -624,7 +645,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
       if (it + 1 < n) {
         tile_copy<D>(K0, V0, cm, Kb, Vb, kst_b, vst_b, w_nxt & 0x7fffffff, L, wv);
         tile_step<kPreScaled, D>(o, negm, mref, lsum, K1, V1, q, w_cur & 0x7fffffff, w_cur < 0,
-                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L);
+                                 li, hh, lo, hi, self, row, sl2, Kh, A.k_st, L, dh);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         w_cur = w_nxt;
@@ -665,8 +686,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = 32 * mb + 8 * g + 4 * hh;
-      *(uint2*)(Op + d) = make_uint2(pack_bf16x2(ob[4 * g] * inv, ob[4 * g + 1] * inv),
-                                     pack_bf16x2(ob[4 * g + 2] * inv, ob[4 * g + 3] * inv));
+      if (d < dh)  // columns past d_head are padding
+        *(uint2*)(Op + d) = make_uint2(pack_bf16x2(ob[4 * g] * inv, ob[4 * g + 1] * inv),
+                                       pack_bf16x2(ob[4 * g + 2] * inv, ob[4 * g + 3] * inv));
     }
   }
   if (A.lse && hh == 0)
@@ -675,15 +697,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_bf16_kernel(PlanView P,
                     : -INFINITY) * pz;
 }
 
-template <int D>
+template <int D, bool kPad>
 hipError_t launch_d(const PlanView& P, const AttnLaunch& a, dim3 grid, hipStream_t s) {
-  if (a.rope_q && a.norm_q)
-    hipLaunchKernelGGL((attn_mfma_bf16_kernel<true, true, D>), grid, dim3(kThreads), 0, s, P, a);
+  // QK Norm runs only at the exact widths
+  if (a.rope_q && a.norm_q && !kPad)
+    hipLaunchKernelGGL((attn_mfma_bf16_kernel<true, true, D, false>), grid, dim3(kThreads), 0, s,
+                       P, a);
+  else if (a.norm_q)
+    return hipErrorInvalidValue;
   else if (a.rope_q)
-    hipLaunchKernelGGL((attn_mfma_bf16_kernel<true, false, D>), grid, dim3(kThreads), 0, s, P, a);
+    hipLaunchKernelGGL((attn_mfma_bf16_kernel<true, false, D, kPad>), grid, dim3(kThreads), 0, s,
+                       P, a);
   else
-    hipLaunchKernelGGL((attn_mfma_bf16_kernel<false, false, D>), grid, dim3(kThreads), 0, s, P,
-                       a);
+    hipLaunchKernelGGL((attn_mfma_bf16_kernel<false, false, D, kPad>), grid, dim3(kThreads), 0, s,
+                       P, a);
   return hipGetLastError();
 }
 
@@ -693,8 +720,12 @@ hipError_t launch_attn_mfma_bf16(const rk_plan* p, const AttnLaunch& a, hipStrea
   if (p->slots == 0) return hipSuccess;
   PlanView P{p->dev.irec, p->dev.row_desc, p->dev.ktile_word};
   const dim3 grid((unsigned)p->grid);
-  if (a.d == 128) return launch_d<128>(P, a, grid, s);
-  return launch_d<64>(P, a, grid, s);
+  if (a.d > a.dp) return hipErrorInvalidValue;
+  if (a.dp == 128) return a.d == 128 ? launch_d<128, false>(P, a, grid, s)
+                                      : launch_d<128, true>(P, a, grid, s);
+  if (a.dp == 64) return a.d == 64 ? launch_d<64, false>(P, a, grid, s)
+                                   : launch_d<64, true>(P, a, grid, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace rk

@@ -5,7 +5,9 @@
 // thread computes its 64 scores, applies the per-element mask on PARTIAL
 // tiles only, and keeps an fp32 online softmax (running max m, sum l) and
 // output accumulator.  Serves the fp32 path (exact to fp32 rounding), bf16
-// with d_head other than 64, and a cross-check of the MFMA kernel.
+// with d_head other than 64, and a cross-check of the MFMA kernel.  The
+// instance width D is d_head rounded up to 32, 64 or 128; columns past
+// d_head are zero and never touch memory.
 //
 // Visibility of key c for query row p (request-local): c in [lo, hi), or
 // c == p when the row is a candidate (bit 31 of hi), from the plan's row
@@ -71,15 +73,16 @@ __global__ __launch_bounds__(128) void attn_ref_kernel(PlanView P, AttnLaunch A)
   const T* V = (const T*)A.v;
   float q[D];
 #pragma unroll
-  for (int c = 0; c < D; ++c) q[c] = valid ? ld(Q + (int64_t)tok * A.q_st + (int64_t)head * A.q_sh + c) : 0.f;
+  for (int c = 0; c < D; ++c)
+    q[c] = valid && c < A.d ? ld(Q + (int64_t)tok * A.q_st + (int64_t)head * A.q_sh + c) : 0.f;
   if (A.norm_q && valid) {
     // QK Norm before the rotation
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < D; ++c) ss = fmaf(q[c], q[c], ss);
-    const float rstd = rsqrtf(ss / (float)D + A.eps);
+    const float rstd = rsqrtf(ss / (float)A.d + A.eps);
 #pragma unroll
-    for (int c = 0; c < D; ++c) q[c] *= rstd * (A.gamma_q ? A.gamma_q[c] : 1.f);
+    for (int c = 0; c < D; ++c) q[c] *= rstd * (A.gamma_q && c < A.d ? A.gamma_q[c] : 1.f);
   }
   if (A.rope_q && valid) {
     const int64_t dt = A.ts[tok] - A.anchors[P.qt_req[qg]];
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(128) void attn_ref_kernel(PlanView P, AttnLaunch A)
     for (int x = t; x < kTileK * D; x += blockDim.x) {
       const int j = x / D, c = x - j * D;
       const int key = kt * kTileK + j;
-      const bool in = key < L;
+      const bool in = key < L && c < A.d;
       const int64_t kk = (int64_t)(m.tok_off + key);
       Ks[j][c] = in ? ld(K + kk * A.k_st + (int64_t)head * A.k_sh + c) : 0.f;
       Vs[j][c] = in ? ld(V + kk * A.v_st + (int64_t)head * A.v_sh + c) : 0.f;
@@ -167,7 +170,8 @@ __global__ __launch_bounds__(128) void attn_ref_kernel(PlanView P, AttnLaunch A)
   const float pz = plan_poison(A.plan_err);
   const float inv = (lsum > 0.f ? 1.f / lsum : 0.f) * pz;
 #pragma unroll
-  for (int c = 0; c < D; ++c) st(O + (int64_t)tok * A.o_st + (int64_t)head * A.o_sh + c, acc[c] * inv);
+  for (int c = 0; c < D; ++c)
+    if (c < A.d) st(O + (int64_t)tok * A.o_st + (int64_t)head * A.o_sh + c, acc[c] * inv);
   if (A.lse) A.lse[(int64_t)head * A.T + tok] = (lsum > 0.f ? mrow + logf(lsum) : -INFINITY) * pz;
 }
 
@@ -184,14 +188,15 @@ hipError_t launch_ref(const rk_plan* p, const AttnLaunch& a, hipStream_t s) {
 
 hipError_t launch_attn_reference(const rk_plan* p, const AttnLaunch& a, rk_dtype dt, hipStream_t s) {
   if (p->slots == 0) return hipSuccess;
+  if (a.d > a.dp) return hipErrorInvalidValue;
   if (dt == RK_F32) {
-    if (a.d == 32) return launch_ref<float, 32>(p, a, s);
-    if (a.d == 64) return launch_ref<float, 64>(p, a, s);
-    if (a.d == 128) return launch_ref<float, 128>(p, a, s);
+    if (a.dp == 32) return launch_ref<float, 32>(p, a, s);
+    if (a.dp == 64) return launch_ref<float, 64>(p, a, s);
+    if (a.dp == 128) return launch_ref<float, 128>(p, a, s);
   } else {
-    if (a.d == 32) return launch_ref<__hip_bfloat16, 32>(p, a, s);
-    if (a.d == 64) return launch_ref<__hip_bfloat16, 64>(p, a, s);
-    if (a.d == 128) return launch_ref<__hip_bfloat16, 128>(p, a, s);
+    if (a.dp == 32) return launch_ref<__hip_bfloat16, 32>(p, a, s);
+    if (a.dp == 64) return launch_ref<__hip_bfloat16, 64>(p, a, s);
+    if (a.dp == 128) return launch_ref<__hip_bfloat16, 128>(p, a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -215,6 +215,9 @@ struct AttnLaunch {
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
   float scale;
   int H, d, T;
+  int dp;                   // the kernels' tile width: d rounded up to an instance (32, 64
+                            // or 128); columns d .. dp - 1 are zero in registers and LDS,
+                            // never read from or written to the tensors
   bool rope_q;              // transform Q while staging: rotate by `tab` (all zero
                             // for no rotation), fold the scale in (K is ready)
   bool norm_q;              // RMSNorm Q before the rotation (QK Norm)

@@ -547,6 +547,33 @@ def test_attention_tm20k_every_item(rk):
         _say(f"[gpu] workload 5 head {h}: {toks.shape[0]} rows match")
 
 
+@pytest.mark.parametrize("d", [8, 40, 88, 120])
+def test_attention_padded_d_head(rk, d):
+    """d_head that is not an instance width (CADET's 88 among them) runs at
+    the next width with zero columns: bf16 on the matrix cores (64 or 128)
+    and on the plain kernel, fp32 on the plain kernel, each against the
+    oracle.  O is a strided view whose head rows are followed by 8 sentinel
+    columns that must stay untouched."""
+    rng = np.random.default_rng(880 + d)
+    reqs = random_layout(rng, 4, 500)
+    for dtype, reference in (("bf16", False), ("bf16", True), ("f32", False)):
+        wl = make_custom(reqs, heads=2, d_head=d, dtype=dtype, delay=3600, seed=d,
+                         name=f"padded-d{d}")
+        _say(f"[gpu] padded d={d} {dtype} reference={reference}")
+        batch, plan = _plan(rk, wl)
+        q, k, v = _tensors(wl)
+        T, H = wl.total_tokens, wl.heads
+        big = torch.full((T, H, d + 8), float("nan"), dtype=q.dtype, device="cuda")
+        o, lse = rk.rk_masked_attn_fwd(plan, q, k, v, out=big[:, :, :d], rope=_rope(wl),
+                                       reference=reference, want_lse=True)
+        torch.cuda.synchronize()
+        assert bool(torch.isnan(big[:, :, d:].float()).all()), "padding columns written"
+        ref, ref_lse = _oracle_full(wl)
+        _check(wl, o.float().cpu().numpy().astype(np.float64), ref,
+               lse.cpu().numpy().astype(np.float64), ref_lse)
+        plan.close()
+
+
 def test_attention_d128_every_item(rk):
     """bf16 with d_head = 128 (the MFMA kernel's two-stage form): four heads
     over requests of 1,500 to 6,000 history tokens with realtime events and

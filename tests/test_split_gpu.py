@@ -155,6 +155,8 @@ CASES = [
     ("bf16", 128, True, False),   # MFMA at d_head 128 (two-stage form)
     ("bf16", 128, False, False),
     ("bf16", 128, True, True),    # plain kernel at d_head 128
+    ("bf16", 88, True, False),    # padded instances: MFMA at 128, plain at 64
+    ("f32", 40, True, False),
 ]
 
 
