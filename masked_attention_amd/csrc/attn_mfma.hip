@@ -99,14 +99,21 @@ __device__ __forceinline__ T ldc(const T* p, int64_t i) {
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// LDS tiles hold 64 rows of 128 bytes (eight 16-byte slots), unpadded.
+// LDS tiles hold 64 rows of 2 D bytes (D / 8 sixteen-byte slots), unpadded.
 // Logical 16-byte chunk c of row r sits in slot c ^ kswz(r) for K and
-// c ^ vswz(r) for V, so that
-//  - the ds_read_b128 of 8 consecutive K rows at one chunk hits 8 distinct
-//    slots, and
+// c ^ vswz(r) for V.  gfx950's LDS serves a ds_read_b128 sixteen lanes at a
+// time over 64 four-byte banks (256 bytes), so
+//  - at D = 64 the 16 rows a lane group reads at one chunk (two rows per
+//    256-byte bank line) must take 8 distinct slots among the even rows and
+//    among the odd rows: kswz(r) = (r / 2) mod 8 (r mod 8 would put rows r
+//    and r + 8 on the same banks: a two-way conflict the LDS counters
+//    showed on every K read);
+//  - at D = 128 a row fills the bank line, so the 16 rows take 16 distinct
+//    slots: kswz(r) = r mod 16;
 //  - a ds_read_b64_tr_b16 group (4 consecutive V rows starting at a
-//    multiple of 4, 32 contiguous bytes each) covers all 32 banks once.
-__device__ __forceinline__ int kswz(int r) { return r & 7; }
+//    multiple of 4, 2 chunks each) takes 8 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return D == 64 ? (r >> 1) & 7 : r & 15; }
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
 
 // Q fragment: lane holds Q[row][16 s + 8 hh .. +7] * qmul, s = 0..3,
@@ -222,7 +229,7 @@ __device__ __forceinline__ CopyMap<D> copy_map(int wv, int lane, unsigned kst_b,
     const int q = (D / 32 * wv + j) * 64 + lane;
     const int r = q / (D / 8), slot = q % (D / 8);
     // lane q writes physical slot q % (D / 8) of row r: logical chunk slot ^ swizzle
-    const int ck = slot ^ kswz(r), cv = slot ^ vswz(r);
+    const int ck = slot ^ kswz<D>(r), cv = slot ^ vswz(r);
     c.koff[j] = 8 * ck < d ? (unsigned)r * kst_b + 16u * (unsigned)ck : kOutOfRange;
     c.voff[j] = 8 * cv < d ? (unsigned)r * vst_b + 16u * (unsigned)cv : kOutOfRange;
   }
@@ -293,8 +300,8 @@ __device__ __forceinline__ void scores(f32x16& s0, f32x16& s1, const unsigned sh
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     const int cc = 2 * s + hh;  // logical chunk: d = 16 s + 8 hh .. +7
-    const bf16x8 k0 = as_bf16x8(*(const uint4*)&kb[li * D + 8 * (cc ^ kswz(li))]);
-    const bf16x8 k1 = as_bf16x8(*(const uint4*)&kb[(32 + li) * D + 8 * (cc ^ kswz(32 + li))]);
+    const bf16x8 k0 = as_bf16x8(*(const uint4*)&kb[li * D + 8 * (cc ^ kswz<D>(li))]);
+    const bf16x8 k1 = as_bf16x8(*(const uint4*)&kb[(32 + li) * D + 8 * (cc ^ kswz<D>(32 + li))]);
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[s], s == 0 ? c : s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s == 0 ? c : s1, 0, 0, 0);
   }

@@ -46,9 +46,12 @@ struct PwView {
 };
 
 // LDS K / V tiles: 64 rows of 128 bytes, 16-byte chunk c of row r in slot
-// c ^ kswz(r) (K: row reads of 8 consecutive rows hit 8 slots) or
-// c ^ vswz(r) (V: transposing reads of 4 consecutive rows cover 32 banks).
-__device__ __forceinline__ int kswz(int r) { return r & 7; }
+// c ^ kswz(r) (K) or c ^ vswz(r) (V).  gfx950's LDS has 64 four-byte banks,
+// two rows per bank line, and serves a K row read 16 lanes (rows) at a
+// time: even and odd rows each need 8 distinct slots, kswz(r) = (r / 2)
+// mod 8.  A V transposing read (4 consecutive rows from a multiple of 4,
+// 4 chunks over 32 lanes) takes 16 distinct bank groups with vswz.
+__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
 
 // floor(log2(1 + |dt|)) capped at nt - 1
