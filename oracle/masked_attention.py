@@ -44,6 +44,14 @@ the design notes of the repository as well):
 * real-time to real-time is p_j <= p_i and t_j <= t_i; target to real-time is
   t_j < t_i ("before");
 * a row with no visible key outputs 0 and has log-sum-exp -inf.
+* SORT section 3.2.2 (query pruning) names linear, exponential and pooling
+  strategies whose formulas did not survive on the page: the exponential
+  schedule is read as N^l = min(L~, max(N_min, Round(L~ * decay^(l - 1))))
+  and pooling as the pruned history tokens of a request averaged into one
+  token placed where they were and dated as their newest member.  The pins
+  of these two check the oracle against that reading (closed forms,
+  conservation of the history total, brute force); the reading itself has
+  no printed formula to be pinned to.
 """
 
 from __future__ import annotations
@@ -702,6 +710,66 @@ def prune_history(req_offsets, seg_kind, timestamps, x, *, l_tilde, n_min: int, 
     sel = np.asarray(sel, np.int64)
     return (np.asarray(offs, np.int32), seg_kind[sel].astype(np.uint8),
             timestamps[sel].astype(np.int64), x[sel])
+
+
+def pruned_history_length_exp(l_tilde: int, n_min: int, decay: float, layer: int) -> int:
+    """SORT's exponential query-pruning schedule (section 3.2.2, reading in
+    the header): L~ * decay^(layer - 1) rounded half away from zero, at least
+    N_min, at most L~."""
+    val = l_tilde * decay ** (layer - 1)
+    rnd = math.floor(abs(val) + 0.5) * (1 if val >= 0 else -1)
+    return min(l_tilde, max(n_min, rnd))
+
+
+def prune_history_keep(req_offsets, seg_kind, timestamps, x, *, keep):
+    """Pruning to given lengths (any schedule, SORT section 3.2.2 without
+    pooling): per request r, the last keep[r] HISTORY tokens and every
+    PROFILE, REALTIME and CANDIDATE token, in their order.  x: [T, ...].
+    Returns (req_offsets, seg_kind, timestamps, y)."""
+    x = np.asarray(x, np.float64)
+    offs, sel = [0], []
+    for r in range(req_offsets.shape[0] - 1):
+        a, b = int(req_offsets[r]), int(req_offsets[r + 1])
+        hist = [j for j in range(a, b) if seg_kind[j] == HISTORY]
+        drop = set(hist[:max(0, len(hist) - int(keep[r]))])
+        kept = [j for j in range(a, b) if j not in drop]
+        sel += kept
+        offs.append(offs[-1] + len(kept))
+    sel = np.asarray(sel, np.int64)
+    return (np.asarray(offs, np.int32), seg_kind[sel].astype(np.uint8),
+            timestamps[sel].astype(np.int64), x[sel])
+
+
+def prune_history_pooled(req_offsets, seg_kind, timestamps, x, *, keep):
+    """SORT's pooled query pruning (section 3.2.2, reading in the header):
+    per request r, the history tokens beyond the last keep[r] are replaced by
+    their mean, one HISTORY token placed where they were and dated as the
+    newest of them; every other token is unchanged.  keep: [R] kept history
+    lengths (from either schedule).  x: [T, ...].
+    Returns (req_offsets, seg_kind, timestamps, y)."""
+    x = np.asarray(x, np.float64)
+    offs, kinds, times, rows = [0], [], [], []
+    for r in range(req_offsets.shape[0] - 1):
+        a, b = int(req_offsets[r]), int(req_offsets[r + 1])
+        hist = [j for j in range(a, b) if seg_kind[j] == HISTORY]
+        dropped = hist[:max(0, len(hist) - int(keep[r]))]
+        n = 0
+        for j in range(a, b):
+            if j in dropped:
+                if j == dropped[0]:
+                    kinds.append(HISTORY)
+                    times.append(int(timestamps[dropped[-1]]))
+                    rows.append(x[dropped].mean(axis=0))
+                    n += 1
+                continue
+            kinds.append(int(seg_kind[j]))
+            times.append(int(timestamps[j]))
+            rows.append(x[j])
+            n += 1
+        offs.append(offs[-1] + n)
+    y = np.stack(rows) if rows else np.zeros((0,) + x.shape[1:])
+    return (np.asarray(offs, np.int32), np.asarray(kinds, np.uint8),
+            np.asarray(times, np.int64), y)
 
 
 # ---------------------------------------------------------------------------
