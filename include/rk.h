@@ -19,7 +19,10 @@
  *                       HSTU's pointwise (SiLU) attention over the same plan;
  *   rk_compress_layout / rk_prune_layout / rk_gather_sum
  *                       LazFormer's history compression and per-layer
- *                       history pruning, before and between layers.
+ *                       history pruning, before and between layers;
+ *   rk_pruned_history_length_ex / rk_prune_layout_ex / rk_gather_mean
+ *                       SORT's query pruning: exponential schedule and the
+ *                       pooled form.
  *
  * Sources (titles and sections of the pages this library follows):
  *  - CADET: Context-Conditioned Ads CTR Prediction With a Decoder-Only
@@ -660,6 +663,60 @@ rk_status rk_prune_layout(const rk_host_layout* in, const int32_t* l_tilde, int3
 rk_status rk_gather_sum(const int32_t* ranges, int32_t n_out, int32_t n_in, const void* x,
                         int64_t x_stride, void* y, int64_t y_stride, int32_t width,
                         rk_dtype dtype, void* stream);
+
+/* ---- SORT query pruning (section 3.2.2) -------------------------------
+ * The page prunes the user side (history and profile; candidates are never
+ * pruned) layer by layer with three strategies, linear, exponential and
+ * pooling, whose formulas did not survive on the page.  Readings taken
+ * (the plainest the text supports; none can be checked against a printed
+ * formula):
+ *   linear      : LazFormer eq. 22 (rk_pruned_history_length), the same
+ *                 even-step shrink;
+ *   exponential : N^l = min(l_tilde, max(n_min, Round(l_tilde * decay^(l -
+ *                 1)))), Round taking halves away from zero, decay in
+ *                 (0, 1] the per-layer factor;
+ *   pooling     : pruning with either schedule in which the pruned history
+ *                 tokens of a request are averaged into one token, placed
+ *                 where they were (before the kept history) and dated as
+ *                 their newest member, so their global content survives.
+ * Only HISTORY tokens are pruned, oldest first (as in rk_prune_layout);
+ * PROFILE, REALTIME and CANDIDATE tokens stay. */
+typedef enum rk_prune_schedule {
+  RK_PRUNE_LINEAR = 0,  /* LazFormer eq. 22 over num_layers */
+  RK_PRUNE_EXP = 1      /* decay^(layer - 1) */
+} rk_prune_schedule;
+
+typedef struct rk_prune_params {
+  uint32_t struct_size;
+  int32_t schedule;    /* rk_prune_schedule */
+  int32_t n_min;       /* floor of the kept history length, >= 0 */
+  int32_t layer;       /* 1-based */
+  int32_t num_layers;  /* RK_PRUNE_LINEAR: >= layer */
+  int32_t pool;        /* nonzero: the pruned tokens become one mean-pooled token */
+  double decay;        /* RK_PRUNE_EXP: in (0, 1] */
+} rk_prune_params;
+
+/* History positions kept at p->layer by p->schedule (pooling aside).
+ * Errors: RK_ERR_INVALID_ARG. */
+rk_status rk_pruned_history_length_ex(int32_t l_tilde, const rk_prune_params* p,
+                                      int32_t* n_out);
+
+/*
+ * Input layout of layer p->layer: per request r, the last
+ * rk_pruned_history_length_ex(l_tilde[r], p) HISTORY tokens of `in` and every
+ * other token, in order; with p->pool, one more HISTORY token where the
+ * pruned ones were, whose range covers them all (move the rows with
+ * rk_gather_mean: a kept token's range is one row, so the mean is the row).
+ * Errors: as rk_compress_layout.
+ */
+rk_status rk_prune_layout_ex(const rk_host_layout* in, const int32_t* l_tilde,
+                             const rk_prune_params* p, rk_layout_out* out);
+
+/* As rk_gather_sum, with each output row divided by its range length (an
+ * empty range gives zeros).  Errors: as rk_gather_sum. */
+rk_status rk_gather_mean(const int32_t* ranges, int32_t n_out, int32_t n_in, const void* x,
+                         int64_t x_stride, void* y, int64_t y_stride, int32_t width,
+                         rk_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

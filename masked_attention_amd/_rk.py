@@ -33,6 +33,8 @@ RK_ATTN_REFERENCE_KERNEL = 0x1
 RK_ATTN_K_PREROTATED = 0x2
 RK_ABI_VERSION = 4
 RK_SPLIT_SLOTS = 768  # extra work-list slots of a candidates-only plan
+RK_PRUNE_LINEAR = 0
+RK_PRUNE_EXP = 1
 
 
 class rk_batch(C.Structure):
@@ -227,6 +229,18 @@ class rk_layout_out(C.Structure):
     ]
 
 
+class rk_prune_params(C.Structure):
+    _fields_ = [
+        ("struct_size", C.c_uint32),
+        ("schedule", C.c_int32),
+        ("n_min", C.c_int32),
+        ("layer", C.c_int32),
+        ("num_layers", C.c_int32),
+        ("pool", C.c_int32),
+        ("decay", C.c_double),
+    ]
+
+
 STRUCTS = {
     "rk_batch": rk_batch,
     "rk_mask_params": rk_mask_params,
@@ -239,6 +253,7 @@ STRUCTS = {
     "rk_pointwise_args": rk_pointwise_args,
     "rk_host_layout": rk_host_layout,
     "rk_layout_out": rk_layout_out,
+    "rk_prune_params": rk_prune_params,
 }
 
 # (name, restype, argtypes) of every exported entry point
@@ -274,6 +289,12 @@ FUNCTIONS = [
                                   C.c_int32, C.POINTER(rk_layout_out)]),
     ("rk_gather_sum", C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int64,
                                 C.c_void_p, C.c_int64, C.c_int32, C.c_int, C.c_void_p]),
+    ("rk_pruned_history_length_ex", C.c_int, [C.c_int32, C.POINTER(rk_prune_params),
+                                              C.POINTER(C.c_int32)]),
+    ("rk_prune_layout_ex", C.c_int, [C.POINTER(rk_host_layout), C.c_void_p,
+                                     C.POINTER(rk_prune_params), C.POINTER(rk_layout_out)]),
+    ("rk_gather_mean", C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int64,
+                                 C.c_void_p, C.c_int64, C.c_int32, C.c_int, C.c_void_p]),
 ]
 
 _lib = None

@@ -511,11 +511,48 @@ def rk_prune_layout(lay: Layout, *, l_tilde, n_min: int, layer: int, num_layers:
                         int(layer), int(num_layers))
 
 
+def prune_params(*, schedule: str = "linear", n_min: int, layer: int, num_layers: int = 1,
+                 decay: float = 1.0, pool: bool = False) -> _rk.rk_prune_params:
+    """SORT query pruning parameters: schedule "linear" (LazFormer eq. 22)
+    or "exp" (decay^(layer - 1)); pool: the pruned history becomes one
+    mean-pooled token."""
+    code = {"linear": _rk.RK_PRUNE_LINEAR, "exp": _rk.RK_PRUNE_EXP}[schedule]
+    return sized(_rk.rk_prune_params, schedule=code, n_min=int(n_min), layer=int(layer),
+                 num_layers=int(num_layers), pool=1 if pool else 0, decay=float(decay))
+
+
+def rk_pruned_history_length_ex(l_tilde: int, **params) -> int:
+    p = prune_params(**params)
+    n = C.c_int32()
+    check(lib().rk_pruned_history_length_ex(int(l_tilde), C.byref(p), C.byref(n)),
+          "rk_pruned_history_length_ex")
+    return int(n.value)
+
+
+def rk_prune_layout_ex(lay: Layout, *, l_tilde, **params) -> Layout:
+    """Layer input layout of SORT's query pruning (linear or exponential
+    schedule, optionally pooled); move rows with rk_gather_mean."""
+    lt = np.ascontiguousarray(l_tilde, dtype=np.int32)
+    p = prune_params(**params)
+    return _layout_call(lib().rk_prune_layout_ex, lay, C.c_void_p(lt.ctypes.data), C.byref(p))
+
+
+def rk_gather_mean(ranges: torch.Tensor, x: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """y[i] = mean of rows ranges[i, 0] .. ranges[i, 1] - 1 of x (zeros for an
+    empty range); arguments as rk_gather_sum."""
+    return _gather(lib().rk_gather_mean, "rk_gather_mean", ranges, x, out, stream)
+
+
 def rk_gather_sum(ranges: torch.Tensor, x: torch.Tensor, *, out: Optional[torch.Tensor] = None,
                   stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """y[i] = sum of rows ranges[i, 0] .. ranges[i, 1] - 1 of x (rows = first
     dimension; the rest of each row contiguous).  ranges: int32 [n, 2] on the
     device."""
+    return _gather(lib().rk_gather_sum, "rk_gather_sum", ranges, x, out, stream)
+
+
+def _gather(fn, name, ranges, x, out, stream):
     if ranges.dtype != torch.int32 or ranges.dim() != 2 or not ranges.is_contiguous():
         raise ValueError("ranges must be a contiguous int32 [n, 2] tensor")
     n_out = ranges.shape[0]
@@ -526,8 +563,8 @@ def rk_gather_sum(ranges: torch.Tensor, x: torch.Tensor, *, out: Optional[torch.
     if out is None:
         out = torch.empty((n_out,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
     y2 = out.reshape(n_out, width)
-    check(lib().rk_gather_sum(C.c_void_p(ranges.data_ptr()), n_out, x2.shape[0],
-                              C.c_void_p(x2.data_ptr()), x2.stride(0) if x2.shape[0] else width,
-                              C.c_void_p(y2.data_ptr()), y2.stride(0) if n_out else width, width,
-                              _dtype_code(x), _stream(stream)), "rk_gather_sum")
+    check(fn(C.c_void_p(ranges.data_ptr()), n_out, x2.shape[0],
+             C.c_void_p(x2.data_ptr()), x2.stride(0) if x2.shape[0] else width,
+             C.c_void_p(y2.data_ptr()), y2.stride(0) if n_out else width, width,
+             _dtype_code(x), _stream(stream)), name)
     return out

@@ -1,6 +1,8 @@
 // Row gather-sum for the LazFormer pre-passes (section 2.3, eq. 16-18 and
 // 22): y[i] = sum of input rows [b_i, e_i) for every output row i.  Group
 // sums (compression) and plain row selection (pruning) are both such ranges.
+// With kMean the sum is divided by the range length (SORT's pooled query
+// pruning: the pruned history rows averaged into one).
 //
 // HBM-bound: every input row is read once and every output row written once.
 // One wave per output row, lanes across the row: 16-byte loads (8 bf16 or 4
@@ -30,7 +32,7 @@ __device__ __forceinline__ void from_f(__hip_bfloat16* p, float v) {
 constexpr int kWaves = 4;  // output rows per 256-thread block
 
 // V elements per lane per access: 16 bytes when vectorised, else 1.
-template <typename T, bool kVec>
+template <typename T, bool kVec, bool kMean>
 __global__ __launch_bounds__(256) void gather_sum_kernel(const int2* __restrict__ ranges,
                                                          int n_out, int n_in,
                                                          const T* __restrict__ x, int64_t xs,
@@ -43,6 +45,7 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const int2* __restrict_
   const int2 rg = ranges[i];
   const int b = min(max(rg.x, 0), n_in);
   const int e = min(max(rg.y, b), n_in);
+  const float scale = kMean && e > b ? 1.f / (float)(e - b) : 1.f;
   for (int c = lane * V; c < width; c += 64 * V) {
     float acc[V];
 #pragma unroll
@@ -63,17 +66,17 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const int2* __restrict_
     if (kVec) {
       T vals[V];
 #pragma unroll
-      for (int v = 0; v < V; ++v) from_f(&vals[v], acc[v]);
+      for (int v = 0; v < V; ++v) from_f(&vals[v], kMean ? acc[v] * scale : acc[v]);
       uint4 u;
       __builtin_memcpy(&u, vals, 16);
       *(uint4*)dst = u;
     } else {
-      from_f(dst, acc[0]);
+      from_f(dst, kMean ? acc[0] * scale : acc[0]);
     }
   }
 }
 
-template <typename T>
+template <typename T, bool kMean>
 hipError_t launch(const int2* ranges, int n_out, int n_in, const void* x, int64_t xs, void* y,
                   int64_t ys, int width, hipStream_t s) {
   const int per = 16 / (int)sizeof(T);
@@ -81,11 +84,11 @@ hipError_t launch(const int2* ranges, int n_out, int n_in, const void* x, int64_
                    xs % per == 0 && ys % per == 0;
   const dim3 grid((unsigned)((n_out + kWaves - 1) / kWaves));
   if (vec)
-    hipLaunchKernelGGL((gather_sum_kernel<T, true>), grid, dim3(256), 0, s, ranges, n_out, n_in,
-                       (const T*)x, xs, (T*)y, ys, width);
+    hipLaunchKernelGGL((gather_sum_kernel<T, true, kMean>), grid, dim3(256), 0, s, ranges, n_out,
+                       n_in, (const T*)x, xs, (T*)y, ys, width);
   else
-    hipLaunchKernelGGL((gather_sum_kernel<T, false>), grid, dim3(256), 0, s, ranges, n_out, n_in,
-                       (const T*)x, xs, (T*)y, ys, width);
+    hipLaunchKernelGGL((gather_sum_kernel<T, false, kMean>), grid, dim3(256), 0, s, ranges, n_out,
+                       n_in, (const T*)x, xs, (T*)y, ys, width);
   return hipGetLastError();
 }
 
@@ -93,10 +96,14 @@ hipError_t launch(const int2* ranges, int n_out, int n_in, const void* x, int64_
 
 hipError_t launch_gather_sum(const int32_t* ranges, int n_out, int n_in, const void* x,
                              int64_t xs, void* y, int64_t ys, int width, rk_dtype dt,
-                             hipStream_t s) {
+                             hipStream_t s, bool mean) {
   if (n_out == 0) return hipSuccess;
-  if (dt == RK_F32) return launch<float>((const int2*)ranges, n_out, n_in, x, xs, y, ys, width, s);
-  return launch<__hip_bfloat16>((const int2*)ranges, n_out, n_in, x, xs, y, ys, width, s);
+  const int2* rg = (const int2*)ranges;
+  if (dt == RK_F32)
+    return mean ? launch<float, true>(rg, n_out, n_in, x, xs, y, ys, width, s)
+                : launch<float, false>(rg, n_out, n_in, x, xs, y, ys, width, s);
+  return mean ? launch<__hip_bfloat16, true>(rg, n_out, n_in, x, xs, y, ys, width, s)
+              : launch<__hip_bfloat16, false>(rg, n_out, n_in, x, xs, y, ys, width, s);
 }
 
 }  // namespace rk

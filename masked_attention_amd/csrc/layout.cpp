@@ -1,7 +1,9 @@
 // LazFormer pre-passes on the host (section 2.3): group-sum compression of
 // long histories (eq. 16-18) and the per-layer history length and pruning of
-// eq. 22.  Each output token is described by a contiguous range of input
-// rows; the rows themselves move on the device (rk_gather_sum).
+// eq. 22; SORT's query pruning (section 3.2.2) with its exponential schedule
+// and its pooled form.  Each output token is described by a contiguous range
+// of input rows; the rows themselves move on the device (rk_gather_sum,
+// rk_gather_mean).
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -67,6 +69,22 @@ rk_status emit(const rk_host_layout* in, rk_layout_out* out, Build build) {
   }
   return RK_OK;
 }
+
+// dv: the dtype argument as the int a C caller passed (read without
+// loading an enum that may hold no enumerator)
+rk_status gather(const int32_t* ranges, int32_t n_out, int32_t n_in, const void* x,
+                 int64_t x_stride, void* y, int64_t y_stride, int32_t width, int dv,
+                 void* stream, bool mean) {
+  if (dv != RK_F32 && dv != RK_BF16) return RK_ERR_INVALID_ARG;
+  if (n_out < 0 || n_in < 0 || width < 0 || x_stride < 0 || y_stride < 0) return RK_ERR_INVALID_ARG;
+  if (n_out == 0 || width == 0) return RK_OK;
+  if (!ranges || !y || (n_in > 0 && !x) || y_stride < width) return RK_ERR_INVALID_ARG;
+  if (n_in > 0 && x_stride < width) return RK_ERR_INVALID_ARG;
+  hipError_t e = rk::launch_gather_sum(ranges, n_out, n_in, x, x_stride, y, y_stride, width,
+                                       (rk_dtype)dv, (hipStream_t)stream, mean);
+  return e == hipSuccess ? RK_OK : RK_ERR_HIP;
+}
+
 
 }  // namespace
 
@@ -147,19 +165,70 @@ rk_status rk_prune_layout(const rk_host_layout* in, const int32_t* l_tilde, int3
   });
 }
 
+rk_status rk_pruned_history_length_ex(int32_t l_tilde, const rk_prune_params* p,
+                                      int32_t* n_out) {
+  if (!p || p->struct_size < sizeof(rk_prune_params) || !n_out) return RK_ERR_INVALID_ARG;
+  if (p->schedule == RK_PRUNE_LINEAR)
+    return rk_pruned_history_length(l_tilde, p->n_min, p->layer, p->num_layers, n_out);
+  if (p->schedule != RK_PRUNE_EXP) return RK_ERR_INVALID_ARG;
+  if (l_tilde < 0 || p->n_min < 0 || p->layer < 1 || !(p->decay > 0.0 && p->decay <= 1.0))
+    return RK_ERR_INVALID_ARG;
+  // l_tilde * decay^(layer - 1), rounded half away from zero, floored at
+  // n_min and capped at l_tilde
+  const double val = (double)l_tilde * std::pow(p->decay, (double)(p->layer - 1));
+  double n = std::floor(val + 0.5);
+  if (n < p->n_min) n = p->n_min;
+  if (n > l_tilde) n = l_tilde;
+  *n_out = (int32_t)n;
+  return RK_OK;
+}
+
+rk_status rk_prune_layout_ex(const rk_host_layout* in, const int32_t* l_tilde,
+                             const rk_prune_params* p, rk_layout_out* out) {
+  rk_status st = check_layout(in);
+  if (st != RK_OK) return st;
+  if ((st = check_out(out, in->num_requests)) != RK_OK) return st;
+  if (!p || p->struct_size < sizeof(rk_prune_params)) return RK_ERR_INVALID_ARG;
+  if (!l_tilde && in->num_requests > 0) return RK_ERR_INVALID_ARG;
+  std::vector<int32_t> keep(in->num_requests);
+  for (int32_t r = 0; r < in->num_requests; ++r)
+    if ((st = rk_pruned_history_length_ex(l_tilde[r], p, &keep[r])) != RK_OK) return st;
+  const int32_t* o = in->req_offsets;
+  const uint8_t* k = in->seg_kind;
+  const int64_t* t = in->timestamps;
+  const bool pool = p->pool != 0;
+  return emit(in, out, [&](int32_t r, std::vector<Tok>& v) {
+    int32_t n_hist = 0;
+    for (int32_t j = o[r]; j < o[r + 1]; ++j) n_hist += k[j] == RK_SEG_HISTORY;
+    const int32_t drop = n_hist - keep[r] > 0 ? n_hist - keep[r] : 0;  // oldest history tokens
+    int32_t seen = 0;
+    for (int32_t j = o[r]; j < o[r + 1]; ++j) {
+      if (k[j] == RK_SEG_HISTORY && seen < drop) {
+        // history is contiguous: the dropped tokens are rows [j, j + drop)
+        // and, pooled, become one token dated as their newest member
+        if (pool && seen == 0) v.push_back({(uint8_t)RK_SEG_HISTORY, t[j + drop - 1], j, j + drop});
+        ++seen;
+        continue;
+      }
+      v.push_back({k[j], t[j], j, j + 1});
+    }
+  });
+}
+
 rk_status rk_gather_sum(const int32_t* ranges, int32_t n_out, int32_t n_in, const void* x,
                         int64_t x_stride, void* y, int64_t y_stride, int32_t width,
                         rk_dtype dtype, void* stream) {
   int dv;
-  std::memcpy(&dv, &dtype, sizeof dv);  // any int a C caller passed
-  if (dv != RK_F32 && dv != RK_BF16) return RK_ERR_INVALID_ARG;
-  if (n_out < 0 || n_in < 0 || width < 0 || x_stride < 0 || y_stride < 0) return RK_ERR_INVALID_ARG;
-  if (n_out == 0 || width == 0) return RK_OK;
-  if (!ranges || !y || (n_in > 0 && !x) || y_stride < width) return RK_ERR_INVALID_ARG;
-  if (n_in > 0 && x_stride < width) return RK_ERR_INVALID_ARG;
-  hipError_t e = rk::launch_gather_sum(ranges, n_out, n_in, x, x_stride, y, y_stride, width,
-                                       (rk_dtype)dv, (hipStream_t)stream);
-  return e == hipSuccess ? RK_OK : RK_ERR_HIP;
+  std::memcpy(&dv, &dtype, sizeof dv);
+  return gather(ranges, n_out, n_in, x, x_stride, y, y_stride, width, dv, stream, false);
+}
+
+rk_status rk_gather_mean(const int32_t* ranges, int32_t n_out, int32_t n_in, const void* x,
+                         int64_t x_stride, void* y, int64_t y_stride, int32_t width,
+                         rk_dtype dtype, void* stream) {
+  int dv;
+  std::memcpy(&dv, &dtype, sizeof dv);
+  return gather(ranges, n_out, n_in, x, x_stride, y, y_stride, width, dv, stream, true);
 }
 
 }  // extern "C"

@@ -264,10 +264,11 @@ hipError_t launch_attn_bwd_reference(const rk_plan* p, const BwdLaunch& a, rk_dt
                                      hipStream_t s);
 hipError_t launch_attn_bwd_mfma_bf16_d64(const rk_plan* p, const BwdLaunch& a, hipStream_t s);
 
-// y[i] = sum of input rows [ranges[2i], ranges[2i+1]) clamped to [0, n_in).
+// y[i] = sum of input rows [ranges[2i], ranges[2i+1]) clamped to [0, n_in),
+// or their mean (mean; 0 for an empty range).
 hipError_t launch_gather_sum(const int32_t* ranges, int n_out, int n_in, const void* x,
                              int64_t xs, void* y, int64_t ys, int width, rk_dtype dt,
-                             hipStream_t s);
+                             hipStream_t s, bool mean);
 
 // HSTU pointwise attention launch description.
 struct PwLaunch {

@@ -249,6 +249,31 @@ static void check_layouts() {
   EXPECT(rk_gather_sum(nullptr, 1, 1, nullptr, 1, nullptr, 1, 1, (rk_dtype)5, nullptr) ==
          RK_ERR_INVALID_ARG);
   EXPECT(rk_gather_sum(nullptr, 0, 0, nullptr, 0, nullptr, 0, 0, RK_F32, nullptr) == RK_OK);
+  // SORT query pruning: exponential schedule, pooled layout
+  rk_prune_params pp;
+  std::memset(&pp, 0, sizeof(pp));
+  pp.struct_size = sizeof(pp);
+  pp.schedule = RK_PRUNE_EXP;
+  pp.n_min = 0;
+  pp.layer = 2;
+  pp.decay = 0.5;
+  EXPECT(rk_pruned_history_length_ex(5, &pp, &m) == RK_OK && m == 3);  // 2.5 rounds away from 0
+  pp.pool = 1;
+  EXPECT(rk_prune_layout_ex(&in, lt.data(), &pp, &out) == RK_OK);
+  // request 0 keeps 3 of 5 history tokens (+1 pooled), request 1 keeps 2 of 3 (+1 pooled)
+  EXPECT(out.total_tokens == 10 && o2[1] == 7 && o2[2] == 10);
+  EXPECT(r2[2] == 1 && r2[3] == 3 && t2[1] == 20);  // pooled rows [1, 3), newest member's time
+  pp.decay = 0.0;
+  EXPECT(rk_pruned_history_length_ex(5, &pp, &m) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_prune_layout_ex(&in, lt.data(), &pp, &out) == RK_ERR_INVALID_ARG);
+  pp.decay = 0.5;
+  pp.schedule = 7;
+  EXPECT(rk_pruned_history_length_ex(5, &pp, &m) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_pruned_history_length_ex(5, nullptr, &m) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_prune_layout_ex(&in, lt.data(), nullptr, &out) == RK_ERR_INVALID_ARG);
+  EXPECT(rk_gather_mean(nullptr, 1, 1, nullptr, 1, nullptr, 1, 1, (rk_dtype)5, nullptr) ==
+         RK_ERR_INVALID_ARG);
+  EXPECT(rk_gather_mean(nullptr, 0, 0, nullptr, 0, nullptr, 0, 0, RK_F32, nullptr) == RK_OK);
 }
 
 int main(int argc, char** argv) {

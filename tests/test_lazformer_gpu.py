@@ -1,5 +1,7 @@
 """GPU parity of the LazFormer pre-passes (section 2.3) through the C ABI.
 
+* rk_gather_mean with the pooled layouts of rk_prune_layout_ex (SORT query
+  pruning, exponential and linear schedules) against the oracle;
 * rk_gather_sum applied with the layouts of rk_compress_layout /
   rk_prune_layout reproduces the oracle's compressed / pruned rows: fp32
   within 1e-5 relative to the row magnitude, bf16 within one bf16 rounding
@@ -89,6 +91,49 @@ def test_gather_sum_clamps_ranges(rk):
     y = rk.rk_gather_sum(rg, x)
     torch.cuda.synchronize()
     assert y.cpu().tolist() == [[2.0, 4.0], [34.0, 36.0], [0.0, 0.0], [6.0, 7.0]]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("width,pad", [(64, 0), (37, 3)])
+def test_gather_mean_pooled_pruning(rk, dtype, width, pad):
+    """SORT's pooled query pruning (section 3.2.2): rk_prune_layout_ex's
+    ranges moved by rk_gather_mean against the oracle's pooled layer input,
+    exponential and linear schedules; padding columns untouched."""
+    rng = np.random.default_rng(900 + width)
+    wl = make_custom(random_layout(rng, 9, 600), heads=1, d_head=2, seed=2, with_qkv=False)
+    x = rng.standard_normal((wl.total_tokens, width)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        x = bf16_round(x)
+    big = torch.zeros((wl.total_tokens, width + pad), dtype=dtype, device="cuda")
+    big[:, :width] = torch.from_numpy(x).to(dtype)
+    xd = big[:, :width]
+    lay = rk.Layout.from_workload(wl)
+    lt = lay.history_lengths()
+    for schedule, layer in (("exp", 2), ("exp", 4), ("linear", 3)):
+        _say(f"[gpu] gather_mean pooled {dtype} width={width} pad={pad} {schedule} layer={layer}")
+        out = rk.rk_prune_layout_ex(lay, l_tilde=lt, schedule=schedule, n_min=16, layer=layer,
+                                    num_layers=4, decay=0.5, pool=True)
+        if schedule == "exp":
+            keep = [oracle.pruned_history_length_exp(int(l), 16, 0.5, layer) for l in lt]
+        else:
+            keep = [oracle.pruned_history_length(int(l), 16, layer, 4) for l in lt]
+        rg = torch.from_numpy(out.ranges.copy()).cuda()
+        yb = torch.full((out.T, width + pad), 7.0, dtype=dtype, device="cuda")
+        rk.rk_gather_mean(rg, xd, out=yb[:, :width])
+        torch.cuda.synchronize()
+        _, _, _, ref = oracle.prune_history_pooled(wl.req_offsets, wl.seg_kind, wl.timestamps,
+                                                   x.astype(np.float64), keep=keep)
+        _close(yb[:, :width].float().cpu().numpy(), ref, dtype)
+        assert torch.all(yb[:, width:] == 7.0)
+
+
+def test_gather_mean_clamps_ranges(rk):
+    x = torch.arange(20, dtype=torch.float32, device="cuda").reshape(10, 2)
+    rg = torch.tensor([[-5, 2], [8, 50], [7, 3], [3, 4]], dtype=torch.int32, device="cuda")
+    y = rk.rk_gather_mean(rg, x)
+    torch.cuda.synchronize()
+    # clamped to [0, 2), [8, 10), empty, [3, 4)
+    assert y.cpu().tolist() == [[1.0, 2.0], [17.0, 18.0], [0.0, 0.0], [6.0, 7.0]]
 
 
 def _lazformer_batch(R, L_hist, n_cand, H, d, seed):
