@@ -453,7 +453,7 @@ __device__ __forceinline__ void tile_step(OAcc& o, f32x16& negm, float& mref,
     }
     mref += sh;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) negm[r] = -mref;
+    for (int r = 0; r < 16; ++r) negm[r] -= sh;
     ts = probs<true, !kPreScaled>(pb, s0, s1, sh, mul);
   }
   lsum += ts;
