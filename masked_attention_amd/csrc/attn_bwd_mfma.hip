@@ -47,13 +47,15 @@
 // transposing LDS reads.
 //
 // LDS tiles hold rows of 128 bytes (eight 16-byte slots), unpadded; logical
-// chunk c of row r sits in slot c ^ swz(r), with m = r / 2 (mod 8) and
-// swz(r) = 4 (m mod 2) + m / 2.  gfx950's LDS has 64 four-byte banks (two
-// rows per bank line) and serves a row read sixteen lanes at a time, so the
-// 16 rows a row read takes at one chunk need 8 distinct slots among the
-// even rows and among the odd ones (swz is a permutation of 0..7 in m); a
-// transposing read (32 lanes: rows 4k .. 4k + 3, four chunks) needs rows
-// 4k and 4k + 2 to differ above bit 0 of swz (they do, by 4).
+// chunk c of row r sits in slot c ^ swz(r), swz(r) = 2 (r & 3) + ((r >> 2) & 1).
+// The transposing reads (rows 4k .. 4k + 3, four chunks over 32 lanes) are
+// free of bank conflicts on gfx950's 64-bank LDS; the row reads (16 rows at
+// one chunk) meet a two-way conflict between rows r and r + 8.  A swizzle
+// free of both needs a 16-row period, which stops rows r and r + 8 of a
+// transposing read from sharing an address register (+1 KB immediate): it
+// took the dq kernel from 166 to 190 VGPRs (3 to 2 waves per SIMD) and the
+// dK/dV kernel to 256 with spills, and measured 0.6 % slower, so this one
+// stays.
 #include "cdna4_common.h"
 
 namespace rk {
@@ -80,7 +82,7 @@ struct BwdPlanView {
   const int32_t* ksched;
 };
 
-__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 // 16-byte chunk c (8 bf16) of row r of an LDS tile
 __device__ __forceinline__ bf16x8 lds_chunk(const unsigned short* t, int r, int c) {
