@@ -31,24 +31,30 @@
 namespace rk {
 namespace {
 
-// number of keys in ts[0, n) with value <= x (ts non-decreasing)
-__device__ __forceinline__ int count_le(const int64_t* __restrict__ ts, int n, int64_t x) {
-  int a = 0, b = n;
+// Number of keys in ts[0, n) (non-decreasing) with value <= x, or < x with
+// kStrict, helped by samples of ts held in LDS: samp[j] = ts[j * step] for
+// j < ceil(n / step) (at most kSamples).  The samples that pass bracket the
+// answer to one step of positions, (p_{k-1}, p_k], searched in memory; with
+// step 1 no memory is read.  On unsorted ts (which the row checks report)
+// the result is still in [0, n].
+constexpr int kSamples = 256;  // one per thread of the block
+template <bool kStrict>
+__device__ __forceinline__ int count_sampled(const int64_t* __restrict__ ts, int n, int64_t x,
+                                             const long long* samp, int step) {
+  if (n <= 0) return 0;
+  const int m = (n + step - 1) / step;
+  int a = 0, b = m;
   while (a < b) {
-    int m = (a + b) >> 1;
-    if (ts[m] <= x) a = m + 1; else b = m;
+    const int mid = (a + b) >> 1;
+    if (kStrict ? samp[mid] < x : samp[mid] <= x) a = mid + 1; else b = mid;
   }
-  return a;
-}
-
-// number of keys in ts[0, n) with value < x (ts non-decreasing)
-__device__ __forceinline__ int count_lt(const int64_t* __restrict__ ts, int n, int64_t x) {
-  int a = 0, b = n;
-  while (a < b) {
-    int m = (a + b) >> 1;
-    if (ts[m] < x) a = m + 1; else b = m;
+  int lo = a == 0 ? 0 : (a - 1) * step + 1;
+  int hi = a == m ? n : a * step;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (kStrict ? ts[mid] < x : ts[mid] <= x) lo = mid + 1; else hi = mid;
   }
-  return a;
+  return lo;
 }
 
 // Sum over the 64 lanes of a wave (integers: order does not matter).
@@ -119,6 +125,8 @@ __device__ void seg_search(const uint8_t* __restrict__ kr, int L, int* lo_s, int
   __syncthreads();
   while (lo_s[0] < hi_s[0] || lo_s[1] < hi_s[1] || lo_s[2] < hi_s[2]) {
     int lo[3], hi[3], step[3], c[3];
+    bool below[3];
+    // the three boundaries' samples are loaded together, then counted
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       lo[k] = lo_s[k];
@@ -126,8 +134,10 @@ __device__ void seg_search(const uint8_t* __restrict__ kr, int L, int* lo_s, int
       const int n = hi[k] - lo[k];  // the boundary lies in [lo, hi]
       step[k] = n > 0 ? (n - 1) / 256 + 1 : 1;
       const int64_t pos = lo[k] + (int64_t)t * step[k];
-      c[k] = __syncthreads_count(n > 0 && pos < hi[k] && kr[pos] <= k);
+      below[k] = n > 0 && pos < hi[k] && kr[pos] <= k;
     }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) c[k] = __syncthreads_count(below[k]);
     if (t < 3) {
       const int k = t;
       if (hi[k] > lo[k]) {
@@ -203,6 +213,7 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
   __shared__ int nnz_s, full_s;
   __shared__ int lim[4];  // lo_max, hi_min, lo_min, hi_max
   __shared__ int lo_s[3], hi_s[3];
+  __shared__ long long samp[3][kSamples];  // PROFILE, HISTORY, REALTIME sample times
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   for (int64_t x = (int64_t)g * blockDim.x + tid; x < slots; x += (int64_t)gridDim.x * blockDim.x) {
@@ -227,6 +238,21 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
     pairs_s = 0; nnz_s = 0; full_s = 0;
     lim[0] = INT_MIN; lim[1] = INT_MAX; lim[2] = INT_MAX; lim[3] = INT_MIN;
   }
+  // Samples of the three time-ordered runs the rows search (profile and
+  // history for the delay cut, real-time for a candidate's events), one
+  // load per thread, so each row's search reads memory for one step of
+  // positions only.
+  const bool cut_static = !bidir && delay > 0;
+  const int n_rt = a_c - a_rt;
+  const int st_p = max(1, (a_h + kSamples - 1) / kSamples);
+  const int st_h = max(1, (a_rt - a_h + kSamples - 1) / kSamples);
+  const int st_r = max(1, (n_rt + kSamples - 1) / kSamples);
+  if (cut_static) {
+    if (tid * st_p < a_h) samp[0][tid] = tr[tid * st_p];
+    if (tid * st_h < a_rt - a_h) samp[1][tid] = tr[a_h + tid * st_h];
+  }
+  if (a_c < L && tid * st_r < n_rt) samp[2][tid] = tr[a_rt + tid * st_r];
+  __syncthreads();
   if (tid < kTileQ) {
     int2 desc = make_int2(0, 0);
     if (tid < nrows) {
@@ -257,8 +283,8 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
             // keys dated at or before the cut: [0, cp) of PROFILE and
             // [a_h, a_h + ch) of HISTORY
             const int64_t cut = ts[i] - delay;
-            const int cp = count_le(tr, a_h, cut);
-            const int ch = count_le(tr + a_h, a_rt - a_h, cut);
+            const int cp = count_sampled<false>(tr, a_h, cut, samp[0], st_p);
+            const int ch = count_sampled<false>(tr + a_h, a_rt - a_h, cut, samp[1], st_h);
             const bool prof_run = min(cp, hi) > lo;
             const bool hist_run = min(a_h + ch, hi) > max(a_h, lo);
             if (cp == a_h) {
@@ -275,7 +301,7 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
       } else if (s == RK_SEG_REALTIME) {
         hi = p + 1;
       } else {
-        hi = a_rt + count_lt(tr + a_rt, a_c - a_rt, ts[i]);
+        hi = a_rt + count_sampled<true>(tr + a_rt, n_rt, ts[i], samp[2], st_r);
         diag = 1;
       }
       if (hi <= lo) { lo = 0; hi = 0; }
