@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -23,6 +24,61 @@ constexpr size_t kAlign = 256;
 constexpr int64_t kInt32Max = 2147483647;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Pinned, fine-grained (coherent) host blocks that carry a plan's host
+// tables to the GPU: the first planner kernel reads them in place and
+// copies them into the workspace, so a plan needs no copy-engine transfer
+// and no wait of the compute queue on one.  The first word of a block is 1
+// while the block is free and 0 while a plan's first kernel may still read
+// it; the planner's second kernel, which starts after the first has ended,
+// sets it back to 1.  Blocks stay allocated until the process ends.  With
+// kMaxBlocks leased at once (plans issued far ahead of the GPU) a plan goes
+// up by an asynchronous copy instead.
+class StagingPool {
+ public:
+  static constexpr size_t kHeader = 256;
+  static constexpr size_t kMinBlock = size_t(64) << 10;
+  static constexpr size_t kMaxBlocks = 64;
+  struct Lease {
+    unsigned char* data = nullptr;
+    unsigned* done = nullptr;
+  };
+  Lease acquire(size_t bytes) {
+    std::lock_guard<std::mutex> lock(mu_);
+    for (const Block& b : blocks_) {
+      if (b.cap - kHeader >= bytes && __atomic_load_n(b.done, __ATOMIC_ACQUIRE) == 1u) {
+        __atomic_store_n(b.done, 0u, __ATOMIC_RELAXED);
+        return {b.base + kHeader, b.done};
+      }
+    }
+    if (blocks_.size() >= kMaxBlocks) return {};
+    size_t cap = kMinBlock;
+    while (cap - kHeader < bytes) cap *= 2;
+    void* mem = nullptr;
+    if (hipHostMalloc(&mem, cap, hipHostMallocCoherent | hipHostMallocPortable) != hipSuccess) {
+      (void)hipGetLastError();
+      return {};
+    }
+    const Block b{static_cast<unsigned char*>(mem), cap, static_cast<unsigned*>(mem)};
+    *b.done = 0u;
+    blocks_.push_back(b);
+    return {b.base + kHeader, b.done};
+  }
+
+ private:
+  struct Block {
+    unsigned char* base;
+    size_t cap;
+    unsigned* done;
+  };
+  std::mutex mu_;
+  std::vector<Block> blocks_;
+};
+
+StagingPool& staging_pool() {
+  static StagingPool* pool = new StagingPool;  // never destroyed: blocks live to process end
+  return *pool;
+}
 
 // Sizes and host-side tables derived from req_offsets_host.
 struct Layout {
@@ -43,7 +99,7 @@ struct Layout {
   size_t off_ilv = 0, off_kilv = 0, off_group_of = 0;
   size_t off_req = 0, off_qt_req = 0, off_groups = 0, off_queue_start = 0, off_totals = 0,
          host_blob = 0, off_row_desc = 0, off_tile_count = 0, off_tile_class = 0, off_qt_nnz = 0,
-         off_qt_pairs = 0, off_qt_full = 0,
+         off_qt_pairs = 0, off_qt_full = 0, off_qt_flags = 0,
          off_qtile_ptr = 0, off_ktile_idx = 0, off_ktile_word = 0, off_qorder = 0, off_sched = 0,
          off_work = 0, off_irec = 0, off_splits = 0, off_act = 0, off_kt_req = 0, off_kgroups = 0,
          off_kqueue_start = 0, off_kt_nnz = 0, off_kt_ptr = 0, off_qtile_word = 0,
@@ -253,6 +309,7 @@ rk_status make_layout(const rk_batch* b, int32_t H, bool with_tables, Layout* L)
   L->off_qt_nnz = take(sizeof(int32_t) * (size_t)nq);
   L->off_qt_pairs = take(sizeof(int64_t) * (size_t)nq);
   L->off_qt_full = take(sizeof(int32_t) * (size_t)nq);
+  L->off_qt_flags = take(sizeof(uint32_t) * (size_t)nq);
   L->off_qtile_ptr = take(sizeof(int32_t) * (size_t)(nq + 1));
   L->off_ktile_idx = take(sizeof(int32_t) * (size_t)nt);
   L->off_ktile_word = take(sizeof(int32_t) * (size_t)nt);
@@ -395,6 +452,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   p->off_qt_nnz = L.off_qt_nnz;
   p->off_qt_pairs = L.off_qt_pairs;
   p->off_qt_full = L.off_qt_full;
+  p->off_qt_flags = L.off_qt_flags;
   p->off_qtile_ptr = L.off_qtile_ptr;
   p->off_ktile_idx = L.off_ktile_idx;
   p->off_ktile_word = L.off_ktile_word;
@@ -432,6 +490,7 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   D.qt_nnz = (int32_t*)(ws + L.off_qt_nnz);
   D.qt_pairs = (int64_t*)(ws + L.off_qt_pairs);
   D.qt_full = (int32_t*)(ws + L.off_qt_full);
+  D.qt_flags = (uint32_t*)(ws + L.off_qt_flags);
   D.qtile_ptr = (int32_t*)(ws + L.off_qtile_ptr);
   D.ktile_idx = (int32_t*)(ws + L.off_ktile_idx);
   D.ktile_word = (int32_t*)(ws + L.off_ktile_word);
@@ -453,31 +512,44 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   D.kilv = (int32_t*)(ws + L.off_kilv);
   D.group_of = (int32_t*)(ws + L.off_group_of);
 
-  p->host_blob = (unsigned char*)std::calloc(L.host_blob ? L.host_blob : 1, 1);
-  if (!p->host_blob) {
-    delete p;
-    return RK_ERR_INVALID_ARG;
+  // The host tables: read in place by the first planner kernel from a
+  // pinned block when one is free (and the batch has tokens, so that the
+  // kernel runs), else copied up from the plan's own host buffer.
+  const StagingPool::Lease lease =
+      L.NQ > 0 ? staging_pool().acquire(L.host_blob) : StagingPool::Lease{};
+  unsigned char* blob = lease.data;
+  if (!blob) {
+    p->host_blob = (unsigned char*)std::malloc(L.host_blob ? L.host_blob : 1);
+    if (!p->host_blob) {
+      delete p;
+      return RK_ERR_INVALID_ARG;
+    }
+    blob = p->host_blob;
   }
-  if (L.R) std::memcpy(p->host_blob + L.off_req, L.req.data(), sizeof(ReqMeta) * L.R);
-  if (L.NQ) std::memcpy(p->host_blob + L.off_qt_req, L.qt_req.data(), sizeof(int32_t) * L.NQ);
-  if (L.G) std::memcpy(p->host_blob + L.off_groups, L.groups.data(), sizeof(Group) * L.G);
-  std::memcpy(p->host_blob + L.off_queue_start, L.queue_start.data(), sizeof(int32_t) * (kNumXcd + 1));
-  if (L.NK) std::memcpy(p->host_blob + L.off_kt_req, L.kt_req.data(), sizeof(int32_t) * L.NK);
-  if (L.G) std::memcpy(p->host_blob + L.off_kgroups, L.kgroups.data(), sizeof(Group) * L.G);
-  std::memcpy(p->host_blob + L.off_kqueue_start, L.kqueue_start.data(),
-              sizeof(int32_t) * (kNumXcd + 1));
-  if (!L.ilv.empty())
-    std::memcpy(p->host_blob + L.off_ilv, L.ilv.data(), sizeof(int32_t) * L.ilv.size());
+  std::memset(blob, 0, L.host_blob);  // totals start at zero
+  if (L.R) std::memcpy(blob + L.off_req, L.req.data(), sizeof(ReqMeta) * L.R);
+  if (L.NQ) std::memcpy(blob + L.off_qt_req, L.qt_req.data(), sizeof(int32_t) * L.NQ);
+  if (L.G) std::memcpy(blob + L.off_groups, L.groups.data(), sizeof(Group) * L.G);
+  std::memcpy(blob + L.off_queue_start, L.queue_start.data(), sizeof(int32_t) * (kNumXcd + 1));
+  if (L.NK) std::memcpy(blob + L.off_kt_req, L.kt_req.data(), sizeof(int32_t) * L.NK);
+  if (L.G) std::memcpy(blob + L.off_kgroups, L.kgroups.data(), sizeof(Group) * L.G);
+  std::memcpy(blob + L.off_kqueue_start, L.kqueue_start.data(), sizeof(int32_t) * (kNumXcd + 1));
+  if (!L.ilv.empty()) std::memcpy(blob + L.off_ilv, L.ilv.data(), sizeof(int32_t) * L.ilv.size());
   if (!L.kilv.empty())
-    std::memcpy(p->host_blob + L.off_kilv, L.kilv.data(), sizeof(int32_t) * L.kilv.size());
+    std::memcpy(blob + L.off_kilv, L.kilv.data(), sizeof(int32_t) * L.kilv.size());
   if (!L.group_of.empty())
-    std::memcpy(p->host_blob + L.off_group_of, L.group_of.data(),
-                sizeof(int32_t) * L.group_of.size());
-  // totals stay zero (calloc)
+    std::memcpy(blob + L.off_group_of, L.group_of.data(), sizeof(int32_t) * L.group_of.size());
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = hipMemcpyAsync(workspace, p->host_blob, L.host_blob, hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = rk::launch_plan(p, s);
+  hipError_t e;
+  if (lease.data) {
+    // a failed launch leaves the block marked in use: a kernel that did
+    // start may still read it
+    e = rk::launch_plan(p, lease.data, lease.done, s);
+  } else {
+    e = hipMemcpyAsync(workspace, p->host_blob, L.host_blob, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = rk::launch_plan(p, nullptr, nullptr, s);
+  }
   if (e != hipSuccess) {
     std::free(p->host_blob);
     delete p;

@@ -38,6 +38,20 @@ namespace {
 // step 1 no memory is read.  On unsorted ts (which the row checks report)
 // the result is still in [0, n].
 constexpr int kSamples = 256;  // one per thread of the block
+
+// Where the first planner kernel finds the plan's host tables: in the
+// workspace already (blob null), or in a pinned host block that it reads
+// directly, copying 16-byte words [lo16, hi16) (the tables past the request
+// records) into the workspace; request records are written by the blocks
+// that read them.
+struct PlanSource {
+  const ReqMeta* req;
+  const int32_t* qt_req;
+  const uint4* blob;
+  uint4* dst;
+  int64_t lo16, hi16;
+  int R;
+};
 template <bool kStrict>
 __device__ __forceinline__ int count_sampled(const int64_t* __restrict__ ts, int n, int64_t x,
                                              const long long* samp, int step) {
@@ -206,29 +220,51 @@ __device__ __forceinline__ ItemRec item_rec(const PlanDev& P, int item, int kbeg
 // consecutive lanes per k-tile (S * nkt <= 256, S <= 64), whose counts
 // meet by shuffles.
 __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
-    PlanDev P, const uint8_t* __restrict__ kind, const int64_t* __restrict__ ts, int64_t delay,
-    int window, int global_tail, int bidir, int check_static_time, int slots) {
+    PlanDev P, PlanSource src, const uint8_t* __restrict__ kind, const int64_t* __restrict__ ts,
+    int64_t delay, int window, int global_tail, int bidir, int check_static_time, int slots) {
   __shared__ int2 d[kTileQ];
   __shared__ unsigned long long pairs_s;
   __shared__ int nnz_s, full_s;
   __shared__ int lim[4];  // lo_max, hi_min, lo_min, hi_max
   __shared__ int lo_s[3], hi_s[3];
   __shared__ long long samp[3][kSamples];  // PROFILE, HISTORY, REALTIME sample times
+  __shared__ unsigned flags_s;              // errors | info << 16 of the q-tile's rows
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
-  for (int64_t x = (int64_t)g * blockDim.x + tid; x < slots; x += (int64_t)gridDim.x * blockDim.x) {
+  const int64_t gstride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t x = (int64_t)g * blockDim.x + tid; x < slots; x += gstride) {
     P.sched[x] = -1;
     P.irec[x] = no_item_rec();
   }
-  const int r = P.qt_req[g];
-  const ReqMeta m = P.req[r];
+  if (src.blob) {
+    // host tables past the request records, into the workspace
+    for (int64_t x = src.lo16 + (int64_t)g * blockDim.x + tid; x < src.hi16; x += gstride)
+      src.dst[x] = src.blob[x];
+    // records of empty requests (a request with q-tiles writes its own below)
+    for (int64_t x = (int64_t)g * blockDim.x + tid; x < src.R; x += gstride) {
+      const ReqMeta e = src.req[x];
+      if (e.nqt == 0) P.req[x] = e;
+    }
+  }
+  const int r = src.qt_req[g];
+  const ReqMeta m = src.req[r];
   const int qt = g - m.qt_off;
   const int L = m.len;
   const int row0 = qt * kTileQ;
   const int nrows = min(kTileQ, L - row0);
   const int64_t* tr = ts + m.tok_off;
+  // the request's first q-tile writes the request's record with its segment
+  // starts (words kSeg.. of the record)
+  constexpr int kSeg = offsetof(ReqMeta, seg) / 4;
+  static_assert(offsetof(ReqMeta, seg) % 4 == 0 && sizeof(ReqMeta) == 4 * (kSeg + 4),
+                "segment starts close the request record");
+  int rec_word = 0;
+  if (qt == 0 && tid < kSeg) rec_word = reinterpret_cast<const int*>(src.req + r)[tid];
+  if (tid == 0) flags_s = 0;
   seg_search(kind + m.tok_off, L, lo_s, hi_s);
-  if (qt == 0 && tid < 4) P.req[r].seg[tid] = tid == 0 ? 0 : lo_s[tid - 1];
+  if (qt == 0 && tid < kSeg + 4)
+    reinterpret_cast<int*>(P.req + r)[tid] =
+        tid < kSeg ? rec_word : (tid == kSeg ? 0 : lo_s[tid - kSeg - 1]);
   // segment boundaries, made monotone and clamped so that any device data
   // yields in-range descriptors
   const int a_rt = min(max(lo_s[RK_SEG_REALTIME - 1], 0), L);
@@ -307,8 +343,7 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
       if (hi <= lo) { lo = 0; hi = 0; }
       desc = make_int2(lo, (int)((unsigned)hi | ((unsigned)diag << 31)));
       P.row_desc[i] = desc;
-      if (err) atomicOr(&P.totals->errors, err);
-      if (info) atomicOr(&P.totals->info, info);
+      if (err | info) atomicOr(&flags_s, err | (info << 16));
     }
     d[tid] = desc;
   }
@@ -394,6 +429,7 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
     P.qt_nnz[g] = nnz_s;
     P.qt_full[g] = full_s;
     P.qt_pairs[g] = (int64_t)pairs_s;
+    P.qt_flags[g] = flags_s;
   }
 }
 
@@ -406,28 +442,40 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
 // position base + C(k) + (ga - first group of its block)).  Block NQ: the
 // plan's totals.
 __global__ __launch_bounds__(256) void plan_csr_sched_kernel(PlanDev P, int NQ, int64_t NT, int H,
-                                                             int G, int write_sched) {
+                                                             int G, int write_sched,
+                                                             unsigned* stage_done) {
   __shared__ int smem[32];
   __shared__ long long red[16];
   __shared__ int w01[2];  // the row's first two CSR words
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   if (g == NQ) {
+    __shared__ unsigned flags_s;
+    if (tid == 0) flags_s = 0;
     long long nnz = 0, pairs = 0, nfull = 0;
+    unsigned fl = 0;
     for (int i = tid; i < NQ; i += blockDim.x) {
       nnz += P.qt_nnz[i];
       pairs += P.qt_pairs[i];
       nfull += P.qt_full[i];
+      fl |= P.qt_flags[i];
     }
-    nnz = block_sum(nnz, red);
+    nnz = block_sum(nnz, red);  // its barriers also order flags_s = 0 before the ORs
     pairs = block_sum(pairs, red);
     nfull = block_sum(nfull, red);
+    if (fl) atomicOr(&flags_s, fl);
+    __syncthreads();
     if (tid == 0) {
       P.qtile_ptr[NQ] = (int)nnz;
       P.totals->visible_pairs = (unsigned long long)pairs;
       P.totals->full_tiles = (unsigned long long)nfull;
       P.totals->partial_tiles = (unsigned long long)(nnz - nfull);
       P.totals->empty_tiles = (unsigned long long)(NT - nnz);
+      P.totals->errors = flags_s & 0xffffu;
+      P.totals->info = flags_s >> 16;
+      // the first kernel, the only reader of the staged host tables, has
+      // ended: their host block may be reused
+      if (stage_done) __hip_atomic_store(stage_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     return;
   }
@@ -790,20 +838,36 @@ __global__ void plan_ksched_kernel(PlanDev P, int64_t slots, int H, int G) {
 
 }  // namespace
 
-hipError_t launch_plan(const rk_plan* p, hipStream_t s) {
+hipError_t launch_plan(const rk_plan* p, const unsigned char* staged, unsigned* stage_done,
+                       hipStream_t s) {
   const PlanDev& P = p->dev;
+  PlanSource src{};
+  if (staged) {
+    // the first kernel reads the request records and q-tile table from the
+    // host block and copies the rest of the host tables into the workspace
+    src.req = reinterpret_cast<const ReqMeta*>(staged + p->off_req);
+    src.qt_req = reinterpret_cast<const int32_t*>(staged + p->off_qt_req);
+    src.blob = reinterpret_cast<const uint4*>(staged);
+    src.dst = reinterpret_cast<uint4*>(p->workspace);
+    src.lo16 = (int64_t)(p->off_qt_req / 16);
+    src.hi16 = (int64_t)(p->host_blob_bytes / 16);
+    src.R = p->R;
+  } else {
+    src.req = P.req;
+    src.qt_req = P.qt_req;
+  }
   const bool cand_only = (p->flags & RK_QUERY_CANDIDATES_ONLY) != 0;
   if (p->NQ > 0) {
     // one block per global q-tile (NQ > 0 whenever T > 0)
     const int check_static = (!(p->flags & RK_STATIC_BIDIRECTIONAL)) && p->delay > 0;
-    hipLaunchKernelGGL(plan_rows_tiles_kernel, dim3((unsigned)p->NQ), dim3(256), 0, s, P,
+    hipLaunchKernelGGL(plan_rows_tiles_kernel, dim3((unsigned)p->NQ), dim3(256), 0, s, P, src,
                        p->seg_kind_dev, p->timestamps_dev, p->delay, p->window, p->global_tail,
                        (int)((p->flags & RK_STATIC_BIDIRECTIONAL) != 0), check_static,
                        (int)p->slots);
   }
   // blocks 0 .. NQ - 1 per q-tile, block NQ the totals (zero tiles: totals only)
   hipLaunchKernelGGL(plan_csr_sched_kernel, dim3((unsigned)(p->NQ + 1)), dim3(256), 0, s, P,
-                     (int)p->NQ, p->NT, p->H, (int)p->G, (int)!cand_only);
+                     (int)p->NQ, p->NT, p->H, (int)p->G, (int)!cand_only, stage_done);
   if (cand_only && p->slots > 0) {
     hipLaunchKernelGGL(plan_sched_kernel, dim3((unsigned)((p->slots + 255) / 256)), dim3(256), 0, s,
                        P, p->slots, p->H, 1, (int)p->G);

@@ -122,6 +122,7 @@ struct PlanDev {
   int32_t* qt_nnz;         // [NQ] non-empty k-tiles of each q-tile
   int64_t* qt_pairs;       // [NQ] visible pairs of each q-tile
   int32_t* qt_full;        // [NQ] FULL k-tiles of each q-tile
+  uint32_t* qt_flags;      // [NQ] device-check errors | info << 16 of each q-tile's rows
   int32_t* qtile_ptr;      // [NQ + 1]
   int32_t* ktile_idx;      // [NT]
   int32_t* ktile_word;     // [NT] CSR entry for the kernels: kt | (PARTIAL << 31)
@@ -170,10 +171,10 @@ struct rk_plan {
       off_tile_class, off_qt_nnz, off_qt_pairs, off_qt_full, off_qtile_ptr, off_ktile_idx, off_ktile_word, off_qorder,
       off_sched, off_work, off_splits, off_act, off_totals, host_blob_bytes, total_bytes,
       off_kt_req, off_kgroups, off_kqueue_start, off_kt_nnz, off_kt_ptr, off_qtile_word,
-      off_korder, off_ksched, off_ilv, off_kilv, off_group_of, off_irec;
+      off_korder, off_ksched, off_ilv, off_kilv, off_group_of, off_irec, off_qt_flags;
   rk::PlanDev dev;
-  // host copy of the first host_blob_bytes of the workspace (kept alive
-  // for the asynchronous upload)
+  // host copy of the first host_blob_bytes of the workspace when it went
+  // up by an asynchronous copy (kept alive for it), else null
   unsigned char* host_blob;
 };
 
@@ -194,7 +195,11 @@ struct RopeTab {
 };
 
 // ---- launchers (defined in the .hip files); return hipSuccess or an error
-hipError_t launch_plan(const rk_plan* p, hipStream_t s);
+// staged: the plan's host tables in a pinned host block the first kernel
+// reads (null: already in the workspace); stage_done: set to 1 by the GPU
+// once that block has been read (null with staged null).
+hipError_t launch_plan(const rk_plan* p, const unsigned char* staged, unsigned* stage_done,
+                       hipStream_t s);
 // kinds: rotate only tokens whose segment kind k has bit k set (0 = all).
 // norm: RMSNorm of every [d] row (x / sqrt(mean(x^2) + eps) * gamma, gamma
 // NULL = 1) before the rotation; needs d in {32, 64, 128}.  A zero table

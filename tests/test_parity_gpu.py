@@ -208,6 +208,30 @@ def test_plan_bit_exact_random(rk, seed):
         _check_plan(wl, plan, ref)
 
 
+def test_plans_queued_ahead_of_the_gpu(rk):
+    """Plans issued while the stream is still busy: each one's host tables
+    wait in a pinned host block until its first planner kernel reads them,
+    so 80 plans in flight take every block the library keeps (then fall back
+    to an asynchronous copy); blocks are reused once read.  Every plan,
+    whichever way its tables went up, is bit-exact, and so is a second round
+    that reuses the blocks."""
+    rng = np.random.default_rng(11)
+    reqs = random_layout(rng, 5, 600)
+    wl = make_custom(reqs, heads=2, d_head=64, dtype="bf16", delay=3600, with_qkv=False,
+                     name="queued")
+    ref = oracle.tile_plan(wl.req_offsets, wl.seg_kind, wl.timestamps, delay=wl.delay, window=0,
+                           static_bidirectional=False)
+    batch = rk.Batch.from_workload(wl)
+    for rnd in range(2):
+        _say(f"[gpu] plans queued ahead, round {rnd}")
+        torch.cuda.synchronize()
+        torch.cuda._sleep(100_000_000)  # the stream stays busy while the plans are issued
+        plans = [rk.Plan(batch, delay=wl.delay, num_heads=wl.heads) for _ in range(80)]
+        for i, plan in enumerate(plans):
+            _check_plan(wl, plan, ref, check_rows=(i % 16 == 0 or i == len(plans) - 1))
+            plan.close()
+
+
 @pytest.mark.parametrize("delay,window,bidir", [(0, 0, False), (3600, 0, False), (0, 300, False),
                                                  (1800, 1000, False), (0, 0, True)])
 def test_plan_bit_exact_lengths(rk, delay, window, bidir):
