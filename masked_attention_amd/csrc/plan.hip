@@ -168,6 +168,42 @@ __device__ void seg_search(const uint8_t* __restrict__ kr, int L, int* lo_s, int
   }
 }
 
+// Request-local starts of kinds 1..3 (lo_s[k - 1] = tokens of kind < k)
+// by counting over the whole request in one memory round: each thread
+// counts the kinds in its 16-byte words of [tok_off, tok_off + L) (a word
+// that is not wholly inside the T-byte array is read byte by byte, inside
+// the request only).  Equal to seg_search's result when kinds are
+// non-decreasing; any kinds give values in [0, L].  Ends with a barrier.
+constexpr int kSegCountMax = 16384;  // longer requests use seg_search
+__device__ void seg_count(const uint8_t* __restrict__ kind, int64_t tok_off, int L, int64_t T,
+                          int* lo_s, long long* red) {
+  const uintptr_t base = reinterpret_cast<uintptr_t>(kind);
+  const uintptr_t rs = base + (uintptr_t)tok_off, re = rs + (uintptr_t)L;
+  const uintptr_t w0 = rs & ~(uintptr_t)15;
+  const int nw = (int)((re - w0 + 15) >> 4);
+  long long c = 0;  // tokens of kind <= 0, <= 1, <= 2 in bits 0, 21, 42
+  auto tally = [&](unsigned b) {
+    c += (long long)(b <= 0u) + ((long long)(b <= 1u) << 21) + ((long long)(b <= 2u) << 42);
+  };
+  for (int w = threadIdx.x; w < nw; w += blockDim.x) {
+    const uintptr_t a = w0 + 16 * (uintptr_t)w;
+    const int jb = rs > a ? (int)(rs - a) : 0;
+    const int je = re < a + 16 ? (int)(re - a) : 16;
+    if (a >= base && a + 16 <= base + (uintptr_t)T) {
+      const uint4 v = *reinterpret_cast<const uint4*>(a);
+      const unsigned wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j >= jb && j < je) tally((wd[j >> 2] >> (8 * (j & 3))) & 0xffu);
+    } else {
+      for (int j = jb; j < je; ++j) tally(*reinterpret_cast<const uint8_t*>(a + j));
+    }
+  }
+  c = block_sum(c, red);
+  if (threadIdx.x < 3) lo_s[threadIdx.x] = (int)((c >> (21 * threadIdx.x)) & ((1 << 21) - 1));
+  __syncthreads();
+}
+
 // Record of a launch slot without work.
 __device__ __forceinline__ ItemRec no_item_rec() {
   ItemRec rc;
@@ -221,7 +257,8 @@ __device__ __forceinline__ ItemRec item_rec(const PlanDev& P, int item, int kbeg
 // meet by shuffles.
 __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
     PlanDev P, PlanSource src, const uint8_t* __restrict__ kind, const int64_t* __restrict__ ts,
-    int64_t delay, int window, int global_tail, int bidir, int check_static_time, int slots) {
+    int64_t T, int64_t delay, int window, int global_tail, int bidir, int check_static_time,
+    int slots) {
   __shared__ int2 d[kTileQ];
   __shared__ unsigned long long pairs_s;
   __shared__ int nnz_s, full_s;
@@ -229,6 +266,9 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
   __shared__ int lo_s[3], hi_s[3];
   __shared__ long long samp[3][kSamples];  // PROFILE, HISTORY, REALTIME sample times
   __shared__ unsigned flags_s;              // errors | info << 16 of the q-tile's rows
+  __shared__ long long red[16];
+  __shared__ int slow[256];                 // k-tiles counted row by row
+  __shared__ int nslow_s;
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t gstride = (int64_t)gridDim.x * blockDim.x;
@@ -253,6 +293,19 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
   const int row0 = qt * kTileQ;
   const int nrows = min(kTileQ, L - row0);
   const int64_t* tr = ts + m.tok_off;
+  // this thread's row (threads below nrows): kind and time of it and of the
+  // row before, loaded ahead of the segment pass so that the two overlap
+  int s_row = 0, s_prev = 0;
+  int64_t t_row = 0, t_prev = 0;
+  if (tid < nrows) {
+    const int64_t i = (int64_t)m.tok_off + row0 + tid;
+    s_row = kind[i];
+    t_row = ts[i];
+    if (row0 + tid > 0) {
+      s_prev = kind[i - 1];
+      t_prev = ts[i - 1];
+    }
+  }
   // the request's first q-tile writes the request's record with its segment
   // starts (words kSeg.. of the record)
   constexpr int kSeg = offsetof(ReqMeta, seg) / 4;
@@ -260,8 +313,14 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
                 "segment starts close the request record");
   int rec_word = 0;
   if (qt == 0 && tid < kSeg) rec_word = reinterpret_cast<const int*>(src.req + r)[tid];
-  if (tid == 0) flags_s = 0;
-  seg_search(kind + m.tok_off, L, lo_s, hi_s);
+  if (tid == 0) {
+    flags_s = 0;
+    nslow_s = 0;
+  }
+  if (L <= kSegCountMax)
+    seg_count(kind, m.tok_off, L, T, lo_s, red);
+  else
+    seg_search(kind + m.tok_off, L, lo_s, hi_s);
   if (qt == 0 && tid < kSeg + 4)
     reinterpret_cast<int*>(P.req + r)[tid] =
         tid < kSeg ? rec_word : (tid == kSeg ? 0 : lo_s[tid - kSeg - 1]);
@@ -295,14 +354,14 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
       const int p = row0 + tid;
       const int i = m.tok_off + p;
       unsigned err = 0, info = 0;
-      int s = kind[i];
+      int s = s_row;
       if (s > RK_SEG_CANDIDATE) { err |= kErrSegment; s = RK_SEG_CANDIDATE; }
       if (p > 0) {
-        int prev = kind[i - 1];
+        int prev = s_prev;
         if (prev > RK_SEG_CANDIDATE) prev = RK_SEG_CANDIDATE;
         if (s < prev) {
           err |= kErrSegment;
-        } else if (s == prev && ts[i] < ts[i - 1]) {
+        } else if (s == prev && t_row < t_prev) {
           if (s == RK_SEG_REALTIME || (check_static_time && s <= RK_SEG_HISTORY)) err |= kErrTime;
           if (s == RK_SEG_HISTORY) info = kInfoHistoryUnsorted;
         }
@@ -318,7 +377,7 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
           if (delay > 0) {
             // keys dated at or before the cut: [0, cp) of PROFILE and
             // [a_h, a_h + ch) of HISTORY
-            const int64_t cut = ts[i] - delay;
+            const int64_t cut = t_row - delay;
             const int cp = count_sampled<false>(tr, a_h, cut, samp[0], st_p);
             const int ch = count_sampled<false>(tr + a_h, a_rt - a_h, cut, samp[1], st_h);
             const bool prof_run = min(cp, hi) > lo;
@@ -337,7 +396,7 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
       } else if (s == RK_SEG_REALTIME) {
         hi = p + 1;
       } else {
-        hi = a_rt + count_sampled<true>(tr + a_rt, n_rt, ts[i], samp[2], st_r);
+        hi = a_rt + count_sampled<true>(tr + a_rt, n_rt, t_row, samp[2], st_r);
         diag = 1;
       }
       if (hi <= lo) { lo = 0; hi = 0; }
@@ -369,28 +428,53 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
   }
   __syncthreads();
   const int lo_max = lim[0], hi_min = lim[1], lo_min = lim[2], hi_max = lim[3];
-  int S = 1;  // lanes per k-tile (uniform over the block)
-  while (S < 64 && 2 * S * m.nkt <= (int)blockDim.x) S *= 2;
-  const int slice = tid & (S - 1);
-  const int per = kTileQ / S;  // rows of a lane: slice * per .. + per
-  const int t0 = slice * per, t1 = min(nrows, t0 + per);
-  const int step = blockDim.x / S;
+  // K-tiles decided from the extremes (FULL or EMPTY) are written at once;
+  // the others of each chunk of 256 are listed and counted row by row with
+  // the block's lanes spread over them: S = 2^j lanes per listed tile
+  // (S * listed <= 256, S <= 64), each over 128 / S rows, meeting by
+  // shuffles.
+  const int64_t trow = m.tile_off + (int64_t)qt * m.nkt;
   unsigned long long pairs = 0;
   int nnz = 0, nfull = 0;
-  // every lane of a k-tile's group runs the same trip count and takes the
-  // same branch (both depend on kt only), so the shuffles below see all S
-  // lanes
-  for (int kt0 = 0; kt0 < m.nkt; kt0 += step) {
-    const int kt = kt0 + tid / S;
-    const int c0 = kt * kTileK;
-    const int c1 = min(L, c0 + kTileK);
-    int cnt = 0;
+  auto put = [&](int kt, int cnt) {
+    const uint8_t cls =
+        cnt == 0 ? RK_TILE_EMPTY : (cnt == kTileQ * kTileK ? RK_TILE_FULL : RK_TILE_PARTIAL);
+    P.tile_count[trow + kt] = cnt;
+    P.tile_class[trow + kt] = cls;
+    pairs += cnt;
+    nnz += cnt > 0;
+    nfull += cls == RK_TILE_FULL;
+  };
+  for (int kt0 = 0; kt0 < m.nkt; kt0 += blockDim.x) {  // uniform trip count
+    const int kt = kt0 + tid;
     if (kt < m.nkt) {
+      const int c0 = kt * kTileK;
+      const int c1 = min(L, c0 + kTileK);
       const bool full = nrows == kTileQ && c1 - c0 == kTileK && lo_max <= c0 && c1 <= hi_min;
       const bool empty = (c0 >= hi_max || c1 <= lo_min) && (c1 <= row0 || c0 >= row0 + nrows);
-      if (full) {
-        cnt = slice == 0 ? kTileQ * kTileK : 0;
-      } else if (!empty) {
+      if (full)
+        put(kt, kTileQ * kTileK);
+      else if (empty)
+        put(kt, 0);
+      else
+        slow[atomicAdd(&nslow_s, 1)] = kt;
+    }
+    __syncthreads();
+    const int ns = nslow_s;
+    int S = 64;
+    while (S > 1 && S * ns > (int)blockDim.x) S >>= 1;
+    const int slice = tid & (S - 1);
+    const int per = kTileQ / S;  // rows of a lane: slice * per .. + per
+    const int t0 = slice * per, t1 = min(nrows, t0 + per);
+    // every lane of a tile's group runs the same trip count and takes the
+    // same branch, so the shuffles below see all S lanes
+    for (int j0 = 0; j0 < ns; j0 += (int)blockDim.x / S) {
+      const int j = j0 + tid / S;
+      int cnt = 0, ktj = 0;
+      if (j < ns) {
+        ktj = slow[j];
+        const int c0 = ktj * kTileK;
+        const int c1 = min(L, c0 + kTileK);
         for (int t = t0; t < t1; ++t) {
           const int lo = d[t].x;
           const int hi = d[t].y & 0x7fffffff;
@@ -402,17 +486,13 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
           }
         }
       }
+      for (int o = 1; o < S; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
+      if (j < ns && slice == 0) put(ktj, cnt);
     }
-    for (int o = 1; o < S; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
-    if (kt < m.nkt && slice == 0) {
-      const uint8_t cls =
-          cnt == 0 ? RK_TILE_EMPTY : (cnt == kTileQ * kTileK ? RK_TILE_FULL : RK_TILE_PARTIAL);
-      const int64_t t_idx = m.tile_off + (int64_t)qt * m.nkt + kt;
-      P.tile_count[t_idx] = cnt;
-      P.tile_class[t_idx] = cls;
-      pairs += cnt;
-      nnz += cnt > 0;
-      nfull += cls == RK_TILE_FULL;
+    if (kt0 + (int)blockDim.x < m.nkt) {  // the list is reused by the next chunk
+      __syncthreads();
+      if (tid == 0) nslow_s = 0;
+      __syncthreads();
     }
   }
   // block sums: wave sums, then one LDS atomic per wave
@@ -861,7 +941,8 @@ hipError_t launch_plan(const rk_plan* p, const unsigned char* staged, unsigned* 
     // one block per global q-tile (NQ > 0 whenever T > 0)
     const int check_static = (!(p->flags & RK_STATIC_BIDIRECTIONAL)) && p->delay > 0;
     hipLaunchKernelGGL(plan_rows_tiles_kernel, dim3((unsigned)p->NQ), dim3(256), 0, s, P, src,
-                       p->seg_kind_dev, p->timestamps_dev, p->delay, p->window, p->global_tail,
+                       p->seg_kind_dev, p->timestamps_dev, (int64_t)p->T, p->delay, p->window,
+                       p->global_tail,
                        (int)((p->flags & RK_STATIC_BIDIRECTIONAL) != 0), check_static,
                        (int)p->slots);
   }
