@@ -355,8 +355,10 @@ rk_status rk_plan_workspace_size(const rk_batch* b, int32_t num_heads, size_t* b
  * Host tables computed from req_offsets_host reach the GPU through pinned
  * host blocks the library keeps for this (at most 64, each 64 KiB or more,
  * reused as the planner kernels finish reading them, held until the process
- * ends); with all of them in use the call copies its tables up with
- * hipMemcpyAsync instead.  The call is asynchronous either way.
+ * ends); with all of them in use, or while `stream` is being captured into
+ * a graph (a replay reads the source again; the plan's own host copy, kept
+ * until rk_plan_destroy, still holds it), the call copies its tables up
+ * with hipMemcpyAsync instead.  The call is asynchronous either way.
  * Errors: RK_ERR_INVALID_ARG, RK_ERR_UNSUPPORTED (more than 2^31-1 tiles
  * or work items), RK_ERR_WORKSPACE_TOO_SMALL, RK_ERR_HIP.
  */

@@ -514,9 +514,21 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
 
   // The host tables: read in place by the first planner kernel from a
   // pinned block when one is free (and the batch has tokens, so that the
-  // kernel runs), else copied up from the plan's own host buffer.
+  // kernel runs), else copied up from the plan's own host buffer.  Under
+  // stream capture the copy is used: a replayed graph reads its source
+  // again, which the plan's own buffer still holds and a reused block
+  // would not.
+  hipStream_t s = (hipStream_t)stream;
+  bool may_stage = false;
+  if (L.NQ > 0) {
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusActive;
+    if (hipStreamIsCapturing(s, &capture) == hipSuccess)
+      may_stage = capture == hipStreamCaptureStatusNone;
+    else
+      (void)hipGetLastError();  // the query's own error; take the copy
+  }
   const StagingPool::Lease lease =
-      L.NQ > 0 ? staging_pool().acquire(L.host_blob) : StagingPool::Lease{};
+      may_stage ? staging_pool().acquire(L.host_blob) : StagingPool::Lease{};
   unsigned char* blob = lease.data;
   if (!blob) {
     p->host_blob = (unsigned char*)std::malloc(L.host_blob ? L.host_blob : 1);
@@ -540,7 +552,6 @@ rk_status rk_mask_plan(const rk_batch* b, const rk_mask_params* m, int32_t num_h
   if (!L.group_of.empty())
     std::memcpy(blob + L.off_group_of, L.group_of.data(), sizeof(int32_t) * L.group_of.size());
 
-  hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (lease.data) {
     // a failed launch leaves the block marked in use: a kernel that did

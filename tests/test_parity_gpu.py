@@ -232,6 +232,41 @@ def test_plans_queued_ahead_of_the_gpu(rk):
             plan.close()
 
 
+def test_plan_captured_in_graph(rk):
+    """A plan built under stream capture: its host tables then go up by a
+    copy from the plan's own buffer (a pinned block could hold another
+    plan's tables by the time a replay runs).  Three replays, with eager
+    plans built and the workspace cleared between them, are each
+    bit-exact."""
+    rng = np.random.default_rng(12)
+    reqs = random_layout(rng, 4, 500)
+    wl = make_custom(reqs, heads=2, d_head=64, dtype="bf16", delay=3600, with_qkv=False,
+                     name="graph")
+    ref = oracle.tile_plan(wl.req_offsets, wl.seg_kind, wl.timestamps, delay=wl.delay, window=0,
+                           static_bidirectional=False)
+    batch = rk.Batch.from_workload(wl)
+    size = rk.binding.rk_plan_workspace_size(batch, wl.heads)
+    ws = torch.zeros(max(size, 256), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=side):
+        plan = rk.Plan(batch, delay=wl.delay, num_heads=wl.heads, workspace=ws)
+    torch.cuda.synchronize()
+    for rnd in range(3):
+        _say(f"[gpu] captured plan, replay {rnd}")
+        ws.zero_()
+        others = [rk.Plan(batch, delay=wl.delay, num_heads=wl.heads) for _ in range(3)]
+        graph.replay()
+        torch.cuda.synchronize()
+        _check_plan(wl, plan, ref, check_rows=(rnd == 0))
+        for o in others:
+            _check_plan(wl, o, ref, check_rows=False)
+            o.close()
+    plan.close()
+    del graph
+
+
 @pytest.mark.parametrize("delay,window,bidir", [(0, 0, False), (3600, 0, False), (0, 300, False),
                                                  (1800, 1000, False), (0, 0, True)])
 def test_plan_bit_exact_lengths(rk, delay, window, bidir):
