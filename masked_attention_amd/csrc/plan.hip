@@ -248,10 +248,10 @@ __device__ __forceinline__ ItemRec item_rec(const PlanDev& P, int item, int kbeg
 //
 // Tile counts: from the extremes of the rows' intervals [lo, hi) (lo_max,
 // hi_min, lo_min, hi_max over the q-tile's rows) most k-tiles [c0, c1) are
-// decided without visiting the rows: a whole tile (128 rows, 64 keys) with
-// lo_max <= c0 and c1 <= hi_min is FULL (8192 pairs; a row's own key, if in
-// the tile, is inside its interval); a tile with c0 >= hi_max or c1 <=
-// lo_min that holds no row's own position is EMPTY.  The rest are counted
+// decided without visiting the rows: a tile with lo_max <= c0 and c1 <=
+// hi_min holds nrows * (c1 - c0) pairs (a row's own key, if in the tile,
+// is inside its interval), FULL when that is 128 * 64; a tile with c0 >=
+// hi_max or c1 <= lo_min that holds no row's own position is EMPTY.  The rest are counted
 // row by row; with fewer than 256 k-tiles the rows are split among S = 2^j
 // consecutive lanes per k-tile (S * nkt <= 256, S <= 64), whose counts
 // meet by shuffles.
@@ -450,10 +450,13 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
     if (kt < m.nkt) {
       const int c0 = kt * kTileK;
       const int c1 = min(L, c0 + kTileK);
-      const bool full = nrows == kTileQ && c1 - c0 == kTileK && lo_max <= c0 && c1 <= hi_min;
+      // every row's interval covers the tile's keys (then so does it hold
+      // each row's own key if in the tile): nrows * width pairs, FULL when
+      // that is 8192
+      const bool cover = lo_max <= c0 && c1 <= hi_min;
       const bool empty = (c0 >= hi_max || c1 <= lo_min) && (c1 <= row0 || c0 >= row0 + nrows);
-      if (full)
-        put(kt, kTileQ * kTileK);
+      if (cover)
+        put(kt, nrows * (c1 - c0));
       else if (empty)
         put(kt, 0);
       else
