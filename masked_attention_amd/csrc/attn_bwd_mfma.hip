@@ -196,18 +196,30 @@ __device__ __forceinline__ void store_row(unsigned short* p, const f32x16& x0, c
   }
 }
 
+// x * c for the eight bf16 of a fragment, rounded back to bf16.
+__device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8& x, float c) {
+  uint4 u;
+  __builtin_memcpy(&u, &x, 16);
+  const unsigned w[4] = {u.x, u.y, u.z, u.w};
+  unsigned o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(bf_lo(w[j]) * c, bf_hi(w[j]) * c);
+  return as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
+}
+
 // ===========================================================================
 // dq kernel
 // ===========================================================================
 
 constexpr int TILE_ELEMS = kTileK * D;  // 64 rows x 64 bf16 = 8 KB
 
-// X^T (64 keys x 32 queries) = X_tile Y_w^T, X from LDS (row reads), Y
-// fragments in registers (lane = query).
+// X^T (64 keys x 32 queries) = X_tile Y_w^T + c, X from LDS (row reads), Y
+// fragments in registers (lane = query), c the lane's query's constant in
+// every accumulator register.
 __device__ __forceinline__ void prod_keys(f32x16& s0, f32x16& s1, const unsigned short* t,
-                                          const bf16x8 (&y)[4], int li, int hh) {
+                                          const bf16x8 (&y)[4], float c, int li, int hh) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+  for (int r = 0; r < 16; ++r) { s0[r] = c; s1[r] = c; }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int c = 2 * s + hh;  // d = 16 s + 8 hh .. +7
@@ -219,12 +231,14 @@ __device__ __forceinline__ void prod_keys(f32x16& s0, f32x16& s1, const unsigned
 __device__ __forceinline__ void dq_tile(f32x16& dq0, f32x16& dq1, const unsigned short* kb,
                                         const unsigned short* vb, const bf16x8 (&q)[4],
                                         const bf16x8 (&g)[4], int kt, bool partial, int li, int hh,
-                                        int lo, int hi, int self, int row, float c2, float lse2,
+                                        int lo, int hi, int self, int row, float lse2,
                                         float dsum) {
+  // q carries scale * log2(e), so the products start from -lse2 and -D and
+  // come out as the exponent of P^T and as dP^T - D
   f32x16 s0, s1, p0, p1;
-  prod_keys(s0, s1, kb, q, li, hh);
+  prod_keys(s0, s1, kb, q, -lse2, li, hh);
   if (partial) mask_keys(s0, s1, kt, hh, lo, hi, self, row);
-  prod_keys(p0, p1, vb, g, li, hh);
+  prod_keys(p0, p1, vb, g, -dsum, li, hh);
   // dS^T = P^T (dP^T - D), packed as the B operand of step s (accumulator
   // block s / 2, registers 8 (s % 2) .. +7)
   bf16x8 ds[4];
@@ -236,10 +250,10 @@ __device__ __forceinline__ void dq_tile(f32x16& dq0, f32x16& dq1, const unsigned
     bf16x2_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float pr0 = __builtin_amdgcn_exp2f(fmaf(sa[r0 + 2 * j], c2, -lse2));
-      const float pr1 = __builtin_amdgcn_exp2f(fmaf(sa[r0 + 2 * j + 1], c2, -lse2));
-      w[j][0] = (__bf16)(pr0 * (pa[r0 + 2 * j] - dsum));
-      w[j][1] = (__bf16)(pr1 * (pa[r0 + 2 * j + 1] - dsum));
+      const float pr0 = __builtin_amdgcn_exp2f(sa[r0 + 2 * j]);
+      const float pr1 = __builtin_amdgcn_exp2f(sa[r0 + 2 * j + 1]);
+      w[j][0] = (__bf16)(pr0 * pa[r0 + 2 * j]);
+      w[j][1] = (__bf16)(pr1 * pa[r0 + 2 * j + 1]);
     }
     __builtin_memcpy(&ds[s], w, 16);
   }
@@ -354,7 +368,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdPlanView P,
   const int lo = rvalid ? dsc.x : 0;
   const int hi = rvalid ? dsc.y & 0x7fffffff : 0;
   const int self = rvalid && dsc.y < 0;
-  const float c2 = A.scale * kLog2e;
+  // scores in log2 units straight from the matrix cores
+#pragma unroll
+  for (int s = 0; s < 4; ++s) q[s] = scale_bf16x8(q[s], A.scale * kLog2e);
 
   f32x16 dq0, dq1;
 #pragma unroll
@@ -367,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdPlanView P,
       const int w_nxt = ldc(P.ktile_word, e0 + min(it + 1, n - 1));
       issue(K1, V1, w_nxt & 0x7fffffff);
       dq_tile(dq0, dq1, K0, V0, q, g, w_cur & 0x7fffffff, w_cur < 0, li, hh, lo, hi, self, row,
-              c2, lse2, dsum);
+              lse2, dsum);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       w_cur = w_nxt;
@@ -376,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdPlanView P,
       const int w_nxt = ldc(P.ktile_word, e0 + min(it + 2, n - 1));
       issue(K0, V0, w_nxt & 0x7fffffff);
       dq_tile(dq0, dq1, K1, V1, q, g, w_cur & 0x7fffffff, w_cur < 0, li, hh, lo, hi, self, row,
-              c2, lse2, dsum);
+              lse2, dsum);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       w_cur = w_nxt;
