@@ -196,17 +196,6 @@ __device__ __forceinline__ void store_row(unsigned short* p, const f32x16& x0, c
   }
 }
 
-// x * c for the eight bf16 of a fragment, rounded back to bf16.
-__device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8& x, float c) {
-  uint4 u;
-  __builtin_memcpy(&u, &x, 16);
-  const unsigned w[4] = {u.x, u.y, u.z, u.w};
-  unsigned o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(bf_lo(w[j]) * c, bf_hi(w[j]) * c);
-  return as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
-}
-
 // ===========================================================================
 // dq kernel
 // ===========================================================================

@@ -9,17 +9,22 @@
 //
 // Work item = (query tile of 128 rows, head); 4 waves of 32 rows, one query
 // per lane, the transposed products of the softmax kernel:
-//   S^T (64 keys x 32 queries) = K Q^T + C     8 x mfma 32x32x16
-//   W = SiLU(S^T * scale (+ rab)), masked keys 0, packed to bf16
-//   O^T (64 d x 32 queries) += V^T W^T         8 x mfma
+//   Y^T (64 keys x 32 queries) = K Q'^T + C    8 x mfma 32x32x16
+//   W' = Y / (1 + 2^Y) (+ rab in Y units), masked keys 0, packed to bf16
+//   O^T (64 d x 32 queries) += V^T W'^T        8 x mfma
+// in units where Y = -log2(e) x for x = scale q . k (+ rab): Q' carries
+// -scale * log2(e) and the bias tables -log2(e), so that SiLU(x) =
+// x / (1 + e^-x) = -ln2 * Y / (1 + 2^Y) costs one exp2, one add, one
+// reciprocal and one multiply per score; the -ln2 is applied to O at the
+// end.
 // The relative bias.  Both buckets are monotone in |p_i - p_j| and
 // |t_i - t_j|, so for one row over one key tile the bias is constant when
 // the bucket at both ends of the tile's position and time ranges is the
 // same and the ranges do not cross zero; the time range is the min / max
 // of the tile's key timestamps (one wave reduction per tile).  When that
 // holds for every lane of the wave, the constant enters the QK^T product
-// as its initial accumulator (C = bias / scale) and costs nothing per
-// score; otherwise (tiles near the diagonal or across a bucket edge) the
+// as its initial accumulator (C = the bias in Y units) and costs nothing
+// per score; otherwise (tiles near the diagonal or across a bucket edge) the
 // wave evaluates the bias per score from the tables in LDS.
 #include "cdna4_common.h"
 
@@ -82,7 +87,8 @@ struct Tabs {
   float time[kMaxTime];
 };
 
-// W = SiLU(S * scale (+ rab)) packed to bf16 as the B operands of the PV
+// W' = Y / (1 + 2^Y) (Y = the scaled score in -log2(e) units, + rab in the
+// same units) packed to bf16 as the B operands of the PV
 // product (step s: accumulator block s / 2, registers 8 (s % 2) .. +7).
 // Register r of block mb holds key c0 + 32 mb + 8 (r / 4) + 4 hh + r % 4.
 // kBias: the bias varies over the tile and is read from the tables per
@@ -91,7 +97,7 @@ struct Tabs {
 // 4 hh).
 template <bool kBias, bool kPartial>
 __device__ __forceinline__ void pw_weights(bf16x8 (&pb)[4], const f32x16& s0, const f32x16& s1,
-                                           float scale, int w0, int w1, const int64_t* tk,
+                                           int w0, int w1, const int64_t* tk,
                                            const Tabs& tab, int c0, int hh, int row, int64_t ti,
                                            const PwLaunch& A, bool has_pos, bool has_time) {
 #pragma unroll
@@ -105,7 +111,7 @@ __device__ __forceinline__ void pw_weights(bf16x8 (&pb)[4], const f32x16& s0, co
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int r = r0 + 2 * j + e;
-        float x = src[r] * scale;
+        float x = src[r];
         if (kBias) {
           const int kk = 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);  // key offset in the tile
           if (has_pos) {
@@ -114,7 +120,7 @@ __device__ __forceinline__ void pw_weights(bf16x8 (&pb)[4], const f32x16& s0, co
           }
           if (has_time) x += tab.time[time_bucket(ti - tk[kk], A.nt)];
         }
-        float wv = x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e));
+        float wv = x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x));
         if (kPartial) {
           const unsigned bit = 8u * (unsigned)(r >> 2) + (unsigned)(r & 3);
           const int m = __builtin_amdgcn_sbfe(mb ? w1 : w0, bit, 1u);  // 0 or -1
@@ -172,7 +178,7 @@ __device__ __forceinline__ void pw_tile(f32x16& o0, f32x16& o1, const unsigned s
     }
   }
   const bool uniform = !__any(!fast);
-  const float init = uniform ? cb / A.scale : 0.f;
+  const float init = uniform ? cb : 0.f;
 
   // ---- S^T = K Q^T + C
   f32x16 s0, s1;
@@ -187,7 +193,7 @@ __device__ __forceinline__ void pw_tile(f32x16& o0, f32x16& o1, const unsigned s
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, q[s], s1, 0, 0, 0);
   }
 
-  // ---- W = SiLU(S * scale (+ rab)), masked keys 0; one code path per
+  // ---- W' = Y / (1 + 2^Y) (+ rab), masked keys 0; one code path per
   // (bias per score, mask) case, chosen per tile and wave
   bf16x8 pb[4];
   int w0 = -1, w1 = -1;
@@ -198,17 +204,17 @@ __device__ __forceinline__ void pw_tile(f32x16& o0, f32x16& o1, const unsigned s
   }
   if (uniform) {
     if (partial)
-      pw_weights<false, true>(pb, s0, s1, A.scale, w0, w1, tk, tab, c0, hh, row, ti, A, has_pos,
+      pw_weights<false, true>(pb, s0, s1, w0, w1, tk, tab, c0, hh, row, ti, A, has_pos,
                               has_time);
     else
-      pw_weights<false, false>(pb, s0, s1, A.scale, w0, w1, tk, tab, c0, hh, row, ti, A, has_pos,
+      pw_weights<false, false>(pb, s0, s1, w0, w1, tk, tab, c0, hh, row, ti, A, has_pos,
                                has_time);
   } else {
     if (partial)
-      pw_weights<true, true>(pb, s0, s1, A.scale, w0, w1, tk, tab, c0, hh, row, ti, A, has_pos,
+      pw_weights<true, true>(pb, s0, s1, w0, w1, tk, tab, c0, hh, row, ti, A, has_pos,
                              has_time);
     else
-      pw_weights<true, false>(pb, s0, s1, A.scale, w0, w1, tk, tab, c0, hh, row, ti, A, has_pos,
+      pw_weights<true, false>(pb, s0, s1, w0, w1, tk, tab, c0, hh, row, ti, A, has_pos,
                               has_time);
   }
 
@@ -282,8 +288,11 @@ __global__ __launch_bounds__(kThreads, 3) void pw_mfma_bf16_d64_kernel(PwView P,
   const int self = rvalid && dsc.y < 0;
   const bool has_pos = A.pos_bias != nullptr, has_time = A.time_bias != nullptr;
   const bool hist_sorted = !(ldc(P.info, 0) & kInfoHistoryUnsorted);
-  for (int x = tid; x < A.np && has_pos; x += kThreads) tab.pos[x] = A.pos_bias[x];
-  for (int x = tid; x < A.nt && has_time; x += kThreads) tab.time[x] = A.time_bias[x];
+  // scores and biases in -log2(e) units (the -ln2 goes onto O at the end)
+  for (int x = tid; x < A.np && has_pos; x += kThreads) tab.pos[x] = -kLog2e * A.pos_bias[x];
+  for (int x = tid; x < A.nt && has_time; x += kThreads) tab.time[x] = -kLog2e * A.time_bias[x];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) q[s] = scale_bf16x8(q[s], -kLog2e * A.scale);
 
   const char* Kb = (const char*)((const unsigned short*)A.k + (int64_t)m.tok_off * A.k_st + (int64_t)head * A.k_sh);
   const char* Vb = (const char*)((const unsigned short*)A.v + (int64_t)m.tok_off * A.v_st + (int64_t)head * A.v_sh);
@@ -366,10 +375,11 @@ __global__ __launch_bounds__(kThreads, 3) void pw_mfma_bf16_d64_kernel(PwView P,
   }
 
   if (!rvalid) return;
+  const float oscale = -0.6931471805599453f * pz;  // -ln2
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    o0[r] *= pz;
-    o1[r] *= pz;
+    o0[r] *= oscale;
+    o1[r] *= oscale;
   }
   unsigned short* Op = (unsigned short*)A.o + (int64_t)tokq * A.o_st + (int64_t)head * A.o_sh;
 #pragma unroll
