@@ -232,6 +232,46 @@ def test_plans_queued_ahead_of_the_gpu(rk):
             plan.close()
 
 
+def test_plans_from_several_host_threads(rk):
+    """Plans built from four host threads at once, each on its own stream:
+    the pinned host blocks are handed out under a lock, so every plan gets
+    its own tables and all of them are bit-exact."""
+    import threading
+    rng = np.random.default_rng(13)
+    reqs = random_layout(rng, 6, 700)
+    wl = make_custom(reqs, heads=2, d_head=64, dtype="bf16", delay=1800, window=300,
+                     with_qkv=False, name="threads")
+    ref = oracle.tile_plan(wl.req_offsets, wl.seg_kind, wl.timestamps, delay=wl.delay,
+                           window=wl.window, static_bidirectional=False)
+    batch = rk.Batch.from_workload(wl)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    plans = [[] for _ in streams]
+    errors = []
+
+    def work(i):
+        try:
+            for _ in range(12):
+                plans[i].append(rk.Plan(batch, delay=wl.delay, window=wl.window,
+                                        num_heads=wl.heads, stream=streams[i]))
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(e)
+
+    _say("[gpu] plans from four host threads")
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(streams))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i, ps in enumerate(plans):
+        assert len(ps) == 12
+        for j, plan in enumerate(ps):
+            _check_plan(wl, plan, ref, check_rows=(j == 0))
+            plan.close()
+
+
 def test_plan_captured_in_graph(rk):
     """A plan built under stream capture: its host tables then go up by a
     copy from the plan's own buffer (a pinned block could hold another
