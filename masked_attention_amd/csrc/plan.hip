@@ -236,11 +236,14 @@ __device__ __forceinline__ ItemRec item_rec(const PlanDev& P, int item, int kbeg
 }
 
 // One block (256 threads) per global q-tile: the request's segment starts
-// (sampled search; the request's first q-tile records them), the order
+// (a counting pass over its kinds, or a sampled search beyond
+// kSegCountMax tokens; the request's first q-tile records them), the order
 // checks and visible interval (row descriptor) of each of its 128 rows, and
 // the exact visible count and class of each of its k-tiles with the
-// q-tile's partial totals (non-empty, FULL, pairs).  It also marks its
-// share of the launch schedule idle; the CSR kernel writes the items.
+// q-tile's partial totals (non-empty, FULL, pairs, check flags).  It also
+// marks its share of the launch schedule idle and, when the host tables
+// come from a pinned host block, copies them into the workspace; the CSR
+// kernel writes the items.
 //
 // Row checks: segment kinds non-decreasing and in range; real-time events
 // in time order; PROFILE and HISTORY each in time order when the delay rule
@@ -251,10 +254,9 @@ __device__ __forceinline__ ItemRec item_rec(const PlanDev& P, int item, int kbeg
 // decided without visiting the rows: a tile with lo_max <= c0 and c1 <=
 // hi_min holds nrows * (c1 - c0) pairs (a row's own key, if in the tile,
 // is inside its interval), FULL when that is 128 * 64; a tile with c0 >=
-// hi_max or c1 <= lo_min that holds no row's own position is EMPTY.  The rest are counted
-// row by row; with fewer than 256 k-tiles the rows are split among S = 2^j
-// consecutive lanes per k-tile (S * nkt <= 256, S <= 64), whose counts
-// meet by shuffles.
+// hi_max or c1 <= lo_min that holds no row's own position is EMPTY.  The
+// rest (diagonal, window and delay boundaries) are listed in LDS and
+// counted row by row, the block's lanes spread over the list.
 __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
     PlanDev P, PlanSource src, const uint8_t* __restrict__ kind, const int64_t* __restrict__ ts,
     int64_t T, int64_t delay, int window, int global_tail, int bidir, int check_static_time,
