@@ -744,6 +744,7 @@ __global__ __launch_bounds__(1024) void plan_work_kernel(PlanDev P, int slots, i
   __shared__ int smem[32];
   __shared__ long long tiles_sh[16];
   __shared__ int s_slot[kMaxAct], s_item[kMaxAct], s_n[kMaxAct];
+  __shared__ int s_c[kMaxAct], s_w[kMaxAct], s_p[kMaxAct];  // chunks, first entry, first part
   const int t = threadIdx.x;
   const int n_act = P.totals->n_act;
   const bool split = n_act < kMaxAct;
@@ -802,16 +803,30 @@ __global__ __launch_bounds__(1024) void plan_work_kernel(PlanDev P, int slots, i
   const int C = (int)max((long long)kSplitMinChunk, cl);
   const int c = t < n_act ? max(1, (n + C - 1) / C) : 0;
   int w_tot, p_tot, s_tot;
-  int w = block_exclusive_scan(c, smem, &w_tot);
-  int part = block_exclusive_scan(c > 1 ? c : 0, smem, &p_tot);
+  const int w = block_exclusive_scan(c, smem, &w_tot);
+  const int part = block_exclusive_scan(c > 1 ? c : 0, smem, &p_tot);
   const int sp = block_exclusive_scan(c > 1 ? 1 : 0, smem, &s_tot);
   if (c > 1) P.splits[sp] = SplitEntry{item, part, c, 0};
-  for (int j = 0; j < c; ++j) {
-    // chunk lengths differ by at most one and none is empty (c <= n)
-    const int kb = (int)((long long)j * n / c), ke = (int)((long long)(j + 1) * n / c);
-    const int pi = c > 1 ? part++ : -1;
-    P.irec[w] = item_rec(P, item, kb, ke, pi, H);
-    P.work[w++] = WorkEntry{item, kb, ke, pi};
+  if (t < n_act) {
+    s_c[t] = c;
+    s_w[t] = w;
+    s_p[t] = c > 1 ? part : -1;
+  }
+  __syncthreads();
+  // entry e of the list: chunk e - s_w[i] of the last item i with s_w[i] <=
+  // e; one entry per thread, so their records' loads go out together.
+  // Chunk lengths differ by at most one and none is empty (c <= n).
+  for (int e = t; e < w_tot; e += blockDim.x) {
+    int a = 0, b = n_act - 1;
+    while (a < b) {
+      const int mid = (a + b + 1) >> 1;
+      if (s_w[mid] <= e) a = mid; else b = mid - 1;
+    }
+    const int j = e - s_w[a], ci = s_c[a], ni = s_n[a], it = s_item[a];
+    const int kb = (int)((long long)j * ni / ci), ke = (int)((long long)(j + 1) * ni / ci);
+    const int pi = ci > 1 ? s_p[a] + j : -1;
+    P.irec[e] = item_rec(P, it, kb, ke, pi, H);
+    P.work[e] = WorkEntry{it, kb, ke, pi};
   }
   for (int s = w_tot + t; s < min(grid, kHead); s += blockDim.x) {
     P.work[s] = WorkEntry{-1, 0, 0, -1};
