@@ -521,15 +521,18 @@ __global__ __launch_bounds__(256) void plan_rows_tiles_kernel(
 // Blocks 0 .. NQ - 1, one per global q-tile: the start of its CSR row (the
 // non-empty k-tiles of all earlier q-tiles), its rank among its request's
 // q-tiles (descending non-empty count, ties by index), the ascending list
-// of its non-empty k-tiles, and, unless the schedule is built by
-// plan_sched_kernel, its H items' slots of the blocked XCD schedule
-// (slot_of below, inverted: the item of group ga at rank k sits at queue
-// position base + C(k) + (ga - first group of its block)).  Block NQ: the
+// of its non-empty k-tiles, and its H items' slots of the blocked XCD
+// schedule (slot_of below, inverted: the item of group ga at rank k sits
+// at queue position base + C(k) + (ga - first group of its block)).  With
+// sched_mode 2 (candidates-only plans) only q-tiles holding a candidate row
+// are scheduled (the others' slots stay idle) and their slots are counted
+// and collected, in arrival order, for the work list.  Block NQ: the
 // plan's totals.
 __global__ __launch_bounds__(256) void plan_csr_sched_kernel(PlanDev P, int NQ, int64_t NT, int H,
-                                                             int G, int write_sched,
+                                                             int G, int sched_mode,
                                                              unsigned* stage_done) {
   __shared__ int smem[32];
+  __shared__ int act_base;
   __shared__ long long red[16];
   __shared__ int w01[2];  // the row's first two CSR words
   const int g = blockIdx.x;
@@ -597,8 +600,15 @@ __global__ __launch_bounds__(256) void plan_csr_sched_kernel(PlanDev P, int NQ, 
     }
     run += total;
   }
-  if (write_sched) {
+  const int first_cand = m.seg[RK_SEG_CANDIDATE];  // == len without candidates
+  const bool keep =
+      sched_mode == 1 || (first_cand < m.len && (qt + 1) * kTileQ > first_cand);
+  if (keep) {  // uniform over the block
     __syncthreads();
+    if (sched_mode == 2) {
+      if (tid == 0) act_base = atomicAdd(&P.totals->n_act, H);
+      __syncthreads();
+    }
     ItemRec rc = no_item_rec();
     rc.tok_off = m.tok_off;
     rc.len = m.len;
@@ -615,9 +625,11 @@ __global__ __launch_bounds__(256) void plan_csr_sched_kernel(PlanDev P, int NQ, 
       const int idx = P.groups[f].base + C[rank] + (ga - f);
       int q = 0;
       while (q < kNumXcd - 1 && ga >= P.queue_start[q + 1]) ++q;
-      P.sched[(int64_t)idx * kNumXcd + q] = g * H + h;
+      const int64_t slot = (int64_t)idx * kNumXcd + q;
+      P.sched[slot] = g * H + h;
       rc.head = h;
-      P.irec[(int64_t)idx * kNumXcd + q] = rc;
+      P.irec[slot] = rc;
+      if (sched_mode == 2 && act_base + h < kSplitTarget / 2) P.act_slots[act_base + h] = (int)slot;
     }
   }
 }
@@ -686,52 +698,10 @@ __device__ void slot_of(const Group* groups, const int32_t* qstart, const int32_
   *ga = f + (local - C[lo]);
 }
 
-// One thread per launch slot: slot s runs on XCD s % 8 as item s / 8 of
-// that XCD's queue.  With cand_only, a query tile without a CANDIDATE row
-// gets no work (-1): candidates are the last segment of a request, so the
-// tiles kept are the ones from the tile of the first candidate on, which
-// within a group come first in the descending-work order.
-__global__ void plan_sched_kernel(PlanDev P, int64_t slots, int H, int cand_only, int G) {
-  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (s >= slots) return;
-  const int q = (int)(s % kNumXcd);
-  const int idx = (int)(s / kNumXcd);
-  int item = -1;
-  int ga = -1, k = -1;  // group and its rank-k item of this slot
-  slot_of(P.groups, P.queue_start, P.ilv, G, q, idx, &ga, &k);
-  if (ga >= 0) {
-    const Group grp = P.groups[ga];
-    if (k >= 0 && k < grp.count) {
-      const ReqMeta m = P.req[grp.req];
-      const int qg = P.qorder[m.qt_off + k];
-      const int first_cand = m.seg[RK_SEG_CANDIDATE];  // == len without candidates
-      const bool keep = !cand_only || (first_cand < m.len &&
-                                       (qg - m.qt_off + 1) * kTileQ > first_cand);
-      if (keep) item = qg * H + grp.head;
-    }
-  }
-  P.sched[s] = item;
-  P.irec[s] = item_rec(P, item, 0, -1, -1, H);
-  if (cand_only) {
-    // count the active slots (one atomic per wave) and keep the first
-    // kSplitTarget / 2 of them, in arrival order, for the work list
-    const unsigned long long act = __ballot(item >= 0);
-    if (item >= 0) {
-      const int lane = threadIdx.x & 63;
-      const int below = __popcll(act & ((1ull << lane) - 1ull));
-      int base = 0;
-      if (below == 0) base = atomicAdd(&P.totals->n_act, __popcll(act));
-      base = __shfl(base, __builtin_ctzll(act), 64);
-      const int idx = base + below;
-      if (idx < kSplitTarget / 2) P.act_slots[idx] = (int)s;
-    }
-  }
-}
-
 // Work list of a candidates-only plan (blocks of 1024 threads over the
 // launch slots).  With at least kSplitTarget / 2 active items the list
 // mirrors the schedule (whole items, kend = -1).  With fewer, block 0 builds
-// it alone from the active slots the schedule kernel collected: they are put
+// it alone from the active slots the CSR kernel collected: they are put
 // back in slot order (rank by slot), and an item whose CSR holds n key tiles
 // is cut into c = ceil(n / C) chunks of equal length (to one tile), where
 // C = max(kSplitMinChunk, ceil(total tiles / kSplitTarget)).  Then sum(c) <=
@@ -750,7 +720,7 @@ __global__ __launch_bounds__(1024) void plan_work_kernel(PlanDev P, int slots, i
   const bool split = n_act < kMaxAct;
   if (!split) {
     const int s = blockIdx.x * blockDim.x + t;
-    if (s < grid && s >= slots) {  // slots below: the schedule kernel wrote their records
+    if (s < grid && s >= slots) {  // slots below: the CSR kernel wrote their records
       P.work[s] = WorkEntry{-1, 0, 0, -1};
       P.irec[s] = no_item_rec();
     } else if (s < slots) {
@@ -968,14 +938,10 @@ hipError_t launch_plan(const rk_plan* p, const unsigned char* staged, unsigned* 
   }
   // blocks 0 .. NQ - 1 per q-tile, block NQ the totals (zero tiles: totals only)
   hipLaunchKernelGGL(plan_csr_sched_kernel, dim3((unsigned)(p->NQ + 1)), dim3(256), 0, s, P,
-                     (int)p->NQ, p->NT, p->H, (int)p->G, (int)!cand_only, stage_done);
-  if (cand_only && p->slots > 0) {
-    hipLaunchKernelGGL(plan_sched_kernel, dim3((unsigned)((p->slots + 255) / 256)), dim3(256), 0, s,
-                       P, p->slots, p->H, 1, (int)p->G);
-    if (p->grid > p->slots)
-      hipLaunchKernelGGL(plan_work_kernel, dim3((unsigned)((p->grid + 1023) / 1024)), dim3(1024), 0,
-                         s, P, (int)p->slots, (int)p->grid, p->H);
-  }
+                     (int)p->NQ, p->NT, p->H, (int)p->G, cand_only ? 2 : 1, stage_done);
+  if (cand_only && p->slots > 0 && p->grid > p->slots)
+    hipLaunchKernelGGL(plan_work_kernel, dim3((unsigned)((p->grid + 1023) / 1024)), dim3(1024), 0,
+                       s, P, (int)p->slots, (int)p->grid, p->H);
   if ((p->flags & RK_PLAN_BACKWARD) && p->NK > 0) {
     hipLaunchKernelGGL(plan_kcount_kernel, dim3((unsigned)p->NK), dim3(256), 0, s, P);
     hipLaunchKernelGGL(plan_kscan_kernel, dim3(1), dim3(1024), 0, s, P, (int)p->NK);
