@@ -8,6 +8,10 @@ the C ABI against the CPU fp64 oracle.
   bf16, d = 32, 64, 128), K normalised by the attention's own pass or
   prepared by rk_qk_norm_rope (RK_ATTN_K_PREROTATED), against the oracle;
   fp32 within 1e-4 max-abs, bf16 within 2e-2 max-abs and 1e-2 relative L2.
+* The serving call with QK Norm: candidate keys normalised and rotated into
+  a key cache by kind, the history's prepared once, a candidates-only plan;
+  candidate rows equal the full call's bit for bit (whole items) or within
+  the split bound (split items) and match the oracle.
 * A full-size workload on sampled rows.  (The backward through QK Norm is
   checked with the other backward tests.)
 """
@@ -158,3 +162,58 @@ def test_qk_norm_workload_sampled_rows(rk):
     err = np.abs(got - ref).max()
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert err <= 2e-2 and rel <= 1e-2, (err, rel)
+
+
+@pytest.mark.parametrize("heads,reqs_seed", [(2, 71), (8, 72)])
+def test_qk_norm_serving_call(rk, heads, reqs_seed):
+    from rk_workloads import CANDIDATE, HISTORY, PROFILE, REALTIME, NOW
+    rng = np.random.default_rng(reqs_seed)
+    reqs = []
+    for n in (1500, 700, 300):
+        hist = np.sort(rng.integers(NOW - 10**6, NOW - 3600, n)).astype(np.int64)
+        reqs.append([(PROFILE, np.full(8, NOW, np.int64)), (HISTORY, hist),
+                     (REALTIME, np.sort(rng.integers(NOW - 3600, NOW, 20)).astype(np.int64)),
+                     (CANDIDATE, np.full(40, NOW, np.int64))])
+    wl = make_custom(reqs, heads=heads, d_head=64, dtype="bf16", seed=reqs_seed, delay=1800)
+    gq = rng.uniform(0.5, 1.5, 64).astype(np.float32)
+    gk = rng.uniform(0.5, 1.5, 64).astype(np.float32)
+    gq_t, gk_t = torch.from_numpy(gq).cuda(), torch.from_numpy(gk).cuda()
+    norm = dict(eps=1e-5, gamma_q=gq_t, gamma_k=gk_t)
+    batch = rk.Batch.from_workload(wl)
+    q, k = (torch.from_numpy(a * 2.0).cuda().to(torch.bfloat16) for a in (wl.q, wl.k))
+    v = torch.from_numpy(wl.v).cuda().to(torch.bfloat16)
+    kw = dict(delay=wl.delay, num_heads=wl.heads)
+    full_plan = rk.Plan(batch, **kw)
+    cand_plan = rk.Plan(batch, candidates_only=True, **kw)
+    _say(f"[gpu] qk-norm serving call heads={heads}")
+    # the history's keys prepared once into the cache, the candidates' per call
+    cache = torch.empty_like(k)
+    rk.rk_qk_norm_rope(batch, k, eps=1e-5, gamma=gk_t, rope=_rope(wl), out=cache,
+                       kinds=(PROFILE, HISTORY, REALTIME))
+    rk.rk_qk_norm_rope(batch, k, eps=1e-5, gamma=gk_t, rope=_rope(wl), out=cache,
+                       kinds=(CANDIDATE,))
+    o_full, _ = rk.rk_masked_attn_fwd(full_plan, q, k, v, rope=_rope(wl), qk_norm=norm)
+    o_c = torch.zeros_like(o_full)
+    rk.rk_masked_attn_fwd(cand_plan, q, cache, v, out=o_c, rope=_rope(wl), qk_norm=norm,
+                          k_prerotated=True)
+    torch.cuda.synchronize()
+    cand = np.nonzero(wl.seg_kind == CANDIDATE)[0]
+    st = cand_plan.stats()
+    got, full = o_c[torch.from_numpy(cand).cuda()], o_full[torch.from_numpy(cand).cuda()]
+    if st["split_items"] == 0:
+        assert torch.equal(got.view(torch.int16), full.view(torch.int16))
+    else:
+        err = (got.float() - full.float()).abs().max().item()
+        assert err <= 2e-2, err
+    qn, kn, vn = (t.float().cpu().numpy().astype(np.float64) for t in (q, k, v))
+    ref, _ = oracle.attention_forward(
+        wl.req_offsets, wl.seg_kind, wl.timestamps, qn, kn, vn, delay=wl.delay, window=0,
+        static_bidirectional=False, rope=_rope(wl), rope_times=_t_rel(wl),
+        qk_norm=dict(eps=1e-5, gamma_q=gq.astype(np.float64), gamma_k=gk.astype(np.float64)))
+    ref = ref[cand]
+    o_np = got.float().cpu().numpy().astype(np.float64)
+    err = np.abs(o_np - ref).max()
+    assert err <= 2e-2, err
+    assert np.linalg.norm(o_np - ref) <= 1e-2 * np.linalg.norm(ref)
+    full_plan.close()
+    cand_plan.close()
