@@ -23,7 +23,9 @@ bounded sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import contextlib
 import ctypes as C
+import gc
 import hashlib
 import json
 import os
@@ -40,6 +42,22 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ATTN_SRC = os.path.join(ROOT, "masked_attention_amd", "csrc", "attn_mfma.hip")
 ATTN_KERNEL = "attn_mfma_bf16_kernel"
 
+
+
+@contextlib.contextmanager
+def _gc_paused():
+    """Python's cyclic garbage collector held off over a timed region, after
+    one collection (as timeit does): a full pass over torch's object graph
+    stalls the host for tens of milliseconds, which a step of a fraction of a
+    millisecond cannot hide behind queued GPU work."""
+    gc.collect()
+    was = gc.isenabled()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if was:
+            gc.enable()
 
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
@@ -291,11 +309,12 @@ def backward_main(args) -> int:
         plans.append(step())
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        plans.append(step(evs[i]))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with _gc_paused():
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            plans.append(step(evs[i]))
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     for p in plans:
         p.close()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -377,11 +396,12 @@ def pointwise_main(args) -> int:
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with _gc_paused():
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     for p in plans:
         p.close()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -474,11 +494,12 @@ def lazformer_main(args) -> int:
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with _gc_paused():
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     for p in plans:
         p.close()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -962,11 +983,12 @@ def main() -> int:
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with _gc_paused():
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     # per-stage times: medians over the timed steps (attention: from the
     # point its inputs are ready to its end, on the stream it runs on)
