@@ -597,6 +597,19 @@ def summarize_trace(args) -> int:
     for r in trace:
         by.setdefault(_short_kernel(r["Kernel_Name"]), []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if "launches" not in b:
+        # the backward, pointwise and LazFormer lines: per-launch medians of
+        # every kernel launched at least ten times, and the line itself
+        out += ["", "Per-launch medians (kernel_trace.csv; microseconds):"]
+        for k, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+            if len(d) >= 10:
+                out.append(f"  {k:<42s} {statistics.median(d):>9.1f}  ({len(d)} launches)")
+        out += ["", "bench.py line of the same run: " + json.dumps(
+                    {k: b[k] for k in ("metric", "value", "unit", "ms_per_step")}),
+                "  stage_ms: " + json.dumps(b.get("stage_ms"))
+                + (f"; roofline frac: {b['roofline']['frac']}" if "roofline" in b else "")]
+        print("\n".join(out))
+        return 0
     la = b["launches"]
     attn_key = [k for k in by if k.startswith("attn_mfma") or k.startswith("attn_ref")]
     out += ["", "Attention kernel over the timed launches (kernel_trace.csv, in launch order: "
