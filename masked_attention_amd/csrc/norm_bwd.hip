@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kReduceThreads) void gamma_reduce_kernel(const floa
   for (; b < nblk; b += groups) s0 += partial[b * d + i];
   sums[threadIdx.x] = (s0 + s1) + (s2 + s3);
   __syncthreads();
-  if (threadIdx.x < d) {
+  if ((int)threadIdx.x < d) {
     float t = 0.f;
     for (int k = 0; k < groups; ++k) t += sums[k * d + threadIdx.x];
     dgamma[threadIdx.x] = t;
