@@ -5,9 +5,13 @@
 // pruning: the pruned history rows averaged into one).
 //
 // HBM-bound: every input row is read once and every output row written once.
-// One wave per output row, lanes across the row: 16-byte loads (8 bf16 or 4
-// fp32 per lane) when rows are 16-byte aligned, one element per lane
-// otherwise; fp32 accumulation, one rounding on the store.
+// Lanes across the row: 16-byte loads (8 bf16 or 4 fp32 per lane) when rows
+// are 16-byte aligned, one element per lane otherwise; a row narrower than
+// half a wave's reach shares the wave with others (2^rpw_log2 output rows
+// per wave, e.g. two at 4 heads x 64 bf16), so no lane idles.  Eight input
+// rows are loaded before they are added, so a group sum keeps eight loads
+// in flight instead of waiting for each; fp32 accumulation in input order,
+// one rounding on the store.
 #include <hip/hip_bf16.h>
 
 #include "rk_internal.h"
@@ -29,7 +33,7 @@ __device__ __forceinline__ void from_f(__hip_bfloat16* p, float v) {
   *(unsigned short*)p = f2bf(v);
 }
 
-constexpr int kWaves = 4;  // output rows per 256-thread block
+constexpr int kWaves = 4;  // waves per 256-thread block
 
 // V elements per lane per access: 16 bytes when vectorised, else 1.
 template <typename T, bool kVec, bool kMean>
@@ -37,21 +41,45 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const int2* __restrict_
                                                          int n_out, int n_in,
                                                          const T* __restrict__ x, int64_t xs,
                                                          T* __restrict__ y, int64_t ys,
-                                                         int width) {
+                                                         int width, int rpw_log2) {
   constexpr int V = kVec ? 16 / (int)sizeof(T) : 1;
   const int lane = threadIdx.x & 63;
-  const int i = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int lanes = 64 >> rpw_log2;  // lanes of one output row
+  const int sl = lane & (lanes - 1);
+  const int i = (((int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6)) << rpw_log2) +
+                (lane >> (6 - rpw_log2));
   if (i >= n_out) return;
   const int2 rg = ranges[i];
   const int b = min(max(rg.x, 0), n_in);
   const int e = min(max(rg.y, b), n_in);
   const float scale = kMean && e > b ? 1.f / (float)(e - b) : 1.f;
-  for (int c = lane * V; c < width; c += 64 * V) {
+  for (int c = sl * V; c < width; c += lanes * V) {
     float acc[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] = 0.f;
-    for (int j = b; j < e; ++j) {
-      const T* src = x + (int64_t)j * xs + c;
+    const T* src = x + (int64_t)b * xs + c;
+    int j = b;
+    for (; j + 8 <= e; j += 8, src += 8 * xs) {
+      if (kVec) {
+        uint4 u[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) u[k] = *(const uint4*)(src + k * xs);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          T vals[V];
+          __builtin_memcpy(vals, &u[k], 16);
+#pragma unroll
+          for (int v = 0; v < V; ++v) acc[v] += to_f(vals[v]);
+        }
+      } else {
+        T u[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) u[k] = src[k * xs];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[0] += to_f(u[k]);
+      }
+    }
+    for (; j < e; ++j, src += xs) {
       if (kVec) {
         const uint4 u = *(const uint4*)src;
         T vals[V];
@@ -82,13 +110,18 @@ hipError_t launch(const int2* ranges, int n_out, int n_in, const void* x, int64_
   const int per = 16 / (int)sizeof(T);
   const bool vec = ((uintptr_t)x % 16) == 0 && ((uintptr_t)y % 16) == 0 && width % per == 0 &&
                    xs % per == 0 && ys % per == 0;
-  const dim3 grid((unsigned)((n_out + kWaves - 1) / kWaves));
+  // output rows per wave: as many as fit whole in 64 lanes, at most 8
+  const int chunks = vec ? width / per : width;
+  int rpw_log2 = 0;
+  while (rpw_log2 < 3 && chunks <= (32 >> rpw_log2)) ++rpw_log2;
+  const int rows_per_block = kWaves << rpw_log2;
+  const dim3 grid((unsigned)((n_out + rows_per_block - 1) / rows_per_block));
   if (vec)
     hipLaunchKernelGGL((gather_sum_kernel<T, true, kMean>), grid, dim3(256), 0, s, ranges, n_out,
-                       n_in, (const T*)x, xs, (T*)y, ys, width);
+                       n_in, (const T*)x, xs, (T*)y, ys, width, rpw_log2);
   else
     hipLaunchKernelGGL((gather_sum_kernel<T, false, kMean>), grid, dim3(256), 0, s, ranges, n_out,
-                       n_in, (const T*)x, xs, (T*)y, ys, width);
+                       n_in, (const T*)x, xs, (T*)y, ys, width, rpw_log2);
   return hipGetLastError();
 }
 
