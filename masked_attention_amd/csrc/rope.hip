@@ -132,46 +132,68 @@ __global__ __launch_bounds__(256) void rope8_kernel(int R, int Tn, const int32_t
   float gm[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) gm[j] = kNorm && gamma ? gamma[8 * g + j] : 1.f;
-  for (int h = 0; h < H; ++h) {
-    float v[8];
-    if constexpr (sizeof(T) == 2) {
-      const uint4 raw = *(const uint4*)(xp + (int64_t)h * ish);
-      const unsigned u[4] = {raw.x, raw.y, raw.z, raw.w};
+  // Heads in chunks of kHc: the chunk's loads go out before any of its
+  // stores, so they are in flight together (input and output may be the
+  // same rows, and each thread reads and writes only its own elements, so
+  // loading ahead of the stores is safe in place too).  With QK Norm each
+  // head waits for a cross-lane sum anyway; one head at a time measured
+  // faster there.
+  constexpr int kHc = kNorm ? 1 : 4;
+  constexpr int kW = sizeof(T) == 2 ? 1 : 2;  // 16-byte words per head
+  for (int h0 = 0; h0 < H; h0 += kHc) {
+    uint4 raw[kHc][kW];
+#pragma unroll
+    for (int k = 0; k < kHc; ++k)
+      if (h0 + k < H)
+#pragma unroll
+        for (int q = 0; q < kW; ++q)
+          raw[k][q] = *(const uint4*)(xp + (int64_t)(h0 + k) * ish + 4 * q);
+#pragma unroll
+    for (int k = 0; k < kHc; ++k) {
+      if (h0 + k >= H) break;
+      const int h = h0 + k;
+      float v[8];
+      if constexpr (sizeof(T) == 2) {
+        const unsigned u[4] = {raw[k][0].x, raw[k][0].y, raw[k][0].z, raw[k][0].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = __uint_as_float(u[j] << 16);
+          v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < kW; ++q) {
+          v[4 * q] = __uint_as_float(raw[k][q].x);
+          v[4 * q + 1] = __uint_as_float(raw[k][q].y);
+          v[4 * q + 2] = __uint_as_float(raw[k][q].z);
+          v[4 * q + 3] = __uint_as_float(raw[k][q].w);
+        }
+      }
+      if (kNorm) {
+        // the d / 8 lanes of a token (consecutive, aligned) hold one row
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+        const float rstd = rsqrtf(row_sum(ss, groups) / (float)d + eps);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] *= rstd * gm[j];
+      }
+      float o[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[2 * j] = __uint_as_float(u[j] << 16);
-        v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+        o[2 * j] = v[2 * j] * cs[j] - v[2 * j + 1] * sn[j];
+        o[2 * j + 1] = v[2 * j] * sn[j] + v[2 * j + 1] * cs[j];
       }
-    } else {
-      const float4 p0 = *(const float4*)(xp + (int64_t)h * ish);
-      const float4 p1 = *(const float4*)(xp + (int64_t)h * ish + 4);
-      v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
-      v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
-    }
-    if (kNorm) {
-      // the d / 8 lanes of a token (consecutive, aligned) hold one row
-      float ss = 0.f;
+      if constexpr (sizeof(T) == 2) {
+        unsigned u[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
-      const float rstd = rsqrtf(row_sum(ss, groups) / (float)d + eps);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] *= rstd * gm[j];
-    }
-    float o[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      o[2 * j] = v[2 * j] * cs[j] - v[2 * j + 1] * sn[j];
-      o[2 * j + 1] = v[2 * j] * sn[j] + v[2 * j + 1] * cs[j];
-    }
-    if constexpr (sizeof(T) == 2) {
-      unsigned u[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        u[j] = (unsigned)f2bf(o[2 * j]) | ((unsigned)f2bf(o[2 * j + 1]) << 16);
-      *(uint4*)(yp + (int64_t)h * osh) = make_uint4(u[0], u[1], u[2], u[3]);
-    } else {
-      *(float4*)(yp + (int64_t)h * osh) = make_float4(o[0], o[1], o[2], o[3]);
-      *(float4*)(yp + (int64_t)h * osh + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        for (int j = 0; j < 4; ++j)
+          u[j] = (unsigned)f2bf(o[2 * j]) | ((unsigned)f2bf(o[2 * j + 1]) << 16);
+        *(uint4*)(yp + (int64_t)h * osh) = make_uint4(u[0], u[1], u[2], u[3]);
+      } else {
+        *(float4*)(yp + (int64_t)h * osh) = make_float4(o[0], o[1], o[2], o[3]);
+        *(float4*)(yp + (int64_t)h * osh + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      }
     }
   }
 }
