@@ -52,7 +52,11 @@ def _close(got, ref, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("width,pad", [(64, 0), (512, 8), (37, 3)])
+# widths that pack 8, 4, 2 and 1 output rows per wave (16-byte lanes: 64 bf16 = 8 lanes,
+# 128 = 16, 256 = 32, 512 = 64) and unaligned widths on the element-per-lane form (13: four
+# rows per wave, 37: one)
+@pytest.mark.parametrize("width,pad", [(64, 0), (128, 8), (256, 0), (512, 8), (13, 3),
+                                       (37, 3)])
 def test_gather_sum_compress_and_prune(rk, dtype, width, pad):
     rng = np.random.default_rng(width + pad)
     wl = make_custom(random_layout(rng, 9, 600), heads=1, d_head=2, seed=1, with_qkv=False)
@@ -94,7 +98,7 @@ def test_gather_sum_clamps_ranges(rk):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("width,pad", [(64, 0), (37, 3)])
+@pytest.mark.parametrize("width,pad", [(64, 0), (256, 0), (13, 3), (37, 3)])
 def test_gather_mean_pooled_pruning(rk, dtype, width, pad):
     """SORT's pooled query pruning (section 3.2.2): rk_prune_layout_ex's
     ranges moved by rk_gather_mean against the oracle's pooled layer input,
