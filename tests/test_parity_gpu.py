@@ -488,11 +488,15 @@ def test_failed_plan_outputs_nan(rk):
 # time RoPE
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 64), ("f32", 128)])
-def test_time_rope_matches_oracle(rk, dtype, d):
+# heads 3, 6 and 9: the vector pass loads heads in chunks of four (a partial chunk, one full
+# and one partial, two full and one partial)
+@pytest.mark.parametrize("dtype,d,heads", [("f32", 32, 2), ("bf16", 64, 3), ("f32", 128, 3),
+                                           ("bf16", 64, 6), ("f32", 64, 9)])
+def test_time_rope_matches_oracle(rk, dtype, d, heads):
     wl = make_config(1) if dtype == "f32" and d == 32 else make_custom(
-        random_layout(np.random.default_rng(5), 4, 300), heads=3, d_head=d, dtype=dtype, seed=4)
-    _say(f"[gpu] rope {dtype} d={d}")
+        random_layout(np.random.default_rng(5), 4, 300), heads=heads, d_head=d, dtype=dtype,
+        seed=4)
+    _say(f"[gpu] rope {dtype} d={d} heads={heads}")
     batch = rk.Batch.from_workload(wl)
     q, k, v = _tensors(wl)
     out = rk.rk_time_rope(batch, k, **_rope(wl))
