@@ -135,10 +135,8 @@ __global__ __launch_bounds__(256) void rope8_kernel(int R, int Tn, const int32_t
   // Heads in chunks of kHc: the chunk's loads go out before any of its
   // stores, so they are in flight together (input and output may be the
   // same rows, and each thread reads and writes only its own elements, so
-  // loading ahead of the stores is safe in place too).  With QK Norm each
-  // head waits for a cross-lane sum anyway; one head at a time measured
-  // faster there.
-  constexpr int kHc = kNorm ? 1 : 4;
+  // loading ahead of the stores is safe in place too).
+  constexpr int kHc = 4;
   constexpr int kW = sizeof(T) == 2 ? 1 : 2;  // 16-byte words per head
   for (int h0 = 0; h0 < H; h0 += kHc) {
     uint4 raw[kHc][kW];
