@@ -110,6 +110,10 @@ def _parse():
                     help="measure the chip's sustained bf16 MFMA rate instead (a whole-chip loop "
                          "of v_mfma_f32_32x32x16_bf16 at 8 waves per SIMD, on constant and on "
                          "random operands; built with hipcc at run time)")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="matrix-core counters of every kernel in a rocprofv3 --pmc run "
+                         "(GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES, SQ_WAVE_CYCLES, ...): "
+                         "busy share, resident waves per SIMD and clock per kernel")
     ap.add_argument("--bench-line", metavar="FILE", help="file whose last line is a bench JSON line")
     ap.add_argument("--profile-cmd", action="append", default=[],
                     help="profiler command to record in a summary (repeatable)")
@@ -733,6 +737,41 @@ def summarize_pmc(args) -> int:
     return 0
 
 
+def summarize_mfma(args) -> int:
+    """Per-kernel matrix-core counters of a --pmc run: means over each
+    kernel's dispatches of the MFMA busy share of its active cycles, the
+    resident waves per SIMD and the clock under the profiler."""
+    import statistics
+    b = _bench_line(args.bench_line)
+    out = _header(f"MFMA utilisation per kernel, {b['config']['workload']} ({b['metric']})", args)
+    m, dur = {}, {}
+    for r in _csv_rows(_find(args.summarize_mfma, "counter_collection.csv")):
+        k = _short_kernel(r["Kernel_Name"])
+        m.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            dur.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out += ["# GRBM_GUI_ACTIVE is summed over the 8 XCDs, SQ_VALU_MFMA_BUSY_CYCLES over the 1024",
+            "# SIMDs (one v_mfma_f32_32x32x16_bf16 counts 32 busy cycles), SQ_WAVE_CYCLES in units",
+            "# of 4 cycles over the chip.  Means over each kernel's dispatches.",
+            f"{'kernel':<44s} {'launches':>8s} {'us':>9s} {'mfma_busy':>9s} {'waves/SIMD':>10s} "
+            f"{'GHz':>6s} {'MFMA TFLOP/s':>12s}"]
+    for k, c in sorted(m.items(), key=lambda kv: -sum(dur.get(kv[0], [0]))):
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in c or "GRBM_GUI_ACTIVE" not in c:
+            continue
+        mean = {n: statistics.mean(v) for n, v in c.items()}
+        act = mean["GRBM_GUI_ACTIVE"] / 8
+        if act <= 0:
+            continue
+        d = statistics.mean(dur[k])
+        busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / act
+        waves = mean.get("SQ_WAVE_CYCLES", 0.0) * 4 / (act * 1024)
+        flops = mean.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        out.append(f"{k:<44s} {len(dur[k]):>8d} {d / 1e3:>9.1f} {busy:>9.4f} {waves:>10.3f} "
+                   f"{act / d:>6.3f} {flops / d / 1e3:>12.1f}")
+    print("\n".join(out))
+    return 0
+
+
 # Whole-chip MFMA loop: 2048 workgroups of 4 waves (8 waves per SIMD), each
 # wave issuing 8 independent-accumulator-pair v_mfma_f32_32x32x16_bf16 per
 # iteration on operands that are either constant or random bf16 values that
@@ -839,6 +878,8 @@ def main() -> int:
         return summarize_trace(args)
     if args.summarize_pmc:
         return summarize_pmc(args)
+    if args.summarize_mfma:
+        return summarize_mfma(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: the masked-attention path is built and "
