@@ -10,10 +10,11 @@
 // App. H, M-FALCON; the flash-decoding split of a long key range).  The
 // kernels keep m in their own units; to_log2 and to_nat convert it.
 //
-// One 512-thread workgroup per split item: four threads per query row, each
-// owning a quarter of d_head.  Parts are read four at a time (their loads in
-// flight together) and merged with the online rescaling, so the running max
-// is never re-read.
+// d_head / 4 threads per query row, each owning four d values (one 16-byte
+// load per part), so a split item's 128 rows spread over d_head / 16
+// workgroups of 512 threads.  Parts are read sixteen at a time (their loads
+// in flight together) and merged with the online rescaling, so the running
+// max is never re-read.
 #include <hip/hip_bf16.h>
 
 #include "rk_internal.h"
@@ -28,22 +29,31 @@ __device__ __forceinline__ void st(__hip_bfloat16* p, float v) {
   *(unsigned short*)p = (unsigned short)(u >> 16);
 }
 
-constexpr int kGroup = 4;  // parts read together
+constexpr int kGroup = 16;  // parts read together
+constexpr int kThreads = 512;
+
+// workgroups per split item at width D: 128 rows of D / 4 threads
+template <int D>
+constexpr int blocks_per_item() { return kTileQ * (D / 4) / kThreads; }
 
 template <typename T, int D>
-__global__ __launch_bounds__(512) void attn_combine_kernel(const ReqMeta* req, const int32_t* qt_req,
-                                                           const SplitEntry* splits, AttnLaunch A,
-                                                           float to_log2, float to_nat) {
-  constexpr int kQ = D / 4;       // d values of this thread
-  constexpr int kV = kQ / 4;      // float4 loads per part
+__global__ __launch_bounds__(kThreads) void attn_combine_kernel(const ReqMeta* req,
+                                                                const int32_t* qt_req,
+                                                                const SplitEntry* splits,
+                                                                AttnLaunch A, float to_log2,
+                                                                float to_nat) {
+  constexpr int kQ = 4;           // d values of this thread
+  constexpr int kV = 1;           // float4 loads per part
+  constexpr int kTpr = D / kQ;    // threads per row
   constexpr int kStride = kTileQ * (D + 2);
-  const SplitEntry se = splits[blockIdx.x];
+  const SplitEntry se = splits[blockIdx.x / blocks_per_item<D>()];
   if (se.item < 0) return;
   const int qg = se.item / A.H;
   const int head = se.item - qg * A.H;
   const ReqMeta m = req[qt_req[qg]];
-  const int rl = threadIdx.x >> 2;
-  const int c0 = (threadIdx.x & 3) * kQ;
+  const int rl = (int)(blockIdx.x % blocks_per_item<D>()) * (kThreads / kTpr) +
+                 (int)threadIdx.x / kTpr;
+  const int c0 = ((int)threadIdx.x % kTpr) * kQ;
   const int row = (qg - m.qt_off) * kTileQ + rl;
   if (row >= m.len) return;
   const int tok = m.tok_off + row;
@@ -104,7 +114,8 @@ template <typename T, int D>
 hipError_t launch(const rk_plan* p, const AttnLaunch& a, float to_log2, float to_nat,
                   hipStream_t s) {
   // at most kSplitTarget / 2 items are split
-  hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3((unsigned)(kSplitTarget / 2)), dim3(512), 0,
+  hipLaunchKernelGGL((attn_combine_kernel<T, D>),
+                     dim3((unsigned)(kSplitTarget / 2 * blocks_per_item<D>())), dim3(kThreads), 0,
                      s, p->dev.req, p->dev.qt_req, p->dev.splits, a, to_log2, to_nat);
   return hipGetLastError();
 }
