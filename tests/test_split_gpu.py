@@ -266,6 +266,40 @@ def test_split_rows_seeing_nothing(rk):
     plan.close()
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 128)])
+def test_split_many_parts(rk, dtype, d):
+    """One request of 20,000 history keys and one candidate, one head: its
+    only item (313 key tiles) splits into ceil(313 / 8) = 40 parts, more than
+    the merge reads in one group, so the merge's online rescaling runs over
+    several groups and a short last one.  Candidate tile rows against the
+    oracle."""
+    rng = np.random.default_rng(530)
+    h = history_raw(rng, 20000, NOW - DAY)
+    reqs = [[(HISTORY, h), (CANDIDATE, np.array([NOW], np.int64))]]
+    wl = make_custom(reqs, heads=1, d_head=d, dtype=dtype, seed=530, name="split-40-parts")
+    batch = rk.Batch.from_workload(wl)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x).to("cuda").to(tdt) for x in (wl.q, wl.k, wl.v))
+    plan = rk.Plan(batch, num_heads=1, candidates_only=True)
+    split = check_work_list(plan, 1)
+    assert list(split.values()) == [40]
+    rope = dict(phi_min=wl.phi_min, dt_max=wl.dt_max, base=wl.base)
+    o, lse = _run(rk, wl, plan, q, k, v, rope, False)
+    (it,) = split
+    a, b = _qtile_rows(wl)[it]
+    rows = np.arange(a, b)
+    ref_o, ref_l = oracle.attention_rows(
+        wl.req_offsets, wl.seg_kind, wl.timestamps, wl.q.astype(np.float64),
+        wl.k.astype(np.float64), wl.v.astype(np.float64), rows, 0, delay=0, window=0,
+        static_bidirectional=False, rope=rope)
+    got_o = o[a:b, 0].float().cpu().numpy()
+    got_l = lse[0, a:b].cpu().numpy()
+    tol = BF16_MAX_ABS if dtype == "bf16" else F32_TOL
+    assert np.abs(got_o - ref_o).max() <= tol * max(1.0, np.abs(ref_o).max())
+    assert np.abs(got_l - ref_l).max() <= 1e-3
+    plan.close()
+
+
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_split_work_list_workloads(rk, cfg):
     """The serving workload (3: 1024 items, the schedule mirrored) and the
