@@ -46,11 +46,12 @@ ATTN_KERNEL = "attn_mfma_bf16_kernel"
 
 @contextlib.contextmanager
 def _gc_paused():
-    """Python's cyclic garbage collector held off over a timed region, after
-    one collection (as timeit does): a full pass over torch's object graph
-    stalls the host for tens of milliseconds, which a step of a fraction of a
-    millisecond cannot hide behind queued GPU work."""
-    gc.collect()
+    """Python's cyclic garbage collector held off over a timed region (as
+    timeit does): a full pass over torch's object graph stalls the host for
+    tens of milliseconds, which a step of a fraction of a millisecond cannot
+    hide behind queued GPU work.  The collection itself runs before the
+    warmup steps (_gc_before_warmup), so that the GPU is not left idle, and
+    its clock low, just before the first timed step."""
     was = gc.isenabled()
     gc.disable()
     try:
@@ -58,6 +59,12 @@ def _gc_paused():
     finally:
         if was:
             gc.enable()
+
+
+def _gc_before_warmup():
+    """One full collection ahead of the warmup steps (see _gc_paused)."""
+    gc.collect()
+
 
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
@@ -309,6 +316,7 @@ def backward_main(args) -> int:
     n = C.c_size_t()
     _rk.check(_rk.lib().rk_attn_bwd_workspace_size(plan.handle, C.byref(a), C.byref(n)), "ws")
     bws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+    _gc_before_warmup()
     for _ in range(args.warmup):
         plans.append(step())
     torch.cuda.synchronize()
@@ -396,6 +404,7 @@ def pointwise_main(args) -> int:
         if ev: ev[2].record(stream)
         plans.append(p)
 
+    _gc_before_warmup()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -494,6 +503,7 @@ def lazformer_main(args) -> int:
             plans.append(p)
         if ev: ev[2].record(stream)
 
+    _gc_before_warmup()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -1023,6 +1033,7 @@ def main() -> int:
         del src, dst
 
     # warmup serially (timed, for the auto choice), then in the chosen mode
+    _gc_before_warmup()
     torch.cuda.synchronize()
     tw = time.perf_counter()
     for _ in range(args.warmup):
